@@ -1,0 +1,88 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one: a dropped sqrt(2), a dropped diagonal, a read-before-update,
+an unnormalised prediction, a reversed selection, a fold of the kept pairs."""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.kla_oracle as K
+from tests import test_oracle_hybrid as TH
+from tests import test_oracle_phi_prefill as TP
+from tests import test_oracle_sre_select as TS
+
+
+def _phi_no_sqrt2(x):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    return np.stack([x[..., i] * x[..., j] for i in range(d) for j in range(i, d)], axis=-1)
+
+
+def _chunked_strict_lower(q, k, v, chunk=256, H0=None, s0=None, eps=0.0, return_parts=False):
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    T, d = q.shape
+    H = np.zeros((O.phi_dim(d), v.shape[1]))
+    s = np.zeros(O.phi_dim(d))
+    o = np.zeros((T, v.shape[1]))
+    for c0 in range(0, T, chunk):
+        Q, Kc, V = q[c0:c0 + chunk], k[c0:c0 + chunk], v[c0:c0 + chunk]
+        S = Q @ Kc.T
+        A = np.tril(S * S, k=-1)  # planted: diagonal dropped
+        num = A @ V + O.phi(Q) @ H
+        den = A.sum(1) + O.phi(Q) @ s
+        o[c0:c0 + chunk] = K._safe_div(num, den)
+        H += O.phi(Kc).T @ V
+        s += O.phi(Kc).sum(0)
+    return o, H, s
+
+
+def _decode_read_first(H, s, q, k, v, eps=0.0):
+    fq = O.phi(q)
+    den = fq @ s + eps
+    o = (fq @ H) / den if den else np.zeros(np.shape(H)[1])  # planted: read before update
+    fk = O.phi(k)
+    return o, H + np.outer(fk, v), s + fk
+
+
+def _sre_unnormalised(H, s, k, v, eps=0.0):
+    pred = O.phi(k) @ H  # planted: no division by phi(k).s
+    return np.sum((pred - v) ** 2, axis=-1)
+
+
+def _select_ascending(scores, m, ids=None):
+    ids = np.arange(len(scores)) if ids is None else np.asarray(ids)
+    return np.lexsort((ids, np.asarray(scores)))[:m]  # planted: lowest first
+
+
+CASES = [
+    ("phi", _phi_no_sqrt2, [TP.test_phi_golden, TP.test_phi_random_float_identity]),
+    ("prefill_chunked", _chunked_strict_lower, [TP.test_first_token_returns_its_value]),
+    ("decode_step", _decode_read_first, [TS.test_decode_step_matches_definition_cases]),
+    ("sre", _sre_unnormalised, [TS.test_sre_golden]),
+    ("select_topk", _select_ascending, [TS.test_select_topk_order_against_python_sort]),
+]
+
+
+@pytest.mark.parametrize("name,bad,pins", CASES, ids=[c[0] for c in CASES])
+def test_pins_catch_planted_mistake(monkeypatch, name, bad, pins):
+    monkeypatch.setattr(O, name, bad)
+    monkeypatch.setattr(K, name, bad)
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"no pin caught the planted mistake in {name}"
+
+
+def test_hybrid_pin_catches_fold_of_kept_pairs(monkeypatch):
+    real_select = K.select_topk
+
+    def select_complement(scores, m, ids=None):
+        # planted: keep the lowest-score pairs (fold the hard ones)
+        order = real_select(-np.asarray(scores), len(scores), ids)
+        return order[:m]
+
+    monkeypatch.setattr(K, "select_topk", select_complement)
+    with pytest.raises(AssertionError):
+        TH.test_refresh_chain_against_token_by_token_enumeration(3, 16, 4, 8)
