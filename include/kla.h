@@ -1,0 +1,218 @@
+/*
+ * kla.h - C ABI of libkla: causal kernelized linear attention on AMD MI355X
+ * (gfx950).
+ *
+ * Pages cited:
+ *   KATA = "Kernelized Linear Attention: Breaking the Capacity Wall with
+ *          Symmetric Cones" (gist.science/pt/paper/2607.17419);
+ *   LoLA = "LoLA: Low-Rank Linear Attention with Sparse Caching", Portuguese
+ *          technical summary (gist.science/pt/paper/2505.23666).
+ *
+ * What is computed (per attention head, tokens t = 0..T-1):
+ *   o_t = phi(q_t)^T H_t / (phi(q_t)^T s_t + eps),
+ *   H_t = sum_{i<=t} phi(k_i) v_i^T,   s_t = sum_{i<=t} phi(k_i)
+ * with the rank-one PSD lift of KATA §2.2, psi(u) = u u^T, vectorised as
+ *   phi(x)_f = x_i^2 (i == j),  sqrt(2) x_i x_j (i < j),
+ *   f(i, j) = i*d - i*(i-1)/2 + (j - i),  D = d(d+1)/2,
+ * so that phi(q) . phi(k) = (q . k)^2. KATA §1 states the problem (normalised
+ * linear attention over a fixed-size state); KATA §2.3 gives the chunked
+ * form with a cross-chunk prefix of the state; LoLA ("Metodologia") names the
+ * state (H_t, s_t) and defines the self-recall error and the three-memory
+ * hybrid ("Estratégia de Inferência").
+ *
+ * Conventions shared by every call:
+ *   - Memory: every tensor pointer is a device pointer owned by the caller.
+ *     The library never allocates or frees device memory and keeps no
+ *     per-call state; scratch memory comes from the caller through `ws`,
+ *     sized by the matching *_workspace_size query.
+ *   - Layout: tensors are dense row-major (C order), shapes given below.
+ *     N = B*H heads, ordered (b, h). The state is H [N, D, d_v] and
+ *     s [N, D], float32, in the coordinate order and sqrt(2) scaling above.
+ *   - Execution: every call enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL is the null stream) and returns without synchronising. Device
+ *     faults surface at the caller's next synchronisation.
+ *   - Errors: every argument is checked on the host before anything is
+ *     enqueued; a call that fails a check returns its status, enqueues
+ *     nothing and writes no output. A failed launch returns KLA_ERR_HIP.
+ *     kla_last_error() gives a text for the last failure on this thread.
+ *     No C++ exception crosses this interface.
+ *   - Data: inputs must be finite; values are not checked.
+ *   - Supported now: d_qk, d_v in {16, 32, 64}; chunk in {32, 64, 128};
+ *     any T >= 1 (the last chunk may be partial). Other shapes return
+ *     KLA_ERR_UNSUPPORTED.
+ */
+#ifndef KLA_H
+#define KLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KLA_API __attribute__((visibility("default")))
+#else
+#define KLA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t, declared here so that C callers need no HIP header. */
+struct ihipStream_t;
+typedef struct ihipStream_t* kla_stream_t;
+
+typedef enum {
+  KLA_OK = 0,
+  KLA_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad size, aliasing */
+  KLA_ERR_UNSUPPORTED = 2,      /* shape or dtype outside the supported set */
+  KLA_ERR_WORKSPACE = 3,        /* ws too small or NULL when needed */
+  KLA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} kla_status_t;
+
+typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define KLA_ABI_VERSION 1
+KLA_API int kla_abi_version(void);
+
+/* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
+KLA_API int kla_phi_dim(int d_qk);
+
+/* Static text for a status code. */
+KLA_API const char* kla_status_string(kla_status_t s);
+
+/* Text describing the last failed call on the calling thread ("" if none). */
+KLA_API const char* kla_last_error(void);
+
+/* Shapes of a prefill-type call. q, k: [B, H, T, d_qk]; v, o: [B, H, T, d_v].
+ * in_dtype applies to q, k and v; out_dtype to o. eps is added to every
+ * denominator; a denominator of exactly 0 gives o = 0. */
+typedef struct {
+  int B, H, T, d_qk, d_v;
+  kla_dtype_t in_dtype, out_dtype;
+  float eps;
+} kla_shape_t;
+
+/* ------------------------------------------------------------------------
+ * kla_prefill - chunked causal prefill (KATA §2.3, "Paralelismo por Blocos"
+ * and the linear chunked-state operating point).
+ *
+ * Splits each head's tokens into chunks of `chunk`. Within a chunk the
+ * masked (Q K^T)∘(Q K^T) scores multiply [V | 1]; across chunks the float32
+ * state (H, s) is carried as a running prefix sum and read out by phi(Q).
+ * Results equal the causal definition above up to rounding for every
+ * supported chunk length.
+ *
+ *   q, k, v : inputs, in_dtype, shapes above (required).
+ *   o       : output [B, H, T, d_v], out_dtype. May be NULL only when H_T and
+ *             s_T are given (state-only mode: no outputs are computed).
+ *   H0, s0  : initial state [N, D, d_v] and [N, D] float32, or both NULL for
+ *             a zero state (resuming a previous call).
+ *   H_T,s_T : final state, or both NULL to skip writing it. May alias H0/s0.
+ *   ws      : workspace of at least kla_prefill_workspace_size() bytes
+ *             (may be NULL when that size is 0).
+ * ------------------------------------------------------------------------ */
+KLA_API kla_status_t kla_prefill_workspace_size(const kla_shape_t* shp, int chunk, int with_output,
+                                        size_t* bytes);
+KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const void* k,
+                         const void* v, void* o, const float* H0, const float* s0, float* H_T,
+                         float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Self-recall error and selection (LoLA, the self-recall-error section and
+ * "Estratégia de Inferência" item 2).
+ *
+ * For candidate c of head n: pred = phi(k_c)^T H / (phi(k_c)^T s + eps)
+ * (pred = 0 when that denominator is 0) and score = ||pred - v_c||^2.
+ * The top_k candidates by (score descending, candidate index ascending) are
+ * selected; `sel` lists them in that order.
+ *
+ *   cand_k : [N, n_cand, d_qk] float32;  cand_v : [N, n_cand, d_v] float32.
+ *   scores : [N, n_cand] float32 output, or NULL.
+ *   sel    : [N, top_k] int32 output (required).
+ *   sel_k, sel_v : optional gather of the selected pairs, [N, top_k, d_qk]
+ *            and [N, top_k, d_v] float32, both or neither; must not overlap
+ *            cand_k / cand_v.
+ * Supported: 1 <= top_k <= n_cand <= 256.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int n_cand, top_k;
+  const float* cand_k;
+  const float* cand_v;
+  float* scores;
+  int32_t* sel;
+  float* sel_k;
+  float* sel_v;
+} kla_sre_args_t;
+
+/* ------------------------------------------------------------------------
+ * kla_decode_step - one recurrent token for N independent head-states
+ * (KATA §1, constant-time recurrent inference; LoLA "Estratégia de
+ * Inferência", token-by-token mode).
+ *
+ * For every head n: s += phi(k); H += phi(k) v^T (the update comes first,
+ * since H_t sums i <= t); o = phi(q)^T H / (phi(q)^T s + eps).
+ * If `sre` is not NULL, the candidates are then scored and selected as in
+ * kla_sre_select, against the UPDATED state, in the same call.
+ *
+ *   H, s : [N, D, d_v], [N, D] float32, updated in place.
+ *   q, k : [N, d_qk]; v : [N, d_v]; in_dtype.   o : [N, d_v], out_dtype.
+ * ------------------------------------------------------------------------ */
+KLA_API kla_status_t kla_decode_workspace_size(int N, int d_qk, int d_v, const kla_sre_args_t* sre,
+                                       size_t* bytes);
+KLA_API kla_status_t kla_decode_step(int N, int d_qk, int d_v, float eps, float* H, float* s,
+                             const void* q, const void* k, const void* v, kla_dtype_t in_dtype,
+                             void* o, kla_dtype_t out_dtype, const kla_sre_args_t* sre, void* ws,
+                             size_t ws_bytes, kla_stream_t stream);
+
+/* kla_sre_select - scoring and selection only; H and s are read, not written. */
+KLA_API kla_status_t kla_sre_workspace_size(int N, int d_qk, int d_v, const kla_sre_args_t* sre,
+                                    size_t* bytes);
+KLA_API kla_status_t kla_sre_select(int N, int d_qk, int d_v, float eps, const float* H, const float* s,
+                            const kla_sre_args_t* sre, void* ws, size_t ws_bytes,
+                            kla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kla_hybrid_prefill - LoLA's three memories over a prefill (LoLA
+ * "Metodologia" items 1-3, "Estratégia de Inferência" items 1-4).
+ *
+ * Tokens are processed in blocks of `refresh`. At the start of block b the
+ * eviction frontier is f = max(0, b*refresh - window); tokens that cross it
+ * join the candidate set together with the current sparse cache. When the
+ * candidates exceed cache_size, each is scored by the self-recall error
+ * against the current linear state (before this refresh's fold); the
+ * cache_size highest (score desc, token id asc) stay in the cache and all
+ * others are folded into (H, s) by outer products. Each query t of the
+ * block then reads one jointly normalised mixture:
+ *   num = sum_{i in [f, t]} e^{a q.k_i} v_i + sum_{j in cache} e^{a q.k_j} v_j
+ *         + phi(q)^T H,
+ *   den = the same sums without v + phi(q)^T s + eps,   o_t = num / den,
+ * with a = softmax_scale.
+ *
+ *   q, k : [B, H, T, d_qk]; v, o : [B, H, T, d_v]  (in_dtype / out_dtype).
+ *   H_T, s_T        : final linear state, or both NULL.
+ *   cache_tokens_T  : [N, cache_size] int32 final cache token ids ascending,
+ *                     -1 for empty slots, or NULL.
+ *   sel_trace       : [N, ceil(T/refresh), cache_size] int32, or NULL. Row b
+ *                     holds the ids kept by block b's scored refresh
+ *                     (ascending); rows of blocks without one are all -1.
+ * Supported: d_qk, d_v in {16, 32, 64}; 1 <= refresh <= 128; window >= 0;
+ * 0 <= cache_size and cache_size + refresh <= 256; softmax_scale finite.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int window, cache_size, refresh;
+  float softmax_scale;
+} kla_hybrid_cfg_t;
+
+KLA_API kla_status_t kla_hybrid_workspace_size(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg,
+                                       size_t* bytes);
+KLA_API kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg,
+                                const void* q, const void* k, const void* v, void* o, float* H_T,
+                                float* s_T, int32_t* cache_tokens_T, int32_t* sel_trace,
+                                void* ws, size_t ws_bytes, kla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H */

@@ -1,0 +1,27 @@
+"""kla — causal kernelized linear attention with the rank-one PSD lift, on
+AMD MI355X (gfx950).
+
+The computation lives in libkla.so (hand-written HIP kernels behind the C
+ABI of include/kla.h); this package only marshals arguments to it:
+
+  prefill         chunked causal prefill over the float32 state (H, s)
+  decode_step     one recurrent token, optionally with self-recall scoring
+  sre_select      self-recall-error scoring and top-k selection
+  hybrid_prefill  sliding window + linear state + sparse cache
+
+``synth`` builds the seeded synthetic workloads.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    KlaError,
+    LIB_PATH,
+    decode_step,
+    hybrid_prefill,
+    load_library,
+    phi_dim,
+    prefill,
+    sre_select,
+)
+
+__all__ = ["prefill", "decode_step", "sre_select", "hybrid_prefill", "phi_dim", "load_library",
+           "KlaError", "EXPORTS", "LIB_PATH"]

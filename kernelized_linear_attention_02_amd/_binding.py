@@ -1,0 +1,303 @@
+"""ctypes binding of libkla's C ABI (include/kla.h).
+
+Argument marshalling only: these functions check Python-level types,
+allocate outputs and workspace with ``torch.empty`` on the inputs' device,
+and pass raw device pointers and the current HIP stream to the library.
+Every step of the computation runs in the library's HIP kernels; there is
+no fallback. If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkla.so")
+
+KLA_OK, KLA_ERR_INVALID_ARGUMENT, KLA_ERR_UNSUPPORTED, KLA_ERR_WORKSPACE, KLA_ERR_HIP = range(5)
+KLA_F32, KLA_BF16 = 0, 1
+
+EXPORTS = (
+    "kla_abi_version", "kla_phi_dim", "kla_status_string", "kla_last_error",
+    "kla_prefill_workspace_size", "kla_prefill",
+    "kla_decode_workspace_size", "kla_decode_step",
+    "kla_sre_workspace_size", "kla_sre_select",
+    "kla_hybrid_workspace_size", "kla_hybrid_prefill",
+)
+
+
+class KlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("T", ctypes.c_int),
+                ("d_qk", ctypes.c_int), ("d_v", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("eps", ctypes.c_float)]
+
+
+class SreArgs(ctypes.Structure):
+    _fields_ = [("n_cand", ctypes.c_int), ("top_k", ctypes.c_int),
+                ("cand_k", ctypes.c_void_p), ("cand_v", ctypes.c_void_p),
+                ("scores", ctypes.c_void_p), ("sel", ctypes.c_void_p),
+                ("sel_k", ctypes.c_void_p), ("sel_v", ctypes.c_void_p)]
+
+
+class HybridCfg(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int), ("cache_size", ctypes.c_int),
+                ("refresh", ctypes.c_int), ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkla.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libkla.so not found at {path}; build it with "
+                          f"`python -m kernelized_linear_attention_02_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    shp = ctypes.POINTER(Shape)
+    srp = ctypes.POINTER(SreArgs)
+    hcp = ctypes.POINTER(HybridCfg)
+    sig = {
+        "kla_abi_version": (i, []),
+        "kla_phi_dim": (i, [i]),
+        "kla_status_string": (ctypes.c_char_p, [i]),
+        "kla_last_error": (ctypes.c_char_p, []),
+        "kla_prefill_workspace_size": (i, [shp, i, i, szp]),
+        "kla_prefill": (i, [shp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
+        "kla_decode_step": (i, [i, i, i, f, vp, vp, vp, vp, vp, i, vp, i, srp, vp, sz, vp]),
+        "kla_sre_workspace_size": (i, [i, i, i, srp, szp]),
+        "kla_sre_select": (i, [i, i, i, f, vp, vp, srp, vp, sz, vp]),
+        "kla_hybrid_workspace_size": (i, [shp, hcp, szp]),
+        "kla_hybrid_prefill": (i, [shp, hcp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int):
+    if status != KLA_OK:
+        lib = load_library()
+        raise KlaError(status, lib.kla_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return KLA_F32
+    if t.dtype == torch.bfloat16:
+        return KLA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return torch.float32 if code == KLA_F32 else torch.bfloat16
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libkla works on device tensors only")
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+
+
+def phi_dim(d: int) -> int:
+    return load_library().kla_phi_dim(int(d))
+
+
+def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, eps: float = 0.0,
+            out_dtype=None, outputs: bool = True):
+    """Chunked causal prefill. q, k [B, H, T, d_qk]; v [B, H, T, d_v] (float32 or
+    bfloat16, same dtype). ``state`` = (H0, s0) float32 resumes a previous call.
+    Returns o, or (o, H_T, s_T) with ``return_state``; with ``outputs=False``
+    only (H_T, s_T)."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(q, k, v)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hh, T, dqk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("shape mismatch between q, k and v")
+    code = _dtype_code(q)
+    ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    shp = Shape(B, Hh, T, dqk, dv, code, ocode, float(eps))
+    D = phi_dim(dqk)
+    dev = q.device
+    o = torch.empty((B, Hh, T, dv), dtype=_torch_dtype(ocode), device=dev) if outputs else None
+    want_state = return_state or not outputs
+    HT = torch.empty((B, Hh, D, dv), dtype=torch.float32, device=dev) if want_state else None
+    sT = torch.empty((B, Hh, D), dtype=torch.float32, device=dev) if want_state else None
+    H0 = s0 = None
+    if state is not None:
+        H0, s0 = (x.contiguous() for x in state)
+        _need_device(H0, s0)
+        if H0.dtype != torch.float32 or s0.dtype != torch.float32:
+            raise TypeError("state must be float32")
+        if H0.numel() != B * Hh * D * dv or s0.numel() != B * Hh * D:
+            raise ValueError("state shape does not match [B, H, D, d_v], [B, H, D]")
+    nbytes = ctypes.c_size_t(0)
+    check(lib.kla_prefill_workspace_size(ctypes.byref(shp), int(chunk), int(outputs), ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    check(lib.kla_prefill(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                          _ptr(H0), _ptr(s0), _ptr(HT), _ptr(sT), _ptr(ws), nbytes.value,
+                          _stream(dev)))
+    if not outputs:
+        return HT, sT
+    return (o, HT, sT) if return_state else o
+
+
+def _sre_struct(cand_k, cand_v, top_k, scores, sel, sel_k, sel_v):
+    return SreArgs(int(cand_k.shape[-2]), int(top_k), cand_k.data_ptr(), cand_v.data_ptr(),
+                   None if scores is None else scores.data_ptr(), sel.data_ptr(),
+                   None if sel_k is None else sel_k.data_ptr(),
+                   None if sel_v is None else sel_v.data_ptr())
+
+
+def _sre_outputs(N, n_cand, top_k, dqk, dv, device, scores, gather, out=None):
+    torch = _torch()
+    if out is not None:
+        return out["scores"], out["sel"], out.get("sel_k"), out.get("sel_v")
+    sc = torch.empty((N, n_cand), dtype=torch.float32, device=device) if scores else None
+    sel = torch.empty((N, top_k), dtype=torch.int32, device=device)
+    sk = torch.empty((N, top_k, dqk), dtype=torch.float32, device=device) if gather else None
+    sv = torch.empty((N, top_k, dv), dtype=torch.float32, device=device) if gather else None
+    return sc, sel, sk, sv
+
+
+def decode_step(H, s, q, k, v, eps: float = 0.0, out_dtype=None, cand_k=None, cand_v=None,
+                top_k: int = 0, scores: bool = True, gather: bool = False, out=None):
+    """One recurrent token for N head-states; H [N, D, d_v], s [N, D] float32
+    updated in place; q, k [N, d_qk], v [N, d_v]. With candidates
+    (cand_k [N, n_cand, d_qk], cand_v [N, n_cand, d_v] float32) and top_k,
+    also scores and selects against the updated state. ``out`` may pass
+    preallocated {'o', 'scores', 'sel', 'sel_k', 'sel_v'} tensors.
+    Returns o, or (o, dict(scores, sel, sel_k, sel_v))."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(H, s, q, k, v)
+    for t in (H, s):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("H and s must be contiguous float32 (updated in place)")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    N, dqk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    dev = q.device
+    o = out["o"] if out is not None else torch.empty((N, dv), dtype=_torch_dtype(ocode), device=dev)
+    sre_p = None
+    res = None
+    if cand_k is not None:
+        cand_k, cand_v = cand_k.contiguous(), cand_v.contiguous()
+        sc, sel, sk, sv = _sre_outputs(N, cand_k.shape[1], top_k, dqk, dv, dev, scores, gather, out)
+        sre = _sre_struct(cand_k, cand_v, top_k, sc, sel, sk, sv)
+        sre_p = ctypes.byref(sre)
+        res = dict(scores=sc, sel=sel, sel_k=sk, sel_v=sv)
+    nbytes = ctypes.c_size_t(0)
+    check(lib.kla_decode_workspace_size(N, dqk, dv, sre_p, ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    check(lib.kla_decode_step(N, dqk, dv, float(eps), _ptr(H), _ptr(s), _ptr(q), _ptr(k), _ptr(v),
+                              code, _ptr(o), ocode, sre_p, _ptr(ws), nbytes.value, _stream(dev)))
+    return o if res is None else (o, res)
+
+
+def sre_select(H, s, cand_k, cand_v, top_k: int, eps: float = 0.0, scores: bool = True,
+               gather: bool = False):
+    """Score candidates by self-recall error against (H, s) and select the
+    top_k. Returns dict(scores, sel, sel_k, sel_v)."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(H, s, cand_k, cand_v)
+    H, s = H.contiguous(), s.contiguous()
+    cand_k, cand_v = cand_k.contiguous(), cand_v.contiguous()
+    if cand_k.dtype != torch.float32 or cand_v.dtype != torch.float32:
+        raise TypeError("candidates must be float32")
+    N, n_cand, dqk = cand_k.shape
+    dv = cand_v.shape[-1]
+    dev = cand_k.device
+    sc, sel, sk, sv = _sre_outputs(N, n_cand, top_k, dqk, dv, dev, scores, gather)
+    sre = _sre_struct(cand_k, cand_v, top_k, sc, sel, sk, sv)
+    nbytes = ctypes.c_size_t(0)
+    check(lib.kla_sre_workspace_size(N, dqk, dv, ctypes.byref(sre), ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    check(lib.kla_sre_select(N, dqk, dv, float(eps), _ptr(H), _ptr(s), ctypes.byref(sre), _ptr(ws),
+                             nbytes.value, _stream(dev)))
+    return dict(scores=sc, sel=sel, sel_k=sk, sel_v=sv)
+
+
+def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, softmax_scale=None,
+                   eps: float = 0.0, return_state: bool = False, return_cache: bool = False,
+                   return_trace: bool = False, out_dtype=None):
+    """Window + linear state + sparse cache prefill. Returns o, plus a dict
+    with H, s, cache (token ids) and trace when requested."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(q, k, v)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    B, Hh, T, dqk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    shp = Shape(B, Hh, T, dqk, dv, code, ocode, float(eps))
+    cfg = HybridCfg(int(window), int(cache_size), int(refresh), float(softmax_scale))
+    dev = q.device
+    D = phi_dim(dqk)
+    nblk = -(-T // refresh)
+    o = torch.empty((B, Hh, T, dv), dtype=_torch_dtype(ocode), device=dev)
+    HT = torch.empty((B, Hh, D, dv), dtype=torch.float32, device=dev) if return_state else None
+    sT = torch.empty((B, Hh, D), dtype=torch.float32, device=dev) if return_state else None
+    cT = torch.empty((B, Hh, cache_size), dtype=torch.int32, device=dev) if return_cache else None
+    tr = torch.empty((B, Hh, nblk, cache_size), dtype=torch.int32, device=dev) if return_trace else None
+    nbytes = ctypes.c_size_t(0)
+    check(lib.kla_hybrid_workspace_size(ctypes.byref(shp), ctypes.byref(cfg), ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    check(lib.kla_hybrid_prefill(ctypes.byref(shp), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(o), _ptr(HT), _ptr(sT), _ptr(cT), _ptr(tr), _ptr(ws),
+                                 nbytes.value, _stream(dev)))
+    if not (return_state or return_cache or return_trace):
+        return o
+    return o, dict(H=HT, s=sT, cache=cT, trace=tr)

@@ -1,0 +1,366 @@
+// C ABI of libkla: host-side argument checks, workspace sizing and dispatch.
+// Every check runs before anything is enqueued, so a call that fails one
+// writes nothing. No exception leaves this file.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kla_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kla_status_t fail(kla_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kla_status_t ok() {
+  g_last_error.clear();
+  return KLA_OK;
+}
+
+kla_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64; }
+bool dtype_ok(kla_dtype_t t) { return t == KLA_F32 || t == KLA_BF16; }
+
+// Grid dimensions y/z are limited to 65535 on this target.
+constexpr int kMaxHeads = 65535;
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+kla_status_t check_shape(const kla_shape_t* shp, const char* fn) {
+  if (!shp) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: shape is NULL", fn);
+  if (shp->B < 1 || shp->H < 1 || shp->T < 1)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: B, H, T must be >= 1 (got %d, %d, %d)", fn, shp->B,
+                shp->H, shp->T);
+  if (shp->d_qk < 1 || shp->d_v < 1)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: d_qk, d_v must be >= 1", fn);
+  if (!dim_ok(shp->d_qk) || !dim_ok(shp->d_v))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: d_qk, d_v must be 16, 32 or 64 (got %d, %d)", fn,
+                shp->d_qk, shp->d_v);
+  if (!dtype_ok(shp->in_dtype) || !dtype_ok(shp->out_dtype))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (!std::isfinite(shp->eps) || shp->eps < 0.0f)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  const long long N = (long long)shp->B * shp->H;
+  if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: B*H = %lld exceeds %d", fn, N, kMaxHeads);
+  if ((long long)shp->T * 256 > 0x7FFFFFFFLL)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: T = %d too large", fn, shp->T);
+  return KLA_OK;
+}
+
+kla_status_t check_ws(size_t need, const void* ws, size_t ws_bytes, const char* fn) {
+  if (need == 0) return KLA_OK;
+  if (!ws) return fail(KLA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, ws is NULL", fn, need);
+  if (ws_bytes < need)
+    return fail(KLA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  return KLA_OK;
+}
+
+kla::PrefillArgs make_prefill(const kla_shape_t* shp, int chunk) {
+  kla::PrefillArgs a{};
+  a.N = shp->B * shp->H;
+  a.T = shp->T;
+  a.dqk = shp->d_qk;
+  a.dv = shp->d_v;
+  a.chunk = chunk;
+  a.in_bf16 = shp->in_dtype == KLA_BF16;
+  a.out_bf16 = shp->out_dtype == KLA_BF16;
+  a.eps = shp->eps;
+  return a;
+}
+
+size_t prefill_ws(const kla::PrefillArgs& a) {
+  if (kla::prefill_mfma_supported(a)) return kla::prefill_mfma_workspace(a);
+  return kla::prefill_valu_workspace(a);
+}
+
+kla_status_t check_sre(int N, int dqk, int dv, const kla_sre_args_t* sre, const char* fn) {
+  if (!sre) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: sre arguments are NULL", fn);
+  if (sre->n_cand < 1 || sre->top_k < 1 || sre->top_k > sre->n_cand)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: need 1 <= top_k <= n_cand (got %d, %d)", fn,
+                sre->top_k, sre->n_cand);
+  if (sre->n_cand > 256)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: n_cand = %d exceeds 256", fn, sre->n_cand);
+  if (!sre->cand_k || !sre->cand_v || !sre->sel)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cand_k, cand_v and sel are required", fn);
+  if ((sre->sel_k == nullptr) != (sre->sel_v == nullptr))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: give both sel_k and sel_v or neither", fn);
+  const size_t nck = (size_t)N * sre->n_cand * dqk * sizeof(float);
+  const size_t ncv = (size_t)N * sre->n_cand * dv * sizeof(float);
+  const size_t nsk = (size_t)N * sre->top_k * dqk * sizeof(float);
+  const size_t nsv = (size_t)N * sre->top_k * dv * sizeof(float);
+  if (overlaps(sre->sel_k, nsk, sre->cand_k, nck) || overlaps(sre->sel_k, nsk, sre->cand_v, ncv) ||
+      overlaps(sre->sel_v, nsv, sre->cand_k, nck) || overlaps(sre->sel_v, nsv, sre->cand_v, ncv))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: sel_k / sel_v overlap the candidates", fn);
+  return KLA_OK;
+}
+
+kla::SreArgs make_sre(const kla_sre_args_t* s) {
+  kla::SreArgs a{};
+  a.n_cand = s->n_cand;
+  a.top_k = s->top_k;
+  a.cand_k = s->cand_k;
+  a.cand_v = s->cand_v;
+  a.scores = s->scores;
+  a.sel = s->sel;
+  a.sel_k = s->sel_k;
+  a.sel_v = s->sel_v;
+  return a;
+}
+
+kla_status_t check_hybrid(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg, const char* fn) {
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  if (!cfg) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cfg is NULL", fn);
+  if (cfg->refresh < 1 || cfg->window < 0 || cfg->cache_size < 0)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: need refresh >= 1, window >= 0, cache_size >= 0", fn);
+  if (!std::isfinite(cfg->softmax_scale))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite", fn);
+  if (cfg->refresh > 128 || cfg->cache_size + cfg->refresh > 256)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: need refresh <= 128 and cache_size + refresh <= 256", fn);
+  return KLA_OK;
+}
+
+kla::HybridArgs make_hybrid(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg) {
+  kla::HybridArgs a{};
+  a.N = shp->B * shp->H;
+  a.T = shp->T;
+  a.dqk = shp->d_qk;
+  a.dv = shp->d_v;
+  a.in_bf16 = shp->in_dtype == KLA_BF16;
+  a.out_bf16 = shp->out_dtype == KLA_BF16;
+  a.eps = shp->eps;
+  a.window = cfg->window;
+  a.cache_size = cfg->cache_size;
+  a.refresh = cfg->refresh;
+  a.scale = cfg->softmax_scale;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kla_abi_version(void) { return KLA_ABI_VERSION; }
+
+int kla_phi_dim(int d_qk) { return d_qk < 1 ? -1 : d_qk * (d_qk + 1) / 2; }
+
+const char* kla_status_string(kla_status_t s) {
+  switch (s) {
+    case KLA_OK: return "ok";
+    case KLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KLA_ERR_UNSUPPORTED: return "unsupported";
+    case KLA_ERR_WORKSPACE: return "workspace too small";
+    case KLA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* kla_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------- prefill
+
+kla_status_t kla_prefill_workspace_size(const kla_shape_t* shp, int chunk, int with_output,
+                                        size_t* bytes) {
+  const char* fn = "kla_prefill_workspace_size";
+  if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  if (chunk != 32 && chunk != 64 && chunk != 128)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: chunk must be 32, 64 or 128 (got %d)", fn, chunk);
+  kla::PrefillArgs a = make_prefill(shp, chunk);
+  a.o = with_output ? reinterpret_cast<void*>(1) : nullptr;
+  *bytes = prefill_ws(a);
+  return ok();
+}
+
+kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const void* k,
+                         const void* v, void* o, const float* H0, const float* s0, float* H_T,
+                         float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
+  const char* fn = "kla_prefill";
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  if (chunk != 32 && chunk != 64 && chunk != 128)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: chunk must be 32, 64 or 128 (got %d)", fn, chunk);
+  if (!q || !k || !v) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v are required", fn);
+  if ((H0 == nullptr) != (s0 == nullptr))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: give both H0 and s0 or neither", fn);
+  if ((H_T == nullptr) != (s_T == nullptr))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: give both H_T and s_T or neither", fn);
+  if (!o && !H_T)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: o may be NULL only when H_T and s_T are given", fn);
+  kla::PrefillArgs a = make_prefill(shp, chunk);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.H0 = H0;
+  a.s0 = s0;
+  a.HT = H_T;
+  a.sT = s_T;
+  const size_t need = prefill_ws(a);
+  st = check_ws(need, ws, ws_bytes, fn);
+  if (st != KLA_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (kla::prefill_mfma_supported(a)) return hip_status(kla::prefill_mfma_launch(a, ws, hs), fn);
+  return hip_status(kla::prefill_valu_launch(a, ws, hs), fn);
+}
+
+// ---------------------------------------------------------------- decode / SRE
+
+kla_status_t kla_decode_workspace_size(int N, int d_qk, int d_v, const kla_sre_args_t* sre,
+                                       size_t* bytes) {
+  const char* fn = "kla_decode_workspace_size";
+  if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (!dim_ok(d_qk) || !dim_ok(d_v))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: d_qk, d_v must be 16, 32 or 64", fn);
+  kla::DecodeArgs a{};
+  a.N = N;
+  a.dqk = d_qk;
+  a.dv = d_v;
+  kla::SreArgs s{};
+  if (sre) {
+    if (sre->n_cand < 1 || sre->n_cand > 256)
+      return fail(KLA_ERR_UNSUPPORTED, "%s: n_cand must be in [1, 256]", fn);
+    s = make_sre(sre);
+  }
+  *bytes = kla::decode_workspace(a, sre ? &s : nullptr);
+  return ok();
+}
+
+kla_status_t kla_decode_step(int N, int d_qk, int d_v, float eps, float* H, float* s,
+                             const void* q, const void* k, const void* v, kla_dtype_t in_dtype,
+                             void* o, kla_dtype_t out_dtype, const kla_sre_args_t* sre, void* ws,
+                             size_t ws_bytes, kla_stream_t stream) {
+  const char* fn = "kla_decode_step";
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (!dim_ok(d_qk) || !dim_ok(d_v))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: d_qk, d_v must be 16, 32 or 64 (got %d, %d)", fn, d_qk, d_v);
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (!std::isfinite(eps) || eps < 0.0f)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  if (!H || !s || !q || !k || !v || !o)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: H, s, q, k, v, o are required", fn);
+  if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
+  kla_status_t st = KLA_OK;
+  kla::SreArgs sa{};
+  if (sre) {
+    st = check_sre(N, d_qk, d_v, sre, fn);
+    if (st != KLA_OK) return st;
+    sa = make_sre(sre);
+  }
+  kla::DecodeArgs a{};
+  a.N = N;
+  a.dqk = d_qk;
+  a.dv = d_v;
+  a.eps = eps;
+  a.H = H;
+  a.s = s;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.in_bf16 = in_dtype == KLA_BF16;
+  a.o = o;
+  a.out_bf16 = out_dtype == KLA_BF16;
+  st = check_ws(kla::decode_workspace(a, sre ? &sa : nullptr), ws, ws_bytes, fn);
+  if (st != KLA_OK) return st;
+  return hip_status(kla::decode_launch(a, sre ? &sa : nullptr, ws, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+kla_status_t kla_sre_workspace_size(int N, int d_qk, int d_v, const kla_sre_args_t* sre,
+                                    size_t* bytes) {
+  const char* fn = "kla_sre_workspace_size";
+  if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (!dim_ok(d_qk) || !dim_ok(d_v))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: d_qk, d_v must be 16, 32 or 64", fn);
+  if (!sre) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: sre arguments are NULL", fn);
+  if (sre->n_cand < 1 || sre->n_cand > 256)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: n_cand must be in [1, 256]", fn);
+  *bytes = kla::sre_workspace(N, d_qk, d_v, make_sre(sre));
+  return ok();
+}
+
+kla_status_t kla_sre_select(int N, int d_qk, int d_v, float eps, const float* H, const float* s,
+                            const kla_sre_args_t* sre, void* ws, size_t ws_bytes,
+                            kla_stream_t stream) {
+  const char* fn = "kla_sre_select";
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (!dim_ok(d_qk) || !dim_ok(d_v))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: d_qk, d_v must be 16, 32 or 64 (got %d, %d)", fn, d_qk, d_v);
+  if (!std::isfinite(eps) || eps < 0.0f)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  if (!H || !s) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: H and s are required", fn);
+  if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
+  kla_status_t st = check_sre(N, d_qk, d_v, sre, fn);
+  if (st != KLA_OK) return st;
+  const kla::SreArgs sa = make_sre(sre);
+  st = check_ws(kla::sre_workspace(N, d_qk, d_v, sa), ws, ws_bytes, fn);
+  if (st != KLA_OK) return st;
+  return hip_status(kla::sre_launch(N, d_qk, d_v, eps, H, s, sa, ws, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+// ---------------------------------------------------------------- hybrid
+
+kla_status_t kla_hybrid_workspace_size(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg,
+                                       size_t* bytes) {
+  const char* fn = "kla_hybrid_workspace_size";
+  if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  kla_status_t st = check_hybrid(shp, cfg, fn);
+  if (st != KLA_OK) return st;
+  *bytes = kla::hybrid_workspace(make_hybrid(shp, cfg));
+  return ok();
+}
+
+kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg,
+                                const void* q, const void* k, const void* v, void* o, float* H_T,
+                                float* s_T, int32_t* cache_tokens_T, int32_t* sel_trace,
+                                void* ws, size_t ws_bytes, kla_stream_t stream) {
+  const char* fn = "kla_hybrid_prefill";
+  kla_status_t st = check_hybrid(shp, cfg, fn);
+  if (st != KLA_OK) return st;
+  if (!q || !k || !v || !o) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o are required", fn);
+  if ((H_T == nullptr) != (s_T == nullptr))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: give both H_T and s_T or neither", fn);
+  kla::HybridArgs a = make_hybrid(shp, cfg);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.HT = H_T;
+  a.sT = s_T;
+  a.cache_T = cache_tokens_T;
+  a.trace = sel_trace;
+  // the workspace size depends on which state outputs the caller provides
+  st = check_ws(kla::hybrid_workspace(a), ws, ws_bytes, fn);
+  if (st != KLA_OK) return st;
+  return hip_status(kla::hybrid_launch(a, ws, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal host-side interface between the C ABI (kla_api.hip) and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kla.h"
+
+namespace kla {
+
+// Workspace carving: every region is 256-byte aligned.
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- prefill
+
+struct PrefillArgs {
+  int N, T, dqk, dv, chunk;
+  bool in_bf16, out_bf16;
+  float eps;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;  // NULL = state only
+  const float* H0;
+  const float* s0;
+  float* HT;
+  float* sT;
+};
+
+// Generic float32-arithmetic path (VALU): any supported shape, either dtype.
+size_t prefill_valu_workspace(const PrefillArgs& a);
+hipError_t prefill_valu_launch(const PrefillArgs& a, void* ws, hipStream_t st);
+
+// bf16 matrix-core path for d_qk = d_v = 64; returns false from *_supported
+// when the shape is outside what it handles.
+bool prefill_mfma_supported(const PrefillArgs& a);
+size_t prefill_mfma_workspace(const PrefillArgs& a);
+hipError_t prefill_mfma_launch(const PrefillArgs& a, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- decode / SRE
+
+struct SreArgs {
+  int n_cand, top_k;
+  const float* cand_k;
+  const float* cand_v;
+  float* scores;
+  int32_t* sel;
+  float* sel_k;
+  float* sel_v;
+};
+
+struct DecodeArgs {
+  int N, dqk, dv;
+  float eps;
+  float* H;
+  float* s;
+  const void* q;
+  const void* k;
+  const void* v;
+  bool in_bf16;
+  void* o;
+  bool out_bf16;
+};
+
+size_t decode_workspace(const DecodeArgs& a, const SreArgs* sre);
+hipError_t decode_launch(const DecodeArgs& a, const SreArgs* sre, void* ws, hipStream_t st);
+
+size_t sre_workspace(int N, int dqk, int dv, const SreArgs& s);
+hipError_t sre_launch(int N, int dqk, int dv, float eps, const float* H, const float* s,
+                      const SreArgs& sre, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- hybrid
+
+struct HybridArgs {
+  int N, T, dqk, dv;
+  bool in_bf16, out_bf16;
+  float eps;
+  int window, cache_size, refresh;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* HT;
+  float* sT;
+  int32_t* cache_T;
+  int32_t* trace;
+};
+
+size_t hybrid_workspace(const HybridArgs& a);
+hipError_t hybrid_launch(const HybridArgs& a, void* ws, hipStream_t st);
+
+}  // namespace kla

@@ -175,7 +175,8 @@ def decode_case(N: int, d: int = 64, T0: int = 2048, steps: int = 128, top_k: in
     """Generate the decode workload for head-states ``ids`` (default 0..N-1).
 
     Draw order per head-state n, from default_rng([seed, n]): prefix k, prefix
-    v, cache0 k, cache0 v, then for the steps q, k, v, fresh k, fresh v.
+    v, cache0 k, cache0 v, then one row per step holding q, k, v, fresh k and
+    fresh v, so a run of S steps is a prefix of any longer run.
     """
     ids = tuple(range(N)) if ids is None else tuple(int(i) for i in ids)
     n = len(ids)
@@ -196,11 +197,15 @@ def decode_case(N: int, d: int = 64, T0: int = 2048, steps: int = 128, top_k: in
         pv[i] = gaussian(rng, (T0, d))
         ck[i] = gaussian(rng, (top_k, d), s)
         cv[i] = gaussian(rng, (top_k, d))
-        q[:, i] = gaussian(rng, (steps, d), s)
-        k[:, i] = gaussian(rng, (steps, d), s)
-        v[:, i] = gaussian(rng, (steps, d))
-        fk[:, i] = gaussian(rng, (steps, n_fresh, d), s)
-        fv[:, i] = gaussian(rng, (steps, n_fresh, d))
+        # one row per step: [q | k | v | fresh k | fresh v]; the stream is
+        # sequential, so the first S rows do not depend on ``steps``
+        rows = gaussian(rng, (steps, (3 + 2 * n_fresh) * d))
+        sc = np.float32(s)
+        q[:, i] = rows[:, 0:d] * sc
+        k[:, i] = rows[:, d:2 * d] * sc
+        v[:, i] = rows[:, 2 * d:3 * d]
+        fk[:, i] = rows[:, 3 * d:(3 + n_fresh) * d].reshape(steps, n_fresh, d) * sc
+        fv[:, i] = rows[:, (3 + n_fresh) * d:].reshape(steps, n_fresh, d)
 
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(work, range(n)))

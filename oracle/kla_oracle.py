@@ -413,6 +413,7 @@ def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, scale: f
                 trace[b] = sorted(keep_set)
                 nref += 1
         cidx = np.array(cache, dtype=int)
+        fQ = phi(q[b0:b1])
         for t in range(b0, b1):
             w_win = np.exp(scale * (k[f:t + 1] @ q[t]))
             num = w_win @ v[f:t + 1]
@@ -421,7 +422,7 @@ def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, scale: f
                 w_c = np.exp(scale * (k[cidx] @ q[t]))
                 num = num + w_c @ v[cidx]
                 den = den + w_c.sum()
-            fq = phi(q[t])
+            fq = fQ[t - b0]
             num = num + fq @ H
             den = den + fq @ s + eps
             o[t] = num / den if den != 0 else 0.0
