@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of causal kernelized linear attention (rank-one PSD lift) on one
+MI355X, with the dominant kernel's roofline fraction and the float64 CPU
+oracle timed beside it.
+
+Main line: bf16 prefill of 4 x 8 heads x 4096 tokens, d = 64 (D = 2080),
+chunk 64 — one step is one kla_prefill call (lift, intra-chunk term,
+cross-chunk state readout and update, combine). Secondary lines (in
+"secondary"): the 16-head x 65536-token long-context prefill, the decode +
+self-recall selection loop (4096 head-states, 128 steps) and the hybrid
+prefill (2 x 16 x 16384). Inputs are seeded synthetic tensors resident in HBM
+before timing.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def phi_dim(d):
+    return d * (d + 1) // 2
+
+
+def timed_calls(torch, K, fn, steps, warmup):
+    """Wall time per call (sync on both sides) and the library's own kernel
+    timing of the dominant kernel (HIP events on the call's stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    K.profile_read()
+    K.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    K.profile_enable(False)
+    kms, nk, dropped = K.profile_read()
+    return (t1 - t0) * 1e3 / steps, (kms / nk if nk else float("nan")), nk / steps
+
+
+def bench_prefill(torch, K, S, name, steps, warmup):
+    cfg = S.CONFIGS[name]
+    c = S.prefill_case(name, cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
+                       cfg["seed"])
+    q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (c.q, c.k, c.v))
+    del c
+    o = torch.empty_like(v)
+    step_ms, kern_ms, per_step = timed_calls(torch, K, lambda: K.prefill(q, k, v, chunk=cfg["chunk"], out=o),
+                                             steps, warmup)
+    B, H, T, d, dv = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
+    D = phi_dim(d)
+    head_tokens = B * H * T
+    # dominant kernel: cross-chunk readout phi(Q)[H|s] and update phi(K)^T[V|1]
+    kern_flops = 4.0 * D * (dv + 1) * head_tokens
+    # whole call: plus the causal intra-chunk term
+    C = cfg["chunk"]
+    call_flops = kern_flops + (C + 1) * (d + dv + 1) * head_tokens
+    mfma = K.prefill_uses_matrix_cores()
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_F32_VALU_TFLOPS
+    achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+    return dict(
+        workload=name, B=B, H=H, T=T, d_qk=d, d_v=dv, chunk=C, step_ms=step_ms,
+        tokens_per_s=B * T / (step_ms * 1e-3), head_tokens_per_s=head_tokens / (step_ms * 1e-3),
+        call_tflops=call_flops / (step_ms * 1e-3) / 1e12,
+        roofline=dict(bound="mfma" if mfma else "alu", achieved=achieved, peak=peak, unit="TFLOP/s",
+                      frac=achieved / peak, traffic=None, kernel_ms=kern_ms,
+                      kernel="prefill state/readout", flops_per_launch=kern_flops),
+        arith="bf16" if mfma else "f32",
+    )
+
+
+def bench_decode(torch, K, S, steps_loop, reps):
+    cfg = S.CONFIGS["decode_sre_4096x128"]
+    N, d, T0, top, nf = cfg["N"], cfg["d"], cfg["T0"], cfg["top_k"], cfg["n_fresh"]
+    nsteps = cfg["steps"] if steps_loop is None else steps_loop
+    t = time.time()
+    case = S.decode_case(N, d=d, T0=T0, steps=nsteps, top_k=top, n_fresh=nf, seed=cfg["seed"],
+                         threads=16)
+    log(f"[bench] decode inputs generated in {time.time() - t:.1f}s")
+    dev = "cuda"
+    pk = torch.from_numpy(case.prefix_k).to(dev)[None]
+    pv = torch.from_numpy(case.prefix_v).to(dev)[None]
+    H, s = K.prefill(pk, pk, pv, chunk=64, outputs=False)
+    H, s = H[0].contiguous(), s[0].contiguous()
+    del pk, pv
+    n_cand = top + nf
+    # candidate slabs per step: rows [0, top) = cache gathered by the previous step
+    ck = torch.empty((nsteps + 1, N, n_cand, d), device=dev)
+    cv = torch.empty((nsteps + 1, N, n_cand, d), device=dev)
+    ck[0, :, :top] = torch.from_numpy(case.cache0_k).to(dev)
+    cv[0, :, :top] = torch.from_numpy(case.cache0_v).to(dev)
+    for i in range(nsteps):
+        ck[i, :, top:] = torch.from_numpy(case.fresh_k[i]).to(dev)
+        cv[i, :, top:] = torch.from_numpy(case.fresh_v[i]).to(dev)
+    q = torch.from_numpy(case.q).to(dev)
+    k = torch.from_numpy(case.k).to(dev)
+    v = torch.from_numpy(case.v).to(dev)
+    del case
+    o = torch.empty((N, d), device=dev)
+    sc = torch.empty((N, n_cand), device=dev)
+    sel = torch.empty((N, top), dtype=torch.int32, device=dev)
+
+    def loop():
+        for i in range(nsteps):
+            K.decode_step(H, s, q[i], k[i], v[i], cand_k=ck[i], cand_v=cv[i], top_k=top, gather=True,
+                          out=dict(o=o, scores=sc, sel=sel, sel_k=ck[i + 1], sel_v=cv[i + 1],
+                                   sel_stride=n_cand))
+
+    loop_ms, kern_ms, per_loop = timed_calls(torch, K, loop, reps, 1)
+    D = phi_dim(d)
+    state_bytes = N * (2 * D * d * 4 + 2 * D * 4 + 4 * d * 4)  # H, s read+write; q, k, v, o
+    achieved = state_bytes / (kern_ms * 1e-3) / 1e9
+    step_ms = loop_ms / nsteps
+    return dict(
+        workload="decode_sre_4096x128", N=N, steps=nsteps, step_ms=step_ms,
+        steps_per_s=1e3 / step_ms, decode_kernel_ms=kern_ms,
+        roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=achieved / PEAK_HBM_GBS, traffic=None, kernel="decode state stream",
+                      bytes_per_launch=state_bytes),
+    )
+
+
+def bench_hybrid(torch, K, S, steps, warmup):
+    cfg = S.CONFIGS["hybrid_2x16x16384"]
+    c = S.hybrid_case("bench", cfg["B"], cfg["H"], cfg["T"], cfg["d"], cfg["window"],
+                      cfg["cache_size"], cfg["refresh"], cfg["seed"], threads=16)
+    q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (c.q, c.k, c.v))
+    fn = lambda: K.hybrid_prefill(q, k, v, cfg["window"], cfg["cache_size"], cfg["refresh"])
+    step_ms, kern_ms, per_call = timed_calls(torch, K, fn, steps, warmup)
+    B, T = cfg["B"], cfg["T"]
+    return dict(workload="hybrid_2x16x16384", step_ms=step_ms, tokens_per_s=B * T / (step_ms * 1e-3),
+                score_kernel_ms_per_call=kern_ms * per_call)
+
+
+def cpu_baseline(S, name, budget_s):
+    """The oracle (float64, NumPy) on a bounded sample of the workload's heads."""
+    import numpy as np
+
+    import oracle as O
+    cfg = S.CONFIGS[name]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    done = 0
+    elapsed = 0.0
+    for (b, h) in heads:
+        c = S.prefill_case(name, B, H, T, cfg["d_qk"], cfg["d_v"], cfg["chunk"], cfg["seed"],
+                           heads=[(b, h)])
+        t = time.perf_counter()
+        O.prefill_chunked(c.q[0, 0], c.k[0, 0], c.v[0, 0], chunk=256)
+        elapsed += time.perf_counter() - t
+        done += 1
+        if elapsed >= budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    tokens = done * T / H  # tokens = B*T over all heads; one head-token is 1/H of a token
+    return dict(value=tokens / elapsed, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{done} of {B * H} heads x {T} tokens, float64 chunked form, "
+                       f"{elapsed:.1f}s of CPU time")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true", help="main prefill line only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); every head "
+              f"is independent, so a multi-GPU run would shard heads with no exchange and is not "
+              f"measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kernelized_linear_attention_02_amd as K
+    from kernelized_linear_attention_02_amd import synth as S
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    K.load_library()
+
+    name = "prefill_4x8x4096"
+    log("[bench] main: prefill_4x8x4096")
+    main_r = bench_prefill(torch, K, S, name, args.steps, args.warmup)
+    log(f"[bench] main done: {main_r['step_ms']:.3f} ms/step")
+    secondary = []
+    if not args.no_secondary:
+        log("[bench] secondary: prefill_1x16x65536")
+        secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1))
+        log("[bench] secondary: decode_sre_4096x128")
+        secondary.append(bench_decode(torch, K, S, args.decode_steps, 2))
+        torch.cuda.empty_cache()
+        log("[bench] secondary: hybrid_2x16x16384")
+        secondary.append(bench_hybrid(torch, K, S, 3, 1))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(S, name, args.cpu_seconds)
+
+    cfg = S.CONFIGS[name]
+    line = {
+        "metric": "prefill tokens/sec and % bf16 MFMA peak; decode steps/sec and % HBM peak",
+        "value": main_r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_r["arith"],
+        "data": "synthetic",
+        "config": {"workload": name, "B": cfg["B"], "H": cfg["H"], "T": cfg["T"],
+                   "d_qk": cfg["d_qk"], "d_v": cfg["d_v"], "chunk": cfg["chunk"],
+                   "inputs": "bf16, q/k rows L2-normalised Gaussian, v ~ N(0,1)",
+                   "parallelism": "single GPU"},
+        "roofline": main_r["roofline"],
+        "cpu_baseline": cpu,
+        "head_tokens_per_s": main_r["head_tokens_per_s"],
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

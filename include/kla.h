@@ -112,6 +112,10 @@ typedef struct {
  *   ws      : workspace of at least kla_prefill_workspace_size() bytes
  *             (may be NULL when that size is 0).
  * ------------------------------------------------------------------------ */
+/* 1 when kla_prefill serves this shape with the bf16 matrix-core kernel,
+ * 0 when it uses the float32 vector-ALU kernel, -1 for an invalid shape. */
+KLA_API int kla_prefill_matrix_path(const kla_shape_t* shp, int chunk);
+
 KLA_API kla_status_t kla_prefill_workspace_size(const kla_shape_t* shp, int chunk, int with_output,
                                         size_t* bytes);
 KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const void* k,
@@ -130,10 +134,13 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
  *   cand_k : [N, n_cand, d_qk] float32;  cand_v : [N, n_cand, d_v] float32.
  *   scores : [N, n_cand] float32 output, or NULL.
  *   sel    : [N, top_k] int32 output (required).
- *   sel_k, sel_v : optional gather of the selected pairs, [N, top_k, d_qk]
- *            and [N, top_k, d_v] float32, both or neither; must not overlap
- *            cand_k / cand_v.
- * Supported: 1 <= top_k <= n_cand <= 256.
+ *   sel_k, sel_v : optional gather of the selected pairs, both or neither:
+ *            head n's j-th selected pair goes to row n * sel_stride + j of
+ *            sel_k ([., d_qk]) and sel_v ([., d_v]), float32. sel_stride = 0
+ *            means top_k (dense [N, top_k, d]); a larger stride lets the gather
+ *            fill the first top_k rows of a following call's candidate array.
+ *            The gathered rows must not overlap cand_k / cand_v.
+ * Supported: 1 <= top_k <= n_cand <= 256; sel_stride = 0 or >= top_k.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int n_cand, top_k;
@@ -143,6 +150,7 @@ typedef struct {
   int32_t* sel;
   float* sel_k;
   float* sel_v;
+  int sel_stride;
 } kla_sre_args_t;
 
 /* ------------------------------------------------------------------------
@@ -210,6 +218,20 @@ KLA_API kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid
                                 const void* q, const void* k, const void* v, void* o, float* H_T,
                                 float* s_T, int32_t* cache_tokens_T, int32_t* sel_trace,
                                 void* ws, size_t ws_bytes, kla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing without a profiler. While enabled on the calling thread,
+ * every call records a pair of HIP events on its stream around its dominant
+ * kernel: the state/readout kernel of kla_prefill, the state-streaming
+ * kernel of kla_decode_step, the scoring kernel of kla_sre_select, and each
+ * scoring kernel of kla_hybrid_prefill. kla_profile_read waits for the last
+ * recorded event, returns the summed elapsed milliseconds and the number of
+ * recorded kernels, and clears the record. Events come from a pool owned by
+ * the thread; up to 65536 pairs are kept per read (later ones are counted in
+ * `dropped`).
+ * ------------------------------------------------------------------------ */
+KLA_API kla_status_t kla_profile_enable(int on);
+KLA_API kla_status_t kla_profile_read(double* total_ms, int* kernels, int* dropped);
 
 #ifdef __cplusplus
 }

@@ -20,8 +20,11 @@ from ._binding import (  # noqa: F401
     load_library,
     phi_dim,
     prefill,
+    prefill_uses_matrix_cores,
+    profile_enable,
+    profile_read,
     sre_select,
 )
 
 __all__ = ["prefill", "decode_step", "sre_select", "hybrid_prefill", "phi_dim", "load_library",
-           "KlaError", "EXPORTS", "LIB_PATH"]
+           "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

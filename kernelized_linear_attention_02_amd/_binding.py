@@ -20,10 +20,11 @@ KLA_F32, KLA_BF16 = 0, 1
 
 EXPORTS = (
     "kla_abi_version", "kla_phi_dim", "kla_status_string", "kla_last_error",
-    "kla_prefill_workspace_size", "kla_prefill",
+    "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill",
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill",
+    "kla_profile_enable", "kla_profile_read",
 )
 
 
@@ -43,7 +44,8 @@ class SreArgs(ctypes.Structure):
     _fields_ = [("n_cand", ctypes.c_int), ("top_k", ctypes.c_int),
                 ("cand_k", ctypes.c_void_p), ("cand_v", ctypes.c_void_p),
                 ("scores", ctypes.c_void_p), ("sel", ctypes.c_void_p),
-                ("sel_k", ctypes.c_void_p), ("sel_v", ctypes.c_void_p)]
+                ("sel_k", ctypes.c_void_p), ("sel_v", ctypes.c_void_p),
+                ("sel_stride", ctypes.c_int)]
 
 
 class HybridCfg(ctypes.Structure):
@@ -73,6 +75,7 @@ def load_library(path: str = LIB_PATH):
         "kla_phi_dim": (i, [i]),
         "kla_status_string": (ctypes.c_char_p, [i]),
         "kla_last_error": (ctypes.c_char_p, []),
+        "kla_prefill_matrix_path": (i, [shp, i]),
         "kla_prefill_workspace_size": (i, [shp, i, i, szp]),
         "kla_prefill": (i, [shp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
@@ -81,6 +84,9 @@ def load_library(path: str = LIB_PATH):
         "kla_sre_select": (i, [i, i, i, f, vp, vp, srp, vp, sz, vp]),
         "kla_hybrid_workspace_size": (i, [shp, hcp, szp]),
         "kla_hybrid_prefill": (i, [shp, hcp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kla_profile_enable": (i, [i]),
+        "kla_profile_read": (i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
+                                 ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -144,8 +150,14 @@ def phi_dim(d: int) -> int:
     return load_library().kla_phi_dim(int(d))
 
 
+def prefill_uses_matrix_cores(B=4, H=8, T=4096, d_qk=64, d_v=64, chunk=64, dtype=KLA_BF16) -> bool:
+    """Whether kla_prefill runs the bf16 matrix-core kernel for this shape."""
+    shp = Shape(B, H, T, d_qk, d_v, dtype, dtype, 0.0)
+    return load_library().kla_prefill_matrix_path(ctypes.byref(shp), int(chunk)) == 1
+
+
 def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, eps: float = 0.0,
-            out_dtype=None, outputs: bool = True):
+            out_dtype=None, outputs: bool = True, out=None):
     """Chunked causal prefill. q, k [B, H, T, d_qk]; v [B, H, T, d_v] (float32 or
     bfloat16, same dtype). ``state`` = (H0, s0) float32 resumes a previous call.
     Returns o, or (o, H_T, s_T) with ``return_state``; with ``outputs=False``
@@ -165,7 +177,12 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     shp = Shape(B, Hh, T, dqk, dv, code, ocode, float(eps))
     D = phi_dim(dqk)
     dev = q.device
-    o = torch.empty((B, Hh, T, dv), dtype=_torch_dtype(ocode), device=dev) if outputs else None
+    if outputs and out is not None:
+        if out.shape != (B, Hh, T, dv) or out.dtype != _torch_dtype(ocode) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B, H, T, d_v] tensor of the output dtype")
+        o = out
+    else:
+        o = torch.empty((B, Hh, T, dv), dtype=_torch_dtype(ocode), device=dev) if outputs else None
     want_state = return_state or not outputs
     HT = torch.empty((B, Hh, D, dv), dtype=torch.float32, device=dev) if want_state else None
     sT = torch.empty((B, Hh, D), dtype=torch.float32, device=dev) if want_state else None
@@ -188,11 +205,11 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     return (o, HT, sT) if return_state else o
 
 
-def _sre_struct(cand_k, cand_v, top_k, scores, sel, sel_k, sel_v):
+def _sre_struct(cand_k, cand_v, top_k, scores, sel, sel_k, sel_v, sel_stride=0):
     return SreArgs(int(cand_k.shape[-2]), int(top_k), cand_k.data_ptr(), cand_v.data_ptr(),
                    None if scores is None else scores.data_ptr(), sel.data_ptr(),
                    None if sel_k is None else sel_k.data_ptr(),
-                   None if sel_v is None else sel_v.data_ptr())
+                   None if sel_v is None else sel_v.data_ptr(), int(sel_stride))
 
 
 def _sre_outputs(N, n_cand, top_k, dqk, dv, device, scores, gather, out=None):
@@ -212,7 +229,9 @@ def decode_step(H, s, q, k, v, eps: float = 0.0, out_dtype=None, cand_k=None, ca
     updated in place; q, k [N, d_qk], v [N, d_v]. With candidates
     (cand_k [N, n_cand, d_qk], cand_v [N, n_cand, d_v] float32) and top_k,
     also scores and selects against the updated state. ``out`` may pass
-    preallocated {'o', 'scores', 'sel', 'sel_k', 'sel_v'} tensors.
+    preallocated {'o', 'scores', 'sel', 'sel_k', 'sel_v'} tensors, and
+    'sel_stride' when sel_k / sel_v point into a slab with that many rows per
+    head (for instance the next step's candidate array).
     Returns o, or (o, dict(scores, sel, sel_k, sel_v))."""
     torch = _torch()
     lib = load_library()
@@ -232,7 +251,11 @@ def decode_step(H, s, q, k, v, eps: float = 0.0, out_dtype=None, cand_k=None, ca
     if cand_k is not None:
         cand_k, cand_v = cand_k.contiguous(), cand_v.contiguous()
         sc, sel, sk, sv = _sre_outputs(N, cand_k.shape[1], top_k, dqk, dv, dev, scores, gather, out)
-        sre = _sre_struct(cand_k, cand_v, top_k, sc, sel, sk, sv)
+        stride = 0
+        if sk is not None and out is not None and "sel_stride" in out:
+            # gathered rows land in a caller slab with `sel_stride` rows per head
+            stride = int(out["sel_stride"])
+        sre = _sre_struct(cand_k, cand_v, top_k, sc, sel, sk, sv, stride)
         sre_p = ctypes.byref(sre)
         res = dict(scores=sc, sel=sel, sel_k=sk, sel_v=sv)
     nbytes = ctypes.c_size_t(0)
@@ -301,3 +324,17 @@ def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, softmax_
     if not (return_state or return_cache or return_trace):
         return o
     return o, dict(H=HT, s=sT, cache=cT, trace=tr)
+
+
+def profile_enable(on: bool = True):
+    """Record HIP events around each call's dominant kernel on this thread."""
+    check(load_library().kla_profile_enable(int(bool(on))))
+
+
+def profile_read():
+    """(summed kernel milliseconds, kernels recorded, dropped) since the last read."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int(0)
+    dr = ctypes.c_int(0)
+    check(load_library().kla_profile_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(dr)))
+    return ms.value, n.value, dr.value

@@ -119,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
                                                         const float* __restrict__ ck,
                                                         const float* __restrict__ cv,
                                                         float* __restrict__ sel_k,
-                                                        float* __restrict__ sel_v, int dqk,
-                                                        int dv) {
+                                                        float* __restrict__ sel_v,
+                                                        int sel_stride, int dqk, int dv) {
   __shared__ uint64_t keys[256];
   const int n = blockIdx.x;
   for (int i = threadIdx.x; i < npow2; i += blockDim.x)
@@ -132,12 +132,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     for (int i = threadIdx.x; i < top_k * dqk; i += blockDim.x) {
       const int j = i / dqk, d = i % dqk;
       const uint32_t c = topk_index(keys[j]);
-      sel_k[((size_t)n * top_k + j) * dqk + d] = ck[((size_t)n * n_cand + c) * dqk + d];
+      sel_k[((size_t)n * sel_stride + j) * dqk + d] = ck[((size_t)n * n_cand + c) * dqk + d];
     }
     for (int i = threadIdx.x; i < top_k * dv; i += blockDim.x) {
       const int j = i / dv, d = i % dv;
       const uint32_t c = topk_index(keys[j]);
-      sel_v[((size_t)n * top_k + j) * dv + d] = cv[((size_t)n * n_cand + c) * dv + d];
+      sel_v[((size_t)n * sel_stride + j) * dv + d] = cv[((size_t)n * n_cand + c) * dv + d];
     }
   }
 }
@@ -150,9 +150,11 @@ int pow2_at_least(int x) {
 
 template <int DQK, int DV, typename Tin, typename Tout>
 hipError_t decode_typed(const DecodeArgs& a, hipStream_t st) {
+  prof_begin(st);
   hipLaunchKernelGGL((decode_kernel<DQK, DV, Tin, Tout>), dim3(a.N), dim3(kThreads), 0, st, a.H,
                      a.s, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), static_cast<Tout*>(a.o), a.eps);
+  prof_end(st);
   return hipGetLastError();
 }
 
@@ -185,15 +187,17 @@ hipError_t dispatch_dd(int dqk, int dv, F&& f) {
 }
 
 hipError_t score_and_select(int N, int dqk, int dv, float eps, const float* H, const float* s,
-                            const SreArgs& sre, void* ws, hipStream_t st) {
+                            const SreArgs& sre, void* ws, hipStream_t st, bool timed) {
   float* scores = sre.scores ? sre.scores : static_cast<float*>(ws);
+  if (timed) prof_begin(st);
   hipError_t e = dispatch_dd(dqk, dv, [&](auto A, auto B) {
     return sre_typed<decltype(A)::value, decltype(B)::value>(N, eps, H, s, sre, scores, st);
   });
+  if (timed) prof_end(st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_kernel, dim3(N), dim3(kThreads), 0, st, scores, sre.n_cand, sre.top_k,
                      pow2_at_least(sre.n_cand), sre.sel, sre.cand_k, sre.cand_v, sre.sel_k,
-                     sre.sel_v, dqk, dv);
+                     sre.sel_v, sre.sel_stride, dqk, dv);
   return hipGetLastError();
 }
 
@@ -205,7 +209,7 @@ size_t sre_workspace(int N, int, int, const SreArgs& s) {
 
 hipError_t sre_launch(int N, int dqk, int dv, float eps, const float* H, const float* s,
                       const SreArgs& sre, void* ws, hipStream_t st) {
-  return score_and_select(N, dqk, dv, eps, H, s, sre, ws, st);
+  return score_and_select(N, dqk, dv, eps, H, s, sre, ws, st, true);
 }
 
 size_t decode_workspace(const DecodeArgs& a, const SreArgs* sre) {
@@ -217,7 +221,7 @@ hipError_t decode_launch(const DecodeArgs& a, const SreArgs* sre, void* ws, hipS
     return decode_dt<decltype(A)::value, decltype(B)::value>(a, st);
   });
   if (e != hipSuccess || !sre) return e;
-  return score_and_select(a.N, a.dqk, a.dv, a.eps, a.H, a.s, *sre, ws, st);
+  return score_and_select(a.N, a.dqk, a.dv, a.eps, a.H, a.s, *sre, ws, st, false);
 }
 
 }  // namespace kla

@@ -387,9 +387,11 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
         KLA_CHECK();
         n_cache = n_cand;
       } else {
+        prof_begin(st);
         hipLaunchKernelGGL((hyb_score_kernel<DQK, DV, Tin>), dim3((n_cand + 63) / 64, N),
                            dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache,
                            f_prev, n_cand, w.scores, kCStride, a.eps);
+        prof_end(st);
         KLA_CHECK();
         hipLaunchKernelGGL(hyb_select_kernel, dim3(N), dim3(kThreads), 0, st, w.scores, kCStride,
                            w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,

@@ -5,6 +5,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "kla_internal.hpp"
 
@@ -105,8 +107,13 @@ kla_status_t check_sre(int N, int dqk, int dv, const kla_sre_args_t* sre, const 
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: give both sel_k and sel_v or neither", fn);
   const size_t nck = (size_t)N * sre->n_cand * dqk * sizeof(float);
   const size_t ncv = (size_t)N * sre->n_cand * dv * sizeof(float);
-  const size_t nsk = (size_t)N * sre->top_k * dqk * sizeof(float);
-  const size_t nsv = (size_t)N * sre->top_k * dv * sizeof(float);
+  if (sre->sel_stride != 0 && sre->sel_stride < sre->top_k)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: sel_stride must be 0 or >= top_k", fn);
+  const size_t stride = sre->sel_stride ? (size_t)sre->sel_stride : (size_t)sre->top_k;
+  // extent of the gathered rows (rows between heads are not written)
+  const size_t rows = (size_t)(N - 1) * stride + sre->top_k;
+  const size_t nsk = rows * dqk * sizeof(float);
+  const size_t nsv = rows * dv * sizeof(float);
   if (overlaps(sre->sel_k, nsk, sre->cand_k, nck) || overlaps(sre->sel_k, nsk, sre->cand_v, ncv) ||
       overlaps(sre->sel_v, nsv, sre->cand_k, nck) || overlaps(sre->sel_v, nsv, sre->cand_v, ncv))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: sel_k / sel_v overlap the candidates", fn);
@@ -123,6 +130,7 @@ kla::SreArgs make_sre(const kla_sre_args_t* s) {
   a.sel = s->sel;
   a.sel_k = s->sel_k;
   a.sel_v = s->sel_v;
+  a.sel_stride = s->sel_stride ? s->sel_stride : s->top_k;
   return a;
 }
 
@@ -155,9 +163,85 @@ kla::HybridArgs make_hybrid(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg)
   return a;
 }
 
+struct ProfState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  size_t used = 0;
+  int dropped = 0;
+  bool open = false;
+  ~ProfState() {
+    for (auto& e : pool) {
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+  }
+};
+thread_local ProfState g_prof;
+constexpr size_t kProfMax = 65536;
+
 }  // namespace
 
+namespace kla {
+
+void prof_begin(hipStream_t st) {
+  ProfState& p = g_prof;
+  if (!p.on) return;
+  if (p.used >= kProfMax) {
+    ++p.dropped;
+    return;
+  }
+  if (p.used == p.pool.size()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      ++p.dropped;
+      return;
+    }
+    p.pool.emplace_back(a, b);
+  }
+  (void)hipEventRecord(p.pool[p.used].first, st);
+  p.open = true;
+}
+
+void prof_end(hipStream_t st) {
+  ProfState& p = g_prof;
+  if (!p.on || !p.open) return;
+  (void)hipEventRecord(p.pool[p.used].second, st);
+  ++p.used;
+  p.open = false;
+}
+
+}  // namespace kla
+
 extern "C" {
+
+kla_status_t kla_profile_enable(int on) {
+  g_prof.on = on != 0;
+  g_prof.open = false;
+  return ok();
+}
+
+kla_status_t kla_profile_read(double* total_ms, int* kernels, int* dropped) {
+  const char* fn = "kla_profile_read";
+  if (!total_ms || !kernels) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: NULL output", fn);
+  ProfState& p = g_prof;
+  double sum = 0.0;
+  if (p.used > 0) {
+    hipError_t e = hipEventSynchronize(p.pool[p.used - 1].second);
+    if (e != hipSuccess) return hip_status(e, fn);
+    for (size_t i = 0; i < p.used; ++i) {
+      float ms = 0.0f;
+      e = hipEventElapsedTime(&ms, p.pool[i].first, p.pool[i].second);
+      if (e != hipSuccess) return hip_status(e, fn);
+      sum += ms;
+    }
+  }
+  *total_ms = sum;
+  *kernels = (int)p.used;
+  if (dropped) *dropped = p.dropped;
+  p.used = 0;
+  p.dropped = 0;
+  return ok();
+}
 
 int kla_abi_version(void) { return KLA_ABI_VERSION; }
 
@@ -177,6 +261,14 @@ const char* kla_status_string(kla_status_t s) {
 const char* kla_last_error(void) { return g_last_error.c_str(); }
 
 // ---------------------------------------------------------------- prefill
+
+int kla_prefill_matrix_path(const kla_shape_t* shp, int chunk) {
+  if (check_shape(shp, "kla_prefill_matrix_path") != KLA_OK) return -1;
+  if (chunk != 32 && chunk != 64 && chunk != 128) return -1;
+  kla::PrefillArgs a = make_prefill(shp, chunk);
+  a.o = reinterpret_cast<void*>(1);
+  return kla::prefill_mfma_supported(a) ? 1 : 0;
+}
 
 kla_status_t kla_prefill_workspace_size(const kla_shape_t* shp, int chunk, int with_output,
                                         size_t* bytes) {

@@ -10,6 +10,10 @@
 
 namespace kla {
 
+// Timing hooks around a call's dominant kernel (no-ops unless enabled).
+void prof_begin(hipStream_t st);
+void prof_end(hipStream_t st);
+
 // Workspace carving: every region is 256-byte aligned.
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
@@ -49,6 +53,7 @@ struct SreArgs {
   int32_t* sel;
   float* sel_k;
   float* sel_v;
+  int sel_stride;  // rows between heads in sel_k / sel_v (>= top_k)
 };
 
 struct DecodeArgs {

@@ -223,10 +223,12 @@ hipError_t launch_typed(const PrefillArgs& a, void* ws, hipStream_t st) {
   const int S = slices_for(D);
   const int Fs = (D + S - 1) / S;
   float* part = a.o ? static_cast<float*>(ws) : nullptr;
+  prof_begin(st);
   hipLaunchKernelGGL((prefill_slice_kernel<DQK, DV, Tin>), dim3(S, a.N), dim3(kThreads), 0, st,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), a.T, a.chunk, S, Fs, a.H0, a.s0, a.HT, a.sT,
                      part);
+  prof_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.o) return e;
   hipLaunchKernelGGL((prefill_combine_kernel<DQK, DV, Tin, Tout>), dim3((a.T + 15) / 16, a.N),
