@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/kla.h"
+#include "kla.h"
 
 namespace kla {
 

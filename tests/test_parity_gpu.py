@@ -116,6 +116,30 @@ def test_prefill_resume_and_state_only(K):
     assert_close(host(H), rH, RTOL_F32, "H vs oracle")
 
 
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_prefill_bf16_resume_and_state_only(K, chunk):
+    # resumed bf16 prefill through the matrix-core path equals one call
+    c = S.prefill_case("resume", 1, 3, 700, 64, 64, chunk, seed=33)
+    Q, Kk, V = (dev(x, torch.bfloat16) for x in (c.q, c.k, c.v))
+    T1 = 300
+    o1, H1, s1 = K.prefill(Q[:, :, :T1], Kk[:, :, :T1], V[:, :, :T1], chunk=chunk, return_state=True)
+    o2, H2, s2 = K.prefill(Q[:, :, T1:], Kk[:, :, T1:], V[:, :, T1:], chunk=chunk, state=(H1, s1),
+                           return_state=True)
+    ro, rH, rs = O.prefill(c.q, c.k, c.v, chunk=100)
+    assert_close(host(torch.cat([o1, o2], dim=2)), ro, RTOL_BF16, "resumed o")
+    assert_close(host(H2), rH, RTOL_BF16, "resumed H")
+    assert_close(host(s2), rs, RTOL_BF16, "resumed s")
+    Hs, ss = K.prefill(Q, Kk, V, chunk=chunk, outputs=False)
+    assert_close(host(Hs), rH, RTOL_BF16, "state-only H")
+    assert_close(host(ss), rs, RTOL_BF16, "state-only s")
+
+
+def test_prefill_matrix_path_selected(K):
+    assert K.prefill_uses_matrix_cores(B=4, H=8, T=4096, d_qk=64, d_v=64, chunk=64)
+    assert not K.prefill_uses_matrix_cores(d_qk=32, d_v=32)
+    assert not K.prefill_uses_matrix_cores(dtype=0)
+
+
 def test_prefill_degenerate_inputs(K):
     # zero queries: every denominator is 0 and the output is 0; eps > 0 keeps it 0
     T, d = 70, 16
