@@ -39,6 +39,44 @@ def phi_dim(d):
     return d * (d + 1) // 2
 
 
+def measured_traffic(kernel_source, profile):
+    """HBM bytes per launch of a kernel, from a committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by a plain-copy calibration).
+    The summary records the sha256 of the kernel's source file; once the
+    source has changed the counters no longer describe it and this returns
+    None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "kernelized_linear_attention_02_amd", "csrc", kernel_source)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, mib):
+    """A plain device-to-device copy of a known size, for scaling the HBM
+    byte counters (run under rocprofv3 --pmc)."""
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "bytes_read": n * 2, "bytes_written": n * 2}), flush=True)
+
+
 def timed_calls(torch, K, fn, steps, warmup):
     """Wall time per call (sync on both sides) and the library's own kernel
     timing of the dominant kernel (HIP events on the call's stream)."""
@@ -82,7 +120,9 @@ def bench_prefill(torch, K, S, name, steps, warmup):
         tokens_per_s=B * T / (step_ms * 1e-3), head_tokens_per_s=head_tokens / (step_ms * 1e-3),
         call_tflops=call_flops / (step_ms * 1e-3) / 1e12,
         roofline=dict(bound="mfma" if mfma else "alu", achieved=achieved, peak=peak, unit="TFLOP/s",
-                      frac=achieved / peak, traffic=None, kernel_ms=kern_ms,
+                      frac=achieved / peak, kernel_ms=kern_ms,
+                      traffic=measured_traffic("prefill_mfma.hip", f"prefill_state_kernel_{name}_traffic.md")
+                      if mfma else None,
                       kernel="prefill state/readout", flops_per_launch=kern_flops),
         arith="bf16" if mfma else "f32",
     )
@@ -190,6 +230,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB bf16 copy three times (HBM counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -206,6 +248,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
     K.load_library()
 
     name = "prefill_4x8x4096"
