@@ -1,6 +1,9 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins
 catch each one: a dropped sqrt(2), a dropped diagonal, a read-before-update,
-an unnormalised prediction, a reversed selection, a fold of the kept pairs."""
+a transposed intra-chunk operand, an unnormalised prediction, a reversed
+selection, a fold of the kept pairs."""
+import functools
+
 import numpy as np
 import pytest
 
@@ -35,6 +38,24 @@ def _chunked_strict_lower(q, k, v, chunk=256, H0=None, s0=None, eps=0.0, return_
     return o, H, s
 
 
+def _chunked_transposed(q, k, v, chunk=256, H0=None, s0=None, eps=0.0, return_parts=False):
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    T, d = q.shape
+    H = np.zeros((O.phi_dim(d), v.shape[1]))
+    s = np.zeros(O.phi_dim(d))
+    o = np.zeros((T, v.shape[1]))
+    for c0 in range(0, T, chunk):
+        Q, Kc, V = q[c0:c0 + chunk], k[c0:c0 + chunk], v[c0:c0 + chunk]
+        S = Kc @ Q.T  # planted: keys against queries
+        A = np.tril(S * S)
+        num = A @ V + O.phi(Q) @ H
+        den = A.sum(1) + O.phi(Q) @ s
+        o[c0:c0 + chunk] = K._safe_div(num, den)
+        H += O.phi(Kc).T @ V
+        s += O.phi(Kc).sum(0)
+    return o, H, s
+
+
 def _decode_read_first(H, s, q, k, v, eps=0.0):
     fq = O.phi(q)
     den = fq @ s + eps
@@ -56,6 +77,9 @@ def _select_ascending(scores, m, ids=None):
 CASES = [
     ("phi", _phi_no_sqrt2, [TP.test_phi_golden, TP.test_phi_random_float_identity]),
     ("prefill_chunked", _chunked_strict_lower, [TP.test_first_token_returns_its_value]),
+    ("prefill_chunked_transposed", _chunked_transposed,
+     [functools.partial(TP.test_forms_agree_on_small_integers, 7),
+      functools.partial(TP.test_three_forms_agree, 3, 57, 32)]),
     ("decode_step", _decode_read_first, [TS.test_decode_step_matches_definition_cases]),
     ("sre", _sre_unnormalised, [TS.test_sre_golden]),
     ("select_topk", _select_ascending, [TS.test_select_topk_order_against_python_sort]),
@@ -64,6 +88,7 @@ CASES = [
 
 @pytest.mark.parametrize("name,bad,pins", CASES, ids=[c[0] for c in CASES])
 def test_pins_catch_planted_mistake(monkeypatch, name, bad, pins):
+    name = name.replace("_transposed", "")
     monkeypatch.setattr(O, name, bad)
     monkeypatch.setattr(K, name, bad)
     caught = 0
