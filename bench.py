@@ -167,15 +167,18 @@ def bench_decode(torch, K, S, steps_loop, reps):
 
     loop_ms, kern_ms, per_loop = timed_calls(torch, K, loop, reps, 1)
     D = phi_dim(d)
-    state_bytes = N * (2 * D * d * 4 + 2 * D * 4 + 4 * d * 4)  # H, s read+write; q, k, v, o
-    achieved = state_bytes / (kern_ms * 1e-3) / 1e9
+    # one fused launch per step: H and s read and written, q, k, v, o, the
+    # candidates' keys and values read, the kept rows, scores and indices written
+    step_bytes = N * (2 * D * d * 4 + 2 * D * 4 + 4 * d * 4 + 2 * n_cand * d * 4 + 2 * top * d * 4
+                      + n_cand * 4 + top * 4)
+    achieved = step_bytes / (kern_ms * 1e-3) / 1e9
     step_ms = loop_ms / nsteps
     return dict(
         workload="decode_sre_4096x128", N=N, steps=nsteps, step_ms=step_ms,
-        steps_per_s=1e3 / step_ms, decode_kernel_ms=kern_ms,
+        steps_per_s=1e3 / step_ms, kernel_ms=kern_ms,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=achieved / PEAK_HBM_GBS, traffic=None, kernel="decode state stream",
-                      bytes_per_launch=state_bytes),
+                      frac=achieved / PEAK_HBM_GBS, traffic=None,
+                      kernel="decode step + SRE + top-k (fused)", bytes_per_launch=step_bytes),
     )
 
 

@@ -203,12 +203,14 @@ hipError_t score_and_select(int N, int dqk, int dv, float eps, const float* H, c
 
 }  // namespace
 
-size_t sre_workspace(int N, int, int, const SreArgs& s) {
+size_t sre_workspace(int N, int dqk, int dv, const SreArgs& s) {
+  if (decode_fused_supported(dqk, dv, s)) return 0;
   return s.scores ? 0 : align_up((size_t)N * s.n_cand * sizeof(float));
 }
 
 hipError_t sre_launch(int N, int dqk, int dv, float eps, const float* H, const float* s,
                       const SreArgs& sre, void* ws, hipStream_t st) {
+  if (decode_fused_supported(dqk, dv, sre)) return sre_fused_launch(N, eps, H, s, sre, st);
   return score_and_select(N, dqk, dv, eps, H, s, sre, ws, st, true);
 }
 
@@ -217,6 +219,7 @@ size_t decode_workspace(const DecodeArgs& a, const SreArgs* sre) {
 }
 
 hipError_t decode_launch(const DecodeArgs& a, const SreArgs* sre, void* ws, hipStream_t st) {
+  if (sre && decode_fused_supported(a.dqk, a.dv, *sre)) return decode_fused_launch(a, *sre, st);
   hipError_t e = dispatch_dd(a.dqk, a.dv, [&](auto A, auto B) {
     return decode_dt<decltype(A)::value, decltype(B)::value>(a, st);
   });

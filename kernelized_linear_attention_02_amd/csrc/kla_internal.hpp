@@ -72,6 +72,13 @@ struct DecodeArgs {
 size_t decode_workspace(const DecodeArgs& a, const SreArgs* sre);
 hipError_t decode_launch(const DecodeArgs& a, const SreArgs* sre, void* ws, hipStream_t st);
 
+// Fused decode + scoring + selection on the matrix cores (d_qk = d_v = 64,
+// n_cand <= 64); no workspace.
+bool decode_fused_supported(int dqk, int dv, const SreArgs& sre);
+hipError_t decode_fused_launch(const DecodeArgs& a, const SreArgs& sre, hipStream_t st);
+hipError_t sre_fused_launch(int N, float eps, const float* H, const float* s, const SreArgs& sre,
+                            hipStream_t st);
+
 size_t sre_workspace(int N, int dqk, int dv, const SreArgs& s);
 hipError_t sre_launch(int N, int dqk, int dv, float eps, const float* H, const float* s,
                       const SreArgs& sre, void* ws, hipStream_t st);

@@ -113,12 +113,18 @@ def test_decode_and_sre_validation(lib):
     bad = _sre(ck=ck, cv=cv, sk=ctypes.c_void_p(0x100000 + 64), sv=ctypes.c_void_p(0x2000000))
     assert _decode(lib, N=1, sre=bad) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"overlap" in lib.kla_last_error()
-    # no scores pointer: the library needs workspace for them
+    # no scores pointer: the vector-unit scorer (d = 32) keeps them in the workspace
     need = ctypes.c_size_t(0)
     s = _sre()
-    assert lib.kla_decode_workspace_size(8, 64, 64, ctypes.byref(s), ctypes.byref(need)) == B.KLA_OK
+    assert lib.kla_decode_workspace_size(8, 32, 32, ctypes.byref(s), ctypes.byref(need)) == B.KLA_OK
     assert need.value >= 8 * 64 * 4
-    assert _decode(lib, sre=_sre(), ws=None) == B.KLA_ERR_WORKSPACE
+    assert _decode(lib, dqk=32, dv=32, sre=_sre(), ws=None) == B.KLA_ERR_WORKSPACE
+    # the fused matrix-core step (d = 64, at most 64 candidates) needs none
+    assert lib.kla_decode_workspace_size(8, 64, 64, ctypes.byref(s), ctypes.byref(need)) == B.KLA_OK
+    assert need.value == 0
+    s65 = _sre(n_cand=65)
+    assert lib.kla_decode_workspace_size(8, 64, 64, ctypes.byref(s65), ctypes.byref(need)) == B.KLA_OK
+    assert need.value >= 8 * 65 * 4
     assert lib.kla_sre_select(8, 64, 64, 0.0, None, P, ctypes.byref(s), P, 1 << 40, None) == \
         B.KLA_ERR_INVALID_ARGUMENT
     assert lib.kla_sre_select(8, 64, 64, 0.0, P, P, None, P, 1 << 40, None) == B.KLA_ERR_INVALID_ARGUMENT

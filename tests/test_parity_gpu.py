@@ -248,6 +248,73 @@ def test_sre_select_against_oracle(K, n_cand, top_k):
         np.testing.assert_array_equal(host(r["sel_v"])[n], cv[n][sel])
 
 
+@pytest.mark.parametrize("n_cand,top_k", [(1, 1), (17, 4), (33, 33), (48, 12)])
+@pytest.mark.parametrize("with_scores,gather", [(True, True), (False, False)])
+def test_sre_select_matrix_path_shapes(K, n_cand, top_k, with_scores, gather):
+    # d = 64 with at most 64 candidates runs on the matrix cores (split bf16)
+    rng = np.random.default_rng(1000 + n_cand)
+    N, d = 7, 64
+    pk = rng.standard_normal((N, 200, d)).astype(np.float32) / 8
+    pv = rng.standard_normal((N, 200, d)).astype(np.float32)
+    H, s = K.prefill(dev(pk)[None], dev(pk)[None], dev(pv)[None], chunk=64, outputs=False)
+    ck = rng.standard_normal((N, n_cand, d)).astype(np.float32) / 8
+    ck[0, 0] = 0.0  # zero key: denominator 0, prediction 0, score ||v||^2
+    cv = rng.standard_normal((N, n_cand, d)).astype(np.float32)
+    H0, s0 = H.clone(), s.clone()
+    r = K.sre_select(H[0], s[0], dev(ck), dev(cv), top_k=top_k, scores=with_scores, gather=gather)
+    torch.cuda.synchronize()
+    assert torch.equal(H, H0) and torch.equal(s, s0), "scoring must not write the state"
+    for n in range(N):
+        fk = O.phi(pk[n])
+        rs = O.sre(fk.T @ pv[n].astype(np.float64), fk.sum(0), ck[n], cv[n])
+        if with_scores:
+            assert_close(host(r["scores"])[n], rs, RTOL_F32, f"scores head {n}")
+        sel = host(r["sel"]).astype(int)[n]
+        assert len(set(sel.tolist())) == top_k and sel.min() >= 0 and sel.max() < n_cand
+        assert O.near_tie_ok(rs, sel, top_k, TIE_REL), f"selection head {n}"
+        if gather:
+            np.testing.assert_array_equal(host(r["sel_k"])[n], ck[n][sel])
+            np.testing.assert_array_equal(host(r["sel_v"])[n], cv[n][sel])
+    if with_scores:
+        assert host(r["scores"])[0, 0] == pytest.approx(float(np.sum(cv[0, 0].astype(np.float64) ** 2)),
+                                                         rel=1e-6)
+
+
+@pytest.mark.parametrize("dtype,out_dtype,eps", [("f32", "f32", 0.0), ("bf16", "bf16", 0.0),
+                                                 ("f32", "f32", 0.25)])
+def test_decode_step_with_selection_matrix_path(K, dtype, out_dtype, eps):
+    rng = np.random.default_rng(77)
+    N, d, n_cand, top_k = 9, 64, 40, 9
+    pk = rng.standard_normal((N, 150, d)).astype(np.float32) / 8
+    pv = rng.standard_normal((N, 150, d)).astype(np.float32)
+    H, s = K.prefill(dev(pk)[None], dev(pk)[None], dev(pv)[None], chunk=32, outputs=False)
+    H, s = H[0].contiguous(), s[0].contiguous()
+    q = rng.standard_normal((N, d)).astype(np.float32) / 8
+    k = rng.standard_normal((N, d)).astype(np.float32) / 8
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = (S.round_to_bf16(x) for x in (q, k, v))
+    ck = rng.standard_normal((N, n_cand, d)).astype(np.float32) / 8
+    cv = rng.standard_normal((N, n_cand, d)).astype(np.float32)
+    tt = tdtype(dtype)
+    o, r = K.decode_step(H, s, dev(q, tt), dev(k, tt), dev(v, tt), eps=eps, out_dtype=tdtype(out_dtype),
+                         cand_k=dev(ck), cand_v=dev(cv), top_k=top_k, gather=True)
+    torch.cuda.synchronize()
+    rtol_o = RTOL_BF16 if out_dtype == "bf16" else RTOL_F32
+    for n in range(N):
+        fk = O.phi(pk[n])
+        rH, rs = fk.T @ pv[n].astype(np.float64), fk.sum(0)
+        ro, rH, rs = O.decode_step(rH, rs, q[n], k[n], v[n], eps=eps)
+        assert_close(host(o)[n], ro, rtol_o, f"o head {n}")
+        assert_close(host(H)[n], rH, RTOL_F32, f"H head {n}")
+        assert_close(host(s)[n], rs, RTOL_F32, f"s head {n}")
+        rsc = O.sre(rH, rs, ck[n], cv[n], eps=eps)
+        assert_close(host(r["scores"])[n], rsc, RTOL_F32, f"scores head {n}")
+        sel = host(r["sel"]).astype(int)[n]
+        assert O.near_tie_ok(rsc, sel, top_k, TIE_REL), f"selection head {n}"
+        np.testing.assert_array_equal(host(r["sel_k"])[n], ck[n][sel])
+
+
 def _decode_chain(K, case, steps, check_ids):
     """Run the decode + selection chain on the GPU for all head-states and
     compare the head-states ``check_ids`` with the oracle, following the GPU
