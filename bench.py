@@ -233,6 +233,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
+    ap.add_argument("--only", choices=["prefill_1x16x65536", "decode_sre_4096x128", "hybrid_2x16x16384"],
+                    help="run just this secondary workload and print its line (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB bf16 copy three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -255,6 +257,15 @@ def main():
         copy_calibration(torch, args.copy_calibration)
         return
     K.load_library()
+    if args.only:
+        if args.only == "prefill_1x16x65536":
+            r = bench_prefill(torch, K, S, args.only, args.steps, args.warmup)
+        elif args.only == "decode_sre_4096x128":
+            r = bench_decode(torch, K, S, args.decode_steps, max(1, args.steps // 10))
+        else:
+            r = bench_hybrid(torch, K, S, args.steps, args.warmup)
+        print(json.dumps(r), flush=True)
+        return
 
     name = "prefill_4x8x4096"
     log("[bench] main: prefill_4x8x4096")

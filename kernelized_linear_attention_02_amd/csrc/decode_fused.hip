@@ -98,6 +98,25 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& 
   }
 }
 
+// The state is touched once per step: its loads and stores are marked
+// nontemporal so they do not displace the candidates in the caches.
+constexpr bool kStreamNT = false;
+__device__ __forceinline__ float4 ld_state(const float* p) {
+  if (kStreamNT) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+  }
+  return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ void st_state(float* p, const float4& v) {
+  if (kStreamNT) {
+    const f32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+  } else {
+    *reinterpret_cast<float4*>(p) = v;
+  }
+}
+
 __device__ __forceinline__ float comp(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -118,6 +137,20 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
+  float* Hn = H + (size_t)n * kD * kDim;
+  float* sn = s + (size_t)n * kD;
+
+  // tile ks: rows f0 .. f0 + 31; this lane's rows f0 + 8*q4 + j
+  auto load_tile = [&](int ks, float4 (&h)[8], float4 (&sv)[2]) {
+    const int fr = kFT * ks + 8 * q4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = ld_state(Hn + (size_t)(fr + j) * kDim + 4 * l16);
+    sv[0] = ld_state(sn + fr);
+    sv[1] = ld_state(sn + fr + 4);
+  };
+  // the first tile is in flight while the block stages its inputs
+  float4 h[8], sv[2];
+  load_tile(w, h, sv);
 
   if (UPDATE && tid < kDim) {
     sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kDim + tid);
@@ -138,8 +171,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   }
   __syncthreads();
 
-  float* Hn = H + (size_t)n * kD * kDim;
-  float* sn = s + (size_t)n * kD;
+
   float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (UPDATE) v4 = *reinterpret_cast<const float4*>(&sh.vs[4 * l16]);
 
@@ -154,17 +186,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
   float oden = 0.0f;
 
-  // tile ks: rows f0 .. f0 + 31; this lane's rows f0 + 8*q4 + j
-  auto load_tile = [&](int ks, float4 (&h)[8], float4 (&sv)[2]) {
-    const int fr = kFT * ks + 8 * q4;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = *reinterpret_cast<const float4*>(Hn + (size_t)(fr + j) * kDim + 4 * l16);
-    sv[0] = *reinterpret_cast<const float4*>(sn + fr);
-    sv[1] = *reinterpret_cast<const float4*>(sn + fr + 4);
-  };
 
-  float4 h[8], sv[2];
-  load_tile(w, h, sv);
 #pragma unroll 1
   for (int ks = w; ks < kTiles; ks += kWaves) {
     float4 hn[8], svn[2];
@@ -194,17 +216,17 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
         h[j].z += pk * v4.z;
         h[j].w += pk * v4.w;
         sj[j] += pk;
-        *reinterpret_cast<float4*>(Hn + (size_t)(fr + j) * kDim + 4 * l16) = h[j];
+        st_state(Hn + (size_t)(fr + j) * kDim + 4 * l16, h[j]);
         oacc.x += pq * h[j].x;
         oacc.y += pq * h[j].y;
         oacc.z += pq * h[j].z;
         oacc.w += pq * h[j].w;
         oden += pq * sj[j];
       }
-      if (l16 == 0) {
-        *reinterpret_cast<float4*>(sn + fr) = make_float4(sj[0], sj[1], sj[2], sj[3]);
-        *reinterpret_cast<float4*>(sn + fr + 4) = make_float4(sj[4], sj[5], sj[6], sj[7]);
-      }
+      // two lanes per quarter write its 8 values: one contiguous 128-byte run
+      if (l16 < 2)
+        st_state(sn + fr + 4 * l16, l16 ? make_float4(sj[4], sj[5], sj[6], sj[7])
+                                        : make_float4(sj[0], sj[1], sj[2], sj[3]));
     }
 
     // A operands (two pieces) for every candidate block, and the float32
