@@ -121,17 +121,53 @@ __device__ __forceinline__ float comp(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// MT: 16-candidate blocks (n_cand <= 16 * MT). UPDATE: decode step first
-// (H and s written back, o produced); otherwise the state is only read.
-template <int MT, bool UPDATE, typename Tin, typename Tout>
+// Candidate sources: rows of float32 arrays [N, n_cand, 64] ...
+struct CandRows {
+  const float* k;
+  const float* v;
+  int n_cand;
+  __device__ __forceinline__ float4 k4(int n, int c, int d4) const {
+    return *reinterpret_cast<const float4*>(k + ((size_t)n * n_cand + c) * kDim + 4 * d4);
+  }
+  __device__ __forceinline__ float4 v4(int n, int c, int d4) const {
+    return *reinterpret_cast<const float4*>(v + ((size_t)n * n_cand + c) * kDim + 4 * d4);
+  }
+};
+
+// ... or bf16 token rows [N, T, 64] picked by token id: the first n_cache
+// candidates are cache[n][j], the rest the consecutive tokens ev0, ev0 + 1, ...
+struct CandTokens {
+  const uint16_t* k;
+  const uint16_t* v;
+  int T;
+  const int32_t* cache;
+  int cstride, n_cache, ev0;
+  __device__ __forceinline__ size_t row(int n, int c) const {
+    const int tok = c < n_cache ? cache[(size_t)n * cstride + c] : ev0 + (c - n_cache);
+    return ((size_t)n * T + tok) * kDim;
+  }
+  static __device__ __forceinline__ float4 bf4(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+  }
+  __device__ __forceinline__ float4 k4(int n, int c, int d4) const { return bf4(k + row(n, c) + 4 * d4); }
+  __device__ __forceinline__ float4 v4(int n, int c, int d4) const { return bf4(v + row(n, c) + 4 * d4); }
+};
+
+// Work-group (n, g) scores candidates 64 g .. 64 g + 16 MT - 1 of head-state n.
+// MT: 16-candidate blocks. UPDATE: decode step first (H and s written back,
+// o produced); otherwise the state is only read. SELECT: top_k selection and
+// gather in the same kernel (requires n_cand <= 16 * MT, one group).
+template <int MT, bool UPDATE, bool SELECT, typename Tin, typename Tout, typename Cand>
 __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     float* __restrict__ H, float* __restrict__ s, const Tin* __restrict__ q,
     const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, float eps,
-    const float* __restrict__ cand_k, const float* __restrict__ cand_v, int n_cand, int top_k,
-    float* __restrict__ scores, int32_t* __restrict__ sel, float* __restrict__ sel_k,
-    float* __restrict__ sel_v, int sel_stride) {
+    Cand cand, int n_cand, int top_k, float* __restrict__ scores, int sstride,
+    int32_t* __restrict__ sel, float* __restrict__ sel_k, float* __restrict__ sel_v, int sel_stride) {
   __shared__ __align__(16) FusedLds sh;
   const int n = blockIdx.x;
+  const int cbase = 64 * blockIdx.y;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -158,12 +194,11 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     sh.vs[tid] = Elem<Tin>::load(v, (size_t)n * kDim + tid);
   }
   for (int i = tid; i < kD; i += kThreadsF) sh.tab[i] = kPairTable.ab[i];
-  const float* ckn = cand_k + (size_t)n * n_cand * kDim;
   for (int i = tid; i < 16 * MT * (kDim / 4); i += kThreadsF) {
     const int c = i / (kDim / 4);
     const int d4 = i % (kDim / 4);
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < n_cand) x = *reinterpret_cast<const float4*>(ckn + (size_t)c * kDim + 4 * d4);
+    if (cbase + c < n_cand) x = cand.k4(n, cbase + c, d4);
     sh.ck[c][4 * d4] = x.x;
     sh.ck[c][4 * d4 + 1] = x.y;
     sh.ck[c][4 * d4 + 2] = x.z;
@@ -329,17 +364,17 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   }
   if (w == kWaves - 1) {
     // lane (l16, q4) holds candidates 16*mt + 4*q4 + i at state columns 4*l16 + nt
-    const float* cvn = cand_v + (size_t)n * n_cand * kDim;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 16 * mt + 4 * q4 + i;
+        const bool live = cbase + c < n_cand;
         float den = eps;
 #pragma unroll
         for (int r = 0; r < kWaves; ++r) den += sh.den[r][c];
         float4 vc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c < n_cand) vc = *reinterpret_cast<const float4*>(cvn + (size_t)c * kDim + 4 * l16);
+        if (live) vc = cand.v4(n, cbase + c, l16);
         float err = 0.0f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -352,24 +387,25 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
         err += __shfl_xor(err, 4, 64);
         err += __shfl_xor(err, 8, 64);
         if (l16 == 0) {
-          if (c < n_cand && scores) scores[(size_t)n * n_cand + c] = err;
-          sh.keys[c] = c < n_cand ? topk_key(err, (uint32_t)c) : 0ull;
+          if (live && scores) scores[(size_t)n * sstride + cbase + c] = err;
+          if (SELECT) sh.keys[c] = live ? topk_key(err, (uint32_t)c) : 0ull;
         }
       }
     }
-    for (int c = 16 * MT + lane; c < kMaxCand; c += 64) sh.keys[c] = 0ull;
+    if (SELECT)
+      for (int c = 16 * MT + lane; c < kMaxCand; c += 64) sh.keys[c] = 0ull;
   }
+  if (!SELECT) return;
   bitonic_sort_desc(sh.keys, kMaxCand);
   for (int i = tid; i < top_k; i += kThreadsF) sel[(size_t)n * top_k + i] = (int32_t)topk_index(sh.keys[i]);
   if (sel_k) {
-    const float* cvn = cand_v + (size_t)n * n_cand * kDim;
     for (int i = tid; i < top_k * (kDim / 4); i += kThreadsF) {
       const int j = i / (kDim / 4);
       const int d4 = i % (kDim / 4);
-      const uint32_t c = topk_index(sh.keys[j]);
+      const int c = (int)topk_index(sh.keys[j]);
       const size_t dst = ((size_t)n * sel_stride + j) * kDim + 4 * d4;
-      *reinterpret_cast<float4*>(sel_k + dst) = *reinterpret_cast<const float4*>(ckn + (size_t)c * kDim + 4 * d4);
-      *reinterpret_cast<float4*>(sel_v + dst) = *reinterpret_cast<const float4*>(cvn + (size_t)c * kDim + 4 * d4);
+      *reinterpret_cast<float4*>(sel_k + dst) = cand.k4(n, c, d4);
+      *reinterpret_cast<float4*>(sel_v + dst) = cand.v4(n, c, d4);
     }
   }
 }
@@ -377,10 +413,11 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
 template <int MT, bool UPDATE, typename Tin, typename Tout>
 void launch_fused(int N, float* H, float* s, const void* q, const void* k, const void* v, void* o,
                   float eps, const SreArgs& sre, hipStream_t st) {
-  hipLaunchKernelGGL((decode_sre_kernel<MT, UPDATE, Tin, Tout>), dim3(N), dim3(kThreadsF), 0, st, H, s,
-                     static_cast<const Tin*>(q), static_cast<const Tin*>(k), static_cast<const Tin*>(v),
-                     static_cast<Tout*>(o), eps, sre.cand_k, sre.cand_v, sre.n_cand, sre.top_k,
-                     sre.scores, sre.sel, sre.sel_k, sre.sel_v, sre.sel_stride ? sre.sel_stride : sre.top_k);
+  const CandRows cand{sre.cand_k, sre.cand_v, sre.n_cand};
+  hipLaunchKernelGGL((decode_sre_kernel<MT, UPDATE, true, Tin, Tout, CandRows>), dim3(N, 1), dim3(kThreadsF), 0, st,
+                     H, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), static_cast<const Tin*>(v),
+                     static_cast<Tout*>(o), eps, cand, sre.n_cand, sre.top_k, sre.scores, sre.n_cand, sre.sel,
+                     sre.sel_k, sre.sel_v, sre.sel_stride ? sre.sel_stride : sre.top_k);
 }
 
 template <bool UPDATE, typename Tin, typename Tout>
@@ -419,6 +456,17 @@ hipError_t sre_fused_launch(int N, float eps, const float* H, const float* s, co
   launch_mt<false, float, float>(N, const_cast<float*>(H), const_cast<float*>(s), nullptr, nullptr, nullptr,
                                  nullptr, eps, sre, st);
   prof_end(st);
+  return hipGetLastError();
+}
+
+hipError_t hybrid_score_mfma(int N, const float* H, const float* s, const uint16_t* k, const uint16_t* v,
+                             int T, const int32_t* cache, int cstride, int n_cache, int ev0, int n_cand,
+                             float* scores, int sstride, float eps, hipStream_t st) {
+  const CandTokens cand{k, v, T, cache, cstride, n_cache, ev0};
+  hipLaunchKernelGGL((decode_sre_kernel<4, false, false, float, float, CandTokens>),
+                     dim3(N, (n_cand + 63) / 64), dim3(kThreadsF), 0, st, const_cast<float*>(H),
+                     const_cast<float*>(s), nullptr, nullptr, nullptr, nullptr, eps, cand, n_cand, 0, scores,
+                     sstride, nullptr, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

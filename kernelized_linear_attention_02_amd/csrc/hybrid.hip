@@ -16,6 +16,7 @@
 // The host knows every count in advance (they depend only on T, window,
 // refresh and cache_size), so no device value is read back.
 #include <algorithm>
+#include <type_traits>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
@@ -388,9 +389,16 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
         n_cache = n_cand;
       } else {
         prof_begin(st);
-        hipLaunchKernelGGL((hyb_score_kernel<DQK, DV, Tin>), dim3((n_cand + 63) / 64, N),
-                           dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache,
-                           f_prev, n_cand, w.scores, kCStride, a.eps);
+        if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
+          // matrix cores, float32-faithful (split bf16 operands)
+          e = hybrid_score_mfma(N, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache, f_prev, n_cand,
+                                w.scores, kCStride, a.eps, st);
+          if (e != hipSuccess) return e;
+        } else {
+          hipLaunchKernelGGL((hyb_score_kernel<DQK, DV, Tin>), dim3((n_cand + 63) / 64, N),
+                             dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache,
+                             f_prev, n_cand, w.scores, kCStride, a.eps);
+        }
         prof_end(st);
         KLA_CHECK();
         hipLaunchKernelGGL(hyb_select_kernel, dim3(N), dim3(kThreads), 0, st, w.scores, kCStride,

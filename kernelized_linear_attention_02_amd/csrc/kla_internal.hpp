@@ -79,6 +79,12 @@ hipError_t decode_fused_launch(const DecodeArgs& a, const SreArgs& sre, hipStrea
 hipError_t sre_fused_launch(int N, float eps, const float* H, const float* s, const SreArgs& sre,
                             hipStream_t st);
 
+// Scores of hybrid candidates (bf16 token rows picked by id; d = 64) on the
+// matrix cores, for the hybrid prefill's refresh steps.
+hipError_t hybrid_score_mfma(int N, const float* H, const float* s, const uint16_t* k, const uint16_t* v,
+                             int T, const int32_t* cache, int cstride, int n_cache, int ev0, int n_cand,
+                             float* scores, int sstride, float eps, hipStream_t st);
+
 size_t sre_workspace(int N, int dqk, int dv, const SreArgs& s);
 hipError_t sre_launch(int N, int dqk, int dv, float eps, const float* H, const float* s,
                       const SreArgs& sre, void* ws, hipStream_t st);
