@@ -26,6 +26,7 @@ namespace kla {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWavesF = kThreads / 64;
 constexpr int kMaxSlice = 256;
 
 __global__ void fill_kernel_f32(float* p, size_t n, float x) {
@@ -173,6 +174,131 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_kernel(float* __restrict__ 
     if (fl < fcount) Hn[(size_t)(f0 + fl) * DV + c] = h[j];
   }
   if (tid < fcount) s[(size_t)n * D + f0 + tid] = sm;
+}
+
+// ---------------------------------------------------------------- matrix-core fold (d = 64, bf16 in)
+//
+// [H | s] += phi(K_r)^T [V_r | 1] over the rejected tokens, on the matrix
+// cores: each wave takes 16-feature tiles (canonical order) and keeps a tile
+// of [H | s] in MFMA accumulators seeded with the stored state. The feature
+// products k_a k_b (times sqrt(2) off the diagonal) are exact float32 values
+// split into three bf16 pieces p0 + p1 + p2 = p; v is bf16 on input, so every
+// MFMA product is exact and the sums are float32, as in a float32 fold.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kFD = 64;
+constexpr int kFPhi = kFD * (kFD + 1) / 2;   // 2080
+constexpr int kFTiles = kFPhi / 16;          // 130
+constexpr int kFoldTilesPerWG = 8;           // two per wave
+constexpr int kFoldRows = 128;               // rejected tokens per call, at most
+
+struct FoldPairs {
+  uint16_t ab[kFPhi];
+  constexpr FoldPairs() : ab{} {
+    int f = 0;
+    for (int a = 0; a < kFD; ++a)
+      for (int b = a; b < kFD; ++b) ab[f++] = static_cast<uint16_t>(a | (b << 8));
+  }
+};
+__constant__ FoldPairs kFoldPairs = FoldPairs();
+
+__device__ __forceinline__ void split3_8(const float (&x)[8], bf16x8& p0, bf16x8& p1, bf16x8& p2) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 a = (__bf16)x[j];
+    const float r = x[j] - (float)a;
+    const __bf16 b = (__bf16)r;
+    p0[j] = a;
+    p1[j] = b;
+    p2[j] = (__bf16)(r - (float)b);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restrict__ H, float* __restrict__ s,
+                                                               const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v, int T,
+                                                               const int32_t* __restrict__ rejected,
+                                                               int rstride, int n_rej) {
+  __shared__ __align__(16) float kt[kFD][kFoldRows + 4];
+  __shared__ __align__(16) uint16_t vt[kFD][kFoldRows + 8];
+  const int n = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int R = (n_rej + 31) & ~31;  // rows padded to whole k-steps (zeros)
+
+  for (int i = tid; i < R * (kFD / 4); i += kThreads) {
+    const int r = i / (kFD / 4);
+    const int d4 = i % (kFD / 4);
+    uint2 ku = make_uint2(0, 0), vu = ku;
+    if (r < n_rej) {
+      const size_t row = ((size_t)n * T + rejected[(size_t)n * rstride + r]) * kFD + 4 * d4;
+      ku = *reinterpret_cast<const uint2*>(k + row);
+      vu = *reinterpret_cast<const uint2*>(v + row);
+    }
+    kt[4 * d4 + 0][r] = __uint_as_float(ku.x << 16);
+    kt[4 * d4 + 1][r] = __uint_as_float(ku.x & 0xFFFF0000u);
+    kt[4 * d4 + 2][r] = __uint_as_float(ku.y << 16);
+    kt[4 * d4 + 3][r] = __uint_as_float(ku.y & 0xFFFF0000u);
+    vt[4 * d4 + 0][r] = (uint16_t)(vu.x & 0xFFFF);
+    vt[4 * d4 + 1][r] = (uint16_t)(vu.x >> 16);
+    vt[4 * d4 + 2][r] = (uint16_t)(vu.y & 0xFFFF);
+    vt[4 * d4 + 3][r] = (uint16_t)(vu.y >> 16);
+  }
+  __syncthreads();
+
+  bf16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
+  float* Hn = H + (size_t)n * kFPhi * kFD;
+  float* sn = s + (size_t)n * kFPhi;
+#pragma unroll 1
+  for (int u = 0; u < kFoldTilesPerWG / kWavesF; ++u) {
+    const int tile = blockIdx.x * kFoldTilesPerWG + u * kWavesF + w;
+    if (tile >= kFTiles) break;
+    const int f0 = tile * 16;
+    // this lane's feature row (A operand) and its factors
+    const uint16_t ab = kFoldPairs.ab[f0 + l16];
+    const int fa = ab & 0xFF, fb = ab >> 8;
+    const float wgt = fa == fb ? 1.0f : 1.41421356237309504880f;
+    // accumulators: rows 4*q4 + i of the tile, column 16*nt + l16 (nt = 4: s in column 0)
+    f32x4 acc[5];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nt][i] = Hn[(size_t)(f0 + 4 * q4 + i) * kFD + 16 * nt + l16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[4][i] = l16 == 0 ? sn[f0 + 4 * q4 + i] : 0.0f;
+    for (int ks = 0; ks < R / 32; ++ks) {
+      const float4* pa = reinterpret_cast<const float4*>(&kt[fa][32 * ks + 8 * q4]);
+      const float4* pb = reinterpret_cast<const float4*>(&kt[fb][32 * ks + 8 * q4]);
+      const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+      const float p[8] = {a0.x * b0.x * wgt, a0.y * b0.y * wgt, a0.z * b0.z * wgt, a0.w * b0.w * wgt,
+                          a1.x * b1.x * wgt, a1.y * b1.y * wgt, a1.z * b1.z * wgt, a1.w * b1.w * wgt};
+      bf16x8 A0, A1, A2;
+      split3_8(p, A0, A1, A2);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&vt[16 * nt + l16][32 * ks + 8 * q4]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc[nt], 0, 0, 0);
+      }
+      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, ones, acc[4], 0, 0, 0);
+      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, ones, acc[4], 0, 0, 0);
+      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, ones, acc[4], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Hn[(size_t)(f0 + 4 * q4 + i) * kFD + 16 * nt + l16] = acc[nt][i];
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sn[f0 + 4 * q4 + i] = acc[4][i];
+    }
+  }
 }
 
 // Output of 16 queries [t0, t0+16) of a block whose window starts at f.
@@ -405,8 +531,14 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
                            w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,
                            kCStride, a.trace, (size_t)a.cache_size, b, nblocks);
         KLA_CHECK();
-        hipLaunchKernelGGL((hyb_fold_kernel<DQK, DV, Tin>), dim3(S, N), dim3(kThreads), 0, st,
-                           w.H, w.s, k, v, a.T, w.rejected, kCStride, n_cand - a.cache_size, Fs);
+        if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
+          hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFTiles + kFoldTilesPerWG - 1) / kFoldTilesPerWG, N),
+                             dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.rejected, kCStride,
+                             n_cand - a.cache_size);
+        } else {
+          hipLaunchKernelGGL((hyb_fold_kernel<DQK, DV, Tin>), dim3(S, N), dim3(kThreads), 0, st,
+                             w.H, w.s, k, v, a.T, w.rejected, kCStride, n_cand - a.cache_size, Fs);
+        }
         KLA_CHECK();
         n_cache = a.cache_size;
       }
