@@ -214,6 +214,16 @@ __device__ __forceinline__ void split3_8(const float (&x)[8], bf16x8& p0, bf16x8
   }
 }
 
+// x ~ p0 + p1 with p0 = bf16(x), p1 = bf16(x - p0): 16 significant bits.
+__device__ __forceinline__ void split2_8(const float (&x)[8], bf16x8& p0, bf16x8& p1) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 a = (__bf16)x[j];
+    p0[j] = a;
+    p1[j] = (__bf16)(x[j] - (float)a);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restrict__ H, float* __restrict__ s,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v, int T,
@@ -297,6 +307,252 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
     if (l16 == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sn[f0 + 4 * q4 + i] = acc[4][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- matrix-core readout (d = 64, bf16 in)
+//
+// One work-group per (head, 64 queries of a block); wave w owns queries
+// t0 + 16 w .. + 15. Softmax keys are the cache entries and then the window
+// [f, t]. Scores come from S^T = K Q^T on bf16 MFMA (exact products, float32
+// sums): lane (l16, q4) holds the scores of query l16 against keys 4 q4 + i
+// of each 16-key half. Pass 1 finds each query's maximum m (clamped at 0, as
+// the joint normalisation divides the linear terms by e^m too); pass 2 forms
+// P = e^(tau s - m) and P [V | 1] on MFMA (P in two bf16 pieces), taking P's k-slots in the order the
+// scores sit in the lanes (keys 4 q4 + j, then 16 + 4 q4 + j) and V in the
+// same order. The linear term phi(q)^T [H | s] streams the state through LDS
+// as two-piece bf16 B fragments (hi*hi + hi*lo + lo*hi with two-piece phi(q)). Output column 4 l16 + nt sits in n-tile nt of lane
+// (l16, q4), rows 4 q4 + i.
+constexpr int kRQ = 64;       // queries per work-group
+constexpr int kRK = 32;       // keys per tile
+constexpr int kRF = 64;       // features per staged state tile (two k-steps)
+
+struct ReadoutLds {
+  uint16_t ks[kRK][kFD + 8];            // key rows of the tile (bf16)
+  uint16_t vt[kFD][kRK + 8];            // value tile, transposed (bf16)
+  float qf[kRQ][kFD + 1];               // query rows (float32) for phi(q)
+  uint16_t tab[kFPhi];                  // feature pairs
+  uint4 hf[2][kRF / 32][5][64];         // state B fragments (hi, lo pieces) of the staged feature tile
+  float mq[kRQ];                        // per-query maximum
+  float den[kRQ];                       // per-query denominator
+};
+
+template <typename Tout>
+__global__ __launch_bounds__(kThreads) void hyb_readout_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    Tout* __restrict__ o, int T, const float* __restrict__ H, const float* __restrict__ s,
+    const int32_t* __restrict__ cache, int cstride, int n_cache, int t_begin, int t_end, int f,
+    float scale, float eps) {
+  __shared__ __align__(16) ReadoutLds sh;
+  const int n = blockIdx.y;
+  const int t0 = t_begin + kRQ * blockIdx.x;
+  const int tq_end = min(t_end, t0 + kRQ);       // queries [t0, tq_end)
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int tw = t0 + 16 * w;                     // this wave's first query
+  const int my_t = tw + l16;                      // query of lane (scores layout)
+  const size_t base = (size_t)n * T * kFD;
+  const int32_t* cn = cache + (size_t)n * cstride;
+  // keys: cache, then window tokens f .. tq_end - 1
+  const int n_keys = n_cache + (tq_end - f);
+
+  for (int i = tid; i < kFPhi; i += kThreads) sh.tab[i] = kFoldPairs.ab[i];
+  for (int i = tid; i < kRQ * (kFD / 4); i += kThreads) {
+    const int r = i / (kFD / 4), d4 = i % (kFD / 4);
+    uint2 u = make_uint2(0, 0);
+    if (t0 + r < tq_end) u = *reinterpret_cast<const uint2*>(q + base + (size_t)(t0 + r) * kFD + 4 * d4);
+    sh.qf[r][4 * d4 + 0] = __uint_as_float(u.x << 16);
+    sh.qf[r][4 * d4 + 1] = __uint_as_float(u.x & 0xFFFF0000u);
+    sh.qf[r][4 * d4 + 2] = __uint_as_float(u.y << 16);
+    sh.qf[r][4 * d4 + 3] = __uint_as_float(u.y & 0xFFFF0000u);
+  }
+  // Q^T as the B operand of S^T = K Q^T: lane (l16 = query, q4) holds dims 8 q4 .. + 7 (+ 32 ks)
+  bf16x8 qb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (my_t < tq_end) u = *reinterpret_cast<const uint4*>(q + base + (size_t)my_t * kFD + 32 * ks + 8 * q4);
+    qb[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+
+  auto key_token = [&](int j) { return j < n_cache ? cn[j] : f + (j - n_cache); };
+  // stage key (and value) rows of tile j0 .. j0 + 31; 256 threads, one 16-byte piece each
+  auto stage = [&](int j0, bool with_v) {
+    const int r = tid >> 3, c8 = tid & 7;
+    uint4 ku = make_uint4(0, 0, 0, 0), vu = ku;
+    if (j0 + r < n_keys) {
+      const size_t row = base + (size_t)key_token(j0 + r) * kFD + 8 * c8;
+      ku = *reinterpret_cast<const uint4*>(k + row);
+      if (with_v) vu = *reinterpret_cast<const uint4*>(v + row);
+    }
+    *reinterpret_cast<uint4*>(&sh.ks[r][8 * c8]) = ku;
+    if (with_v) {
+      const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sh.vt[8 * c8 + 2 * e][r] = (uint16_t)(vw[e] & 0xFFFF);
+        sh.vt[8 * c8 + 2 * e + 1][r] = (uint16_t)(vw[e] >> 16);
+      }
+    }
+  };
+  // scores of this wave's queries against the staged tile: sc[h][i] = key 16 h + 4 q4 + i
+  auto scores = [&](int j0, float (&sc)[2][4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sh.ks[16 * h + l16][32 * ks + 8 * q4]);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], c, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 16 * h + 4 * q4 + i;
+        // cache keys precede every query; window keys are causal
+        const bool ok = j < n_keys && my_t < tq_end && (j < n_cache || f + (j - n_cache) <= my_t);
+        sc[h][i] = ok ? scale * c[i] : -INFINITY;
+      }
+    }
+  };
+  const int wave_keys = min(n_keys, n_cache + (min(tq_end, tw + 16) - f));  // keys any query of the wave sees
+
+  // ---- pass 1: per-query maximum
+  float mx = 0.0f;  // never below 0
+  for (int j0 = 0; j0 < n_keys; j0 += kRK) {
+    __syncthreads();
+    stage(j0, false);
+    __syncthreads();
+    if (j0 < wave_keys) {
+      float sc[2][4];
+      scores(j0, sc);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[h][i]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (q4 == 0) sh.mq[16 * w + l16] = mx;
+
+  // ---- pass 2: P [V | 1]
+  bf16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
+  f32x4 acc[5];
+#pragma unroll
+  for (int nt = 0; nt < 5; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < n_keys; j0 += kRK) {
+    __syncthreads();
+    stage(j0, true);
+    __syncthreads();
+    if (j0 < wave_keys) {
+      float sc[2][4];
+      scores(j0, sc);
+      // P = p0 + p1 (two bf16 pieces, 16 significant bits); v and 1 are exact in bf16
+      float pf[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pf[4 * h + i] = __expf(sc[h][i] - mx);
+      bf16x8 p0, p1;
+      split2_8(pf, p0, p1);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(&sh.vt[4 * l16 + nt][4 * q4]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&sh.vt[4 * l16 + nt][16 + 4 * q4]);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, b, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, b, acc[nt], 0, 0, 0);
+      }
+      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, ones, acc[4], 0, 0, 0);
+      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, ones, acc[4], 0, 0, 0);
+    }
+  }
+
+  // ---- linear readout phi(q)^T [H | s], state staged kRF features at a time
+  f32x4 lin[5];
+#pragma unroll
+  for (int nt = 0; nt < 5; ++nt) lin[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* Hn = H + (size_t)n * kFPhi * kFD;
+  const float* sn = s + (size_t)n * kFPhi;
+  const float* qrow = sh.qf[16 * w + l16];
+  for (int g0 = 0; g0 < kFPhi; g0 += kRF) {
+    __syncthreads();
+    // fragments: for k-step kk, n-tile nt and lane L = (l16', q4'), the 8 rows
+    // g0 + 32 kk + 8 q4' + j at column 4 l16' + nt; n-tile 4 holds s (lane l16' == 0)
+    for (int i = tid; i < (kRF / 32) * 5 * 64; i += kThreads) {
+      const int L = i & 63;
+      const int nt = (i >> 6) % 5;
+      const int kk = (i >> 6) / 5;
+      const int lq = L >> 4, ll = L & 15;
+      const int r0 = g0 + 32 * kk + 8 * lq;
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[j] = 0.0f;
+        if (r0 + j < kFPhi) x[j] = nt < 4 ? Hn[(size_t)(r0 + j) * kFD + 4 * ll + nt] : (ll == 0 ? sn[r0 + j] : 0.0f);
+      }
+      bf16x8 b0, b1;
+      split2_8(x, b0, b1);
+      sh.hf[0][kk][nt][L] = __builtin_bit_cast(uint4, b0);
+      sh.hf[1][kk][nt][L] = __builtin_bit_cast(uint4, b1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kRF / 32; ++kk) {
+      const int fr = g0 + 32 * kk + 8 * q4;
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float x = 0.0f;
+        if (fr + j < kFPhi) {
+          const uint16_t ab = sh.tab[fr + j];
+          const int a = ab & 0xFF, bb = ab >> 8;
+          x = qrow[a] * qrow[bb] * (a == bb ? 1.0f : 1.41421356237309504880f);
+        }
+        p[j] = x;
+      }
+      // phi(q) and the state in two bf16 pieces each: hi*hi + hi*lo + lo*hi
+      bf16x8 A0, A1;
+      split2_8(p, A0, A1);
+#pragma unroll
+      for (int nt = 0; nt < 5; ++nt) {
+        const bf16x8 B0 = __builtin_bit_cast(bf16x8, sh.hf[0][kk][nt][lane]);
+        const bf16x8 B1 = __builtin_bit_cast(bf16x8, sh.hf[1][kk][nt][lane]);
+        lin[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, lin[nt], 0, 0, 0);
+        lin[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B1, lin[nt], 0, 0, 0);
+        lin[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, lin[nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- combine: rows 4 q4 + i of the wave, columns 4 l16 + nt
+  __syncthreads();
+  if (l16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = __expf(-sh.mq[16 * w + 4 * q4 + i]);
+      sh.den[16 * w + 4 * q4 + i] = acc[4][i] + e * (lin[4][i] + eps);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * q4 + i;
+    const int t = t0 + r;
+    if (t < tq_end) {
+      const float e = __expf(-sh.mq[r]);
+      const float den = sh.den[r];
+      const float inv = den != 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        Elem<Tout>::store(o, base + (size_t)t * kFD + 4 * l16 + nt,
+                          den != 0.0f ? (acc[nt][i] + e * lin[nt][i]) * inv : 0.0f);
     }
   }
 }
@@ -544,9 +800,15 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
       }
     }
     f_prev = f;
-    hipLaunchKernelGGL((hyb_readout_kernel<DQK, DV, Tin, Tout>), dim3((b1 - b0 + 15) / 16, N),
-                       dim3(kThreads), 0, st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride,
-                       n_cache, b0, b1, f, a.scale, a.eps);
+    if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
+      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N), dim3(kThreads), 0,
+                         st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride, n_cache, b0, b1, f, a.scale,
+                         a.eps);
+    } else {
+      hipLaunchKernelGGL((hyb_readout_kernel<DQK, DV, Tin, Tout>), dim3((b1 - b0 + 15) / 16, N),
+                         dim3(kThreads), 0, st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride,
+                         n_cache, b0, b1, f, a.scale, a.eps);
+    }
     KLA_CHECK();
   }
   if (a.cache_T && a.cache_size > 0) {
