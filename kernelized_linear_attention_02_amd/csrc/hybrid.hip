@@ -324,9 +324,13 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
 // same order. The linear term phi(q)^T [H | s] streams the state through LDS
 // as two-piece bf16 B fragments (hi*hi + hi*lo + lo*hi with two-piece phi(q)). Output column 4 l16 + nt sits in n-tile nt of lane
 // (l16, q4), rows 4 q4 + i.
-constexpr int kRQ = 64;       // queries per work-group
+constexpr int kRW = 4;        // waves (16 queries each) per work-group
+constexpr int kRT = 64 * kRW; // threads
+constexpr int kRQ = 16 * kRW; // queries per work-group
 constexpr int kRK = 32;       // keys per tile
 constexpr int kRF = 64;       // features per staged state tile (two k-steps)
+constexpr int kKVP = kRK * 8 / kRT;          // 16-byte key/value pieces per thread and tile
+constexpr int kHP = kRF * (kFD / 4) / kRT;   // float4 state pieces per thread and tile
 
 struct ReadoutLds {
   uint16_t ks[kRK][kFD + 8];            // key rows of the tile (bf16)
@@ -339,7 +343,7 @@ struct ReadoutLds {
 };
 
 template <typename Tout>
-__global__ __launch_bounds__(kThreads) void hyb_readout_mfma_kernel(
+__global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     Tout* __restrict__ o, int T, const float* __restrict__ H, const float* __restrict__ s,
     const int32_t* __restrict__ cache, int cstride, int n_cache, int t_begin, int t_end, int f,
@@ -360,8 +364,8 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_mfma_kernel(
   // keys: cache, then window tokens f .. tq_end - 1
   const int n_keys = n_cache + (tq_end - f);
 
-  for (int i = tid; i < kFPhi; i += kThreads) sh.tab[i] = kFoldPairs.ab[i];
-  for (int i = tid; i < kRQ * (kFD / 4); i += kThreads) {
+  for (int i = tid; i < kFPhi; i += kRT) sh.tab[i] = kFoldPairs.ab[i];
+  for (int i = tid; i < kRQ * (kFD / 4); i += kRT) {
     const int r = i / (kFD / 4), d4 = i % (kFD / 4);
     uint2 u = make_uint2(0, 0);
     if (t0 + r < tq_end) u = *reinterpret_cast<const uint2*>(q + base + (size_t)(t0 + r) * kFD + 4 * d4);
@@ -380,22 +384,33 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_mfma_kernel(
   }
 
   auto key_token = [&](int j) { return j < n_cache ? cn[j] : f + (j - n_cache); };
-  // stage key (and value) rows of tile j0 .. j0 + 31; 256 threads, one 16-byte piece each
-  auto stage = [&](int j0, bool with_v) {
-    const int r = tid >> 3, c8 = tid & 7;
-    uint4 ku = make_uint4(0, 0, 0, 0), vu = ku;
-    if (j0 + r < n_keys) {
-      const size_t row = base + (size_t)key_token(j0 + r) * kFD + 8 * c8;
-      ku = *reinterpret_cast<const uint4*>(k + row);
-      if (with_v) vu = *reinterpret_cast<const uint4*>(v + row);
-    }
-    *reinterpret_cast<uint4*>(&sh.ks[r][8 * c8]) = ku;
-    if (with_v) {
-      const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+  // key (and value) rows of tile j0 .. j0 + 31 in 16-byte pieces (row p / 8, piece p % 8),
+  // loaded into registers one tile ahead, then stored to LDS
+  auto load_kv = [&](int j0, bool with_v, uint4 (&ku)[kKVP], uint4 (&vu)[kKVP]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sh.vt[8 * c8 + 2 * e][r] = (uint16_t)(vw[e] & 0xFFFF);
-        sh.vt[8 * c8 + 2 * e + 1][r] = (uint16_t)(vw[e] >> 16);
+    for (int e = 0; e < kKVP; ++e) {
+      const int pidx = tid + kRT * e, sr = pidx >> 3, sc8 = pidx & 7;
+      ku[e] = make_uint4(0, 0, 0, 0);
+      vu[e] = ku[e];
+      if (j0 + sr < n_keys) {
+        const size_t row = base + (size_t)key_token(j0 + sr) * kFD + 8 * sc8;
+        ku[e] = *reinterpret_cast<const uint4*>(k + row);
+        if (with_v) vu[e] = *reinterpret_cast<const uint4*>(v + row);
+      }
+    }
+  };
+  auto store_kv = [&](bool with_v, const uint4 (&ku)[kKVP], const uint4 (&vu)[kKVP]) {
+#pragma unroll
+    for (int e = 0; e < kKVP; ++e) {
+      const int pidx = tid + kRT * e, sr = pidx >> 3, sc8 = pidx & 7;
+      *reinterpret_cast<uint4*>(&sh.ks[sr][8 * sc8]) = ku[e];
+      if (with_v) {
+        const uint32_t vw[4] = {vu[e].x, vu[e].y, vu[e].z, vu[e].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          sh.vt[8 * sc8 + 2 * c][sr] = (uint16_t)(vw[c] & 0xFFFF);
+          sh.vt[8 * sc8 + 2 * c + 1][sr] = (uint16_t)(vw[c] >> 16);
+        }
       }
     }
   };
@@ -422,10 +437,13 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_mfma_kernel(
 
   // ---- pass 1: per-query maximum
   float mx = 0.0f;  // never below 0
+  uint4 kpre[kKVP], vpre[kKVP];
+  load_kv(0, false, kpre, vpre);
   for (int j0 = 0; j0 < n_keys; j0 += kRK) {
     __syncthreads();
-    stage(j0, false);
+    store_kv(false, kpre, vpre);
     __syncthreads();
+    if (j0 + kRK < n_keys) load_kv(j0 + kRK, false, kpre, vpre);
     if (j0 < wave_keys) {
       float sc[2][4];
       scores(j0, sc);
@@ -446,10 +464,12 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_mfma_kernel(
   f32x4 acc[5];
 #pragma unroll
   for (int nt = 0; nt < 5; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load_kv(0, true, kpre, vpre);
   for (int j0 = 0; j0 < n_keys; j0 += kRK) {
     __syncthreads();
-    stage(j0, true);
+    store_kv(true, kpre, vpre);
     __syncthreads();
+    if (j0 + kRK < n_keys) load_kv(j0 + kRK, true, kpre, vpre);
     if (j0 < wave_keys) {
       float sc[2][4];
       scores(j0, sc);
@@ -481,28 +501,55 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_mfma_kernel(
   const float* Hn = H + (size_t)n * kFPhi * kFD;
   const float* sn = s + (size_t)n * kFPhi;
   const float* qrow = sh.qf[16 * w + l16];
+  // state rows g0 .. g0 + 63 in float4 pieces p = tid + kRT m (row p / 16, columns 4 (p % 16) .. + 3),
+  // one tile ahead; row r, column 4 c4 + nt goes to fragment (k-step r / 32, n-tile nt,
+  // lane 16 ((r % 32) / 8) + c4, element r % 8); the normaliser fragment holds s in lane column 0
+  for (int i = tid; i < 2 * (kRF / 32) * 64; i += kRT) {
+    // zero the normaliser fragments once (only lane column 0 is written later)
+    const int pc = i / ((kRF / 32) * 64), rest = i % ((kRF / 32) * 64);
+    sh.hf[pc][rest / 64][4][rest % 64] = make_uint4(0, 0, 0, 0);
+  }
+  float4 hpre[kHP];
+  float spre[kHP];
+  auto load_h = [&](int g0) {
+#pragma unroll
+    for (int m = 0; m < kHP; ++m) {
+      const int pidx = tid + kRT * m;
+      const int r = g0 + (pidx >> 4), c4 = pidx & 15;
+      hpre[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+      spre[m] = 0.0f;
+      if (r < kFPhi) {
+        hpre[m] = *reinterpret_cast<const float4*>(Hn + (size_t)r * kFD + 4 * c4);
+        if (c4 == 0) spre[m] = sn[r];
+      }
+    }
+  };
+  auto put = [&](int pc, int kk, int nt, int L, int j, __bf16 x) {
+    reinterpret_cast<__bf16*>(&sh.hf[pc][kk][nt][L])[j] = x;
+  };
+  load_h(0);
   for (int g0 = 0; g0 < kFPhi; g0 += kRF) {
     __syncthreads();
-    // fragments: for k-step kk, n-tile nt and lane L = (l16', q4'), the 8 rows
-    // g0 + 32 kk + 8 q4' + j at column 4 l16' + nt; n-tile 4 holds s (lane l16' == 0)
-    for (int i = tid; i < (kRF / 32) * 5 * 64; i += kThreads) {
-      const int L = i & 63;
-      const int nt = (i >> 6) % 5;
-      const int kk = (i >> 6) / 5;
-      const int lq = L >> 4, ll = L & 15;
-      const int r0 = g0 + 32 * kk + 8 * lq;
-      float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        x[j] = 0.0f;
-        if (r0 + j < kFPhi) x[j] = nt < 4 ? Hn[(size_t)(r0 + j) * kFD + 4 * ll + nt] : (ll == 0 ? sn[r0 + j] : 0.0f);
+    for (int m = 0; m < kHP; ++m) {
+      const int pidx = tid + kRT * m;
+      const int r = pidx >> 4, c4 = pidx & 15;
+      const int kk = r >> 5, L = 16 * ((r & 31) >> 3) + c4, j = r & 7;
+      const float xs[4] = {hpre[m].x, hpre[m].y, hpre[m].z, hpre[m].w};
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const __bf16 a = (__bf16)xs[nt];
+        put(0, kk, nt, L, j, a);
+        put(1, kk, nt, L, j, (__bf16)(xs[nt] - (float)a));
       }
-      bf16x8 b0, b1;
-      split2_8(x, b0, b1);
-      sh.hf[0][kk][nt][L] = __builtin_bit_cast(uint4, b0);
-      sh.hf[1][kk][nt][L] = __builtin_bit_cast(uint4, b1);
+      if (c4 == 0) {
+        const __bf16 a = (__bf16)spre[m];
+        put(0, kk, 4, L, j, a);
+        put(1, kk, 4, L, j, (__bf16)(spre[m] - (float)a));
+      }
     }
     __syncthreads();
+    if (g0 + kRF < kFPhi) load_h(g0 + kRF);
 #pragma unroll
     for (int kk = 0; kk < kRF / 32; ++kk) {
       const int fr = g0 + 32 * kk + 8 * q4;
@@ -801,7 +848,7 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
     }
     f_prev = f;
     if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
-      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N), dim3(kThreads), 0,
+      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N), dim3(kRT), 0,
                          st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride, n_cache, b0, b1, f, a.scale,
                          a.eps);
     } else {
