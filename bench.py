@@ -177,7 +177,8 @@ def bench_decode(torch, K, S, steps_loop, reps):
         workload="decode_sre_4096x128", N=N, steps=nsteps, step_ms=step_ms,
         steps_per_s=1e3 / step_ms, kernel_ms=kern_ms,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=achieved / PEAK_HBM_GBS, traffic=None,
+                      frac=achieved / PEAK_HBM_GBS,
+                      traffic=measured_traffic("decode_fused.hip", "decode_sre_kernel_decode_sre_4096x128_traffic.md"),
                       kernel="decode step + SRE + top-k (fused)", bytes_per_launch=step_bytes),
     )
 
