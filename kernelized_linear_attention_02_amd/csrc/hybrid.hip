@@ -179,17 +179,21 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_kernel(float* __restrict__ 
 // ---------------------------------------------------------------- matrix-core fold (d = 64, bf16 in)
 //
 // [H | s] += phi(K_r)^T [V_r | 1] over the rejected tokens, on the matrix
-// cores: each wave takes 16-feature tiles (canonical order) and keeps a tile
-// of [H | s] in MFMA accumulators seeded with the stored state. The feature
-// products k_a k_b (times sqrt(2) off the diagonal) are exact float32 values
-// split into three bf16 pieces p0 + p1 + p2 = p; v is bf16 on input, so every
-// MFMA product is exact and the sums are float32, as in a float32 fold.
+// cores: each wave takes 32-feature k-steps (canonical order, two 16-row
+// tiles) and keeps them in MFMA accumulators seeded with the stored state.
+// The feature products k_a k_b (times sqrt(2) off the diagonal) are exact
+// float32 values split into three bf16 pieces p0 + p1 + p2 = p; v is bf16 on
+// input, so every MFMA product is exact and the sums are float32, as in a
+// float32 fold. Output column n-tile nt of lane (l16, q4) is state column
+// 4 l16 + nt. Besides the float32 state, the fold writes it as readout B
+// fragments (two bf16 pieces): fragment (k-step ks, n-tile nt) of lane
+// (l16, q4) holds rows 32 ks + 4 q4 + i and 32 ks + 16 + 4 q4 + i (i < 4) of
+// column 4 l16 + nt - exactly the lane's accumulators of the two tiles - and
+// n-tile 4 holds s in lane column 0.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFD = 64;
 constexpr int kFPhi = kFD * (kFD + 1) / 2;   // 2080
-constexpr int kFTiles = kFPhi / 16;          // 130
-constexpr int kFoldTilesPerWG = 8;           // two per wave
 constexpr int kFoldRows = 128;               // rejected tokens per call, at most
 
 struct FoldPairs {
@@ -224,7 +228,16 @@ __device__ __forceinline__ void split2_8(const float (&x)[8], bf16x8& p0, bf16x8
   }
 }
 
+constexpr int kFKS = kFPhi / 32;             // 65 k-steps
+constexpr int kFoldKsPerWG = 8;              // two per wave
+
+// index of fragment (n, ks, piece, nt, lane) in uint4 units
+__device__ __forceinline__ size_t hf_index(int n, int ks, int pc, int nt, int lane) {
+  return ((((size_t)n * kFKS + ks) * 2 + pc) * 5 + nt) * 64 + lane;
+}
+
 __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restrict__ H, float* __restrict__ s,
+                                                               uint4* __restrict__ HF,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v, int T,
                                                                const int32_t* __restrict__ rejected,
@@ -265,48 +278,69 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
   float* Hn = H + (size_t)n * kFPhi * kFD;
   float* sn = s + (size_t)n * kFPhi;
 #pragma unroll 1
-  for (int u = 0; u < kFoldTilesPerWG / kWavesF; ++u) {
-    const int tile = blockIdx.x * kFoldTilesPerWG + u * kWavesF + w;
-    if (tile >= kFTiles) break;
-    const int f0 = tile * 16;
-    // this lane's feature row (A operand) and its factors
-    const uint16_t ab = kFoldPairs.ab[f0 + l16];
-    const int fa = ab & 0xFF, fb = ab >> 8;
-    const float wgt = fa == fb ? 1.0f : 1.41421356237309504880f;
-    // accumulators: rows 4*q4 + i of the tile, column 16*nt + l16 (nt = 4: s in column 0)
-    f32x4 acc[5];
+  for (int u = 0; u < kFoldKsPerWG / kWavesF; ++u) {
+    const int ks = blockIdx.x * kFoldKsPerWG + u * kWavesF + w;
+    if (ks >= kFKS) break;
+    f32x4 acc[2][5];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int t = 0; t < 2; ++t) {
+      const int f0 = 32 * ks + 16 * t;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nt][i] = Hn[(size_t)(f0 + 4 * q4 + i) * kFD + 16 * nt + l16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[4][i] = l16 == 0 ? sn[f0 + 4 * q4 + i] : 0.0f;
-    for (int ks = 0; ks < R / 32; ++ks) {
-      const float4* pa = reinterpret_cast<const float4*>(&kt[fa][32 * ks + 8 * q4]);
-      const float4* pb = reinterpret_cast<const float4*>(&kt[fb][32 * ks + 8 * q4]);
-      const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
-      const float p[8] = {a0.x * b0.x * wgt, a0.y * b0.y * wgt, a0.z * b0.z * wgt, a0.w * b0.w * wgt,
-                          a1.x * b1.x * wgt, a1.y * b1.y * wgt, a1.z * b1.z * wgt, a1.w * b1.w * wgt};
-      bf16x8 A0, A1, A2;
-      split3_8(p, A0, A1, A2);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&vt[16 * nt + l16][32 * ks + 8 * q4]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc[nt], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const float4 h = *reinterpret_cast<const float4*>(Hn + (size_t)(f0 + 4 * q4 + i) * kFD + 4 * l16);
+        acc[t][0][i] = h.x;
+        acc[t][1][i] = h.y;
+        acc[t][2][i] = h.z;
+        acc[t][3][i] = h.w;
+        acc[t][4][i] = l16 == 0 ? sn[f0 + 4 * q4 + i] : 0.0f;
       }
-      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, ones, acc[4], 0, 0, 0);
-      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, ones, acc[4], 0, 0, 0);
-      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, ones, acc[4], 0, 0, 0);
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int t = 0; t < 2; ++t) {
+      // this lane's feature row (A operand) and its factors
+      const uint16_t ab = kFoldPairs.ab[32 * ks + 16 * t + l16];
+      const int fa = ab & 0xFF, fb = ab >> 8;
+      const float wgt = fa == fb ? 1.0f : 1.41421356237309504880f;
+      for (int kk = 0; kk < R / 32; ++kk) {
+        const float4* pa = reinterpret_cast<const float4*>(&kt[fa][32 * kk + 8 * q4]);
+        const float4* pb = reinterpret_cast<const float4*>(&kt[fb][32 * kk + 8 * q4]);
+        const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+        const float p[8] = {a0.x * b0.x * wgt, a0.y * b0.y * wgt, a0.z * b0.z * wgt, a0.w * b0.w * wgt,
+                            a1.x * b1.x * wgt, a1.y * b1.y * wgt, a1.z * b1.z * wgt, a1.w * b1.w * wgt};
+        bf16x8 A0, A1, A2;
+        split3_8(p, A0, A1, A2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Hn[(size_t)(f0 + 4 * q4 + i) * kFD + 16 * nt + l16] = acc[nt][i];
-    if (l16 == 0) {
+        for (int nt = 0; nt < 4; ++nt) {
+          // value column 4 l16 + nt of the 8 tokens 32 kk + 8 q4 + j
+          const bf16x8 B = *reinterpret_cast<const bf16x8*>(&vt[4 * l16 + nt][32 * kk + 8 * q4]);
+          acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[t][nt], 0, 0, 0);
+          acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[t][nt], 0, 0, 0);
+          acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc[t][nt], 0, 0, 0);
+        }
+        acc[t][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, ones, acc[t][4], 0, 0, 0);
+        acc[t][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, ones, acc[t][4], 0, 0, 0);
+        acc[t][4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, ones, acc[t][4], 0, 0, 0);
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sn[f0 + 4 * q4 + i] = acc[4][i];
+    for (int t = 0; t < 2; ++t) {
+      const int f0 = 32 * ks + 16 * t;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<float4*>(Hn + (size_t)(f0 + 4 * q4 + i) * kFD + 4 * l16) =
+            make_float4(acc[t][0][i], acc[t][1][i], acc[t][2][i], acc[t][3][i]);
+        if (l16 == 0) sn[f0 + 4 * q4 + i] = acc[t][4][i];
+      }
+    }
+    // readout fragments of this k-step
+#pragma unroll
+    for (int nt = 0; nt < 5; ++nt) {
+      const float x[8] = {acc[0][nt][0], acc[0][nt][1], acc[0][nt][2], acc[0][nt][3],
+                          acc[1][nt][0], acc[1][nt][1], acc[1][nt][2], acc[1][nt][3]};
+      bf16x8 p0, p1;
+      split2_8(x, p0, p1);
+      HF[hf_index(n, ks, 0, nt, lane)] = __builtin_bit_cast(uint4, p0);
+      HF[hf_index(n, ks, 1, nt, lane)] = __builtin_bit_cast(uint4, p1);
     }
   }
 }
@@ -314,30 +348,30 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
 // ---------------------------------------------------------------- matrix-core readout (d = 64, bf16 in)
 //
 // One work-group per (head, 64 queries of a block); wave w owns queries
-// t0 + 16 w .. + 15. Softmax keys are the cache entries and then the window
-// [f, t]. Scores come from S^T = K Q^T on bf16 MFMA (exact products, float32
-// sums): lane (l16, q4) holds the scores of query l16 against keys 4 q4 + i
-// of each 16-key half. Pass 1 finds each query's maximum m (clamped at 0, as
-// the joint normalisation divides the linear terms by e^m too); pass 2 forms
-// P = e^(tau s - m) and P [V | 1] on MFMA (P in two bf16 pieces), taking P's k-slots in the order the
-// scores sit in the lanes (keys 4 q4 + j, then 16 + 4 q4 + j) and V in the
-// same order. The linear term phi(q)^T [H | s] streams the state through LDS
-// as two-piece bf16 B fragments (hi*hi + hi*lo + lo*hi with two-piece phi(q)). Output column 4 l16 + nt sits in n-tile nt of lane
-// (l16, q4), rows 4 q4 + i.
+// t0 + 16 w .. + 15 for the softmax part. Softmax keys are the cache entries
+// and then the window [f, t]. Scores come from S^T = K Q^T on bf16 MFMA
+// (exact products, float32 sums): lane (l16, q4) holds the scores of query
+// l16 against keys 4 q4 + i of each 16-key half. Pass 1 finds each query's
+// maximum m (clamped at 0, since the joint normalisation divides the linear
+// terms by e^m too); pass 2 forms P = e^(tau s - m) in two bf16 pieces and
+// P [V | 1], taking P's k-slots in the order the scores sit in the lanes
+// (keys 4 q4 + j, then 16 + 4 q4 + j) and V in the same order. Key and value
+// fragments are loaded straight from memory, one tile ahead; the softmax
+// part needs no LDS and no barrier.
+// The linear term phi(q)^T [H | s] reads the state fragments the fold wrote
+// (two bf16 pieces, hi*hi + hi*lo + lo*hi with two-piece phi(q)); wave w
+// takes the k-steps ks = w mod 4 for all 64 queries and the four partial
+// sums meet in LDS at the end. Output column 4 l16 + nt sits in n-tile nt of
+// lane (l16, q4), rows 4 q4 + i.
 constexpr int kRW = 4;        // waves (16 queries each) per work-group
 constexpr int kRT = 64 * kRW; // threads
 constexpr int kRQ = 16 * kRW; // queries per work-group
 constexpr int kRK = 32;       // keys per tile
-constexpr int kRF = 64;       // features per staged state tile (two k-steps)
-constexpr int kKVP = kRK * 8 / kRT;          // 16-byte key/value pieces per thread and tile
-constexpr int kHP = kRF * (kFD / 4) / kRT;   // float4 state pieces per thread and tile
 
 struct ReadoutLds {
-  uint16_t ks[kRK][kFD + 8];            // key rows of the tile (bf16)
-  uint16_t vt[kFD][kRK + 8];            // value tile, transposed (bf16)
   float qf[kRQ][kFD + 1];               // query rows (float32) for phi(q)
   uint16_t tab[kFPhi];                  // feature pairs
-  uint4 hf[2][kRF / 32][5][64];         // state B fragments (hi, lo pieces) of the staged feature tile
+  float4 red[kRW][kRW][5][64];          // linear partials: [source wave][token tile][n-tile][lane]
   float mq[kRQ];                        // per-query maximum
   float den[kRQ];                       // per-query denominator
 };
@@ -345,9 +379,8 @@ struct ReadoutLds {
 template <typename Tout>
 __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    Tout* __restrict__ o, int T, const float* __restrict__ H, const float* __restrict__ s,
-    const int32_t* __restrict__ cache, int cstride, int n_cache, int t_begin, int t_end, int f,
-    float scale, float eps) {
+    Tout* __restrict__ o, int T, const uint4* __restrict__ HF, const int32_t* __restrict__ cache,
+    int cstride, int n_cache, int t_begin, int t_end, int f, float scale, float eps) {
   __shared__ __align__(16) ReadoutLds sh;
   const int n = blockIdx.y;
   const int t0 = t_begin + kRQ * blockIdx.x;
@@ -382,48 +415,40 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
     if (my_t < tq_end) u = *reinterpret_cast<const uint4*>(q + base + (size_t)my_t * kFD + 32 * ks + 8 * q4);
     qb[ks] = __builtin_bit_cast(bf16x8, u);
   }
+  __syncthreads();
 
   auto key_token = [&](int j) { return j < n_cache ? cn[j] : f + (j - n_cache); };
-  // key (and value) rows of tile j0 .. j0 + 31 in 16-byte pieces (row p / 8, piece p % 8),
-  // loaded into registers one tile ahead, then stored to LDS
-  auto load_kv = [&](int j0, bool with_v, uint4 (&ku)[kKVP], uint4 (&vu)[kKVP]) {
+  const int wave_keys = max(0, min(n_keys, n_cache + (min(tq_end, tw + 16) - f)));
+
+  // key fragments of tile j0: ka[h][ks] = key j0 + 16 h + l16, dims 32 ks + 8 q4 .. + 7
+  auto load_k = [&](int j0, uint4 (&ka)[2][2]) {
 #pragma unroll
-    for (int e = 0; e < kKVP; ++e) {
-      const int pidx = tid + kRT * e, sr = pidx >> 3, sc8 = pidx & 7;
-      ku[e] = make_uint4(0, 0, 0, 0);
-      vu[e] = ku[e];
-      if (j0 + sr < n_keys) {
-        const size_t row = base + (size_t)key_token(j0 + sr) * kFD + 8 * sc8;
-        ku[e] = *reinterpret_cast<const uint4*>(k + row);
-        if (with_v) vu[e] = *reinterpret_cast<const uint4*>(v + row);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int j = j0 + 16 * h + l16;
+      const bool ok = j < wave_keys;
+      const size_t row = base + (size_t)(ok ? key_token(j) : 0) * kFD;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        ka[h][ks] = ok ? *reinterpret_cast<const uint4*>(k + row + 32 * ks + 8 * q4) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_kv = [&](bool with_v, const uint4 (&ku)[kKVP], const uint4 (&vu)[kKVP]) {
+  // value rows of the 8 keys of this lane's k-slots: key 4 q4 + j (j < 4), 16 + 4 q4 + j - 4
+  // (j >= 4), columns 4 l16 .. + 3
+  auto load_v = [&](int j0, uint2 (&vr)[8]) {
 #pragma unroll
-    for (int e = 0; e < kKVP; ++e) {
-      const int pidx = tid + kRT * e, sr = pidx >> 3, sc8 = pidx & 7;
-      *reinterpret_cast<uint4*>(&sh.ks[sr][8 * sc8]) = ku[e];
-      if (with_v) {
-        const uint32_t vw[4] = {vu[e].x, vu[e].y, vu[e].z, vu[e].w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          sh.vt[8 * sc8 + 2 * c][sr] = (uint16_t)(vw[c] & 0xFFFF);
-          sh.vt[8 * sc8 + 2 * c + 1][sr] = (uint16_t)(vw[c] >> 16);
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int kj = j0 + (j < 4 ? 4 * q4 + j : 16 + 4 * q4 + (j - 4));
+      vr[j] = kj < wave_keys ? *reinterpret_cast<const uint2*>(v + base + (size_t)key_token(kj) * kFD + 4 * l16)
+                             : make_uint2(0, 0);
     }
   };
-  // scores of this wave's queries against the staged tile: sc[h][i] = key 16 h + 4 q4 + i
-  auto scores = [&](int j0, float (&sc)[2][4]) {
+  auto scores = [&](int j0, const uint4 (&ka)[2][2], float (&sc)[2][4]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sh.ks[16 * h + l16][32 * ks + 8 * q4]);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], c, 0, 0, 0);
-      }
+      for (int ks = 0; ks < 2; ++ks)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[h][ks]), qb[ks], c, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 16 * h + 4 * q4 + i;
@@ -433,24 +458,27 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
       }
     }
   };
-  const int wave_keys = min(n_keys, n_cache + (min(tq_end, tw + 16) - f));  // keys any query of the wave sees
 
   // ---- pass 1: per-query maximum
   float mx = 0.0f;  // never below 0
-  uint4 kpre[kKVP], vpre[kKVP];
-  load_kv(0, false, kpre, vpre);
-  for (int j0 = 0; j0 < n_keys; j0 += kRK) {
-    __syncthreads();
-    store_kv(false, kpre, vpre);
-    __syncthreads();
-    if (j0 + kRK < n_keys) load_kv(j0 + kRK, false, kpre, vpre);
-    if (j0 < wave_keys) {
+  {
+    uint4 ka[2][2];
+    if (wave_keys > 0) load_k(0, ka);
+    for (int j0 = 0; j0 < wave_keys; j0 += kRK) {
+      uint4 kn[2][2];
+      if (j0 + kRK < wave_keys) load_k(j0 + kRK, kn);
       float sc[2][4];
-      scores(j0, sc);
+      scores(j0, ka, sc);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[h][i]);
+      if (j0 + kRK < wave_keys) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) ka[h][ks] = kn[h][ks];
+      }
     }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -464,15 +492,23 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
   f32x4 acc[5];
 #pragma unroll
   for (int nt = 0; nt < 5; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  load_kv(0, true, kpre, vpre);
-  for (int j0 = 0; j0 < n_keys; j0 += kRK) {
-    __syncthreads();
-    store_kv(true, kpre, vpre);
-    __syncthreads();
-    if (j0 + kRK < n_keys) load_kv(j0 + kRK, true, kpre, vpre);
-    if (j0 < wave_keys) {
+  {
+    uint4 ka[2][2];
+    uint2 vr[8];
+    if (wave_keys > 0) {
+      load_k(0, ka);
+      load_v(0, vr);
+    }
+    for (int j0 = 0; j0 < wave_keys; j0 += kRK) {
+      uint4 kn[2][2];
+      uint2 vn[8];
+      const bool more = j0 + kRK < wave_keys;
+      if (more) {
+        load_k(j0 + kRK, kn);
+        load_v(j0 + kRK, vn);
+      }
       float sc[2][4];
-      scores(j0, sc);
+      scores(j0, ka, sc);
       // P = p0 + p1 (two bf16 pieces, 16 significant bits); v and 1 are exact in bf16
       float pf[8];
 #pragma unroll
@@ -483,108 +519,110 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
       split2_8(pf, p0, p1);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(&sh.vt[4 * l16 + nt][4 * q4]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&sh.vt[4 * l16 + nt][16 + 4 * q4]);
-        const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        bf16x8 b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t word = (nt < 2) ? vr[j].x : vr[j].y;
+          const uint16_t bits = (nt & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFF);
+          b[j] = __builtin_bit_cast(__bf16, bits);
+        }
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, b, acc[nt], 0, 0, 0);
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, b, acc[nt], 0, 0, 0);
       }
       acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, ones, acc[4], 0, 0, 0);
       acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, ones, acc[4], 0, 0, 0);
+      if (more) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) ka[h][ks] = kn[h][ks];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vr[j] = vn[j];
+      }
     }
   }
 
-  // ---- linear readout phi(q)^T [H | s], state staged kRF features at a time
-  f32x4 lin[5];
+  // ---- linear readout phi(q)^T [H | s]: this wave's k-steps, all 64 queries
+  f32x4 lin[kRW][5];
 #pragma unroll
-  for (int nt = 0; nt < 5; ++nt) lin[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* Hn = H + (size_t)n * kFPhi * kFD;
-  const float* sn = s + (size_t)n * kFPhi;
-  const float* qrow = sh.qf[16 * w + l16];
-  // state rows g0 .. g0 + 63 in float4 pieces p = tid + kRT m (row p / 16, columns 4 (p % 16) .. + 3),
-  // one tile ahead; row r, column 4 c4 + nt goes to fragment (k-step r / 32, n-tile nt,
-  // lane 16 ((r % 32) / 8) + c4, element r % 8); the normaliser fragment holds s in lane column 0
-  for (int i = tid; i < 2 * (kRF / 32) * 64; i += kRT) {
-    // zero the normaliser fragments once (only lane column 0 is written later)
-    const int pc = i / ((kRF / 32) * 64), rest = i % ((kRF / 32) * 64);
-    sh.hf[pc][rest / 64][4][rest % 64] = make_uint4(0, 0, 0, 0);
-  }
-  float4 hpre[kHP];
-  float spre[kHP];
-  auto load_h = [&](int g0) {
+  for (int tt = 0; tt < kRW; ++tt)
 #pragma unroll
-    for (int m = 0; m < kHP; ++m) {
-      const int pidx = tid + kRT * m;
-      const int r = g0 + (pidx >> 4), c4 = pidx & 15;
-      hpre[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-      spre[m] = 0.0f;
-      if (r < kFPhi) {
-        hpre[m] = *reinterpret_cast<const float4*>(Hn + (size_t)r * kFD + 4 * c4);
-        if (c4 == 0) spre[m] = sn[r];
-      }
-    }
-  };
-  auto put = [&](int pc, int kk, int nt, int L, int j, __bf16 x) {
-    reinterpret_cast<__bf16*>(&sh.hf[pc][kk][nt][L])[j] = x;
-  };
-  load_h(0);
-  for (int g0 = 0; g0 < kFPhi; g0 += kRF) {
-    __syncthreads();
+    for (int nt = 0; nt < 5; ++nt) lin[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    uint4 fr[2][5];
+    auto load_f = [&](int ks, uint4 (&x)[2][5]) {
 #pragma unroll
-    for (int m = 0; m < kHP; ++m) {
-      const int pidx = tid + kRT * m;
-      const int r = pidx >> 4, c4 = pidx & 15;
-      const int kk = r >> 5, L = 16 * ((r & 31) >> 3) + c4, j = r & 7;
-      const float xs[4] = {hpre[m].x, hpre[m].y, hpre[m].z, hpre[m].w};
+      for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const __bf16 a = (__bf16)xs[nt];
-        put(0, kk, nt, L, j, a);
-        put(1, kk, nt, L, j, (__bf16)(xs[nt] - (float)a));
-      }
-      if (c4 == 0) {
-        const __bf16 a = (__bf16)spre[m];
-        put(0, kk, 4, L, j, a);
-        put(1, kk, 4, L, j, (__bf16)(spre[m] - (float)a));
-      }
-    }
-    __syncthreads();
-    if (g0 + kRF < kFPhi) load_h(g0 + kRF);
-#pragma unroll
-    for (int kk = 0; kk < kRF / 32; ++kk) {
-      const int fr = g0 + 32 * kk + 8 * q4;
-      float p[8];
+        for (int nt = 0; nt < 5; ++nt) x[pc][nt] = HF[hf_index(n, ks, pc, nt, lane)];
+    };
+    if (w < kFKS) load_f(w, fr);
+    for (int ks = w; ks < kFKS; ks += kRW) {
+      uint4 fn[2][5];
+      const bool more = ks + kRW < kFKS;
+      if (more) load_f(ks + kRW, fn);
+      // features of this lane's k-slots: 32 ks + 4 q4 + j (j < 4), 32 ks + 16 + 4 q4 + j - 4 (j >= 4)
+      int fa[8], fb[8];
+      float wg[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float x = 0.0f;
-        if (fr + j < kFPhi) {
-          const uint16_t ab = sh.tab[fr + j];
-          const int a = ab & 0xFF, bb = ab >> 8;
-          x = qrow[a] * qrow[bb] * (a == bb ? 1.0f : 1.41421356237309504880f);
-        }
-        p[j] = x;
+        const uint16_t ab = sh.tab[32 * ks + (j < 4 ? 4 * q4 + j : 16 + 4 * q4 + (j - 4))];
+        fa[j] = ab & 0xFF;
+        fb[j] = ab >> 8;
+        wg[j] = fa[j] == fb[j] ? 1.0f : 1.41421356237309504880f;
       }
-      // phi(q) and the state in two bf16 pieces each: hi*hi + hi*lo + lo*hi
-      bf16x8 A0, A1;
-      split2_8(p, A0, A1);
 #pragma unroll
-      for (int nt = 0; nt < 5; ++nt) {
-        const bf16x8 B0 = __builtin_bit_cast(bf16x8, sh.hf[0][kk][nt][lane]);
-        const bf16x8 B1 = __builtin_bit_cast(bf16x8, sh.hf[1][kk][nt][lane]);
-        lin[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, lin[nt], 0, 0, 0);
-        lin[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B1, lin[nt], 0, 0, 0);
-        lin[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, lin[nt], 0, 0, 0);
+      for (int tt = 0; tt < kRW; ++tt) {
+        const float* qrow = sh.qf[16 * tt + l16];
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = qrow[fa[j]] * qrow[fb[j]] * wg[j];
+        bf16x8 A0, A1;
+        split2_8(p, A0, A1);
+#pragma unroll
+        for (int nt = 0; nt < 5; ++nt) {
+          const bf16x8 B0 = __builtin_bit_cast(bf16x8, fr[0][nt]);
+          const bf16x8 B1 = __builtin_bit_cast(bf16x8, fr[1][nt]);
+          lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, lin[tt][nt], 0, 0, 0);
+          lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B1, lin[tt][nt], 0, 0, 0);
+          lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, lin[tt][nt], 0, 0, 0);
+        }
       }
+      if (more) {
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+          for (int nt = 0; nt < 5; ++nt) fr[pc][nt] = fn[pc][nt];
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < kRW; ++tt)
+#pragma unroll
+    for (int nt = 0; nt < 5; ++nt)
+      sh.red[w][tt][nt][lane] = make_float4(lin[tt][nt][0], lin[tt][nt][1], lin[tt][nt][2], lin[tt][nt][3]);
+  __syncthreads();
+  // this wave's queries (token tile w): sum of the four partials
+  f32x4 ln[5];
+#pragma unroll
+  for (int nt = 0; nt < 5; ++nt) {
+    ln[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < kRW; ++r) {
+      const float4 y = sh.red[r][w][nt][lane];
+      ln[nt][0] += y.x;
+      ln[nt][1] += y.y;
+      ln[nt][2] += y.z;
+      ln[nt][3] += y.w;
     }
   }
 
   // ---- combine: rows 4 q4 + i of the wave, columns 4 l16 + nt
-  __syncthreads();
   if (l16 == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float e = __expf(-sh.mq[16 * w + 4 * q4 + i]);
-      sh.den[16 * w + 4 * q4 + i] = acc[4][i] + e * (lin[4][i] + eps);
+      sh.den[16 * w + 4 * q4 + i] = acc[4][i] + e * (ln[4][i] + eps);
     }
   }
   __syncthreads();
@@ -599,7 +637,7 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         Elem<Tout>::store(o, base + (size_t)t * kFD + 4 * l16 + nt,
-                          den != 0.0f ? (acc[nt][i] + e * lin[nt][i]) * inv : 0.0f);
+                          den != 0.0f ? (acc[nt][i] + e * ln[nt][i]) * inv : 0.0f);
     }
   }
 }
@@ -749,7 +787,11 @@ struct Ws {
   int32_t* cache;
   float* scores;
   int32_t* rejected;
+  uint4* HF;  // readout fragments of the state (matrix-core path only)
 };
+
+bool matrix_path(const HybridArgs& a) { return a.dqk == 64 && a.dv == 64 && a.in_bf16; }
+size_t hf_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kFKS * 2 * 5 * 64 * sizeof(uint4)); }
 
 constexpr int kCStride = 256;
 
@@ -774,6 +816,8 @@ Ws carve(const HybridArgs& a, void* ws) {
   w.scores = reinterpret_cast<float*>(p);
   p += align_up((size_t)a.N * kCStride * sizeof(float));
   w.rejected = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
+  w.HF = matrix_path(a) ? reinterpret_cast<uint4*>(p) : nullptr;
   return w;
 }
 
@@ -796,6 +840,9 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
   hipLaunchKernelGGL(fill_kernel_f32, dim3(1024), dim3(256), 0, st, w.H, (size_t)N * D * DV, 0.0f);
   hipLaunchKernelGGL(fill_kernel_f32, dim3(64), dim3(256), 0, st, w.s, (size_t)N * D, 0.0f);
   hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, w.cache, (size_t)N * kCStride, -1);
+  if (w.HF)
+    hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, reinterpret_cast<int32_t*>(w.HF),
+                       hf_bytes(a) / sizeof(int32_t), 0);
   if (a.trace && a.cache_size > 0)
     hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, a.trace,
                        (size_t)N * nblocks * a.cache_size, -1);
@@ -835,8 +882,8 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
                            kCStride, a.trace, (size_t)a.cache_size, b, nblocks);
         KLA_CHECK();
         if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
-          hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFTiles + kFoldTilesPerWG - 1) / kFoldTilesPerWG, N),
-                             dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.rejected, kCStride,
+          hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFKS + kFoldKsPerWG - 1) / kFoldKsPerWG, N),
+                             dim3(kThreads), 0, st, w.H, w.s, w.HF, k, v, a.T, w.rejected, kCStride,
                              n_cand - a.cache_size);
         } else {
           hipLaunchKernelGGL((hyb_fold_kernel<DQK, DV, Tin>), dim3(S, N), dim3(kThreads), 0, st,
@@ -849,8 +896,7 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
     f_prev = f;
     if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
       hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N), dim3(kRT), 0,
-                         st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride, n_cache, b0, b1, f, a.scale,
-                         a.eps);
+                         st, q, k, v, o, a.T, w.HF, w.cache, kCStride, n_cache, b0, b1, f, a.scale, a.eps);
     } else {
       hipLaunchKernelGGL((hyb_readout_kernel<DQK, DV, Tin, Tout>), dim3((b1 - b0 + 15) / 16, N),
                          dim3(kThreads), 0, st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride,
@@ -885,6 +931,7 @@ size_t hybrid_workspace(const HybridArgs& a) {
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   b += align_up((size_t)a.N * kCStride * sizeof(float));
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
+  if (matrix_path(a)) b += hf_bytes(a);
   return b;
 }
 
