@@ -367,6 +367,8 @@ constexpr int kRW = 4;        // waves (16 queries each) per work-group
 constexpr int kRT = 64 * kRW; // threads
 constexpr int kRQ = 16 * kRW; // queries per work-group
 constexpr int kRK = 32;       // keys per tile
+constexpr int kPT = 2;        // key tiles per iteration (and in flight)
+constexpr int kPF = 2;        // state k-steps per iteration (and in flight)
 
 struct ReadoutLds {
   float qf[kRQ][kFD + 1];               // query rows (float32) for phi(q)
@@ -376,13 +378,19 @@ struct ReadoutLds {
   float den[kRQ];                       // per-query denominator
 };
 
+// Work-group (b, n, sp) of ns splits handles keys [sp * span, (sp + 1) * span)
+// and state k-steps sp * kRW + w (mod ns * kRW); with ns > 1 it writes, per
+// query, the partial numerator and denominator scaled by e^-m_sp, and m_sp,
+// to xp[n][query][sp][66] for hyb_readout_combine_kernel.
 template <typename Tout>
 __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     Tout* __restrict__ o, int T, const uint4* __restrict__ HF, const int32_t* __restrict__ cache,
-    int cstride, int n_cache, int t_begin, int t_end, int f, float scale, float eps) {
+    int cstride, int n_cache, int t_begin, int t_end, int f, float scale, float eps, int ns,
+    float* __restrict__ xp, int xq) {
   __shared__ __align__(16) ReadoutLds sh;
   const int n = blockIdx.y;
+  const int sp = blockIdx.z;
   const int t0 = t_begin + kRQ * blockIdx.x;
   const int tq_end = min(t_end, t0 + kRQ);       // queries [t0, tq_end)
   const int tid = threadIdx.x;
@@ -418,7 +426,10 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
   __syncthreads();
 
   auto key_token = [&](int j) { return j < n_cache ? cn[j] : f + (j - n_cache); };
-  const int wave_keys = max(0, min(n_keys, n_cache + (min(tq_end, tw + 16) - f)));
+  // this split's keys, cut to the ones any query of the wave sees
+  const int span = (((n_keys + ns - 1) / ns) + kRK - 1) / kRK * kRK;
+  const int kbeg = min(n_keys, sp * span);
+  const int wave_keys = max(kbeg, min(min(n_keys, kbeg + span), n_cache + (min(tq_end, tw + 16) - f)));
 
   // key fragments of tile j0: ka[h][ks] = key j0 + 16 h + l16, dims 32 ks + 8 q4 .. + 7
   auto load_k = [&](int j0, uint4 (&ka)[2][2]) {
@@ -452,32 +463,43 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + 16 * h + 4 * q4 + i;
-        // cache keys precede every query; window keys are causal
-        const bool ok = j < n_keys && my_t < tq_end && (j < n_cache || f + (j - n_cache) <= my_t);
+        // keys of this split only (wave_keys <= n_keys); cache keys precede every
+        // query; window keys are causal
+        const bool ok = j < wave_keys && my_t < tq_end && (j < n_cache || f + (j - n_cache) <= my_t);
         sc[h][i] = ok ? scale * c[i] : -INFINITY;
       }
     }
   };
 
-  // ---- pass 1: per-query maximum
+  // ---- pass 1: per-query maximum (kPT key tiles per iteration, the next kPT in flight)
   float mx = 0.0f;  // never below 0
   {
-    uint4 ka[2][2];
-    if (wave_keys > 0) load_k(0, ka);
-    for (int j0 = 0; j0 < wave_keys; j0 += kRK) {
-      uint4 kn[2][2];
-      if (j0 + kRK < wave_keys) load_k(j0 + kRK, kn);
-      float sc[2][4];
-      scores(j0, ka, sc);
+    uint4 ka[kPT][2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int t = 0; t < kPT; ++t) load_k(kbeg + kRK * t, ka[t]);
+    for (int j0 = kbeg; j0 < wave_keys; j0 += kRK * kPT) {
+      uint4 kn[kPT][2][2];
+      const bool more = j0 + kRK * kPT < wave_keys;
+      if (more) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[h][i]);
-      if (j0 + kRK < wave_keys) {
+        for (int t = 0; t < kPT; ++t) load_k(j0 + kRK * (kPT + t), kn[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < kPT; ++t) {
+        float sc[2][4];
+        scores(j0 + kRK * t, ka[t], sc);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) ka[h][ks] = kn[h][ks];
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[h][i]);
+      }
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < kPT; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) ka[t][h][ks] = kn[t][h][ks];
       }
     }
   }
@@ -493,51 +515,61 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
 #pragma unroll
   for (int nt = 0; nt < 5; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    uint4 ka[2][2];
-    uint2 vr[8];
-    if (wave_keys > 0) {
-      load_k(0, ka);
-      load_v(0, vr);
+    uint4 ka[kPT][2][2];
+    uint2 vr[kPT][8];
+#pragma unroll
+    for (int t = 0; t < kPT; ++t) {
+      load_k(kbeg + kRK * t, ka[t]);
+      load_v(kbeg + kRK * t, vr[t]);
     }
-    for (int j0 = 0; j0 < wave_keys; j0 += kRK) {
-      uint4 kn[2][2];
-      uint2 vn[8];
-      const bool more = j0 + kRK < wave_keys;
+    for (int j0 = kbeg; j0 < wave_keys; j0 += kRK * kPT) {
+      uint4 kn[kPT][2][2];
+      uint2 vn[kPT][8];
+      const bool more = j0 + kRK * kPT < wave_keys;
       if (more) {
-        load_k(j0 + kRK, kn);
-        load_v(j0 + kRK, vn);
-      }
-      float sc[2][4];
-      scores(j0, ka, sc);
-      // P = p0 + p1 (two bf16 pieces, 16 significant bits); v and 1 are exact in bf16
-      float pf[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pf[4 * h + i] = __expf(sc[h][i] - mx);
-      bf16x8 p0, p1;
-      split2_8(pf, p0, p1);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        bf16x8 b;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t word = (nt < 2) ? vr[j].x : vr[j].y;
-          const uint16_t bits = (nt & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFF);
-          b[j] = __builtin_bit_cast(__bf16, bits);
+        for (int t = 0; t < kPT; ++t) {
+          load_k(j0 + kRK * (kPT + t), kn[t]);
+          load_v(j0 + kRK * (kPT + t), vn[t]);
         }
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, b, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, b, acc[nt], 0, 0, 0);
       }
-      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, ones, acc[4], 0, 0, 0);
-      acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, ones, acc[4], 0, 0, 0);
-      if (more) {
+#pragma unroll
+      for (int t = 0; t < kPT; ++t) {
+        float sc[2][4];
+        scores(j0 + kRK * t, ka[t], sc);
+        // P = p0 + p1 (two bf16 pieces, 16 significant bits); v and 1 are exact in bf16
+        float pf[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) ka[h][ks] = kn[h][ks];
+          for (int i = 0; i < 4; ++i) pf[4 * h + i] = __expf(sc[h][i] - mx);
+        bf16x8 p0, p1;
+        split2_8(pf, p0, p1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vr[j] = vn[j];
+        for (int nt = 0; nt < 4; ++nt) {
+          bf16x8 b;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t word = (nt < 2) ? vr[t][j].x : vr[t][j].y;
+            const uint16_t bits = (nt & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFF);
+            b[j] = __builtin_bit_cast(__bf16, bits);
+          }
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, b, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, b, acc[nt], 0, 0, 0);
+        }
+        acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p0, ones, acc[4], 0, 0, 0);
+        acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p1, ones, acc[4], 0, 0, 0);
+      }
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < kPT; ++t) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) ka[t][h][ks] = kn[t][h][ks];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vr[t][j] = vn[t][j];
+        }
       }
     }
   }
@@ -549,50 +581,65 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
 #pragma unroll
     for (int nt = 0; nt < 5; ++nt) lin[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    uint4 fr[2][5];
+    // k-steps ks = w + kRW (kPF i + t): kPF per iteration, the next kPF in flight
     auto load_f = [&](int ks, uint4 (&x)[2][5]) {
 #pragma unroll
       for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
-        for (int nt = 0; nt < 5; ++nt) x[pc][nt] = HF[hf_index(n, ks, pc, nt, lane)];
+        for (int nt = 0; nt < 5; ++nt)
+          x[pc][nt] = ks < kFKS ? HF[hf_index(n, ks, pc, nt, lane)] : make_uint4(0, 0, 0, 0);
     };
-    if (w < kFKS) load_f(w, fr);
-    for (int ks = w; ks < kFKS; ks += kRW) {
-      uint4 fn[2][5];
-      const bool more = ks + kRW < kFKS;
-      if (more) load_f(ks + kRW, fn);
-      // features of this lane's k-slots: 32 ks + 4 q4 + j (j < 4), 32 ks + 16 + 4 q4 + j - 4 (j >= 4)
-      int fa[8], fb[8];
-      float wg[8];
+    uint4 fr[kPF][2][5];
+    const int kst = ns * kRW;  // k-step stride of this split's waves
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint16_t ab = sh.tab[32 * ks + (j < 4 ? 4 * q4 + j : 16 + 4 * q4 + (j - 4))];
-        fa[j] = ab & 0xFF;
-        fb[j] = ab >> 8;
-        wg[j] = fa[j] == fb[j] ? 1.0f : 1.41421356237309504880f;
+    for (int t = 0; t < kPF; ++t) load_f(sp * kRW + w + kst * t, fr[t]);
+    for (int ks0 = sp * kRW + w; ks0 < kFKS; ks0 += kst * kPF) {
+      uint4 fn[kPF][2][5];
+      const bool more = ks0 + kst * kPF < kFKS;
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < kPF; ++t) load_f(ks0 + kst * (kPF + t), fn[t]);
       }
 #pragma unroll
-      for (int tt = 0; tt < kRW; ++tt) {
-        const float* qrow = sh.qf[16 * tt + l16];
-        float p[8];
+      for (int t = 0; t < kPF; ++t) {
+        const int ks = ks0 + kst * t;
+        if (ks < kFKS) {
+          // features of this lane's k-slots: 32 ks + 4 q4 + j (j < 4), 32 ks + 16 + 4 q4 + j - 4 (j >= 4)
+          int fa[8], fb[8];
+          float wg[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = qrow[fa[j]] * qrow[fb[j]] * wg[j];
-        bf16x8 A0, A1;
-        split2_8(p, A0, A1);
+          for (int j = 0; j < 8; ++j) {
+            const uint16_t ab = sh.tab[32 * ks + (j < 4 ? 4 * q4 + j : 16 + 4 * q4 + (j - 4))];
+            fa[j] = ab & 0xFF;
+            fb[j] = ab >> 8;
+            wg[j] = fa[j] == fb[j] ? 1.0f : 1.41421356237309504880f;
+          }
 #pragma unroll
-        for (int nt = 0; nt < 5; ++nt) {
-          const bf16x8 B0 = __builtin_bit_cast(bf16x8, fr[0][nt]);
-          const bf16x8 B1 = __builtin_bit_cast(bf16x8, fr[1][nt]);
-          lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, lin[tt][nt], 0, 0, 0);
-          lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B1, lin[tt][nt], 0, 0, 0);
-          lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, lin[tt][nt], 0, 0, 0);
+          for (int tt = 0; tt < kRW; ++tt) {
+            const float* qrow = sh.qf[16 * tt + l16];
+            float p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = qrow[fa[j]] * qrow[fb[j]] * wg[j];
+            bf16x8 A0, A1;
+            split2_8(p, A0, A1);
+#pragma unroll
+            for (int nt = 0; nt < 5; ++nt) {
+              const bf16x8 B0 = __builtin_bit_cast(bf16x8, fr[t][0][nt]);
+              const bf16x8 B1 = __builtin_bit_cast(bf16x8, fr[t][1][nt]);
+              lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B0, lin[tt][nt], 0, 0, 0);
+              lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B1, lin[tt][nt], 0, 0, 0);
+              lin[tt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, lin[tt][nt], 0, 0, 0);
+            }
+          }
         }
       }
       if (more) {
 #pragma unroll
-        for (int pc = 0; pc < 2; ++pc)
+        for (int t = 0; t < kPF; ++t)
 #pragma unroll
-          for (int nt = 0; nt < 5; ++nt) fr[pc][nt] = fn[pc][nt];
+          for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+            for (int nt = 0; nt < 5; ++nt) fr[t][pc][nt] = fn[t][pc][nt];
       }
     }
   }
@@ -618,6 +665,25 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
   }
 
   // ---- combine: rows 4 q4 + i of the wave, columns 4 l16 + nt
+  if (ns > 1) {
+    // partials of this split, scaled by e^-m_sp: numerator, denominator (no eps), m_sp
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * q4 + i;
+      if (t0 + r < tq_end) {
+        const float m = sh.mq[r];
+        const float e = __expf(-m);
+        float* xr = xp + (((size_t)n * xq + (t0 + r - t_begin)) * ns + sp) * 66;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) xr[4 * l16 + nt] = acc[nt][i] + e * ln[nt][i];
+        if (l16 == 0) {
+          xr[64] = acc[4][i] + e * ln[4][i];
+          xr[65] = m;
+        }
+      }
+    }
+    return;
+  }
   if (l16 == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -640,6 +706,29 @@ __global__ __launch_bounds__(kRT) void hyb_readout_mfma_kernel(
                           den != 0.0f ? (acc[nt][i] + e * ln[nt][i]) * inv : 0.0f);
     }
   }
+}
+
+// Joins the ns split partials of queries [t_begin, t_end): m = max m_sp,
+// o = sum e^(m_sp - m) num_sp / (sum e^(m_sp - m) den_sp + e^-m eps).
+template <typename Tout>
+__global__ __launch_bounds__(kThreads) void hyb_readout_combine_kernel(const float* __restrict__ xp, int xq, int ns,
+                                                                     Tout* __restrict__ o, int T, int t_begin,
+                                                                     int t_end, float eps) {
+  const int n = blockIdx.y;
+  const int idx = blockIdx.x * kThreads + threadIdx.x;  // (query, column)
+  const int r = idx >> 6, c = idx & 63;
+  const int t = t_begin + r;
+  if (t >= t_end) return;
+  const float* xr = xp + ((size_t)n * xq + r) * ns * 66;
+  float m = 0.0f;
+  for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, xr[sp * 66 + 65]);
+  float num = 0.0f, den = __expf(-m) * eps;
+  for (int sp = 0; sp < ns; ++sp) {
+    const float e = __expf(xr[sp * 66 + 65] - m);
+    num += e * xr[sp * 66 + c];
+    den += e * xr[sp * 66 + 64];
+  }
+  Elem<Tout>::store(o, ((size_t)n * T + t) * kFD + c, den != 0.0f ? num / den : 0.0f);
 }
 
 // Output of 16 queries [t0, t0+16) of a block whose window starts at f.
@@ -788,10 +877,13 @@ struct Ws {
   float* scores;
   int32_t* rejected;
   uint4* HF;  // readout fragments of the state (matrix-core path only)
+  float* xp;  // readout split partials [N][refresh][kRNS][66] (matrix-core path only)
 };
 
 bool matrix_path(const HybridArgs& a) { return a.dqk == 64 && a.dv == 64 && a.in_bf16; }
 size_t hf_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kFKS * 2 * 5 * 64 * sizeof(uint4)); }
+constexpr int kRNS = 8;  // readout splits per (head, query block)
+size_t xp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * a.refresh * kRNS * 66 * sizeof(float)); }
 
 constexpr int kCStride = 256;
 
@@ -818,6 +910,8 @@ Ws carve(const HybridArgs& a, void* ws) {
   w.rejected = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   w.HF = matrix_path(a) ? reinterpret_cast<uint4*>(p) : nullptr;
+  if (w.HF) p += hf_bytes(a);
+  w.xp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
   return w;
 }
 
@@ -895,8 +989,12 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
     }
     f_prev = f;
     if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
-      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N), dim3(kRT), 0,
-                         st, q, k, v, o, a.T, w.HF, w.cache, kCStride, n_cache, b0, b1, f, a.scale, a.eps);
+      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N, kRNS), dim3(kRT),
+                         0, st, q, k, v, o, a.T, w.HF, w.cache, kCStride, n_cache, b0, b1, f, a.scale, a.eps,
+                         kRNS, w.xp, a.refresh);
+      if (kRNS > 1)
+        hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>), dim3(((b1 - b0) * kFD + kThreads - 1) / kThreads, N),
+                           dim3(kThreads), 0, st, w.xp, a.refresh, kRNS, o, a.T, b0, b1, a.eps);
     } else {
       hipLaunchKernelGGL((hyb_readout_kernel<DQK, DV, Tin, Tout>), dim3((b1 - b0 + 15) / 16, N),
                          dim3(kThreads), 0, st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride,
@@ -931,7 +1029,7 @@ size_t hybrid_workspace(const HybridArgs& a) {
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   b += align_up((size_t)a.N * kCStride * sizeof(float));
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
-  if (matrix_path(a)) b += hf_bytes(a);
+  if (matrix_path(a)) b += hf_bytes(a) + xp_bytes(a);
   return b;
 }
 
