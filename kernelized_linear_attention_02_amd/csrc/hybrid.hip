@@ -8,7 +8,8 @@
 // refresh depends on the fold of the previous one, so the chain is
 // sequential per head; every step runs for all heads at once:
 //   score  : SRE of every candidate (cache + newly evicted) against (H, s);
-//   select : bitonic sort of (score, token id) keys; keep cache_size, list
+//   select : order the (score, token id) keys (a bitonic sort, or ranks
+//            by counting on the matrix-core path); keep cache_size, list
 //            the rest;
 //   fold   : H += phi(k_i) v_i^T, s += phi(k_i) over the rejected tokens;
 //   readout: for the block's queries, window and cache softmax terms and
@@ -870,6 +871,104 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_kernel(
   }
 }
 
+constexpr int kCandMax = 256;  // candidates per refresh, at most (cache + evicted)
+
+// Matrix-core form of the selection (d = 64, bf16 token rows): the scores are
+// first assembled from Z feature-split partials part[((n Z + z) pstride + c) 68
+// + {0..63 numerator, 64 denominator}],
+//   score_c = || num_c / (den_c + eps) - v_c ||^2   (prediction 0 when the
+//   denominator is 0),
+// then every candidate finds its place by counting: its rank is the number of
+// larger (score, token id) keys, so ranks are distinct; the keep best go to
+// the cache in ascending token order (their place is the number of kept
+// tokens with a lower id) and the rest, in rank order, to the rejected list.
+// The result is the one the sort of the generic form gives.
+constexpr int kSelThreads = 1024;
+__global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
+    const float* __restrict__ part, int Z, int pstride, const uint16_t* __restrict__ v, int T,
+    float eps, int32_t* __restrict__ cache, int cstride, int n_cache, int ev0, int n_cand, int keep,
+    int32_t* __restrict__ rejected, int rstride, int32_t* __restrict__ trace, size_t trace_row_stride,
+    int block, int nblocks, float* __restrict__ scores, int sstride) {
+  static_assert(kSelThreads == 4 * kCandMax, "four threads per candidate");
+  __shared__ uint64_t keys[kCandMax];
+  __shared__ int32_t tok[kCandMax];
+  __shared__ int32_t kid[kCandMax];
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  // four adjacent threads per candidate: quarter qd of its columns, and of
+  // the keys it counts against
+  const int c = tid >> 2;
+  const int qd = tid & 3;
+  const bool live = c < n_cand;
+  const int32_t* cn = cache + (size_t)n * cstride;
+  if (qd == 0 && live) tok[c] = cand_token(cn, n_cache, ev0, c);
+  __syncthreads();
+  float err = 0.0f;
+  if (live) {
+    float num[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) num[j] = 0.0f;
+    float den = 0.0f;
+    for (int z = 0; z < Z; ++z) {
+      const float* pc = part + (((size_t)n * Z + z) * pstride + c) * 68;
+      const float4* p4 = reinterpret_cast<const float4*>(pc + 16 * qd);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 x = p4[j];
+        num[4 * j] += x.x;
+        num[4 * j + 1] += x.y;
+        num[4 * j + 2] += x.z;
+        num[4 * j + 3] += x.w;
+      }
+      den += pc[64];
+    }
+    den += eps;
+    const uint4* vp = reinterpret_cast<const uint4*>(v + ((size_t)n * T + tok[c]) * kFD + 16 * qd);
+    const uint4 va = vp[0], vb = vp[1];
+    const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float vj = __uint_as_float((j & 1) ? (vw[j >> 1] & 0xFFFF0000u) : (vw[j >> 1] << 16));
+      const float pred = den != 0.0f ? num[j] / den : 0.0f;
+      const float d = pred - vj;
+      err += d * d;
+    }
+  }
+  err += __shfl_xor(err, 1, 64);
+  err += __shfl_xor(err, 2, 64);
+  if (qd == 0 && live) {
+    keys[c] = topk_key(err, (uint32_t)tok[c]);
+    if (scores) scores[(size_t)n * sstride + c] = err;
+  }
+  __syncthreads();
+  uint64_t key = 0;
+  int rank = 0;
+  if (live) {
+    key = keys[c];
+    for (int j = qd; j < n_cand; j += 4) rank += keys[j] > key ? 1 : 0;
+  }
+  rank += __shfl_xor(rank, 1, 64);
+  rank += __shfl_xor(rank, 2, 64);
+  if (qd == 0 && live) kid[c] = rank < keep ? tok[c] : 0x7FFFFFFF;
+  __syncthreads();
+  int pos = 0;
+  if (live && rank < keep) {
+    const int32_t id = tok[c];
+    for (int j = qd; j < n_cand; j += 4) pos += kid[j] < id ? 1 : 0;
+  }
+  pos += __shfl_xor(pos, 1, 64);
+  pos += __shfl_xor(pos, 2, 64);
+  if (qd == 0 && live) {
+    const int32_t id = tok[c];
+    if (rank >= keep) {
+      rejected[(size_t)n * rstride + rank - keep] = id;
+    } else {
+      cache[(size_t)n * cstride + pos] = id;
+      if (trace) trace[((size_t)n * nblocks + block) * trace_row_stride + pos] = id;
+    }
+  }
+}
+
 struct Ws {
   float* H;
   float* s;
@@ -878,6 +977,7 @@ struct Ws {
   int32_t* rejected;
   uint4* HF;  // readout fragments of the state (matrix-core path only)
   float* xp;  // readout split partials [N][refresh][kRNS][66] (matrix-core path only)
+  float* sp;  // score split partials [N][kSZ][kCStride][68] (matrix-core path only)
 };
 
 bool matrix_path(const HybridArgs& a) { return a.dqk == 64 && a.dv == 64 && a.in_bf16; }
@@ -885,7 +985,9 @@ size_t hf_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kFKS * 2 * 
 constexpr int kRNS = 8;  // readout splits per (head, query block)
 size_t xp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * a.refresh * kRNS * 66 * sizeof(float)); }
 
-constexpr int kCStride = 256;
+constexpr int kCStride = kCandMax;
+constexpr int kSZ = 5;  // score splits of the feature sum per (head, candidate block)
+size_t sp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kSZ * kCStride * 68 * sizeof(float)); }
 
 Ws carve(const HybridArgs& a, void* ws) {
   const int D = phi_dim(a.dqk);
@@ -912,6 +1014,8 @@ Ws carve(const HybridArgs& a, void* ws) {
   w.HF = matrix_path(a) ? reinterpret_cast<uint4*>(p) : nullptr;
   if (w.HF) p += hf_bytes(a);
   w.xp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
+  if (w.xp) p += xp_bytes(a);
+  w.sp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
   return w;
 }
 
@@ -961,19 +1065,21 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
         prof_begin(st);
         if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
           // matrix cores, float32-faithful (split bf16 operands)
-          e = hybrid_score_mfma(N, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache, f_prev, n_cand,
-                                w.scores, kCStride, a.eps, st);
+          e = hybrid_score_mfma(N, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache, f_prev, n_cand, kSZ,
+                                w.sp, kCStride, st);
           if (e != hipSuccess) return e;
+          hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ, kCStride, v,
+                             a.T, a.eps, w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,
+                             kCStride, a.trace, (size_t)a.cache_size, b, nblocks, w.scores, kCStride);
         } else {
           hipLaunchKernelGGL((hyb_score_kernel<DQK, DV, Tin>), dim3((n_cand + 63) / 64, N),
                              dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache,
                              f_prev, n_cand, w.scores, kCStride, a.eps);
+          hipLaunchKernelGGL(hyb_select_kernel, dim3(N), dim3(kThreads), 0, st, w.scores, kCStride,
+                             w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,
+                             kCStride, a.trace, (size_t)a.cache_size, b, nblocks);
         }
         prof_end(st);
-        KLA_CHECK();
-        hipLaunchKernelGGL(hyb_select_kernel, dim3(N), dim3(kThreads), 0, st, w.scores, kCStride,
-                           w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,
-                           kCStride, a.trace, (size_t)a.cache_size, b, nblocks);
         KLA_CHECK();
         if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
           hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFKS + kFoldKsPerWG - 1) / kFoldKsPerWG, N),
@@ -1029,7 +1135,7 @@ size_t hybrid_workspace(const HybridArgs& a) {
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   b += align_up((size_t)a.N * kCStride * sizeof(float));
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
-  if (matrix_path(a)) b += hf_bytes(a) + xp_bytes(a);
+  if (matrix_path(a)) b += hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
   return b;
 }
 
