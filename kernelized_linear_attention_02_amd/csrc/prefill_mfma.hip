@@ -16,20 +16,22 @@
 // diagonal instead, and the state is rescaled when it crosses the ABI.
 //
 // State kernel. A work-group owns one head and a contiguous range of tiles
-// (a feature slice); its four waves split the tiles, keep their slice of H
-// in MFMA accumulators (fp32) and their slice of s in LDS, and walk the
-// chunks in order. Per chunk:
-//   readout  num_x = phi(Q) H,  den_x = phi(Q) s  (MFMA 16x16x32 bf16 for
-//            num; bf16 dot products for den) - partial over the slice;
-//   update   H += phi(K)^T V (MFMA), s += phi(K)^T 1.
-// The four waves' partials are summed in LDS, then added into an fp32
-// accumulator [N, T, d_v + 1] with relaxed device-scope atomics. A head's
-// work-groups are placed on one XCD (work-groups are dealt to the 8 XCDs in
-// turn), so its atomics meet in one L2.
+// (a feature slice) and walks the chunks in order, a staged sub-chunk of q,
+// k and v at a time. Its four update waves split the tiles and keep their
+// slice of H in MFMA accumulators (fp32) and of s in LDS:
+//   update   H += phi(K)^T V (MFMA 16x16x32 bf16), s += phi(K)^T 1;
+// at each chunk end they publish the state as bf16 MFMA B fragments in LDS
+// (double buffered). Its four readout waves each take a 16-token tile and
+// read out against the state of the chunk start:
+//   readout  num_x = phi(Q) H (MFMA), den_x = phi(Q) s (bf16 dot products),
+// partial over the slice, written as bf16 to a workspace [head, chunk,
+// slice, d_v + 1, chunk]. A head's work-groups are placed on one XCD
+// (work-groups are dealt to the 8 XCDs in turn), so their shared q, k and v
+// reads meet in one L2.
 //
 // Finish kernel. One work-group per (head, chunk): the exact intra-chunk
-// term A [V | 1] with A = lower-triangular (Q K^T)^2 (MFMA), plus the
-// accumulator, divided, cast to the output type.
+// term A [V | 1] with A = lower-triangular (Q K^T)^2 (MFMA), plus the sum of
+// the slice partials, divided, cast to the output type.
 #include <algorithm>
 
 #include "kla_device.hpp"
@@ -51,7 +53,6 @@ constexpr int kBlk = kDim / 4;                    // 16 blocks per side
 constexpr int kTiles = kBlk * (kBlk + 1) / 2;     // 136
 constexpr int kTW = 5;                            // tiles per wave, at most
 constexpr int kMinSlices = 8;                     // tiles per work-group <= 17
-constexpr int kQS = kDim + 4;                     // q row stride; 64..67 read as zero
 constexpr int kKR = kDim + 4;                     // k^T rows; 64..67 are zero
 constexpr int kAcc = kDim + 1;                    // accumulator row: num | den
 
@@ -120,8 +121,10 @@ static_assert(kTiles / kMinSlices + 1 <= kWG, "a work-group's tiles must fit its
 
 template <int CS>
 struct StateLds {
-  float qs[CS][kQS];                              // q rows (fp32)
-  float kt[kKR][CS + 4];                          // k transposed (fp32), rows 64..67 zero
+  // q and k transposed (fp32, rows 64..67 zero); the row paddings spread the
+  // readout's and the update's reads over the LDS banks
+  float qt[kKR][CS + 16];
+  float kt[kKR][CS + 12];
   uint16_t vt[kDim][CS + 8];                      // v transposed (bf16)
   uint4 hs[2][kPairs][4][64];                     // H as bf16 B fragments, double buffer
   uint4 ss[2][kPairs][4];                         // s as bf16 per pair and lane quarter
@@ -169,8 +172,14 @@ __device__ __forceinline__ void stage(StateLds<CS>& sh, const Prefetch& p, int t
   lo.z = bf16f(qw[1] & 0xFFFF); lo.w = bf16f(qw[1] >> 16);
   hi.x = bf16f(qw[2] & 0xFFFF); hi.y = bf16f(qw[2] >> 16);
   hi.z = bf16f(qw[3] & 0xFFFF); hi.w = bf16f(qw[3] >> 16);
-  *reinterpret_cast<float4*>(&sh.qs[t][d0]) = lo;
-  *reinterpret_cast<float4*>(&sh.qs[t][d0 + 4]) = hi;
+  sh.qt[d0][t] = lo.x;
+  sh.qt[d0 + 1][t] = lo.y;
+  sh.qt[d0 + 2][t] = lo.z;
+  sh.qt[d0 + 3][t] = lo.w;
+  sh.qt[d0 + 4][t] = hi.x;
+  sh.qt[d0 + 5][t] = hi.y;
+  sh.qt[d0 + 6][t] = hi.z;
+  sh.qt[d0 + 7][t] = hi.w;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     sh.kt[d0 + 2 * e][t] = bf16f(kw[e] & 0xFFFF);
@@ -242,8 +251,8 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
   const int lw0 = w * base + min(w, extra);
 
   // zero pads and both fragment buffers
-  for (int i = tid; i < CS * 4; i += kThreads3) sh.qs[i >> 2][kDim + (i & 3)] = 0.0f;
-  for (int i = tid; i < 4 * (CS + 4); i += kThreads3) sh.kt[kDim + i / (CS + 4)][i % (CS + 4)] = 0.0f;
+  for (int i = tid; i < CS * 4; i += kThreads3) sh.qt[kDim + (i & 3)][i >> 2] = 0.0f;
+  for (int i = tid; i < 4 * (CS + 12); i += kThreads3) sh.kt[kDim + i / (CS + 12)][i % (CS + 12)] = 0.0f;
   for (int i = tid; i < 2 * kPairs * 4 * 64; i += kThreads3) (&sh.hs[0][0][0][0])[i] = make_uint4(0, 0, 0, 0);
   for (int i = tid; i < 2 * kPairs * 4; i += kThreads3) (&sh.ss[0][0][0])[i] = make_uint4(0, 0, 0, 0);
 
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
 #pragma unroll
         for (int nt4 = 0; nt4 < 4; ++nt4) ra[nt4] = f32x4{0.f, 0.f, 0.f, 0.f};
         float dn = 0.0f;
-        const float* qrow = sh.qs[w * 16 + l16];
+        const int qcol = w * 16 + l16;
         // absent tiles have zero fragments in hs/ss, so they add nothing
 #pragma unroll
         for (int pr = 0; pr < NP; ++pr) {
@@ -415,15 +424,15 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
           const int bo = 4 * (gi[2 * pr + 1] + gj[2 * pr + 1]) + q4;
           // doubled off-diagonal weight; the diagonal feature (first column of
           // a tile with j == 0) keeps 1
-          const float qe = 2.0f * qrow[ae];
-          const float qo = 2.0f * qrow[ao];
+          const float qe = 2.0f * sh.qt[ae][qcol];
+          const float qo = 2.0f * sh.qt[ao][qcol];
           const float de = gj[2 * pr] == 0 ? 0.5f : 1.0f;
           const float dd = gj[2 * pr + 1] == 0 ? 0.5f : 1.0f;
           float p[8];
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
-            p[cc] = qe * qrow[be + cc];
-            p[4 + cc] = qo * qrow[bo + cc];
+            p[cc] = qe * sh.qt[be + cc][qcol];
+            p[4 + cc] = qo * sh.qt[bo + cc][qcol];
           }
           p[0] *= de;
           p[4] *= dd;
