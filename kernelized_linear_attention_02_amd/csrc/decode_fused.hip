@@ -121,7 +121,7 @@ __device__ __forceinline__ float comp(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Candidate sources: rows of float32 arrays [N, n_cand, 64] ...
+// Candidate source: rows of float32 arrays [N, n_cand, 64].
 struct CandRows {
   const float* k;
   const float* v;
@@ -134,36 +134,11 @@ struct CandRows {
   }
 };
 
-// ... or bf16 token rows [N, T, 64] picked by token id: the first n_cache
-// candidates are cache[n][j], the rest the consecutive tokens ev0, ev0 + 1, ...
-struct CandTokens {
-  const uint16_t* k;
-  const uint16_t* v;
-  int T;
-  const int32_t* cache;
-  int cstride, n_cache, ev0;
-  __device__ __forceinline__ size_t row(int n, int c) const {
-    const int tok = c < n_cache ? cache[(size_t)n * cstride + c] : ev0 + (c - n_cache);
-    return ((size_t)n * T + tok) * kDim;
-  }
-  static __device__ __forceinline__ float4 bf4(const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-  }
-  __device__ __forceinline__ float4 k4(int n, int c, int d4) const { return bf4(k + row(n, c) + 4 * d4); }
-  __device__ __forceinline__ float4 v4(int n, int c, int d4) const { return bf4(v + row(n, c) + 4 * d4); }
-};
-
-// Work-group (n, g, z) scores candidates 64 g .. 64 g + 16 MT - 1 of
-// head-state n over feature tiles z * 65 / Z .. (z + 1) * 65 / Z - 1, Z being
-// gridDim.z. MT: 16-candidate blocks. UPDATE: decode step first (H and s
-// written back, o produced); otherwise the state is only read. SELECT: top_k
-// selection and gather in the same kernel (requires n_cand <= 16 * MT, one
-// group, Z = 1). PART: no scores; the work-group's numerator and denominator
-// partials go to scores[((n Z + z) sstride + c) 68 + {0..63, 64}], to be summed
-// over z by the consumer (a split of the feature sum across work-groups).
-template <int MT, bool UPDATE, bool SELECT, typename Tin, typename Tout, typename Cand, bool PART = false>
+// Work-group (n, g) scores candidates 64 g .. 64 g + 16 MT - 1 of head-state n.
+// MT: 16-candidate blocks. UPDATE: decode step first (H and s written back,
+// o produced); otherwise the state is only read. SELECT: top_k selection and
+// gather in the same kernel (requires n_cand <= 16 * MT, one group).
+template <int MT, bool UPDATE, bool SELECT, typename Tin, typename Tout, typename Cand>
 __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     float* __restrict__ H, float* __restrict__ s, const Tin* __restrict__ q,
     const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, float eps,
@@ -188,12 +163,9 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     sv[0] = ld_state(sn + fr);
     sv[1] = ld_state(sn + fr + 4);
   };
-  // this work-group's feature tiles
-  const int tz0 = (int)((blockIdx.z * kTiles) / gridDim.z);
-  const int tz1 = (int)(((blockIdx.z + 1) * kTiles) / gridDim.z);
   // the first tile is in flight while the block stages its inputs
   float4 h[8], sv[2];
-  load_tile(min(tz0 + w, kTiles - 1), h, sv);
+  load_tile(w, h, sv);
 
   if (UPDATE && tid < kDim) {
     sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kDim + tid);
@@ -230,9 +202,9 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
 
 
 #pragma unroll 1
-  for (int ks = tz0 + w; ks < tz1; ks += kWaves) {
+  for (int ks = w; ks < kTiles; ks += kWaves) {
     float4 hn[8], svn[2];
-    const bool more = ks + kWaves < tz1;
+    const bool more = ks + kWaves < kTiles;
     if (more) load_tile(ks + kWaves, hn, svn);
 
     const int fr = kFT * ks + 8 * q4;
@@ -369,31 +341,6 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     }
     Elem<Tout>::store(o, (size_t)n * kDim + tid, den != 0.0f ? num / den : 0.0f);
   }
-  if (PART) {
-    if (w == kWaves - 1) {
-      // lane (l16, q4) holds candidates 16*mt + 4*q4 + i at state columns 4*l16 + nt
-      float* pz = scores + ((size_t)n * gridDim.z + blockIdx.z) * sstride * 68;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * mt + 4 * q4 + i;
-          if (cbase + c < n_cand) {
-            float* pc = pz + (size_t)(cbase + c) * 68;
-            *reinterpret_cast<float4*>(pc + 4 * l16) =
-                make_float4(acc[mt][0][i], acc[mt][1][i], acc[mt][2][i], acc[mt][3][i]);
-            if (l16 == 0) {
-              float den = 0.0f;
-#pragma unroll
-              for (int r = 0; r < kWaves; ++r) den += sh.den[r][c];
-              pc[64] = den;
-            }
-          }
-        }
-      }
-    }
-    return;
-  }
   if (w == kWaves - 1) {
     // lane (l16, q4) holds candidates 16*mt + 4*q4 + i at state columns 4*l16 + nt
 #pragma unroll
@@ -488,18 +435,6 @@ hipError_t sre_fused_launch(int N, float eps, const float* H, const float* s, co
   launch_mt<false, float, float>(N, const_cast<float*>(H), const_cast<float*>(s), nullptr, nullptr, nullptr,
                                  nullptr, eps, sre, st);
   prof_end(st);
-  return hipGetLastError();
-}
-
-hipError_t hybrid_score_mfma(int N, const float* H, const float* s, const uint16_t* k, const uint16_t* v,
-                             int T, const int32_t* cache, int cstride, int n_cache, int ev0, int n_cand,
-                             int Z, float* part, int pstride, hipStream_t st) {
-  if (Z < 1 || Z > kTiles || pstride < n_cand) return hipErrorInvalidValue;
-  const CandTokens cand{k, v, T, cache, cstride, n_cache, ev0};
-  hipLaunchKernelGGL((decode_sre_kernel<4, false, false, float, float, CandTokens, true>),
-                     dim3(N, (n_cand + 63) / 64, Z), dim3(kThreadsF), 0, st, const_cast<float*>(H),
-                     const_cast<float*>(s), nullptr, nullptr, nullptr, nullptr, 0.0f, cand, n_cand, 0, part,
-                     pstride, nullptr, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@
 // The host knows every count in advance (they depend only on T, window,
 // refresh and cache_size), so no device value is read back.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kla_device.hpp"
@@ -197,7 +198,7 @@ constexpr int kFD = 64;
 constexpr int kFPhi = kFD * (kFD + 1) / 2;   // 2080
 constexpr int kFoldRows = 128;               // rejected tokens per call, at most
 
-struct FoldPairs {
+struct alignas(16) FoldPairs {
   uint16_t ab[kFPhi];
   constexpr FoldPairs() : ab{} {
     int f = 0;
@@ -230,11 +231,13 @@ __device__ __forceinline__ void split2_8(const float (&x)[8], bf16x8& p0, bf16x8
 }
 
 constexpr int kFKS = kFPhi / 32;             // 65 k-steps
-constexpr int kFoldKsPerWG = 8;              // two per wave
+constexpr int kFoldKsPerWG = 4;              // one per wave
 
-// index of fragment (n, ks, piece, nt, lane) in uint4 units
+// index of fragment (n, ks, piece, nt, lane) in uint4 units; three exact
+// bf16 pieces per value (the readout uses the first two)
+constexpr int kHFPieces = 3;
 __device__ __forceinline__ size_t hf_index(int n, int ks, int pc, int nt, int lane) {
-  return ((((size_t)n * kFKS + ks) * 2 + pc) * 5 + nt) * 64 + lane;
+  return ((((size_t)n * kFKS + ks) * kHFPieces + pc) * 5 + nt) * 64 + lane;
 }
 
 __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restrict__ H, float* __restrict__ s,
@@ -338,10 +341,209 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
     for (int nt = 0; nt < 5; ++nt) {
       const float x[8] = {acc[0][nt][0], acc[0][nt][1], acc[0][nt][2], acc[0][nt][3],
                           acc[1][nt][0], acc[1][nt][1], acc[1][nt][2], acc[1][nt][3]};
-      bf16x8 p0, p1;
-      split2_8(x, p0, p1);
+      bf16x8 p0, p1, p2;
+      split3_8(x, p0, p1, p2);
       HF[hf_index(n, ks, 0, nt, lane)] = __builtin_bit_cast(uint4, p0);
       HF[hf_index(n, ks, 1, nt, lane)] = __builtin_bit_cast(uint4, p1);
+      HF[hf_index(n, ks, 2, nt, lane)] = __builtin_bit_cast(uint4, p2);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- matrix-core scoring (d = 64, bf16 in)
+//
+// Self-recall partials of the refresh candidates (LoLA page, self-recall
+// error): for candidate c and the work-group's feature k-steps,
+//   num_c = sum_f phi_f(k_c) H_f,   den_c = sum_f phi_f(k_c) s_f,
+// written to part[((n Z + z) pstride + c) 68 + {0..63, 64}] for the
+// selection to add over z. Grid (heads, candidate blocks of 64, Z); wave w
+// takes k-steps z 65 / Z + w, + 4, ... The B operands are the state
+// fragments the fold wrote (three exact bf16 pieces h0 + h1 + h2, rows in
+// the fold's order: lane quarter q4 holds features 32 ks + 4 q4 + j and
+// 32 ks + 16 + 4 q4 + j, j < 4); the candidate features, in the same order,
+// are split into two pieces p0 + p1 and the product is taken as
+// p0 (h0 + h1 + h2) + p1 h0 in float32 (dropped terms below 2^-16
+// relative). Denominators stay in float32 on the vector units.
+constexpr int kScoreCand = 64;
+struct ScoreLds {
+  uint16_t tab[kFPhi];
+  float den[kWavesF][kScoreCand];
+  union {
+    float ck[kScoreCand][kFD + 1];   // candidate keys (float32), padded rows
+    float4 red[4][4][64];            // numerator partials, accumulator layout
+  };
+};
+
+__global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
+    const uint4* __restrict__ HF, const float* __restrict__ s, const uint16_t* __restrict__ k, int T,
+    const int32_t* __restrict__ cache, int cstride, int n_cache, int ev0, int n_cand,
+    float* __restrict__ part, int pstride) {
+  __shared__ __align__(16) ScoreLds sh;
+  const int n = blockIdx.x;
+  const int cbase = kScoreCand * blockIdx.y;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int Z = gridDim.z;
+  const int tz0 = (int)((blockIdx.z * kFKS) / Z);
+  const int tz1 = (int)(((blockIdx.z + 1) * kFKS) / Z);
+  const float* sn = s + (size_t)n * kFPhi;
+
+  auto load_b = [&](int ks, uint4 (&b)[3][4], float4 (&sv)[2]) {
+#pragma unroll
+    for (int pc = 0; pc < 3; ++pc)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) b[pc][nt] = HF[hf_index(n, ks, pc, nt, lane)];
+    sv[0] = *reinterpret_cast<const float4*>(sn + 32 * ks + 4 * q4);
+    sv[1] = *reinterpret_cast<const float4*>(sn + 32 * ks + 16 + 4 * q4);
+  };
+  uint4 bf[3][4];
+  float4 sv[2];
+  const int ks_first = min(tz0 + w, kFKS - 1);
+  load_b(ks_first, bf, sv);
+
+  // candidate keys: four threads per candidate, 16 dimensions each
+  {
+    const int c = tid >> 2;
+    const int qd = tid & 3;
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = 0.0f;
+    if (cbase + c < n_cand) {
+      const int cc = cbase + c;
+      const int tok = cc < n_cache ? cache[(size_t)n * cstride + cc] : ev0 + (cc - n_cache);
+      const uint4* kp = reinterpret_cast<const uint4*>(k + ((size_t)n * T + tok) * kFD + 16 * qd);
+      const uint4 u0 = kp[0], u1 = kp[1];
+      const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x[2 * j] = __uint_as_float(uw[j] << 16);
+        x[2 * j + 1] = __uint_as_float(uw[j] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sh.ck[c][16 * qd + j] = x[j];
+  }
+  for (int i = tid; i < kFPhi / 8; i += kThreads)
+    reinterpret_cast<uint4*>(sh.tab)[i] = reinterpret_cast<const uint4*>(kFoldPairs.ab)[i];
+  __syncthreads();
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dacc[4] = {0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 1
+  for (int ks = tz0 + w; ks < tz1; ks += kWavesF) {
+    uint4 bn[3][4];
+    float4 svn[2];
+    const bool more = ks + kWavesF < tz1;
+    if (more) load_b(ks + kWavesF, bn, svn);
+    // this lane's eight features and their weights
+    const uint2 t0 = *reinterpret_cast<const uint2*>(&sh.tab[32 * ks + 4 * q4]);
+    const uint2 t1 = *reinterpret_cast<const uint2*>(&sh.tab[32 * ks + 16 + 4 * q4]);
+    const uint32_t words[4] = {t0.x, t0.y, t1.x, t1.y};
+    int pa[8], pb[8];
+    float wt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = (j & 1) ? (words[j >> 1] >> 16) : (words[j >> 1] & 0xFFFFu);
+      pa[j] = u & 0xFF;
+      pb[j] = u >> 8;
+      wt[j] = pa[j] == pb[j] ? 1.0f : 1.41421356237309504880f;
+    }
+    const float sj[8] = {sv[0].x, sv[0].y, sv[0].z, sv[0].w, sv[1].x, sv[1].y, sv[1].z, sv[1].w};
+    bf16x8 B[3][4];
+#pragma unroll
+    for (int pc = 0; pc < 3; ++pc)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) B[pc][nt] = __builtin_bit_cast(bf16x8, bf[pc][nt]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float* kc = sh.ck[16 * mt + l16];
+      float p[8];
+      float dd = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = kc[pa[j]] * kc[pb[j]] * wt[j];
+        dd += p[j] * sj[j];
+      }
+      dacc[mt] += dd;
+      bf16x8 A0, A1;
+      split2_8(p, A0, A1);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B[0][nt], acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B[1][nt], acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B[2][nt], acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B[0][nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bf[pc][nt] = bn[pc][nt];
+      sv[0] = svn[0];
+      sv[1] = svn[1];
+    }
+  }
+
+  // denominators: lane l16 of block mt is candidate 16 mt + l16
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    float d = dacc[mt];
+    d += __shfl_xor(d, 16, 64);
+    d += __shfl_xor(d, 32, 64);
+    if (q4 == 0) sh.den[w][16 * mt + l16] = d;
+  }
+  // numerators: waves add into the LDS copy in turn; the last one keeps the
+  // sum (the first barrier also ends every read of the candidate keys, whose
+  // LDS the partials reuse)
+  for (int r = 0; r < kWavesF; ++r) {
+    __syncthreads();
+    if (w == r) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          f32x4 x = acc[mt][nt];
+          if (r > 0) {
+            const float4 y = sh.red[mt][nt][lane];
+            x[0] += y.x;
+            x[1] += y.y;
+            x[2] += y.z;
+            x[3] += y.w;
+          }
+          acc[mt][nt] = x;
+          if (r + 1 < kWavesF) sh.red[mt][nt][lane] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    }
+  }
+  if (w == kWavesF - 1) {
+    // lane (l16, q4) holds candidates 16 mt + 4 q4 + i at state columns 4 l16 + nt
+    float* pz = part + ((size_t)n * Z + blockIdx.z) * pstride * 68;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * mt + 4 * q4 + i;
+        if (cbase + c < n_cand) {
+          float* pc = pz + (size_t)(cbase + c) * 68;
+          *reinterpret_cast<float4*>(pc + 4 * l16) =
+              make_float4(acc[mt][0][i], acc[mt][1][i], acc[mt][2][i], acc[mt][3][i]);
+          if (l16 == 0) {
+            float den = 0.0f;
+#pragma unroll
+            for (int r = 0; r < kWavesF; ++r) den += sh.den[r][c];
+            pc[64] = den;
+          }
+        }
+      }
     }
   }
 }
@@ -882,11 +1084,13 @@ constexpr int kCandMax = 256;  // candidates per refresh, at most (cache + evict
 // larger (score, token id) keys, so ranks are distinct; the keep best go to
 // the cache in ascending token order (their place is the number of kept
 // tokens with a lower id) and the rest, in rank order, to the rejected list.
-// The result is the one the sort of the generic form gives.
+// The result is the one the sort of the generic form gives. The new cache goes
+// to cache_out (not the cache it reads).
 constexpr int kSelThreads = 1024;
 __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
     const float* __restrict__ part, int Z, int pstride, const uint16_t* __restrict__ v, int T,
-    float eps, int32_t* __restrict__ cache, int cstride, int n_cache, int ev0, int n_cand, int keep,
+    float eps, const int32_t* __restrict__ cache, int cstride, int32_t* __restrict__ cache_out,
+    int ostride, int n_cache, int ev0, int n_cand, int keep,
     int32_t* __restrict__ rejected, int rstride, int32_t* __restrict__ trace, size_t trace_row_stride,
     int block, int nblocks, float* __restrict__ scores, int sstride) {
   static_assert(kSelThreads == 4 * kCandMax, "four threads per candidate");
@@ -909,6 +1113,7 @@ __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) num[j] = 0.0f;
     float den = 0.0f;
+#pragma unroll 5
     for (int z = 0; z < Z; ++z) {
       const float* pc = part + (((size_t)n * Z + z) * pstride + c) * 68;
       const float4* p4 = reinterpret_cast<const float4*>(pc + 16 * qd);
@@ -945,6 +1150,7 @@ __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
   int rank = 0;
   if (live) {
     key = keys[c];
+#pragma unroll 8
     for (int j = qd; j < n_cand; j += 4) rank += keys[j] > key ? 1 : 0;
   }
   rank += __shfl_xor(rank, 1, 64);
@@ -954,6 +1160,7 @@ __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
   int pos = 0;
   if (live && rank < keep) {
     const int32_t id = tok[c];
+#pragma unroll 8
     for (int j = qd; j < n_cand; j += 4) pos += kid[j] < id ? 1 : 0;
   }
   pos += __shfl_xor(pos, 1, 64);
@@ -963,7 +1170,7 @@ __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
     if (rank >= keep) {
       rejected[(size_t)n * rstride + rank - keep] = id;
     } else {
-      cache[(size_t)n * cstride + pos] = id;
+      cache_out[(size_t)n * ostride + pos] = id;
       if (trace) trace[((size_t)n * nblocks + block) * trace_row_stride + pos] = id;
     }
   }
@@ -973,15 +1180,17 @@ struct Ws {
   float* H;
   float* s;
   int32_t* cache;
+  int32_t* cache2;  // second cache buffer (matrix-core path only)
   float* scores;
   int32_t* rejected;
-  uint4* HF;  // readout fragments of the state (matrix-core path only)
+  uint4* HF;   // readout fragments of the state (matrix-core path only) ...
+  uint4* HF2;  // ... and their second buffer
   float* xp;  // readout split partials [N][refresh][kRNS][66] (matrix-core path only)
   float* sp;  // score split partials [N][kSZ][kCStride][68] (matrix-core path only)
 };
 
 bool matrix_path(const HybridArgs& a) { return a.dqk == 64 && a.dv == 64 && a.in_bf16; }
-size_t hf_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kFKS * 2 * 5 * 64 * sizeof(uint4)); }
+size_t hf_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kFKS * kHFPieces * 5 * 64 * sizeof(uint4)); }
 constexpr int kRNS = 8;  // readout splits per (head, query block)
 size_t xp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * a.refresh * kRNS * 66 * sizeof(float)); }
 
@@ -1007,12 +1216,19 @@ Ws carve(const HybridArgs& a, void* ws) {
   }
   w.cache = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
+  w.cache2 = nullptr;
+  if (matrix_path(a)) {
+    w.cache2 = reinterpret_cast<int32_t*>(p);
+    p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
+  }
   w.scores = reinterpret_cast<float*>(p);
   p += align_up((size_t)a.N * kCStride * sizeof(float));
   w.rejected = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   w.HF = matrix_path(a) ? reinterpret_cast<uint4*>(p) : nullptr;
   if (w.HF) p += hf_bytes(a);
+  w.HF2 = matrix_path(a) ? reinterpret_cast<uint4*>(p) : nullptr;
+  if (w.HF2) p += hf_bytes(a);
   w.xp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
   if (w.xp) p += xp_bytes(a);
   w.sp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
@@ -1038,9 +1254,6 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
   hipLaunchKernelGGL(fill_kernel_f32, dim3(1024), dim3(256), 0, st, w.H, (size_t)N * D * DV, 0.0f);
   hipLaunchKernelGGL(fill_kernel_f32, dim3(64), dim3(256), 0, st, w.s, (size_t)N * D, 0.0f);
   hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, w.cache, (size_t)N * kCStride, -1);
-  if (w.HF)
-    hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, reinterpret_cast<int32_t*>(w.HF),
-                       hf_bytes(a) / sizeof(int32_t), 0);
   if (a.trace && a.cache_size > 0)
     hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, a.trace,
                        (size_t)N * nblocks * a.cache_size, -1);
@@ -1063,49 +1276,24 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
         n_cache = n_cand;
       } else {
         prof_begin(st);
-        if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
-          // matrix cores, float32-faithful (split bf16 operands)
-          e = hybrid_score_mfma(N, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache, f_prev, n_cand, kSZ,
-                                w.sp, kCStride, st);
-          if (e != hipSuccess) return e;
-          hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ, kCStride, v,
-                             a.T, a.eps, w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,
-                             kCStride, a.trace, (size_t)a.cache_size, b, nblocks, w.scores, kCStride);
-        } else {
-          hipLaunchKernelGGL((hyb_score_kernel<DQK, DV, Tin>), dim3((n_cand + 63) / 64, N),
-                             dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache,
-                             f_prev, n_cand, w.scores, kCStride, a.eps);
-          hipLaunchKernelGGL(hyb_select_kernel, dim3(N), dim3(kThreads), 0, st, w.scores, kCStride,
-                             w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,
-                             kCStride, a.trace, (size_t)a.cache_size, b, nblocks);
-        }
+        hipLaunchKernelGGL((hyb_score_kernel<DQK, DV, Tin>), dim3((n_cand + 63) / 64, N),
+                           dim3(kThreads), 0, st, w.H, w.s, k, v, a.T, w.cache, kCStride, n_cache,
+                           f_prev, n_cand, w.scores, kCStride, a.eps);
+        hipLaunchKernelGGL(hyb_select_kernel, dim3(N), dim3(kThreads), 0, st, w.scores, kCStride,
+                           w.cache, kCStride, n_cache, f_prev, n_cand, a.cache_size, w.rejected,
+                           kCStride, a.trace, (size_t)a.cache_size, b, nblocks);
         prof_end(st);
         KLA_CHECK();
-        if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
-          hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFKS + kFoldKsPerWG - 1) / kFoldKsPerWG, N),
-                             dim3(kThreads), 0, st, w.H, w.s, w.HF, k, v, a.T, w.rejected, kCStride,
-                             n_cand - a.cache_size);
-        } else {
-          hipLaunchKernelGGL((hyb_fold_kernel<DQK, DV, Tin>), dim3(S, N), dim3(kThreads), 0, st,
-                             w.H, w.s, k, v, a.T, w.rejected, kCStride, n_cand - a.cache_size, Fs);
-        }
+        hipLaunchKernelGGL((hyb_fold_kernel<DQK, DV, Tin>), dim3(S, N), dim3(kThreads), 0, st,
+                           w.H, w.s, k, v, a.T, w.rejected, kCStride, n_cand - a.cache_size, Fs);
         KLA_CHECK();
         n_cache = a.cache_size;
       }
     }
     f_prev = f;
-    if constexpr (DQK == 64 && DV == 64 && std::is_same<Tin, uint16_t>::value) {
-      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N, kRNS), dim3(kRT),
-                         0, st, q, k, v, o, a.T, w.HF, w.cache, kCStride, n_cache, b0, b1, f, a.scale, a.eps,
-                         kRNS, w.xp, a.refresh);
-      if (kRNS > 1)
-        hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>), dim3(((b1 - b0) * kFD + kThreads - 1) / kThreads, N),
-                           dim3(kThreads), 0, st, w.xp, a.refresh, kRNS, o, a.T, b0, b1, a.eps);
-    } else {
-      hipLaunchKernelGGL((hyb_readout_kernel<DQK, DV, Tin, Tout>), dim3((b1 - b0 + 15) / 16, N),
-                         dim3(kThreads), 0, st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride,
-                         n_cache, b0, b1, f, a.scale, a.eps);
-    }
+    hipLaunchKernelGGL((hyb_readout_kernel<DQK, DV, Tin, Tout>), dim3((b1 - b0 + 15) / 16, N),
+                       dim3(kThreads), 0, st, q, k, v, o, a.T, w.H, w.s, w.cache, kCStride,
+                       n_cache, b0, b1, f, a.scale, a.eps);
     KLA_CHECK();
   }
   if (a.cache_T && a.cache_size > 0) {
@@ -1117,8 +1305,155 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
   return hipSuccess;
 }
 
+// A second stream per device for the readouts of the matrix-core path, and
+// the events that order it against the caller's stream. Default priority.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, ready = nullptr, used[2] = {nullptr, nullptr};
+};
+
+hipError_t side_stream(SideStream** out) {
+  static SideStream pool[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = pool[dev];
+  static std::mutex init_mu;
+  std::lock_guard<std::mutex> g(init_mu);
+  if (!ss.s) {
+    hipStream_t s;
+    if ((e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking)) != hipSuccess) return e;
+    hipEvent_t* evs[5] = {&ss.fork, &ss.join, &ss.ready, &ss.used[0], &ss.used[1]};
+    for (hipEvent_t* p : evs)
+      if ((e = hipEventCreateWithFlags(p, hipEventDisableTiming)) != hipSuccess) return e;
+    ss.s = s;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
+// The matrix-core path (d = 64, bf16 in). The refresh chain (score, select,
+// fold, or append) runs on the caller's stream; each block's readout and
+// combine run on the side stream once the chain has produced the block's
+// state and cache. The fold writes the state fragments and the selection
+// writes the cache into the buffer the previous block's readout does not
+// read (two of each, swapped at every refresh), so the readout of block b
+// overlaps the scoring and selection of block b + 1; a buffer is rewritten
+// only after the readout that last read it has finished (event used[x]).
+template <typename Tout>
+hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
+  const Ws w = carve(a, ws);
+  const int N = a.N;
+  const int nblocks = (a.T + a.refresh - 1) / a.refresh;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  Tout* o = static_cast<Tout*>(a.o);
+  SideStream* ss = nullptr;
+  hipError_t e = side_stream(&ss);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(ss->mu);
+  const hipStream_t sb = ss->s;
+#define KLA_TRY(x)                       \
+  do {                                   \
+    e = (x);                             \
+    if (e != hipSuccess) return e;       \
+  } while (0)
+#define KLA_CHECK() KLA_TRY(hipGetLastError())
+  int32_t* cache[2] = {w.cache, w.cache2};
+  uint4* hf[2] = {w.HF, w.HF2};
+  bool used[2] = {false, false};
+  hipLaunchKernelGGL(fill_kernel_f32, dim3(1024), dim3(256), 0, st, w.H, (size_t)N * kFPhi * kFD, 0.0f);
+  hipLaunchKernelGGL(fill_kernel_f32, dim3(64), dim3(256), 0, st, w.s, (size_t)N * kFPhi, 0.0f);
+  hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, cache[0], (size_t)N * kCStride, -1);
+  hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, cache[1], (size_t)N * kCStride, -1);
+  hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, reinterpret_cast<int32_t*>(hf[0]),
+                     hf_bytes(a) / sizeof(int32_t), 0);
+  if (a.trace && a.cache_size > 0)
+    hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, a.trace,
+                       (size_t)N * nblocks * a.cache_size, -1);
+  KLA_CHECK();
+  // the side stream starts after everything the caller queued so far
+  KLA_TRY(hipEventRecord(ss->fork, st));
+  KLA_TRY(hipStreamWaitEvent(sb, ss->fork, 0));
+  int cur = 0;
+  // everything after the fork also joins the side stream back, on error too
+  const hipError_t loop_err = [&]() -> hipError_t {
+    hipError_t e;
+    int n_cache = 0;
+    int f_prev = 0;
+    for (int b = 0; b < nblocks; ++b) {
+      const int b0 = b * a.refresh;
+      const int b1 = std::min(a.T, b0 + a.refresh);
+      const int f = std::max(0, b0 - a.window);
+      const int n_ev = f - f_prev;
+      if (n_ev > 0) {
+        const int n_cand = n_cache + n_ev;
+        if (n_cand <= a.cache_size) {
+          // appends past the entries any queued readout reads
+          hipLaunchKernelGGL(append_kernel, dim3(N), dim3(256), 0, st, cache[cur], kCStride, n_cache,
+                             f_prev, n_ev);
+          KLA_CHECK();
+          n_cache = n_cand;
+        } else {
+          const int nxt = cur ^ 1;
+          // the cache and fragment buffers about to be rewritten are free
+          if (used[nxt]) KLA_TRY(hipStreamWaitEvent(st, ss->used[nxt], 0));
+          prof_begin(st);
+          // float32-faithful matrix-core score partials (split bf16 operands)
+          hipLaunchKernelGGL(hyb_score_frag_kernel, dim3(N, (n_cand + kScoreCand - 1) / kScoreCand, kSZ),
+                             dim3(kThreads), 0, st, hf[cur], w.s, k, a.T, cache[cur], kCStride, n_cache, f_prev,
+                             n_cand, w.sp, kCStride);
+          hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ, kCStride, v,
+                             a.T, a.eps, cache[cur], kCStride, cache[nxt], kCStride, n_cache, f_prev, n_cand,
+                             a.cache_size, w.rejected, kCStride, a.trace, (size_t)a.cache_size, b, nblocks,
+                             w.scores, kCStride);
+          prof_end(st);
+          KLA_CHECK();
+          hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFKS + kFoldKsPerWG - 1) / kFoldKsPerWG, N),
+                             dim3(kThreads), 0, st, w.H, w.s, hf[nxt], k, v, a.T, w.rejected, kCStride,
+                             n_cand - a.cache_size);
+          KLA_CHECK();
+          n_cache = a.cache_size;
+          cur = nxt;
+        }
+      }
+      f_prev = f;
+      // the block's readout, on the side stream, after the chain so far
+      KLA_TRY(hipEventRecord(ss->ready, st));
+      KLA_TRY(hipStreamWaitEvent(sb, ss->ready, 0));
+      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N, kRNS), dim3(kRT), 0,
+                         sb, q, k, v, o, a.T, hf[cur], cache[cur], kCStride, n_cache, b0, b1, f, a.scale, a.eps,
+                         kRNS, w.xp, a.refresh);
+      hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>),
+                         dim3(((b1 - b0) * kFD + kThreads - 1) / kThreads, N), dim3(kThreads), 0, sb, w.xp,
+                         a.refresh, kRNS, o, a.T, b0, b1, a.eps);
+      KLA_CHECK();
+      KLA_TRY(hipEventRecord(ss->used[cur], sb));
+      used[cur] = true;
+    }
+    return hipSuccess;
+  }();
+  // the caller's stream continues after the last readout
+  KLA_TRY(hipEventRecord(ss->join, sb));
+  KLA_TRY(hipStreamWaitEvent(st, ss->join, 0));
+  if (loop_err != hipSuccess) return loop_err;
+  if (a.cache_T && a.cache_size > 0) {
+    hipLaunchKernelGGL(copy_rows_kernel, dim3(N), dim3(256), 0, st, a.cache_T, a.cache_size,
+                       cache[cur], kCStride);
+    KLA_CHECK();
+  }
+#undef KLA_CHECK
+#undef KLA_TRY
+  return hipSuccess;
+}
+
 template <int DQK, int DV>
 hipError_t run_dt(const HybridArgs& a, void* ws, hipStream_t st) {
+  if (DQK == 64 && DV == 64 && a.in_bf16)
+    return a.out_bf16 ? run_matrix<uint16_t>(a, ws, st) : run_matrix<float>(a, ws, st);
   if (a.in_bf16)
     return a.out_bf16 ? run<DQK, DV, uint16_t, uint16_t>(a, ws, st)
                       : run<DQK, DV, uint16_t, float>(a, ws, st);
@@ -1135,7 +1470,8 @@ size_t hybrid_workspace(const HybridArgs& a) {
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   b += align_up((size_t)a.N * kCStride * sizeof(float));
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
-  if (matrix_path(a)) b += hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
+  if (matrix_path(a))
+    b += align_up((size_t)a.N * kCStride * sizeof(int32_t)) + 2 * hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
   return b;
 }
 

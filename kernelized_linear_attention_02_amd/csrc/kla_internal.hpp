@@ -79,15 +79,6 @@ hipError_t decode_fused_launch(const DecodeArgs& a, const SreArgs& sre, hipStrea
 hipError_t sre_fused_launch(int N, float eps, const float* H, const float* s, const SreArgs& sre,
                             hipStream_t st);
 
-// Self-recall partials of hybrid candidates (bf16 token rows picked by id;
-// d = 64) on the matrix cores, for the hybrid prefill's refresh steps: the
-// feature sum is split over Z work-groups per candidate block, and
-// part[((n Z + z) pstride + c) 68 + {0..63, 64}] receives the numerator and
-// denominator partials of candidate c (no eps).
-hipError_t hybrid_score_mfma(int N, const float* H, const float* s, const uint16_t* k, const uint16_t* v,
-                             int T, const int32_t* cache, int cstride, int n_cache, int ev0, int n_cand,
-                             int Z, float* part, int pstride, hipStream_t st);
-
 size_t sre_workspace(int N, int dqk, int dv, const SreArgs& s);
 hipError_t sre_launch(int N, int dqk, int dv, float eps, const float* H, const float* s,
                       const SreArgs& sre, void* ws, hipStream_t st);
