@@ -372,12 +372,12 @@ def test_decode_sre_4096_full_size(K):
 
 # ------------------------------------------------------------------ hybrid
 
-def _hybrid_check(K, c, heads, dtype, rtol):
+def _hybrid_check(K, c, heads, dtype, rtol, eps=0.0, out_dtype=None):
     B, H, T, d = c.q.shape
     scale = 1.0 / math.sqrt(d)
     o, extra = K.hybrid_prefill(dev(c.q, dtype), dev(c.k, dtype), dev(c.v, dtype), c.window,
-                                c.cache_size, c.refresh, scale, return_state=True,
-                                return_cache=True, return_trace=True)
+                                c.cache_size, c.refresh, scale, eps=eps, return_state=True,
+                                return_cache=True, return_trace=True, out_dtype=out_dtype)
     torch.cuda.synchronize()
     go, gH, gs = host(o), host(extra["H"]), host(extra["s"])
     gc = extra["cache"].cpu().numpy()
@@ -393,7 +393,7 @@ def _hybrid_check(K, c, heads, dtype, rtol):
                 return keep
             return np.array(g)
         ref = O.hybrid_prefill(c.q[b, h], c.k[b, h], c.v[b, h], c.window, c.cache_size, c.refresh,
-                               scale, choose=choose)
+                               scale, eps=eps, choose=choose)
         assert not bad, f"head ({b},{h}): selections differ outside near-ties at blocks {bad[:5]}"
         nblk = gt.shape[2]
         for blk in range(nblk):
@@ -411,6 +411,19 @@ def _hybrid_check(K, c, heads, dtype, rtol):
 def test_hybrid_small_bf16(K, d, W, lam, R, T):
     c = S.hybrid_case("small", 1, 2, T, d, W, lam, R, seed=60 + d + T, dup_frac=0.1)
     _hybrid_check(K, c, [(0, 0), (0, 1)], torch.bfloat16, RTOL_BF16)
+
+
+@pytest.mark.parametrize("W,lam,R,T,H,eps,out", [
+    (32, 0, 16, 200, 2, 0.0, torch.bfloat16),     # empty cache: every evicted pair folds
+    (0, 16, 16, 190, 3, 0.0, torch.bfloat16),     # no window, three heads, ragged last block
+    (64, 128, 128, 1000, 2, 0.0, torch.float32),  # largest cache + refresh (256 candidates)
+    (40, 24, 7, 333, 3, 0.5, torch.float32),      # odd refresh, eps > 0, float32 output
+])
+def test_hybrid_matrix_path_edge_cases(K, W, lam, R, T, H, eps, out):
+    # d = 64 with bf16 inputs takes the matrix-core path (two streams,
+    # fragment scorer, counting selection)
+    c = S.hybrid_case("edge", 1, H, T, 64, W, lam, R, seed=90 + T + R, dup_frac=0.1)
+    _hybrid_check(K, c, [(0, h) for h in range(H)], torch.bfloat16, RTOL_BF16, eps=eps, out_dtype=out)
 
 
 def test_hybrid_special_cases_f32(K):
