@@ -25,7 +25,9 @@
 // read out against the state of the chunk start:
 //   readout  num_x = phi(Q) H (MFMA), den_x = phi(Q) s (bf16 dot products),
 // partial over the slice, written as bf16 to a workspace [head, chunk,
-// slice, d_v + 1, chunk]. A head's work-groups are placed on one XCD
+// slice, token tile, 16 x (d_v + 1)] in the MFMA accumulator order, so that
+// both its writes and the finish kernel's reads are whole 512-byte runs per
+// wave. A head's work-groups are placed on one XCD
 // (work-groups are dealt to the 8 XCDs in turn), so their shared q, k and v
 // reads meet in one L2.
 //
@@ -55,6 +57,9 @@ constexpr int kTW = 5;                            // tiles per wave, at most
 constexpr int kMinSlices = 8;                     // tiles per work-group <= 17
 constexpr int kKR = kDim + 4;                     // k^T rows; 64..67 are zero
 constexpr int kAcc = kDim + 1;                    // accumulator row: num | den
+// Slice partials of one 16-token tile (bf16): the numerators in MFMA
+// accumulator order [n-tile][lane][4 tokens], then the 16 denominators.
+constexpr int kTileAcc = 16 * kAcc;
 
 __device__ __forceinline__ void tile_coords(int t, int& i, int& j) {
   int start = 0;
@@ -441,19 +446,20 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
 #pragma unroll
           for (int nt4 = 0; nt4 < 4; ++nt4) ra[nt4] = mfma(A, B[nt4], ra[nt4]);
         }
-        // lane holds num for tokens w*16 + 4*q4 + i, column 16*nt4 + l16:
-        // four consecutive tokens of one column, stored as bf16
-        uint16_t* pc = part + ((((size_t)n * NC + c) * S + slice) * kAcc) * C + (st % SUB) * CS + w * 16;
+        // lane holds num for tokens w*16 + 4*q4 + i, column 16*nt4 + l16;
+        // the partial block of this token tile keeps that layout (bf16)
+        const int tt = ((st % SUB) * CS) / 16 + w;
+        uint16_t* pc = part + ((((size_t)n * NC + c) * S + slice) * (C / 16) + tt) * kTileAcc;
 #pragma unroll
         for (int nt4 = 0; nt4 < 4; ++nt4) {
           bf16x4 b;
 #pragma unroll
           for (int i = 0; i < 4; ++i) b[i] = (__bf16)ra[nt4][i];
-          *reinterpret_cast<bf16x4*>(pc + (size_t)(16 * nt4 + l16) * C + 4 * q4) = b;
+          *reinterpret_cast<bf16x4*>(pc + (nt4 * 64 + lane) * 4) = b;
         }
         dn += __shfl_xor(dn, 16, 64);
         dn += __shfl_xor(dn, 32, 64);
-        if (q4 == 0) pc[(size_t)kDim * C + l16] = __builtin_bit_cast(uint16_t, (__bf16)dn);
+        if (q4 == 0) pc[4 * 64 * 4 + l16] = __builtin_bit_cast(uint16_t, (__bf16)dn);
         (void)L;
       }
       lds_barrier();  // (B2)
@@ -560,16 +566,16 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
     float den[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) den[i] = sh.den[mq * 16 + 4 * q4 + i] + eps;
-    const uint16_t* pc = part + ((size_t)(n * gridDim.x + blockIdx.x) * S) * kAcc * C + mq * 16 + 4 * q4;
+    const uint16_t* pc = part + ((size_t)(n * gridDim.x + blockIdx.x) * S * (C / 16) + mq) * kTileAcc;
     for (int s = 0; s < S; ++s) {
-      const uint16_t* ps = pc + (size_t)s * kAcc * C;
+      const uint16_t* ps = pc + (size_t)s * (C / 16) * kTileAcc;
 #pragma unroll
       for (int nt4 = 0; nt4 < 4; ++nt4) {
-        const bf16x4 b = *reinterpret_cast<const bf16x4*>(ps + (size_t)(16 * nt4 + l16) * C);
+        const bf16x4 b = *reinterpret_cast<const bf16x4*>(ps + (nt4 * 64 + lane) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ra[nt4][i] += (float)b[i];
       }
-      const bf16x4 b = *reinterpret_cast<const bf16x4*>(ps + (size_t)kDim * C);
+      const bf16x4 b = *reinterpret_cast<const bf16x4*>(ps + 4 * 64 * 4 + 4 * q4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) den[i] += (float)b[i];
     }
