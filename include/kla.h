@@ -23,8 +23,9 @@
  * Conventions shared by every call:
  *   - Memory: every tensor pointer is a device pointer owned by the caller.
  *     The library never allocates or frees device memory and keeps no
- *     per-call state; scratch memory comes from the caller through `ws`,
- *     sized by the matching *_workspace_size query.
+ *     per-call state (the one exception, a per-device stream and its events
+ *     for kla_hybrid_prefill, is described there); scratch memory comes from
+ *     the caller through `ws`, sized by the matching *_workspace_size query.
  *   - Layout: tensors are dense row-major (C order), shapes given below.
  *     N = B*H heads, ordered (b, h). The state is H [N, D, d_v] and
  *     s [N, D], float32, in the coordinate order and sqrt(2) scaling above.
@@ -206,6 +207,14 @@ KLA_API kla_status_t kla_sre_select(int N, int d_qk, int d_v, float eps, const f
  *                     (ascending); rows of blocks without one are all -1.
  * Supported: d_qk, d_v in {16, 32, 64}; 1 <= refresh <= 128; window >= 0;
  * 0 <= cache_size and cache_size + refresh <= 256; softmax_scale finite.
+ *
+ * Streams: with d_qk = d_v = 64 and bf16 inputs, each block's readout runs on
+ * a second stream that the library creates on the device at first use
+ * (default priority, kept until the process ends), forked from `stream`
+ * inside the call and joined back into it before the call returns; work
+ * queued on `stream` afterwards is ordered after every kernel of the call.
+ * Concurrent calls on one device from several host threads serialise while
+ * they enqueue.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int window, cache_size, refresh;
