@@ -124,6 +124,25 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
                          float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kla_prefill_quadratic - the same causal outputs in the quadratic form
+ * (KATA §2.3, the first of its two operating points: a FlashAttention-style
+ * forward that never forms the state). Since phi(q) . phi(k) = (q . k)^2,
+ *   num_t = sum_{i<=t} (q_t . k_i)^2 v_i,  den_t = sum_{i<=t} (q_t . k_i)^2,
+ *   o_t = num_t / (den_t + eps)  (0 when that denominator is 0),
+ * equal to kla_prefill's outputs up to rounding. Work grows as T^2 (against
+ * T D for the state form), so it is the cheaper form up to T of about
+ * 2 D d_v / (d_qk + d_v) tokens. No state is produced and no workspace is
+ * needed.
+ *
+ *   q, k, v : [B, H, T, 64] bf16 (required);  o : [B, H, T, 64], out_dtype
+ *             (required).
+ * Supported: d_qk = d_v = 64, in_dtype bf16, out_dtype bf16 or float32;
+ * other shapes return KLA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+KLA_API kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const void* k,
+                                   const void* v, void* o, kla_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Self-recall error and selection (LoLA, the self-recall-error section and
  * "Estratégia de Inferência" item 2).
  *

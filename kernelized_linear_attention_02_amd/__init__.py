@@ -5,6 +5,7 @@ The computation lives in libkla.so (hand-written HIP kernels behind the C
 ABI of include/kla.h); this package only marshals arguments to it:
 
   prefill         chunked causal prefill over the float32 state (H, s)
+  prefill_quadratic  the same outputs in the quadratic (no state) form
   decode_step     one recurrent token, optionally with self-recall scoring
   sre_select      self-recall-error scoring and top-k selection
   hybrid_prefill  sliding window + linear state + sparse cache
@@ -20,11 +21,12 @@ from ._binding import (  # noqa: F401
     load_library,
     phi_dim,
     prefill,
+    prefill_quadratic,
     prefill_uses_matrix_cores,
     profile_enable,
     profile_read,
     sre_select,
 )
 
-__all__ = ["prefill", "decode_step", "sre_select", "hybrid_prefill", "phi_dim", "load_library",
+__all__ = ["prefill", "prefill_quadratic", "decode_step", "sre_select", "hybrid_prefill", "phi_dim", "load_library",
            "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

@@ -20,7 +20,7 @@ KLA_F32, KLA_BF16 = 0, 1
 
 EXPORTS = (
     "kla_abi_version", "kla_phi_dim", "kla_status_string", "kla_last_error",
-    "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill",
+    "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill", "kla_prefill_quadratic",
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill",
@@ -78,6 +78,7 @@ def load_library(path: str = LIB_PATH):
         "kla_prefill_matrix_path": (i, [shp, i]),
         "kla_prefill_workspace_size": (i, [shp, i, i, szp]),
         "kla_prefill": (i, [shp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kla_prefill_quadratic": (i, [shp, vp, vp, vp, vp, vp]),
         "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
         "kla_decode_step": (i, [i, i, i, f, vp, vp, vp, vp, vp, i, vp, i, srp, vp, sz, vp]),
         "kla_sre_workspace_size": (i, [i, i, i, srp, szp]),
@@ -203,6 +204,32 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     if not outputs:
         return HT, sT
     return (o, HT, sT) if return_state else o
+
+
+def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None):
+    """Causal prefill in the quadratic form (no state): q, k, v [B, H, T, 64]
+    bfloat16. Returns o [B, H, T, 64] (bfloat16, or ``out_dtype``)."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(q, k, v)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hh, T, dqk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("shape mismatch between q, k and v")
+    code = _dtype_code(q)
+    ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    shp = Shape(B, Hh, T, dqk, dv, code, ocode, float(eps))
+    if out is not None:
+        if out.shape != (B, Hh, T, dv) or out.dtype != _torch_dtype(ocode) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B, H, T, d_v] tensor of the output dtype")
+        o = out
+    else:
+        o = torch.empty((B, Hh, T, dv), dtype=_torch_dtype(ocode), device=q.device)
+    check(lib.kla_prefill_quadratic(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(q.device)))
+    return o
 
 
 def _sre_struct(cand_k, cand_v, top_k, scores, sel, sel_k, sel_v, sel_stride=0):

@@ -317,6 +317,22 @@ kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const
   return hip_status(kla::prefill_valu_launch(a, ws, hs), fn);
 }
 
+kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const void* k, const void* v,
+                                   void* o, kla_stream_t stream) {
+  const char* fn = "kla_prefill_quadratic";
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  if (!q || !k || !v || !o) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v and o are required", fn);
+  kla::PrefillArgs a = make_prefill(shp, 64);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  if (!kla::prefill_quad_supported(a))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: needs d_qk = d_v = 64 and bf16 inputs", fn);
+  return hip_status(kla::prefill_quad_launch(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 // ---------------------------------------------------------------- decode / SRE
 
 kla_status_t kla_decode_workspace_size(int N, int d_qk, int d_v, const kla_sre_args_t* sre,

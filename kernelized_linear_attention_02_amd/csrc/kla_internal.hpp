@@ -43,6 +43,10 @@ bool prefill_mfma_supported(const PrefillArgs& a);
 size_t prefill_mfma_workspace(const PrefillArgs& a);
 hipError_t prefill_mfma_launch(const PrefillArgs& a, void* ws, hipStream_t st);
 
+// Quadratic (O(T^2)) form, d_qk = d_v = 64 and bf16 inputs; no workspace.
+bool prefill_quad_supported(const PrefillArgs& a);
+hipError_t prefill_quad_launch(const PrefillArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- decode / SRE
 
 struct SreArgs {

@@ -1,0 +1,233 @@
+// Causal prefill in the quadratic form on the bf16 matrix cores (d_qk = d_v
+// = 64, bf16 inputs).
+//
+// KATA page, §2.3, the quadratic of its two operating points: a
+// FlashAttention-style forward that never forms the state. With the rank-one
+// PSD lift, phi(q) . phi(k) = (q . k)^2, so for every query t
+//   num_t = sum_{i <= t} (q_t . k_i)^2 v_i,   den_t = sum_{i <= t} (q_t . k_i)^2,
+//   o_t = num_t / (den_t + eps)   (0 when that is 0),
+// the same outputs as the chunked state form. The weights are squares, never
+// negative and never exponentiated, so no running maximum is needed.
+//
+// One work-group per head and pair of 128-query blocks (x, nqb - 1 - x),
+// the heavy one first, so that every work-group does the same causal work;
+// wave w owns queries 32 w .. 32 w + 31 of a block as two 16-query tiles.
+// Keys come in blocks of 64, staged in LDS (double buffered: k rows, v
+// transposed) while the previous block computes. Per key block a wave
+//   * forms S^T = K Q^T on MFMA 16x16x32 bf16 (float32 sums): lane (l16, q4)
+//     holds the scores of query l16 against keys 4 q4 + i of each 16-key tile;
+//   * squares them in float32 (causal mask on the diagonal blocks), adds them
+//     to its float32 denominators, and rounds them to bf16 as the B operand
+//     of O^T = V^T P^T, taking P's k-slots in the order they sit in the lanes
+//     (keys 4 q4 + j of tile 2p, then of tile 2p + 1) and V^T's in the same
+//     order, so no value moves between lanes.
+// Each K and V fragment read from LDS serves both query tiles of the wave.
+#include <algorithm>
+
+#include "kla_device.hpp"
+#include "kla_internal.hpp"
+
+namespace kla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQD = 64;           // d_qk = d_v
+constexpr int kQW = 4;            // waves per work-group
+constexpr int kQT = 64 * kQW;     // threads
+constexpr int kBQ = 32 * kQW;     // queries per work-group
+constexpr int kBK = 64;           // keys per block
+constexpr int kKS = kQD + 8;      // k row stride (bf16)
+constexpr int kVS = kBK + 8;      // v^T row stride (bf16)
+
+struct QuadLds {
+  uint16_t k[2][kBK][kKS];        // key rows
+  uint16_t vt[2][kQD][kVS];       // values transposed: [dim][key]
+};
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One thread's share of a key block: key `lane`, dims 16 w .. 16 w + 15 of k and v.
+struct KVLoad {
+  uint4 k0, k1, v0, v1;
+};
+
+__device__ __forceinline__ KVLoad load_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                          size_t row0, int key, int T, int w) {
+  KVLoad r;
+  r.k0 = r.k1 = r.v0 = r.v1 = make_uint4(0, 0, 0, 0);
+  if (key < T) {
+    const size_t off = (row0 + key) * kQD + 16 * w;
+    const uint4* kp = reinterpret_cast<const uint4*>(k + off);
+    const uint4* vp = reinterpret_cast<const uint4*>(v + off);
+    r.k0 = kp[0];
+    r.k1 = kp[1];
+    r.v0 = vp[0];
+    r.v1 = vp[1];
+  }
+  return r;
+}
+
+__device__ __forceinline__ void stage_kv(QuadLds& sh, int buf, const KVLoad& r, int key, int w) {
+  *reinterpret_cast<uint4*>(&sh.k[buf][key][16 * w]) = r.k0;
+  *reinterpret_cast<uint4*>(&sh.k[buf][key][16 * w + 8]) = r.k1;
+  const uint32_t vw[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sh.vt[buf][16 * w + 2 * e][key] = (uint16_t)(vw[e] & 0xFFFF);
+    sh.vt[buf][16 * w + 2 * e + 1][key] = (uint16_t)(vw[e] >> 16);
+  }
+}
+
+template <typename Tout>
+__global__ __launch_bounds__(kQT, 2) void prefill_quad_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v,
+                                                              Tout* __restrict__ o, int T, float eps) {
+  __shared__ __align__(16) QuadLds sh;
+  const int nqb = (T + kBQ - 1) / kBQ;
+  const int n = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  const size_t row0 = (size_t)n * T;
+  // query blocks nqb - 1 - x and x: every work-group does the same causal work
+  for (int rep = 0; rep < 2; ++rep) {
+    const int qb = rep == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    if (rep == 1 && qb >= nqb - 1 - (int)blockIdx.x) break;
+    const int qw0 = qb * kBQ + 32 * w;              // this wave's first query
+    const int q_last = min(T, (qb + 1) * kBQ) - 1;  // the block's last query
+    const int nkb = q_last / kBK + 1;               // key blocks with keys <= q_last
+
+    // Q as the B operand of S^T = K Q^T: [tile][k-step], dims 32 ks + 8 q4 + j of query l16
+    bf16x8 qf[2][2];
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq) {
+      const int t = qw0 + 16 * tq + l16;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (t < T) u = *reinterpret_cast<const uint4*>(q + (row0 + t) * kQD + 32 * ks + 8 * q4);
+        qf[tq][ks] = __builtin_bit_cast(bf16x8, u);
+      }
+    }
+
+    KVLoad pf = load_kv(k, v, row0, lane, T, w);
+    stage_kv(sh, 0, pf, lane, w);
+    if (nkb > 1) pf = load_kv(k, v, row0, kBK + lane, T, w);
+    __syncthreads();
+
+    f32x4 acc[2][4];  // O^T: [query tile][dim tile], lane holds dims 16 dt + 4 q4 + i of query l16
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[tq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float den[2] = {0.f, 0.f};
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      const int k0 = kb * kBK;
+      // keys above the wave's first query need the causal mask
+      const bool diag = k0 + kBK - 1 > qw0;
+      // S^T for 4 key tiles x 2 query tiles
+      f32x4 s[4][2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        bf16x8 a[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          a[ks] = *reinterpret_cast<const bf16x8*>(&sh.k[buf][16 * kt + l16][32 * ks + 8 * q4]);
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+          f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+          c = mfma(a[0], qf[tq][0], c);
+          c = mfma(a[1], qf[tq][1], c);
+          s[kt][tq] = c;
+        }
+      }
+      // P = S^2 (masked), denominators, and the bf16 B operands of O^T = V^T P^T
+      bf16x8 pb[2][2];  // [key pair][query tile]
+#pragma unroll
+      for (int tq = 0; tq < 2; ++tq) {
+        const int t = qw0 + 16 * tq + l16;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p = s[kt][tq][i] * s[kt][tq][i];
+            if (diag && k0 + 16 * kt + 4 * q4 + i > t) p = 0.0f;
+            den[tq] += p;
+            pb[kt >> 1][tq][4 * (kt & 1) + i] = (__bf16)p;
+          }
+        }
+      }
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          // V^T rows 16 dt + l16, keys 32 p2 + 4 q4 + j and 32 p2 + 16 + 4 q4 + j
+          const uint2 lo = *reinterpret_cast<const uint2*>(&sh.vt[buf][16 * dt + l16][32 * p2 + 4 * q4]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&sh.vt[buf][16 * dt + l16][32 * p2 + 16 + 4 * q4]);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+          for (int tq = 0; tq < 2; ++tq) acc[tq][dt] = mfma(av, pb[p2][tq], acc[tq][dt]);
+        }
+      }
+      // next block: stage the registers loaded during this one, load the one after
+      if (kb + 1 < nkb) {
+        stage_kv(sh, buf ^ 1, pf, lane, w);
+        if (kb + 2 < nkb) pf = load_kv(k, v, row0, (kb + 2) * kBK + lane, T, w);
+      }
+      __syncthreads();
+    }
+
+    // denominators of query l16: sum over the four lane quarters
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq) {
+      den[tq] += __shfl_xor(den[tq], 16, 64);
+      den[tq] += __shfl_xor(den[tq], 32, 64);
+    }
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq) {
+      const int t = qw0 + 16 * tq + l16;
+      if (t >= T) continue;
+      const float d = den[tq] + eps;
+      const float inv = d != 0.0f ? 1.0f / d : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Elem<Tout>::store(o, (row0 + t) * kQD + 16 * dt + 4 * q4 + i, d != 0.0f ? acc[tq][dt][i] * inv : 0.0f);
+      }
+    }
+  }  // rep
+}
+
+}  // namespace
+
+bool prefill_quad_supported(const PrefillArgs& a) { return a.in_bf16 && a.dqk == kQD && a.dv == kQD; }
+
+hipError_t prefill_quad_launch(const PrefillArgs& a, hipStream_t st) {
+  if (!prefill_quad_supported(a) || a.T < 1 || !a.o) return hipErrorInvalidValue;
+  const int nqb = (a.T + kBQ - 1) / kBQ;
+  const dim3 grid((nqb + 1) / 2, a.N);
+  prof_begin(st);
+  if (a.out_bf16)
+    hipLaunchKernelGGL(prefill_quad_kernel<uint16_t>, grid, dim3(kQT), 0, st, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       static_cast<uint16_t*>(a.o), a.T, a.eps);
+  else
+    hipLaunchKernelGGL(prefill_quad_kernel<float>, grid, dim3(kQT), 0, st, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       static_cast<float*>(a.o), a.T, a.eps);
+  prof_end(st);
+  return hipGetLastError();
+}
+
+}  // namespace kla

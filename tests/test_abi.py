@@ -158,3 +158,15 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         K.prefill(x, x, x, chunk=32)
+
+
+def test_prefill_quadratic_rejects(lib):
+    call = lib.kla_prefill_quadratic
+    assert call(None, P, P, P, P, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(_shape()), None, P, P, P, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(_shape()), P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"required" in lib.kla_last_error()
+    # only d = 64 with bf16 inputs
+    assert call(ctypes.byref(_shape(d_qk=32, d_v=32)), P, P, P, P, None) == B.KLA_ERR_UNSUPPORTED
+    assert call(ctypes.byref(_shape(in_dtype=B.KLA_F32)), P, P, P, P, None) == B.KLA_ERR_UNSUPPORTED
+    assert call(ctypes.byref(_shape(eps=-1.0)), P, P, P, P, None) == B.KLA_ERR_INVALID_ARGUMENT

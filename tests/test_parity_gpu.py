@@ -187,6 +187,65 @@ def test_prefill_1x16x65536_full_size(K):
     _prefill_full(K, "prefill_1x16x65536", 48, [(0, 5)])
 
 
+# ------------------------------------------------------------------ quadratic form
+
+def _bruteforce_heads(q, k, v, eps=0.0):
+    B, H = q.shape[:2]
+    return np.stack([np.stack([O.prefill_bruteforce(q[b, h], k[b, h], v[b, h], eps=eps) for h in range(H)])
+                     for b in range(B)])
+
+
+@pytest.mark.parametrize("T", [1, 5, 64, 127, 128, 129, 300, 1000])
+def test_prefill_quadratic_shapes(K, T):
+    # against the float64 brute-force definition (every row), bf16 and f32 outputs
+    c = S.prefill_case("quad", 1, 3, T, 64, 64, 64, seed=120 + T)
+    Q, Kk, V = (dev(x, torch.bfloat16) for x in (c.q, c.k, c.v))
+    ref = _bruteforce_heads(c.q, c.k, c.v)
+    o = K.prefill_quadratic(Q, Kk, V)
+    assert o.dtype == torch.bfloat16
+    assert_close(host(o), ref, RTOL_BF16, f"quadratic o, T={T}")
+    o32 = K.prefill_quadratic(Q, Kk, V, out_dtype=torch.float32, eps=0.3)
+    assert o32.dtype == torch.float32
+    assert_close(host(o32), _bruteforce_heads(c.q, c.k, c.v, eps=0.3), RTOL_BF16,
+                 f"quadratic o, T={T}, eps")
+
+
+def test_prefill_quadratic_degenerate(K):
+    # zero queries: every denominator is 0 and the output is 0 (also with eps);
+    # a single token returns its own value
+    T = 200
+    z = torch.zeros((1, 2, T, 64), device="cuda", dtype=torch.bfloat16)
+    kk = torch.randn((1, 2, T, 64), device="cuda").to(torch.bfloat16)
+    vv = torch.randn((1, 2, T, 64), device="cuda").to(torch.bfloat16)
+    assert torch.all(K.prefill_quadratic(z, kk, vv) == 0)
+    assert torch.all(K.prefill_quadratic(z, kk, vv, eps=1e-3) == 0)
+    q1 = torch.randn((2, 3, 1, 64), device="cuda").to(torch.bfloat16)
+    k1 = torch.randn((2, 3, 1, 64), device="cuda").to(torch.bfloat16)
+    v1 = torch.randn((2, 3, 1, 64), device="cuda").to(torch.bfloat16)
+    assert_close(host(K.prefill_quadratic(q1, k1, v1, out_dtype=torch.float32)), host(v1), RTOL_BF16, "T=1")
+
+
+def test_prefill_quadratic_4x8x4096_full_size(K):
+    # the headline workload through the quadratic form: sampled rows against the
+    # brute force, and every row against the chunked matrix-core path
+    cfg = S.CONFIGS["prefill_4x8x4096"]
+    c = S.prefill_case("prefill_4x8x4096", cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"],
+                       cfg["chunk"], cfg["seed"])
+    Q, Kk, V = (dev(x, torch.bfloat16) for x in (c.q, c.k, c.v))
+    oq = K.prefill_quadratic(Q, Kk, V, out_dtype=torch.float32)
+    oc = K.prefill(Q, Kk, V, chunk=cfg["chunk"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    go = oq.cpu().numpy()
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    rng = np.random.default_rng(98)
+    for b in range(B):
+        for h in range(H):
+            rows = np.unique(np.concatenate([[0, 1, T - 1], rng.integers(0, T, 16)]))
+            ref = O.prefill_bruteforce_rows(c.q[b, h], c.k[b, h], c.v[b, h], rows)
+            assert_close(go[b, h, rows], ref, RTOL_BF16, f"quadratic rows of head ({b},{h})")
+    assert_close(go, oc.cpu().numpy(), 2 * RTOL_BF16, "quadratic vs chunked")
+
+
 # ------------------------------------------------------------------ decode + SRE
 
 def _initial_state(K, case):
