@@ -9,20 +9,22 @@
 // the same outputs as the chunked state form. The weights are squares, never
 // negative and never exponentiated, so no running maximum is needed.
 //
-// One work-group per head and pair of 128-query blocks (x, nqb - 1 - x),
+// One work-group per head and pair of 256-query blocks (x, nqb - 1 - x),
 // the heavy one first, so that every work-group does the same causal work;
 // wave w owns queries 32 w .. 32 w + 31 of a block as two 16-query tiles.
 // Keys come in blocks of 64, staged in LDS (double buffered: k rows, v
 // transposed) while the previous block computes. Per key block a wave
 //   * forms S^T = K Q^T on MFMA 16x16x32 bf16 (float32 sums): lane (l16, q4)
 //     holds the scores of query l16 against keys 4 q4 + i of each 16-key tile;
-//   * squares them in float32 (causal mask on the diagonal blocks), adds them
-//     to its float32 denominators, and rounds them to bf16 as the B operand
+//   * squares them in float32 (causal mask only on the blocks that reach
+//     past the wave's first query) and rounds them to bf16 as the B operand
 //     of O^T = V^T P^T, taking P's k-slots in the order they sit in the lanes
 //     (keys 4 q4 + j of tile 2p, then of tile 2p + 1) and V^T's in the same
-//     order, so no value moves between lanes.
+//     order, so no value moves between lanes; a row of ones beside V^T gives
+//     the denominators from the same bf16 weights.
 // Each K and V fragment read from LDS serves both query tiles of the wave.
 #include <algorithm>
+#include <type_traits>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
@@ -35,7 +37,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQD = 64;           // d_qk = d_v
-constexpr int kQW = 4;            // waves per work-group
+constexpr int kQW = 8;            // waves per work-group
 constexpr int kQT = 64 * kQW;     // threads
 constexpr int kBQ = 32 * kQW;     // queries per work-group
 constexpr int kBK = 64;           // keys per block
@@ -51,40 +53,46 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One thread's share of a key block: key `lane`, dims 16 w .. 16 w + 15 of k and v.
+// One thread's share of a key block: key `lane`, dims kDPT w .. kDPT w + kDPT - 1 of k and v.
+constexpr int kDPT = kQD / kQW;   // dims per staging thread
+constexpr int kU4 = kDPT / 8;     // 16-byte groups per thread and tensor
 struct KVLoad {
-  uint4 k0, k1, v0, v1;
+  uint4 k[kU4], v[kU4];
 };
 
 __device__ __forceinline__ KVLoad load_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                           size_t row0, int key, int T, int w) {
   KVLoad r;
-  r.k0 = r.k1 = r.v0 = r.v1 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kU4; ++j) r.k[j] = r.v[j] = make_uint4(0, 0, 0, 0);
   if (key < T) {
-    const size_t off = (row0 + key) * kQD + 16 * w;
+    const size_t off = (row0 + key) * kQD + kDPT * w;
     const uint4* kp = reinterpret_cast<const uint4*>(k + off);
     const uint4* vp = reinterpret_cast<const uint4*>(v + off);
-    r.k0 = kp[0];
-    r.k1 = kp[1];
-    r.v0 = vp[0];
-    r.v1 = vp[1];
+#pragma unroll
+    for (int j = 0; j < kU4; ++j) {
+      r.k[j] = kp[j];
+      r.v[j] = vp[j];
+    }
   }
   return r;
 }
 
 __device__ __forceinline__ void stage_kv(QuadLds& sh, int buf, const KVLoad& r, int key, int w) {
-  *reinterpret_cast<uint4*>(&sh.k[buf][key][16 * w]) = r.k0;
-  *reinterpret_cast<uint4*>(&sh.k[buf][key][16 * w + 8]) = r.k1;
-  const uint32_t vw[8] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w, r.v1.x, r.v1.y, r.v1.z, r.v1.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    sh.vt[buf][16 * w + 2 * e][key] = (uint16_t)(vw[e] & 0xFFFF);
-    sh.vt[buf][16 * w + 2 * e + 1][key] = (uint16_t)(vw[e] >> 16);
+  for (int j = 0; j < kU4; ++j) {
+    *reinterpret_cast<uint4*>(&sh.k[buf][key][kDPT * w + 8 * j]) = r.k[j];
+    const uint32_t vw[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sh.vt[buf][kDPT * w + 8 * j + 2 * e][key] = (uint16_t)(vw[e] & 0xFFFF);
+      sh.vt[buf][kDPT * w + 8 * j + 2 * e + 1][key] = (uint16_t)(vw[e] >> 16);
+    }
   }
 }
 
 template <typename Tout>
-__global__ __launch_bounds__(kQT, 2) void prefill_quad_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               Tout* __restrict__ o, int T, float eps) {
@@ -124,17 +132,22 @@ __global__ __launch_bounds__(kQT, 2) void prefill_quad_kernel(const uint16_t* __
     __syncthreads();
 
     f32x4 acc[2][4];  // O^T: [query tile][dim tile], lane holds dims 16 dt + 4 q4 + i of query l16
+    f32x4 dacc[2];    // row 0: the denominators (a row of ones in V^T), in lanes q4 = 0
 #pragma unroll
-    for (int tq = 0; tq < 2; ++tq)
+    for (int tq = 0; tq < 2; ++tq) {
+      dacc[tq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[tq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float den[2] = {0.f, 0.f};
+    }
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
 
-    for (int kb = 0; kb < nkb; ++kb) {
+    // one key block; MASKED: apply the causal mask (blocks with keys above a query of the wave)
+    auto key_block = [&](int kb, auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       const int buf = kb & 1;
       const int k0 = kb * kBK;
-      // keys above the wave's first query need the causal mask
-      const bool diag = k0 + kBK - 1 > qw0;
       // S^T for 4 key tiles x 2 query tiles
       f32x4 s[4][2];
 #pragma unroll
@@ -151,7 +164,7 @@ __global__ __launch_bounds__(kQT, 2) void prefill_quad_kernel(const uint16_t* __
           s[kt][tq] = c;
         }
       }
-      // P = S^2 (masked), denominators, and the bf16 B operands of O^T = V^T P^T
+      // P = S^2 as the bf16 B operands of O^T = V^T P^T
       bf16x8 pb[2][2];  // [key pair][query tile]
 #pragma unroll
       for (int tq = 0; tq < 2; ++tq) {
@@ -161,8 +174,7 @@ __global__ __launch_bounds__(kQT, 2) void prefill_quad_kernel(const uint16_t* __
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float p = s[kt][tq][i] * s[kt][tq][i];
-            if (diag && k0 + 16 * kt + 4 * q4 + i > t) p = 0.0f;
-            den[tq] += p;
+            if (MASKED && k0 + 16 * kt + 4 * q4 + i > t) p = 0.0f;
             pb[kt >> 1][tq][4 * (kt & 1) + i] = (__bf16)p;
           }
         }
@@ -178,26 +190,31 @@ __global__ __launch_bounds__(kQT, 2) void prefill_quad_kernel(const uint16_t* __
 #pragma unroll
           for (int tq = 0; tq < 2; ++tq) acc[tq][dt] = mfma(av, pb[p2][tq], acc[tq][dt]);
         }
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) dacc[tq] = mfma(ones, pb[p2][tq], dacc[tq]);
       }
+    };
+
+    // blocks below kb_mask have no key above the wave's first query
+    const int kb_mask = min(nkb, (qw0 + 1) / kBK);
+    for (int kb = 0; kb < nkb; ++kb) {
+      if (kb < kb_mask) key_block(kb, std::false_type{});
+      else key_block(kb, std::true_type{});
       // next block: stage the registers loaded during this one, load the one after
       if (kb + 1 < nkb) {
-        stage_kv(sh, buf ^ 1, pf, lane, w);
+        stage_kv(sh, (kb & 1) ^ 1, pf, lane, w);
         if (kb + 2 < nkb) pf = load_kv(k, v, row0, (kb + 2) * kBK + lane, T, w);
       }
       __syncthreads();
     }
 
-    // denominators of query l16: sum over the four lane quarters
-#pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      den[tq] += __shfl_xor(den[tq], 16, 64);
-      den[tq] += __shfl_xor(den[tq], 32, 64);
-    }
+    // denominators of query l16 sit in lane (l16, 0)
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
       const int t = qw0 + 16 * tq + l16;
+      const float dsum = __shfl(dacc[tq][0], l16, 64);
       if (t >= T) continue;
-      const float d = den[tq] + eps;
+      const float d = dsum + eps;
       const float inv = d != 0.0f ? 1.0f / d : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
