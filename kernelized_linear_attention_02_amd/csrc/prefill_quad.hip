@@ -13,7 +13,8 @@
 // the heavy one first, so that every work-group does the same causal work;
 // wave w owns queries 32 w .. 32 w + 31 of a block as two 16-query tiles.
 // Keys come in blocks of 64, staged in LDS (double buffered: k rows, v
-// transposed) while the previous block computes. Per key block a wave
+// transposed) while the previous block computes, with the next three blocks
+// in flight from memory. Per key block a wave
 //   * forms S^T = K Q^T on MFMA 16x16x32 bf16 (float32 sums): lane (l16, q4)
 //     holds the scores of query l16 against keys 4 q4 + i of each 16-key tile;
 //   * squares them in float32 (causal mask only on the blocks that reach
@@ -53,8 +54,9 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One thread's share of a key block: key `lane`, dims kDPT w .. kDPT w + kDPT - 1 of k and v.
-constexpr int kDPT = kQD / kQW;   // dims per staging thread
+// One thread's share of a key block: key tid % kBK, dims kDPT g .. kDPT g + kDPT - 1
+// of k and v with g = tid / kBK.
+constexpr int kDPT = kQD * kBK / kQT;  // dims per staging thread
 constexpr int kU4 = kDPT / 8;     // 16-byte groups per thread and tensor
 struct KVLoad {
   uint4 k[kU4], v[kU4];
@@ -126,9 +128,16 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
       }
     }
 
-    KVLoad pf = load_kv(k, v, row0, lane, T, w);
-    stage_kv(sh, 0, pf, lane, w);
-    if (nkb > 1) pf = load_kv(k, v, row0, kBK + lane, T, w);
+    const int skey = tid % kBK;  // staging role
+    const int sgrp = tid / kBK;
+    // blocks 1..3 in flight in three register slots (block b in slot b mod 3)
+    // while block 0 is staged; each key block's compute is far shorter than
+    // a memory round trip
+    KVLoad pf0 = load_kv(k, v, row0, skey, T, sgrp);
+    stage_kv(sh, 0, pf0, skey, sgrp);
+    KVLoad pf1 = load_kv(k, v, row0, kBK + skey, T, sgrp);
+    KVLoad pf2 = load_kv(k, v, row0, 2 * kBK + skey, T, sgrp);
+    pf0 = load_kv(k, v, row0, 3 * kBK + skey, T, sgrp);
     __syncthreads();
 
     f32x4 acc[2][4];  // O^T: [query tile][dim tile], lane holds dims 16 dt + 4 q4 + i of query l16
@@ -148,10 +157,10 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
       constexpr bool MASKED = decltype(masked_c)::value;
       const int buf = kb & 1;
       const int k0 = kb * kBK;
-      // S^T for 4 key tiles x 2 query tiles
-      f32x4 s[4][2];
+      // S^T for kBK / 16 key tiles x 2 query tiles
+      f32x4 s[kBK / 16][2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < kBK / 16; ++kt) {
         bf16x8 a[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -165,12 +174,12 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
         }
       }
       // P = S^2 as the bf16 B operands of O^T = V^T P^T
-      bf16x8 pb[2][2];  // [key pair][query tile]
+      bf16x8 pb[kBK / 32][2];  // [key pair][query tile]
 #pragma unroll
       for (int tq = 0; tq < 2; ++tq) {
         const int t = qw0 + 16 * tq + l16;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < kBK / 16; ++kt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float p = s[kt][tq][i] * s[kt][tq][i];
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
         }
       }
 #pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2) {
+      for (int p2 = 0; p2 < kBK / 32; ++p2) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           // V^T rows 16 dt + l16, keys 32 p2 + 4 q4 + j and 32 p2 + 16 + 4 q4 + j
@@ -197,15 +206,20 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
 
     // blocks below kb_mask have no key above the wave's first query
     const int kb_mask = min(nkb, (qw0 + 1) / kBK);
-    for (int kb = 0; kb < nkb; ++kb) {
+    // block kb, then stage block kb + 1 from its slot and load block kb + 4 into it
+    auto step = [&](int kb, KVLoad& slot) {
       if (kb < kb_mask) key_block(kb, std::false_type{});
       else key_block(kb, std::true_type{});
-      // next block: stage the registers loaded during this one, load the one after
       if (kb + 1 < nkb) {
-        stage_kv(sh, (kb & 1) ^ 1, pf, lane, w);
-        if (kb + 2 < nkb) pf = load_kv(k, v, row0, (kb + 2) * kBK + lane, T, w);
+        stage_kv(sh, (kb & 1) ^ 1, slot, skey, sgrp);
+        if (kb + 4 < nkb) slot = load_kv(k, v, row0, (kb + 4) * kBK + skey, T, sgrp);
       }
       __syncthreads();
+    };
+    for (int kb = 0; kb < nkb; kb += 3) {
+      step(kb, pf1);
+      if (kb + 1 < nkb) step(kb + 1, pf2);
+      if (kb + 2 < nkb) step(kb + 2, pf0);
     }
 
     // denominators of query l16 sit in lane (l16, 0)
