@@ -80,15 +80,25 @@ __device__ __forceinline__ KVLoad load_kv(const uint16_t* __restrict__ k, const 
   return r;
 }
 
+// Column of key `key` in a v^T row. Within each group of 32 keys, key
+// 16 t + 4 g + i goes to column 8 g + 4 t + i, so that the eight keys a lane
+// quarter g holds in its P^T fragment (4 g + i of both 16-key tiles) are
+// eight adjacent columns: one 16-byte read.
+__device__ __forceinline__ int vt_col(int key) {
+  const int r = key & 15;
+  return (key & ~31) + 8 * (r >> 2) + 4 * ((key >> 4) & 1) + (r & 3);
+}
+
 __device__ __forceinline__ void stage_kv(QuadLds& sh, int buf, const KVLoad& r, int key, int w) {
+  const int col = vt_col(key);
 #pragma unroll
   for (int j = 0; j < kU4; ++j) {
     *reinterpret_cast<uint4*>(&sh.k[buf][key][kDPT * w + 8 * j]) = r.k[j];
     const uint32_t vw[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sh.vt[buf][kDPT * w + 8 * j + 2 * e][key] = (uint16_t)(vw[e] & 0xFFFF);
-      sh.vt[buf][kDPT * w + 8 * j + 2 * e + 1][key] = (uint16_t)(vw[e] >> 16);
+      sh.vt[buf][kDPT * w + 8 * j + 2 * e][col] = (uint16_t)(vw[e] & 0xFFFF);
+      sh.vt[buf][kDPT * w + 8 * j + 2 * e + 1][col] = (uint16_t)(vw[e] >> 16);
     }
   }
 }
@@ -193,9 +203,8 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           // V^T rows 16 dt + l16, keys 32 p2 + 4 q4 + j and 32 p2 + 16 + 4 q4 + j
-          const uint2 lo = *reinterpret_cast<const uint2*>(&sh.vt[buf][16 * dt + l16][32 * p2 + 4 * q4]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(&sh.vt[buf][16 * dt + l16][32 * p2 + 16 + 4 * q4]);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          // (columns 32 p2 + 8 q4 .. + 7)
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sh.vt[buf][16 * dt + l16][32 * p2 + 8 * q4]);
 #pragma unroll
           for (int tq = 0; tq < 2; ++tq) acc[tq][dt] = mfma(av, pb[p2][tq], acc[tq][dt]);
         }
