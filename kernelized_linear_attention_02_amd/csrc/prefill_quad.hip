@@ -89,17 +89,32 @@ __device__ __forceinline__ int vt_col(int key) {
   return (key & ~31) + 8 * (r >> 2) + 4 * ((key >> 4) & 1) + (r & 3);
 }
 
+// The value of the neighbouring lane (lane ^ 1, the other key of the pair).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+}
+
+// Keys 2m and 2m + 1 sit in adjacent lanes and adjacent v^T columns; the two
+// lanes trade half of their eight values so that each writes four whole
+// 32-bit words (both keys of one dimension) instead of eight 16-bit halves.
 __device__ __forceinline__ void stage_kv(QuadLds& sh, int buf, const KVLoad& r, int key, int w) {
-  const int col = vt_col(key);
+  const int col = vt_col(key) & ~1;
+  const bool even = (key & 1) == 0;
 #pragma unroll
   for (int j = 0; j < kU4; ++j) {
     *reinterpret_cast<uint4*>(&sh.k[buf][key][kDPT * w + 8 * j]) = r.k[j];
-    const uint32_t vw[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sh.vt[buf][kDPT * w + 8 * j + 2 * e][col] = (uint16_t)(vw[e] & 0xFFFF);
-      sh.vt[buf][kDPT * w + 8 * j + 2 * e + 1][col] = (uint16_t)(vw[e] >> 16);
-    }
+    // dims (2e, 2e + 1) of this key in r.v[j] word e
+    const uint4 u = r.v[j];
+    const uint32_t x0 = pair_swap(even ? u.z : u.x);
+    const uint32_t x1 = pair_swap(even ? u.w : u.y);
+    // the even lane writes dims 0..3 of its group, the odd lane dims 4..7
+    const uint32_t a0 = even ? u.x : x0, a1 = even ? u.y : x1;  // key 2m
+    const uint32_t b0 = even ? x0 : u.z, b1 = even ? x1 : u.w;  // key 2m + 1
+    const int d = kDPT * w + 8 * j + (even ? 0 : 4);
+    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d][col]) = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d + 1][col]) = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d + 2][col]) = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d + 3][col]) = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
   }
 }
 
