@@ -130,8 +130,8 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
  *   num_t = sum_{i<=t} (q_t . k_i)^2 v_i,  den_t = sum_{i<=t} (q_t . k_i)^2,
  *   o_t = num_t / (den_t + eps)  (0 when that denominator is 0),
  * equal to kla_prefill's outputs up to rounding. Work grows as T^2 (against
- * T D for the state form), so it is the cheaper form up to T of about
- * 2 D d_v / (d_qk + d_v) tokens. No state is produced and no workspace is
+ * T D for the state form); the two are about equal at T of about
+ * 4 D d_v / (d_qk + d_v) tokens. No state is produced and no workspace is
  * needed.
  *
  *   q, k, v : [B, H, T, 64] bf16 (required);  o : [B, H, T, 64], out_dtype
