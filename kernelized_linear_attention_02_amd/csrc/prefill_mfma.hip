@@ -567,6 +567,8 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) den[i] = sh.den[mq * 16 + 4 * q4 + i] + eps;
     const uint16_t* pc = part + ((size_t)(n * gridDim.x + blockIdx.x) * S * (C / 16) + mq) * kTileAcc;
+    // the slices' loads are independent: keep several in flight
+#pragma unroll 4
     for (int s = 0; s < S; ++s) {
       const uint16_t* ps = pc + (size_t)s * (C / 16) * kTileAcc;
 #pragma unroll
