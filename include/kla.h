@@ -248,11 +248,71 @@ KLA_API kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid
                                 void* ws, size_t ws_bytes, kla_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kla_hybrid_decode_step - LoLA's three memories token by token (LoLA
+ * "Estratégia de Inferência", the token-by-token mode of items 1-4;
+ * "Metodologia" items 1-3). One call advances every head-state by one token
+ * and gives the same outputs as kla_hybrid_prefill with refresh = 1.
+ *
+ * `t` is the number of tokens each head-state has already seen (the new
+ * token's id). With W = window and lambda = cache_size:
+ *   1. when t > W, token e = t - W - 1 leaves the window. If the cache holds
+ *      fewer than lambda pairs, e is added to it. Otherwise the lambda cached
+ *      pairs and e are scored by the self-recall error against (H, s) as
+ *      they are before this call; the lambda highest (score desc, token id
+ *      asc) stay in the cache and the remaining one is folded into the
+ *      state: H += phi(k) v^T, s += phi(k);
+ *   2. the new token's query reads one jointly normalised mixture of the
+ *      window [max(0, t - W), t] (the new token included), the cache and the
+ *      folded state, with the weights of kla_hybrid_prefill;
+ *   3. the new token's (k, v) enters the window.
+ *
+ * State (device memory owned by the caller, float32, updated in place):
+ *   H, s       : [N, D, d_v], [N, D] (zero before the first token).
+ *   win_k/win_v: [N, W + 1, d_qk] / [N, W + 1, d_v]; token i is kept in row
+ *                i mod (W + 1) while it is in the window.
+ *   cache_k/cache_v/cache_ids : [N, lambda, d_qk] / [N, lambda, d_v] /
+ *                [N, lambda] int32. Rows 0 .. n-1 hold the cached pairs and
+ *                their token ids, in no particular order, with
+ *                n = min(lambda, max(0, t - W - 1)) before the call and
+ *                min(lambda, max(0, t - W)) after it; other rows are unused.
+ *                May be NULL when lambda = 0.
+ * To continue from a prefill of t tokens, the caller fills the window rows of
+ * tokens max(0, t - W - 1) .. t - 1, the cache rows and the state the prefill
+ * left.
+ *
+ *   q, k : [N, d_qk]; v : [N, d_v]; in_dtype.   o : [N, d_v], out_dtype.
+ *   rejected : [N] int32, or NULL: the token id folded into the state by this
+ *              call, -1 when there was none.
+ * Every state pointer must be 16-byte aligned.
+ * Supported: d_qk, d_v in {16, 32, 64}; refresh = 1; window >= 0;
+ * 0 <= cache_size <= 255; t >= 0; softmax_scale finite.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float* H;
+  float* s;
+  float* win_k;
+  float* win_v;
+  float* cache_k;
+  float* cache_v;
+  int32_t* cache_ids;
+} kla_hybrid_state_t;
+
+KLA_API kla_status_t kla_hybrid_decode_workspace_size(int N, int d_qk, int d_v,
+                                              const kla_hybrid_cfg_t* cfg, size_t* bytes);
+KLA_API kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps,
+                                    const kla_hybrid_cfg_t* cfg, int t,
+                                    const kla_hybrid_state_t* state, const void* q,
+                                    const void* k, const void* v, kla_dtype_t in_dtype, void* o,
+                                    kla_dtype_t out_dtype, int32_t* rejected, void* ws,
+                                    size_t ws_bytes, kla_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing without a profiler. While enabled on the calling thread,
  * every call records a pair of HIP events on its stream around its dominant
  * kernel: the state/readout kernel of kla_prefill, the state-streaming
- * kernel of kla_decode_step, the scoring kernel of kla_sre_select, and each
- * scoring kernel of kla_hybrid_prefill. kla_profile_read waits for the last
+ * kernel of kla_decode_step, the scoring kernel of kla_sre_select, each
+ * scoring kernel of kla_hybrid_prefill, and every kernel of a
+ * kla_hybrid_decode_step (one span). kla_profile_read waits for the last
  * recorded event, returns the summed elapsed milliseconds and the number of
  * recorded kernels, and clears the record. Events come from a pool owned by
  * the thread; up to 65536 pairs are kept per read (later ones are counted in

@@ -9,6 +9,7 @@ ABI of include/kla.h); this package only marshals arguments to it:
   decode_step     one recurrent token, optionally with self-recall scoring
   sre_select      self-recall-error scoring and top-k selection
   hybrid_prefill  sliding window + linear state + sparse cache
+  hybrid_decode_step  the same three memories, one token at a time
 
 ``synth`` builds the seeded synthetic workloads.
 """
@@ -17,6 +18,8 @@ from ._binding import (  # noqa: F401
     KlaError,
     LIB_PATH,
     decode_step,
+    hybrid_decode_state,
+    hybrid_decode_step,
     hybrid_prefill,
     load_library,
     phi_dim,
@@ -28,5 +31,6 @@ from ._binding import (  # noqa: F401
     sre_select,
 )
 
-__all__ = ["prefill", "prefill_quadratic", "decode_step", "sre_select", "hybrid_prefill", "phi_dim", "load_library",
+__all__ = ["prefill", "prefill_quadratic", "decode_step", "sre_select", "hybrid_prefill",
+           "hybrid_decode_state", "hybrid_decode_step", "phi_dim", "load_library",
            "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

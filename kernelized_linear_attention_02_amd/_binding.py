@@ -24,6 +24,7 @@ EXPORTS = (
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill",
+    "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step",
     "kla_profile_enable", "kla_profile_read",
 )
 
@@ -53,6 +54,13 @@ class HybridCfg(ctypes.Structure):
                 ("refresh", ctypes.c_int), ("softmax_scale", ctypes.c_float)]
 
 
+class HybridState(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
+                ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
+                ("cache_ids", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -70,6 +78,7 @@ def load_library(path: str = LIB_PATH):
     shp = ctypes.POINTER(Shape)
     srp = ctypes.POINTER(SreArgs)
     hcp = ctypes.POINTER(HybridCfg)
+    hsp = ctypes.POINTER(HybridState)
     sig = {
         "kla_abi_version": (i, []),
         "kla_phi_dim": (i, [i]),
@@ -85,6 +94,8 @@ def load_library(path: str = LIB_PATH):
         "kla_sre_select": (i, [i, i, i, f, vp, vp, srp, vp, sz, vp]),
         "kla_hybrid_workspace_size": (i, [shp, hcp, szp]),
         "kla_hybrid_prefill": (i, [shp, hcp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kla_hybrid_decode_workspace_size": (i, [i, i, i, hcp, szp]),
+        "kla_hybrid_decode_step": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp, sz, vp]),
         "kla_profile_enable": (i, [i]),
         "kla_profile_read": (i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                  ctypes.POINTER(ctypes.c_int)]),
@@ -351,6 +362,59 @@ def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, softmax_
     if not (return_state or return_cache or return_trace):
         return o
     return o, dict(H=HT, s=sT, cache=cT, trace=tr)
+
+
+def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: int, device):
+    """Zeroed token-by-token hybrid state for N head-states: a dict of device
+    tensors H [N, D, d_v], s [N, D], win_k [N, window+1, d_qk],
+    win_v [N, window+1, d_v], cache_k [N, cache_size, d_qk],
+    cache_v [N, cache_size, d_v] (float32) and cache_ids [N, cache_size] int32."""
+    torch = _torch()
+    D = phi_dim(d_qk)
+    f32 = dict(dtype=torch.float32, device=device)
+    return dict(
+        H=torch.zeros((N, D, d_v), **f32), s=torch.zeros((N, D), **f32),
+        win_k=torch.zeros((N, window + 1, d_qk), **f32), win_v=torch.zeros((N, window + 1, d_v), **f32),
+        cache_k=torch.zeros((N, cache_size, d_qk), **f32), cache_v=torch.zeros((N, cache_size, d_v), **f32),
+        cache_ids=torch.full((N, cache_size), -1, dtype=torch.int32, device=device))
+
+
+def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, softmax_scale=None,
+                       eps: float = 0.0, out_dtype=None, rejected: bool = False, out=None, ws=None):
+    """One token of the window + linear state + sparse cache decode for every
+    head-state. ``state`` is the dict of hybrid_decode_state (updated in
+    place); ``t`` is the number of tokens already seen; q, k [N, d_qk],
+    v [N, d_v]. Returns o [N, d_v], or (o, rejected [N] int32) with
+    ``rejected``. ``out`` / ``ws`` may pass a preallocated output and
+    workspace (uint8 tensor)."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(q, k, v)
+    for name in ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids"):
+        t_ = state[name]
+        if not t_.is_cuda or not t_.is_contiguous():
+            raise TypeError(f"state['{name}'] must be a contiguous device tensor (updated in place)")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    N, dqk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    cfg = HybridCfg(int(window), int(cache_size), 1, float(softmax_scale))
+    dev = q.device
+    st = HybridState(*(state[n].data_ptr() for n in ("H", "s", "win_k", "win_v", "cache_k", "cache_v",
+                                                     "cache_ids")))
+    o = out if out is not None else torch.empty((N, dv), dtype=_torch_dtype(ocode), device=dev)
+    rej = torch.empty((N,), dtype=torch.int32, device=dev) if rejected else None
+    nbytes = ctypes.c_size_t(0)
+    check(lib.kla_hybrid_decode_workspace_size(N, dqk, dv, ctypes.byref(cfg), ctypes.byref(nbytes)))
+    if ws is None or ws.numel() < nbytes.value:
+        ws = _workspace(nbytes.value, dev)
+    check(lib.kla_hybrid_decode_step(N, dqk, dv, float(eps), ctypes.byref(cfg), int(t), ctypes.byref(st),
+                                     _ptr(q), _ptr(k), _ptr(v), code, _ptr(o), ocode, _ptr(rej), _ptr(ws),
+                                     nbytes.value, _stream(dev)))
+    return (o, rej) if rejected else o
 
 
 def profile_enable(on: bool = True):

@@ -471,4 +471,102 @@ kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid_cfg_t* 
   return hip_status(kla::hybrid_launch(a, ws, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+// ---------------------------------------------------------------- hybrid decode
+
+}  // extern "C"
+
+namespace {
+
+kla_status_t check_hybrid_decode(int N, int d_qk, int d_v, const kla_hybrid_cfg_t* cfg, const char* fn) {
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (!dim_ok(d_qk) || !dim_ok(d_v))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: d_qk, d_v must be 16, 32 or 64 (got %d, %d)", fn, d_qk, d_v);
+  if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
+  if (!cfg) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cfg is NULL", fn);
+  if (cfg->window < 0 || cfg->cache_size < 0)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: need window >= 0, cache_size >= 0", fn);
+  if (cfg->refresh != 1)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: token-by-token decode needs refresh = 1 (got %d)", fn, cfg->refresh);
+  if (cfg->cache_size > 255)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: cache_size = %d exceeds 255", fn, cfg->cache_size);
+  if (cfg->window > (1 << 24))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: window = %d too large", fn, cfg->window);
+  if (!std::isfinite(cfg->softmax_scale))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite", fn);
+  return KLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+kla_status_t kla_hybrid_decode_workspace_size(int N, int d_qk, int d_v, const kla_hybrid_cfg_t* cfg,
+                                              size_t* bytes) {
+  const char* fn = "kla_hybrid_decode_workspace_size";
+  if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  kla_status_t st = check_hybrid_decode(N, d_qk, d_v, cfg, fn);
+  if (st != KLA_OK) return st;
+  kla::HybridDecodeArgs a{};
+  a.N = N;
+  a.dqk = d_qk;
+  a.dv = d_v;
+  a.window = cfg->window;
+  a.cache_size = cfg->cache_size;
+  *bytes = kla::hybrid_decode_workspace(a);
+  return ok();
+}
+
+kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const kla_hybrid_cfg_t* cfg, int t,
+                                    const kla_hybrid_state_t* state, const void* q, const void* k,
+                                    const void* v, kla_dtype_t in_dtype, void* o, kla_dtype_t out_dtype,
+                                    int32_t* rejected, void* ws, size_t ws_bytes, kla_stream_t stream) {
+  const char* fn = "kla_hybrid_decode_step";
+  kla_status_t st = check_hybrid_decode(N, d_qk, d_v, cfg, fn);
+  if (st != KLA_OK) return st;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(KLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (!std::isfinite(eps) || eps < 0.0f)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  if (t < 0) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: t must be >= 0 (got %d)", fn, t);
+  if (!state) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state is NULL", fn);
+  if (!q || !k || !v || !o) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o are required", fn);
+  const kla_hybrid_state_t& S = *state;
+  if (!S.H || !S.s || !S.win_k || !S.win_v)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, win_k, win_v are required", fn);
+  if (cfg->cache_size > 0 && (!S.cache_k || !S.cache_v || !S.cache_ids))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cache_k, cache_v, cache_ids are required when cache_size > 0",
+                fn);
+  if (!aligned16(S.H) || !aligned16(S.s) || !aligned16(S.win_k) || !aligned16(S.win_v) ||
+      !aligned16(S.cache_k) || !aligned16(S.cache_v) || !aligned16(S.cache_ids))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state pointers must be 16-byte aligned", fn);
+  kla::HybridDecodeArgs a{};
+  a.N = N;
+  a.dqk = d_qk;
+  a.dv = d_v;
+  a.in_bf16 = in_dtype == KLA_BF16;
+  a.out_bf16 = out_dtype == KLA_BF16;
+  a.eps = eps;
+  a.window = cfg->window;
+  a.cache_size = cfg->cache_size;
+  a.scale = cfg->softmax_scale;
+  a.t = t;
+  a.H = S.H;
+  a.s = S.s;
+  a.win_k = S.win_k;
+  a.win_v = S.win_v;
+  a.cache_k = S.cache_k;
+  a.cache_v = S.cache_v;
+  a.cache_ids = S.cache_ids;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.rejected = rejected;
+  st = check_ws(kla::hybrid_decode_workspace(a), ws, ws_bytes, fn);
+  if (st != KLA_OK) return st;
+  return hip_status(kla::hybrid_decode_launch(a, ws, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

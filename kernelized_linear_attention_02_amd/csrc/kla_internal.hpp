@@ -108,4 +108,29 @@ struct HybridArgs {
 size_t hybrid_workspace(const HybridArgs& a);
 hipError_t hybrid_launch(const HybridArgs& a, void* ws, hipStream_t st);
 
+// Token-by-token hybrid: one token for every head-state.
+struct HybridDecodeArgs {
+  int N, dqk, dv;
+  bool in_bf16, out_bf16;
+  float eps;
+  int window, cache_size;
+  float scale;
+  int t;  // tokens each head-state has seen before this one
+  float* H;
+  float* s;
+  float* win_k;
+  float* win_v;
+  float* cache_k;
+  float* cache_v;
+  int32_t* cache_ids;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int32_t* rejected;
+};
+
+size_t hybrid_decode_workspace(const HybridDecodeArgs& a);
+hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t st);
+
 }  // namespace kla

@@ -170,3 +170,43 @@ def test_prefill_quadratic_rejects(lib):
     assert call(ctypes.byref(_shape(d_qk=32, d_v=32)), P, P, P, P, None) == B.KLA_ERR_UNSUPPORTED
     assert call(ctypes.byref(_shape(in_dtype=B.KLA_F32)), P, P, P, P, None) == B.KLA_ERR_UNSUPPORTED
     assert call(ctypes.byref(_shape(eps=-1.0)), P, P, P, P, None) == B.KLA_ERR_INVALID_ARGUMENT
+
+
+def test_hybrid_decode_validation(lib):
+    st = B.HybridState(*([0x10000] * 7))
+    cfg = B.HybridCfg(512, 128, 1, 0.125)
+
+    def call(cfg=cfg, N=8, dqk=64, dv=64, t=600, state=st, o=P, ws=P, nbytes=1 << 40, eps=0.0,
+             in_dtype=B.KLA_BF16):
+        return lib.kla_hybrid_decode_step(N, dqk, dv, eps, ctypes.byref(cfg) if cfg else None, t,
+                                          ctypes.byref(state) if state else None, P, P, P, in_dtype, o,
+                                          B.KLA_F32, None, ws, nbytes, None)
+
+    assert call(cfg=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(N=0) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(dqk=48) == B.KLA_ERR_UNSUPPORTED
+    assert call(cfg=B.HybridCfg(512, 128, 64, 0.125)) == B.KLA_ERR_UNSUPPORTED
+    assert b"refresh = 1" in lib.kla_last_error()
+    assert call(cfg=B.HybridCfg(-1, 128, 1, 0.125)) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(cfg=B.HybridCfg(512, 256, 1, 0.125)) == B.KLA_ERR_UNSUPPORTED
+    assert call(cfg=B.HybridCfg(512, 128, 1, float("nan"))) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(t=-1) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(eps=-1.0) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(in_dtype=7) == B.KLA_ERR_UNSUPPORTED
+    assert call(state=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(o=None) == B.KLA_ERR_INVALID_ARGUMENT
+    no_cache = B.HybridState(0x10000, 0x10000, 0x10000, 0x10000, None, None, None)
+    assert call(state=no_cache) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"cache_size > 0" in lib.kla_last_error()
+    # without a cache, the cache pointers may be NULL (only the workspace check is left)
+    assert call(cfg=B.HybridCfg(512, 0, 1, 0.125), state=no_cache, ws=None) == B.KLA_ERR_WORKSPACE
+    odd = B.HybridState(0x10000, 0x10004, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+    assert call(state=odd) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.kla_last_error()
+    need = ctypes.c_size_t(0)
+    assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == B.KLA_OK
+    assert need.value >= 8 * 129 * 4 + 8 * 64 * 4 * 2
+    assert call(ws=None) == B.KLA_ERR_WORKSPACE
+    assert call(nbytes=need.value - 1) == B.KLA_ERR_WORKSPACE
+    assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, None, ctypes.byref(need)) == \
+        B.KLA_ERR_INVALID_ARGUMENT

@@ -103,7 +103,9 @@ def _hybrid_token_by_token(q, k, v, W, lam, R, scale):
     return o, trace, cache
 
 
-@pytest.mark.parametrize("seed,W,lam,R", [(3, 16, 4, 8), (4, 24, 6, 8), (5, 8, 3, 4)])
+# refresh = 1 is the token-by-token decode: one eviction and at most one fold per token
+@pytest.mark.parametrize("seed,W,lam,R", [(3, 16, 4, 8), (4, 24, 6, 8), (5, 8, 3, 4), (6, 8, 3, 1),
+                                         (7, 0, 2, 1), (8, 5, 0, 1)])
 def test_refresh_chain_against_token_by_token_enumeration(seed, W, lam, R):
     q, k, v = _data(120, 4, seed, dup=10)
     scale = 0.5
