@@ -8,8 +8,9 @@ chunk 64 — one step is one kla_prefill call (lift, intra-chunk term,
 cross-chunk state readout and update, combine). Secondary lines (in
 "secondary"): the 16-head x 65536-token long-context prefill, the main
 workload again through the quadratic (no state) form, the decode +
-self-recall selection loop (4096 head-states, 128 steps) and the hybrid
-prefill (2 x 16 x 16384). Inputs are seeded synthetic tensors resident in HBM
+self-recall selection loop (4096 head-states, 128 steps), the hybrid
+prefill (2 x 16 x 16384) and the token-by-token hybrid decode (4096
+head-states, 128 steps after a 2048-token fill). Inputs are seeded synthetic tensors resident in HBM
 before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
@@ -220,6 +221,50 @@ def bench_hybrid(torch, K, S, steps, warmup):
                 score_kernel_ms_per_call=kern_ms * per_call)
 
 
+def hybrid_decode_step_bytes(N, d, W, lam):
+    """Algorithmic HBM bytes of one steady-state token-by-token hybrid step
+    (window full, cache full, one fold): H and s read and written once; the
+    W older window rows and the lam cache rows read once (keys and values,
+    float32); the evicted row read and the replaced cache row and the new
+    window row written; q, k, v (bf16) read and o (bf16) written."""
+    D = phi_dim(d)
+    row = 2 * d * 4
+    per = 2 * D * d * 4 + 2 * D * 4 + (W + lam) * row + 3 * row + 3 * d * 2 + d * 2 + 2 * 4
+    return N * per
+
+
+def bench_hybrid_decode(torch, K, S, steps=None):
+    cfg = S.CONFIGS["hybrid_decode_4096"]
+    N, d, W, lam, T0 = cfg["N"], cfg["d"], cfg["window"], cfg["cache_size"], cfg["T0"]
+    nsteps = cfg["steps"] if steps is None else steps
+    q, k, v = S.hybrid_decode_tokens(N, T0 + nsteps, d, cfg["seed"], cfg["dup_frac"])
+    st = K.hybrid_decode_state(N, d, d, W, lam, "cuda")
+    o = torch.empty((N, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
+    t = time.time()
+    for i in range(T0):  # untimed: fills the window and the cache
+        K.hybrid_decode_step(st, i, q[i], k[i], v[i], W, lam, out=o, ws=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] hybrid decode: {T0} warm-up tokens in {time.time() - t:.1f}s")
+
+    def loop():
+        for i in range(T0, T0 + nsteps):
+            K.hybrid_decode_step(st, i, q[i], k[i], v[i], W, lam, out=o, ws=ws)
+
+    loop_ms, span_ms, _ = timed_calls(torch, K, loop, 1, 0)
+    step_ms = loop_ms / nsteps
+    step_bytes = hybrid_decode_step_bytes(N, d, W, lam)
+    achieved = step_bytes / (span_ms * 1e-3) / 1e9
+    return dict(
+        workload="hybrid_decode_4096", N=N, window=W, cache_size=lam, start_token=T0, steps=nsteps,
+        step_ms=step_ms, steps_per_s=1e3 / step_ms, kernel_ms=span_ms,
+        roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=achieved / PEAK_HBM_GBS, traffic=None,
+                      kernel="hybrid decode step (score, reject, readout; one span)",
+                      bytes_per_launch=step_bytes),
+    )
+
+
 def cpu_baseline(S, name, budget_s):
     """The oracle (float64, NumPy) on a bounded sample of the workload's heads."""
     import numpy as np
@@ -260,7 +305,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
     ap.add_argument("--only", choices=["prefill_1x16x65536", "prefill_4x8x4096_quadratic", "decode_sre_4096x128",
-                                       "hybrid_2x16x16384"],
+                                       "hybrid_2x16x16384", "hybrid_decode_4096"],
                     help="run just this secondary workload and print its line (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB bf16 copy three times (HBM counter calibration)")
@@ -291,6 +336,8 @@ def main():
             r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
         elif args.only == "decode_sre_4096x128":
             r = bench_decode(torch, K, S, args.decode_steps, max(1, args.steps // 10))
+        elif args.only == "hybrid_decode_4096":
+            r = bench_hybrid_decode(torch, K, S, args.decode_steps)
         else:
             r = bench_hybrid(torch, K, S, args.steps, args.warmup)
         print(json.dumps(r), flush=True)
@@ -311,6 +358,9 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] secondary: hybrid_2x16x16384")
         secondary.append(bench_hybrid(torch, K, S, 3, 1))
+        torch.cuda.empty_cache()
+        log("[bench] secondary: hybrid_decode_4096")
+        secondary.append(bench_hybrid_decode(torch, K, S))
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

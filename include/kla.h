@@ -257,17 +257,26 @@ KLA_API kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid
  * token's id). With W = window and lambda = cache_size:
  *   1. when t > W, token e = t - W - 1 leaves the window. If the cache holds
  *      fewer than lambda pairs, e is added to it. Otherwise the lambda cached
- *      pairs and e are scored by the self-recall error against (H, s) as
- *      they are before this call; the lambda highest (score desc, token id
- *      asc) stay in the cache and the remaining one is folded into the
- *      state: H += phi(k) v^T, s += phi(k);
+ *      pairs and e are scored by the self-recall error against the linear
+ *      state as it is before this call; the lambda highest (score desc,
+ *      token id asc) stay in the cache and the remaining one, r, is folded
+ *      into the state: H += phi(k_r) v_r^T, s += phi(k_r);
  *   2. the new token's query reads one jointly normalised mixture of the
  *      window [max(0, t - W), t] (the new token included), the cache and the
- *      folded state, with the weights of kla_hybrid_prefill;
+ *      linear state after the fold, with the weights of kla_hybrid_prefill;
  *   3. the new token's (k, v) enters the window.
+ *
+ * Deferred fold: the call does not add r's fold to H and s itself. It
+ * stores r as the state's pending pair (pend_k, pend_v), and the next call
+ * folds it in its own pass over H (so H is read and written once per
+ * token). The linear state is therefore always
+ *   H + phi(pend_k) pend_v^T,  s + phi(pend_k),
+ * and a zero pending pair means nothing is pending. kla_hybrid_decode_flush
+ * applies the pending fold to H and s and zeroes the pair.
  *
  * State (device memory owned by the caller, float32, updated in place):
  *   H, s       : [N, D, d_v], [N, D] (zero before the first token).
+ *   pend_k/pend_v : [N, d_qk] / [N, d_v] (zero before the first token).
  *   win_k/win_v: [N, W + 1, d_qk] / [N, W + 1, d_v]; token i is kept in row
  *                i mod (W + 1) while it is in the window.
  *   cache_k/cache_v/cache_ids : [N, lambda, d_qk] / [N, lambda, d_v] /
@@ -278,14 +287,17 @@ KLA_API kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid
  *                May be NULL when lambda = 0.
  * To continue from a prefill of t tokens, the caller fills the window rows of
  * tokens max(0, t - W - 1) .. t - 1, the cache rows and the state the prefill
- * left.
+ * left, with a zero pending pair.
  *
  *   q, k : [N, d_qk]; v : [N, d_v]; in_dtype.   o : [N, d_v], out_dtype.
- *   rejected : [N] int32, or NULL: the token id folded into the state by this
- *              call, -1 when there was none.
+ *   rejected : [N] int32, or NULL: the token id folded by this call (now
+ *              pending), -1 when there was none.
+ *   ws : workspace of kla_hybrid_decode_workspace_size bytes.
  * Every state pointer must be 16-byte aligned.
  * Supported: d_qk, d_v in {16, 32, 64}; refresh = 1; window >= 0;
- * 0 <= cache_size <= 255; t >= 0; softmax_scale finite.
+ * 0 <= cache_size <= 255; t >= 0; softmax_scale finite. With
+ * d_qk = d_v = 64 and 1 <= cache_size <= 128 the scoring runs on the matrix
+ * cores in the same pass over H as the fold and the readout.
  * ------------------------------------------------------------------------ */
 typedef struct {
   float* H;
@@ -295,6 +307,8 @@ typedef struct {
   float* cache_k;
   float* cache_v;
   int32_t* cache_ids;
+  float* pend_k;
+  float* pend_v;
 } kla_hybrid_state_t;
 
 KLA_API kla_status_t kla_hybrid_decode_workspace_size(int N, int d_qk, int d_v,
@@ -305,6 +319,10 @@ KLA_API kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps,
                                     const void* k, const void* v, kla_dtype_t in_dtype, void* o,
                                     kla_dtype_t out_dtype, int32_t* rejected, void* ws,
                                     size_t ws_bytes, kla_stream_t stream);
+/* Folds the pending pair into (H, s) and zeroes it (H, s, pend_k, pend_v of
+ * `state` are used). */
+KLA_API kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_state_t* state,
+                                     kla_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing without a profiler. While enabled on the calling thread,

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     KlaError,
     LIB_PATH,
     decode_step,
+    hybrid_decode_flush,
     hybrid_decode_state,
     hybrid_decode_step,
     hybrid_prefill,
@@ -32,5 +33,5 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["prefill", "prefill_quadratic", "decode_step", "sre_select", "hybrid_prefill",
-           "hybrid_decode_state", "hybrid_decode_step", "phi_dim", "load_library",
+           "hybrid_decode_state", "hybrid_decode_step", "hybrid_decode_flush", "phi_dim", "load_library",
            "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

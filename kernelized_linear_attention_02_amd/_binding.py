@@ -24,7 +24,7 @@ EXPORTS = (
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill",
-    "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step",
+    "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step", "kla_hybrid_decode_flush",
     "kla_profile_enable", "kla_profile_read",
 )
 
@@ -58,7 +58,7 @@ class HybridState(ctypes.Structure):
     _fields_ = [("H", ctypes.c_void_p), ("s", ctypes.c_void_p),
                 ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
                 ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
-                ("cache_ids", ctypes.c_void_p)]
+                ("cache_ids", ctypes.c_void_p), ("pend_k", ctypes.c_void_p), ("pend_v", ctypes.c_void_p)]
 
 
 _lib = None
@@ -96,6 +96,7 @@ def load_library(path: str = LIB_PATH):
         "kla_hybrid_prefill": (i, [shp, hcp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_hybrid_decode_workspace_size": (i, [i, i, i, hcp, szp]),
         "kla_hybrid_decode_step": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp, sz, vp]),
+        "kla_hybrid_decode_flush": (i, [i, i, i, hsp, vp]),
         "kla_profile_enable": (i, [i]),
         "kla_profile_read": (i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                  ctypes.POINTER(ctypes.c_int)]),
@@ -368,7 +369,8 @@ def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: in
     """Zeroed token-by-token hybrid state for N head-states: a dict of device
     tensors H [N, D, d_v], s [N, D], win_k [N, window+1, d_qk],
     win_v [N, window+1, d_v], cache_k [N, cache_size, d_qk],
-    cache_v [N, cache_size, d_v] (float32) and cache_ids [N, cache_size] int32."""
+    cache_v [N, cache_size, d_v], pend_k [N, d_qk], pend_v [N, d_v] (float32)
+    and cache_ids [N, cache_size] int32."""
     torch = _torch()
     D = phi_dim(d_qk)
     f32 = dict(dtype=torch.float32, device=device)
@@ -376,7 +378,19 @@ def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: in
         H=torch.zeros((N, D, d_v), **f32), s=torch.zeros((N, D), **f32),
         win_k=torch.zeros((N, window + 1, d_qk), **f32), win_v=torch.zeros((N, window + 1, d_v), **f32),
         cache_k=torch.zeros((N, cache_size, d_qk), **f32), cache_v=torch.zeros((N, cache_size, d_v), **f32),
-        cache_ids=torch.full((N, cache_size), -1, dtype=torch.int32, device=device))
+        cache_ids=torch.full((N, cache_size), -1, dtype=torch.int32, device=device),
+        pend_k=torch.zeros((N, d_qk), **f32), pend_v=torch.zeros((N, d_v), **f32))
+
+
+_STATE_FIELDS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids", "pend_k", "pend_v")
+
+
+def _hybrid_state_struct(state):
+    for name in _STATE_FIELDS:
+        t_ = state[name]
+        if not t_.is_cuda or not t_.is_contiguous():
+            raise TypeError(f"state['{name}'] must be a contiguous device tensor (updated in place)")
+    return HybridState(*(state[n].data_ptr() for n in _STATE_FIELDS))
 
 
 def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, softmax_scale=None,
@@ -390,10 +404,7 @@ def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, sof
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
-    for name in ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids"):
-        t_ = state[name]
-        if not t_.is_cuda or not t_.is_contiguous():
-            raise TypeError(f"state['{name}'] must be a contiguous device tensor (updated in place)")
+    st = _hybrid_state_struct(state)
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     N, dqk = q.shape
     dv = v.shape[-1]
@@ -403,8 +414,6 @@ def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, sof
         softmax_scale = 1.0 / math.sqrt(dqk)
     cfg = HybridCfg(int(window), int(cache_size), 1, float(softmax_scale))
     dev = q.device
-    st = HybridState(*(state[n].data_ptr() for n in ("H", "s", "win_k", "win_v", "cache_k", "cache_v",
-                                                     "cache_ids")))
     o = out if out is not None else torch.empty((N, dv), dtype=_torch_dtype(ocode), device=dev)
     rej = torch.empty((N,), dtype=torch.int32, device=dev) if rejected else None
     nbytes = ctypes.c_size_t(0)
@@ -415,6 +424,16 @@ def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, sof
                                      _ptr(q), _ptr(k), _ptr(v), code, _ptr(o), ocode, _ptr(rej), _ptr(ws),
                                      nbytes.value, _stream(dev)))
     return (o, rej) if rejected else o
+
+
+def hybrid_decode_flush(state):
+    """Fold the state's pending pair into (H, s) and zero it, so that H and s
+    alone hold the linear memory."""
+    lib = load_library()
+    st = _hybrid_state_struct(state)
+    N, dqk = state["pend_k"].shape
+    dv = state["pend_v"].shape[-1]
+    check(lib.kla_hybrid_decode_flush(N, dqk, dv, ctypes.byref(st), _stream(state["H"].device)))
 
 
 def profile_enable(on: bool = True):

@@ -28,12 +28,10 @@
 // candidate keys sit in LDS.
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
+#include "mfma_bf16.hpp"
 
 namespace kla {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDim = 64;
 constexpr int kD = kDim * (kDim + 1) / 2;  // 2080
@@ -44,16 +42,7 @@ constexpr int kThreadsF = 64 * kWaves;
 constexpr int kMaxCand = 64;
 static_assert(kD % kFT == 0, "tiles must cover the features exactly");
 
-// (a, b) of every feature in canonical order, packed a | b << 8.
-struct PairTable {
-  uint16_t ab[kD];
-  constexpr PairTable() : ab{} {
-    int f = 0;
-    for (int a = 0; a < kDim; ++a)
-      for (int b = a; b < kDim; ++b) ab[f++] = static_cast<uint16_t>(a | (b << 8));
-  }
-};
-__constant__ PairTable kPairTable = PairTable();
+__constant__ PairTable64 kPairTable = PairTable64();
 
 struct FusedLds {
   float qs[kDim];
@@ -71,35 +60,11 @@ struct FusedLds {
 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  return mfma16x16x32(a, b, c);
 }
 
-// x ~ hi + lo with hi = bf16(x), lo = bf16(x - hi): 16 significant bits.
-__device__ __forceinline__ void split2(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)x[j];
-    hi[j] = h;
-    lo[j] = (__bf16)(x[j] - (float)h);
-  }
-}
-
-// x = p0 + p1 + p2 exactly (for normal x): each remainder is exact in float32
-// and the last one has at most 8 significant bits.
-__device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& p1, bf16x8& p2) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 a = (__bf16)x[j];
-    const float r = x[j] - (float)a;
-    const __bf16 b = (__bf16)r;
-    p0[j] = a;
-    p1[j] = b;
-    p2[j] = (__bf16)(r - (float)b);
-  }
-}
-
-// The state is touched once per step: its loads and stores are marked
-// nontemporal so they do not displace the candidates in the caches.
+// State loads and stores. kStreamNT switches them to nontemporal hints,
+// which measured slower on the decode workload, so they stay plain.
 constexpr bool kStreamNT = false;
 __device__ __forceinline__ float4 ld_state(const float* p) {
   if (kStreamNT) {
@@ -115,10 +80,6 @@ __device__ __forceinline__ void st_state(float* p, const float4& v) {
   } else {
     *reinterpret_cast<float4*>(p) = v;
   }
-}
-
-__device__ __forceinline__ float comp(const float4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 // Candidate source: rows of float32 arrays [N, n_cand, 64].

@@ -7,133 +7,50 @@
 //   1. token e = t - W - 1 leaves the window when t > W. While the cache has
 //      room it joins the cache; once the cache is full, e and the lambda
 //      cached pairs are scored by the self-recall error against (H, s), the
-//      lambda highest (score desc, token id asc) stay and the lowest one is
-//      folded into the state: H += phi(k_e') v_e'^T, s += phi(k_e');
+//      lambda highest (score desc, token id asc) stay and the lowest one, r,
+//      is folded into the state: H += phi(k_r) v_r^T, s += phi(k_r);
 //   2. the query reads one jointly normalised mixture of the window
 //      [max(0, t - W), t] (softmax weights e^{a q.k}), the cache (the same
 //      weights) and the linear state (phi(q)^T H, phi(q)^T s + eps), as the
 //      blocked hybrid prefill does with refresh = 1;
 //   3. token t enters the window ring in the row the evicted token left.
+//
+// Deferred fold: the fold of step 1 is not written into (H, s) by the call
+// that decides it. The rejected pair is kept in the state as the pending
+// pair (pend_k, pend_v) and folded by the next call's pass over H, which has
+// to read and write H anyway; the call's own readout adds the fold in closed
+// form, phi(q)^T phi(k_r) = (q . k_r)^2:
+//   num += (q . k_r)^2 v_r,   den += (q . k_r)^2.
+// H is then read and written once per token. A zero pending pair folds
+// nothing (phi(0) = 0).
+//
 // Kernels (all counts are known on the host from t):
-//   score   : SRE of the lambda + 1 candidates (float32, shared SRE block);
-//   reject  : the lowest (score, -id) candidate; the evicted pair takes its
-//             cache row; the rejected pair is kept for the fold;
-//   append  : while the cache fills, the evicted pair takes the next row;
-//   readout : fold (when there is one) and linear readout in one pass over
-//             H, then the window and cache softmax, the joint division, and
-//             the window insert.
+//   state pass  d_qk = d_v = 64, cache <= 128: one work-group per
+//               head-state streams H once: pending fold, linear readout of
+//               q, and the self-recall numerators of the cache candidates on
+//               the bf16 matrix cores (float32-faithful split products) and
+//               of the evicted pair on the vector units;
+//   other shapes: a fold + readout pass over H, then the shared float32
+//               scoring block over the cache + evicted candidates;
+//   mix         per head-state: the rejected pair (lowest (score, -id)), cache
+//               update, the closed-form fold term, the window and cache
+//               softmax (online maximum), the joint division, the window
+//               insert, and the new pending pair.
 #include <algorithm>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
+#include "mfma_bf16.hpp"
 #include "sre_block.hpp"
 
 namespace kla {
 namespace {
 
 constexpr int kThreads = 256;
-
-template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads) void hdec_score_kernel(
-    const float* __restrict__ H, const float* __restrict__ s, const float* __restrict__ cache_k,
-    const float* __restrict__ cache_v, const float* __restrict__ win_k, const float* __restrict__ win_v,
-    int lambda, int wrows, int slot, float* __restrict__ scores, int sstride, float eps) {
-  constexpr int D = phi_dim(DQK);
-  __shared__ SreShared<DQK, DV> sh;
-  const int n = blockIdx.y;
-  // candidates: cache rows 0..lambda-1, then the evicted window row
-  auto load_k = [&](int c, int d) {
-    return c < lambda ? cache_k[((size_t)n * lambda + c) * DQK + d]
-                      : win_k[((size_t)n * wrows + slot) * DQK + d];
-  };
-  auto load_v = [&](int c, int d) {
-    return c < lambda ? cache_v[((size_t)n * lambda + c) * DV + d]
-                      : win_v[((size_t)n * wrows + slot) * DV + d];
-  };
-  sre_block<DQK, DV>(sh, H + (size_t)n * D * DV, s + (size_t)n * D, blockIdx.x * 64, lambda + 1, load_k,
-                     load_v, scores + (size_t)n * sstride, eps);
-}
-
-// The rejected candidate is the last in (score desc, token id asc) order.
-template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads) void hdec_reject_kernel(
-    const float* __restrict__ scores, int sstride, float* __restrict__ cache_k, float* __restrict__ cache_v,
-    int32_t* __restrict__ cache_ids, const float* __restrict__ win_k, const float* __restrict__ win_v,
-    int lambda, int wrows, int slot, int evicted_id, float* __restrict__ rej_k, float* __restrict__ rej_v,
-    int32_t* __restrict__ rejected) {
-  __shared__ uint64_t red[kThreads];
-  __shared__ float ek[DQK], ev[DV];
-  const int n = blockIdx.x;
-  const int tid = threadIdx.x;
-  uint64_t worst = ~0ull;
-  for (int c = tid; c <= lambda; c += kThreads) {
-    const int id = c < lambda ? cache_ids[(size_t)n * lambda + c] : evicted_id;
-    const float sc = lambda > 0 ? scores[(size_t)n * sstride + c] : 0.0f;  // lone candidate: not scored
-    worst = min(worst, topk_key(sc, (uint32_t)id));
-  }
-  red[tid] = worst;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = min(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const int rid = (int)topk_index(red[0]);
-  // the rejected candidate's row: the evicted pair, or the cache row holding rid
-  int r = lambda;
-  if (rid != evicted_id)
-    for (int c = 0; c < lambda; ++c)
-      if (cache_ids[(size_t)n * lambda + c] == rid) r = c;
-  const float* rk = r < lambda ? cache_k + ((size_t)n * lambda + r) * DQK : win_k + ((size_t)n * wrows + slot) * DQK;
-  const float* rv = r < lambda ? cache_v + ((size_t)n * lambda + r) * DV : win_v + ((size_t)n * wrows + slot) * DV;
-  for (int d = tid; d < DQK; d += kThreads) {
-    rej_k[(size_t)n * DQK + d] = rk[d];
-    ek[d] = win_k[((size_t)n * wrows + slot) * DQK + d];
-  }
-  for (int d = tid; d < DV; d += kThreads) {
-    rej_v[(size_t)n * DV + d] = rv[d];
-    ev[d] = win_v[((size_t)n * wrows + slot) * DV + d];
-  }
-  __syncthreads();  // every read of row r is done before it is replaced
-  if (r < lambda) {
-    for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + r) * DQK + d] = ek[d];
-    for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + r) * DV + d] = ev[d];
-    if (tid == 0) cache_ids[(size_t)n * lambda + r] = evicted_id;
-  }
-  if (rejected && tid == 0) rejected[n] = rid;
-}
-
-template <int DQK, int DV>
-__global__ void hdec_append_kernel(float* __restrict__ cache_k, float* __restrict__ cache_v,
-                                   int32_t* __restrict__ cache_ids, const float* __restrict__ win_k,
-                                   const float* __restrict__ win_v, int lambda, int wrows, int slot, int row,
-                                   int evicted_id) {
-  const int n = blockIdx.x;
-  for (int d = threadIdx.x; d < DQK; d += blockDim.x)
-    cache_k[((size_t)n * lambda + row) * DQK + d] = win_k[((size_t)n * wrows + slot) * DQK + d];
-  for (int d = threadIdx.x; d < DV; d += blockDim.x)
-    cache_v[((size_t)n * lambda + row) * DV + d] = win_v[((size_t)n * wrows + slot) * DV + d];
-  if (threadIdx.x == 0) cache_ids[(size_t)n * lambda + row] = evicted_id;
-}
-
-constexpr int kKeyTile = kThreads;  // softmax keys scored per pass (online max across passes)
 constexpr int kWaves = kThreads / 64;
+constexpr int kKeyTile = kThreads;  // softmax keys scored per pass (online max across passes)
 
-template <int DQK, int DV>
-struct ReadLds {
-  static constexpr int D = phi_dim(DQK);
-  float pq[D];             // phi(q)_f
-  float pk[D];             // phi(k_rejected)_f (fold only)
-  alignas(16) float qv[DQK];
-  alignas(16) float kn[DQK];  // the new token
-  float vn[DV];
-  float rv[DV];            // the rejected value (fold only)
-  float sc[kKeyTile];      // one tile's scores, then weights
-  float red[kWaves];
-  float num[kThreads / DV][DV];
-  uint16_t tab[D];
-};
-
-// Block-wide reductions; every thread gets the result.
+// Block-wide reductions (kThreads threads); every thread gets the result.
 __device__ __forceinline__ float block_sum(float x, float* red) {
   x = wave_sum(x);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
@@ -155,19 +72,429 @@ __device__ __forceinline__ float block_max(float x, float* red) {
   return r;
 }
 
-// One work-group per head-state.
-template <int DQK, int DV, typename Tin, typename Tout>
-__global__ __launch_bounds__(kThreads) void hdec_readout_kernel(
-    float* __restrict__ H, float* __restrict__ s, const Tin* __restrict__ q, const Tin* __restrict__ k,
-    const Tin* __restrict__ v, Tout* __restrict__ o, float* __restrict__ win_k, float* __restrict__ win_v,
-    const float* __restrict__ cache_k, const float* __restrict__ cache_v, int lambda, int n_cache,
-    int wrows, int win_first, int t, int slot, bool fold, const float* __restrict__ rej_k,
-    const float* __restrict__ rej_v, float scale, float eps) {
+// ---------------------------------------------------------------- generic state pass
+
+// One work-group per head-state: the pending pair is folded into (H, s)
+// and cleared; with READ, lin[n] = (phi(q)^T H, phi(q)^T s) of the folded
+// state (denominator without eps) at lin[n * lstride + 0 .. d_v].
+template <int DQK, int DV, typename Tin, bool READ>
+__global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
+    float* __restrict__ H, float* __restrict__ s, float* __restrict__ pend_k, float* __restrict__ pend_v,
+    const Tin* __restrict__ q, float* __restrict__ lin, int lstride) {
   constexpr int D = phi_dim(DQK);
-  constexpr int G = kThreads / DV;  // feature groups (one value column per thread)
+  constexpr int G = kThreads / DV;
+  __shared__ float pq[READ ? D : 1];
+  __shared__ float pk[D];
+  __shared__ float qv[DQK], kv[DQK], vv[DV];
+  __shared__ uint16_t tab[D];
+  __shared__ float num[G][DV];
+  __shared__ float red[kWaves];
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int c = tid % DV;
+  const int g = tid / DV;
+  for (int d = tid; d < DQK; d += kThreads) {
+    if (READ) qv[d] = Elem<Tin>::load(q, (size_t)n * DQK + d);
+    kv[d] = pend_k[(size_t)n * DQK + d];
+  }
+  for (int d = tid; d < DV; d += kThreads) vv[d] = pend_v[(size_t)n * DV + d];
+  build_phi_table(tab, 0, D, DQK);
+  __syncthreads();
+  for (int f = tid; f < D; f += kThreads) {
+    pk[f] = phi_of(kv, tab[f]);
+    if (READ) pq[f] = phi_of(qv, tab[f]);
+  }
+  __syncthreads();
+  float* Hn = H + (size_t)n * D * DV;
+  float* sn = s + (size_t)n * D;
+  const float vc = vv[c];
+  float acc = 0.0f;
+#pragma unroll 8
+  for (int f = g; f < D; f += G) {
+    const float h = Hn[(size_t)f * DV + c] + pk[f] * vc;
+    Hn[(size_t)f * DV + c] = h;
+    if (READ) acc += pq[f] * h;
+  }
+  float den = 0.0f;
+  for (int f = tid; f < D; f += kThreads) {
+    const float x = sn[f] + pk[f];
+    sn[f] = x;
+    if (READ) den += pq[f] * x;
+  }
+  if (READ) {
+    num[g][c] = acc;
+    const float dsum = block_sum(den, red);  // its barriers also publish num
+    if (g == 0) {
+      float x = 0.0f;
+#pragma unroll
+      for (int i = 0; i < G; ++i) x += num[i][c];
+      lin[(size_t)n * lstride + c] = x;
+    }
+    if (tid == 0) lin[(size_t)n * lstride + DV] = dsum;
+  }
+  // every read of the pending pair went through LDS before the first barrier
+  for (int d = tid; d < DQK; d += kThreads) pend_k[(size_t)n * DQK + d] = 0.0f;
+  for (int d = tid; d < DV; d += kThreads) pend_v[(size_t)n * DV + d] = 0.0f;
+}
+
+// Self-recall error of the lambda + 1 candidates (cache rows, then the
+// evicted window row) against the folded state, in float32.
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads) void hdec_score_kernel(
+    const float* __restrict__ H, const float* __restrict__ s, const float* __restrict__ cache_k,
+    const float* __restrict__ cache_v, const float* __restrict__ win_k, const float* __restrict__ win_v,
+    int lambda, int wrows, int slot, float* __restrict__ scores, int sstride, float eps) {
+  constexpr int D = phi_dim(DQK);
+  __shared__ SreShared<DQK, DV> sh;
+  const int n = blockIdx.y;
+  auto load_k = [&](int c, int d) {
+    return c < lambda ? cache_k[((size_t)n * lambda + c) * DQK + d]
+                      : win_k[((size_t)n * wrows + slot) * DQK + d];
+  };
+  auto load_v = [&](int c, int d) {
+    return c < lambda ? cache_v[((size_t)n * lambda + c) * DV + d]
+                      : win_v[((size_t)n * wrows + slot) * DV + d];
+  };
+  sre_block<DQK, DV>(sh, H + (size_t)n * D * DV, s + (size_t)n * D, blockIdx.x * 64, lambda + 1, load_k,
+                     load_v, scores + (size_t)n * sstride, eps);
+}
+
+// ---------------------------------------------------------------- matrix-core state pass
+
+constexpr int kFD = 64;
+constexpr int kFDim = kFD * (kFD + 1) / 2;  // 2080
+constexpr int kFT = 32;                     // features per tile (one MFMA k-step)
+constexpr int kFTiles = kFDim / kFT;        // 65
+constexpr int kFMaxCache = 128;
+static_assert(kFDim % kFT == 0, "tiles must cover the features exactly");
+
+__constant__ PairTable64 kPairs = PairTable64();
+
+struct StateLds {
+  float qs[kFD];
+  float pk[kFD];
+  float pv[kFD];
+  float ek[kFD];
+  uint16_t tab[kFDim];
+  union {
+    float ck[kFMaxCache][kFD + 1];            // cache keys, padded rows (tile loop)
+    float4 red[kFMaxCache / 16][4][64];       // numerator partials (after it)
+  };
+  float den[kWaves][kFMaxCache];
+  float onum[kWaves][kFD];
+  float enm[kWaves][kFD];
+  float oden[kWaves];
+  float eden[kWaves];
+};
+
+// One work-group per head-state; its four waves take the 65 tiles of 32
+// features in turn. A lane (l16, q4) holds rows 8*q4 .. 8*q4+7 of a tile at
+// columns 4*l16 .. 4*l16+3 (16-byte loads), adds the pending fold, writes the
+// tile back and accumulates the float32 readouts of q and of the evicted
+// key. The same registers are the B operand of the cache candidates'
+// numerators phi(K_c) H on the matrix cores: the state is split exactly into
+// three bf16 pieces, the candidate features into two, and the product is
+// p0 (h0 + h1 + h2) + p1 h0 with float32 accumulation. MT 16-row candidate
+// blocks (0: no scoring in this call).
+template <int MT, typename Tin>
+__global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
+    float* __restrict__ H, float* __restrict__ s, const float* __restrict__ pend_k,
+    const float* __restrict__ pend_v, const Tin* __restrict__ q, const float* __restrict__ cache_k,
+    const float* __restrict__ cache_v, const float* __restrict__ win_k, const float* __restrict__ win_v,
+    int wrows, int slot, int lambda, float* __restrict__ scores, int sstride, float* __restrict__ lin,
+    int lstride, float eps) {
+  constexpr int MTA = MT > 0 ? MT : 1;
+  __shared__ __align__(16) StateLds sh;
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  float* Hn = H + (size_t)n * kFDim * kFD;
+  float* sn = s + (size_t)n * kFDim;
+
+  auto load_tile = [&](int ks, float4 (&h)[8], float4 (&sv)[2]) {
+    const int fr = kFT * ks + 8 * q4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = *reinterpret_cast<const float4*>(Hn + (size_t)(fr + j) * kFD + 4 * l16);
+    sv[0] = *reinterpret_cast<const float4*>(sn + fr);
+    sv[1] = *reinterpret_cast<const float4*>(sn + fr + 4);
+  };
+  float4 h[8], sv[2];
+  load_tile(w, h, sv);
+
+  if (tid < kFD) {
+    sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kFD + tid);
+    sh.pk[tid] = pend_k[(size_t)n * kFD + tid];
+    sh.pv[tid] = pend_v[(size_t)n * kFD + tid];
+    if (MT > 0) sh.ek[tid] = win_k[((size_t)n * wrows + slot) * kFD + tid];
+  }
+  for (int i = tid; i < kFDim; i += kThreads) sh.tab[i] = kPairs.ab[i];
+  if (MT > 0) {
+    for (int i = tid; i < 16 * MT * (kFD / 4); i += kThreads) {
+      const int c = i / (kFD / 4);
+      const int d4 = i % (kFD / 4);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < lambda) x = *reinterpret_cast<const float4*>(cache_k + ((size_t)n * lambda + c) * kFD + 4 * d4);
+      sh.ck[c][4 * d4] = x.x;
+      sh.ck[c][4 * d4 + 1] = x.y;
+      sh.ck[c][4 * d4 + 2] = x.z;
+      sh.ck[c][4 * d4 + 3] = x.w;
+    }
+  }
+  __syncthreads();
+
+  const float4 v4 = *reinterpret_cast<const float4*>(&sh.pv[4 * l16]);
+  f32x4 acc[MTA][4];
+#pragma unroll
+  for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dacc[MTA];
+#pragma unroll
+  for (int mt = 0; mt < MTA; ++mt) dacc[mt] = 0.0f;
+  float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 eacc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float oden = 0.0f, eden = 0.0f;
+
+#pragma unroll 1
+  for (int ks = w; ks < kFTiles; ks += kWaves) {
+    float4 hn[8], svn[2];
+    const bool more = ks + kWaves < kFTiles;
+    if (more) load_tile(ks + kWaves, hn, svn);
+
+    const int fr = kFT * ks + 8 * q4;
+    const uint4 pw = *reinterpret_cast<const uint4*>(&sh.tab[fr]);
+    const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
+    int pa[8], pb[8];
+    float wt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = (j & 1) ? (words[j >> 1] >> 16) : (words[j >> 1] & 0xFFFFu);
+      pa[j] = u & 0xFF;
+      pb[j] = u >> 8;
+      wt[j] = pa[j] == pb[j] ? 1.0f : kSqrt2;
+    }
+    float sj[8] = {sv[0].x, sv[0].y, sv[0].z, sv[0].w, sv[1].x, sv[1].y, sv[1].z, sv[1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pk = sh.pk[pa[j]] * sh.pk[pb[j]] * wt[j];
+      const float pq = sh.qs[pa[j]] * sh.qs[pb[j]] * wt[j];
+      h[j].x += pk * v4.x;
+      h[j].y += pk * v4.y;
+      h[j].z += pk * v4.z;
+      h[j].w += pk * v4.w;
+      sj[j] += pk;
+      *reinterpret_cast<float4*>(Hn + (size_t)(fr + j) * kFD + 4 * l16) = h[j];
+      oacc.x += pq * h[j].x;
+      oacc.y += pq * h[j].y;
+      oacc.z += pq * h[j].z;
+      oacc.w += pq * h[j].w;
+      oden += pq * sj[j];
+      if (MT > 0) {
+        const float pe = sh.ek[pa[j]] * sh.ek[pb[j]] * wt[j];
+        eacc.x += pe * h[j].x;
+        eacc.y += pe * h[j].y;
+        eacc.z += pe * h[j].z;
+        eacc.w += pe * h[j].w;
+        eden += pe * sj[j];
+      }
+    }
+    // two lanes per quarter write its 8 values of s: one contiguous 32-byte run
+    if (l16 < 2)
+      *reinterpret_cast<float4*>(sn + fr + 4 * l16) =
+          l16 ? make_float4(sj[4], sj[5], sj[6], sj[7]) : make_float4(sj[0], sj[1], sj[2], sj[3]);
+
+    if (MT > 0) {
+      bf16x8 ahi[MTA], alo[MTA];
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt) {
+        const float* kc = sh.ck[16 * mt + l16];
+        float p[8];
+        float dd = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = kc[pa[j]] * kc[pb[j]] * wt[j];
+          dd += p[j] * sj[j];
+        }
+        dacc[mt] += dd;
+        split2(p, ahi[mt], alo[mt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
+        bf16x8 b0, b1, b2;
+        split3(x, b0, b1, b2);
+#pragma unroll
+        for (int mt = 0; mt < MTA; ++mt) {
+          acc[mt][nt] = mfma16x16x32(ahi[mt], b0, acc[mt][nt]);
+          acc[mt][nt] = mfma16x16x32(ahi[mt], b1, acc[mt][nt]);
+          acc[mt][nt] = mfma16x16x32(ahi[mt], b2, acc[mt][nt]);
+          acc[mt][nt] = mfma16x16x32(alo[mt], b0, acc[mt][nt]);
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = hn[j];
+      sv[0] = svn[0];
+      sv[1] = svn[1];
+    }
+  }
+
+  // ---- vector-unit readouts: sum over the lane quarters, then over waves
+  {
+    float ox[4] = {oacc.x, oacc.y, oacc.z, oacc.w};
+    float ex[4] = {eacc.x, eacc.y, eacc.z, eacc.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ox[i] += __shfl_xor(ox[i], 16, 64);
+      ox[i] += __shfl_xor(ox[i], 32, 64);
+      if (MT > 0) {
+        ex[i] += __shfl_xor(ex[i], 16, 64);
+        ex[i] += __shfl_xor(ex[i], 32, 64);
+      }
+    }
+    oden += __shfl_xor(oden, 16, 64);
+    oden += __shfl_xor(oden, 32, 64);
+    if (MT > 0) {
+      eden += __shfl_xor(eden, 16, 64);
+      eden += __shfl_xor(eden, 32, 64);
+    }
+    if (q4 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sh.onum[w][4 * l16 + i] = ox[i];
+        if (MT > 0) sh.enm[w][4 * l16 + i] = ex[i];
+      }
+    }
+    if (lane == 0) {
+      sh.oden[w] = oden;
+      if (MT > 0) sh.eden[w] = eden;
+    }
+  }
+  if (MT > 0) {
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) {
+      float d = dacc[mt];
+      d += __shfl_xor(d, 16, 64);
+      d += __shfl_xor(d, 32, 64);
+      if (q4 == 0) sh.den[w][16 * mt + l16] = d;
+    }
+  }
+  // numerators: the waves add into the LDS copy in turn and the last one keeps
+  // the sum (the first barrier also ends every read of the cache keys, whose
+  // LDS the partials reuse); with MT = 0 this only publishes the readouts
+  for (int r = 0; r < kWaves; ++r) {
+    __syncthreads();
+    if (MT > 0 && w == r) {
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          f32x4 x = acc[mt][nt];
+          if (r > 0) {
+            const float4 y = sh.red[mt][nt][lane];
+            x[0] += y.x;
+            x[1] += y.y;
+            x[2] += y.z;
+            x[3] += y.w;
+          }
+          acc[mt][nt] = x;
+          if (r + 1 < kWaves) sh.red[mt][nt][lane] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    }
+  }
+  if (w == 0) {
+    // wave 0: the linear readout of q, then the evicted pair's score
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kWaves; ++r) {
+      num += sh.onum[r][lane];
+      den += sh.oden[r];
+    }
+    lin[(size_t)n * lstride + lane] = num;
+    if (lane == 0) lin[(size_t)n * lstride + kFD] = den;
+    if (MT > 0) {
+      float en = 0.0f, ed = eps;
+#pragma unroll
+      for (int r = 0; r < kWaves; ++r) {
+        en += sh.enm[r][lane];
+        ed += sh.eden[r];
+      }
+      const float pred = ed != 0.0f ? en / ed : 0.0f;
+      const float diff = pred - win_v[((size_t)n * wrows + slot) * kFD + lane];
+      const float err = wave_sum(diff * diff);
+      if (lane == 0) scores[(size_t)n * sstride + lambda] = err;
+    }
+  }
+  if (MT > 0 && w == kWaves - 1) {
+    // lane (l16, q4) holds candidates 16*mt + 4*q4 + i at state columns 4*l16 + nt
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * mt + 4 * q4 + i;
+        const bool live = c < lambda;
+        float den = eps;
+#pragma unroll
+        for (int r = 0; r < kWaves; ++r) den += sh.den[r][c];
+        float4 vc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) vc = *reinterpret_cast<const float4*>(cache_v + ((size_t)n * lambda + c) * kFD + 4 * l16);
+        float err = 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float pred = den != 0.0f ? acc[mt][nt][i] / den : 0.0f;
+          const float diff = pred - comp(vc, nt);
+          err += diff * diff;
+        }
+        err += __shfl_xor(err, 1, 64);
+        err += __shfl_xor(err, 2, 64);
+        err += __shfl_xor(err, 4, 64);
+        err += __shfl_xor(err, 8, 64);
+        if (l16 == 0 && live) scores[(size_t)n * sstride + c] = err;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- mix
+
+template <int DQK, int DV>
+struct MixLds {
+  alignas(16) float qv[DQK];
+  alignas(16) float kn[DQK];  // the new token
+  alignas(16) float ek[DQK];  // the evicted token
+  float vn[DV];
+  float ev[DV];
+  float rk[DQK];              // the rejected pair
+  float rv[DV];
+  float sc[kKeyTile];         // one tile's scores, then weights
+  float red[kWaves];
+  float num[kThreads / DV][DV];
+  unsigned long long kred[kWaves];
+  int rrow;
+  float corr;
+};
+
+// One work-group per head-state. `refresh`: the cache is full and a token
+// is evicted (scores of the lambda + 1 candidates are in `scores`); else with
+// `evict` the evicted token is appended at cache row n_before.
+template <int DQK, int DV, typename Tin, typename Tout>
+__global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o,
+    float* __restrict__ win_k, float* __restrict__ win_v, float* __restrict__ cache_k,
+    float* __restrict__ cache_v, int32_t* __restrict__ cache_ids, float* __restrict__ pend_k,
+    float* __restrict__ pend_v, int32_t* __restrict__ rejected, const float* __restrict__ scores, int sstride,
+    const float* __restrict__ lin, int lstride, int lambda, int n_before, int n_after, bool refresh,
+    bool evict, int wrows, int win_first, int t, int slot, int evicted_id, float scale, float eps) {
+  constexpr int G = kThreads / DV;  // groups of d_v threads (one value column per thread)
   constexpr int LPK = DQK / 4;      // lanes per key in the score pass (a float4 each)
   constexpr int KPW = 64 / LPK;     // keys per wave and pass
-  __shared__ ReadLds<DQK, DV> sh;
+  __shared__ MixLds<DQK, DV> sh;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -175,69 +502,98 @@ __global__ __launch_bounds__(kThreads) void hdec_readout_kernel(
   const int c = tid % DV;
   const int g = tid / DV;
 
+  const size_t srow = (size_t)n * wrows + slot;
   for (int d = tid; d < DQK; d += kThreads) {
     sh.qv[d] = Elem<Tin>::load(q, (size_t)n * DQK + d);
     sh.kn[d] = Elem<Tin>::load(k, (size_t)n * DQK + d);
+    if (evict) sh.ek[d] = win_k[srow * DQK + d];
   }
   for (int d = tid; d < DV; d += kThreads) {
     sh.vn[d] = Elem<Tin>::load(v, (size_t)n * DV + d);
-    if (fold) sh.rv[d] = rej_v[(size_t)n * DV + d];
+    if (evict) sh.ev[d] = win_v[srow * DV + d];
   }
-  build_phi_table(sh.tab, 0, D, DQK);
-  __syncthreads();
-  const float* rk = rej_k + (size_t)n * DQK;
-  for (int f = tid; f < D; f += kThreads) {
-    sh.pq[f] = phi_of(sh.qv, sh.tab[f]);
-    if (fold) sh.pk[f] = phi_of(rk, sh.tab[f]);
-  }
-  __syncthreads();
+  if (tid == 0) sh.rrow = -1;
 
-  // ---- state: fold, then the linear readout against the folded state
-  float* Hn = H + (size_t)n * D * DV;
-  float* sn = s + (size_t)n * D;
-  const float vr = fold ? sh.rv[c] : 0.0f;
-  float lin = 0.0f;
-#pragma unroll 8
-  for (int f = g; f < D; f += G) {
-    float h = Hn[(size_t)f * DV + c];
-    if (fold) {
-      h += sh.pk[f] * vr;
-      Hn[(size_t)f * DV + c] = h;
+  // ---- the rejected pair: the last of the lambda + 1 candidates in
+  // (score desc, token id asc) order
+  int replaced = -1;  // the cache row the evicted pair now holds
+  if (refresh) {
+    unsigned long long worst = ~0ull;
+    for (int i = tid; i <= lambda; i += kThreads) {
+      const int id = i < lambda ? cache_ids[(size_t)n * lambda + i] : evicted_id;
+      const float x = lambda > 0 ? scores[(size_t)n * sstride + i] : 0.0f;  // a lone candidate is not scored
+      worst = min(worst, (unsigned long long)topk_key(x, (uint32_t)id));
     }
-    lin += sh.pq[f] * h;
-  }
-  float den = 0.0f;
-  for (int f = tid; f < D; f += kThreads) {
-    float x = sn[f];
-    if (fold) {
-      x += sh.pk[f];
-      sn[f] = x;
-    }
-    den += sh.pq[f] * x;
-  }
-  sh.num[g][c] = lin;
-  const float lin_den = block_sum(den, sh.red);  // its barrier also publishes sh.num
-  float lin_num = 0.0f;
 #pragma unroll
-  for (int i = 0; i < G; ++i) lin_num += sh.num[i][c];
+    for (int off = 32; off > 0; off >>= 1) worst = min(worst, __shfl_xor(worst, off, 64));
+    if (lane == 0) sh.kred[wave] = worst;
+    __syncthreads();
+    unsigned long long m = sh.kred[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) m = min(m, sh.kred[i]);
+    const int rid = (int)topk_index(m);
+    if (rid != evicted_id)
+      for (int i = tid; i < lambda; i += kThreads)
+        if (cache_ids[(size_t)n * lambda + i] == rid) sh.rrow = i;
+    __syncthreads();
+    const int r = sh.rrow;
+    for (int d = tid; d < DQK; d += kThreads) sh.rk[d] = r >= 0 ? cache_k[((size_t)n * lambda + r) * DQK + d] : sh.ek[d];
+    for (int d = tid; d < DV; d += kThreads) sh.rv[d] = r >= 0 ? cache_v[((size_t)n * lambda + r) * DV + d] : sh.ev[d];
+    __syncthreads();  // row r is read before it is replaced
+    // the rejected pair's fold is deferred to the next call
+    for (int d = tid; d < DQK; d += kThreads) pend_k[(size_t)n * DQK + d] = sh.rk[d];
+    for (int d = tid; d < DV; d += kThreads) pend_v[(size_t)n * DV + d] = sh.rv[d];
+    if (r >= 0) {
+      for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + r) * DQK + d] = sh.ek[d];
+      for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + r) * DV + d] = sh.ev[d];
+      if (tid == 0) cache_ids[(size_t)n * lambda + r] = evicted_id;
+    }
+    if (rejected && tid == 0) rejected[n] = rid;
+    replaced = r;
+    // (q . k_r)^2 = phi(q)^T phi(k_r), the readout's share of the deferred fold
+    if (wave == 0) {
+      float x = 0.0f;
+      for (int d = lane; d < DQK; d += 64) x += sh.qv[d] * sh.rk[d];
+      x = wave_sum(x);
+      if (lane == 0) sh.corr = x * x;
+    }
+  } else {
+    __syncthreads();
+    for (int d = tid; d < DQK; d += kThreads) pend_k[(size_t)n * DQK + d] = 0.0f;
+    for (int d = tid; d < DV; d += kThreads) pend_v[(size_t)n * DV + d] = 0.0f;
+    if (evict) {
+      for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + n_before) * DQK + d] = sh.ek[d];
+      for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + n_before) * DV + d] = sh.ev[d];
+      if (tid == 0) cache_ids[(size_t)n * lambda + n_before] = evicted_id;
+      replaced = n_before;
+    }
+    if (rejected && tid == 0) rejected[n] = -1;
+    if (tid == 0) sh.corr = 0.0f;
+  }
   __syncthreads();
+  const float corr = sh.corr;
+  const float lin_num = lin[(size_t)n * lstride + c] + (refresh ? corr * sh.rv[c] : 0.0f);
+  const float lin_den = lin[(size_t)n * lstride + DV] + corr;
 
   // ---- softmax keys: window tokens win_first .. t - 1 (ring rows), the new
-  // token t (kept in LDS), then the cache rows
+  // token t, then the cache rows 0 .. n_after - 1; the row the evicted token
+  // took is read from its LDS copy
   const int n_old = t - win_first;
-  const int n_keys = n_old + 1 + n_cache;
+  const int n_keys = n_old + 1 + n_after;
   auto key_row = [&](int j) -> const float* {
     if (j < n_old) return win_k + ((size_t)n * wrows + (win_first + j) % wrows) * DQK;
     if (j == n_old) return sh.kn;
-    return cache_k + ((size_t)n * lambda + (j - n_old - 1)) * DQK;
+    const int r = j - n_old - 1;
+    return r == replaced ? sh.ek : cache_k + ((size_t)n * lambda + r) * DQK;
   };
   auto val_row = [&](int j) -> const float* {
     if (j < n_old) return win_v + ((size_t)n * wrows + (win_first + j) % wrows) * DV;
     if (j == n_old) return sh.vn;
-    return cache_v + ((size_t)n * lambda + (j - n_old - 1)) * DV;
+    const int r = j - n_old - 1;
+    return r == replaced ? sh.ev : cache_v + ((size_t)n * lambda + r) * DV;
   };
   const float4 q4 = *reinterpret_cast<const float4*>(&sh.qv[4 * (lane % LPK)]);
-  // Running maximum, starting at 0: the linear terms are scaled by e^{-m} too.
+  // running maximum, starting at 0: the linear terms are scaled by e^{-m} too
   float m = 0.0f;
   float wsum = 0.0f, acc = 0.0f;
   for (int j0 = 0; j0 < n_keys; j0 += kKeyTile) {
@@ -256,9 +612,9 @@ __global__ __launch_bounds__(kThreads) void hdec_readout_kernel(
     __syncthreads();
     const float tmax = block_max(tid < nt ? sh.sc[tid] : -INFINITY, sh.red);
     const float m_new = fmaxf(m, tmax);
-    const float r = __expf(m - m_new);
-    wsum *= r;
-    acc *= r;
+    const float rs = __expf(m - m_new);
+    wsum *= rs;
+    acc *= rs;
     if (tid < nt) {
       const float p = __expf(sh.sc[tid] - m_new);
       sh.sc[tid] = p;
@@ -281,40 +637,49 @@ __global__ __launch_bounds__(kThreads) void hdec_readout_kernel(
     const float dd = sm_den + e * (lin_den + eps);
     Elem<Tout>::store(o, (size_t)n * DV + c, dd != 0.0f ? nn / dd : 0.0f);
   }
-  // ---- the new token enters the window, in the evicted token's row
-  for (int d = tid; d < DQK; d += kThreads) win_k[((size_t)n * wrows + slot) * DQK + d] = sh.kn[d];
-  for (int d = tid; d < DV; d += kThreads) win_v[((size_t)n * wrows + slot) * DV + d] = sh.vn[d];
+  // ---- the new token enters the window, in the evicted token's row (whose
+  // values were copied to LDS before the first barrier)
+  for (int d = tid; d < DQK; d += kThreads) win_k[srow * DQK + d] = sh.kn[d];
+  for (int d = tid; d < DV; d += kThreads) win_v[srow * DV + d] = sh.vn[d];
 }
 
-__global__ void fill_i32_kernel(int32_t* p, size_t n, int32_t x) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = x;
+// ---------------------------------------------------------------- host
+
+size_t scores_bytes(const HybridDecodeArgs& a) { return align_up((size_t)a.N * (a.cache_size + 1) * sizeof(float)); }
+int lin_stride(int dv) { return (dv + 1 + 3) / 4 * 4; }
+
+bool use_matrix_pass(const HybridDecodeArgs& a) {
+  return a.dqk == kFD && a.dv == kFD && a.cache_size >= 1 && a.cache_size <= kFMaxCache;
 }
 
-struct HdWs {
-  float* scores;  // [N, cache_size + 1]
-  float* rej_k;   // [N, d_qk]
-  float* rej_v;   // [N, d_v]
-};
-
-size_t scores_bytes(const HybridDecodeArgs& a) {
-  return align_up((size_t)a.N * (a.cache_size + 1) * sizeof(float));
-}
-
-HdWs carve_hd(const HybridDecodeArgs& a, void* ws) {
-  char* p = static_cast<char*>(ws);
-  HdWs w;
-  w.scores = reinterpret_cast<float*>(p);
-  p += scores_bytes(a);
-  w.rej_k = reinterpret_cast<float*>(p);
-  p += align_up((size_t)a.N * a.dqk * sizeof(float));
-  w.rej_v = reinterpret_cast<float*>(p);
-  return w;
+template <typename Tin>
+hipError_t launch_state(const HybridDecodeArgs& a, int mt, int wrows, int slot, float* scores, int sstride,
+                        float* lin, int lstride, hipStream_t st) {
+#define KLA_STATE(M)                                                                                            \
+  hipLaunchKernelGGL((hdec_state_kernel<M, Tin>), dim3(a.N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,       \
+                     a.pend_v, static_cast<const Tin*>(a.q), a.cache_k, a.cache_v, a.win_k, a.win_v, wrows,   \
+                     slot, a.cache_size, scores, sstride, lin, lstride, a.eps)
+  switch (mt) {
+    case 0: KLA_STATE(0); break;
+    case 1: KLA_STATE(1); break;
+    case 2: KLA_STATE(2); break;
+    case 3: KLA_STATE(3); break;
+    case 4: KLA_STATE(4); break;
+    case 5: KLA_STATE(5); break;
+    case 6: KLA_STATE(6); break;
+    case 7: KLA_STATE(7); break;
+    case 8: KLA_STATE(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef KLA_STATE
+  return hipGetLastError();
 }
 
 template <int DQK, int DV, typename Tin, typename Tout>
 hipError_t run_hd(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
-  const HdWs w = carve_hd(a, ws);
+  char* p = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(p);
+  float* lin = reinterpret_cast<float*>(p + scores_bytes(a));
   const int N = a.N, W = a.window, lam = a.cache_size, t = a.t;
   const int wrows = W + 1;
   const int slot = t % wrows;  // the evicted token's row, then the new token's
@@ -324,26 +689,25 @@ hipError_t run_hd(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
   const bool refresh = evict && n_before == lam;
   const int n_after = std::min(lam, std::max(0, t - W));
   const int sstride = lam + 1;
+  const int lstride = lin_stride(DV);
+  hipError_t e;
   prof_begin(st);
-  if (evict && !refresh) {
-    hipLaunchKernelGGL((hdec_append_kernel<DQK, DV>), dim3(N), dim3(64), 0, st, a.cache_k, a.cache_v, a.cache_ids,
-                       a.win_k, a.win_v, lam, wrows, slot, n_before, evicted_id);
-  } else if (refresh) {
-    if (lam > 0)
+  if (use_matrix_pass(a)) {
+    e = launch_state<Tin>(a, refresh ? (lam + 15) / 16 : 0, wrows, slot, scores, sstride, lin, lstride, st);
+  } else {
+    hipLaunchKernelGGL((hdec_fold_kernel<DQK, DV, Tin, true>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
+                       a.pend_v, static_cast<const Tin*>(a.q), lin, lstride);
+    if (refresh && lam > 0)
       hipLaunchKernelGGL((hdec_score_kernel<DQK, DV>), dim3((lam + 1 + 63) / 64, N), dim3(kThreads), 0, st, a.H,
-                         a.s, a.cache_k, a.cache_v, a.win_k, a.win_v, lam, wrows, slot, w.scores, sstride, a.eps);
-    hipLaunchKernelGGL((hdec_reject_kernel<DQK, DV>), dim3(N), dim3(kThreads), 0, st, w.scores, sstride,
-                       a.cache_k, a.cache_v, a.cache_ids, a.win_k, a.win_v, lam, wrows, slot, evicted_id, w.rej_k,
-                       w.rej_v, a.rejected);
+                         a.s, a.cache_k, a.cache_v, a.win_k, a.win_v, lam, wrows, slot, scores, sstride, a.eps);
+    e = hipGetLastError();
   }
-  if (!refresh && a.rejected)
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, a.rejected, (size_t)N, -1);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((hdec_readout_kernel<DQK, DV, Tin, Tout>), dim3(N), dim3(kThreads), 0, st, a.H, a.s,
+  hipLaunchKernelGGL((hdec_mix_kernel<DQK, DV, Tin, Tout>), dim3(N), dim3(kThreads), 0, st,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
-                     static_cast<Tout*>(a.o), a.win_k, a.win_v, a.cache_k, a.cache_v, lam, n_after, wrows,
-                     std::max(0, t - W), t, slot, refresh, w.rej_k, w.rej_v, a.scale, a.eps);
+                     static_cast<Tout*>(a.o), a.win_k, a.win_v, a.cache_k, a.cache_v, a.cache_ids, a.pend_k,
+                     a.pend_v, a.rejected, scores, sstride, lin, lstride, lam, n_before, n_after, refresh, evict,
+                     wrows, std::max(0, t - W), t, slot, evicted_id, a.scale, a.eps);
   prof_end(st);
   return hipGetLastError();
 }
@@ -358,13 +722,26 @@ hipError_t run_hd_dt(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
 }  // namespace
 
 size_t hybrid_decode_workspace(const HybridDecodeArgs& a) {
-  return scores_bytes(a) + align_up((size_t)a.N * a.dqk * sizeof(float)) +
-         align_up((size_t)a.N * a.dv * sizeof(float));
+  return scores_bytes(a) + align_up((size_t)a.N * lin_stride(a.dv) * sizeof(float));
 }
 
 hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
 #define KLA_CASE(A, B) \
   if (a.dqk == A && a.dv == B) return run_hd_dt<A, B>(a, ws, st);
+  KLA_CASE(16, 16) KLA_CASE(16, 32) KLA_CASE(16, 64)
+  KLA_CASE(32, 16) KLA_CASE(32, 32) KLA_CASE(32, 64)
+  KLA_CASE(64, 16) KLA_CASE(64, 32) KLA_CASE(64, 64)
+#undef KLA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st) {
+#define KLA_CASE(A, B)                                                                                          \
+  if (a.dqk == A && a.dv == B) {                                                                                \
+    hipLaunchKernelGGL((hdec_fold_kernel<A, B, float, false>), dim3(a.N), dim3(kThreads), 0, st, a.H, a.s,      \
+                       a.pend_k, a.pend_v, nullptr, nullptr, 0);                                               \
+    return hipGetLastError();                                                                                   \
+  }
   KLA_CASE(16, 16) KLA_CASE(16, 32) KLA_CASE(16, 64)
   KLA_CASE(32, 16) KLA_CASE(32, 32) KLA_CASE(32, 64)
   KLA_CASE(64, 16) KLA_CASE(64, 32) KLA_CASE(64, 64)

@@ -533,13 +533,14 @@ kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const k
   if (!state) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state is NULL", fn);
   if (!q || !k || !v || !o) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o are required", fn);
   const kla_hybrid_state_t& S = *state;
-  if (!S.H || !S.s || !S.win_k || !S.win_v)
-    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, win_k, win_v are required", fn);
+  if (!S.H || !S.s || !S.win_k || !S.win_v || !S.pend_k || !S.pend_v)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, win_k, win_v, pend_k, pend_v are required", fn);
   if (cfg->cache_size > 0 && (!S.cache_k || !S.cache_v || !S.cache_ids))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cache_k, cache_v, cache_ids are required when cache_size > 0",
                 fn);
   if (!aligned16(S.H) || !aligned16(S.s) || !aligned16(S.win_k) || !aligned16(S.win_v) ||
-      !aligned16(S.cache_k) || !aligned16(S.cache_v) || !aligned16(S.cache_ids))
+      !aligned16(S.cache_k) || !aligned16(S.cache_v) || !aligned16(S.cache_ids) || !aligned16(S.pend_k) ||
+      !aligned16(S.pend_v))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state pointers must be 16-byte aligned", fn);
   kla::HybridDecodeArgs a{};
   a.N = N;
@@ -559,6 +560,8 @@ kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const k
   a.cache_k = S.cache_k;
   a.cache_v = S.cache_v;
   a.cache_ids = S.cache_ids;
+  a.pend_k = S.pend_k;
+  a.pend_v = S.pend_v;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -567,6 +570,26 @@ kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const k
   st = check_ws(kla::hybrid_decode_workspace(a), ws, ws_bytes, fn);
   if (st != KLA_OK) return st;
   return hip_status(kla::hybrid_decode_launch(a, ws, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_state_t* state,
+                                     kla_stream_t stream) {
+  const char* fn = "kla_hybrid_decode_flush";
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (!dim_ok(d_qk) || !dim_ok(d_v))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: d_qk, d_v must be 16, 32 or 64 (got %d, %d)", fn, d_qk, d_v);
+  if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
+  if (!state || !state->H || !state->s || !state->pend_k || !state->pend_v)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, pend_k, pend_v are required", fn);
+  kla::HybridDecodeArgs a{};
+  a.N = N;
+  a.dqk = d_qk;
+  a.dv = d_v;
+  a.H = state->H;
+  a.s = state->s;
+  a.pend_k = state->pend_k;
+  a.pend_v = state->pend_v;
+  return hip_status(kla::hybrid_decode_flush_launch(a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

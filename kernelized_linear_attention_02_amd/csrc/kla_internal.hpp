@@ -123,6 +123,8 @@ struct HybridDecodeArgs {
   float* cache_k;
   float* cache_v;
   int32_t* cache_ids;
+  float* pend_k;  // the rejected pair whose fold is deferred to the next call
+  float* pend_v;
   const void* q;
   const void* k;
   const void* v;
@@ -132,5 +134,7 @@ struct HybridDecodeArgs {
 
 size_t hybrid_decode_workspace(const HybridDecodeArgs& a);
 hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t st);
+// Folds the pending pair into (H, s) and clears it (uses N, dqk, dv, H, s, pend_k, pend_v).
+hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st);
 
 }  // namespace kla

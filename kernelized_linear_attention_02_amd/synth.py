@@ -39,6 +39,7 @@ __all__ = [
     "decode_case",
     "HybridCase",
     "hybrid_case",
+    "hybrid_decode_tokens",
     "CONFIGS",
 ]
 
@@ -272,8 +273,43 @@ def hybrid_case(name: str, B: int, H: int, T: int, d: int, window: int, cache_si
                       window, cache_size, refresh, tuple(dups))
 
 
+def hybrid_decode_tokens(N: int, T: int, d: int, seed: int, dup_frac: float = 0.05,
+                         noise: float = 0.04, device="cuda"):
+    """Token stream of the token-by-token hybrid decode, drawn on ``device``
+    with torch's seeded generator (too large to draw per head on the host):
+    q, k, v as [T, N, d] bfloat16. q, k rows are L2-normalised Gaussian and
+    v ~ N(0,1), as in hybrid_case. Each key position t >= 1 independently
+    becomes, with probability ``dup_frac``, a near-duplicate
+    normalise(k0_src + noise * z) of an earlier original key k0_src,
+    src ~ U[0, t) (no cosine re-draw: with noise 0.04 in d = 64 the cosine
+    is about 0.95). The tests copy sampled heads back to the host, so the
+    oracle sees the same values."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+
+    def unit_rows():
+        x = torch.randn((T, N, d), generator=g, device=device, dtype=torch.float32)
+        return x / x.norm(dim=-1, keepdim=True)
+
+    q = unit_rows().to(torch.bfloat16)
+    k0 = unit_rows()
+    v = torch.randn((T, N, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    dup = torch.rand((T, N), generator=g, device=device) < dup_frac
+    dup[0] = False
+    tt, nn = dup.nonzero(as_tuple=True)
+    src = (torch.rand(tt.shape, generator=g, device=device) * tt.to(torch.float32)).long()
+    src = torch.minimum(src, tt - 1)
+    z = torch.randn((tt.numel(), d), generator=g, device=device, dtype=torch.float32)
+    kd = k0[src, nn] + float(noise) * z
+    k = k0.clone()
+    k[tt, nn] = kd / kd.norm(dim=-1, keepdim=True)
+    del k0
+    return q, k.to(torch.bfloat16), v
+
+
 # ----------------------------------------------------------------------------
-# The five workloads
+# The workloads
 # ----------------------------------------------------------------------------
 
 CONFIGS = {
@@ -292,4 +328,9 @@ CONFIGS = {
     # hybrid prefill: window 512, sparse cache 128, refresh every 64 tokens
     "hybrid_2x16x16384": dict(kind="hybrid", B=2, H=16, T=16384, d=64, window=512,
                               cache_size=128, refresh=64, seed=5),
+    # token-by-token hybrid decode with the hybrid prefill's memories (window
+    # 512, cache 128) over the decode workload's 256 seq x 16 heads: 2048
+    # tokens bring every head-state to a full window and cache, then 128 steps
+    "hybrid_decode_4096": dict(kind="hybrid_decode", N=4096, d=64, window=512, cache_size=128,
+                               T0=2048, steps=128, seed=6, dup_frac=0.05),
 }

@@ -71,14 +71,12 @@ def phi(x: np.ndarray) -> np.ndarray:
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
-    cols = []
-    for i in range(d):
-        for j in range(i, d):
-            if i == j:
-                cols.append(x[..., i] * x[..., i])
-            else:
-                cols.append(SQRT2 * x[..., i] * x[..., j])
-    return np.stack(cols, axis=-1)
+    pairs = phi_pairs(d)
+    i = np.array([a for a, _ in pairs], dtype=np.intp)
+    j = np.array([b for _, b in pairs], dtype=np.intp)
+    c = np.where(i == j, 1.0, SQRT2)
+    # (c_f * x_i) * x_j: 1 * x_i * x_i on the diagonal, sqrt(2) * x_i * x_j above it
+    return (c * x[..., i]) * x[..., j]
 
 
 def _safe_div(num: np.ndarray, den: np.ndarray) -> np.ndarray:

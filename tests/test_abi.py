@@ -173,7 +173,7 @@ def test_prefill_quadratic_rejects(lib):
 
 
 def test_hybrid_decode_validation(lib):
-    st = B.HybridState(*([0x10000] * 7))
+    st = B.HybridState(*([0x10000] * 9))
     cfg = B.HybridCfg(512, 128, 1, 0.125)
 
     def call(cfg=cfg, N=8, dqk=64, dv=64, t=600, state=st, o=P, ws=P, nbytes=1 << 40, eps=0.0,
@@ -195,18 +195,27 @@ def test_hybrid_decode_validation(lib):
     assert call(in_dtype=7) == B.KLA_ERR_UNSUPPORTED
     assert call(state=None) == B.KLA_ERR_INVALID_ARGUMENT
     assert call(o=None) == B.KLA_ERR_INVALID_ARGUMENT
-    no_cache = B.HybridState(0x10000, 0x10000, 0x10000, 0x10000, None, None, None)
+    no_cache = B.HybridState(0x10000, 0x10000, 0x10000, 0x10000, None, None, None, 0x10000, 0x10000)
     assert call(state=no_cache) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"cache_size > 0" in lib.kla_last_error()
     # without a cache, the cache pointers may be NULL (only the workspace check is left)
     assert call(cfg=B.HybridCfg(512, 0, 1, 0.125), state=no_cache, ws=None) == B.KLA_ERR_WORKSPACE
-    odd = B.HybridState(0x10000, 0x10004, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+    odd = B.HybridState(0x10000, 0x10004, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
     assert call(state=odd) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"aligned" in lib.kla_last_error()
+    no_pend = B.HybridState(*([0x10000] * 7), None, None)
+    assert call(state=no_pend) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"pend_k" in lib.kla_last_error()
     need = ctypes.c_size_t(0)
     assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == B.KLA_OK
-    assert need.value >= 8 * 129 * 4 + 8 * 64 * 4 * 2
+    assert need.value >= 8 * 129 * 4 + 8 * 65 * 4  # scores of lambda + 1 candidates, linear readouts
     assert call(ws=None) == B.KLA_ERR_WORKSPACE
     assert call(nbytes=need.value - 1) == B.KLA_ERR_WORKSPACE
     assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, None, ctypes.byref(need)) == \
         B.KLA_ERR_INVALID_ARGUMENT
+
+    flush = lib.kla_hybrid_decode_flush
+    assert flush(8, 64, 64, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert flush(8, 64, 64, ctypes.byref(no_pend), None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert flush(0, 64, 64, ctypes.byref(st), None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert flush(8, 48, 64, ctypes.byref(st), None) == B.KLA_ERR_UNSUPPORTED

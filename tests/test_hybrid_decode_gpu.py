@@ -58,8 +58,27 @@ def _run_gpu(K, q, k, v, W, lam, scale, eps, in_dtype, out_dtype, state=None, t0
                                     out_dtype=out_dtype, rejected=True)
         outs.append(o)
         rejs.append(r)
-    torch.cuda.synchronize()
+    _flush_checked(K, st)
     return host(torch.stack(outs, 1)), torch.stack(rejs, 1).cpu().numpy(), st
+
+
+def _flush_checked(K, st):
+    """Apply the deferred fold and check it: H gains phi(pend_k) pend_v^T and
+    s gains phi(pend_k) (phi from the oracle), the pending pair becomes zero,
+    and a second flush changes nothing."""
+    pk = host(st["pend_k"])
+    pv = host(st["pend_v"])
+    H0, s0 = host(st["H"]), host(st["s"])
+    K.hybrid_decode_flush(st)
+    torch.cuda.synchronize()
+    fk = O.phi(pk)
+    H1, s1 = host(st["H"]), host(st["s"])
+    assert_close(H1, H0 + fk[:, :, None] * pv[:, None, :], RTOL_F32, "flush H")
+    assert_close(s1, s0 + fk, RTOL_F32, "flush s")
+    assert not st["pend_k"].any() and not st["pend_v"].any()
+    K.hybrid_decode_flush(st)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(st["H"]), H1) and np.array_equal(host(st["s"]), s1)
 
 
 def _check(q, k, v, W, lam, scale, eps, go, grej, st, rtol, heads=None, t0=0, pre_trace=None):
@@ -147,3 +166,36 @@ def test_hybrid_decode_continues_a_prefill(K):
     go, grej, st = _run_gpu(K, q, k, v, W, lam, scale, 0.0, torch.float32, None, state=st, t0=T0)
     _check(q, k, v, W, lam, scale, 0.0, go, grej, st, RTOL_F32, t0=T0,
            pre_trace=extra["trace"][0].cpu().numpy())
+
+
+def test_hybrid_decode_4096_full_size(K):
+    # The benchmark's workload and launch configuration: 4096 head-states,
+    # window 512, cache 128, bf16 tokens, 2048 filling tokens then 128 steps.
+    # Every step's rejected ids are kept for all head-states; sampled
+    # head-states are re-run by the oracle in lockstep.
+    cfg = S.CONFIGS["hybrid_decode_4096"]
+    N, d, W, lam = cfg["N"], cfg["d"], cfg["window"], cfg["cache_size"]
+    T = cfg["T0"] + cfg["steps"]
+    q, k, v = S.hybrid_decode_tokens(N, T, d, cfg["seed"], cfg["dup_frac"])
+    heads = [0, 2901]
+    hidx = torch.tensor(heads, device="cuda")
+    st = K.hybrid_decode_state(N, d, d, W, lam, "cuda")
+    o = torch.empty((N, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
+    rej = torch.empty((T, N), dtype=torch.int32, device="cuda")
+    o_s = torch.empty((T, len(heads), d), device="cuda")
+    for t in range(T):
+        _, r = K.hybrid_decode_step(st, t, q[t], k[t], v[t], W, lam, out=o, ws=ws, rejected=True)
+        rej[t] = r
+        o_s[t] = o.index_select(0, hidx).float()
+    K.hybrid_decode_flush(st)
+    torch.cuda.synchronize()
+    grej = rej.cpu().numpy()
+    # every head-state folds exactly one pair per step once its cache is full
+    assert np.all(grej[: W + 1 + lam] == -1)
+    assert np.all(grej[W + 1 + lam:] >= 0)
+    scale = 1.0 / math.sqrt(d)
+    sub = {n: host(x[:, heads].transpose(0, 1)) for n, x in (("q", q), ("k", k), ("v", v))}
+    sub_state = {name: st[name].index_select(0, hidx) for name in ("H", "s", "cache_ids")}
+    _check(sub["q"], sub["k"], sub["v"], W, lam, scale, 0.0, host(o_s.transpose(0, 1)),
+           grej[:, heads].T, sub_state, RTOL_BF16)
