@@ -163,21 +163,37 @@ __global__ __launch_bounds__(kThreads) void hdec_score_kernel(
 
 constexpr int kFD = 64;
 constexpr int kFDim = kFD * (kFD + 1) / 2;  // 2080
-constexpr int kFT = 32;                     // features per tile (one MFMA k-step)
-constexpr int kFTiles = kFDim / kFT;        // 65
 constexpr int kFMaxCache = 128;
-static_assert(kFDim % kFT == 0, "tiles must cover the features exactly");
+constexpr int kKS = kFD + 4;                // padded LDS key rows (16-byte aligned)
+// Feature order of the pass: 8 x 8 blocks (A, B), A <= B, of the pairs
+// (a, b), a <= b; a block is two MFMA k-steps ("tiles") of 32 features. In
+// tile t of block (A, B) the lane quarter q4 takes a = 8A + 4t + q4 and
+// b = 8B .. 8B + 7: eight consecutive state rows. Diagonal blocks hold 36
+// pairs in 64 slots; the slots with b < a are zero rows.
+constexpr int kBlocks = 8 * 9 / 2;          // 36
+constexpr int kFTiles = 2 * kBlocks;        // 72
 
-__constant__ PairTable64 kPairs = PairTable64();
+struct BlockTable {
+  uint8_t A[kBlocks], B[kBlocks];
+  constexpr BlockTable() : A{}, B{} {
+    int i = 0;
+    for (int a = 0; a < 8; ++a)
+      for (int b = a; b < 8; ++b) {
+        A[i] = static_cast<uint8_t>(a);
+        B[i] = static_cast<uint8_t>(b);
+        ++i;
+      }
+  }
+};
+__constant__ BlockTable kBlockTab = BlockTable();
 
 struct StateLds {
-  float qs[kFD];
-  float pk[kFD];
-  float pv[kFD];
-  float ek[kFD];
-  uint16_t tab[kFDim];
+  alignas(16) float qs[kFD];
+  alignas(16) float pk[kFD];
+  alignas(16) float pv[kFD];
+  alignas(16) float ek[kFD];
   union {
-    float ck[kFMaxCache][kFD + 1];            // cache keys, padded rows (tile loop)
+    float ck[kFMaxCache][kKS];                // cache keys (tile loop)
     float4 red[kFMaxCache / 16][4][64];       // numerator partials (after it)
   };
   float den[kWaves][kFMaxCache];
@@ -187,13 +203,43 @@ struct StateLds {
   float eden[kWaves];
 };
 
-// One work-group per head-state; its four waves take the 65 tiles of 32
-// features in turn. A lane (l16, q4) holds rows 8*q4 .. 8*q4+7 of a tile at
-// columns 4*l16 .. 4*l16+3 (16-byte loads), adds the pending fold, writes the
-// tile back and accumulates the float32 readouts of q and of the evicted
-// key. The same registers are the B operand of the cache candidates'
-// numerators phi(K_c) H on the matrix cores: the state is split exactly into
-// three bf16 pieces, the candidate features into two, and the product is
+// Where a lane's eight features of tile T lie: first state row f0 (row of
+// (a, 8B)), the first valid slot jmin, the diagonal slot jd (b == a; -1 off
+// the diagonal), and the key coordinates a and 8B.
+struct TileCoords {
+  int f0, jmin, jd, a, b0;
+};
+__device__ __forceinline__ TileCoords tile_coords(int T, int q4) {
+  const int blk = T >> 1;
+  const int A = kBlockTab.A[blk];
+  const int B = kBlockTab.B[blk];
+  TileCoords c;
+  c.a = 8 * A + 4 * (T & 1) + q4;
+  c.b0 = 8 * B;
+  c.f0 = c.a * kFD - c.a * (c.a - 1) / 2 + (c.b0 - c.a);
+  c.jmin = A == B ? c.a - c.b0 : 0;
+  c.jd = A == B ? c.a - c.b0 : -1;
+  return c;
+}
+
+// phi over a lane's eight features of one vector x in LDS: out_j = c_j x_a x_{b0+j}.
+__device__ __forceinline__ void phi8(const float* x, const TileCoords& tc, float (&out)[8]) {
+  const float xa = x[tc.a];
+  const float4 lo = *reinterpret_cast<const float4*>(x + tc.b0);
+  const float4 hi = *reinterpret_cast<const float4*>(x + tc.b0 + 4);
+  const float xs = xa * kSqrt2;
+  const float xb[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = (j == tc.jd ? xa : xs) * xb[j];
+}
+
+// One work-group per head-state; its four waves take the 72 tiles in turn.
+// A lane (l16, q4) holds its eight state rows of a tile at columns
+// 4*l16 .. 4*l16+3 (16-byte loads), adds the pending fold, writes them back
+// and accumulates the float32 readouts of q and of the evicted key. The same
+// registers are the B operand of the cache candidates' numerators
+// phi(K_c) H on the matrix cores: the state is split exactly into three bf16
+// pieces, the candidate features into two, and the product is
 // p0 (h0 + h1 + h2) + p1 h0 with float32 accumulation. MT 16-row candidate
 // blocks (0: no scoring in this call).
 template <int MT, typename Tin>
@@ -214,15 +260,22 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
   float* Hn = H + (size_t)n * kFDim * kFD;
   float* sn = s + (size_t)n * kFDim;
 
-  auto load_tile = [&](int ks, float4 (&h)[8], float4 (&sv)[2]) {
-    const int fr = kFT * ks + 8 * q4;
+  // rows of slots j < jmin are not features: zero, never loaded or stored
+  auto load_tile = [&](const TileCoords& tc, float4 (&h)[8], float (&sj)[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = *reinterpret_cast<const float4*>(Hn + (size_t)(fr + j) * kFD + 4 * l16);
-    sv[0] = *reinterpret_cast<const float4*>(sn + fr);
-    sv[1] = *reinterpret_cast<const float4*>(sn + fr + 4);
+    for (int j = 0; j < 8; ++j) {
+      h[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      sj[j] = 0.0f;
+      if (j >= tc.jmin) {
+        h[j] = *reinterpret_cast<const float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16);
+        sj[j] = sn[tc.f0 + j];
+      }
+    }
   };
-  float4 h[8], sv[2];
-  load_tile(w, h, sv);
+  TileCoords tc = tile_coords(w, q4);
+  float4 h[8];
+  float sj[8];
+  load_tile(tc, h, sj);
 
   if (tid < kFD) {
     sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kFD + tid);
@@ -230,17 +283,13 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
     sh.pv[tid] = pend_v[(size_t)n * kFD + tid];
     if (MT > 0) sh.ek[tid] = win_k[((size_t)n * wrows + slot) * kFD + tid];
   }
-  for (int i = tid; i < kFDim; i += kThreads) sh.tab[i] = kPairs.ab[i];
   if (MT > 0) {
     for (int i = tid; i < 16 * MT * (kFD / 4); i += kThreads) {
       const int c = i / (kFD / 4);
       const int d4 = i % (kFD / 4);
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (c < lambda) x = *reinterpret_cast<const float4*>(cache_k + ((size_t)n * lambda + c) * kFD + 4 * d4);
-      sh.ck[c][4 * d4] = x.x;
-      sh.ck[c][4 * d4 + 1] = x.y;
-      sh.ck[c][4 * d4 + 2] = x.z;
-      sh.ck[c][4 * d4 + 3] = x.w;
+      *reinterpret_cast<float4*>(&sh.ck[c][4 * d4]) = x;
     }
   }
   __syncthreads();
@@ -259,65 +308,60 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
   float oden = 0.0f, eden = 0.0f;
 
 #pragma unroll 1
-  for (int ks = w; ks < kFTiles; ks += kWaves) {
-    float4 hn[8], svn[2];
-    const bool more = ks + kWaves < kFTiles;
-    if (more) load_tile(ks + kWaves, hn, svn);
-
-    const int fr = kFT * ks + 8 * q4;
-    const uint4 pw = *reinterpret_cast<const uint4*>(&sh.tab[fr]);
-    const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
-    int pa[8], pb[8];
-    float wt[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t u = (j & 1) ? (words[j >> 1] >> 16) : (words[j >> 1] & 0xFFFFu);
-      pa[j] = u & 0xFF;
-      pb[j] = u >> 8;
-      wt[j] = pa[j] == pb[j] ? 1.0f : kSqrt2;
+  for (int T = w; T < kFTiles; T += kWaves) {
+    float4 hn[8];
+    float sjn[8];
+    const bool more = T + kWaves < kFTiles;
+    TileCoords tcn = tc;
+    if (more) {
+      tcn = tile_coords(T + kWaves, q4);
+      load_tile(tcn, hn, sjn);
     }
-    float sj[8] = {sv[0].x, sv[0].y, sv[0].z, sv[0].w, sv[1].x, sv[1].y, sv[1].z, sv[1].w};
+
+    float pk[8], pq[8], pe[8];
+    phi8(sh.pk, tc, pk);
+    phi8(sh.qs, tc, pq);
+    if (MT > 0) phi8(sh.ek, tc, pe);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pk = sh.pk[pa[j]] * sh.pk[pb[j]] * wt[j];
-      const float pq = sh.qs[pa[j]] * sh.qs[pb[j]] * wt[j];
-      h[j].x += pk * v4.x;
-      h[j].y += pk * v4.y;
-      h[j].z += pk * v4.z;
-      h[j].w += pk * v4.w;
-      sj[j] += pk;
-      *reinterpret_cast<float4*>(Hn + (size_t)(fr + j) * kFD + 4 * l16) = h[j];
-      oacc.x += pq * h[j].x;
-      oacc.y += pq * h[j].y;
-      oacc.z += pq * h[j].z;
-      oacc.w += pq * h[j].w;
-      oden += pq * sj[j];
+      if (j >= tc.jmin) {
+        h[j].x += pk[j] * v4.x;
+        h[j].y += pk[j] * v4.y;
+        h[j].z += pk[j] * v4.z;
+        h[j].w += pk[j] * v4.w;
+        sj[j] += pk[j];
+        *reinterpret_cast<float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16) = h[j];
+      }
+      oacc.x += pq[j] * h[j].x;
+      oacc.y += pq[j] * h[j].y;
+      oacc.z += pq[j] * h[j].z;
+      oacc.w += pq[j] * h[j].w;
+      oden += pq[j] * sj[j];
       if (MT > 0) {
-        const float pe = sh.ek[pa[j]] * sh.ek[pb[j]] * wt[j];
-        eacc.x += pe * h[j].x;
-        eacc.y += pe * h[j].y;
-        eacc.z += pe * h[j].z;
-        eacc.w += pe * h[j].w;
-        eden += pe * sj[j];
+        eacc.x += pe[j] * h[j].x;
+        eacc.y += pe[j] * h[j].y;
+        eacc.z += pe[j] * h[j].z;
+        eacc.w += pe[j] * h[j].w;
+        eden += pe[j] * sj[j];
       }
     }
-    // two lanes per quarter write its 8 values of s: one contiguous 32-byte run
-    if (l16 < 2)
-      *reinterpret_cast<float4*>(sn + fr + 4 * l16) =
-          l16 ? make_float4(sj[4], sj[5], sj[6], sj[7]) : make_float4(sj[0], sj[1], sj[2], sj[3]);
+    // lane l16 = j of each quarter writes s of slot j: a contiguous 32-byte run
+    {
+      float x = sj[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) x = l16 == j ? sj[j] : x;
+      if (l16 < 8 && l16 >= tc.jmin) sn[tc.f0 + l16] = x;
+    }
 
     if (MT > 0) {
       bf16x8 ahi[MTA], alo[MTA];
 #pragma unroll
       for (int mt = 0; mt < MTA; ++mt) {
-        const float* kc = sh.ck[16 * mt + l16];
         float p[8];
+        phi8(sh.ck[16 * mt + l16], tc, p);
         float dd = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = kc[pa[j]] * kc[pb[j]] * wt[j];
-          dd += p[j] * sj[j];
-        }
+        for (int j = 0; j < 8; ++j) dd += p[j] * sj[j];
         dacc[mt] += dd;
         split2(p, ahi[mt], alo[mt]);
       }
@@ -339,9 +383,11 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
     }
     if (more) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = hn[j];
-      sv[0] = svn[0];
-      sv[1] = svn[1];
+      for (int j = 0; j < 8; ++j) {
+        h[j] = hn[j];
+        sj[j] = sjn[j];
+      }
+      tc = tcn;
     }
   }
 
@@ -456,6 +502,320 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
         err += __shfl_xor(err, 4, 64);
         err += __shfl_xor(err, 8, 64);
         if (l16 == 0 && live) scores[(size_t)n * sstride + c] = err;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- matrix-core state pass, 8 waves
+
+// LDS-only work-group barrier: waits for this wave's LDS traffic, not for its
+// global loads in flight.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kThreads2 = 512;
+constexpr int kPairs2 = 4;  // producer/consumer wave pairs, one per SIMD
+
+struct State2Lds {
+  alignas(16) float qs[kFD];
+  alignas(16) float pk[kFD];
+  alignas(16) float pv[kFD];
+  alignas(16) float ek[kFD];
+  union {
+    struct {
+      float ck[kFMaxCache][kKS];        // cache keys
+      uint4 bp[kPairs2][2][12][64];     // B pieces [pair][buffer][3 * nt + piece][lane]
+      float sj[kPairs2][2][4][8];       // s of each lane quarter's 8 slots
+    } lp;
+    float4 red[kFMaxCache / 16][4][64];  // numerator partials (after the tile loop)
+  };
+  float den[kPairs2][kFMaxCache];
+  float onum[kPairs2][kFD];
+  float enm[kPairs2][kFD];
+  float oden[kPairs2];
+  float eden[kPairs2];
+};
+
+// Same pass as hdec_state_kernel with two waves per SIMD. Pair p = (wave p,
+// wave p + 4) walks tiles p, p + 4, ...: the producer (wave p) loads its
+// tile, folds, writes it back, accumulates the readouts, splits it into the
+// three bf16 B pieces and publishes them in LDS; after the barrier both
+// waves take them from there. The producer runs candidate
+// blocks 0..3 and the consumer blocks 4..MT-1 against the same pieces, so
+// each wave keeps at most four blocks of accumulators.
+template <int MT, typename Tin>
+__global__ __launch_bounds__(kThreads2, 1) void hdec_state2_kernel(
+    float* __restrict__ H, float* __restrict__ s, const float* __restrict__ pend_k,
+    const float* __restrict__ pend_v, const Tin* __restrict__ q, const float* __restrict__ cache_k,
+    const float* __restrict__ cache_v, const float* __restrict__ win_k, const float* __restrict__ win_v,
+    int wrows, int slot, int lambda, float* __restrict__ scores, int sstride, float* __restrict__ lin,
+    int lstride, float eps) {
+  static_assert(MT > 4 && MT <= kFMaxCache / 16, "the consumer needs one to four blocks");
+  __shared__ __align__(16) State2Lds sh;
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wv & 3;
+  const bool prod = wv < kPairs2;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  float* Hn = H + (size_t)n * kFDim * kFD;
+  float* sn = s + (size_t)n * kFDim;
+  const int mb = prod ? 0 : 4;       // first candidate block of this wave
+  const int mc = prod ? 4 : MT - 4;  // its number of blocks
+
+  auto load_tile = [&](const TileCoords& tc, float4 (&h)[8], float (&sj)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      sj[j] = 0.0f;
+      if (j >= tc.jmin) {
+        h[j] = *reinterpret_cast<const float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16);
+        sj[j] = sn[tc.f0 + j];
+      }
+    }
+  };
+  TileCoords tc = tile_coords(pair, q4);
+  float4 h[8];
+  float sj[8];
+  if (prod) load_tile(tc, h, sj);
+
+  if (tid < kFD) {
+    sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kFD + tid);
+    sh.pk[tid] = pend_k[(size_t)n * kFD + tid];
+    sh.pv[tid] = pend_v[(size_t)n * kFD + tid];
+    sh.ek[tid] = win_k[((size_t)n * wrows + slot) * kFD + tid];
+  }
+  for (int i = tid; i < 16 * MT * (kFD / 4); i += kThreads2) {
+    const int c = i / (kFD / 4);
+    const int d4 = i % (kFD / 4);
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < lambda) x = *reinterpret_cast<const float4*>(cache_k + ((size_t)n * lambda + c) * kFD + 4 * d4);
+    *reinterpret_cast<float4*>(&sh.lp.ck[c][4 * d4]) = x;
+  }
+  __syncthreads();
+
+  const float4 v4 = *reinterpret_cast<const float4*>(&sh.pv[4 * l16]);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dacc[4] = {0.f, 0.f, 0.f, 0.f};
+  float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 eacc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float oden = 0.0f, eden = 0.0f;
+
+  int it = 0;
+#pragma unroll 1
+  for (int T = pair; T < kFTiles; T += kPairs2, ++it) {
+    const int buf = it & 1;
+    const bool more = T + kPairs2 < kFTiles;
+    const TileCoords tcn = more ? tile_coords(T + kPairs2, q4) : tc;
+    float4 hn[8];
+    float sjn[8];
+    if (prod) {
+      if (more) load_tile(tcn, hn, sjn);
+      float pk[8], pq[8], pe[8];
+      phi8(sh.pk, tc, pk);
+      phi8(sh.qs, tc, pq);
+      phi8(sh.ek, tc, pe);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= tc.jmin) {
+          h[j].x += pk[j] * v4.x;
+          h[j].y += pk[j] * v4.y;
+          h[j].z += pk[j] * v4.z;
+          h[j].w += pk[j] * v4.w;
+          sj[j] += pk[j];
+          *reinterpret_cast<float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16) = h[j];
+        }
+        oacc.x += pq[j] * h[j].x;
+        oacc.y += pq[j] * h[j].y;
+        oacc.z += pq[j] * h[j].z;
+        oacc.w += pq[j] * h[j].w;
+        oden += pq[j] * sj[j];
+        eacc.x += pe[j] * h[j].x;
+        eacc.y += pe[j] * h[j].y;
+        eacc.z += pe[j] * h[j].z;
+        eacc.w += pe[j] * h[j].w;
+        eden += pe[j] * sj[j];
+      }
+      {
+        float x = sj[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) x = l16 == j ? sj[j] : x;
+        if (l16 < 8 && l16 >= tc.jmin) sn[tc.f0 + l16] = x;
+        if (l16 < 8) sh.lp.sj[pair][buf][q4][l16] = x;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
+        bf16x8 b0, b1, b2;
+        split3(x, b0, b1, b2);
+        sh.lp.bp[pair][buf][3 * nt][lane] = __builtin_bit_cast(uint4, b0);
+        sh.lp.bp[pair][buf][3 * nt + 1][lane] = __builtin_bit_cast(uint4, b1);
+        sh.lp.bp[pair][buf][3 * nt + 2][lane] = __builtin_bit_cast(uint4, b2);
+      }
+    }
+    lds_sync();  // tile T's pieces and s are published
+    if (!prod) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sj[j] = sh.lp.sj[pair][buf][q4][j];
+    }
+    bf16x8 ahi[4], alo[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m < mc) {
+        float p[8];
+        phi8(sh.lp.ck[16 * (mb + m) + l16], tc, p);
+        float dd = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dd += p[j] * sj[j];
+        dacc[m] += dd;
+        split2(p, ahi[m], alo[m]);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, sh.lp.bp[pair][buf][3 * nt][lane]);
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, sh.lp.bp[pair][buf][3 * nt + 1][lane]);
+      const bf16x8 b2 = __builtin_bit_cast(bf16x8, sh.lp.bp[pair][buf][3 * nt + 2][lane]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < mc) {
+          acc[m][nt] = mfma16x16x32(ahi[m], b0, acc[m][nt]);
+          acc[m][nt] = mfma16x16x32(ahi[m], b1, acc[m][nt]);
+          acc[m][nt] = mfma16x16x32(ahi[m], b2, acc[m][nt]);
+          acc[m][nt] = mfma16x16x32(alo[m], b0, acc[m][nt]);
+        }
+      }
+    }
+    if (prod && more) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h[j] = hn[j];
+        sj[j] = sjn[j];
+      }
+    }
+    tc = tcn;
+  }
+
+  // ---- vector-unit readouts (producers): over the lane quarters, then the pairs
+  if (prod) {
+    float ox[4] = {oacc.x, oacc.y, oacc.z, oacc.w};
+    float ex[4] = {eacc.x, eacc.y, eacc.z, eacc.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ox[i] += __shfl_xor(ox[i], 16, 64);
+      ox[i] += __shfl_xor(ox[i], 32, 64);
+      ex[i] += __shfl_xor(ex[i], 16, 64);
+      ex[i] += __shfl_xor(ex[i], 32, 64);
+    }
+    oden += __shfl_xor(oden, 16, 64);
+    oden += __shfl_xor(oden, 32, 64);
+    eden += __shfl_xor(eden, 16, 64);
+    eden += __shfl_xor(eden, 32, 64);
+    if (q4 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sh.onum[pair][4 * l16 + i] = ox[i];
+        sh.enm[pair][4 * l16 + i] = ex[i];
+      }
+    }
+    if (lane == 0) {
+      sh.oden[pair] = oden;
+      sh.eden[pair] = eden;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m < mc) {
+      float d = dacc[m];
+      d += __shfl_xor(d, 16, 64);
+      d += __shfl_xor(d, 32, 64);
+      if (q4 == 0) sh.den[pair][16 * (mb + m) + l16] = d;
+    }
+  }
+  // numerators: the pairs add into the LDS copy in turn (producers blocks
+  // 0..3, consumers blocks 4..); the last pair keeps the sums. The first
+  // barrier also ends every read of the keys and pieces, whose LDS the
+  // partials reuse.
+  for (int r = 0; r < kPairs2; ++r) {
+    __syncthreads();
+    if (pair == r) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < mc) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            f32x4 x = acc[m][nt];
+            if (r > 0) {
+              const float4 y = sh.red[mb + m][nt][lane];
+              x[0] += y.x;
+              x[1] += y.y;
+              x[2] += y.z;
+              x[3] += y.w;
+            }
+            acc[m][nt] = x;
+            if (r + 1 < kPairs2) sh.red[mb + m][nt][lane] = make_float4(x[0], x[1], x[2], x[3]);
+          }
+        }
+      }
+    }
+  }
+  if (wv == 0) {
+    // the linear readout of q, then the evicted pair's score
+    float num = 0.0f, den = 0.0f, en = 0.0f, ed = eps;
+#pragma unroll
+    for (int r = 0; r < kPairs2; ++r) {
+      num += sh.onum[r][lane];
+      den += sh.oden[r];
+      en += sh.enm[r][lane];
+      ed += sh.eden[r];
+    }
+    lin[(size_t)n * lstride + lane] = num;
+    if (lane == 0) lin[(size_t)n * lstride + kFD] = den;
+    const float pred = ed != 0.0f ? en / ed : 0.0f;
+    const float diff = pred - win_v[((size_t)n * wrows + slot) * kFD + lane];
+    const float err = wave_sum(diff * diff);
+    if (lane == 0) scores[(size_t)n * sstride + lambda] = err;
+  }
+  if (pair == kPairs2 - 1) {
+    // lane (l16, q4) holds candidates 16*(mb + m) + 4*q4 + i at state columns 4*l16 + nt
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m < mc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * (mb + m) + 4 * q4 + i;
+          const bool live = c < lambda;
+          float den = eps;
+#pragma unroll
+          for (int r = 0; r < kPairs2; ++r) den += sh.den[r][c];
+          float4 vc = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (live) vc = *reinterpret_cast<const float4*>(cache_v + ((size_t)n * lambda + c) * kFD + 4 * l16);
+          float err = 0.0f;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const float pred = den != 0.0f ? acc[m][nt][i] / den : 0.0f;
+            const float diff = pred - comp(vc, nt);
+            err += diff * diff;
+          }
+          err += __shfl_xor(err, 1, 64);
+          err += __shfl_xor(err, 2, 64);
+          err += __shfl_xor(err, 4, 64);
+          err += __shfl_xor(err, 8, 64);
+          if (l16 == 0 && live) scores[(size_t)n * sstride + c] = err;
+        }
       }
     }
   }
@@ -659,19 +1019,25 @@ hipError_t launch_state(const HybridDecodeArgs& a, int mt, int wrows, int slot, 
   hipLaunchKernelGGL((hdec_state_kernel<M, Tin>), dim3(a.N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,       \
                      a.pend_v, static_cast<const Tin*>(a.q), a.cache_k, a.cache_v, a.win_k, a.win_v, wrows,   \
                      slot, a.cache_size, scores, sstride, lin, lstride, a.eps)
+#define KLA_STATE2(M)                                                                                           \
+  hipLaunchKernelGGL((hdec_state2_kernel<M, Tin>), dim3(a.N), dim3(kThreads2), 0, st, a.H, a.s, a.pend_k,     \
+                     a.pend_v, static_cast<const Tin*>(a.q), a.cache_k, a.cache_v, a.win_k, a.win_v, wrows,   \
+                     slot, a.cache_size, scores, sstride, lin, lstride, a.eps)
+  // up to 64 candidates: one wave per SIMD holds every block; more: two
   switch (mt) {
     case 0: KLA_STATE(0); break;
     case 1: KLA_STATE(1); break;
     case 2: KLA_STATE(2); break;
     case 3: KLA_STATE(3); break;
     case 4: KLA_STATE(4); break;
-    case 5: KLA_STATE(5); break;
-    case 6: KLA_STATE(6); break;
-    case 7: KLA_STATE(7); break;
-    case 8: KLA_STATE(8); break;
+    case 5: KLA_STATE2(5); break;
+    case 6: KLA_STATE2(6); break;
+    case 7: KLA_STATE2(7); break;
+    case 8: KLA_STATE2(8); break;
     default: return hipErrorInvalidValue;
   }
 #undef KLA_STATE
+#undef KLA_STATE2
   return hipGetLastError();
 }
 

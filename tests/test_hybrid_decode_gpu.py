@@ -122,6 +122,9 @@ def _check(q, k, v, W, lam, scale, eps, go, grej, st, rtol, heads=None, t0=0, pr
     (16, 64, 5, 0, 90, 2, 0.0),        # no cache: every evicted token folds
     (64, 32, 0, 6, 80, 2, 0.0),        # no window: only the new token is softmax-local
     (64, 64, 300, 255, 700, 2, 0.0),   # largest cache; window + cache span several key tiles
+    (64, 64, 40, 100, 400, 2, 0.0),    # matrix-core scoring, two waves per SIMD, ragged last block
+    (64, 64, 16, 72, 300, 2, 0.5),     # the same with five candidate blocks and eps > 0
+    (64, 64, 24, 48, 260, 2, 0.0),     # matrix-core scoring, one wave per SIMD
 ])
 def test_hybrid_decode_f32(K, dqk, dv, W, lam, T, N, eps):
     q, k, v = _gaussian_heads(N, T, dqk, dv, seed=500 + dqk + dv + W + lam)
