@@ -14,6 +14,8 @@ from .kla_oracle import (  # noqa: F401
     phi_dim,
     phi_pairs,
     prefill,
+    prefill_backward,
+    prefill_backward_rows,
     prefill_bruteforce,
     prefill_bruteforce_rows,
     prefill_chunked,

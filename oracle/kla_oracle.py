@@ -221,6 +221,71 @@ def prefill(q, k, v, chunk: int = 256, H0=None, s0=None, eps: float = 0.0):
 
 
 # ----------------------------------------------------------------------------
+# Backward: gradients of the causal prefill outputs
+# ----------------------------------------------------------------------------
+
+def prefill_backward(q, k, v, do, eps: float = 0.0):
+    """Gradients of L = sum_t do_t . o_t with respect to q, k and v, for the
+    causal prefill of KATA §1 with the lift of §2.2 written in its brute-force
+    form (phi(q).phi(k) = (q.k)^2):
+      s_ti = q_t . k_i,  w_ti = s_ti^2 (i <= t),  D_t = sum_i w_ti + eps,
+      o_t = sum_i w_ti v_i / D_t  (0 when D_t is 0).
+    The chain rule gives, with c_t = do_t . o_t,
+      dv_i = sum_{t >= i} (w_ti / D_t) do_t,
+      dw_ti = (do_t . v_i - c_t) / D_t,   ds_ti = 2 s_ti dw_ti,
+      dq_t = sum_{i <= t} ds_ti k_i,      dk_i = sum_{t >= i} ds_ti q_t.
+    Rows with D_t = 0 have a constant zero output and pass no gradient.
+    Returns dq [T, d], dk [T, d], dv [T, dv] (float64).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    S = np.tril(q @ k.T)
+    W = S * S
+    D = W.sum(axis=1) + eps
+    live = D != 0
+    inv = np.zeros_like(D)
+    inv[live] = 1.0 / D[live]
+    o = (W @ v) * inv[:, None]
+    c = np.sum(do * o, axis=1)
+    dv = (W * inv[:, None]).T @ do
+    dW = ((do @ v.T) - c[:, None]) * inv[:, None]
+    dS = np.tril(2.0 * S * dW)
+    dq = dS @ k
+    dk = dS.T @ q
+    return dq, dk, dv
+
+
+def prefill_backward_rows(q, k, v, do, q_rows, k_rows, eps: float = 0.0, chunk: int = 256):
+    """prefill_backward for selected rows only: dq at the queries q_rows and
+    dk, dv at the keys k_rows, each in O(T (d + d_v)) once every o_t and D_t
+    are known (from the chunked form). Same formulas as prefill_backward."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    o, _, _, _, D = prefill_chunked(q, k, v, chunk=chunk, eps=eps, return_parts=True)
+    live = D != 0
+    inv = np.zeros_like(D)
+    inv[live] = 1.0 / D[live]
+    c = np.sum(do * o, axis=1)
+    dq = np.zeros((len(q_rows), q.shape[1]))
+    for r, t in enumerate(q_rows):
+        st = k[: t + 1] @ q[t]
+        dw = (v[: t + 1] @ do[t] - c[t]) * inv[t]
+        dq[r] = (2.0 * st * dw) @ k[: t + 1]
+    dk = np.zeros((len(k_rows), k.shape[1]))
+    dv = np.zeros((len(k_rows), v.shape[1]))
+    for r, i in enumerate(k_rows):
+        si = q[i:] @ k[i]
+        dv[r] = (si * si * inv[i:]) @ do[i:]
+        dw = (do[i:] @ v[i] - c[i:]) * inv[i:]
+        dk[r] = (2.0 * si * dw) @ q[i:]
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
 # Decode step, self-recall error, selection
 # ----------------------------------------------------------------------------
 

@@ -1,7 +1,8 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins
 catch each one: a dropped sqrt(2), a dropped diagonal, a read-before-update,
 a transposed intra-chunk operand, an unnormalised prediction, a reversed
-selection, a fold of the kept pairs."""
+selection, a fold of the kept pairs, a gradient without its centering term,
+swapped query and key gradients."""
 import functools
 
 import numpy as np
@@ -9,6 +10,7 @@ import pytest
 
 import oracle as O
 import oracle.kla_oracle as K
+from tests import test_oracle_backward as TB
 from tests import test_oracle_hybrid as TH
 from tests import test_oracle_phi_prefill as TP
 from tests import test_oracle_sre_select as TS
@@ -74,6 +76,25 @@ def _select_ascending(scores, m, ids=None):
     return np.lexsort((ids, np.asarray(scores)))[:m]  # planted: lowest first
 
 
+def _backward_no_centering(q, k, v, do, eps=0.0):
+    # planted: forgets the -c_t term of the denominator's derivative
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    S = np.tril(q @ k.T)
+    W = S * S
+    D = W.sum(axis=1) + eps
+    dv = (W / D[:, None]).T @ do
+    dS = np.tril(2.0 * S * (do @ v.T) / D[:, None])
+    return dS @ k, dS.T @ q, dv
+
+
+def _backward_transposed(q, k, v, do, eps=0.0):
+    # planted: query and key gradients swapped
+    dq, dk, dv = REAL_BACKWARD(q, k, v, do, eps=eps)
+    return dk, dq, dv
+
+
+REAL_BACKWARD = O.prefill_backward
+
 CASES = [
     ("phi", _phi_no_sqrt2, [TP.test_phi_golden, TP.test_phi_random_float_identity]),
     ("prefill_chunked", _chunked_strict_lower, [TP.test_first_token_returns_its_value]),
@@ -83,6 +104,9 @@ CASES = [
     ("decode_step", _decode_read_first, [TS.test_decode_step_matches_definition_cases]),
     ("sre", _sre_unnormalised, [TS.test_sre_golden]),
     ("select_topk", _select_ascending, [TS.test_select_topk_order_against_python_sort]),
+    ("prefill_backward", _backward_no_centering, [TB.test_homogeneity_identities]),
+    ("prefill_backward_transposed", _backward_transposed,
+     [functools.partial(TB.test_gradients_match_finite_differences, 7, 3, 2, 0.0)]),
 ]
 
 
