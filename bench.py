@@ -7,11 +7,11 @@ Main line: bf16 prefill of 4 x 8 heads x 4096 tokens, d = 64 (D = 2080),
 chunk 64 — one step is one kla_prefill call (lift, intra-chunk term,
 cross-chunk state readout and update, combine). Secondary lines (in
 "secondary"): the 16-head x 65536-token long-context prefill, the main
-workload again through the quadratic (no state) form, the decode +
-self-recall selection loop (4096 head-states, 128 steps), the hybrid
-prefill (2 x 16 x 16384) and the token-by-token hybrid decode (4096
-head-states, 128 steps after a 2048-token fill). Inputs are seeded synthetic tensors resident in HBM
-before timing.
+workload again through the quadratic (no state) form, its gradients (the
+quadratic-form backward), the decode + self-recall selection loop (4096
+head-states, 128 steps), the hybrid prefill (2 x 16 x 16384) and the
+token-by-token hybrid decode (4096 head-states, 128 steps after a 2048-token
+fill). Inputs are seeded synthetic tensors resident in HBM before timing.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
 """
@@ -150,6 +150,34 @@ def bench_prefill_quadratic(torch, K, S, name, steps, warmup):
         roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=achieved / PEAK_BF16_TFLOPS, kernel_ms=kern_ms, traffic=None,
                       kernel="quadratic-form prefill", flops_per_launch=kern_flops),
+        arith="bf16",
+    )
+
+
+def bench_prefill_backward(torch, K, S, name, steps, warmup):
+    """Gradients of the main workload (quadratic-form backward), after one
+    forward that stores the row denominators."""
+    cfg = S.CONFIGS[name]
+    c = S.prefill_case(name, cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
+                       cfg["seed"])
+    q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (c.q, c.k, c.v))
+    del c
+    g = torch.randn(v.shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(8)).to(
+        torch.bfloat16)
+    _, den = K.prefill_quadratic(q, k, v, return_den=True)
+    step_ms, kern_ms, per_step = timed_calls(
+        torch, K, lambda: K.prefill_quadratic_backward(q, k, v, den, g), steps, warmup)
+    B, H, T, d, dv = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
+    # causal pairs x (S = q.k, dP = g.v, dV += P g, dK += dS q, dQ += dS k), 2 flop per multiply-add
+    kern_flops = B * H * T * (T + 1) / 2 * 2.0 * (3 * d + 2 * dv)
+    achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+    return dict(
+        workload=name + " backward (quadratic form)", B=B, H=H, T=T, d_qk=d, d_v=dv, step_ms=step_ms,
+        tokens_per_s=B * T / (step_ms * 1e-3),
+        roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                      frac=achieved / PEAK_BF16_TFLOPS, kernel_ms=kern_ms, traffic=None,
+                      kernel="quadratic-form backward (dQ and dK/dV kernels, one span)",
+                      flops_per_launch=kern_flops),
         arith="bf16",
     )
 
@@ -304,7 +332,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
-    ap.add_argument("--only", choices=["prefill_1x16x65536", "prefill_4x8x4096_quadratic", "decode_sre_4096x128",
+    ap.add_argument("--only", choices=["prefill_1x16x65536", "prefill_4x8x4096_quadratic",
+                                       "prefill_4x8x4096_backward", "decode_sre_4096x128",
                                        "hybrid_2x16x16384", "hybrid_decode_4096"],
                     help="run just this secondary workload and print its line (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -334,6 +363,8 @@ def main():
             r = bench_prefill(torch, K, S, args.only, args.steps, args.warmup)
         elif args.only == "prefill_4x8x4096_quadratic":
             r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
+        elif args.only == "prefill_4x8x4096_backward":
+            r = bench_prefill_backward(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
         elif args.only == "decode_sre_4096x128":
             r = bench_decode(torch, K, S, args.decode_steps, max(1, args.steps // 10))
         elif args.only == "hybrid_decode_4096":
@@ -353,6 +384,8 @@ def main():
         secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1))
         log("[bench] secondary: prefill_4x8x4096 in the quadratic form")
         secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup))
+        log("[bench] secondary: prefill_4x8x4096 backward")
+        secondary.append(bench_prefill_backward(torch, K, S, name, args.steps, args.warmup))
         log("[bench] secondary: decode_sre_4096x128")
         secondary.append(bench_decode(torch, K, S, args.decode_steps, 2))
         torch.cuda.empty_cache()

@@ -73,7 +73,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 1
+#define KLA_ABI_VERSION 2
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -136,11 +136,39 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
  *
  *   q, k, v : [B, H, T, 64] bf16 (required);  o : [B, H, T, 64], out_dtype
  *             (required).
+ *   den     : [B, H, T] float32, or NULL: den_t + eps, the row denominators
+ *             kla_prefill_quadratic_backward needs.
  * Supported: d_qk = d_v = 64, in_dtype bf16, out_dtype bf16 or float32;
  * other shapes return KLA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 KLA_API kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const void* k,
-                                   const void* v, void* o, kla_stream_t stream);
+                                   const void* v, void* o, float* den, kla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kla_prefill_quadratic_backward - gradients of the causal prefill (the
+ * function of kla_prefill and kla_prefill_quadratic) for training. With
+ * s_ti = q_t . k_i, w_ti = s_ti^2 (i <= t), D_t = sum_i w_ti + eps and a
+ * loss gradient g_t = dL/do_t, c_t = g_t . o_t = sum_i (w_ti / D_t) g_t . v_i:
+ *   dv_i = sum_{t>=i} (w_ti / D_t) g_t,
+ *   ds_ti = 2 s_ti (g_t . v_i - c_t) / D_t,
+ *   dq_t = sum_{i<=t} ds_ti k_i,   dk_i = sum_{t>=i} ds_ti q_t
+ * (the chain rule on the outputs of KATA §1 with the lift of §2.2). Rows
+ * whose D_t is 0 pass no gradient. Computed in the quadratic form on the
+ * bf16 matrix cores (float32 sums); c_t is recomputed from the same products
+ * the gradients use, so the forward's output is not an input.
+ *
+ *   q, k, v     : [B, H, T, 64] bf16, the forward's inputs.
+ *   den         : [B, H, T] float32 from kla_prefill_quadratic.
+ *   dout        : [B, H, T, 64] out_dtype, dL/do.
+ *   dq, dk, dv  : [B, H, T, 64] out_dtype outputs.
+ *   ws          : kla_prefill_quadratic_backward_workspace_size bytes.
+ * Supported: d_qk = d_v = 64, in_dtype bf16, out_dtype bf16 or float32.
+ * ------------------------------------------------------------------------ */
+KLA_API kla_status_t kla_prefill_quadratic_backward_workspace_size(const kla_shape_t* shp, size_t* bytes);
+KLA_API kla_status_t kla_prefill_quadratic_backward(const kla_shape_t* shp, const void* q, const void* k,
+                                            const void* v, const float* den, const void* dout, void* dq,
+                                            void* dk, void* dv, void* ws, size_t ws_bytes,
+                                            kla_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Self-recall error and selection (LoLA, the self-recall-error section and
@@ -329,8 +357,9 @@ KLA_API kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla
  * every call records a pair of HIP events on its stream around its dominant
  * kernel: the state/readout kernel of kla_prefill, the state-streaming
  * kernel of kla_decode_step, the scoring kernel of kla_sre_select, each
- * scoring kernel of kla_hybrid_prefill, and every kernel of a
- * kla_hybrid_decode_step (one span). kla_profile_read waits for the last
+ * scoring kernel of kla_hybrid_prefill, every kernel of a
+ * kla_hybrid_decode_step (one span), the kernel of kla_prefill_quadratic and
+ * the two kernels of kla_prefill_quadratic_backward (one span). kla_profile_read waits for the last
  * recorded event, returns the summed elapsed milliseconds and the number of
  * recorded kernels, and clears the record. Events come from a pool owned by
  * the thread; up to 65536 pairs are kept per read (later ones are counted in

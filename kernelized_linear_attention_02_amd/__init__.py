@@ -6,6 +6,7 @@ ABI of include/kla.h); this package only marshals arguments to it:
 
   prefill         chunked causal prefill over the float32 state (H, s)
   prefill_quadratic  the same outputs in the quadratic (no state) form
+  prefill_quadratic_backward  gradients of the prefill (quadratic form)
   decode_step     one recurrent token, optionally with self-recall scoring
   sre_select      self-recall-error scoring and top-k selection
   hybrid_prefill  sliding window + linear state + sparse cache
@@ -26,12 +27,13 @@ from ._binding import (  # noqa: F401
     phi_dim,
     prefill,
     prefill_quadratic,
+    prefill_quadratic_backward,
     prefill_uses_matrix_cores,
     profile_enable,
     profile_read,
     sre_select,
 )
 
-__all__ = ["prefill", "prefill_quadratic", "decode_step", "sre_select", "hybrid_prefill",
+__all__ = ["prefill", "prefill_quadratic", "prefill_quadratic_backward", "decode_step", "sre_select", "hybrid_prefill",
            "hybrid_decode_state", "hybrid_decode_step", "hybrid_decode_flush", "phi_dim", "load_library",
            "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

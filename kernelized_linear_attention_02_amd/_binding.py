@@ -21,6 +21,7 @@ KLA_F32, KLA_BF16 = 0, 1
 EXPORTS = (
     "kla_abi_version", "kla_phi_dim", "kla_status_string", "kla_last_error",
     "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill", "kla_prefill_quadratic",
+    "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill",
@@ -87,7 +88,9 @@ def load_library(path: str = LIB_PATH):
         "kla_prefill_matrix_path": (i, [shp, i]),
         "kla_prefill_workspace_size": (i, [shp, i, i, szp]),
         "kla_prefill": (i, [shp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
-        "kla_prefill_quadratic": (i, [shp, vp, vp, vp, vp, vp]),
+        "kla_prefill_quadratic": (i, [shp, vp, vp, vp, vp, vp, vp]),
+        "kla_prefill_quadratic_backward_workspace_size": (i, [shp, szp]),
+        "kla_prefill_quadratic_backward": (i, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
         "kla_decode_step": (i, [i, i, i, f, vp, vp, vp, vp, vp, i, vp, i, srp, vp, sz, vp]),
         "kla_sre_workspace_size": (i, [i, i, i, srp, szp]),
@@ -218,9 +221,11 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     return (o, HT, sT) if return_state else o
 
 
-def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None):
+def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None, return_den: bool = False):
     """Causal prefill in the quadratic form (no state): q, k, v [B, H, T, 64]
-    bfloat16. Returns o [B, H, T, 64] (bfloat16, or ``out_dtype``)."""
+    bfloat16. Returns o [B, H, T, 64] (bfloat16, or ``out_dtype``), and with
+    ``return_den`` also the row denominators den [B, H, T] float32 (for
+    prefill_quadratic_backward)."""
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
@@ -240,8 +245,36 @@ def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None):
         o = out
     else:
         o = torch.empty((B, Hh, T, dv), dtype=_torch_dtype(ocode), device=q.device)
-    check(lib.kla_prefill_quadratic(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(q.device)))
-    return o
+    den = torch.empty((B, Hh, T), dtype=torch.float32, device=q.device) if return_den else None
+    check(lib.kla_prefill_quadratic(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                                    _stream(q.device)))
+    return (o, den) if return_den else o
+
+
+def prefill_quadratic_backward(q, k, v, den, dout, eps: float = 0.0):
+    """Gradients (dq, dk, dv) of the causal prefill for dL/do = ``dout``:
+    q, k, v [B, H, T, 64] bfloat16; den [B, H, T] float32 from
+    prefill_quadratic(..., return_den=True); dout [B, H, T, 64] bfloat16 or
+    float32. The gradients come back in the dtype of dout."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(q, k, v, den, dout)
+    q, k, v, den, dout = (x.contiguous() for x in (q, k, v, den, dout))
+    if not (q.dtype == k.dtype == v.dtype) or den.dtype != torch.float32:
+        raise TypeError("q, k, v share one dtype; den is float32")
+    B, Hh, T, dqk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != q.shape[:3] + (dv,) or dout.shape != v.shape or den.shape != q.shape[:3]:
+        raise ValueError("shape mismatch between q, k, v, den and dout")
+    shp = Shape(B, Hh, T, dqk, dv, _dtype_code(q), _dtype_code(dout), float(eps))
+    dq, dk, dvv = torch.empty_like(dout), torch.empty_like(dout), torch.empty_like(dout)
+    nbytes = ctypes.c_size_t(0)
+    check(lib.kla_prefill_quadratic_backward_workspace_size(ctypes.byref(shp), ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, q.device)
+    check(lib.kla_prefill_quadratic_backward(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(den), _ptr(dout),
+                                             _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(ws), nbytes.value,
+                                             _stream(q.device)))
+    return dq, dk, dvv
 
 
 def _sre_struct(cand_k, cand_v, top_k, scores, sel, sel_k, sel_v, sel_stride=0):

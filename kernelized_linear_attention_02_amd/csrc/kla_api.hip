@@ -318,7 +318,7 @@ kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const
 }
 
 kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const void* k, const void* v,
-                                   void* o, kla_stream_t stream) {
+                                   void* o, float* den, kla_stream_t stream) {
   const char* fn = "kla_prefill_quadratic";
   kla_status_t st = check_shape(shp, fn);
   if (st != KLA_OK) return st;
@@ -328,9 +328,50 @@ kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const 
   a.k = k;
   a.v = v;
   a.o = o;
+  a.den = den;
   if (!kla::prefill_quad_supported(a))
     return fail(KLA_ERR_UNSUPPORTED, "%s: needs d_qk = d_v = 64 and bf16 inputs", fn);
   return hip_status(kla::prefill_quad_launch(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+kla_status_t kla_prefill_quadratic_backward_workspace_size(const kla_shape_t* shp, size_t* bytes) {
+  const char* fn = "kla_prefill_quadratic_backward_workspace_size";
+  if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  kla::QuadBwdArgs a{};
+  a.N = shp->B * shp->H;
+  a.T = shp->T;
+  *bytes = kla::prefill_quad_bwd_workspace(a);
+  return ok();
+}
+
+kla_status_t kla_prefill_quadratic_backward(const kla_shape_t* shp, const void* q, const void* k, const void* v,
+                                            const float* den, const void* dout, void* dq, void* dk, void* dv,
+                                            void* ws, size_t ws_bytes, kla_stream_t stream) {
+  const char* fn = "kla_prefill_quadratic_backward";
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  if (!q || !k || !v || !den || !dout || !dq || !dk || !dv)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v, den, dout, dq, dk and dv are required", fn);
+  if (shp->in_dtype != KLA_BF16 || shp->d_qk != 64 || shp->d_v != 64)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: needs d_qk = d_v = 64 and bf16 inputs", fn);
+  kla::QuadBwdArgs a{};
+  a.N = shp->B * shp->H;
+  a.T = shp->T;
+  a.out_bf16 = shp->out_dtype == KLA_BF16;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.den = den;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  st = check_ws(kla::prefill_quad_bwd_workspace(a), ws, ws_bytes, fn);
+  if (st != KLA_OK) return st;
+  return hip_status(kla::prefill_quad_bwd_launch(a, ws, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 // ---------------------------------------------------------------- decode / SRE

@@ -31,6 +31,7 @@ struct PrefillArgs {
   const float* s0;
   float* HT;
   float* sT;
+  float* den;  // quadratic form only: row denominators [N, T], or NULL
 };
 
 // Generic float32-arithmetic path (VALU): any supported shape, either dtype.
@@ -46,6 +47,23 @@ hipError_t prefill_mfma_launch(const PrefillArgs& a, void* ws, hipStream_t st);
 // Quadratic (O(T^2)) form, d_qk = d_v = 64 and bf16 inputs; no workspace.
 bool prefill_quad_supported(const PrefillArgs& a);
 hipError_t prefill_quad_launch(const PrefillArgs& a, hipStream_t st);
+
+// Its backward: dq, dk, dv from q, k, v (bf16), do (out dtype) and the
+// forward's row denominators.
+struct QuadBwdArgs {
+  int N, T;
+  bool out_bf16;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* den;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+};
+size_t prefill_quad_bwd_workspace(const QuadBwdArgs& a);
+hipError_t prefill_quad_bwd_launch(const QuadBwdArgs& a, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------- decode / SRE
 

@@ -21,14 +21,18 @@
 //     past the wave's first query) and rounds them to bf16 as the B operand
 //     of O^T = V^T P^T, taking P's k-slots in the order they sit in the lanes
 //     (keys 4 q4 + j of tile 2p, then of tile 2p + 1) and V^T's in the same
-//     order, so no value moves between lanes; a row of ones beside V^T gives
-//     the denominators from the same bf16 weights.
+//     order, so no value moves between lanes; the denominators are float32
+//     sums of the unrounded weights on the vector units (the backward needs
+//     them accurate: it divides by them again).
 // Each K and V fragment read from LDS serves both query tiles of the wave.
+// On request the row denominators den_t + eps are stored as well (float32),
+// for the backward.
 #include <algorithm>
 #include <type_traits>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
+#include "quad_tiles.hpp"
 
 namespace kla {
 namespace {
@@ -80,41 +84,13 @@ __device__ __forceinline__ KVLoad load_kv(const uint16_t* __restrict__ k, const 
   return r;
 }
 
-// Column of key `key` in a v^T row. Within each group of 32 keys, key
-// 16 t + 4 g + i goes to column 8 g + 4 t + i, so that the eight keys a lane
-// quarter g holds in its P^T fragment (4 g + i of both 16-key tiles) are
-// eight adjacent columns: one 16-byte read.
-__device__ __forceinline__ int vt_col(int key) {
-  const int r = key & 15;
-  return (key & ~31) + 8 * (r >> 2) + 4 * ((key >> 4) & 1) + (r & 3);
-}
-
-// The value of the neighbouring lane (lane ^ 1, the other key of the pair).
-__device__ __forceinline__ uint32_t pair_swap(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-}
-
-// Keys 2m and 2m + 1 sit in adjacent lanes and adjacent v^T columns; the two
-// lanes trade half of their eight values so that each writes four whole
-// 32-bit words (both keys of one dimension) instead of eight 16-bit halves.
+// Key rows as they are, values transposed with the column permutation of
+// vt_col (see quad_tiles.hpp).
 __device__ __forceinline__ void stage_kv(QuadLds& sh, int buf, const KVLoad& r, int key, int w) {
-  const int col = vt_col(key) & ~1;
-  const bool even = (key & 1) == 0;
 #pragma unroll
   for (int j = 0; j < kU4; ++j) {
     *reinterpret_cast<uint4*>(&sh.k[buf][key][kDPT * w + 8 * j]) = r.k[j];
-    // dims (2e, 2e + 1) of this key in r.v[j] word e
-    const uint4 u = r.v[j];
-    const uint32_t x0 = pair_swap(even ? u.z : u.x);
-    const uint32_t x1 = pair_swap(even ? u.w : u.y);
-    // the even lane writes dims 0..3 of its group, the odd lane dims 4..7
-    const uint32_t a0 = even ? u.x : x0, a1 = even ? u.y : x1;  // key 2m
-    const uint32_t b0 = even ? x0 : u.z, b1 = even ? x1 : u.w;  // key 2m + 1
-    const int d = kDPT * w + 8 * j + (even ? 0 : 4);
-    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d][col]) = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
-    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d + 1][col]) = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
-    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d + 2][col]) = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
-    *reinterpret_cast<uint32_t*>(&sh.vt[buf][d + 3][col]) = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+    store_transposed8(&sh.vt[buf][0][0], kVS, r.v[j], key, kDPT * w + 8 * j);
   }
 }
 
@@ -122,7 +98,8 @@ template <typename Tout>
 __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
-                                                              Tout* __restrict__ o, int T, float eps) {
+                                                              Tout* __restrict__ o, float* __restrict__ den,
+                                                              int T, float eps) {
   __shared__ __align__(16) QuadLds sh;
   const int nqb = (T + kBQ - 1) / kBQ;
   const int n = blockIdx.y;
@@ -166,16 +143,13 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
     __syncthreads();
 
     f32x4 acc[2][4];  // O^T: [query tile][dim tile], lane holds dims 16 dt + 4 q4 + i of query l16
-    f32x4 dacc[2];    // row 0: the denominators (a row of ones in V^T), in lanes q4 = 0
+    float dsv[2];     // float32 sums of the weights of query l16 over this lane's keys
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
-      dacc[tq] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dsv[tq] = 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[tq][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    bf16x8 ones;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
 
     // one key block; MASKED: apply the causal mask (blocks with keys above a query of the wave)
     auto key_block = [&](int kb, auto masked_c) {
@@ -209,6 +183,7 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
           for (int i = 0; i < 4; ++i) {
             float p = s[kt][tq][i] * s[kt][tq][i];
             if (MASKED && k0 + 16 * kt + 4 * q4 + i > t) p = 0.0f;
+            dsv[tq] += p;
             pb[kt >> 1][tq][4 * (kt & 1) + i] = (__bf16)p;
           }
         }
@@ -223,8 +198,6 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
 #pragma unroll
           for (int tq = 0; tq < 2; ++tq) acc[tq][dt] = mfma(av, pb[p2][tq], acc[tq][dt]);
         }
-#pragma unroll
-        for (int tq = 0; tq < 2; ++tq) dacc[tq] = mfma(ones, pb[p2][tq], dacc[tq]);
       }
     };
 
@@ -246,13 +219,16 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
       if (kb + 2 < nkb) step(kb + 2, pf0);
     }
 
-    // denominators of query l16 sit in lane (l16, 0)
+    // denominators: the four lane quarters of query l16 hold disjoint keys
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
       const int t = qw0 + 16 * tq + l16;
-      const float dsum = __shfl(dacc[tq][0], l16, 64);
+      float dsum = dsv[tq];
+      dsum += __shfl_xor(dsum, 16, 64);
+      dsum += __shfl_xor(dsum, 32, 64);
       if (t >= T) continue;
       const float d = dsum + eps;
+      if (den && q4 == 0) den[row0 + t] = d;
       const float inv = d != 0.0f ? 1.0f / d : 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -276,11 +252,11 @@ hipError_t prefill_quad_launch(const PrefillArgs& a, hipStream_t st) {
   if (a.out_bf16)
     hipLaunchKernelGGL(prefill_quad_kernel<uint16_t>, grid, dim3(kQT), 0, st, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                       static_cast<uint16_t*>(a.o), a.T, a.eps);
+                       static_cast<uint16_t*>(a.o), a.den, a.T, a.eps);
   else
     hipLaunchKernelGGL(prefill_quad_kernel<float>, grid, dim3(kQT), 0, st, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                       static_cast<float*>(a.o), a.T, a.eps);
+                       static_cast<float*>(a.o), a.den, a.T, a.eps);
   prof_end(st);
   return hipGetLastError();
 }

@@ -162,14 +162,36 @@ def test_binding_rejects_host_tensors():
 
 def test_prefill_quadratic_rejects(lib):
     call = lib.kla_prefill_quadratic
-    assert call(None, P, P, P, P, None) == B.KLA_ERR_INVALID_ARGUMENT
-    assert call(ctypes.byref(_shape()), None, P, P, P, None) == B.KLA_ERR_INVALID_ARGUMENT
-    assert call(ctypes.byref(_shape()), P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(None, P, P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(_shape()), None, P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(_shape()), P, P, P, None, None, None) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"required" in lib.kla_last_error()
     # only d = 64 with bf16 inputs
-    assert call(ctypes.byref(_shape(d_qk=32, d_v=32)), P, P, P, P, None) == B.KLA_ERR_UNSUPPORTED
-    assert call(ctypes.byref(_shape(in_dtype=B.KLA_F32)), P, P, P, P, None) == B.KLA_ERR_UNSUPPORTED
-    assert call(ctypes.byref(_shape(eps=-1.0)), P, P, P, P, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(_shape(d_qk=32, d_v=32)), P, P, P, P, None, None) == B.KLA_ERR_UNSUPPORTED
+    assert call(ctypes.byref(_shape(in_dtype=B.KLA_F32)), P, P, P, P, None, None) == B.KLA_ERR_UNSUPPORTED
+    assert call(ctypes.byref(_shape(eps=-1.0)), P, P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_quadratic_backward_rejects(lib):
+    call = lib.kla_prefill_quadratic_backward
+    shp = ctypes.byref(_shape())
+
+    def go(shape=shp, den=P, ws=P, nbytes=1 << 40, dq=P):
+        return call(shape, P, P, P, den, P, dq, P, P, ws, nbytes, None)
+
+    assert go(shape=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert go(den=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert go(dq=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"required" in lib.kla_last_error()
+    assert go(shape=ctypes.byref(_shape(d_qk=32, d_v=32))) == B.KLA_ERR_UNSUPPORTED
+    assert go(shape=ctypes.byref(_shape(in_dtype=B.KLA_F32))) == B.KLA_ERR_UNSUPPORTED
+    need = ctypes.c_size_t(0)
+    assert lib.kla_prefill_quadratic_backward_workspace_size(shp, ctypes.byref(need)) == B.KLA_OK
+    assert need.value >= 2 * 100 * 4  # c for B*H*T tokens
+    assert go(ws=None) == B.KLA_ERR_WORKSPACE
+    assert go(nbytes=need.value - 1) == B.KLA_ERR_WORKSPACE
+    assert lib.kla_prefill_quadratic_backward_workspace_size(None, ctypes.byref(need)) == \
+        B.KLA_ERR_INVALID_ARGUMENT
 
 
 def test_hybrid_decode_validation(lib):

@@ -79,3 +79,4 @@ def test_row_form_matches_full(eps):
     np.testing.assert_allclose(rq, dq[rows], rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(rk, dk[rows], rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(rv, dv_[rows], rtol=1e-9, atol=1e-12)
+
