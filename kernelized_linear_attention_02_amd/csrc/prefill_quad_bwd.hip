@@ -15,14 +15,15 @@
 // here from the same S and dP values that ds then uses, not from a stored
 // output: any mismatch between the two would be amplified.
 //
-// Two kernels:
-//   q    one work-group per head and pair of 64-query blocks, wave w owning
-//        queries 16 w .. 16 w + 15. Pass 1 over the key blocks at or before
-//        the query block: S^T = K Q_w^T and dP^T = V G_w^T on MFMA
+// Kernels:
+//   q    one work-group per head and pair of 128-query blocks, wave w owning
+//        queries 32 w .. 32 w + 31 as two 16-query tiles, launched twice.
+//        Pass 1 over the key blocks up to the block's last query: S^T = K Q_w^T and dP^T = V G_w^T on MFMA
 //        16x16x32 bf16, c_t = sum_i P_ti dP_ti in float32 (stored for the
 //        kv kernel). Pass 2: the same products, dS, and dQ += dS K;
-//   kv   one work-group per head and pair of 64-key blocks (x, last - x),
-//        wave w owning keys 16 w .. 16 w + 15. For every query block at or
+//   kv   one work-group per head and pair of 128-key blocks (x, last - x),
+//        wave w owning keys 32 w .. 32 w + 31 as two 16-key tiles (every
+//        LDS fragment read then serves both). For every query block at or
 //        after the key block (staged in LDS as rows and as transposed
 //        tiles, double buffered) it forms S = Q K_w^T and dP = G V_w^T,
 //        then P = S^2 / D and dS in float32, and adds P^T G into dV and
@@ -116,13 +117,17 @@ struct KVLds {
   float inv[2][kBB];
 };
 
+constexpr int kKT = 2;                 // 16-key tiles per wave in the dK/dV kernel
+constexpr int kKB = 16 * kKT * kBW;    // keys per dK/dV work-group
+
 template <typename Tout>
 __global__ __launch_bounds__(kBT, 2) void quad_bwd_kv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const Tout* __restrict__ g, const float* __restrict__ cvec, const float* __restrict__ den,
     Tout* __restrict__ dk, Tout* __restrict__ dv, int T) {
   __shared__ __align__(16) KVLds sh;
-  const int nb = (T + kBB - 1) / kBB;
+  const int nkb = (T + kKB - 1) / kKB;  // key blocks
+  const int nqb = (T + kBB - 1) / kBB;  // query blocks
   const int n = blockIdx.y;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,113 +148,139 @@ __global__ __launch_bounds__(kBT, 2) void quad_bwd_kv_kernel(
       sh.inv[buf][stok] = iv;
     }
   };
+  auto fetch = [&](int qb, RowLoad& rq, RowLoad& rg, float& c, float& iv) {
+    const int t = qb * kBB + stok;
+    rq = load_rows(q, row0, t, T, sgrp);
+    rg = load_rows(g, row0, t, T, sgrp);
+    c = 0.0f;
+    iv = 0.0f;
+    if (sgrp == 0 && t < T) {
+      const float d = den[row0 + t];
+      c = cvec[row0 + t];
+      iv = d != 0.0f ? 1.0f / d : 0.0f;
+    }
+  };
 
-  // key blocks nb - 1 - x and x: every work-group does the same causal work
+  // key blocks nkb - 1 - x and x: every work-group does the same causal work
   for (int rep = 0; rep < 2; ++rep) {
-    const int kb = rep == 0 ? nb - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    if (rep == 1 && kb >= nb - 1 - (int)blockIdx.x) break;
-    const int kw0 = kb * kBB + 16 * w;  // this wave's first key
-    const int key = kw0 + l16;          // the key this lane's score columns belong to
+    const int kb = rep == 0 ? nkb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    if (rep == 1 && kb >= nkb - 1 - (int)blockIdx.x) break;
+    const int kw0 = kb * kKB + 16 * kKT * w;  // this wave's first key; tile kk: keys kw0 + 16 kk + l16
 
     // K_w and V_w as the B operands of S = Q K_w^T and dP = G V_w^T
-    bf16x8 kf[2], vf[2];
+    bf16x8 kf[kKT][2], vf[kKT][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      kf[ks] = frag_global(k, row0, key, T, ks, q4);
-      vf[ks] = frag_global(v, row0, key, T, ks, q4);
-    }
-    f32x4 dka[4], dva[4];  // [dim tile]: lane holds keys kw0 + 4 q4 + i at dim 16 nt + l16
+    for (int kk = 0; kk < kKT; ++kk)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) dka[nt] = dva[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // query blocks kb .. nb - 1; block qb + 1 in registers while qb computes
-    auto fetch = [&](int qb, RowLoad& rq, RowLoad& rg, float& c, float& iv) {
-      const int t = qb * kBB + stok;
-      rq = load_rows(q, row0, t, T, sgrp);
-      rg = load_rows(g, row0, t, T, sgrp);
-      c = 0.0f;
-      iv = 0.0f;
-      if (sgrp == 0 && t < T) {
-        const float d = den[row0 + t];
-        c = cvec[row0 + t];
-        iv = d != 0.0f ? 1.0f / d : 0.0f;
+      for (int ks = 0; ks < 2; ++ks) {
+        kf[kk][ks] = frag_global(k, row0, kw0 + 16 * kk + l16, T, ks, q4);
+        vf[kk][ks] = frag_global(v, row0, kw0 + 16 * kk + l16, T, ks, q4);
       }
-    };
+    // [key tile][dim tile]: lane holds keys kw0 + 16 kk + 4 q4 + i at dim 16 nt + l16
+    f32x4 dka[kKT][4], dva[kKT][4];
+#pragma unroll
+    for (int kk = 0; kk < kKT; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) dka[kk][nt] = dva[kk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // query blocks from the one holding the key block's first key; block
+    // qb + 1 in registers while qb computes
+    const int qb0 = kb * kKB / kBB;
     RowLoad rq, rg;
     float pc, piv;
-    fetch(kb, rq, rg, pc, piv);
+    fetch(qb0, rq, rg, pc, piv);
     stage(0, rq, rg, pc, piv);
-    if (kb + 1 < nb) fetch(kb + 1, rq, rg, pc, piv);
+    if (qb0 + 1 < nqb) fetch(qb0 + 1, rq, rg, pc, piv);
     __syncthreads();
 
-    for (int qb = kb; qb < nb; ++qb) {
-      const int buf = (qb - kb) & 1;
+    for (int qb = qb0; qb < nqb; ++qb) {
+      const int buf = (qb - qb0) & 1;
       const int t0 = qb * kBB;
-      // S and dP: query tiles mt (rows), this wave's 16 keys (columns)
-      f32x4 sv[4], dp[4];
+      const bool diag = t0 < (kb + 1) * kKB;  // the block reaches keys above some of its queries
+      // S and dP: query tiles mt (rows), key tile kk (columns); each row
+      // fragment read serves every key tile
+      f32x4 sv[kKT][4], dp[kKT][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 aq[2], ag[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          x = mfma16x16x32(frag(sh.q[buf], 16 * mt + l16, ks, q4), kf[ks], x);
-          y = mfma16x16x32(frag(sh.g[buf], 16 * mt + l16, ks, q4), vf[ks], y);
+          aq[ks] = frag(sh.q[buf], 16 * mt + l16, ks, q4);
+          ag[ks] = frag(sh.g[buf], 16 * mt + l16, ks, q4);
         }
-        sv[mt] = x;
-        dp[mt] = y;
+#pragma unroll
+        for (int kk = 0; kk < kKT; ++kk) {
+          f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            x = mfma16x16x32(aq[ks], kf[kk][ks], x);
+            y = mfma16x16x32(ag[ks], vf[kk][ks], y);
+          }
+          sv[kk][mt] = x;
+          dp[kk][mt] = y;
+        }
       }
       // P = S^2 / D and dS = 2 S (dP - c) / D (zero where key > query); lane
       // (l16, q4) holds queries 16 mt + 4 q4 + i: k-slot 4 (mt & 1) + i of pair mt >> 1
-      const bool diag = qb == kb;
-      bf16x8 ph[2], pl[2], dh[2], dl[2];  // P and dS, each as hi + lo bf16 pieces
+      bf16x8 ph[kKT][2], pl[kKT][2], dh[kKT][2], dl[kKT][2];  // hi + lo bf16 pieces
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float p[8], ds[8];
+      for (int kk = 0; kk < kKT; ++kk) {
+        const int key = kw0 + 16 * kk + l16;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int mt = 2 * ks + (j >> 2);
-          const int i = j & 3;
-          const int tl = 16 * mt + 4 * q4 + i;
-          const float s = sv[mt][i];
-          const float iv = sh.inv[buf][tl];
-          p[j] = s * s * iv;
-          ds[j] = 2.0f * s * (dp[mt][i] - sh.c[buf][tl]) * iv;
-          if (diag && key > t0 + tl) p[j] = ds[j] = 0.0f;
+        for (int ks = 0; ks < 2; ++ks) {
+          float p[8], ds[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int mt = 2 * ks + (j >> 2);
+            const int i = j & 3;
+            const int tl = 16 * mt + 4 * q4 + i;
+            const float s = sv[kk][mt][i];
+            const float iv = sh.inv[buf][tl];
+            p[j] = s * s * iv;
+            ds[j] = 2.0f * s * (dp[kk][mt][i] - sh.c[buf][tl]) * iv;
+            if (diag && key > t0 + tl) p[j] = ds[j] = 0.0f;
+          }
+          split2(p, ph[kk][ks], pl[kk][ks]);
+          split2(ds, dh[kk][ks], dl[kk][ks]);
         }
-        split2(p, ph[ks], pl[ks]);
-        split2(ds, dh[ks], dl[ks]);
       }
-      // dV += P^T G and dK += dS^T Q over the block's 64 queries (two k-steps)
+      // dV += P^T G and dK += dS^T Q over the block's 64 queries (two k-steps);
+      // each transposed fragment read serves every key tile
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const bf16x8 bg = *reinterpret_cast<const bf16x8*>(&sh.gt[buf][16 * nt + l16][32 * ks + 8 * q4]);
           const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sh.qt[buf][16 * nt + l16][32 * ks + 8 * q4]);
-          dva[nt] = mfma16x16x32(ph[ks], bg, dva[nt]);
-          dva[nt] = mfma16x16x32(pl[ks], bg, dva[nt]);
-          dka[nt] = mfma16x16x32(dh[ks], bq, dka[nt]);
-          dka[nt] = mfma16x16x32(dl[ks], bq, dka[nt]);
+#pragma unroll
+          for (int kk = 0; kk < kKT; ++kk) {
+            dva[kk][nt] = mfma16x16x32(ph[kk][ks], bg, dva[kk][nt]);
+            dva[kk][nt] = mfma16x16x32(pl[kk][ks], bg, dva[kk][nt]);
+            dka[kk][nt] = mfma16x16x32(dh[kk][ks], bq, dka[kk][nt]);
+            dka[kk][nt] = mfma16x16x32(dl[kk][ks], bq, dka[kk][nt]);
+          }
         }
       }
-      if (qb + 1 < nb) {
+      if (qb + 1 < nqb) {
         stage(buf ^ 1, rq, rg, pc, piv);
-        if (qb + 2 < nb) fetch(qb + 2, rq, rg, pc, piv);
+        if (qb + 2 < nqb) fetch(qb + 2, rq, rg, pc, piv);
       }
       __syncthreads();
     }
 
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int kk = 0; kk < kKT; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kr = kw0 + 4 * q4 + i;
-        if (kr < T) {
-          Elem<Tout>::store(dk, (row0 + kr) * kBD + 16 * nt + l16, dka[nt][i]);
-          Elem<Tout>::store(dv, (row0 + kr) * kBD + 16 * nt + l16, dva[nt][i]);
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kr = kw0 + 16 * kk + 4 * q4 + i;
+          if (kr < T) {
+            Elem<Tout>::store(dk, (row0 + kr) * kBD + 16 * nt + l16, dka[kk][nt][i]);
+            Elem<Tout>::store(dv, (row0 + kr) * kBD + 16 * nt + l16, dva[kk][nt][i]);
+          }
         }
       }
-    }
   }  // rep
 }
 
@@ -261,13 +292,17 @@ struct QLds {
   uint16_t v[2][kBB][kRS];    // value rows
 };
 
-template <typename Tout>
+constexpr int kQT = 2;                 // 16-query tiles per wave in the dQ kernel
+constexpr int kQB = 16 * kQT * kBW;    // queries per dQ work-group
+
+// PASS 0 stores c for the block's queries; PASS 1 reads it back and forms dQ.
+template <int PASS, typename Tout>
 __global__ __launch_bounds__(kBT, 2) void quad_bwd_q_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const Tout* __restrict__ g, const float* __restrict__ den, float* __restrict__ cvec, Tout* __restrict__ dq,
     int T) {
   __shared__ __align__(16) QLds sh;
-  const int nb = (T + kBB - 1) / kBB;
+  const int nqb = (T + kQB - 1) / kQB;  // query blocks
   const int n = blockIdx.y;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -280,7 +315,7 @@ __global__ __launch_bounds__(kBT, 2) void quad_bwd_q_kernel(
 
   auto stage = [&](int buf, const RowLoad& rk, const RowLoad& rv) {
     stage_rows(sh.k[buf], rk, stok, sgrp);
-    stage_transposed(sh.kt[buf], rk, stok, sgrp);
+    if (PASS == 1) stage_transposed(sh.kt[buf], rk, stok, sgrp);  // for dS K only
     stage_rows(sh.v[buf], rv, stok, sgrp);
   };
   auto fetch = [&](int kb, RowLoad& rk, RowLoad& rv) {
@@ -288,128 +323,176 @@ __global__ __launch_bounds__(kBT, 2) void quad_bwd_q_kernel(
     rv = load_rows(v, row0, kb * kBB + stok, T, sgrp);
   };
 
-  // query blocks nb - 1 - x and x
+  // query blocks nqb - 1 - x and x
   for (int rep = 0; rep < 2; ++rep) {
-    const int qb = rep == 0 ? nb - 1 - (int)blockIdx.x : (int)blockIdx.x;
-    if (rep == 1 && qb >= nb - 1 - (int)blockIdx.x) break;
-    const int qw0 = qb * kBB + 16 * w;  // this wave's first query
-    const int qry = qw0 + l16;          // the query this lane's score columns belong to
+    const int qb = rep == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    if (rep == 1 && qb >= nqb - 1 - (int)blockIdx.x) break;
+    const int qw0 = qb * kQB + 16 * kQT * w;  // this wave's first query; tile tq: queries qw0 + 16 tq + l16
+    const int last = min(T, (qb + 1) * kQB) - 1;  // the block's last query
+    const int nkb = last / kBB + 1;               // key blocks with keys <= last
 
     // Q_w and G_w as the B operands of S^T = K Q_w^T and dP^T = V G_w^T
-    bf16x8 qf[2], gf[2];
+    bf16x8 qf[kQT][2], gf[kQT][2];
+    float iq[kQT];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      qf[ks] = frag_global(q, row0, qry, T, ks, q4);
-      gf[ks] = frag_global(g, row0, qry, T, ks, q4);
-    }
-    float iq = 0.0f;
-    if (qry < T) {
-      const float d = den[row0 + qry];
-      iq = d != 0.0f ? 1.0f / d : 0.0f;
-    }
-    float cq = 0.0f;  // c of query qry, after pass 1
-    f32x4 dqa[4];     // [dim tile]: lane holds queries qw0 + 4 q4 + i at dim 16 nt + l16
+    for (int tq = 0; tq < kQT; ++tq) {
+      const int qry = qw0 + 16 * tq + l16;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) dqa[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 2; ++ks) {
+        qf[tq][ks] = frag_global(q, row0, qry, T, ks, q4);
+        gf[tq][ks] = frag_global(g, row0, qry, T, ks, q4);
+      }
+      iq[tq] = 0.0f;
+      if (qry < T) {
+        const float d = den[row0 + qry];
+        iq[tq] = d != 0.0f ? 1.0f / d : 0.0f;
+      }
+    }
+    float cq[kQT] = {};  // c of the lane's queries (PASS 1)
+    if (PASS == 1) {
+#pragma unroll
+      for (int tq = 0; tq < kQT; ++tq) {
+        const int qry = qw0 + 16 * tq + l16;
+        if (qry < T) cq[tq] = cvec[row0 + qry];
+      }
+    }
+    f32x4 dqa[kQT][4];   // lane holds queries qw0 + 16 tq + 4 q4 + i at dim 16 nt + l16
+#pragma unroll
+    for (int tq = 0; tq < kQT; ++tq)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) dqa[tq][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int pass = 0; pass < 2; ++pass) {
+    {
       RowLoad rk, rv;
       fetch(0, rk, rv);
       stage(0, rk, rv);
-      if (qb >= 1) fetch(1, rk, rv);
+      if (nkb > 1) fetch(1, rk, rv);
       __syncthreads();
-      float cpart = 0.0f;
-      for (int kb = 0; kb <= qb; ++kb) {
+      float cpart[kQT] = {};
+      for (int kb = 0; kb < nkb; ++kb) {
         const int buf = kb & 1;
         const int k0 = kb * kBB;
-        // S^T and dP^T: key tiles kt (rows), this wave's 16 queries (columns)
-        f32x4 st[4], dpt[4];
+        const bool diag = k0 + kBB - 1 > qw0;  // some key of the block is above a query of the wave
+        // S^T and dP^T: key tiles kt (rows), query tile tq (columns); each row
+        // fragment read serves every query tile
+        f32x4 st[kQT][4], dpt[kQT][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = f32x4{0.f, 0.f, 0.f, 0.f};
+          bf16x8 ak[2], av[2];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            x = mfma16x16x32(frag(sh.k[buf], 16 * kt + l16, ks, q4), qf[ks], x);
-            y = mfma16x16x32(frag(sh.v[buf], 16 * kt + l16, ks, q4), gf[ks], y);
+            ak[ks] = frag(sh.k[buf], 16 * kt + l16, ks, q4);
+            av[ks] = frag(sh.v[buf], 16 * kt + l16, ks, q4);
           }
-          st[kt] = x;
-          dpt[kt] = y;
+#pragma unroll
+          for (int tq = 0; tq < kQT; ++tq) {
+            f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              x = mfma16x16x32(ak[ks], qf[tq][ks], x);
+              y = mfma16x16x32(av[ks], gf[tq][ks], y);
+            }
+            st[tq][kt] = x;
+            dpt[tq][kt] = y;
+          }
         }
-        const bool diag = kb == qb;
-        if (pass == 0) {
+        if (PASS == 0) {
           // c: sum over this lane's keys 16 kt + 4 q4 + i of P dP
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
+          for (int tq = 0; tq < kQT; ++tq) {
+            const int qry = qw0 + 16 * tq + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float s = st[kt][i];
-              float pd = s * s * iq * dpt[kt][i];
-              if (diag && k0 + 16 * kt + 4 * q4 + i > qry) pd = 0.0f;
-              cpart += pd;
+            for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float s = st[tq][kt][i];
+                float pd = s * s * iq[tq] * dpt[tq][kt][i];
+                if (diag && k0 + 16 * kt + 4 * q4 + i > qry) pd = 0.0f;
+                cpart[tq] += pd;
+              }
             }
           }
         } else {
-          // dS for keys 16 kt + 4 q4 + i: k-slot 4 (kt & 1) + i of pair kt >> 1
-          bf16x8 dh[2], dl[2];  // dS as hi + lo bf16 pieces
+          // per k-step: dS for keys 32 ks + 16 (j >> 2) + 4 q4 + (j & 3) as hi + lo
+          // bf16 pieces (k-slot j), then dQ += dS K over those 32 keys; each
+          // transposed fragment read serves every query tile
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            float ds[8];
+            bf16x8 dh[kQT], dl[kQT];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int kt = 2 * ks + (j >> 2);
-              const int i = j & 3;
-              const float s = st[kt][i];
-              ds[j] = 2.0f * s * (dpt[kt][i] - cq) * iq;
-              if (diag && k0 + 16 * kt + 4 * q4 + i > qry) ds[j] = 0.0f;
+            for (int tq = 0; tq < kQT; ++tq) {
+              const int qry = qw0 + 16 * tq + l16;
+              float ds[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int kt = 2 * ks + (j >> 2);
+                const int i = j & 3;
+                const float s = st[tq][kt][i];
+                ds[j] = 2.0f * s * (dpt[tq][kt][i] - cq[tq]) * iq[tq];
+                if (diag && k0 + 16 * kt + 4 * q4 + i > qry) ds[j] = 0.0f;
+              }
+              split2(ds, dh[tq], dl[tq]);
             }
-            split2(ds, dh[ks], dl[ks]);
-          }
-          // dQ += dS K over the block's 64 keys (two k-steps)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
               const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sh.kt[buf][16 * nt + l16][32 * ks + 8 * q4]);
-              dqa[nt] = mfma16x16x32(dh[ks], bk, dqa[nt]);
-              dqa[nt] = mfma16x16x32(dl[ks], bk, dqa[nt]);
+#pragma unroll
+              for (int tq = 0; tq < kQT; ++tq) {
+                dqa[tq][nt] = mfma16x16x32(dh[tq], bk, dqa[tq][nt]);
+                dqa[tq][nt] = mfma16x16x32(dl[tq], bk, dqa[tq][nt]);
+              }
             }
           }
         }
-        if (kb + 1 <= qb) {
+        if (kb + 1 < nkb) {
           stage(buf ^ 1, rk, rv);
-          if (kb + 2 <= qb) fetch(kb + 2, rk, rv);
+          if (kb + 2 < nkb) fetch(kb + 2, rk, rv);
         }
         __syncthreads();
       }
-      if (pass == 0) {
-        // the four lane quarters of query qry hold disjoint keys
-        cpart += __shfl_xor(cpart, 16, 64);
-        cpart += __shfl_xor(cpart, 32, 64);
-        cq = cpart;
-        if (q4 == 0 && qry < T) cvec[row0 + qry] = cq;
+      if (PASS == 0) {
+        // the four lane quarters of a query hold disjoint keys
+#pragma unroll
+        for (int tq = 0; tq < kQT; ++tq) {
+          float c = cpart[tq];
+          c += __shfl_xor(c, 16, 64);
+          c += __shfl_xor(c, 32, 64);
+          cq[tq] = c;
+          const int qry = qw0 + 16 * tq + l16;
+          if (q4 == 0 && qry < T) cvec[row0 + qry] = c;
+        }
       }
     }
 
+    if (PASS == 1) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+      for (int tq = 0; tq < kQT; ++tq)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qr = qw0 + 4 * q4 + i;
-        if (qr < T) Elem<Tout>::store(dq, (row0 + qr) * kBD + 16 * nt + l16, dqa[nt][i]);
-      }
+        for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int qr = qw0 + 16 * tq + 4 * q4 + i;
+            if (qr < T) Elem<Tout>::store(dq, (row0 + qr) * kBD + 16 * nt + l16, dqa[tq][nt][i]);
+          }
+        }
     }
   }  // rep
 }
 
 template <typename Tout>
 hipError_t launch_bwd(const QuadBwdArgs& a, float* cvec, hipStream_t st) {
-  const int nb = (a.T + kBB - 1) / kBB;
-  const dim3 grid((nb + 1) / 2, a.N);
-  // c comes out of the dQ kernel's first pass; the dK/dV kernel reads it
-  hipLaunchKernelGGL(quad_bwd_q_kernel<Tout>, grid, dim3(kBT), 0, st, static_cast<const uint16_t*>(a.q),
+  const int nqb = (a.T + kQB - 1) / kQB;
+  const int nkb = (a.T + kKB - 1) / kKB;
+  // c comes out of the dQ kernel's first pass; the second and the dK/dV kernel read it
+  const dim3 qgrid((nqb + 1) / 2, a.N);
+  hipLaunchKernelGGL((quad_bwd_q_kernel<0, Tout>), qgrid, dim3(kBT), 0, st, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const Tout*>(a.dout), a.den, cvec, static_cast<Tout*>(a.dq), a.T);
-  hipLaunchKernelGGL(quad_bwd_kv_kernel<Tout>, grid, dim3(kBT), 0, st, static_cast<const uint16_t*>(a.q),
+  hipLaunchKernelGGL((quad_bwd_q_kernel<1, Tout>), qgrid, dim3(kBT), 0, st, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<const Tout*>(a.dout), a.den, cvec, static_cast<Tout*>(a.dq), a.T);
+  hipLaunchKernelGGL(quad_bwd_kv_kernel<Tout>, dim3((nkb + 1) / 2, a.N), dim3(kBT), 0, st,
+                     static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const Tout*>(a.dout), cvec, a.den, static_cast<Tout*>(a.dk),
                      static_cast<Tout*>(a.dv), a.T);
