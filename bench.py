@@ -287,8 +287,10 @@ def bench_hybrid_decode(torch, K, S, steps=None):
         workload="hybrid_decode_4096", N=N, window=W, cache_size=lam, start_token=T0, steps=nsteps,
         step_ms=step_ms, steps_per_s=1e3 / step_ms, kernel_ms=span_ms,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
-                      frac=achieved / PEAK_HBM_GBS, traffic=None,
-                      kernel="hybrid decode step (score, reject, readout; one span)",
+                      frac=achieved / PEAK_HBM_GBS,
+                      traffic=measured_traffic("hybrid_decode.hip",
+                                               "hybrid_decode_step_hybrid_decode_4096_traffic.md"),
+                      kernel="hybrid decode step (state pass + mix; one span)",
                       bytes_per_launch=step_bytes),
     )
 
