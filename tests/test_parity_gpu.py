@@ -95,6 +95,19 @@ def test_prefill_bf16_d64(K, chunk, T):
     assert_close(host(o32), ro, RTOL_BF16, "o (f32 out)")
 
 
+@pytest.mark.parametrize("B,H,chunk,T", [(2, 10, 64, 150), (3, 8, 128, 260), (1, 17, 32, 97)])
+def test_prefill_bf16_d64_many_heads(K, B, H, chunk, T):
+    # more than 16 heads: the matrix path splits each head's features in 8
+    # slices of two tile columns instead of 16 slices of one
+    c = S.prefill_case("many", B, H, T, 64, 64, chunk, seed=40 + H)
+    o, HT, sT = K.prefill(dev(c.q, torch.bfloat16), dev(c.k, torch.bfloat16),
+                          dev(c.v, torch.bfloat16), chunk=chunk, return_state=True)
+    ro, rH, rs = O.prefill(c.q, c.k, c.v, chunk=128)
+    assert_close(host(o), ro, RTOL_BF16, "o")
+    assert_close(host(HT), rH, RTOL_BF16, "H_T")
+    assert_close(host(sT), rs, RTOL_BF16, "s_T")
+
+
 def test_prefill_resume_and_state_only(K):
     rng = np.random.default_rng(31)
     T1, T2, d = 130, 90, 32
