@@ -161,11 +161,12 @@ struct Slice {
 
 template <int S>
 struct StateLds {
-  float qs[kCS][kQS];                             // q rows (fp32)
-  float kt[kDim][kKS];                            // k transposed (fp32)
-  uint16_t vt[kDim][kCS + 8];                     // v transposed (bf16)
-  uint4 hs[2][Slice<S>::kPairs][4][64];           // G as bf16 B fragments, double buffer
-  uint4 ss[2][Slice<S>::kPairs][4];               // s as bf16 per pair and lane quarter
+  // staged sub-chunks, double buffered (the next is staged during this one)
+  float qs[2][kCS][kQS];                          // q rows (fp32)
+  float kt[2][kDim][kKS];                         // k transposed (fp32)
+  uint16_t vt[2][kDim][kCS + 8];                  // v transposed (bf16)
+  uint4 hs[Slice<S>::kPairs][4][64];              // G at the chunk start, bf16 B fragments
+  uint4 ss[Slice<S>::kPairs][4];                  // s as bf16 per pair and lane quarter
   f32x4 xs[kRW][5][64];                           // readout trade: one token tile's accumulators
 };
 
@@ -199,7 +200,7 @@ __device__ __forceinline__ Prefetch prefetch(const uint16_t* __restrict__ q, con
 // Staging: thread (token t, 8-dim group grp) writes q as fp32 rows, k as
 // fp32 columns and v as bf16 columns.
 template <int S>
-__device__ __forceinline__ void stage(StateLds<S>& sh, const Prefetch& p, int t, int grp) {
+__device__ __forceinline__ void stage(StateLds<S>& sh, const Prefetch& p, int t, int grp, int buf) {
   const uint4 z = make_uint4(0, 0, 0, 0);
   const uint4 pq = p.ok ? p.q : z, pk = p.ok ? p.k : z, pv = p.ok ? p.v : z;
   const uint32_t qw[4] = {pq.x, pq.y, pq.z, pq.w};
@@ -208,14 +209,14 @@ __device__ __forceinline__ void stage(StateLds<S>& sh, const Prefetch& p, int t,
   const int d0 = 8 * grp;
   const float4 lo = make_float4(bf16f(qw[0] & 0xFFFF), bf16f(qw[0] >> 16), bf16f(qw[1] & 0xFFFF), bf16f(qw[1] >> 16));
   const float4 hi = make_float4(bf16f(qw[2] & 0xFFFF), bf16f(qw[2] >> 16), bf16f(qw[3] & 0xFFFF), bf16f(qw[3] >> 16));
-  *reinterpret_cast<float4*>(&sh.qs[t][d0]) = lo;
-  *reinterpret_cast<float4*>(&sh.qs[t][d0 + 4]) = hi;
+  *reinterpret_cast<float4*>(&sh.qs[buf][t][d0]) = lo;
+  *reinterpret_cast<float4*>(&sh.qs[buf][t][d0 + 4]) = hi;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    sh.kt[d0 + 2 * e][t] = bf16f(kw[e] & 0xFFFF);
-    sh.kt[d0 + 2 * e + 1][t] = bf16f(kw[e] >> 16);
-    sh.vt[d0 + 2 * e][t] = (uint16_t)(vw[e] & 0xFFFF);
-    sh.vt[d0 + 2 * e + 1][t] = (uint16_t)(vw[e] >> 16);
+    sh.kt[buf][d0 + 2 * e][t] = bf16f(kw[e] & 0xFFFF);
+    sh.kt[buf][d0 + 2 * e + 1][t] = bf16f(kw[e] >> 16);
+    sh.vt[buf][d0 + 2 * e][t] = (uint16_t)(vw[e] & 0xFFFF);
+    sh.vt[buf][d0 + 2 * e + 1][t] = (uint16_t)(vw[e] >> 16);
   }
 }
 
@@ -273,7 +274,7 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
 
-  auto publish = [&](int buf) {
+  auto publish = [&]() {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int pr = (U0 + u) >> 1;
@@ -283,17 +284,17 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
         bf16x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (__bf16)h[u][nt][i];
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&sh.hs[buf][pr][nt][lane]) + 8 * half) = x;
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&sh.hs[pr][nt][lane]) + 8 * half) = x;
       }
       if (l16 == 0) {
         bf16x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (__bf16)h[u][4][i];
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&sh.ss[buf][pr][q4]) + 8 * half) = x;
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&sh.ss[pr][q4]) + 8 * half) = x;
       }
     }
   };
-  publish(1);  // the state at the start of chunk 0
+  publish();  // the state at the start of chunk 0
 
   // k_b sources: lane j' < kJ of each row holds k[token][16 Y + j0 + j']; the
   // other lanes keep whatever they held (only these lanes are broadcast)
@@ -303,19 +304,20 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
 #pragma unroll
     for (int i = 0; i < 8; ++i) kr[b][i] = 0.0f;
 
+  lds_barrier();  // (B0) initial state published, first sub-chunk staged
   for (int st = 0; st < nsteps; ++st) {
-    lds_barrier();  // (B1) sub-chunk staged by the readout waves
+    const int buf = st & 1;
 #pragma unroll
     for (int ks = 0; ks < CS / 32; ++ks) {
       const int t0 = ks * 32 + 8 * q4;
       bf16x8 vb[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = *reinterpret_cast<const bf16x8*>(&sh.vt[16 * nt + l16][t0]);
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = *reinterpret_cast<const bf16x8*>(&sh.vt[buf][16 * nt + l16][t0]);
       float ka[4][8];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (SL::upd_uses_x(W, b)) {
-          const float4* p = reinterpret_cast<const float4*>(&sh.kt[16 * b + l16][t0]);
+          const float4* p = reinterpret_cast<const float4*>(&sh.kt[buf][16 * b + l16][t0]);
           const float4 x0 = p[0], x1 = p[1];
           ka[b][0] = x0.x; ka[b][1] = x0.y; ka[b][2] = x0.z; ka[b][3] = x0.w;
           ka[b][4] = x1.x; ka[b][5] = x1.y; ka[b][6] = x1.z; ka[b][7] = x1.w;
@@ -325,7 +327,7 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           if (SL::upd_uses_y(W, b)) {
-            const float4* p = reinterpret_cast<const float4*>(&sh.kt[16 * b + cx.j0 + l16][t0]);
+            const float4* p = reinterpret_cast<const float4*>(&sh.kt[buf][16 * b + cx.j0 + l16][t0]);
             const float4 x0 = p[0], x1 = p[1];
             kr[b][0] = x0.x; kr[b][1] = x0.y; kr[b][2] = x0.z; kr[b][3] = x0.w;
             kr[b][4] = x1.x; kr[b][5] = x1.y; kr[b][6] = x1.z; kr[b][7] = x1.w;
@@ -346,8 +348,9 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
         h[u][4] = mfma(A, ones, h[u][4]);
       }
     }
-    if (st % SUB == SUB - 1) publish((st / SUB) & 1);
-    lds_barrier();  // (B2) sub-chunk consumed
+    lds_barrier();  // (B2) sub-chunk consumed, readouts done
+    if (st % SUB == SUB - 1) publish();
+    lds_barrier();  // (B1) state published, next sub-chunk staged
   }
 
   // final state in the ABI layout (sqrt(2) on the off-diagonal features);
@@ -424,34 +427,40 @@ __device__ __forceinline__ void readout_wave(StateLds<S>& sh, const StateCtx& cx
   };
 
   // The readout waves stage the sub-chunks for the whole work-group (wave W:
-  // 8-dim groups 2W and 2W + 1 of every token) and keep the loads of the next
-  // two in flight, so that the global load latency spans two sub-steps.
+  // 8-dim groups 2W and 2W + 1 of every token): the next sub-chunk into the
+  // other buffer while this one is computed, with its loads issued a whole
+  // sub-step earlier.
   auto pre = [&](int st, Prefetch (&p)[2]) {
     const int n0 = (st / SUB) * C + (st % SUB) * CS;
 #pragma unroll
     for (int g = 0; g < 2; ++g) p[g] = prefetch(cx.q, cx.k, cx.v, row0, n0, cx.T, lane, 2 * W + g);
   };
-  Prefetch pa[2], pb[2];
-  pre(0, pa);
-  pre(1, pb);
-
-  auto step = [&](int st, Prefetch (&pf)[2]) {
+  auto stage2 = [&](const Prefetch (&p)[2], int buf) {
     if (lane < CS) {
-      stage<S>(sh, pf[0], lane, 2 * W);
-      stage<S>(sh, pf[1], lane, 2 * W + 1);
+      stage<S>(sh, p[0], lane, 2 * W, buf);
+      stage<S>(sh, p[1], lane, 2 * W + 1, buf);
     }
-    if (active && st > 0) flush(st - 1);
-    lds_barrier();  // (B1)
-    pre(st + 2, pf);  // past the end: clamped reads, never staged
+  };
+  Prefetch pf[2];
+  pre(0, pf);
+  stage2(pf, 0);
+  pre(1, pf);  // past the end: clamped reads, never staged
+  lds_barrier();  // (B0)
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nsteps) {
+      stage2(pf, buf ^ 1);
+      pre(st + 2, pf);
+    }
     if (active) {
-      const int pb = ((st / SUB) + 1) & 1;  // the state at the chunk start
       // q factors of this lane's token in each of the two token tiles:
       // qa[tt][X] = q[16 X + 4 q4 + 0..3], qb[tt][u] = w_u q[16 Y_u + j_u]
       float qa[2][4][4];
       float qb[2][2 * NP];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const float* qrow = sh.qs[32 * TP + 16 * tt + l16];
+        const float* qrow = sh.qs[buf][32 * TP + 16 * tt + l16];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           if (SL::rd_uses_x(HF, b)) {
@@ -477,9 +486,9 @@ __device__ __forceinline__ void readout_wave(StateLds<S>& sh, const StateCtx& cx
         const int pr = P0 + p;
         bf16x8 B[5];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) B[nt] = __builtin_bit_cast(bf16x8, sh.hs[pb][pr][nt][lane]);
+        for (int nt = 0; nt < 4; ++nt) B[nt] = __builtin_bit_cast(bf16x8, sh.hs[pr][nt][lane]);
         // s of this lane's k-slots in column 0, zero elsewhere
-        const uint4 sw = sh.ss[pb][pr][q4];
+        const uint4 sw = sh.ss[pr][q4];
         B[4] = __builtin_bit_cast(bf16x8, l16 == 0 ? sw : make_uint4(0, 0, 0, 0));
         const int X0 = SL::X(2 * pr);
         const int X1 = SL::X(2 * pr + 1);
@@ -505,12 +514,9 @@ __device__ __forceinline__ void readout_wave(StateLds<S>& sh, const StateCtx& cx
       }
     }
     lds_barrier();  // (B2)
-  };
-  for (int st = 0; st < nsteps; st += 2) {
-    step(st, pa);
-    if (st + 1 < nsteps) step(st + 1, pb);
+    if (active) flush(st);
+    lds_barrier();  // (B1)
   }
-  if (active && nsteps > 0) flush(nsteps - 1);
 }
 
 // C: the chunk (intra-chunk region of the output); the state kernel stages it
