@@ -92,6 +92,86 @@ def _safe_div(num: np.ndarray, den: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Multi-factor PSD lifts (KATA §2.3, "Variantes": KATA-Mg with several PSD
+# factors and KATA-Sigma-g with summed PSD factors). The page names the two
+# variants and their purpose (trading state size against packing) but not how
+# the factors are formed. Reading taken here: the d dimensions of q and k are
+# split into g equal factors x_1 .. x_g of p = d / g dimensions each, and
+#   Mg:  phi(x) = [psi(x_1), ..., psi(x_g)], the rank-one lifts concatenated
+#        (g p(p+1)/2 features), so phi(q).phi(k) = sum_i (q_i . k_i)^2;
+#   Sg:  phi(x) = psi-vectorisation of sum_i x_i x_i^T, the factors' outer
+#        products summed before the lift (p(p+1)/2 features), so
+#        phi(q).phi(k) = <sum_i q_i q_i^T, sum_j k_j k_j^T>_F
+#                      = sum_{i,j} (q_i . k_j)^2.
+# With g = 1 both are the rank-one lift above.
+# ----------------------------------------------------------------------------
+
+FACTOR_KINDS = ("concat", "sum")
+
+
+def _factors(x: np.ndarray, g: int):
+    d = x.shape[-1]
+    if g < 1 or d % g:
+        raise ValueError(f"g = {g} must divide d = {d}")
+    p = d // g
+    return [x[..., i * p:(i + 1) * p] for i in range(g)]
+
+
+def phi_factors(x, g: int, kind: str) -> np.ndarray:
+    """The feature vector of the KATA-Mg ("concat") or KATA-Sigma-g ("sum")
+    variant; x: [..., d] -> [..., g p(p+1)/2] or [..., p(p+1)/2]."""
+    x = np.asarray(x, dtype=np.float64)
+    parts = _factors(x, g)
+    if kind == "concat":
+        return np.concatenate([phi(u) for u in parts], axis=-1)
+    if kind != "sum":
+        raise ValueError(kind)
+    p = parts[0].shape[-1]
+    M = sum(u[..., :, None] * u[..., None, :] for u in parts)      # sum_i x_i x_i^T
+    i, j = np.triu_indices(p)
+    return np.where(i == j, 1.0, SQRT2) * M[..., i, j]
+
+
+def factor_weights(q, k, g: int, kind: str) -> np.ndarray:
+    """Closed-form kernel between every query and key row: W[t, s] =
+    sum_i (q_t,i . k_s,i)^2 (concat) or sum_{i,j} (q_t,i . k_s,j)^2 (sum)."""
+    qs, ks = _factors(np.asarray(q, np.float64), g), _factors(np.asarray(k, np.float64), g)
+    if kind == "concat":
+        return sum((a @ b.T) ** 2 for a, b in zip(qs, ks))
+    if kind != "sum":
+        raise ValueError(kind)
+    return sum((a @ b.T) ** 2 for a in qs for b in ks)
+
+
+def prefill_factors_bruteforce(q, k, v, g: int, kind: str, eps: float = 0.0, return_parts: bool = False):
+    """Causal attention with the variant's closed-form weights, normalised
+    over i <= t (the O(T^2) definition, as prefill_bruteforce for g = 1)."""
+    W = np.tril(factor_weights(q, k, g, kind))
+    v = np.asarray(v, np.float64)
+    num = W @ v
+    den = W.sum(axis=1) + eps
+    o = _safe_div(num, den)
+    return (o, num, den) if return_parts else o
+
+
+def prefill_factors_recurrent(q, k, v, g: int, kind: str, eps: float = 0.0):
+    """The same outputs through the variant's fixed-size state:
+    H += phi(k_t) v_t^T, s += phi(k_t), o_t = phi(q_t)^T H / (phi(q_t)^T s + eps).
+    Returns o [T, dv], H [D_g, dv], s [D_g]."""
+    fq, fk = phi_factors(q, g, kind), phi_factors(k, g, kind)
+    v = np.asarray(v, np.float64)
+    H = np.zeros((fk.shape[1], v.shape[1]))
+    s = np.zeros(fk.shape[1])
+    o = np.zeros_like(v)
+    for t in range(v.shape[0]):
+        H += np.outer(fk[t], v[t])
+        s += fk[t]
+        den = fq[t] @ s + eps
+        o[t] = fq[t] @ H / den if den != 0 else 0.0
+    return o, H, s
+
+
+# ----------------------------------------------------------------------------
 # Prefill: three forms of the same result (one (b, h) head; q,k [T,d], v [T,dv])
 # ----------------------------------------------------------------------------
 

@@ -135,3 +135,51 @@ def test_hybrid_pin_catches_fold_of_kept_pairs(monkeypatch):
     monkeypatch.setattr(K, "select_topk", select_complement)
     with pytest.raises(AssertionError):
         TH.test_refresh_chain_against_token_by_token_enumeration(3, 16, 4, 8)
+
+
+# ---- multi-factor lifts (KATA-Mg / KATA-Sigma-g)
+
+from tests import test_oracle_factors as TF  # noqa: E402
+
+_real_factor_weights = K.factor_weights
+_real_phi_factors = K.phi_factors
+
+
+def _weights_no_cross_terms(q, k, g, kind):
+    return _real_factor_weights(q, k, g, "concat")  # planted: Sigma-g loses q_i . k_j, i != j
+
+
+def _weights_square_of_sum(q, k, g, kind):
+    if kind == "concat":  # planted: (sum_i q_i . k_i)^2, the rank-one kernel again
+        qs, ks = K._factors(np.asarray(q, np.float64), g), K._factors(np.asarray(k, np.float64), g)
+        return sum(a @ b.T for a, b in zip(qs, ks)) ** 2
+    return _real_factor_weights(q, k, g, kind)
+
+
+def _phi_factors_no_sqrt2(x, g, kind):
+    if kind != "sum":
+        return _real_phi_factors(x, g, kind)
+    parts = K._factors(np.asarray(x, np.float64), g)
+    p = parts[0].shape[-1]
+    M = sum(u[..., :, None] * u[..., None, :] for u in parts)
+    i, j = np.triu_indices(p)
+    return M[..., i, j]  # planted: off-diagonal sqrt(2) dropped
+
+
+@pytest.mark.parametrize("name,bad", [("factor_weights", _weights_no_cross_terms),
+                                      ("factor_weights", _weights_square_of_sum),
+                                      ("phi_factors", _phi_factors_no_sqrt2)],
+                         ids=["sum_without_cross_terms", "concat_as_square_of_sum", "sum_lift_without_sqrt2"])
+def test_factor_pins_catch_planted_mistake(monkeypatch, name, bad):
+    monkeypatch.setattr(O, name, bad)
+    monkeypatch.setattr(K, name, bad)
+    pins = [TF.test_worked_integer_example,
+            functools.partial(TF.test_state_form_equals_closed_form, 2, "sum"),
+            functools.partial(TF.test_state_form_equals_closed_form, 2, "concat")]
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"no pin caught the planted mistake in {name}"
