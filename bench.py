@@ -7,8 +7,9 @@ Main line: bf16 prefill of 4 x 8 heads x 4096 tokens, d = 64 (D = 2080),
 chunk 64 — one step is one kla_prefill call (lift, intra-chunk term,
 cross-chunk state readout and update, combine). Secondary lines (in
 "secondary"): the 16-head x 65536-token long-context prefill, the main
-workload again through the quadratic (no state) form, its gradients (the
-quadratic-form backward), the decode + self-recall selection loop (4096
+workload again through the quadratic (no state) form, and with the
+multi-factor lifts KATA-M2 (two concatenated factor lifts) and KATA-Sigma-2
+(two summed factors), its gradients (the quadratic-form backward), the decode + self-recall selection loop (4096
 head-states, 128 steps), the hybrid prefill (2 x 16 x 16384) and the
 token-by-token hybrid decode (4096 head-states, 128 steps after a 2048-token
 fill). Inputs are seeded synthetic tensors resident in HBM before timing.
@@ -130,22 +131,27 @@ def bench_prefill(torch, K, S, name, steps, warmup):
     )
 
 
-def bench_prefill_quadratic(torch, K, S, name, steps, warmup):
-    """The same workload through the quadratic (no state) form."""
+def bench_prefill_quadratic(torch, K, S, name, steps, warmup, factors=1, factor_kind="concat"):
+    """The same workload through the quadratic (no state) form; factors > 1
+    selects a multi-factor lift (KATA-Mg "concat", KATA-Sigma-g "sum")."""
     cfg = S.CONFIGS[name]
     c = S.prefill_case(name, cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
                        cfg["seed"])
     q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (c.q, c.k, c.v))
     del c
     o = torch.empty_like(v)
-    step_ms, kern_ms, per_step = timed_calls(torch, K, lambda: K.prefill_quadratic(q, k, v, out=o),
-                                             steps, warmup)
+    step_ms, kern_ms, per_step = timed_calls(
+        torch, K, lambda: K.prefill_quadratic(q, k, v, out=o, factors=factors, factor_kind=factor_kind),
+        steps, warmup)
     B, H, T, d, dv = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
-    # causal pairs x (q.k: 2 d_qk flop, weight times [v | 1]: 2 (d_v + 1) flop)
-    kern_flops = B * H * T * (T + 1) / 2 * 2.0 * (d + dv + 1)
+    # causal pairs x (the factor inner products: 2 d_qk flop, times g for the
+    # g^2 crossed products of Sigma-g; weight times [v | 1]: 2 (d_v + 1) flop)
+    score = d * (factors if factor_kind == "sum" else 1)
+    kern_flops = B * H * T * (T + 1) / 2 * 2.0 * (score + dv + 1)
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+    variant = "" if factors == 1 else f", KATA-{'M' if factor_kind == 'concat' else 'Sigma-'}{factors}"
     return dict(
-        workload=name + " (quadratic form)", B=B, H=H, T=T, d_qk=d, d_v=dv, step_ms=step_ms,
+        workload=name + f" (quadratic form{variant})", B=B, H=H, T=T, d_qk=d, d_v=dv, step_ms=step_ms,
         tokens_per_s=B * T / (step_ms * 1e-3),
         roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=achieved / PEAK_BF16_TFLOPS, kernel_ms=kern_ms, traffic=None,
@@ -335,6 +341,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
     ap.add_argument("--only", choices=["prefill_1x16x65536", "prefill_4x8x4096_quadratic",
+                                       "prefill_4x8x4096_m2", "prefill_4x8x4096_sigma2",
                                        "prefill_4x8x4096_backward", "decode_sre_4096x128",
                                        "hybrid_2x16x16384", "hybrid_decode_4096"],
                     help="run just this secondary workload and print its line (for profiling)")
@@ -365,6 +372,9 @@ def main():
             r = bench_prefill(torch, K, S, args.only, args.steps, args.warmup)
         elif args.only == "prefill_4x8x4096_quadratic":
             r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
+        elif args.only in ("prefill_4x8x4096_m2", "prefill_4x8x4096_sigma2"):
+            kind = "concat" if args.only.endswith("m2") else "sum"
+            r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup, 2, kind)
         elif args.only == "prefill_4x8x4096_backward":
             r = bench_prefill_backward(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
         elif args.only == "decode_sre_4096x128":
@@ -386,6 +396,9 @@ def main():
         secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1))
         log("[bench] secondary: prefill_4x8x4096 in the quadratic form")
         secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup))
+        for g, kind in ((2, "concat"), (2, "sum")):
+            log(f"[bench] secondary: prefill_4x8x4096 in the quadratic form, {kind} of {g} factors")
+            secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup, g, kind))
         log("[bench] secondary: prefill_4x8x4096 backward")
         secondary.append(bench_prefill_backward(torch, K, S, name, args.steps, args.warmup))
         log("[bench] secondary: decode_sre_4096x128")

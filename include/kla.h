@@ -73,7 +73,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 2
+#define KLA_ABI_VERSION 3
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -143,6 +143,34 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
  * ------------------------------------------------------------------------ */
 KLA_API kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const void* k,
                                    const void* v, void* o, float* den, kla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kla_prefill_quadratic_factors - kla_prefill_quadratic with a multi-factor
+ * PSD lift (KATA §2.3, "Variantes": KATA-Mg, several PSD factors, and
+ * KATA-Sigma-g, summed PSD factors). The page names the variants but not how
+ * the factors are formed; this library reads them as g equal slices of the
+ * d = 64 dimensions, q = (q_1, ..., q_g), k = (k_1, ..., k_g):
+ *   kind KLA_FACTORS_CONCAT (KATA-Mg): the factors' rank-one lifts are
+ *       concatenated (g p(p+1)/2 features, p = 64 / g), so the weight is
+ *       w(q, k) = sum_i (q_i . k_i)^2;
+ *   kind KLA_FACTORS_SUM (KATA-Sigma-g): the lift of sum_i x_i x_i^T
+ *       (p(p+1)/2 features), so w(q, k) = sum_{i,j} (q_i . k_j)^2;
+ * and o_t = sum_{i<=t} w(q_t, k_i) v_i / (sum_{i<=t} w(q_t, k_i) + eps).
+ * factors = 1 is the rank-one lift of kla_prefill_quadratic (either kind).
+ *
+ *   kind    : KLA_FACTORS_CONCAT or KLA_FACTORS_SUM.
+ *   factors : 1, 2 or 4.
+ *   q, k, v, o, den : as for kla_prefill_quadratic (den holds the variant's
+ *             denominators).
+ * Supported: d_qk = d_v = 64, in_dtype bf16, out_dtype bf16 or float32;
+ * another kind or factor count returns KLA_ERR_INVALID_ARGUMENT, other shapes
+ * KLA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+#define KLA_FACTORS_CONCAT 0
+#define KLA_FACTORS_SUM 1
+KLA_API kla_status_t kla_prefill_quadratic_factors(const kla_shape_t* shp, int kind, int factors,
+                                                   const void* q, const void* k, const void* v, void* o,
+                                                   float* den, kla_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * kla_prefill_quadratic_backward - gradients of the causal prefill (the

@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(HERE, "libkla.so")
 
 KLA_OK, KLA_ERR_INVALID_ARGUMENT, KLA_ERR_UNSUPPORTED, KLA_ERR_WORKSPACE, KLA_ERR_HIP = range(5)
 KLA_F32, KLA_BF16 = 0, 1
+KLA_FACTORS_CONCAT, KLA_FACTORS_SUM = 0, 1
 
 EXPORTS = (
     "kla_abi_version", "kla_phi_dim", "kla_status_string", "kla_last_error",
     "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill", "kla_prefill_quadratic",
-    "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
+    "kla_prefill_quadratic_factors", "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill",
@@ -89,6 +90,7 @@ def load_library(path: str = LIB_PATH):
         "kla_prefill_workspace_size": (i, [shp, i, i, szp]),
         "kla_prefill": (i, [shp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_prefill_quadratic": (i, [shp, vp, vp, vp, vp, vp, vp]),
+        "kla_prefill_quadratic_factors": (i, [shp, i, i, vp, vp, vp, vp, vp, vp]),
         "kla_prefill_quadratic_backward_workspace_size": (i, [shp, szp]),
         "kla_prefill_quadratic_backward": (i, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
@@ -221,11 +223,18 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     return (o, HT, sT) if return_state else o
 
 
-def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None, return_den: bool = False):
+FACTOR_KINDS = {"concat": 0, "sum": 1}
+
+
+def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None, return_den: bool = False,
+                      factors: int = 1, factor_kind: str = "concat"):
     """Causal prefill in the quadratic form (no state): q, k, v [B, H, T, 64]
     bfloat16. Returns o [B, H, T, 64] (bfloat16, or ``out_dtype``), and with
     ``return_den`` also the row denominators den [B, H, T] float32 (for
-    prefill_quadratic_backward)."""
+    prefill_quadratic_backward). ``factors`` > 1 selects a multi-factor lift
+    (kla_prefill_quadratic_factors): ``factor_kind`` "concat" (KATA-Mg,
+    weights sum_i (q_i.k_i)^2) or "sum" (KATA-Sigma-g, sum_{i,j} (q_i.k_j)^2)
+    over ``factors`` equal slices of the 64 dimensions."""
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
@@ -246,8 +255,15 @@ def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None, retur
     else:
         o = torch.empty((B, Hh, T, dv), dtype=_torch_dtype(ocode), device=q.device)
     den = torch.empty((B, Hh, T), dtype=torch.float32, device=q.device) if return_den else None
-    check(lib.kla_prefill_quadratic(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
-                                    _stream(q.device)))
+    if factors == 1 and factor_kind == "concat":
+        check(lib.kla_prefill_quadratic(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                                        _stream(q.device)))
+    else:
+        if factor_kind not in FACTOR_KINDS:
+            raise ValueError(f"factor_kind must be one of {sorted(FACTOR_KINDS)}")
+        check(lib.kla_prefill_quadratic_factors(ctypes.byref(shp), FACTOR_KINDS[factor_kind], int(factors),
+                                                _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den),
+                                                _stream(q.device)))
     return (o, den) if return_den else o
 
 

@@ -334,6 +334,29 @@ kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const 
   return hip_status(kla::prefill_quad_launch(a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+kla_status_t kla_prefill_quadratic_factors(const kla_shape_t* shp, int kind, int factors, const void* q,
+                                           const void* k, const void* v, void* o, float* den, kla_stream_t stream) {
+  const char* fn = "kla_prefill_quadratic_factors";
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  if (!q || !k || !v || !o) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v and o are required", fn);
+  if (kind != KLA_FACTORS_CONCAT && kind != KLA_FACTORS_SUM)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: kind %d is neither KLA_FACTORS_CONCAT nor KLA_FACTORS_SUM", fn, kind);
+  if (factors != 1 && factors != 2 && factors != 4)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: factors = %d (1, 2 or 4 supported)", fn, factors);
+  kla::PrefillArgs a = make_prefill(shp, 64);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.den = den;
+  a.factor_kind = kind;
+  a.factors = factors;
+  if (!kla::prefill_quad_supported(a))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: needs d_qk = d_v = 64 and bf16 inputs", fn);
+  return hip_status(kla::prefill_quad_launch(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 kla_status_t kla_prefill_quadratic_backward_workspace_size(const kla_shape_t* shp, size_t* bytes) {
   const char* fn = "kla_prefill_quadratic_backward_workspace_size";
   if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);

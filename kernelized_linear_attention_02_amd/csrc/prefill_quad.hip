@@ -27,6 +27,15 @@
 // Each K and V fragment read from LDS serves both query tiles of the wave.
 // On request the row denominators den_t + eps are stored as well (float32),
 // for the backward.
+//
+// Multi-factor variants (KATA §2.3, "Variantes"; the reading: the 64
+// dimensions split into G equal factors). KATA-Mg concatenates the factors'
+// rank-one lifts, so the weight is sum_i (q_i . k_i)^2; KATA-Sigma-g lifts the
+// summed outer products, so it is sum_{i,j} (q_i . k_j)^2. Only the weights
+// change: for G = 2 the two 32-dimension k-steps of the score product are the
+// factors (their products are kept apart, and Sigma-2 adds the two crossed
+// ones); for G = 4 the scores of each factor pair come from
+// mfma_f32_16x16x16_bf16, whose k-range is one 16-dimension factor.
 #include <algorithm>
 #include <type_traits>
 
@@ -57,6 +66,82 @@ struct QuadLds {
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// 16x16x16: lane (l16, q4) holds k-values 4 q4 .. 4 q4 + 3 of its row (A) or column (B)
+__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 sq(const f32x4& x) { return x * x; }
+
+// Factor structure of the weights: KIND 0 concatenated lifts (KATA-Mg), 1
+// summed lifts (KATA-Sigma-g); G factors (G = 1: the rank-one lift).
+template <int KIND, int G>
+struct Factors {
+  static_assert(G == 1 || G == 2 || G == 4, "factors");
+  // query operands of one 16-query tile: G <= 2: [k-step] bf16x8; G = 4: [factor] 4 x bf16
+  struct Q {
+    bf16x8 f[2];
+    s16x4 h[4];
+  };
+  static __device__ __forceinline__ Q load_q(const uint16_t* __restrict__ row, bool ok, int q4) {
+    Q r;
+    if constexpr (G == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint2 u = make_uint2(0, 0);
+        if (ok) u = *reinterpret_cast<const uint2*>(row + 16 * i + 4 * q4);
+        r.h[i] = __builtin_bit_cast(s16x4, u);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (ok) u = *reinterpret_cast<const uint4*>(row + 32 * ks + 8 * q4);
+        r.f[ks] = __builtin_bit_cast(bf16x8, u);
+      }
+    }
+    return r;
+  }
+  // weights of keys 16 kt + 4 q4 + i (rows of S^T) against query l16; krow is
+  // key row 16 kt + l16 in LDS
+  static __device__ __forceinline__ void weights(const uint16_t* krow, int q4, const Q (&qf)[2], f32x4 (&w)[2]) {
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (G == 4) {
+      s16x4 a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const s16x4*>(krow + 16 * j + 4 * q4);
+#pragma unroll
+      for (int tq = 0; tq < 2; ++tq) {
+        f32x4 acc = z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (KIND == 0 && i != j) continue;
+            acc += sq(mfma16(a[j], qf[tq].h[i], z));
+          }
+        }
+        w[tq] = acc;
+      }
+    } else {
+      bf16x8 a[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks + 8 * q4);
+#pragma unroll
+      for (int tq = 0; tq < 2; ++tq) {
+        if constexpr (G == 1) {
+          w[tq] = sq(mfma(a[1], qf[tq].f[1], mfma(a[0], qf[tq].f[0], z)));
+        } else {
+          f32x4 acc = sq(mfma(a[0], qf[tq].f[0], z)) + sq(mfma(a[1], qf[tq].f[1], z));
+          if (KIND == 1) acc += sq(mfma(a[1], qf[tq].f[0], z)) + sq(mfma(a[0], qf[tq].f[1], z));
+          w[tq] = acc;
+        }
+      }
+    }
+  }
+};
 
 // One thread's share of a key block: key tid % kBK, dims kDPT g .. kDPT g + kDPT - 1
 // of k and v with g = tid / kBK.
@@ -94,7 +179,7 @@ __device__ __forceinline__ void stage_kv(QuadLds& sh, int buf, const KVLoad& r, 
   }
 }
 
-template <typename Tout>
+template <typename Tout, int KIND, int G>
 __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
@@ -117,17 +202,13 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
     const int q_last = min(T, (qb + 1) * kBQ) - 1;  // the block's last query
     const int nkb = q_last / kBK + 1;               // key blocks with keys <= q_last
 
-    // Q as the B operand of S^T = K Q^T: [tile][k-step], dims 32 ks + 8 q4 + j of query l16
-    bf16x8 qf[2][2];
+    // Q as the B operand of S^T = K Q^T (per query tile)
+    using F = Factors<KIND, G>;
+    typename F::Q qf[2];
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
       const int t = qw0 + 16 * tq + l16;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (t < T) u = *reinterpret_cast<const uint4*>(q + (row0 + t) * kQD + 32 * ks + 8 * q4);
-        qf[tq][ks] = __builtin_bit_cast(bf16x8, u);
-      }
+      qf[tq] = F::load_q(q + (row0 + min(t, T - 1)) * kQD, t < T, q4);
     }
 
     const int skey = tid % kBK;  // staging role
@@ -156,22 +237,11 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
       constexpr bool MASKED = decltype(masked_c)::value;
       const int buf = kb & 1;
       const int k0 = kb * kBK;
-      // S^T for kBK / 16 key tiles x 2 query tiles
+      // weights (squared scores, summed over factor pairs) for kBK / 16 key
+      // tiles x 2 query tiles
       f32x4 s[kBK / 16][2];
 #pragma unroll
-      for (int kt = 0; kt < kBK / 16; ++kt) {
-        bf16x8 a[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          a[ks] = *reinterpret_cast<const bf16x8*>(&sh.k[buf][16 * kt + l16][32 * ks + 8 * q4]);
-#pragma unroll
-        for (int tq = 0; tq < 2; ++tq) {
-          f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-          c = mfma(a[0], qf[tq][0], c);
-          c = mfma(a[1], qf[tq][1], c);
-          s[kt][tq] = c;
-        }
-      }
+      for (int kt = 0; kt < kBK / 16; ++kt) F::weights(&sh.k[buf][16 * kt + l16][0], q4, qf, s[kt]);
       // P = S^2 as the bf16 B operands of O^T = V^T P^T
       bf16x8 pb[kBK / 32][2];  // [key pair][query tile]
 #pragma unroll
@@ -181,7 +251,7 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
         for (int kt = 0; kt < kBK / 16; ++kt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float p = s[kt][tq][i] * s[kt][tq][i];
+            float p = s[kt][tq][i];
             if (MASKED && k0 + 16 * kt + 4 * q4 + i > t) p = 0.0f;
             dsv[tq] += p;
             pb[kt >> 1][tq][4 * (kt & 1) + i] = (__bf16)p;
@@ -240,23 +310,39 @@ __global__ __launch_bounds__(kQT, 1) void prefill_quad_kernel(const uint16_t* __
   }  // rep
 }
 
+template <int KIND, int G>
+void launch_quad(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  if (a.out_bf16)
+    hipLaunchKernelGGL((prefill_quad_kernel<uint16_t, KIND, G>), grid, dim3(kQT), 0, st,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.den, a.T, a.eps);
+  else
+    hipLaunchKernelGGL((prefill_quad_kernel<float, KIND, G>), grid, dim3(kQT), 0, st,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<float*>(a.o), a.den, a.T, a.eps);
+}
+
 }  // namespace
 
-bool prefill_quad_supported(const PrefillArgs& a) { return a.in_bf16 && a.dqk == kQD && a.dv == kQD; }
+bool prefill_quad_supported(const PrefillArgs& a) {
+  return a.in_bf16 && a.dqk == kQD && a.dv == kQD && (a.factor_kind == 0 || a.factor_kind == 1) &&
+         (a.factors == 1 || a.factors == 2 || a.factors == 4);
+}
 
 hipError_t prefill_quad_launch(const PrefillArgs& a, hipStream_t st) {
   if (!prefill_quad_supported(a) || a.T < 1 || !a.o) return hipErrorInvalidValue;
   const int nqb = (a.T + kBQ - 1) / kBQ;
   const dim3 grid((nqb + 1) / 2, a.N);
   prof_begin(st);
-  if (a.out_bf16)
-    hipLaunchKernelGGL(prefill_quad_kernel<uint16_t>, grid, dim3(kQT), 0, st, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                       static_cast<uint16_t*>(a.o), a.den, a.T, a.eps);
-  else
-    hipLaunchKernelGGL(prefill_quad_kernel<float>, grid, dim3(kQT), 0, st, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                       static_cast<float*>(a.o), a.den, a.T, a.eps);
+  switch (a.factor_kind * 8 + a.factors) {
+    case 0 * 8 + 1:
+    case 1 * 8 + 1: launch_quad<0, 1>(a, grid, st); break;
+    case 0 * 8 + 2: launch_quad<0, 2>(a, grid, st); break;
+    case 1 * 8 + 2: launch_quad<1, 2>(a, grid, st); break;
+    case 0 * 8 + 4: launch_quad<0, 4>(a, grid, st); break;
+    case 1 * 8 + 4: launch_quad<1, 4>(a, grid, st); break;
+    default: prof_end(st); return hipErrorInvalidValue;
+  }
   prof_end(st);
   return hipGetLastError();
 }

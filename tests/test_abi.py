@@ -172,6 +172,20 @@ def test_prefill_quadratic_rejects(lib):
     assert call(ctypes.byref(_shape(eps=-1.0)), P, P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
 
 
+def test_prefill_quadratic_factors_rejects(lib):
+    call = lib.kla_prefill_quadratic_factors
+    shp = ctypes.byref(_shape())
+    assert call(None, 0, 2, P, P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(shp, 0, 2, P, P, P, None, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(shp, 2, 2, P, P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"kind" in lib.kla_last_error()
+    for g in (0, 3, 8, -1):
+        assert call(shp, B.KLA_FACTORS_SUM, g, P, P, P, P, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"factors" in lib.kla_last_error()
+    assert call(ctypes.byref(_shape(d_qk=32, d_v=32)), 0, 2, P, P, P, P, None, None) == B.KLA_ERR_UNSUPPORTED
+    assert call(ctypes.byref(_shape(in_dtype=B.KLA_F32)), 1, 4, P, P, P, P, None, None) == B.KLA_ERR_UNSUPPORTED
+
+
 def test_prefill_quadratic_backward_rejects(lib):
     call = lib.kla_prefill_quadratic_backward
     shp = ctypes.byref(_shape())
