@@ -7,8 +7,9 @@ Main line: bf16 prefill of 4 x 8 heads x 4096 tokens, d = 64 (D = 2080),
 chunk 64 — one step is one kla_prefill call (lift, intra-chunk term,
 cross-chunk state readout and update, combine). Secondary lines (in
 "secondary"): the 16-head x 65536-token long-context prefill, the main
-workload again through the quadratic (no state) form, and with the
-multi-factor lifts KATA-M2 (two concatenated factor lifts) and KATA-Sigma-2
+workload again through the quadratic (no state) form, both prefill workloads
+with the multi-factor lift KATA-M2 (two concatenated factor lifts, chunked
+state form), the main one in the quadratic form with KATA-M2 and KATA-Sigma-2
 (two summed factors), its gradients (the quadratic-form backward), the decode + self-recall selection loop (4096
 head-states, 128 steps), the hybrid prefill (2 x 16 x 16384) and the
 token-by-token hybrid decode (4096 head-states, 128 steps after a 2048-token
@@ -98,17 +99,19 @@ def timed_calls(torch, K, fn, steps, warmup):
     return (t1 - t0) * 1e3 / steps, (kms / nk if nk else float("nan")), nk / steps
 
 
-def bench_prefill(torch, K, S, name, steps, warmup):
+def bench_prefill(torch, K, S, name, steps, warmup, factors=1):
+    """kla_prefill on a configuration (factors > 1: the concatenated
+    multi-factor lift KATA-Mg through kla_prefill_factors)."""
     cfg = S.CONFIGS[name]
     c = S.prefill_case(name, cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
                        cfg["seed"])
     q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (c.q, c.k, c.v))
     del c
     o = torch.empty_like(v)
-    step_ms, kern_ms, per_step = timed_calls(torch, K, lambda: K.prefill(q, k, v, chunk=cfg["chunk"], out=o),
-                                             steps, warmup)
+    step_ms, kern_ms, per_step = timed_calls(
+        torch, K, lambda: K.prefill(q, k, v, chunk=cfg["chunk"], out=o, factors=factors), steps, warmup)
     B, H, T, d, dv = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
-    D = phi_dim(d)
+    D = phi_dim(d) if factors == 1 else K.factor_phi_dim(d, factors)
     head_tokens = B * H * T
     # dominant kernel: cross-chunk readout phi(Q)[H|s] and update phi(K)^T[V|1]
     kern_flops = 4.0 * D * (dv + 1) * head_tokens
@@ -118,14 +121,17 @@ def bench_prefill(torch, K, S, name, steps, warmup):
     mfma = K.prefill_uses_matrix_cores()
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_F32_VALU_TFLOPS
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+    traffic = None
+    if mfma and factors == 1:
+        traffic = measured_traffic("prefill_mfma.hip", f"prefill_state_kernel_{name}_traffic.md")
     return dict(
-        workload=name, B=B, H=H, T=T, d_qk=d, d_v=dv, chunk=C, step_ms=step_ms,
+        workload=name + ("" if factors == 1 else f" (KATA-M{factors}, chunked state form, D = {D})"),
+        B=B, H=H, T=T, d_qk=d, d_v=dv, chunk=C, step_ms=step_ms,
         tokens_per_s=B * T / (step_ms * 1e-3), head_tokens_per_s=head_tokens / (step_ms * 1e-3),
         call_tflops=call_flops / (step_ms * 1e-3) / 1e12,
         roofline=dict(bound="mfma" if mfma else "alu", achieved=achieved, peak=peak, unit="TFLOP/s",
                       frac=achieved / peak, kernel_ms=kern_ms,
-                      traffic=measured_traffic("prefill_mfma.hip", f"prefill_state_kernel_{name}_traffic.md")
-                      if mfma else None,
+                      traffic=traffic,
                       kernel="prefill state/readout", flops_per_launch=kern_flops),
         arith="bf16" if mfma else "f32",
     )
@@ -342,6 +348,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
     ap.add_argument("--only", choices=["prefill_1x16x65536", "prefill_4x8x4096_quadratic",
                                        "prefill_4x8x4096_m2", "prefill_4x8x4096_sigma2",
+                                       "prefill_4x8x4096_m2_state", "prefill_1x16x65536_m2_state",
                                        "prefill_4x8x4096_backward", "decode_sre_4096x128",
                                        "hybrid_2x16x16384", "hybrid_decode_4096"],
                     help="run just this secondary workload and print its line (for profiling)")
@@ -372,6 +379,8 @@ def main():
             r = bench_prefill(torch, K, S, args.only, args.steps, args.warmup)
         elif args.only == "prefill_4x8x4096_quadratic":
             r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
+        elif args.only.endswith("_m2_state"):
+            r = bench_prefill(torch, K, S, args.only[:-len("_m2_state")], args.steps, args.warmup, factors=2)
         elif args.only in ("prefill_4x8x4096_m2", "prefill_4x8x4096_sigma2"):
             kind = "concat" if args.only.endswith("m2") else "sum"
             r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup, 2, kind)
@@ -396,6 +405,10 @@ def main():
         secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1))
         log("[bench] secondary: prefill_4x8x4096 in the quadratic form")
         secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup))
+        log("[bench] secondary: prefill_4x8x4096 with the KATA-M2 lift (chunked state form)")
+        secondary.append(bench_prefill(torch, K, S, name, args.steps, args.warmup, factors=2))
+        log("[bench] secondary: prefill_1x16x65536 with the KATA-M2 lift (chunked state form)")
+        secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1, factors=2))
         for g, kind in ((2, "concat"), (2, "sum")):
             log(f"[bench] secondary: prefill_4x8x4096 in the quadratic form, {kind} of {g} factors")
             secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup, g, kind))

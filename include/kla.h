@@ -123,6 +123,36 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
                          const void* v, void* o, const float* H0, const float* s0, float* H_T,
                          float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream);
 
+/* Multi-factor lifts (KATA-Mg, KATA-Sigma-g); see kla_prefill_factors and
+ * kla_prefill_quadratic_factors. */
+#define KLA_FACTORS_CONCAT 0
+#define KLA_FACTORS_SUM 1
+
+/* ------------------------------------------------------------------------
+ * kla_prefill_factors - kla_prefill with the concatenated multi-factor lift
+ * (KATA §2.3, "Variantes": KATA-Mg; the factors read as g equal slices of the
+ * 64 dimensions, see kla_prefill_quadratic_factors below). The state holds
+ * only the features inside each factor:
+ *   D_g = g p (p + 1) / 2 features, p = 64 / g  (2080, 1056, 544 for g = 1, 2, 4),
+ * laid out factor by factor, each block in the vec_sym order of kla_prefill
+ * (upper triangle row-major, sqrt(2) off the diagonal) over its p dimensions;
+ * H0/s0/H_T/s_T are [N, D_g, d_v] and [N, D_g] float32. The outputs are those
+ * of kla_prefill_quadratic_factors with KLA_FACTORS_CONCAT.
+ *
+ *   kind    : KLA_FACTORS_CONCAT (KLA_FACTORS_SUM returns
+ *             KLA_ERR_UNSUPPORTED: the summed lift is served by the quadratic
+ *             form only).
+ *   factors : 1, 2 or 4 (1 is kla_prefill).
+ *   other arguments and the workspace: as for kla_prefill
+ *             (kla_prefill_workspace_size of the same shape and chunk).
+ * Supported for factors > 1: the bf16 matrix path (d_qk = d_v = 64, bf16
+ * inputs); other shapes return KLA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+KLA_API kla_status_t kla_prefill_factors(const kla_shape_t* shp, int chunk, int kind, int factors,
+                                         const void* q, const void* k, const void* v, void* o,
+                                         const float* H0, const float* s0, float* H_T, float* s_T,
+                                         void* ws, size_t ws_bytes, kla_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * kla_prefill_quadratic - the same causal outputs in the quadratic form
  * (KATA §2.3, the first of its two operating points: a FlashAttention-style
@@ -166,8 +196,6 @@ KLA_API kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q
  * another kind or factor count returns KLA_ERR_INVALID_ARGUMENT, other shapes
  * KLA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
-#define KLA_FACTORS_CONCAT 0
-#define KLA_FACTORS_SUM 1
 KLA_API kla_status_t kla_prefill_quadratic_factors(const kla_shape_t* shp, int kind, int factors,
                                                    const void* q, const void* k, const void* v, void* o,
                                                    float* den, kla_stream_t stream);

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     KlaError,
     LIB_PATH,
     decode_step,
+    factor_phi_dim,
     hybrid_decode_flush,
     hybrid_decode_state,
     hybrid_decode_step,
@@ -35,5 +36,6 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["prefill", "prefill_quadratic", "prefill_quadratic_backward", "decode_step", "sre_select", "hybrid_prefill",
-           "hybrid_decode_state", "hybrid_decode_step", "hybrid_decode_flush", "phi_dim", "load_library",
+           "hybrid_decode_state", "hybrid_decode_step", "hybrid_decode_flush", "phi_dim", "factor_phi_dim",
+           "load_library",
            "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

@@ -22,7 +22,7 @@ KLA_FACTORS_CONCAT, KLA_FACTORS_SUM = 0, 1
 EXPORTS = (
     "kla_abi_version", "kla_phi_dim", "kla_status_string", "kla_last_error",
     "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill", "kla_prefill_quadratic",
-    "kla_prefill_quadratic_factors", "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
+    "kla_prefill_quadratic_factors", "kla_prefill_factors", "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill",
@@ -91,6 +91,7 @@ def load_library(path: str = LIB_PATH):
         "kla_prefill": (i, [shp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_prefill_quadratic": (i, [shp, vp, vp, vp, vp, vp, vp]),
         "kla_prefill_quadratic_factors": (i, [shp, i, i, vp, vp, vp, vp, vp, vp]),
+        "kla_prefill_factors": (i, [shp, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_prefill_quadratic_backward_workspace_size": (i, [shp, szp]),
         "kla_prefill_quadratic_backward": (i, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
@@ -175,11 +176,13 @@ def prefill_uses_matrix_cores(B=4, H=8, T=4096, d_qk=64, d_v=64, chunk=64, dtype
 
 
 def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, eps: float = 0.0,
-            out_dtype=None, outputs: bool = True, out=None):
+            out_dtype=None, outputs: bool = True, out=None, factors: int = 1):
     """Chunked causal prefill. q, k [B, H, T, d_qk]; v [B, H, T, d_v] (float32 or
     bfloat16, same dtype). ``state`` = (H0, s0) float32 resumes a previous call.
     Returns o, or (o, H_T, s_T) with ``return_state``; with ``outputs=False``
-    only (H_T, s_T)."""
+    only (H_T, s_T). ``factors`` > 1 selects the concatenated multi-factor
+    lift KATA-Mg (kla_prefill_factors; bf16, d = 64), whose state has
+    factor_phi_dim(d_qk, factors) features."""
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
@@ -193,7 +196,7 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     code = _dtype_code(q)
     ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
     shp = Shape(B, Hh, T, dqk, dv, code, ocode, float(eps))
-    D = phi_dim(dqk)
+    D = phi_dim(dqk) if factors == 1 else factor_phi_dim(dqk, factors)
     dev = q.device
     if outputs and out is not None:
         if out.shape != (B, Hh, T, dv) or out.dtype != _torch_dtype(ocode) or not out.is_contiguous():
@@ -215,15 +218,26 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     nbytes = ctypes.c_size_t(0)
     check(lib.kla_prefill_workspace_size(ctypes.byref(shp), int(chunk), int(outputs), ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
-    check(lib.kla_prefill(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                          _ptr(H0), _ptr(s0), _ptr(HT), _ptr(sT), _ptr(ws), nbytes.value,
-                          _stream(dev)))
+    if factors == 1:
+        check(lib.kla_prefill(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                              _ptr(H0), _ptr(s0), _ptr(HT), _ptr(sT), _ptr(ws), nbytes.value,
+                              _stream(dev)))
+    else:
+        check(lib.kla_prefill_factors(ctypes.byref(shp), int(chunk), KLA_FACTORS_CONCAT, int(factors),
+                                      _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(H0), _ptr(s0), _ptr(HT),
+                                      _ptr(sT), _ptr(ws), nbytes.value, _stream(dev)))
     if not outputs:
         return HT, sT
     return (o, HT, sT) if return_state else o
 
 
 FACTOR_KINDS = {"concat": 0, "sum": 1}
+
+
+def factor_phi_dim(d: int, factors: int) -> int:
+    """State features of the concatenated multi-factor lift: g p(p+1)/2, p = d / g."""
+    p = d // factors
+    return factors * p * (p + 1) // 2
 
 
 def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None, return_den: bool = False,

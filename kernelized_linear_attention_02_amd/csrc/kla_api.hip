@@ -285,10 +285,11 @@ kla_status_t kla_prefill_workspace_size(const kla_shape_t* shp, int chunk, int w
   return ok();
 }
 
-kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const void* k,
-                         const void* v, void* o, const float* H0, const float* s0, float* H_T,
-                         float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
-  const char* fn = "kla_prefill";
+namespace {
+
+kla_status_t prefill_call(const char* fn, const kla_shape_t* shp, int chunk, int factors, const void* q,
+                          const void* k, const void* v, void* o, const float* H0, const float* s0, float* H_T,
+                          float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
   kla_status_t st = check_shape(shp, fn);
   if (st != KLA_OK) return st;
   if (chunk != 32 && chunk != 64 && chunk != 128)
@@ -309,12 +310,37 @@ kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const
   a.s0 = s0;
   a.HT = H_T;
   a.sT = s_T;
+  a.factors = factors;
+  if (factors != 1 && !kla::prefill_mfma_supported(a))
+    return fail(KLA_ERR_UNSUPPORTED, "%s: %d factors need d_qk = d_v = 64 and bf16 inputs", fn, factors);
   const size_t need = prefill_ws(a);
   st = check_ws(need, ws, ws_bytes, fn);
   if (st != KLA_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (kla::prefill_mfma_supported(a)) return hip_status(kla::prefill_mfma_launch(a, ws, hs), fn);
   return hip_status(kla::prefill_valu_launch(a, ws, hs), fn);
+}
+
+}  // namespace
+
+kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const void* k,
+                         const void* v, void* o, const float* H0, const float* s0, float* H_T,
+                         float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
+  return prefill_call("kla_prefill", shp, chunk, 1, q, k, v, o, H0, s0, H_T, s_T, ws, ws_bytes, stream);
+}
+
+kla_status_t kla_prefill_factors(const kla_shape_t* shp, int chunk, int kind, int factors, const void* q,
+                                 const void* k, const void* v, void* o, const float* H0, const float* s0,
+                                 float* H_T, float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
+  const char* fn = "kla_prefill_factors";
+  if (kind == KLA_FACTORS_SUM)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: the summed-factor lift is served by kla_prefill_quadratic_factors only",
+                fn);
+  if (kind != KLA_FACTORS_CONCAT)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: kind %d is neither KLA_FACTORS_CONCAT nor KLA_FACTORS_SUM", fn, kind);
+  if (factors != 1 && factors != 2 && factors != 4)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: factors = %d (1, 2 or 4 supported)", fn, factors);
+  return prefill_call(fn, shp, chunk, factors, q, k, v, o, H0, s0, H_T, s_T, ws, ws_bytes, stream);
 }
 
 kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const void* k, const void* v,

@@ -54,6 +54,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -64,7 +65,6 @@ constexpr int kAcc = kDim + 1;                    // accumulator row: num | den
 // accumulator order [n-tile][lane][4 tokens], then the 16 denominators.
 constexpr int kTileAcc = 16 * kAcc;
 
-__device__ __forceinline__ int feat_index(int a, int b) { return a * kDim - a * (a - 1) / 2 + (b - a); }
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -123,25 +123,38 @@ constexpr int kKS = kCS + 4;                      // k^T row stride (floats)
 __host__ __device__ constexpr int bp_x(int bp) { return bp < 4 ? 0 : bp < 7 ? 1 : bp < 9 ? 2 : 3; }
 __host__ __device__ constexpr int bp_y(int bp) { return bp < 4 ? bp : bp < 7 ? bp - 3 : bp < 9 ? bp - 5 : 3; }
 
+// Block pairs of the lift with G factors (KATA-Mg, concatenated factor lifts:
+// only pairs of dimensions inside one factor of 64 / G dimensions are
+// features): G = 1 all ten, G = 2 the six inside the halves, G = 4 the four
+// diagonal blocks.
+__host__ __device__ constexpr int factor_bps(int G) { return G == 1 ? 10 : G == 2 ? 6 : 4; }
+__host__ __device__ constexpr int factor_bp(int G, int i) {
+  return G == 1 ? i : G == 2 ? (i < 2 ? i : i == 2 ? 4 : i + 4) : (i == 0 ? 0 : i == 1 ? 4 : i == 2 ? 7 : 9);
+}
+
 // The tiles of one slice. S = 8: tile u is (block pair u / 2, j = j0 + u % 2)
-// with j0 = 2 * slice; S = 16: tile u is (block pair u, j = slice). Readout
-// pairs are tiles (2p, 2p + 1).
-template <int S>
+// with j0 = 2 * slice; S = 16: tile u is (block pair u, j = slice), block
+// pairs taken from the factor structure's list. Readout pairs are tiles
+// (2p, 2p + 1); update wave w and readout half h take contiguous shares.
+template <int S, int G>
 struct Slice {
   static_assert(S == 8 || S == 16, "slices per head");
-  static constexpr int kTiles = S == 8 ? 20 : 10;
+  static_assert(G == 1 || G == 2 || G == 4, "factors");
+  static constexpr int kBP = factor_bps(G);
+  static constexpr int kTiles = S == 8 ? 2 * kBP : kBP;
   static constexpr int kPairs = kTiles / 2;
   static constexpr int kJ = S == 8 ? 2 : 1;  // values of j in a slice
-  __host__ __device__ static constexpr int bp(int u) { return S == 8 ? u >> 1 : u; }
+  static constexpr int kMaxU = (kTiles + 3) / 4;
+  __host__ __device__ static constexpr int bp(int u) { return factor_bp(G, S == 8 ? u >> 1 : u); }
   __host__ __device__ static constexpr int jj(int u) { return S == 8 ? (u & 1) : 0; }
   __host__ __device__ static constexpr int X(int u) { return bp_x(bp(u)); }
   __host__ __device__ static constexpr int Y(int u) { return bp_y(bp(u)); }
   // update wave w owns tiles [upd_first(w), upd_first(w) + upd_count(w))
-  __host__ __device__ static constexpr int upd_first(int w) { return S == 8 ? 5 * w : (w < 2 ? 3 * w : 2 * w + 2); }
-  __host__ __device__ static constexpr int upd_count(int w) { return S == 8 ? 5 : (w < 2 ? 3 : 2); }
+  __host__ __device__ static constexpr int upd_count(int w) { return kTiles / 4 + (w < kTiles % 4 ? 1 : 0); }
+  __host__ __device__ static constexpr int upd_first(int w) { return w * (kTiles / 4) + (w < kTiles % 4 ? w : kTiles % 4); }
   // readout half h owns pairs [rd_first(h), rd_first(h) + rd_count(h))
-  __host__ __device__ static constexpr int rd_first(int h) { return S == 8 ? 5 * h : 3 * h; }
-  __host__ __device__ static constexpr int rd_count(int h) { return S == 8 ? 5 : 3 - h; }
+  __host__ __device__ static constexpr int rd_first(int h) { return h * ((kPairs + 1) / 2); }
+  __host__ __device__ static constexpr int rd_count(int h) { return h == 0 ? (kPairs + 1) / 2 : kPairs / 2; }
   __host__ __device__ static constexpr bool upd_uses_x(int w, int b) {
     for (int u = upd_first(w); u < upd_first(w) + upd_count(w); ++u)
       if (X(u) == b) return true;
@@ -159,14 +172,24 @@ struct Slice {
   }
 };
 
-template <int S>
+// Index of feature (a, b), a <= b in one factor, in the ABI's state layout:
+// the factors' vec_sym blocks in order, each upper-triangular row-major.
+template <int G>
+__device__ __forceinline__ int feat_abi(int a, int b) {
+  constexpr int p = kDim / G;
+  const int f = a / p;
+  const int i = a - f * p, j = b - f * p;
+  return f * (p * (p + 1) / 2) + i * p - i * (i - 1) / 2 + (j - i);
+}
+
+template <int S, int G>
 struct StateLds {
   // staged sub-chunks, double buffered (the next is staged during this one)
   float qs[2][kCS][kQS];                          // q rows (fp32)
   float kt[2][kDim][kKS];                         // k transposed (fp32)
   uint16_t vt[2][kDim][kCS + 8];                  // v transposed (bf16)
-  uint4 hs[Slice<S>::kPairs][4][64];              // G at the chunk start, bf16 B fragments
-  uint4 ss[Slice<S>::kPairs][4];                  // s as bf16 per pair and lane quarter
+  uint4 hs[Slice<S, G>::kPairs][4][64];           // G at the chunk start, bf16 B fragments
+  uint4 ss[Slice<S, G>::kPairs][4];               // s as bf16 per pair and lane quarter
   f32x4 xs[kRW][5][64];                           // readout trade: one token tile's accumulators
 };
 
@@ -199,8 +222,8 @@ __device__ __forceinline__ Prefetch prefetch(const uint16_t* __restrict__ q, con
 
 // Staging: thread (token t, 8-dim group grp) writes q as fp32 rows, k as
 // fp32 columns and v as bf16 columns.
-template <int S>
-__device__ __forceinline__ void stage(StateLds<S>& sh, const Prefetch& p, int t, int grp, int buf) {
+template <class Lds>
+__device__ __forceinline__ void stage(Lds& sh, const Prefetch& p, int t, int grp, int buf) {
   const uint4 z = make_uint4(0, 0, 0, 0);
   const uint4 pq = p.ok ? p.q : z, pk = p.ok ? p.k : z, pv = p.ok ? p.v : z;
   const uint32_t qw[4] = {pq.x, pq.y, pq.z, pq.w};
@@ -226,6 +249,7 @@ struct StateCtx {
   const uint16_t* k;
   const uint16_t* v;
   int T, NC, S, n, slice, j0;
+  int D;  // features per head in the ABI layout
   const float* H0;
   const float* s0;
   float* HT;
@@ -235,9 +259,9 @@ struct StateCtx {
 
 // ------------------------------------------------------------- update waves
 
-template <int C, int CS, int S, int W>
-__device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx) {
-  using SL = Slice<S>;
+template <int C, int CS, int S, int G, int W>
+__device__ __forceinline__ void update_wave(StateLds<S, G>& sh, const StateCtx& cx) {
+  using SL = Slice<S, G>;
   constexpr int U0 = SL::upd_first(W);
   constexpr int NU = SL::upd_count(W);
   constexpr int SUB = C / CS;
@@ -259,7 +283,7 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int a = a0 + i;
-      const size_t f = (size_t)cx.n * kD + feat_index(min(a, b), max(a, b));
+      const size_t f = (size_t)cx.n * cx.D + feat_abi<G>(min(a, b), max(a, b));
       const float sc = a != b ? inv_sqrt2 : 1.0f;
       if (cx.H0) {
 #pragma unroll
@@ -364,7 +388,7 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
     for (int i = 0; i < 4; ++i) {
       const int a = a0 + i;
       if (a > b) continue;
-      const size_t f = (size_t)cx.n * kD + feat_index(a, b);
+      const size_t f = (size_t)cx.n * cx.D + feat_abi<G>(a, b);
       const float sc = a < b ? sqrt2 : 1.0f;
       if (cx.HT) {
 #pragma unroll
@@ -377,9 +401,9 @@ __device__ __forceinline__ void update_wave(StateLds<S>& sh, const StateCtx& cx)
 
 // ------------------------------------------------------------ readout waves
 
-template <int C, int CS, int S, int W>
-__device__ __forceinline__ void readout_wave(StateLds<S>& sh, const StateCtx& cx) {
-  using SL = Slice<S>;
+template <int C, int CS, int S, int G, int W>
+__device__ __forceinline__ void readout_wave(StateLds<S, G>& sh, const StateCtx& cx) {
+  using SL = Slice<S, G>;
   constexpr int HF = W & 1;                       // half of the pairs
   constexpr int TP = W >> 1;                      // token tiles 2 TP, 2 TP + 1 of a sub-chunk
   constexpr int P0 = SL::rd_first(HF);
@@ -437,8 +461,8 @@ __device__ __forceinline__ void readout_wave(StateLds<S>& sh, const StateCtx& cx
   };
   auto stage2 = [&](const Prefetch (&p)[2], int buf) {
     if (lane < CS) {
-      stage<S>(sh, p[0], lane, 2 * W, buf);
-      stage<S>(sh, p[1], lane, 2 * W + 1, buf);
+      stage(sh, p[0], lane, 2 * W, buf);
+      stage(sh, p[1], lane, 2 * W + 1, buf);
     }
   };
   Prefetch pf[2];
@@ -521,14 +545,14 @@ __device__ __forceinline__ void readout_wave(StateLds<S>& sh, const StateCtx& cx
 
 // C: the chunk (intra-chunk region of the output); the state kernel stages it
 // in sub-chunks of CS tokens, all read out against the state at the chunk start.
-template <int C, int S>
+template <int C, int S, int G>
 __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int T,
     const float* __restrict__ H0, const float* __restrict__ s0, float* __restrict__ HT, float* __restrict__ sT,
     uint16_t* __restrict__ part) {
   constexpr int CS = C < kCS ? C : kCS;
   static_assert(C % CS == 0 && CS % 32 == 0, "chunk must be a multiple of the sub-chunk");
-  __shared__ __align__(16) StateLds<S> sh;
+  __shared__ __align__(16) StateLds<S, G> sh;
   StateCtx cx;
   cx.q = q;
   cx.k = k;
@@ -536,6 +560,7 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
   cx.T = T;
   cx.NC = (T + C - 1) / C;
   cx.S = S;
+  cx.D = G * (kDim / G) * (kDim / G + 1) / 2;
   wg_identity(N, S, cx.n, cx.slice);
   cx.j0 = S == 8 ? 2 * cx.slice : cx.slice;
   cx.H0 = H0;
@@ -545,14 +570,14 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
   cx.part = part;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wv) {
-    case 0: update_wave<C, CS, S, 0>(sh, cx); break;
-    case 1: update_wave<C, CS, S, 1>(sh, cx); break;
-    case 2: update_wave<C, CS, S, 2>(sh, cx); break;
-    case 3: update_wave<C, CS, S, 3>(sh, cx); break;
-    case 4: readout_wave<C, CS, S, 0>(sh, cx); break;
-    case 5: readout_wave<C, CS, S, 1>(sh, cx); break;
-    case 6: readout_wave<C, CS, S, 2>(sh, cx); break;
-    default: readout_wave<C, CS, S, 3>(sh, cx); break;
+    case 0: update_wave<C, CS, S, G, 0>(sh, cx); break;
+    case 1: update_wave<C, CS, S, G, 1>(sh, cx); break;
+    case 2: update_wave<C, CS, S, G, 2>(sh, cx); break;
+    case 3: update_wave<C, CS, S, G, 3>(sh, cx); break;
+    case 4: readout_wave<C, CS, S, G, 0>(sh, cx); break;
+    case 5: readout_wave<C, CS, S, G, 1>(sh, cx); break;
+    case 6: readout_wave<C, CS, S, G, 2>(sh, cx); break;
+    default: readout_wave<C, CS, S, G, 3>(sh, cx); break;
   }
 }
 
@@ -566,7 +591,7 @@ struct FinishLds {
 };
 
 // One work-group per (chunk, head): intra-chunk term + accumulator -> output.
-template <int C, typename Tout>
+template <int C, typename Tout, int G>
 __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ part, int S,
@@ -609,19 +634,33 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
     const int kmax = ((mq >> 1) << 1) + 1;  // last key tile of the 32-key step
     float den_part[4] = {0.f, 0.f, 0.f, 0.f};
     for (int kq = 0; kq <= kmax && kq < C / 16; ++kq) {
-      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+      // lane holds the weight of query mq*16 + 4*q4 + i and key kq*16 + l16:
+      // (q . k)^2, or the sum over the G factors of (q_f . k_f)^2
+      f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (G == 4) {
 #pragma unroll
-      for (int ks = 0; ks < kDim / 32; ++ks) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.qs[mq * 16 + l16][ks * 32 + 8 * q4]);
-        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.ks[kq * 16 + l16][ks * 32 + 8 * q4]);
-        s4 = mfma(A, B, s4);
+        for (int f = 0; f < 4; ++f) {
+          const s16x4 A = *reinterpret_cast<const s16x4*>(&sh.qs[mq * 16 + l16][16 * f + 4 * q4]);
+          const s16x4 B = *reinterpret_cast<const s16x4*>(&sh.ks[kq * 16 + l16][16 * f + 4 * q4]);
+          const f32x4 s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          w4 += s4 * s4;
+        }
+      } else {
+        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kDim / 32; ++ks) {
+          const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.qs[mq * 16 + l16][ks * 32 + 8 * q4]);
+          const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.ks[kq * 16 + l16][ks * 32 + 8 * q4]);
+          s4 = mfma(A, B, G == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : s4);
+          if (G == 2) w4 += s4 * s4;
+        }
+        if (G == 1) w4 = s4 * s4;
       }
-      // lane holds S[query mq*16 + 4*q4 + i][key kq*16 + l16]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qi = mq * 16 + 4 * q4 + i;
         const int ki = kq * 16 + l16;
-        const float sq = s4[i] * s4[i];
+        const float sq = w4[i];
         const float a = (ki <= qi && ki < L) ? sq : 0.0f;
         den_part[i] += a;
         sh.at[qi][ki] = __builtin_bit_cast(uint16_t, (__bf16)a);
@@ -700,48 +739,58 @@ size_t part_bytes(const PrefillArgs& a) {
   return align_up((size_t)a.N * nc * S * kAcc * C * sizeof(uint16_t));
 }
 
-template <int C, int S>
+template <int C, int S, int G>
 void launch_state(const PrefillArgs& a, uint16_t* part, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_state_kernel<C, S>), dim3(S * a.N), dim3(kThreads3), 0, st,
+  hipLaunchKernelGGL((prefill_state_kernel<C, S, G>), dim3(S * a.N), dim3(kThreads3), 0, st,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.N, a.T, a.H0, a.s0, a.HT, a.sT, part);
 }
 
-template <int C>
+template <int C, int G>
 hipError_t launch_c(const PrefillArgs& a, void* ws, hipStream_t st) {
   uint16_t* part = a.o ? static_cast<uint16_t*>(ws) : nullptr;
   const int S = slices_for(a.N);
   prof_begin(st);
-  if (S == 16) launch_state<C, 16>(a, part, st);
-  else launch_state<C, 8>(a, part, st);
+  if (S == 16) launch_state<C, 16, G>(a, part, st);
+  else launch_state<C, 8, G>(a, part, st);
   prof_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
   const dim3 grid((a.T + C - 1) / C, a.N);
   if (a.out_bf16)
-    hipLaunchKernelGGL((prefill_finish_kernel<C, uint16_t>), grid, dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((prefill_finish_kernel<C, uint16_t, G>), grid, dim3(kThreads), 0, st,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), part, S, static_cast<uint16_t*>(a.o), a.T, a.eps);
   else
-    hipLaunchKernelGGL((prefill_finish_kernel<C, float>), grid, dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((prefill_finish_kernel<C, float, G>), grid, dim3(kThreads), 0, st,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), part, S, static_cast<float*>(a.o), a.T, a.eps);
   return hipGetLastError();
 }
 
+template <int G>
+hipError_t launch_g(const PrefillArgs& a, void* ws, hipStream_t st) {
+  switch (run_chunk(a.chunk)) {
+    case 64: return launch_c<64, G>(a, ws, st);
+    case 128: return launch_c<128, G>(a, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool prefill_mfma_supported(const PrefillArgs& a) {
-  return a.in_bf16 && a.dqk == kDim && a.dv == kDim &&
-         (a.chunk == 32 || a.chunk == 64 || a.chunk == 128);
+  return a.in_bf16 && a.dqk == kDim && a.dv == kDim && (a.chunk == 32 || a.chunk == 64 || a.chunk == 128) &&
+         a.factor_kind == 0 && (a.factors == 1 || a.factors == 2 || a.factors == 4);
 }
 
 size_t prefill_mfma_workspace(const PrefillArgs& a) { return a.o ? part_bytes(a) : 0; }
 
 hipError_t prefill_mfma_launch(const PrefillArgs& a, void* ws, hipStream_t st) {
-  switch (run_chunk(a.chunk)) {
-    case 64: return launch_c<64>(a, ws, st);
-    case 128: return launch_c<128>(a, ws, st);
+  switch (a.factors) {
+    case 1: return launch_g<1>(a, ws, st);
+    case 2: return launch_g<2>(a, ws, st);
+    case 4: return launch_g<4>(a, ws, st);
   }
   return hipErrorInvalidValue;
 }

@@ -186,6 +186,24 @@ def test_prefill_quadratic_factors_rejects(lib):
     assert call(ctypes.byref(_shape(in_dtype=B.KLA_F32)), 1, 4, P, P, P, P, None, None) == B.KLA_ERR_UNSUPPORTED
 
 
+def test_prefill_factors_rejects(lib):
+    call = lib.kla_prefill_factors
+    shp = ctypes.byref(_shape())
+
+    def go(kind=B.KLA_FACTORS_CONCAT, g=2, shape=shp, chunk=64):
+        return call(shape, chunk, kind, g, P, P, P, P, None, None, None, None, P, 1 << 40, None)
+    assert go(kind=B.KLA_FACTORS_SUM) == B.KLA_ERR_UNSUPPORTED
+    assert b"quadratic" in lib.kla_last_error()
+    assert go(kind=5) == B.KLA_ERR_INVALID_ARGUMENT
+    for g in (0, 3, 8):
+        assert go(g=g) == B.KLA_ERR_INVALID_ARGUMENT
+    assert go(chunk=48) == B.KLA_ERR_UNSUPPORTED
+    # factors > 1 only on the bf16 matrix path
+    assert go(shape=ctypes.byref(_shape(in_dtype=B.KLA_F32))) == B.KLA_ERR_UNSUPPORTED
+    assert go(shape=ctypes.byref(_shape(d_qk=32, d_v=32))) == B.KLA_ERR_UNSUPPORTED
+    assert go(shape=None) == B.KLA_ERR_INVALID_ARGUMENT
+
+
 def test_prefill_quadratic_backward_rejects(lib):
     call = lib.kla_prefill_quadratic_backward
     shp = ctypes.byref(_shape())

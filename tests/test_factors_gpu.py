@@ -86,3 +86,70 @@ def test_factors_4x8x4096_full_size(K, kind):
         W = np.where(np.arange(T)[None, :] <= rows[:, None], O.factor_weights(c.q[b, h][rows], c.k[b, h], 2, kind), 0.0)
         ref = (W @ c.v[b, h].astype(np.float64)) / W.sum(axis=1)[:, None]
         assert_close(go[b, h, rows], ref, RTOL_BF16, f"o rows {kind} head ({b},{h})")
+
+
+# ---- the concatenated lift through the chunked state form (kla_prefill_factors)
+
+@pytest.mark.parametrize("g", [2, 4])
+@pytest.mark.parametrize("B,H,chunk,T", [(1, 3, 64, 50), (2, 2, 128, 300), (2, 10, 64, 130), (1, 17, 32, 97)])
+def test_factors_state_form_every_row(K, g, B, H, chunk, T):
+    # against the oracle's fixed-size state form: outputs and the final state
+    # (H_T, s_T in the concatenated per-factor vec_sym layout); more than 16
+    # heads exercises the 8-slice split
+    c = S.prefill_case("factors_state", B, H, T, 64, 64, chunk, seed=70 + g + T)
+    o, HT, sT = K.prefill(dev(c.q), dev(c.k), dev(c.v), chunk=chunk, return_state=True, factors=g)
+    torch.cuda.synchronize()
+    D = K.factor_phi_dim(64, g)
+    assert HT.shape == (B, H, D, 64) and sT.shape == (B, H, D)
+    for b in range(B):
+        for h in range(H):
+            ro, rH, rs = O.prefill_factors_recurrent(c.q[b, h], c.k[b, h], c.v[b, h], g, "concat")
+            assert_close(host(o)[b, h], ro, RTOL_BF16, f"o g={g} head ({b},{h})")
+            assert_close(host(HT)[b, h], rH, RTOL_BF16, f"H_T g={g} head ({b},{h})")
+            assert_close(host(sT)[b, h], rs, RTOL_BF16, f"s_T g={g} head ({b},{h})")
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_factors_state_form_resume(K, g):
+    # two calls carrying the state equal one call; state-only mode as well
+    c = S.prefill_case("factors_resume", 1, 3, 500, 64, 64, 64, seed=91 + g)
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    T1 = 192
+    o1, H1, s1 = K.prefill(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], chunk=64, return_state=True, factors=g)
+    o2, H2, s2 = K.prefill(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], chunk=128, state=(H1, s1),
+                           return_state=True, factors=g)
+    Hs, ss = K.prefill(q, k, v, chunk=64, outputs=False, factors=g)
+    ro = np.stack([O.prefill_factors_bruteforce(c.q[0, h], c.k[0, h], c.v[0, h], g, "concat") for h in range(3)])
+    assert_close(host(torch.cat([o1, o2], dim=2))[0], ro, RTOL_BF16, "resumed o")
+    for h in range(3):
+        _, rH, rs = O.prefill_factors_recurrent(c.q[0, h], c.k[0, h], c.v[0, h], g, "concat")
+        assert_close(host(H2)[0, h], rH, RTOL_BF16, "resumed H")
+        assert_close(host(Hs)[0, h], rH, RTOL_BF16, "state-only H")
+        assert_close(host(ss)[0, h], rs, RTOL_BF16, "state-only s")
+
+
+def test_factors_state_form_one_factor_is_prefill(K):
+    c = S.prefill_case("factors_one", 1, 2, 200, 64, 64, 64, seed=95)
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    a = K.prefill(q, k, v, chunk=64)
+    b = K.prefill(q, k, v, chunk=64, factors=1)
+    assert torch.equal(a, b)
+
+
+def test_factors_state_form_4x8x4096_full_size(K):
+    # KATA-M2 on the main prefill workload: sampled rows and one head's state
+    cfg = S.CONFIGS["prefill_4x8x4096"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    c = S.prefill_case("prefill_4x8x4096", B, H, T, cfg["d_qk"], cfg["d_v"], cfg["chunk"], cfg["seed"])
+    o, HT, sT = K.prefill(dev(c.q), dev(c.k), dev(c.v), chunk=64, return_state=True, factors=2)
+    go = host(o)
+    rng = np.random.default_rng(6)
+    for (b, h) in [(0, 0), (B - 1, H - 1)]:
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, T - 1], rng.integers(0, T, 12)]))
+        W = np.where(np.arange(T)[None, :] <= rows[:, None],
+                     O.factor_weights(c.q[b, h][rows], c.k[b, h], 2, "concat"), 0.0)
+        ref = (W @ c.v[b, h].astype(np.float64)) / W.sum(axis=1)[:, None]
+        assert_close(go[b, h, rows], ref, RTOL_BF16, f"o rows head ({b},{h})")
+    fk = O.phi_factors(c.k[1, 3], 2, "concat")
+    assert_close(host(HT)[1, 3], fk.T @ c.v[1, 3].astype(np.float64), RTOL_BF16, "H_T head (1,3)")
+    assert_close(host(sT)[1, 3], fk.sum(axis=0), RTOL_BF16, "s_T head (1,3)")
