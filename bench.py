@@ -81,6 +81,31 @@ def copy_calibration(torch, mib):
     print(json.dumps({"copy_calibration_mib": mib, "bytes_read": n * 2, "bytes_written": n * 2}), flush=True)
 
 
+def stream_ceiling(torch, mib):
+    """Achievable HBM rates of plain streaming on this machine (HIP events):
+    an in-place multiply (read and write one buffer, the decode state's 1:1
+    pattern), a copy (1:1, two buffers) and an in-place add of a second
+    buffer (2 reads : 1 write)."""
+    n = mib * (1 << 20) // 4
+    a = torch.rand(n, device="cuda")
+    b = torch.rand(n, device="cuda")
+    out = {}
+    for name, fn, nbytes in (("rmw_mul", lambda: a.mul_(1.0000001), 2 * 4 * n),
+                             ("copy", lambda: b.copy_(a), 2 * 4 * n),
+                             ("add_inplace", lambda: a.add_(b), 3 * 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        out[name] = dict(ms=ms, tb_per_s=nbytes / (ms * 1e-3) / 1e12)
+    print(json.dumps({"stream_ceiling_mib": mib, **out}), flush=True)
+
+
 def timed_calls(torch, K, fn, steps, warmup):
     """Wall time per call (sync on both sides) and the library's own kernel
     timing of the dominant kernel (HIP events on the call's stream)."""
@@ -352,6 +377,8 @@ def main():
                                        "prefill_4x8x4096_backward", "decode_sre_4096x128",
                                        "hybrid_2x16x16384", "hybrid_decode_4096"],
                     help="run just this secondary workload and print its line (for profiling)")
+    ap.add_argument("--stream-ceiling", type=int, default=0, metavar="MIB",
+                    help="only time plain streaming (in-place multiply, copy, in-place add) over MIB-MiB buffers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB bf16 copy three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -370,6 +397,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.stream_ceiling:
+        stream_ceiling(torch, args.stream_ceiling)
+        return
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
         return
