@@ -222,10 +222,12 @@ __device__ __forceinline__ Prefetch prefetch(const uint16_t* __restrict__ q, con
 
 // Staging: thread (token t, 8-dim group grp) writes q as fp32 rows, k as
 // fp32 columns and v as bf16 columns.
-template <class Lds>
+// FULL: every token of the sub-chunk exists, so nothing is zeroed.
+template <bool FULL, class Lds>
 __device__ __forceinline__ void stage(Lds& sh, const Prefetch& p, int t, int grp, int buf) {
   const uint4 z = make_uint4(0, 0, 0, 0);
-  const uint4 pq = p.ok ? p.q : z, pk = p.ok ? p.k : z, pv = p.ok ? p.v : z;
+  const bool ok = FULL || p.ok;
+  const uint4 pq = ok ? p.q : z, pk = ok ? p.k : z, pv = ok ? p.v : z;
   const uint32_t qw[4] = {pq.x, pq.y, pq.z, pq.w};
   const uint32_t kw[4] = {pk.x, pk.y, pk.z, pk.w};
   const uint32_t vw[4] = {pv.x, pv.y, pv.z, pv.w};
@@ -459,22 +461,27 @@ __device__ __forceinline__ void readout_wave(StateLds<S, G>& sh, const StateCtx&
 #pragma unroll
     for (int g = 0; g < 2; ++g) p[g] = prefetch(cx.q, cx.k, cx.v, row0, n0, cx.T, lane, 2 * W + g);
   };
-  auto stage2 = [&](const Prefetch (&p)[2], int buf) {
+  auto stage2 = [&](const Prefetch (&p)[2], int buf, int st) {
     if (lane < CS) {
-      stage(sh, p[0], lane, 2 * W, buf);
-      stage(sh, p[1], lane, 2 * W + 1, buf);
+      if ((st / SUB) * C + (st % SUB) * CS + CS <= cx.T) {  // uniform: a full sub-chunk
+        stage<true>(sh, p[0], lane, 2 * W, buf);
+        stage<true>(sh, p[1], lane, 2 * W + 1, buf);
+      } else {
+        stage<false>(sh, p[0], lane, 2 * W, buf);
+        stage<false>(sh, p[1], lane, 2 * W + 1, buf);
+      }
     }
   };
   Prefetch pf[2];
   pre(0, pf);
-  stage2(pf, 0);
+  stage2(pf, 0, 0);
   pre(1, pf);  // past the end: clamped reads, never staged
   lds_barrier();  // (B0)
 
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
     if (st + 1 < nsteps) {
-      stage2(pf, buf ^ 1);
+      stage2(pf, buf ^ 1, st + 1);
       pre(st + 2, pf);
     }
     if (active) {
