@@ -16,32 +16,44 @@
 // s(a, b) = sum_t k_a k_b (no sqrt(2)); the ABI's vec_sym layout is converted
 // on import and export.
 //
+// Multi-factor lift (KATA-Mg, KATA §2.3 "Variantes", read as G equal factors
+// of 64 / G dimensions with their rank-one lifts concatenated): its features
+// are the pairs inside one factor, i.e. the tiles of the block pairs inside
+// the factors (G = 2: six of the ten, G = 4: the four diagonal blocks); the
+// finish kernel then sums the factors' squared scores.
+//
 // Slices. A work-group owns one head and the tiles of one value of j (16
-// slices per head) or two (8 slices) across all ten block pairs, so the tile
+// slices per head) or two (8 slices) across the block pairs, so the tile
 // structure inside a work-group is fixed at compile time and only j varies.
 //
-// State kernel, eight waves, stepping through a staged sub-chunk of q, k and v
-// at a time:
+// State kernel, eight waves, stepping through 64-token sub-chunks; each step
+// has two barriers: between them the update waves publish the state and the
+// readout waves flush their partials, around them every wave computes on the
+// staged sub-chunk while the next one is staged into the other buffer:
 //   update waves (4) hold their tiles of G and s in MFMA accumulators (fp32)
 //   for the whole sequence and add phi(K)^T [V | 1] per 32 tokens (MFMA
 //   16x16x32 bf16; a column of ones gives s). In the A operand a lane holds
 //   feature row r for eight tokens: it keeps k_a in registers and takes k_b
 //   from the lane of its 16-lane row that loaded it, by a DPP row broadcast
 //   folded into the multiply. At each chunk end they publish the state as bf16
-//   B fragments in LDS (double buffered).
+//   B fragments in LDS.
 //   readout waves (4): each takes 32 tokens and half of the tiles and reads
-//   out num = phi(Q) G, den = phi(Q) s against the state of the chunk start; a
-//   lane holds one token and forms its products from q values in registers.
-//   The two waves sharing tokens trade halves through LDS, and each writes one
-//   summed bf16 partial of a 16-token tile to a workspace [head, chunk, slice,
-//   token tile, 16 x (d_v + 1)] in the MFMA accumulator order, so that both
-//   its writes and the finish kernel's reads are whole 512-byte runs per wave.
+//   out num = phi(Q) G and den = phi(Q) s (a fifth MFMA n-tile whose first
+//   column is s) against the state of the chunk start; a lane holds one token
+//   and forms its products from q values in registers. The two waves sharing
+//   tokens trade halves through LDS, and each writes one summed bf16 partial
+//   of a 16-token tile to a workspace [head, chunk, slice, token tile,
+//   16 x (d_v + 1)] in the MFMA accumulator order, so that both its writes and
+//   the finish kernel's reads are whole 512-byte runs per wave. They also
+//   stage the sub-chunks (q as fp32 rows, k as fp32 columns, v as bf16
+//   columns) from loads issued one sub-step ahead.
 // A head's work-groups are placed on one XCD (work-groups are dealt to the 8
 // XCDs in turn), so their shared q, k and v reads meet in one L2.
 //
 // Finish kernel. One work-group per (head, chunk): the exact intra-chunk
-// term A [V | 1] with A = lower-triangular (Q K^T)^2 (MFMA), plus the sum of
-// the slice partials, divided, cast to the output type.
+// term A [V | 1] with A = lower-triangular (Q K^T)^2 (MFMA; for G factors the
+// sum of the factors' squared scores), plus the sum of the slice partials,
+// divided, cast to the output type.
 #include <algorithm>
 
 #include "kla_device.hpp"
@@ -52,14 +64,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kDim = 64;                          // d_qk = d_v
-constexpr int kD = kDim * (kDim + 1) / 2;         // 2080
 constexpr int kAcc = kDim + 1;                    // accumulator row: num | den
 // Slice partials of one 16-token tile (bf16): the numerators in MFMA
 // accumulator order [n-tile][lane][4 tokens], then the 16 denominators.
@@ -77,17 +87,6 @@ __device__ __forceinline__ bf16x8 pack8(const float* p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = (__bf16)p[j];
   return r;
-}
-
-// Sum of 8 bf16 products a_j * b_j added to c (four v_dot2 steps).
-__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b, float c) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    bf16x2 x = {a[2 * j], a[2 * j + 1]};
-    bf16x2 y = {b[2 * j], b[2 * j + 1]};
-    c = __builtin_amdgcn_fdot2_f32_bf16(x, y, c, false);
-  }
-  return c;
 }
 
 // x from lane J of this lane's 16-lane row (DPP row broadcast).
@@ -144,7 +143,6 @@ struct Slice {
   static constexpr int kTiles = S == 8 ? 2 * kBP : kBP;
   static constexpr int kPairs = kTiles / 2;
   static constexpr int kJ = S == 8 ? 2 : 1;  // values of j in a slice
-  static constexpr int kMaxU = (kTiles + 3) / 4;
   __host__ __device__ static constexpr int bp(int u) { return factor_bp(G, S == 8 ? u >> 1 : u); }
   __host__ __device__ static constexpr int jj(int u) { return S == 8 ? (u & 1) : 0; }
   __host__ __device__ static constexpr int X(int u) { return bp_x(bp(u)); }
