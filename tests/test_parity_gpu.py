@@ -479,7 +479,8 @@ def _hybrid_check(K, c, heads, dtype, rtol, eps=0.0, out_dtype=None):
 
 
 @pytest.mark.parametrize("d,W,lam,R,T", [(16, 32, 8, 16, 300), (64, 64, 16, 16, 410),
-                                         (32, 48, 20, 8, 257), (64, 128, 64, 64, 700)])
+                                         (32, 48, 20, 8, 257), (64, 128, 64, 64, 700),
+                                         (64, 96, 32, 64, 2100)])
 def test_hybrid_small_bf16(K, d, W, lam, R, T):
     c = S.hybrid_case("small", 1, 2, T, d, W, lam, R, seed=60 + d + T, dup_frac=0.1)
     _hybrid_check(K, c, [(0, 0), (0, 1)], torch.bfloat16, RTOL_BF16)
