@@ -131,9 +131,10 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
 /* ------------------------------------------------------------------------
  * kla_prefill_factors - kla_prefill with the concatenated multi-factor lift
  * (KATA §2.3, "Variantes": KATA-Mg; the factors read as g equal slices of the
- * 64 dimensions, see kla_prefill_quadratic_factors below). The state holds
+ * d_qk dimensions, see kla_prefill_quadratic_factors below). The state holds
  * only the features inside each factor:
- *   D_g = g p (p + 1) / 2 features, p = 64 / g  (2080, 1056, 544 for g = 1, 2, 4),
+ *   D_g = g p (p + 1) / 2 features, p = d_qk / g  (2080, 1056, 544 for
+ *   d_qk = 64 and g = 1, 2, 4),
  * laid out factor by factor, each block in the vec_sym order of kla_prefill
  * (upper triangle row-major, sqrt(2) off the diagonal) over its p dimensions;
  * H0/s0/H_T/s_T are [N, D_g, d_v] and [N, D_g] float32. The outputs are those
@@ -145,8 +146,8 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
  *   factors : 1, 2 or 4 (1 is kla_prefill).
  *   other arguments and the workspace: as for kla_prefill
  *             (kla_prefill_workspace_size of the same shape and chunk).
- * Supported for factors > 1: the bf16 matrix path (d_qk = d_v = 64, bf16
- * inputs); other shapes return KLA_ERR_UNSUPPORTED.
+ * Every shape kla_prefill supports: bf16 inputs with d_qk = d_v = 64 run on
+ * the matrix path, the rest on the float32 vector path (1e-4 relative).
  * ------------------------------------------------------------------------ */
 KLA_API kla_status_t kla_prefill_factors(const kla_shape_t* shp, int chunk, int kind, int factors,
                                          const void* q, const void* k, const void* v, void* o,

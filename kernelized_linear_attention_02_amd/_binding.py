@@ -181,7 +181,7 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     bfloat16, same dtype). ``state`` = (H0, s0) float32 resumes a previous call.
     Returns o, or (o, H_T, s_T) with ``return_state``; with ``outputs=False``
     only (H_T, s_T). ``factors`` > 1 selects the concatenated multi-factor
-    lift KATA-Mg (kla_prefill_factors; bf16, d = 64), whose state has
+    lift KATA-Mg (kla_prefill_factors; any supported shape), whose state has
     factor_phi_dim(d_qk, factors) features."""
     torch = _torch()
     lib = load_library()

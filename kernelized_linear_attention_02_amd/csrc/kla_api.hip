@@ -311,8 +311,6 @@ kla_status_t prefill_call(const char* fn, const kla_shape_t* shp, int chunk, int
   a.HT = H_T;
   a.sT = s_T;
   a.factors = factors;
-  if (factors != 1 && !kla::prefill_mfma_supported(a))
-    return fail(KLA_ERR_UNSUPPORTED, "%s: %d factors need d_qk = d_v = 64 and bf16 inputs", fn, factors);
   const size_t need = prefill_ws(a);
   st = check_ws(need, ws, ws_bytes, fn);
   if (st != KLA_OK) return st;

@@ -6,7 +6,11 @@
 //
 // This is the general path: any supported (d_qk, d_v, chunk), float32 or
 // bf16 inputs, float32 arithmetic throughout (1e-4 relative parity). It is
-// also the state builder for decode (state-only mode, no outputs).
+// also the state builder for decode (state-only mode, no outputs). With G > 1
+// factors (KATA-Mg, KATA §2.3 "Variantes", read as G equal slices of the
+// d_qk dimensions with their rank-one lifts concatenated) the features are
+// the pairs inside each factor, factor by factor, and the intra-chunk weight
+// is the sum of the factors' squared scores.
 //
 // Work split. The state of one head is D x d_v floats (D = d_qk(d_qk+1)/2),
 // too large for one CU at d_qk = 64, so every head is split into S feature
@@ -25,12 +29,21 @@ constexpr int kThreads = 256;
 constexpr int kMaxSlice = 256;  // features per slice
 constexpr int kTok = 16;        // token tile
 
+// Pair (a, b) of feature f of the G-factor lift over d dimensions (G = 1:
+// the rank-one lift), packed as a | (b << 8).
+__device__ __forceinline__ uint16_t factor_pair(int f, int d, int G) {
+  const int p = d / G;
+  const int dp = p * (p + 1) / 2;
+  const int fi = f / dp;
+  const uint16_t ab = phi_pair(f - fi * dp, p);
+  return static_cast<uint16_t>(ab + (fi * p) * 0x0101);
+}
+
 template <int DQK, int DV, typename Tin>
 __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, int T,
     int chunk, int S, int Fs, const float* __restrict__ H0, const float* __restrict__ s0,
-    float* __restrict__ HT, float* __restrict__ sT, float* __restrict__ part) {
-  constexpr int D = phi_dim(DQK);
+    float* __restrict__ HT, float* __restrict__ sT, float* __restrict__ part, int D, int factors) {
   constexpr int G = kThreads / DV;    // feature groups
   constexpr int J = kMaxSlice / G;    // features per thread
   constexpr int W = kThreads / 64;    // waves
@@ -49,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
   __shared__ float red[kTok][G][DV];
   __shared__ float rden[kTok][W];
 
-  build_phi_table(tab, f0, fcount, DQK);
+  for (int i = threadIdx.x; i < fcount; i += blockDim.x) tab[i] = factor_pair(f0 + i, DQK, factors);
 
   float h[J];
 #pragma unroll
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
 template <int DQK, int DV, typename Tin, typename Tout>
 __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    Tout* __restrict__ o, int T, int chunk, int S, const float* __restrict__ part, float eps) {
+    Tout* __restrict__ o, int T, int chunk, int S, const float* __restrict__ part, float eps, int factors) {
   constexpr int QB = 16;
   constexpr int KB = 32;
   constexpr int M = DV / 16;
@@ -183,11 +196,18 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(
     __syncthreads();
     for (int i = tid; i < QB * KB; i += kThreads) {
       const int qq = i / KB, kk = i % KB;
-      float dot = 0.0f;
+      // sum over the factors (p dimensions each) of the squared factor scores
+      const int pm = DQK / factors - 1;
+      float dot = 0.0f, wsum = 0.0f;
 #pragma unroll
-      for (int d = 0; d < DQK; ++d) dot += qs[qq][d] * ks[kk][d];
+      for (int d = 0; d < DQK; ++d) {
+        dot += qs[qq][d] * ks[kk][d];
+        const bool end = ((d + 1) & pm) == 0;
+        wsum += end ? dot * dot : 0.0f;
+        dot = end ? 0.0f : dot;
+      }
       const bool ok = (kk < nk) && (kt + kk <= t0 + qq) && (qq < nq);
-      w[qq][kk] = ok ? dot * dot : 0.0f;
+      w[qq][kk] = ok ? wsum : 0.0f;
     }
     __syncthreads();
     for (int kk = 0; kk < nk; ++kk) {
@@ -217,9 +237,15 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(
 
 int slices_for(int D) { return (D + kMaxSlice - 1) / kMaxSlice; }
 
+// features of the G-factor lift over d dimensions
+int factor_dim(int d, int G) {
+  const int p = d / G;
+  return G * p * (p + 1) / 2;
+}
+
 template <int DQK, int DV, typename Tin, typename Tout>
 hipError_t launch_typed(const PrefillArgs& a, void* ws, hipStream_t st) {
-  constexpr int D = phi_dim(DQK);
+  const int D = factor_dim(DQK, a.factors);
   const int S = slices_for(D);
   const int Fs = (D + S - 1) / S;
   float* part = a.o ? static_cast<float*>(ws) : nullptr;
@@ -227,14 +253,14 @@ hipError_t launch_typed(const PrefillArgs& a, void* ws, hipStream_t st) {
   hipLaunchKernelGGL((prefill_slice_kernel<DQK, DV, Tin>), dim3(S, a.N), dim3(kThreads), 0, st,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), a.T, a.chunk, S, Fs, a.H0, a.s0, a.HT, a.sT,
-                     part);
+                     part, D, a.factors);
   prof_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.o) return e;
   hipLaunchKernelGGL((prefill_combine_kernel<DQK, DV, Tin, Tout>), dim3((a.T + 15) / 16, a.N),
                      dim3(kThreads), 0, st, static_cast<const Tin*>(a.q),
                      static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
-                     static_cast<Tout*>(a.o), a.T, a.chunk, S, part, a.eps);
+                     static_cast<Tout*>(a.o), a.T, a.chunk, S, part, a.eps, a.factors);
   return hipGetLastError();
 }
 
@@ -267,6 +293,7 @@ size_t prefill_valu_workspace(const PrefillArgs& a) {
 }
 
 hipError_t prefill_valu_launch(const PrefillArgs& a, void* ws, hipStream_t st) {
+  if (a.factor_kind != 0 || (a.factors != 1 && a.factors != 2 && a.factors != 4)) return hipErrorInvalidValue;
   switch (a.dqk) {
     case 16: return launch_dv<16>(a, ws, st);
     case 32: return launch_dv<32>(a, ws, st);

@@ -198,9 +198,7 @@ def test_prefill_factors_rejects(lib):
     for g in (0, 3, 8):
         assert go(g=g) == B.KLA_ERR_INVALID_ARGUMENT
     assert go(chunk=48) == B.KLA_ERR_UNSUPPORTED
-    # factors > 1 only on the bf16 matrix path
-    assert go(shape=ctypes.byref(_shape(in_dtype=B.KLA_F32))) == B.KLA_ERR_UNSUPPORTED
-    assert go(shape=ctypes.byref(_shape(d_qk=32, d_v=32))) == B.KLA_ERR_UNSUPPORTED
+    assert go(shape=ctypes.byref(_shape(d_qk=48, d_v=32))) == B.KLA_ERR_UNSUPPORTED
     assert go(shape=None) == B.KLA_ERR_INVALID_ARGUMENT
 
 

@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 from kernelized_linear_attention_02_amd import synth as S
-from tests.tolerance import RTOL_BF16, assert_close
+from tests.tolerance import RTOL_BF16, RTOL_F32, assert_close
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -153,3 +153,38 @@ def test_factors_state_form_4x8x4096_full_size(K):
     fk = O.phi_factors(c.k[1, 3], 2, "concat")
     assert_close(host(HT)[1, 3], fk.T @ c.v[1, 3].astype(np.float64), RTOL_BF16, "H_T head (1,3)")
     assert_close(host(sT)[1, 3], fk.sum(axis=0), RTOL_BF16, "s_T head (1,3)")
+
+
+# ---- the concatenated lift on the float32 vector path (float32 inputs, any
+# supported head size): float32 arithmetic throughout, so the fp32 bound
+
+@pytest.mark.parametrize("g", [2, 4])
+@pytest.mark.parametrize("B,H,T,dqk,dv,chunk,eps", [(1, 2, 100, 64, 64, 64, 0.0), (2, 3, 77, 32, 16, 32, 0.2),
+                                                    (1, 2, 300, 16, 64, 128, 0.0), (1, 1, 1, 32, 32, 64, 0.0)])
+def test_factors_f32_every_row(K, g, B, H, T, dqk, dv, chunk, eps):
+    c = S.prefill_case("factors_f32", B, H, T, dqk, dv, chunk, seed=300 + g + T + dqk)
+    f32 = lambda x: dev(x, torch.float32)
+    o, HT, sT = K.prefill(f32(c.q), f32(c.k), f32(c.v), chunk=chunk, eps=eps, return_state=True, factors=g)
+    torch.cuda.synchronize()
+    assert HT.shape == (B, H, K.factor_phi_dim(dqk, g), dv)
+    for b in range(B):
+        for h in range(H):
+            ro, rH, rs = O.prefill_factors_recurrent(c.q[b, h], c.k[b, h], c.v[b, h], g, "concat", eps=eps)
+            assert_close(host(o)[b, h], ro, RTOL_F32, f"o g={g} head ({b},{h})")
+            assert_close(host(HT)[b, h], rH, RTOL_F32, f"H_T g={g} head ({b},{h})")
+            assert_close(host(sT)[b, h], rs, RTOL_F32, f"s_T g={g} head ({b},{h})")
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_factors_f32_resume_and_bf16_out(K, g):
+    # resuming from a carried state, and the bf16 output of float32 inputs
+    c = S.prefill_case("factors_f32_resume", 1, 2, 260, 32, 32, 64, seed=77 + g)
+    q, k, v = (dev(x, torch.float32) for x in (c.q, c.k, c.v))
+    T1 = 100
+    o1, H1, s1 = K.prefill(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], chunk=64, return_state=True, factors=g)
+    o2 = K.prefill(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], chunk=32, state=(H1, s1), factors=g)
+    ob = K.prefill(q, k, v, chunk=64, out_dtype=torch.bfloat16, factors=g)
+    for h in range(2):
+        ro = O.prefill_factors_bruteforce(c.q[0, h], c.k[0, h], c.v[0, h], g, "concat")
+        assert_close(host(torch.cat([o1, o2], dim=2))[0, h], ro, RTOL_F32, f"resumed o head {h}")
+        assert_close(host(ob)[0, h], ro, RTOL_BF16, f"bf16 out head {h}")
