@@ -591,11 +591,42 @@ struct FinishLds {
   uint16_t qs[C][kDim + 8];
   uint16_t ks[C][kDim + 8];
   uint16_t vt[kDim][C + 8];
-  uint16_t at[C][C + 8];
-  float den[C];
 };
 
+// Weights of one 16-key x 16-query tile, key-major: the lane with query
+// column l16 and group q4 gets keys 4 q4 + i of the tile. (q . k)^2, or for
+// G factors the sum of the factors' squared scores.
+template <int C, int G>
+__device__ __forceinline__ f32x4 finish_weights(const FinishLds<C>& sh, int kq, int mq, int l16, int q4) {
+  f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (G == 4) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const s16x4 A = *reinterpret_cast<const s16x4*>(&sh.ks[kq * 16 + l16][16 * f + 4 * q4]);
+      const s16x4 B = *reinterpret_cast<const s16x4*>(&sh.qs[mq * 16 + l16][16 * f + 4 * q4]);
+      const f32x4 s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      w4 += s4 * s4;
+    }
+  } else {
+    f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDim / 32; ++ks) {
+      const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.ks[kq * 16 + l16][ks * 32 + 8 * q4]);
+      const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.qs[mq * 16 + l16][ks * 32 + 8 * q4]);
+      s4 = mfma(A, B, G == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : s4);
+      if (G == 2) w4 += s4 * s4;
+    }
+    if (G == 1) w4 = s4 * s4;
+  }
+  return w4;
+}
+
 // One work-group per (chunk, head): intra-chunk term + accumulator -> output.
+// The weights are formed transposed (keys as MFMA rows), so the accumulator
+// of two 16-key tiles already is the A operand of the 32-key step of A [V | 1]
+// when its k-slots are read as keys 4 q4 + i (i < 4) of the first tile and
+// 4 q4 + i - 4 of the second; the value fragments take the same key order.
+// The weights never leave registers.
 template <int C, typename Tout, int G>
 __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -630,74 +661,47 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
       sh.vt[p + 2 * e + 1][t] = (uint16_t)(vw[e] >> 16);
     }
   }
-  for (int i = tid; i < C; i += kThreads) sh.den[i] = 0.0f;
-  __syncthreads();
-
-  // A = lower-triangular (Q K^T)^2 for the query tiles of this wave; each
-  // query tile mq needs key tiles up to the end of its 32-key step.
-  for (int mq = w; mq < C / 16; mq += kWaves) {
-    const int kmax = ((mq >> 1) << 1) + 1;  // last key tile of the 32-key step
-    float den_part[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int kq = 0; kq <= kmax && kq < C / 16; ++kq) {
-      // lane holds the weight of query mq*16 + 4*q4 + i and key kq*16 + l16:
-      // (q . k)^2, or the sum over the G factors of (q_f . k_f)^2
-      f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (G == 4) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const s16x4 A = *reinterpret_cast<const s16x4*>(&sh.qs[mq * 16 + l16][16 * f + 4 * q4]);
-          const s16x4 B = *reinterpret_cast<const s16x4*>(&sh.ks[kq * 16 + l16][16 * f + 4 * q4]);
-          const f32x4 s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          w4 += s4 * s4;
-        }
-      } else {
-        f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kDim / 32; ++ks) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.qs[mq * 16 + l16][ks * 32 + 8 * q4]);
-          const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.ks[kq * 16 + l16][ks * 32 + 8 * q4]);
-          s4 = mfma(A, B, G == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : s4);
-          if (G == 2) w4 += s4 * s4;
-        }
-        if (G == 1) w4 = s4 * s4;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = mq * 16 + 4 * q4 + i;
-        const int ki = kq * 16 + l16;
-        const float sq = w4[i];
-        const float a = (ki <= qi && ki < L) ? sq : 0.0f;
-        den_part[i] += a;
-        sh.at[qi][ki] = __builtin_bit_cast(uint16_t, (__bf16)a);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float d = den_part[i];
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) d += __shfl_xor(d, off, 64);
-      if (l16 == 0) sh.den[mq * 16 + 4 * q4 + i] = d;
-    }
-  }
   __syncthreads();
 
   for (int mq = w; mq < C / 16; mq += kWaves) {
     f32x4 ra[4];
 #pragma unroll
     for (int nt4 = 0; nt4 < 4; ++nt4) ra[nt4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // this lane's query (column) and its running denominator over its keys
+    const int qi = mq * 16 + l16;
+    float dpart = 0.0f;
     for (int ks = 0; ks <= (mq >> 1); ++ks) {
-      const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.at[mq * 16 + l16][ks * 32 + 8 * q4]);
+      bf16x8 A;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kq = 2 * ks + h;
+        const f32x4 w4 = finish_weights<C, G>(sh, kq, mq, l16, q4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ki = kq * 16 + 4 * q4 + i;
+          const float a = (ki <= qi && ki < L) ? w4[i] : 0.0f;
+          dpart += a;
+          A[4 * h + i] = (__bf16)a;
+        }
+      }
 #pragma unroll
       for (int nt4 = 0; nt4 < 4; ++nt4) {
-        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.vt[16 * nt4 + l16][ks * 32 + 8 * q4]);
+        const uint16_t* vr = &sh.vt[16 * nt4 + l16][ks * 32 + 4 * q4];
+        const bf16x4 b0 = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 b1 = *reinterpret_cast<const bf16x4*>(vr + 16);
+        const bf16x8 B = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
         ra[nt4] = mfma(A, B, ra[nt4]);
       }
     }
+    // the lanes of one query column hold disjoint keys: add the four groups,
+    // then fetch the denominators of the accumulator rows 4 q4 + i
+    dpart += __shfl_xor(dpart, 16, 64);
+    dpart += __shfl_xor(dpart, 32, 64);
     // lane holds O_in[query mq*16 + 4*q4 + i][value 16*nt4 + l16]; the slice
     // partials hold four consecutive tokens of one column as bf16
     float den[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) den[i] = sh.den[mq * 16 + 4 * q4 + i] + eps;
+    for (int i = 0; i < 4; ++i) den[i] = __shfl(dpart, 4 * q4 + i, 64) + eps;
     const uint16_t* pc = part + ((size_t)(n * gridDim.x + blockIdx.x) * S * (C / 16) + mq) * kTileAcc;
     // the slices' loads are independent: keep several in flight
 #pragma unroll 4
