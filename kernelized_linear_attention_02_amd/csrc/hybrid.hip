@@ -356,14 +356,17 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
 // error): for candidate c and the work-group's feature k-steps,
 //   num_c = sum_f phi_f(k_c) H_f,   den_c = sum_f phi_f(k_c) s_f,
 // written to part[((n Z + z) pstride + c) 68 + {0..63, 64}] for the
-// selection to add over z. Grid (heads, candidate blocks of 64, Z); wave w
-// takes k-steps z 65 / Z + w, + 4, ... The B operands are the state
-// fragments the fold wrote (three exact bf16 pieces h0 + h1 + h2, rows in
-// the fold's order: lane quarter q4 holds features 32 ks + 4 q4 + j and
-// 32 ks + 16 + 4 q4 + j, j < 4); the candidate features, in the same order,
-// are split into two pieces p0 + p1 and the product is taken as
-// p0 (h0 + h1 + h2) + p1 h0 in float32 (dropped terms below 2^-16
-// relative). Denominators stay in float32 on the vector units.
+// selection to add over z. Grid (heads, candidate blocks of 64, Z); slices
+// z < zs sum the state's feature k-steps (wave w takes k-steps
+// z 65 / zs + w, + 4, ...), slice zs (when Z > zs) adds the pairs folded by
+// the previous refresh in closed form (hyb_score_correction). The B operands
+// are the state fragments the fold wrote (three exact bf16 pieces
+// h0 + h1 + h2, rows in the fold's order: lane quarter q4 holds features
+// 32 ks + 4 q4 + j and 32 ks + 16 + 4 q4 + j, j < 4); the candidate features,
+// in the same order, are split into two pieces p0 + p1 and the product is
+// taken as p0 (h0 + h1 + h2) + p1 h0 in float32 (dropped terms below 2^-16
+// relative). Denominators stay in float32 on the vector units, with s read
+// back exactly from its three pieces in n-tile 4 of the fragments.
 constexpr int kScoreCand = 64;
 struct ScoreLds {
   uint16_t tab[kFPhi];
@@ -373,34 +376,155 @@ struct ScoreLds {
     float4 red[4][4][64];            // numerator partials, accumulator layout
   };
 };
+struct CorrLds {
+  uint16_t kc[kScoreCand][kFD + 8];  // candidate keys (bf16 rows)
+  uint16_t kr[kFoldRows][kFD + 8];   // folded keys (bf16 rows, zero past the count)
+  uint16_t vt[kFD][kFoldRows + 8];   // folded values, transposed
+};
+union ScoreShared {
+  ScoreLds s;
+  CorrLds c;
+};
 
-__global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
-    const uint4* __restrict__ HF, const float* __restrict__ s, const uint16_t* __restrict__ k, int T,
-    const int32_t* __restrict__ cache, int cstride, int n_cache, int ev0, int n_cand,
-    float* __restrict__ part, int pstride) {
-  __shared__ __align__(16) ScoreLds sh;
-  const int n = blockIdx.x;
-  const int cbase = kScoreCand * blockIdx.y;
+// Token of refresh candidate c: the cache entries, then the evicted tokens.
+__device__ __forceinline__ int candidate_token(const int32_t* cache_n, int n_cache, int ev0, int c) {
+  return c < n_cache ? cache_n[c] : ev0 + (c - n_cache);
+}
+
+// Slice zs of the scorer: the pairs j that the previous refresh folded, whose
+// fold the state fragments it reads do not hold yet. phi(k_c) . phi(k_j) =
+// (k_c . k_j)^2 (KATA §2.2), so they add
+//   num_c += sum_j (k_c . k_j)^2 v_j,   den_c += sum_j (k_c . k_j)^2.
+// S^T = K_j K_c^T on bf16 MFMA (exact products, float32 sums), squared in
+// float32; the squares are split into three exact bf16 pieces for the product
+// with V (bf16), so the numerators are float32 sums of exact products, as in
+// a fold; the denominators are float32 sums. Wave w takes candidates
+// 16 w .. 16 w + 15 of the block; the A operand of a 32-pair step is the two
+// 16-pair score tiles as the lanes hold them (pairs 4 q4 + i of each), and
+// the value fragments take the same pair order.
+__device__ __forceinline__ void hyb_score_correction(
+    CorrLds& sh, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T, int n,
+    const int32_t* __restrict__ cache_n, int n_cache, int ev0, int n_cand, int cbase,
+    const int32_t* __restrict__ rej_n, int n_rej, float* __restrict__ pz) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
-  const int Z = gridDim.z;
-  const int tz0 = (int)((blockIdx.z * kFKS) / Z);
-  const int tz1 = (int)(((blockIdx.z + 1) * kFKS) / Z);
-  const float* sn = s + (size_t)n * kFPhi;
+  const int R = (n_rej + 31) & ~31;
+  for (int i = tid; i < kScoreCand * (kFD / 8); i += kThreads) {
+    const int c = i >> 3, p = (i & 7) * 8;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (cbase + c < n_cand) {
+      const int tok = candidate_token(cache_n, n_cache, ev0, cbase + c);
+      u = *reinterpret_cast<const uint4*>(k + ((size_t)n * T + tok) * kFD + p);
+    }
+    *reinterpret_cast<uint4*>(&sh.kc[c][p]) = u;
+  }
+  for (int i = tid; i < R * (kFD / 8); i += kThreads) {
+    const int j = i >> 3, p = (i & 7) * 8;
+    uint4 ku = make_uint4(0, 0, 0, 0), vu = ku;
+    if (j < n_rej) {
+      const size_t row = ((size_t)n * T + rej_n[j]) * kFD + p;
+      ku = *reinterpret_cast<const uint4*>(k + row);
+      vu = *reinterpret_cast<const uint4*>(v + row);
+    }
+    *reinterpret_cast<uint4*>(&sh.kr[j][p]) = ku;
+    const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sh.vt[p + 2 * e][j] = (uint16_t)(vw[e] & 0xFFFF);
+      sh.vt[p + 2 * e + 1][j] = (uint16_t)(vw[e] >> 16);
+    }
+  }
+  __syncthreads();
 
-  auto load_b = [&](int ks, uint4 (&b)[3][4], float4 (&sv)[2]) {
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dpart = 0.0f;
+  for (int jj = 0; jj < R / 32; ++jj) {
+    float x[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int jt = 2 * jj + h;
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kFD / 32; ++ks) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.kr[16 * jt + l16][32 * ks + 8 * q4]);
+        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.kc[16 * w + l16][32 * ks + 8 * q4]);
+        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, s4, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float wgt = 16 * jt + 4 * q4 + i < n_rej ? s4[i] * s4[i] : 0.0f;
+        dpart += wgt;
+        x[4 * h + i] = wgt;
+      }
+    }
+    bf16x8 A0, A1, A2;
+    split3_8(x, A0, A1, A2);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint16_t* vr = &sh.vt[16 * nt + l16][32 * jj + 4 * q4];
+      const uint2 b0 = *reinterpret_cast<const uint2*>(vr);
+      const uint2 b1 = *reinterpret_cast<const uint2*>(vr + 16);
+      const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y));
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, B, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B, acc[nt], 0, 0, 0);
+    }
+  }
+  // lanes of one candidate column hold disjoint pairs
+  dpart += __shfl_xor(dpart, 16, 64);
+  dpart += __shfl_xor(dpart, 32, 64);
+  // lane (l16, q4) holds candidates 16 w + 4 q4 + i at value column 16 nt + l16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 16 * w + 4 * q4 + i;
+    if (cbase + c < n_cand) {
+      float* pc = pz + (size_t)(cbase + c) * 68;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) pc[16 * nt + l16] = acc[nt][i];
+    }
+  }
+  if (q4 == 0 && cbase + 16 * w + l16 < n_cand) pz[(size_t)(cbase + 16 * w + l16) * 68 + 64] = dpart;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
+    const uint4* __restrict__ HF, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T,
+    const int32_t* __restrict__ cache, int cstride, int n_cache, int ev0, int n_cand,
+    const int32_t* __restrict__ rej, int rstride, int n_rej, int zs, float* __restrict__ part, int pstride) {
+  __shared__ __align__(16) ScoreShared shu;
+  const int n = blockIdx.x;
+  const int cbase = kScoreCand * blockIdx.y;
+  const int Z = gridDim.z;
+  if ((int)blockIdx.z == zs) {
+    hyb_score_correction(shu.c, k, v, T, n, cache + (size_t)n * cstride, n_cache, ev0, n_cand, cbase,
+                         rej + (size_t)n * rstride, n_rej, part + ((size_t)n * Z + zs) * pstride * 68);
+    return;
+  }
+  ScoreLds& sh = shu.s;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int tz0 = (int)((blockIdx.z * kFKS) / zs);
+  const int tz1 = (int)(((blockIdx.z + 1) * kFKS) / zs);
+
+  // B fragments of k-step ks, and the three pieces of s for this lane's
+  // features (n-tile 4, lane column 0 of the lane's quarter)
+  auto load_b = [&](int ks, uint4 (&b)[3][4], uint4 (&sv)[3]) {
 #pragma unroll
     for (int pc = 0; pc < 3; ++pc)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) b[pc][nt] = HF[hf_index(n, ks, pc, nt, lane)];
-    sv[0] = *reinterpret_cast<const float4*>(sn + 32 * ks + 4 * q4);
-    sv[1] = *reinterpret_cast<const float4*>(sn + 32 * ks + 16 + 4 * q4);
+#pragma unroll
+    for (int pc = 0; pc < 3; ++pc) sv[pc] = HF[hf_index(n, ks, pc, 4, 16 * q4)];
   };
   uint4 bf[3][4];
-  float4 sv[2];
+  uint4 sv[3];
   const int ks_first = min(tz0 + w, kFKS - 1);
   load_b(ks_first, bf, sv);
 
@@ -412,8 +536,7 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[j] = 0.0f;
     if (cbase + c < n_cand) {
-      const int cc = cbase + c;
-      const int tok = cc < n_cache ? cache[(size_t)n * cstride + cc] : ev0 + (cc - n_cache);
+      const int tok = candidate_token(cache + (size_t)n * cstride, n_cache, ev0, cbase + c);
       const uint4* kp = reinterpret_cast<const uint4*>(k + ((size_t)n * T + tok) * kFD + 16 * qd);
       const uint4 u0 = kp[0], u1 = kp[1];
       const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
@@ -440,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
 #pragma unroll 1
   for (int ks = tz0 + w; ks < tz1; ks += kWavesF) {
     uint4 bn[3][4];
-    float4 svn[2];
+    uint4 svn[3];
     const bool more = ks + kWavesF < tz1;
     if (more) load_b(ks + kWavesF, bn, svn);
     // this lane's eight features and their weights
@@ -456,7 +579,14 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
       pb[j] = u >> 8;
       wt[j] = pa[j] == pb[j] ? 1.0f : 1.41421356237309504880f;
     }
-    const float sj[8] = {sv[0].x, sv[0].y, sv[0].z, sv[0].w, sv[1].x, sv[1].y, sv[1].z, sv[1].w};
+    // s from its pieces: (p0 + p1) + p2 restores the float32 value exactly
+    float sj[8];
+    {
+      const bf16x8 s0 = __builtin_bit_cast(bf16x8, sv[0]), s1 = __builtin_bit_cast(bf16x8, sv[1]),
+                   s2 = __builtin_bit_cast(bf16x8, sv[2]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sj[j] = ((float)s0[j] + (float)s1[j]) + (float)s2[j];
+    }
     bf16x8 B[3][4];
 #pragma unroll
     for (int pc = 0; pc < 3; ++pc)
@@ -488,8 +618,8 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
       for (int pc = 0; pc < 3; ++pc)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) bf[pc][nt] = bn[pc][nt];
-      sv[0] = svn[0];
-      sv[1] = svn[1];
+#pragma unroll
+      for (int pc = 0; pc < 3; ++pc) sv[pc] = svn[pc];
     }
   }
 
@@ -1183,10 +1313,10 @@ struct Ws {
   int32_t* cache2;  // second cache buffer (matrix-core path only)
   float* scores;
   int32_t* rejected;
-  uint4* HF;   // readout fragments of the state (matrix-core path only) ...
-  uint4* HF2;  // ... and their second buffer
+  int32_t* rejected2;  // second rejected list (matrix-core path only)
+  uint4* HF[3];  // state fragments, three versions (matrix-core path only)
   float* xp;  // readout split partials [N][refresh][kRNS][66] (matrix-core path only)
-  float* sp;  // score split partials [N][kSZ][kCStride][68] (matrix-core path only)
+  float* sp;  // score split partials [N][kSZ + 1][kCStride][68] (matrix-core path only)
 };
 
 bool matrix_path(const HybridArgs& a) { return a.dqk == 64 && a.dv == 64 && a.in_bf16; }
@@ -1196,7 +1326,8 @@ size_t xp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * a.refresh *
 
 constexpr int kCStride = kCandMax;
 constexpr int kSZ = 5;  // score splits of the feature sum per (head, candidate block)
-size_t sp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kSZ * kCStride * 68 * sizeof(float)); }
+// plus one slice for the pairs the previous refresh folded
+size_t sp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * (kSZ + 1) * kCStride * 68 * sizeof(float)); }
 
 Ws carve(const HybridArgs& a, void* ws) {
   const int D = phi_dim(a.dqk);
@@ -1225,10 +1356,16 @@ Ws carve(const HybridArgs& a, void* ws) {
   p += align_up((size_t)a.N * kCStride * sizeof(float));
   w.rejected = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
-  w.HF = matrix_path(a) ? reinterpret_cast<uint4*>(p) : nullptr;
-  if (w.HF) p += hf_bytes(a);
-  w.HF2 = matrix_path(a) ? reinterpret_cast<uint4*>(p) : nullptr;
-  if (w.HF2) p += hf_bytes(a);
+  w.rejected2 = nullptr;
+  for (uint4*& h : w.HF) h = nullptr;
+  if (matrix_path(a)) {
+    w.rejected2 = reinterpret_cast<int32_t*>(p);
+    p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
+    for (uint4*& h : w.HF) {
+      h = reinterpret_cast<uint4*>(p);
+      p += hf_bytes(a);
+    }
+  }
   w.xp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
   if (w.xp) p += xp_bytes(a);
   w.sp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
@@ -1305,12 +1442,17 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
   return hipSuccess;
 }
 
-// A second stream per device for the readouts of the matrix-core path, and
-// the events that order it against the caller's stream. Default priority.
+// Two more streams per device for the matrix-core path (the readouts, the
+// folds) and the events that order them against the caller's stream.
+// Default priority.
 struct SideStream {
   std::mutex mu;
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, ready = nullptr, used[2] = {nullptr, nullptr};
+  hipStream_t s = nullptr;  // readouts
+  hipStream_t f = nullptr;  // folds
+  hipEvent_t fork = nullptr, join = nullptr, fjoin = nullptr, ready = nullptr, selected = nullptr;
+  hipEvent_t used[2] = {nullptr, nullptr};                // cache buffer x last read by a readout
+  hipEvent_t hf_used[3] = {nullptr, nullptr, nullptr};    // fragment buffer x last read by a readout
+  hipEvent_t folded[3] = {nullptr, nullptr, nullptr};     // fragment buffer x written by its fold
 };
 
 hipError_t side_stream(SideStream** out) {
@@ -1323,27 +1465,37 @@ hipError_t side_stream(SideStream** out) {
   static std::mutex init_mu;
   std::lock_guard<std::mutex> g(init_mu);
   if (!ss.s) {
-    hipStream_t s;
-    if ((e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking)) != hipSuccess) return e;
-    hipEvent_t* evs[5] = {&ss.fork, &ss.join, &ss.ready, &ss.used[0], &ss.used[1]};
+    hipStream_t sr, sf;
+    if ((e = hipStreamCreateWithFlags(&sf, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&sr, hipStreamNonBlocking)) != hipSuccess) return e;
+    hipEvent_t* evs[13] = {&ss.fork,       &ss.join,       &ss.fjoin,      &ss.ready,     &ss.selected,
+                           &ss.used[0],    &ss.used[1],    &ss.hf_used[0], &ss.hf_used[1], &ss.hf_used[2],
+                           &ss.folded[0],  &ss.folded[1],  &ss.folded[2]};
     for (hipEvent_t* p : evs)
       if ((e = hipEventCreateWithFlags(p, hipEventDisableTiming)) != hipSuccess) return e;
-    ss.s = s;
+    ss.f = sf;
+    ss.s = sr;
   }
   *out = &ss;
   return hipSuccess;
 }
 
-// The matrix-core path (d = 64, bf16 in). The refresh chain (score, select,
-// fold, or append) runs on the caller's stream; each block's readout and
-// combine run on the side stream once the chain has produced the block's
-// state and cache. The fold writes the state fragments and the selection
-// writes the cache into the buffer the previous block's readout does not
-// read (two of each, swapped at every refresh), so the readout of block b
-// overlaps the scoring and selection of block b + 1; a buffer is rewritten
-// only after the readout that last read it has finished (event used[x]).
+// The matrix-core path (d = 64, bf16 in). Three streams:
+//   st: the refresh chain, scoring and selection (or the append);
+//   the fold stream: fold r of the pairs that refresh r rejects;
+//   the readout stream: each block's readout and combine.
+// Scoring at refresh r reads the state after fold r - 2 and adds the pairs of
+// refresh r - 1 in closed form (slice zs of hyb_score_frag_kernel), so fold
+// r - 1 overlaps scoring and selection r instead of preceding them: the
+// chain waits only for fold r - 2. State fragments have three buffers
+// (version r in buffer r mod 3; the zero state before the first fold in
+// buffers 1 and 2): scoring reads version r - 2, the readouts version r - 1
+// or r, the fold writes version r. The cache and the rejected list have two
+// buffers each. A buffer is rewritten only after the last kernel that read it
+// has finished (events used, hf_used; stream order elsewhere). The host knows
+// every count in advance, so nothing is read back.
 template <typename Tout>
-hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
+hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStream* ss, bool prof) {
   const Ws w = carve(a, ws);
   const int N = a.N;
   const int nblocks = (a.T + a.refresh - 1) / a.refresh;
@@ -1351,11 +1503,9 @@ hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
   const uint16_t* k = static_cast<const uint16_t*>(a.k);
   const uint16_t* v = static_cast<const uint16_t*>(a.v);
   Tout* o = static_cast<Tout*>(a.o);
-  SideStream* ss = nullptr;
-  hipError_t e = side_stream(&ss);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> g(ss->mu);
+  hipError_t e = hipSuccess;
   const hipStream_t sb = ss->s;
+  const hipStream_t sf = ss->f;
 #define KLA_TRY(x)                       \
   do {                                   \
     e = (x);                             \
@@ -1363,32 +1513,39 @@ hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
   } while (0)
 #define KLA_CHECK() KLA_TRY(hipGetLastError())
   int32_t* cache[2] = {w.cache, w.cache2};
-  uint4* hf[2] = {w.HF, w.HF2};
+  int32_t* rej[2] = {w.rejected, w.rejected2};
   bool used[2] = {false, false};
+  bool hf_used[3] = {false, false, false};
   hipLaunchKernelGGL(fill_kernel_f32, dim3(1024), dim3(256), 0, st, w.H, (size_t)N * kFPhi * kFD, 0.0f);
   hipLaunchKernelGGL(fill_kernel_f32, dim3(64), dim3(256), 0, st, w.s, (size_t)N * kFPhi, 0.0f);
   hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, cache[0], (size_t)N * kCStride, -1);
   hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, cache[1], (size_t)N * kCStride, -1);
-  hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, reinterpret_cast<int32_t*>(hf[0]),
-                     hf_bytes(a) / sizeof(int32_t), 0);
+  for (uint4* h : w.HF)
+    hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, reinterpret_cast<int32_t*>(h),
+                       hf_bytes(a) / sizeof(int32_t), 0);
   if (a.trace && a.cache_size > 0)
     hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, a.trace,
                        (size_t)N * nblocks * a.cache_size, -1);
   KLA_CHECK();
-  // the side stream starts after everything the caller queued so far
+  // the side streams start after everything the caller queued so far
   KLA_TRY(hipEventRecord(ss->fork, st));
   KLA_TRY(hipStreamWaitEvent(sb, ss->fork, 0));
-  int cur = 0;
-  // everything after the fork also joins the side stream back, on error too
+  KLA_TRY(hipStreamWaitEvent(sf, ss->fork, 0));
+  int cur = 0;   // cache buffer of the current cache
+  int hv = 2;    // fragment buffer of the newest state (the zero state at first)
+  // everything after the fork also joins the side streams back, on error too
   const hipError_t loop_err = [&]() -> hipError_t {
     hipError_t e;
     int n_cache = 0;
     int f_prev = 0;
+    int r = 0;          // refreshes issued
+    int n_rej_prev = 0;  // pairs rejected by refresh r - 1
     for (int b = 0; b < nblocks; ++b) {
       const int b0 = b * a.refresh;
       const int b1 = std::min(a.T, b0 + a.refresh);
       const int f = std::max(0, b0 - a.window);
       const int n_ev = f - f_prev;
+      bool refreshed = false;
       if (n_ev > 0) {
         const int n_cand = n_cache + n_ev;
         if (n_cand <= a.cache_size) {
@@ -1399,46 +1556,68 @@ hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
           n_cache = n_cand;
         } else {
           const int nxt = cur ^ 1;
-          // the cache and fragment buffers about to be rewritten are free
+          const int v_old = (r + 1) % 3;  // version r - 2 (the zero state for r < 2)
+          const int v_new = r % 3;
+          const int n_rej = n_cand - a.cache_size;
+          // the cache buffer about to be rewritten is free, and fold r - 2 is done
           if (used[nxt]) KLA_TRY(hipStreamWaitEvent(st, ss->used[nxt], 0));
-          prof_begin(st);
-          // float32-faithful matrix-core score partials (split bf16 operands)
-          hipLaunchKernelGGL(hyb_score_frag_kernel, dim3(N, (n_cand + kScoreCand - 1) / kScoreCand, kSZ),
-                             dim3(kThreads), 0, st, hf[cur], w.s, k, a.T, cache[cur], kCStride, n_cache, f_prev,
-                             n_cand, w.sp, kCStride);
-          hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ, kCStride, v,
-                             a.T, a.eps, cache[cur], kCStride, cache[nxt], kCStride, n_cache, f_prev, n_cand,
-                             a.cache_size, w.rejected, kCStride, a.trace, (size_t)a.cache_size, b, nblocks,
+          if (r >= 2) KLA_TRY(hipStreamWaitEvent(st, ss->folded[v_old], 0));
+          if (prof) prof_begin(st);
+          // float32-faithful matrix-core score partials (split bf16 operands),
+          // plus the closed-form terms of the pairs refresh r - 1 rejected
+          hipLaunchKernelGGL(hyb_score_frag_kernel, dim3(N, (n_cand + kScoreCand - 1) / kScoreCand, kSZ + 1),
+                             dim3(kThreads), 0, st, w.HF[v_old], k, v, a.T, cache[cur], kCStride, n_cache,
+                             f_prev, n_cand, rej[(r + 1) & 1], kCStride, r > 0 ? n_rej_prev : 0, kSZ, w.sp,
+                             kCStride);
+          hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ + 1, kCStride,
+                             v, a.T, a.eps, cache[cur], kCStride, cache[nxt], kCStride, n_cache, f_prev, n_cand,
+                             a.cache_size, rej[r & 1], kCStride, a.trace, (size_t)a.cache_size, b, nblocks,
                              w.scores, kCStride);
-          prof_end(st);
+          if (prof) prof_end(st);
           KLA_CHECK();
+          // fold r on its own stream, once the selection is done and no
+          // readout still reads the fragment buffer it rewrites
+          KLA_TRY(hipEventRecord(ss->selected, st));
+          KLA_TRY(hipStreamWaitEvent(sf, ss->selected, 0));
+          if (hf_used[v_new]) KLA_TRY(hipStreamWaitEvent(sf, ss->hf_used[v_new], 0));
           hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFKS + kFoldKsPerWG - 1) / kFoldKsPerWG, N),
-                             dim3(kThreads), 0, st, w.H, w.s, hf[nxt], k, v, a.T, w.rejected, kCStride,
-                             n_cand - a.cache_size);
+                             dim3(kThreads), 0, sf, w.H, w.s, w.HF[v_new], k, v, a.T, rej[r & 1], kCStride,
+                             n_rej);
           KLA_CHECK();
+          KLA_TRY(hipEventRecord(ss->folded[v_new], sf));
           n_cache = a.cache_size;
+          n_rej_prev = n_rej;
           cur = nxt;
+          hv = v_new;
+          ++r;
+          refreshed = true;
         }
       }
       f_prev = f;
-      // the block's readout, on the side stream, after the chain so far
+      // the block's readout, on the readout stream, after the chain so far
+      // and the fold of the state it reads
       KLA_TRY(hipEventRecord(ss->ready, st));
       KLA_TRY(hipStreamWaitEvent(sb, ss->ready, 0));
+      if (refreshed) KLA_TRY(hipStreamWaitEvent(sb, ss->folded[hv], 0));
       hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N, kRNS), dim3(kRT), 0,
-                         sb, q, k, v, o, a.T, hf[cur], cache[cur], kCStride, n_cache, b0, b1, f, a.scale, a.eps,
+                         sb, q, k, v, o, a.T, w.HF[hv], cache[cur], kCStride, n_cache, b0, b1, f, a.scale, a.eps,
                          kRNS, w.xp, a.refresh);
       hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>),
                          dim3(((b1 - b0) * kFD + kThreads - 1) / kThreads, N), dim3(kThreads), 0, sb, w.xp,
                          a.refresh, kRNS, o, a.T, b0, b1, a.eps);
       KLA_CHECK();
       KLA_TRY(hipEventRecord(ss->used[cur], sb));
+      KLA_TRY(hipEventRecord(ss->hf_used[hv], sb));
       used[cur] = true;
+      hf_used[hv] = true;
     }
     return hipSuccess;
   }();
-  // the caller's stream continues after the last readout
+  // the caller's stream continues after the last readout and the last fold
   KLA_TRY(hipEventRecord(ss->join, sb));
+  KLA_TRY(hipEventRecord(ss->fjoin, sf));
   KLA_TRY(hipStreamWaitEvent(st, ss->join, 0));
+  KLA_TRY(hipStreamWaitEvent(st, ss->fjoin, 0));
   if (loop_err != hipSuccess) return loop_err;
   if (a.cache_T && a.cache_size > 0) {
     hipLaunchKernelGGL(copy_rows_kernel, dim3(N), dim3(256), 0, st, a.cache_T, a.cache_size,
@@ -1448,6 +1627,15 @@ hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
 #undef KLA_CHECK
 #undef KLA_TRY
   return hipSuccess;
+}
+
+template <typename Tout>
+hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
+  SideStream* ss = nullptr;
+  hipError_t e = side_stream(&ss);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(ss->mu);
+  return enqueue_matrix<Tout>(a, ws, st, ss, true);
 }
 
 template <int DQK, int DV>
@@ -1471,7 +1659,7 @@ size_t hybrid_workspace(const HybridArgs& a) {
   b += align_up((size_t)a.N * kCStride * sizeof(float));
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   if (matrix_path(a))
-    b += align_up((size_t)a.N * kCStride * sizeof(int32_t)) + 2 * hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
+    b += 2 * align_up((size_t)a.N * kCStride * sizeof(int32_t)) + 3 * hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
   return b;
 }
 
