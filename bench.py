@@ -280,10 +280,21 @@ def bench_hybrid(torch, K, S, steps, warmup):
                       cfg["cache_size"], cfg["refresh"], cfg["seed"], threads=16)
     q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (c.q, c.k, c.v))
     fn = lambda: K.hybrid_prefill(q, k, v, cfg["window"], cfg["cache_size"], cfg["refresh"])
-    step_ms, kern_ms, per_call = timed_calls(torch, K, fn, steps, warmup)
+    # the call issues a few kernels and events per 64-token block, so the
+    # library's timing hooks (two more events per refresh) would inflate the
+    # wall time: the plain calls are timed, the hooked ones apart
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    hooked_ms, kern_ms, per_call = timed_calls(torch, K, fn, max(1, steps // 4), 1)
     B, T = cfg["B"], cfg["T"]
     return dict(workload="hybrid_2x16x16384", step_ms=step_ms, tokens_per_s=B * T / (step_ms * 1e-3),
-                score_kernel_ms_per_call=kern_ms * per_call)
+                hooked_step_ms=hooked_ms, refresh_chain_ms_per_call=kern_ms * per_call)
 
 
 def hybrid_decode_step_bytes(N, d, W, lam):

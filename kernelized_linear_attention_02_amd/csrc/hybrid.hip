@@ -14,11 +14,16 @@
 //   fold   : H += phi(k_i) v_i^T, s += phi(k_i) over the rejected tokens;
 //   readout: for the block's queries, window and cache softmax terms and
 //            the linear readout join one numerator and one denominator.
+// On the matrix-core path the score of refresh r reads the state before the
+// fold of refresh r - 1 and adds that fold's pairs in closed form
+// ((k_c . k_j)^2 weights), so the fold of r - 1 and the score of r share one
+// launch (hyb_refresh_kernel).
 // The host knows every count in advance (they depend only on T, window,
 // refresh and cache_size), so no device value is read back.
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
@@ -240,15 +245,20 @@ __device__ __forceinline__ size_t hf_index(int n, int ks, int pc, int nt, int la
   return ((((size_t)n * kFKS + ks) * kHFPieces + pc) * 5 + nt) * 64 + lane;
 }
 
-__global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restrict__ H, float* __restrict__ s,
-                                                               uint4* __restrict__ HF,
-                                                               const uint16_t* __restrict__ k,
-                                                               const uint16_t* __restrict__ v, int T,
-                                                               const int32_t* __restrict__ rejected,
-                                                               int rstride, int n_rej) {
-  __shared__ __align__(16) float kt[kFD][kFoldRows + 4];
-  __shared__ __align__(16) uint16_t vt[kFD][kFoldRows + 8];
-  const int n = blockIdx.y;
+struct FoldLds {
+  float kt[kFD][kFoldRows + 4];
+  uint16_t vt[kFD][kFoldRows + 8];
+};
+constexpr int kFoldWGs = (kFKS + kFoldKsPerWG - 1) / kFoldKsPerWG;  // work-groups per head
+
+// Work-group (bx, n) of the fold: k-steps bx kFoldKsPerWG .. + kFoldKsPerWG - 1 of head n.
+__device__ __forceinline__ void hyb_fold_block(FoldLds& sh, int bx, int n, float* __restrict__ H,
+                                               float* __restrict__ s, uint4* __restrict__ HF,
+                                               const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                               int T, const int32_t* __restrict__ rejected, int rstride,
+                                               int n_rej) {
+  float (&kt)[kFD][kFoldRows + 4] = sh.kt;
+  uint16_t (&vt)[kFD][kFoldRows + 8] = sh.vt;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
   float* sn = s + (size_t)n * kFPhi;
 #pragma unroll 1
   for (int u = 0; u < kFoldKsPerWG / kWavesF; ++u) {
-    const int ks = blockIdx.x * kFoldKsPerWG + u * kWavesF + w;
+    const int ks = bx * kFoldKsPerWG + u * kWavesF + w;
     if (ks >= kFKS) break;
     f32x4 acc[2][5];
 #pragma unroll
@@ -368,6 +378,7 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_mfma_kernel(float* __restri
 // relative). Denominators stay in float32 on the vector units, with s read
 // back exactly from its three pieces in n-tile 4 of the fragments.
 constexpr int kScoreCand = 64;
+constexpr int kSZ = 5;  // score splits of the feature sum per (head, candidate block)
 struct ScoreLds {
   uint16_t tab[kFPhi];
   float den[kWavesF][kScoreCand];
@@ -491,15 +502,14 @@ __device__ __forceinline__ void hyb_score_correction(
   if (q4 == 0 && cbase + 16 * w + l16 < n_cand) pz[(size_t)(cbase + 16 * w + l16) * 68 + 64] = dpart;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
-    const uint4* __restrict__ HF, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T,
-    const int32_t* __restrict__ cache, int cstride, int n_cache, int ev0, int n_cand,
-    const int32_t* __restrict__ rej, int rstride, int n_rej, int zs, float* __restrict__ part, int pstride) {
-  __shared__ __align__(16) ScoreShared shu;
-  const int n = blockIdx.x;
-  const int cbase = kScoreCand * blockIdx.y;
-  const int Z = gridDim.z;
-  if ((int)blockIdx.z == zs) {
+// Work-group (n, by, bz) of the scorer, bz < Z = zs + 1.
+__device__ __forceinline__ void hyb_score_block(
+    ScoreShared& shu, int n, int by, int bz, int Z, const uint4* __restrict__ HF, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int T, const int32_t* __restrict__ cache, int cstride, int n_cache, int ev0,
+    int n_cand, const int32_t* __restrict__ rej, int rstride, int n_rej, int zs, float* __restrict__ part,
+    int pstride) {
+  const int cbase = kScoreCand * by;
+  if (bz == zs) {
     hyb_score_correction(shu.c, k, v, T, n, cache + (size_t)n * cstride, n_cache, ev0, n_cand, cbase,
                          rej + (size_t)n * rstride, n_rej, part + ((size_t)n * Z + zs) * pstride * 68);
     return;
@@ -510,8 +520,8 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
-  const int tz0 = (int)((blockIdx.z * kFKS) / zs);
-  const int tz1 = (int)(((blockIdx.z + 1) * kFKS) / zs);
+  const int tz0 = (bz * kFKS) / zs;
+  const int tz1 = ((bz + 1) * kFKS) / zs;
 
   // B fragments of k-step ks, and the three pieces of s for this lane's
   // features (n-tile 4, lane column 0 of the lane's quarter)
@@ -656,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
   }
   if (w == kWavesF - 1) {
     // lane (l16, q4) holds candidates 16 mt + 4 q4 + i at state columns 4 l16 + nt
-    float* pz = part + ((size_t)n * Z + blockIdx.z) * pstride * 68;
+    float* pz = part + ((size_t)n * Z + bz) * pstride * 68;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -675,6 +685,39 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_score_frag_kernel(
         }
       }
     }
+  }
+}
+
+// One launch for the two halves of a refresh step that wait on the same
+// work: the scoring of refresh r (work-groups 0 .. n_score - 1, decoded as
+// (head, candidate block, slice)) and the fold of refresh r - 1 (the rest,
+// decoded as (k-step block, head)). Either part may be empty.
+union RefreshShared {
+  ScoreShared score;
+  FoldLds fold;
+};
+
+__global__ __launch_bounds__(kThreads, 2) void hyb_refresh_kernel(
+    // scoring of refresh r
+    int n_score, int n_cblk, const uint4* __restrict__ HFs, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int T, const int32_t* __restrict__ cache, int cstride, int n_cache, int ev0,
+    int n_cand, const int32_t* __restrict__ rej_prev, int rstride, int n_rej_prev, float* __restrict__ part,
+    int pstride,
+    // fold of refresh r - 1
+    float* __restrict__ H, float* __restrict__ s, uint4* __restrict__ HFf, const int32_t* __restrict__ rej_fold,
+    int n_rej_fold) {
+  __shared__ __align__(16) RefreshShared sh;
+  const int bid = blockIdx.x;
+  constexpr int Z = kSZ + 1;
+  if (bid < n_score) {
+    const int bz = bid % Z;
+    const int by = (bid / Z) % n_cblk;
+    const int n = bid / (Z * n_cblk);
+    hyb_score_block(sh.score, n, by, bz, Z, HFs, k, v, T, cache, cstride, n_cache, ev0, n_cand, rej_prev, rstride,
+                    n_rej_prev, kSZ, part, pstride);
+  } else {
+    const int f = bid - n_score;
+    hyb_fold_block(sh.fold, f % kFoldWGs, f / kFoldWGs, H, s, HFf, k, v, T, rej_fold, rstride, n_rej_fold);
   }
 }
 
@@ -1310,7 +1353,8 @@ struct Ws {
   float* H;
   float* s;
   int32_t* cache;
-  int32_t* cache2;  // second cache buffer (matrix-core path only)
+  int32_t* cache2;  // second and third cache buffers (matrix-core path only)
+  int32_t* cache3;
   float* scores;
   int32_t* rejected;
   int32_t* rejected2;  // second rejected list (matrix-core path only)
@@ -1325,7 +1369,6 @@ constexpr int kRNS = 8;  // readout splits per (head, query block)
 size_t xp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * a.refresh * kRNS * 66 * sizeof(float)); }
 
 constexpr int kCStride = kCandMax;
-constexpr int kSZ = 5;  // score splits of the feature sum per (head, candidate block)
 // plus one slice for the pairs the previous refresh folded
 size_t sp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * (kSZ + 1) * kCStride * 68 * sizeof(float)); }
 
@@ -1347,9 +1390,11 @@ Ws carve(const HybridArgs& a, void* ws) {
   }
   w.cache = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
-  w.cache2 = nullptr;
+  w.cache2 = w.cache3 = nullptr;
   if (matrix_path(a)) {
     w.cache2 = reinterpret_cast<int32_t*>(p);
+    p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
+    w.cache3 = reinterpret_cast<int32_t*>(p);
     p += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   }
   w.scores = reinterpret_cast<float*>(p);
@@ -1442,17 +1487,13 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
   return hipSuccess;
 }
 
-// Two more streams per device for the matrix-core path (the readouts, the
-// folds) and the events that order them against the caller's stream.
-// Default priority.
+// A second stream per device for the readouts of the matrix-core path, and
+// the events that order it against the caller's stream. Default priority.
 struct SideStream {
   std::mutex mu;
-  hipStream_t s = nullptr;  // readouts
-  hipStream_t f = nullptr;  // folds
-  hipEvent_t fork = nullptr, join = nullptr, fjoin = nullptr, ready = nullptr, selected = nullptr;
-  hipEvent_t used[2] = {nullptr, nullptr};                // cache buffer x last read by a readout
-  hipEvent_t hf_used[3] = {nullptr, nullptr, nullptr};    // fragment buffer x last read by a readout
-  hipEvent_t folded[3] = {nullptr, nullptr, nullptr};     // fragment buffer x written by its fold
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, ready = nullptr;
+  hipEvent_t used[3] = {nullptr, nullptr, nullptr};  // slot x last read by a readout
 };
 
 hipError_t side_stream(SideStream** out) {
@@ -1465,35 +1506,33 @@ hipError_t side_stream(SideStream** out) {
   static std::mutex init_mu;
   std::lock_guard<std::mutex> g(init_mu);
   if (!ss.s) {
-    hipStream_t sr, sf;
-    if ((e = hipStreamCreateWithFlags(&sf, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipStreamCreateWithFlags(&sr, hipStreamNonBlocking)) != hipSuccess) return e;
-    hipEvent_t* evs[13] = {&ss.fork,       &ss.join,       &ss.fjoin,      &ss.ready,     &ss.selected,
-                           &ss.used[0],    &ss.used[1],    &ss.hf_used[0], &ss.hf_used[1], &ss.hf_used[2],
-                           &ss.folded[0],  &ss.folded[1],  &ss.folded[2]};
+    hipStream_t s;
+    if ((e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking)) != hipSuccess) return e;
+    hipEvent_t* evs[6] = {&ss.fork, &ss.join, &ss.ready, &ss.used[0], &ss.used[1], &ss.used[2]};
     for (hipEvent_t* p : evs)
       if ((e = hipEventCreateWithFlags(p, hipEventDisableTiming)) != hipSuccess) return e;
-    ss.f = sf;
-    ss.s = sr;
+    ss.s = s;
   }
   *out = &ss;
   return hipSuccess;
 }
 
-// The matrix-core path (d = 64, bf16 in). Three streams:
-//   st: the refresh chain, scoring and selection (or the append);
-//   the fold stream: fold r of the pairs that refresh r rejects;
-//   the readout stream: each block's readout and combine.
-// Scoring at refresh r reads the state after fold r - 2 and adds the pairs of
-// refresh r - 1 in closed form (slice zs of hyb_score_frag_kernel), so fold
-// r - 1 overlaps scoring and selection r instead of preceding them: the
-// chain waits only for fold r - 2. State fragments have three buffers
-// (version r in buffer r mod 3; the zero state before the first fold in
-// buffers 1 and 2): scoring reads version r - 2, the readouts version r - 1
-// or r, the fold writes version r. The cache and the rejected list have two
-// buffers each. A buffer is rewritten only after the last kernel that read it
-// has finished (events used, hf_used; stream order elsewhere). The host knows
-// every count in advance, so nothing is read back.
+// The matrix-core path (d = 64, bf16 in). Scoring at refresh r reads the
+// state after fold r - 2 and adds the pairs refresh r - 1 rejected in closed
+// form (slice zs of the scorer), so it no longer waits for fold r - 1: the
+// two run in one launch (hyb_refresh_kernel), followed by selection r. The
+// refresh chain runs on the caller's stream; the readouts run on the
+// library's second stream, those of the blocks that refresh r serves once
+// fold r is issued (in the launch of refresh r + 1, or alone after the last
+// block), so they overlap the next refresh. Each refresh r owns slot r mod 3
+// (state fragments of version r and cache r; slot 2 holds the zero state and
+// the cache filled by appends before the first refresh, slot 1 the zero
+// state too); the rejected lists alternate. A slot is rewritten only after
+// the readouts that read it have finished (event used[slot]); everything
+// else is ordered by the chain's stream. The host knows every count in
+// advance, so nothing is read back. Per refresh block the host issues four
+// kernels (refresh, selection, readout, combine) and at most five event
+// records and waits.
 template <typename Tout>
 hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStream* ss, bool prof) {
   const Ws w = carve(a, ws);
@@ -1505,21 +1544,19 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
   Tout* o = static_cast<Tout*>(a.o);
   hipError_t e = hipSuccess;
   const hipStream_t sb = ss->s;
-  const hipStream_t sf = ss->f;
 #define KLA_TRY(x)                       \
   do {                                   \
     e = (x);                             \
     if (e != hipSuccess) return e;       \
   } while (0)
 #define KLA_CHECK() KLA_TRY(hipGetLastError())
-  int32_t* cache[2] = {w.cache, w.cache2};
+  int32_t* cache[3] = {w.cache, w.cache2, w.cache3};
   int32_t* rej[2] = {w.rejected, w.rejected2};
-  bool used[2] = {false, false};
-  bool hf_used[3] = {false, false, false};
+  bool used[3] = {false, false, false};
   hipLaunchKernelGGL(fill_kernel_f32, dim3(1024), dim3(256), 0, st, w.H, (size_t)N * kFPhi * kFD, 0.0f);
   hipLaunchKernelGGL(fill_kernel_f32, dim3(64), dim3(256), 0, st, w.s, (size_t)N * kFPhi, 0.0f);
-  hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, cache[0], (size_t)N * kCStride, -1);
-  hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, cache[1], (size_t)N * kCStride, -1);
+  for (int32_t* c : cache)
+    hipLaunchKernelGGL(fill_kernel_i32, dim3(64), dim3(256), 0, st, c, (size_t)N * kCStride, -1);
   for (uint4* h : w.HF)
     hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, reinterpret_cast<int32_t*>(h),
                        hf_bytes(a) / sizeof(int32_t), 0);
@@ -1527,101 +1564,115 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
     hipLaunchKernelGGL(fill_kernel_i32, dim3(1024), dim3(256), 0, st, a.trace,
                        (size_t)N * nblocks * a.cache_size, -1);
   KLA_CHECK();
-  // the side streams start after everything the caller queued so far
+  // the side stream starts after everything the caller queued so far
   KLA_TRY(hipEventRecord(ss->fork, st));
   KLA_TRY(hipStreamWaitEvent(sb, ss->fork, 0));
-  KLA_TRY(hipStreamWaitEvent(sf, ss->fork, 0));
-  int cur = 0;   // cache buffer of the current cache
-  int hv = 2;    // fragment buffer of the newest state (the zero state at first)
-  // everything after the fork also joins the side streams back, on error too
+  int slot = 2;  // slot of the newest state and cache
+  // everything after the fork also joins the side stream back, on error too
   const hipError_t loop_err = [&]() -> hipError_t {
     hipError_t e;
+    struct Pending {
+      int b0, b1, f, n_cache;
+    };
+    std::vector<Pending> pending;  // blocks whose readout waits for the fold of the newest refresh
     int n_cache = 0;
     int f_prev = 0;
-    int r = 0;          // refreshes issued
+    int r = 0;           // refreshes issued
     int n_rej_prev = 0;  // pairs rejected by refresh r - 1
+    // readouts of the blocks in `pending`, reading slot x
+    auto flush = [&](int x) -> hipError_t {
+      if (pending.empty()) return hipSuccess;
+      hipError_t e;
+      KLA_TRY(hipEventRecord(ss->ready, st));
+      KLA_TRY(hipStreamWaitEvent(sb, ss->ready, 0));
+      for (const Pending& p : pending) {
+        hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((p.b1 - p.b0 + kRQ - 1) / kRQ, N, kRNS),
+                           dim3(kRT), 0, sb, q, k, v, o, a.T, w.HF[x], cache[x], kCStride, p.n_cache, p.b0, p.b1,
+                           p.f, a.scale, a.eps, kRNS, w.xp, a.refresh);
+        hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>),
+                           dim3(((p.b1 - p.b0) * kFD + kThreads - 1) / kThreads, N), dim3(kThreads), 0, sb,
+                           w.xp, a.refresh, kRNS, o, a.T, p.b0, p.b1, a.eps);
+        KLA_CHECK();
+      }
+      KLA_TRY(hipEventRecord(ss->used[x], sb));
+      used[x] = true;
+      pending.clear();
+      return hipSuccess;
+    };
+    // The fold of refresh r - 1 rewrites slot (r - 1) mod 3 (last read by the
+    // readouts of refresh r - 4) and selection r rewrites slot r mod 3 (last
+    // read by those of refresh r - 3); readouts finish in order, so waiting
+    // for the latter before the fold frees both.
+    auto slots_free = [&](int x) -> hipError_t {
+      if (used[x]) return hipStreamWaitEvent(st, ss->used[x], 0);
+      return hipSuccess;
+    };
     for (int b = 0; b < nblocks; ++b) {
       const int b0 = b * a.refresh;
       const int b1 = std::min(a.T, b0 + a.refresh);
       const int f = std::max(0, b0 - a.window);
       const int n_ev = f - f_prev;
-      bool refreshed = false;
-      if (n_ev > 0) {
+      if (n_ev > 0 && n_cache + n_ev > a.cache_size) {
         const int n_cand = n_cache + n_ev;
-        if (n_cand <= a.cache_size) {
-          // appends past the entries any queued readout reads
-          hipLaunchKernelGGL(append_kernel, dim3(N), dim3(256), 0, st, cache[cur], kCStride, n_cache,
-                             f_prev, n_ev);
+        const int n_rej = n_cand - a.cache_size;
+        const int x_new = r % 3;          // slot of refresh r
+        const int x_cur = (r + 2) % 3;    // slot of refresh r - 1 (2 before the first)
+        const int x_old = (r + 1) % 3;    // slot of refresh r - 2 (the zero state for r < 2)
+        // scoring r (state r - 2 + pairs of r - 1) and fold r - 1 in one launch
+        KLA_TRY(slots_free(x_new));
+        const int n_cblk = (n_cand + kScoreCand - 1) / kScoreCand;
+        const int n_score = N * n_cblk * (kSZ + 1);
+        const int n_fold = r >= 1 ? N * kFoldWGs : 0;
+        if (prof) prof_begin(st);
+        hipLaunchKernelGGL(hyb_refresh_kernel, dim3(n_score + n_fold), dim3(kThreads), 0, st, n_score, n_cblk,
+                           w.HF[x_old], k, v, a.T, cache[x_cur], kCStride, n_cache, f_prev, n_cand,
+                           rej[(r + 1) & 1], kCStride, r >= 1 ? n_rej_prev : 0, w.sp, kCStride, w.H, w.s,
+                           w.HF[x_cur], rej[(r + 1) & 1], n_rej_prev);
+        KLA_CHECK();
+        // fold r - 1 is issued: the readouts of the blocks refresh r - 1 serves
+        KLA_TRY(flush(x_cur));
+        hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ + 1, kCStride, v,
+                           a.T, a.eps, cache[x_cur], kCStride, cache[x_new], kCStride, n_cache, f_prev, n_cand,
+                           a.cache_size, rej[r & 1], kCStride, a.trace, (size_t)a.cache_size, b, nblocks,
+                           w.scores, kCStride);
+        if (prof) prof_end(st);
+        KLA_CHECK();
+        n_cache = a.cache_size;
+        n_rej_prev = n_rej;
+        slot = x_new;
+        ++r;
+        pending.push_back({b0, b1, f, n_cache});
+      } else {
+        if (n_ev > 0) {
+          // appends past the entries any queued readout reads (before the first refresh only)
+          hipLaunchKernelGGL(append_kernel, dim3(N), dim3(256), 0, st, cache[slot], kCStride, n_cache, f_prev,
+                             n_ev);
           KLA_CHECK();
-          n_cache = n_cand;
-        } else {
-          const int nxt = cur ^ 1;
-          const int v_old = (r + 1) % 3;  // version r - 2 (the zero state for r < 2)
-          const int v_new = r % 3;
-          const int n_rej = n_cand - a.cache_size;
-          // the cache buffer about to be rewritten is free, and fold r - 2 is done
-          if (used[nxt]) KLA_TRY(hipStreamWaitEvent(st, ss->used[nxt], 0));
-          if (r >= 2) KLA_TRY(hipStreamWaitEvent(st, ss->folded[v_old], 0));
-          if (prof) prof_begin(st);
-          // float32-faithful matrix-core score partials (split bf16 operands),
-          // plus the closed-form terms of the pairs refresh r - 1 rejected
-          hipLaunchKernelGGL(hyb_score_frag_kernel, dim3(N, (n_cand + kScoreCand - 1) / kScoreCand, kSZ + 1),
-                             dim3(kThreads), 0, st, w.HF[v_old], k, v, a.T, cache[cur], kCStride, n_cache,
-                             f_prev, n_cand, rej[(r + 1) & 1], kCStride, r > 0 ? n_rej_prev : 0, kSZ, w.sp,
-                             kCStride);
-          hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ + 1, kCStride,
-                             v, a.T, a.eps, cache[cur], kCStride, cache[nxt], kCStride, n_cache, f_prev, n_cand,
-                             a.cache_size, rej[r & 1], kCStride, a.trace, (size_t)a.cache_size, b, nblocks,
-                             w.scores, kCStride);
-          if (prof) prof_end(st);
-          KLA_CHECK();
-          // fold r on its own stream, once the selection is done and no
-          // readout still reads the fragment buffer it rewrites
-          KLA_TRY(hipEventRecord(ss->selected, st));
-          KLA_TRY(hipStreamWaitEvent(sf, ss->selected, 0));
-          if (hf_used[v_new]) KLA_TRY(hipStreamWaitEvent(sf, ss->hf_used[v_new], 0));
-          hipLaunchKernelGGL(hyb_fold_mfma_kernel, dim3((kFKS + kFoldKsPerWG - 1) / kFoldKsPerWG, N),
-                             dim3(kThreads), 0, sf, w.H, w.s, w.HF[v_new], k, v, a.T, rej[r & 1], kCStride,
-                             n_rej);
-          KLA_CHECK();
-          KLA_TRY(hipEventRecord(ss->folded[v_new], sf));
-          n_cache = a.cache_size;
-          n_rej_prev = n_rej;
-          cur = nxt;
-          hv = v_new;
-          ++r;
-          refreshed = true;
+          n_cache += n_ev;
         }
+        pending.push_back({b0, b1, f, n_cache});
+        // before any refresh the state is final (zero): read out at once
+        if (r == 0) KLA_TRY(flush(slot));
       }
       f_prev = f;
-      // the block's readout, on the readout stream, after the chain so far
-      // and the fold of the state it reads
-      KLA_TRY(hipEventRecord(ss->ready, st));
-      KLA_TRY(hipStreamWaitEvent(sb, ss->ready, 0));
-      if (refreshed) KLA_TRY(hipStreamWaitEvent(sb, ss->folded[hv], 0));
-      hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((b1 - b0 + kRQ - 1) / kRQ, N, kRNS), dim3(kRT), 0,
-                         sb, q, k, v, o, a.T, w.HF[hv], cache[cur], kCStride, n_cache, b0, b1, f, a.scale, a.eps,
-                         kRNS, w.xp, a.refresh);
-      hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>),
-                         dim3(((b1 - b0) * kFD + kThreads - 1) / kThreads, N), dim3(kThreads), 0, sb, w.xp,
-                         a.refresh, kRNS, o, a.T, b0, b1, a.eps);
-      KLA_CHECK();
-      KLA_TRY(hipEventRecord(ss->used[cur], sb));
-      KLA_TRY(hipEventRecord(ss->hf_used[hv], sb));
-      used[cur] = true;
-      hf_used[hv] = true;
     }
-    return hipSuccess;
+    // the fold of the last refresh alone, then the remaining readouts
+    if (r >= 1) {
+      KLA_TRY(slots_free(r % 3));
+      hipLaunchKernelGGL(hyb_refresh_kernel, dim3(N * kFoldWGs), dim3(kThreads), 0, st, 0, 1, w.HF[0], k, v, a.T,
+                         cache[slot], kCStride, 0, 0, 0, rej[(r + 1) & 1], kCStride, 0, w.sp, kCStride, w.H, w.s,
+                         w.HF[slot], rej[(r + 1) & 1], n_rej_prev);
+      KLA_CHECK();
+    }
+    return flush(slot);
   }();
-  // the caller's stream continues after the last readout and the last fold
+  // the caller's stream continues after the last readout
   KLA_TRY(hipEventRecord(ss->join, sb));
-  KLA_TRY(hipEventRecord(ss->fjoin, sf));
   KLA_TRY(hipStreamWaitEvent(st, ss->join, 0));
-  KLA_TRY(hipStreamWaitEvent(st, ss->fjoin, 0));
   if (loop_err != hipSuccess) return loop_err;
   if (a.cache_T && a.cache_size > 0) {
     hipLaunchKernelGGL(copy_rows_kernel, dim3(N), dim3(256), 0, st, a.cache_T, a.cache_size,
-                       cache[cur], kCStride);
+                       cache[slot], kCStride);
     KLA_CHECK();
   }
 #undef KLA_CHECK
@@ -1659,7 +1710,7 @@ size_t hybrid_workspace(const HybridArgs& a) {
   b += align_up((size_t)a.N * kCStride * sizeof(float));
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   if (matrix_path(a))
-    b += 2 * align_up((size_t)a.N * kCStride * sizeof(int32_t)) + 3 * hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
+    b += 3 * align_up((size_t)a.N * kCStride * sizeof(int32_t)) + 3 * hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
   return b;
 }
 
