@@ -188,3 +188,20 @@ def test_factors_f32_resume_and_bf16_out(K, g):
         ro = O.prefill_factors_bruteforce(c.q[0, h], c.k[0, h], c.v[0, h], g, "concat")
         assert_close(host(torch.cat([o1, o2], dim=2))[0, h], ro, RTOL_F32, f"resumed o head {h}")
         assert_close(host(ob)[0, h], ro, RTOL_BF16, f"bf16 out head {h}")
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_factors_vector_path_bf16_inputs(K, g):
+    # bf16 inputs with d_qk = 32 (not the matrix path): float32 arithmetic on
+    # exact bf16 values, so the float32 bound against the oracle on the same
+    # rounded inputs
+    c = S.prefill_case("factors_vec_bf16", 1, 2, 150, 32, 64, 64, seed=510 + g)
+    qb, kb, vb = (dev(x) for x in (c.q, c.k, c.v))
+    o, HT, sT = K.prefill(qb, kb, vb, chunk=64, return_state=True, out_dtype=torch.float32, factors=g)
+    torch.cuda.synchronize()
+    q, k, v = host(qb), host(kb), host(vb)
+    for h in range(2):
+        ro, rH, rs = O.prefill_factors_recurrent(q[0, h], k[0, h], v[0, h], g, "concat")
+        assert_close(host(o)[0, h], ro, RTOL_F32, f"o g={g} head {h}")
+        assert_close(host(HT)[0, h], rH, RTOL_F32, f"H_T g={g} head {h}")
+        assert_close(host(sT)[0, h], rs, RTOL_F32, f"s_T g={g} head {h}")
