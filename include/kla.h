@@ -23,15 +23,19 @@
  * Conventions shared by every call:
  *   - Memory: every tensor pointer is a device pointer owned by the caller.
  *     The library never allocates or frees device memory and keeps no
- *     per-call state (the one exception, a per-device stream and its events
- *     for kla_hybrid_prefill, is described there); scratch memory comes from
- *     the caller through `ws`, sized by the matching *_workspace_size query.
+ *     state between calls; scratch memory comes from the caller through
+ *     `ws`, sized by the matching *_workspace_size query. Every device
+ *     pointer (tensors and `ws`) must be 16-byte aligned: the kernels move
+ *     rows with 16-byte vector accesses. A misaligned pointer is rejected
+ *     with KLA_ERR_INVALID_ARGUMENT.
  *   - Layout: tensors are dense row-major (C order), shapes given below.
  *     N = B*H heads, ordered (b, h). The state is H [N, D, d_v] and
  *     s [N, D], float32, in the coordinate order and sqrt(2) scaling above.
  *   - Execution: every call enqueues its kernels on `stream` (a hipStream_t;
- *     NULL is the null stream) and returns without synchronising. Device
- *     faults surface at the caller's next synchronisation.
+ *     NULL is the null stream) and returns without synchronising; it
+ *     launches on no other stream unless the caller passes one
+ *     (kla_hybrid_prefill_streams). Device faults surface at the caller's
+ *     next synchronisation.
  *   - Errors: every argument is checked on the host before anything is
  *     enqueued; a call that fails a check returns its status, enqueues
  *     nothing and writes no output. A failed launch returns KLA_ERR_HIP.
@@ -73,7 +77,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 3
+#define KLA_ABI_VERSION 4
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -312,13 +316,7 @@ KLA_API kla_status_t kla_sre_select(int N, int d_qk, int d_v, float eps, const f
  * Supported: d_qk, d_v in {16, 32, 64}; 1 <= refresh <= 128; window >= 0;
  * 0 <= cache_size and cache_size + refresh <= 256; softmax_scale finite.
  *
- * Streams: with d_qk = d_v = 64 and bf16 inputs, each block's readout runs on
- * a second stream that the library creates on the device at first use
- * (default priority, kept until the process ends), forked from `stream`
- * inside the call and joined back into it before the call returns; work
- * queued on `stream` afterwards is ordered after every kernel of the call.
- * Concurrent calls on one device from several host threads serialise while
- * they enqueue.
+ * Every kernel runs on `stream`, in order.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int window, cache_size, refresh;
@@ -331,6 +329,22 @@ KLA_API kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid
                                 const void* q, const void* k, const void* v, void* o, float* H_T,
                                 float* s_T, int32_t* cache_tokens_T, int32_t* sel_trace,
                                 void* ws, size_t ws_bytes, kla_stream_t stream);
+
+/* kla_hybrid_prefill with a second stream of the caller's (same results,
+ * same passages). With d_qk = d_v = 64 and bf16 inputs, each block's
+ * readout runs on `aux_stream` so that it overlaps the next refresh; the
+ * call forks `aux_stream` from `stream` at its start and joins it back
+ * before returning, so work queued afterwards on `stream` is ordered after
+ * every kernel of the call, and work queued on `aux_stream` afterwards is
+ * ordered after the call's readouts. The fork and join events are created
+ * and released by the call itself. aux_stream = NULL (or = stream) runs
+ * everything on `stream`. Two calls must not share one aux_stream
+ * concurrently from different host threads. */
+KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg,
+                                                const void* q, const void* k, const void* v, void* o,
+                                                float* H_T, float* s_T, int32_t* cache_tokens_T,
+                                                int32_t* sel_trace, void* ws, size_t ws_bytes,
+                                                kla_stream_t stream, kla_stream_t aux_stream);
 
 /* ------------------------------------------------------------------------
  * kla_hybrid_decode_step - LoLA's three memories token by token (LoLA

@@ -25,7 +25,7 @@ EXPORTS = (
     "kla_prefill_quadratic_factors", "kla_prefill_factors", "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
-    "kla_hybrid_workspace_size", "kla_hybrid_prefill",
+    "kla_hybrid_workspace_size", "kla_hybrid_prefill", "kla_hybrid_prefill_streams",
     "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step", "kla_hybrid_decode_flush",
     "kla_profile_enable", "kla_profile_read",
 )
@@ -100,6 +100,7 @@ def load_library(path: str = LIB_PATH):
         "kla_sre_select": (i, [i, i, i, f, vp, vp, srp, vp, sz, vp]),
         "kla_hybrid_workspace_size": (i, [shp, hcp, szp]),
         "kla_hybrid_prefill": (i, [shp, hcp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kla_hybrid_prefill_streams": (i, [shp, hcp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]),
         "kla_hybrid_decode_workspace_size": (i, [i, i, i, hcp, szp]),
         "kla_hybrid_decode_step": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp, sz, vp]),
         "kla_hybrid_decode_flush": (i, [i, i, i, hsp, vp]),
@@ -153,6 +154,16 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _dense(t):
+    """A contiguous tensor whose data pointer is 16-byte aligned (the library
+    rejects misaligned pointers): views at an odd storage offset are copied
+    into fresh storage. Values are unchanged."""
+    t = t.contiguous()
+    if t.data_ptr() % 16:
+        t = t.clone()
+    return t
+
+
 def _need_device(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -186,7 +197,7 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
-    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    q, k, v = _dense(q), _dense(k), _dense(v)
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     B, Hh, T, dqk = q.shape
@@ -209,7 +220,7 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     sT = torch.empty((B, Hh, D), dtype=torch.float32, device=dev) if want_state else None
     H0 = s0 = None
     if state is not None:
-        H0, s0 = (x.contiguous() for x in state)
+        H0, s0 = (_dense(x) for x in state)
         _need_device(H0, s0)
         if H0.dtype != torch.float32 or s0.dtype != torch.float32:
             raise TypeError("state must be float32")
@@ -252,7 +263,7 @@ def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None, retur
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
-    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    q, k, v = _dense(q), _dense(k), _dense(v)
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     B, Hh, T, dqk = q.shape
@@ -289,7 +300,7 @@ def prefill_quadratic_backward(q, k, v, den, dout, eps: float = 0.0):
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v, den, dout)
-    q, k, v, den, dout = (x.contiguous() for x in (q, k, v, den, dout))
+    q, k, v, den, dout = (_dense(x) for x in (q, k, v, den, dout))
     if not (q.dtype == k.dtype == v.dtype) or den.dtype != torch.float32:
         raise TypeError("q, k, v share one dtype; den is float32")
     B, Hh, T, dqk = q.shape
@@ -341,7 +352,7 @@ def decode_step(H, s, q, k, v, eps: float = 0.0, out_dtype=None, cand_k=None, ca
     for t in (H, s):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise TypeError("H and s must be contiguous float32 (updated in place)")
-    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    q, k, v = _dense(q), _dense(k), _dense(v)
     N, dqk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
@@ -351,7 +362,7 @@ def decode_step(H, s, q, k, v, eps: float = 0.0, out_dtype=None, cand_k=None, ca
     sre_p = None
     res = None
     if cand_k is not None:
-        cand_k, cand_v = cand_k.contiguous(), cand_v.contiguous()
+        cand_k, cand_v = _dense(cand_k), _dense(cand_v)
         sc, sel, sk, sv = _sre_outputs(N, cand_k.shape[1], top_k, dqk, dv, dev, scores, gather, out)
         stride = 0
         if sk is not None and out is not None and "sel_stride" in out:
@@ -375,8 +386,8 @@ def sre_select(H, s, cand_k, cand_v, top_k: int, eps: float = 0.0, scores: bool 
     torch = _torch()
     lib = load_library()
     _need_device(H, s, cand_k, cand_v)
-    H, s = H.contiguous(), s.contiguous()
-    cand_k, cand_v = cand_k.contiguous(), cand_v.contiguous()
+    H, s = _dense(H), _dense(s)
+    cand_k, cand_v = _dense(cand_k), _dense(cand_v)
     if cand_k.dtype != torch.float32 or cand_v.dtype != torch.float32:
         raise TypeError("candidates must be float32")
     N, n_cand, dqk = cand_k.shape
@@ -394,13 +405,15 @@ def sre_select(H, s, cand_k, cand_v, top_k: int, eps: float = 0.0, scores: bool 
 
 def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, softmax_scale=None,
                    eps: float = 0.0, return_state: bool = False, return_cache: bool = False,
-                   return_trace: bool = False, out_dtype=None):
+                   return_trace: bool = False, out_dtype=None, aux_stream=None):
     """Window + linear state + sparse cache prefill. Returns o, plus a dict
-    with H, s, cache (token ids) and trace when requested."""
+    with H, s, cache (token ids) and trace when requested. ``aux_stream``
+    (a torch.cuda.Stream of the same device, default priority) lets the
+    readouts overlap the refresh chain (kla_hybrid_prefill_streams)."""
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
-    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    q, k, v = _dense(q), _dense(k), _dense(v)
     B, Hh, T, dqk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
@@ -420,9 +433,10 @@ def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, softmax_
     nbytes = ctypes.c_size_t(0)
     check(lib.kla_hybrid_workspace_size(ctypes.byref(shp), ctypes.byref(cfg), ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
-    check(lib.kla_hybrid_prefill(ctypes.byref(shp), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(o), _ptr(HT), _ptr(sT), _ptr(cT), _ptr(tr), _ptr(ws),
-                                 nbytes.value, _stream(dev)))
+    aux = None if aux_stream is None else ctypes.c_void_p(aux_stream.cuda_stream)
+    check(lib.kla_hybrid_prefill_streams(ctypes.byref(shp), ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(o), _ptr(HT), _ptr(sT), _ptr(cT), _ptr(tr), _ptr(ws),
+                                         nbytes.value, _stream(dev), aux))
     if not (return_state or return_cache or return_trace):
         return o
     return o, dict(H=HT, s=sT, cache=cT, trace=tr)
@@ -468,7 +482,7 @@ def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, sof
     lib = load_library()
     _need_device(q, k, v)
     st = _hybrid_state_struct(state)
-    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    q, k, v = _dense(q), _dense(k), _dense(v)
     N, dqk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)

@@ -21,7 +21,6 @@
 // The host knows every count in advance (they depend only on T, window,
 // refresh and cache_size), so no device value is read back.
 #include <algorithm>
-#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -1487,54 +1486,47 @@ hipError_t run(const HybridArgs& a, void* ws, hipStream_t st) {
   return hipSuccess;
 }
 
-// A second stream per device for the readouts of the matrix-core path, and
-// the events that order it against the caller's stream. Default priority.
-struct SideStream {
-  std::mutex mu;
-  hipStream_t s = nullptr;
+// Events that order the caller's auxiliary stream against its main stream
+// during one call. They belong to the call: created at its start and
+// released at its end (a pending event is released by the runtime once it
+// completes), so the library keeps nothing between calls.
+struct CallEvents {
   hipEvent_t fork = nullptr, join = nullptr, ready = nullptr;
   hipEvent_t used[3] = {nullptr, nullptr, nullptr};  // slot x last read by a readout
-};
-
-hipError_t side_stream(SideStream** out) {
-  static SideStream pool[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  SideStream& ss = pool[dev];
-  static std::mutex init_mu;
-  std::lock_guard<std::mutex> g(init_mu);
-  if (!ss.s) {
-    hipStream_t s;
-    if ((e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking)) != hipSuccess) return e;
-    hipEvent_t* evs[6] = {&ss.fork, &ss.join, &ss.ready, &ss.used[0], &ss.used[1], &ss.used[2]};
-    for (hipEvent_t* p : evs)
-      if ((e = hipEventCreateWithFlags(p, hipEventDisableTiming)) != hipSuccess) return e;
-    ss.s = s;
+  hipError_t create() {
+    hipEvent_t* evs[6] = {&fork, &join, &ready, &used[0], &used[1], &used[2]};
+    for (hipEvent_t* p : evs) {
+      const hipError_t e = hipEventCreateWithFlags(p, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
-  *out = &ss;
-  return hipSuccess;
-}
+  ~CallEvents() {
+    hipEvent_t evs[6] = {fork, join, ready, used[0], used[1], used[2]};
+    for (hipEvent_t e : evs)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
 
 // The matrix-core path (d = 64, bf16 in). Scoring at refresh r reads the
 // state after fold r - 2 and adds the pairs refresh r - 1 rejected in closed
 // form (slice zs of the scorer), so it no longer waits for fold r - 1: the
 // two run in one launch (hyb_refresh_kernel), followed by selection r. The
 // refresh chain runs on the caller's stream; the readouts run on the
-// library's second stream, those of the blocks that refresh r serves once
-// fold r is issued (in the launch of refresh r + 1, or alone after the last
-// block), so they overlap the next refresh. Each refresh r owns slot r mod 3
+// caller's auxiliary stream when one is given (else on the same stream, in
+// order), those of the blocks that refresh r serves once fold r is issued
+// (in the launch of refresh r + 1, or alone after the last block), so they
+// overlap the next refresh. Each refresh r owns slot r mod 3
 // (state fragments of version r and cache r; slot 2 holds the zero state and
 // the cache filled by appends before the first refresh, slot 1 the zero
 // state too); the rejected lists alternate. A slot is rewritten only after
-// the readouts that read it have finished (event used[slot]); everything
-// else is ordered by the chain's stream. The host knows every count in
+// the readouts that read it have finished (event used[slot], only needed
+// with two streams); everything else is ordered by the chain's stream. The host knows every count in
 // advance, so nothing is read back. Per refresh block the host issues four
 // kernels (refresh, selection, readout, combine) and at most five event
 // records and waits.
 template <typename Tout>
-hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStream* ss, bool prof) {
+hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux, bool prof) {
   const Ws w = carve(a, ws);
   const int N = a.N;
   const int nblocks = (a.T + a.refresh - 1) / a.refresh;
@@ -1543,7 +1535,13 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
   const uint16_t* v = static_cast<const uint16_t*>(a.v);
   Tout* o = static_cast<Tout*>(a.o);
   hipError_t e = hipSuccess;
-  const hipStream_t sb = ss->s;
+  // readouts go to the caller's auxiliary stream when one is given, else
+  // everything runs in order on `st` and no event is needed
+  const bool two = aux != nullptr && aux != st;
+  const hipStream_t sb = two ? aux : st;
+  CallEvents ev;
+  if (two && (e = ev.create()) != hipSuccess) return e;
+  CallEvents* ss = &ev;
 #define KLA_TRY(x)                       \
   do {                                   \
     e = (x);                             \
@@ -1565,8 +1563,10 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
                        (size_t)N * nblocks * a.cache_size, -1);
   KLA_CHECK();
   // the side stream starts after everything the caller queued so far
-  KLA_TRY(hipEventRecord(ss->fork, st));
-  KLA_TRY(hipStreamWaitEvent(sb, ss->fork, 0));
+  if (two) {
+    KLA_TRY(hipEventRecord(ss->fork, st));
+    KLA_TRY(hipStreamWaitEvent(sb, ss->fork, 0));
+  }
   int slot = 2;  // slot of the newest state and cache
   // everything after the fork also joins the side stream back, on error too
   const hipError_t loop_err = [&]() -> hipError_t {
@@ -1583,8 +1583,10 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
     auto flush = [&](int x) -> hipError_t {
       if (pending.empty()) return hipSuccess;
       hipError_t e;
-      KLA_TRY(hipEventRecord(ss->ready, st));
-      KLA_TRY(hipStreamWaitEvent(sb, ss->ready, 0));
+      if (two) {
+        KLA_TRY(hipEventRecord(ss->ready, st));
+        KLA_TRY(hipStreamWaitEvent(sb, ss->ready, 0));
+      }
       for (const Pending& p : pending) {
         hipLaunchKernelGGL((hyb_readout_mfma_kernel<Tout>), dim3((p.b1 - p.b0 + kRQ - 1) / kRQ, N, kRNS),
                            dim3(kRT), 0, sb, q, k, v, o, a.T, w.HF[x], cache[x], kCStride, p.n_cache, p.b0, p.b1,
@@ -1594,8 +1596,10 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
                            w.xp, a.refresh, kRNS, o, a.T, p.b0, p.b1, a.eps);
         KLA_CHECK();
       }
-      KLA_TRY(hipEventRecord(ss->used[x], sb));
-      used[x] = true;
+      if (two) {
+        KLA_TRY(hipEventRecord(ss->used[x], sb));
+        used[x] = true;
+      }
       pending.clear();
       return hipSuccess;
     };
@@ -1667,8 +1671,10 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
     return flush(slot);
   }();
   // the caller's stream continues after the last readout
-  KLA_TRY(hipEventRecord(ss->join, sb));
-  KLA_TRY(hipStreamWaitEvent(st, ss->join, 0));
+  if (two) {
+    KLA_TRY(hipEventRecord(ss->join, sb));
+    KLA_TRY(hipStreamWaitEvent(st, ss->join, 0));
+  }
   if (loop_err != hipSuccess) return loop_err;
   if (a.cache_T && a.cache_size > 0) {
     hipLaunchKernelGGL(copy_rows_kernel, dim3(N), dim3(256), 0, st, a.cache_T, a.cache_size,
@@ -1681,18 +1687,14 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, SideStr
 }
 
 template <typename Tout>
-hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st) {
-  SideStream* ss = nullptr;
-  hipError_t e = side_stream(&ss);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> g(ss->mu);
-  return enqueue_matrix<Tout>(a, ws, st, ss, true);
+hipError_t run_matrix(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux) {
+  return enqueue_matrix<Tout>(a, ws, st, aux, true);
 }
 
 template <int DQK, int DV>
-hipError_t run_dt(const HybridArgs& a, void* ws, hipStream_t st) {
+hipError_t run_dt(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux) {
   if (DQK == 64 && DV == 64 && a.in_bf16)
-    return a.out_bf16 ? run_matrix<uint16_t>(a, ws, st) : run_matrix<float>(a, ws, st);
+    return a.out_bf16 ? run_matrix<uint16_t>(a, ws, st, aux) : run_matrix<float>(a, ws, st, aux);
   if (a.in_bf16)
     return a.out_bf16 ? run<DQK, DV, uint16_t, uint16_t>(a, ws, st)
                       : run<DQK, DV, uint16_t, float>(a, ws, st);
@@ -1714,9 +1716,9 @@ size_t hybrid_workspace(const HybridArgs& a) {
   return b;
 }
 
-hipError_t hybrid_launch(const HybridArgs& a, void* ws, hipStream_t st) {
+hipError_t hybrid_launch(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux) {
 #define KLA_CASE(A, B) \
-  if (a.dqk == A && a.dv == B) return run_dt<A, B>(a, ws, st);
+  if (a.dqk == A && a.dv == B) return run_dt<A, B>(a, ws, st, aux);
   KLA_CASE(16, 16) KLA_CASE(16, 32) KLA_CASE(16, 64)
   KLA_CASE(32, 16) KLA_CASE(32, 32) KLA_CASE(32, 64)
   KLA_CASE(64, 16) KLA_CASE(64, 32) KLA_CASE(64, 64)

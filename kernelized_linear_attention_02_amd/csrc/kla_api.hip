@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 #include <utility>
 #include <vector>
@@ -45,6 +46,22 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const char* pa = static_cast<const char*>(a);
   const char* pb = static_cast<const char*>(b);
   return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Every device pointer of a call must be 16-byte aligned: the kernels move
+// rows with 16-byte vector accesses. NULL (an absent optional argument)
+// passes.
+struct NamedPtr {
+  const char* name;
+  const void* p;
+};
+kla_status_t check_align(const char* fn, std::initializer_list<NamedPtr> ptrs) {
+  for (const NamedPtr& x : ptrs)
+    if (x.p && !aligned16(x.p))
+      return fail(KLA_ERR_INVALID_ARGUMENT, "%s: %s must be 16-byte aligned (got %p)", fn, x.name, x.p);
+  return KLA_OK;
 }
 
 kla_status_t check_shape(const kla_shape_t* shp, const char* fn) {
@@ -117,7 +134,8 @@ kla_status_t check_sre(int N, int dqk, int dv, const kla_sre_args_t* sre, const 
   if (overlaps(sre->sel_k, nsk, sre->cand_k, nck) || overlaps(sre->sel_k, nsk, sre->cand_v, ncv) ||
       overlaps(sre->sel_v, nsv, sre->cand_k, nck) || overlaps(sre->sel_v, nsv, sre->cand_v, ncv))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: sel_k / sel_v overlap the candidates", fn);
-  return KLA_OK;
+  return check_align(fn, {{"cand_k", sre->cand_k}, {"cand_v", sre->cand_v}, {"scores", sre->scores},
+                          {"sel", sre->sel}, {"sel_k", sre->sel_k}, {"sel_v", sre->sel_v}});
 }
 
 kla::SreArgs make_sre(const kla_sre_args_t* s) {
@@ -301,6 +319,9 @@ kla_status_t prefill_call(const char* fn, const kla_shape_t* shp, int chunk, int
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: give both H_T and s_T or neither", fn);
   if (!o && !H_T)
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: o may be NULL only when H_T and s_T are given", fn);
+  st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"H0", H0}, {"s0", s0}, {"H_T", H_T},
+                        {"s_T", s_T}, {"ws", ws}});
+  if (st != KLA_OK) return st;
   kla::PrefillArgs a = make_prefill(shp, chunk);
   a.q = q;
   a.k = k;
@@ -347,6 +368,8 @@ kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const 
   kla_status_t st = check_shape(shp, fn);
   if (st != KLA_OK) return st;
   if (!q || !k || !v || !o) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v and o are required", fn);
+  st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"den", den}});
+  if (st != KLA_OK) return st;
   kla::PrefillArgs a = make_prefill(shp, 64);
   a.q = q;
   a.k = k;
@@ -368,6 +391,8 @@ kla_status_t kla_prefill_quadratic_factors(const kla_shape_t* shp, int kind, int
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: kind %d is neither KLA_FACTORS_CONCAT nor KLA_FACTORS_SUM", fn, kind);
   if (factors != 1 && factors != 2 && factors != 4)
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: factors = %d (1, 2 or 4 supported)", fn, factors);
+  st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"den", den}});
+  if (st != KLA_OK) return st;
   kla::PrefillArgs a = make_prefill(shp, 64);
   a.q = q;
   a.k = k;
@@ -404,6 +429,9 @@ kla_status_t kla_prefill_quadratic_backward(const kla_shape_t* shp, const void* 
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v, den, dout, dq, dk and dv are required", fn);
   if (shp->in_dtype != KLA_BF16 || shp->d_qk != 64 || shp->d_v != 64)
     return fail(KLA_ERR_UNSUPPORTED, "%s: needs d_qk = d_v = 64 and bf16 inputs", fn);
+  st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"den", den}, {"dout", dout}, {"dq", dq}, {"dk", dk},
+                        {"dv", dv}, {"ws", ws}});
+  if (st != KLA_OK) return st;
   kla::QuadBwdArgs a{};
   a.N = shp->B * shp->H;
   a.T = shp->T;
@@ -460,7 +488,8 @@ kla_status_t kla_decode_step(int N, int d_qk, int d_v, float eps, float* H, floa
   if (!H || !s || !q || !k || !v || !o)
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: H, s, q, k, v, o are required", fn);
   if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
-  kla_status_t st = KLA_OK;
+  kla_status_t st = check_align(fn, {{"H", H}, {"s", s}, {"q", q}, {"k", k}, {"v", v}, {"o", o}, {"ws", ws}});
+  if (st != KLA_OK) return st;
   kla::SreArgs sa{};
   if (sre) {
     st = check_sre(N, d_qk, d_v, sre, fn);
@@ -514,6 +543,8 @@ kla_status_t kla_sre_select(int N, int d_qk, int d_v, float eps, const float* H,
   if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
   kla_status_t st = check_sre(N, d_qk, d_v, sre, fn);
   if (st != KLA_OK) return st;
+  st = check_align(fn, {{"H", H}, {"s", s}, {"ws", ws}});
+  if (st != KLA_OK) return st;
   const kla::SreArgs sa = make_sre(sre);
   st = check_ws(kla::sre_workspace(N, d_qk, d_v, sa), ws, ws_bytes, fn);
   if (st != KLA_OK) return st;
@@ -534,16 +565,19 @@ kla_status_t kla_hybrid_workspace_size(const kla_shape_t* shp, const kla_hybrid_
   return ok();
 }
 
-kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg,
-                                const void* q, const void* k, const void* v, void* o, float* H_T,
-                                float* s_T, int32_t* cache_tokens_T, int32_t* sel_trace,
-                                void* ws, size_t ws_bytes, kla_stream_t stream) {
+kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg, const void* q,
+                                        const void* k, const void* v, void* o, float* H_T, float* s_T,
+                                        int32_t* cache_tokens_T, int32_t* sel_trace, void* ws, size_t ws_bytes,
+                                        kla_stream_t stream, kla_stream_t aux_stream) {
   const char* fn = "kla_hybrid_prefill";
   kla_status_t st = check_hybrid(shp, cfg, fn);
   if (st != KLA_OK) return st;
   if (!q || !k || !v || !o) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: q, k, v, o are required", fn);
   if ((H_T == nullptr) != (s_T == nullptr))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: give both H_T and s_T or neither", fn);
+  st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"H_T", H_T}, {"s_T", s_T},
+                        {"cache_tokens_T", cache_tokens_T}, {"sel_trace", sel_trace}, {"ws", ws}});
+  if (st != KLA_OK) return st;
   kla::HybridArgs a = make_hybrid(shp, cfg);
   a.q = q;
   a.k = k;
@@ -556,7 +590,17 @@ kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid_cfg_t* 
   // the workspace size depends on which state outputs the caller provides
   st = check_ws(kla::hybrid_workspace(a), ws, ws_bytes, fn);
   if (st != KLA_OK) return st;
-  return hip_status(kla::hybrid_launch(a, ws, reinterpret_cast<hipStream_t>(stream)), fn);
+  return hip_status(kla::hybrid_launch(a, ws, reinterpret_cast<hipStream_t>(stream),
+                                       reinterpret_cast<hipStream_t>(aux_stream)),
+                    fn);
+}
+
+kla_status_t kla_hybrid_prefill(const kla_shape_t* shp, const kla_hybrid_cfg_t* cfg,
+                                const void* q, const void* k, const void* v, void* o, float* H_T,
+                                float* s_T, int32_t* cache_tokens_T, int32_t* sel_trace,
+                                void* ws, size_t ws_bytes, kla_stream_t stream) {
+  return kla_hybrid_prefill_streams(shp, cfg, q, k, v, o, H_T, s_T, cache_tokens_T, sel_trace, ws, ws_bytes,
+                                    stream, nullptr);
 }
 
 // ---------------------------------------------------------------- hybrid decode
@@ -583,8 +627,6 @@ kla_status_t check_hybrid_decode(int N, int d_qk, int d_v, const kla_hybrid_cfg_
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: softmax_scale must be finite", fn);
   return KLA_OK;
 }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -630,6 +672,8 @@ kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const k
       !aligned16(S.cache_k) || !aligned16(S.cache_v) || !aligned16(S.cache_ids) || !aligned16(S.pend_k) ||
       !aligned16(S.pend_v))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state pointers must be 16-byte aligned", fn);
+  st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"rejected", rejected}, {"ws", ws}});
+  if (st != KLA_OK) return st;
   kla::HybridDecodeArgs a{};
   a.N = N;
   a.dqk = d_qk;
@@ -669,6 +713,9 @@ kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_
   if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
   if (!state || !state->H || !state->s || !state->pend_k || !state->pend_v)
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, pend_k, pend_v are required", fn);
+  kla_status_t st = check_align(fn, {{"H", state->H}, {"s", state->s}, {"pend_k", state->pend_k},
+                                     {"pend_v", state->pend_v}});
+  if (st != KLA_OK) return st;
   kla::HybridDecodeArgs a{};
   a.N = N;
   a.dqk = d_qk;

@@ -128,7 +128,9 @@ struct HybridArgs {
 };
 
 size_t hybrid_workspace(const HybridArgs& a);
-hipError_t hybrid_launch(const HybridArgs& a, void* ws, hipStream_t st);
+// aux: a second stream of the caller's for the readouts of the matrix-core
+// path, or NULL to run everything on `st`.
+hipError_t hybrid_launch(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux);
 
 // Token-by-token hybrid: one token for every head-state.
 struct HybridDecodeArgs {

@@ -1,60 +1,68 @@
-// Chunked causal prefill on the bf16 matrix cores (d_qk = d_v = 64).
+// Chunked causal prefill on the matrix cores (d_qk = d_v = 64, bf16 inputs).
 //
 // KATA page, §2.3 ("Paralelismo por Blocos"; the linear chunked-state
 // operating point): inside a chunk, masked (Q K^T)∘(Q K^T) scores multiply
-// [V | 1]; across chunks the state (H, s) is a running prefix sum, read out by
-// phi(Q) and updated by phi(K)^T [V | 1]. The lift is the rank-one PSD feature
-// of KATA §2.2, phi(x)_ab = x_a x_b (times sqrt(2) off the diagonal).
+// V; across chunks the state H is a running prefix sum, read out by phi(Q)
+// and updated by phi(K)^T V. The lift is the rank-one PSD feature of KATA
+// §2.2, phi(x)_ab = x_a x_b (times sqrt(2) off the diagonal), so
+// phi(q).phi(k) = (q.k)^2. The normaliser phi(q)^T s equals q^T S q with
+// S = sum_t k_t k_t^T (the keys' Gram matrix, which holds s up to the sqrt(2)
+// scaling), so it is formed from S in float32.
 //
 // Feature tiles. The 64 dimensions form four blocks of 16. A tile is 16
-// ordered pairs sharing b: row r is a = 16 X + r, with b = 16 Y + j, for one of
-// the ten block pairs X <= Y and j = 0..15, so 160 tiles. Off the diagonal
-// blocks (X < Y) each unordered pair appears once and carries the weight 2 of
-// phi(q)_ab phi(k)_ab = 2 q_a q_b k_a k_b; a diagonal block (X = Y) holds all
-// 256 ordered pairs of its dimensions, each pair and its mirror, with weight
-// 1, which sums to the same. The kernels keep G(a, b) = sum_t k_a k_b v_t and
-// s(a, b) = sum_t k_a k_b (no sqrt(2)); the ABI's vec_sym layout is converted
-// on import and export.
+// ordered pairs sharing b: row r is a = 16 X + r, with b = 16 Y + j, for one
+// of the ten block pairs X <= Y and j = 0..15. Rows of a diagonal block with
+// a > b are mirrors of rows with a < b: they are accumulated (the tile's
+// shape needs them) but carry weight 0 in the readout and never cross the
+// ABI, so every feature a <= b has exactly one owner. The kernels keep
+// G(a, b) = sum_t k_a k_b v_t; the ABI's vec_sym layout (sqrt(2) off the
+// diagonal) is converted on import and export.
 //
-// Multi-factor lift (KATA-Mg, KATA §2.3 "Variantes", read as G equal factors
-// of 64 / G dimensions with their rank-one lifts concatenated): its features
-// are the pairs inside one factor, i.e. the tiles of the block pairs inside
-// the factors (G = 2: six of the ten, G = 4: the four diagonal blocks); the
-// finish kernel then sums the factors' squared scores.
+// Work split. A head's features are cut into SF slices (the tiles of 16 / SF
+// values of j) and its 64 value columns into two halves: one work-group per
+// (head, slice, half), 2 SF work-groups per head, all on one XCD (work-groups
+// are dealt to the 8 XCDs in turn) so their q, k, v reads meet in one L2.
 //
-// Slices. A work-group owns one head and the tiles of one value of j (16
-// slices per head) or two (8 slices) across the block pairs, so the tile
-// structure inside a work-group is fixed at compile time and only j varies.
+// Precision. The feature products and the state are float16 (11-bit
+// significands) with exact power-of-two scales that keep every value in
+// float16 range whatever the inputs: each sub-chunk's keys are scaled by
+// 2^-ek (largest |k| below 1) and its values by 2^(2 ek - G), where the
+// running exponent G >= 2 ek + log2 max|v| of every sub-chunk seen; the
+// accumulators hold H 2^-G (rescaled when G grows). Queries are scaled per
+// token (undone before the partials are written). The published state is
+// scaled by 2^-P so that its largest weighted entry stays below 2^15.
+// Accumulation is float32 throughout; the slice partials are float32.
 //
-// State kernel, eight waves, stepping through 64-token sub-chunks; each step
-// has two barriers: between them the update waves publish the state and the
-// readout waves flush their partials, around them every wave computes on the
-// staged sub-chunk while the next one is staged into the other buffer:
-//   update waves (4) hold their tiles of G and s in MFMA accumulators (fp32)
-//   for the whole sequence and add phi(K)^T [V | 1] per 32 tokens (MFMA
-//   16x16x32 bf16; a column of ones gives s). In the A operand a lane holds
-//   feature row r for eight tokens: it keeps k_a in registers and takes k_b
-//   from the lane of its 16-lane row that loaded it, by a DPP row broadcast
-//   folded into the multiply. At each chunk end they publish the state as bf16
-//   B fragments in LDS.
-//   readout waves (4): each takes 32 tokens and half of the tiles and reads
-//   out num = phi(Q) G and den = phi(Q) s (a fifth MFMA n-tile whose first
-//   column is s) against the state of the chunk start; a lane holds one token
-//   and forms its products from q values in registers. The two waves sharing
-//   tokens trade halves through LDS, and each writes one summed bf16 partial
-//   of a 16-token tile to a workspace [head, chunk, slice, token tile,
-//   16 x (d_v + 1)] in the MFMA accumulator order, so that both its writes and
-//   the finish kernel's reads are whole 512-byte runs per wave. They also
-//   stage the sub-chunks (q as fp32 rows, k as fp32 columns, v as bf16
-//   columns) from loads issued one sub-step ahead.
-// A head's work-groups are placed on one XCD (work-groups are dealt to the 8
-// XCDs in turn), so their shared q, k and v reads meet in one L2.
+// State kernel, eight waves, stepping through sub-chunks of up to 64 tokens;
+// each step has two barriers: between them the update waves publish the
+// state (at chunk ends), the readout waves write their partials and stage
+// the next sub-chunk; around them every wave computes on the staged one.
+//   update waves (4) hold their tiles of G for the whole sequence in MFMA
+//   accumulators and add phi(K)^T V per 32 tokens (mfma 16x16x32 f16): a lane
+//   of the A operand holds feature row r for eight tokens and forms them as
+//   packed float16 products of its k_a and k_b, k_b coming from lane 0 of its
+//   16-lane row by a DPP broadcast. In the first value half's work-group each
+//   wave also accumulates one X block of the keys' Gram matrix for the
+//   slice's columns b (raw bf16 keys: exact products, float32 sums). At each
+//   chunk end they publish the weighted state (2 off the diagonal, 1 on it, 0
+//   for mirror rows) as float16 B fragments in LDS and the Gram matrix to
+//   memory.
+//   readout waves (4): each takes 32 tokens and half of the tile pairs and
+//   reads out phi(Q) G against the state of the chunk start; a lane holds one
+//   token and forms its products from q values in registers. The two waves
+//   sharing tokens trade halves through LDS, and each writes one float32
+//   partial [16 tokens x 32 columns] per token tile in the MFMA accumulator
+//   order. They also stage the sub-chunks (q rows, k columns and raw k
+//   columns, v columns of the work-group's half), in two passes: the scales'
+//   maxima before the middle barrier, the scaled values after it.
 //
-// Finish kernel. One work-group per (head, chunk): the exact intra-chunk
-// term A [V | 1] with A = lower-triangular (Q K^T)^2 (MFMA; for G factors the
-// sum of the factors' squared scores), plus the sum of the slice partials,
-// divided, cast to the output type.
+// Finish kernel. One work-group per (head, chunk): the exact intra-chunk term
+// (squared scores as two bf16 pieces times V), the denominator's state term
+// q^T S q from the Gram matrix of the chunk start (two bf16 pieces on the
+// matrix cores, float32 sums), the sum of the slice partials, divided, cast
+// to the output type.
 #include <algorithm>
+#include <climits>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
@@ -62,6 +70,8 @@
 namespace kla {
 namespace {
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -69,54 +79,90 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kDim = 64;                          // d_qk = d_v
-constexpr int kAcc = kDim + 1;                    // accumulator row: num | den
-// Slice partials of one 16-token tile (bf16): the numerators in MFMA
-// accumulator order [n-tile][lane][4 tokens], then the 16 denominators.
-constexpr int kTileAcc = 16 * kAcc;
+constexpr int kDim = 64;      // d_qk = d_v
+constexpr int kCols = 32;     // value columns per work-group (two per head)
+constexpr int kUW = 4;        // update waves
+constexpr int kRW = 4;        // readout (and staging) waves
+constexpr int kThreads3 = 64 * (kUW + kRW);
+constexpr int kCS = 64;       // staged sub-chunk (tokens), at most
+constexpr int kPad = 8;       // halves of padding per LDS row
+constexpr int kNoExp = INT_MIN / 4;
+// float32 partials of one 16-token tile: 4 column n-tiles x 64 lanes x 4 tokens
+constexpr int kTilePart = 4 * 64 * 4;
 
+__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
 
-__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+__device__ __forceinline__ f32x4 mfma_h(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_b(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float* p) {
-  bf16x8 r;
+// e with m 2^-e in [0.5, 1) for m > 0 (so |x| <= m gives |x| 2^-e < 1);
+// kNoExp for m = 0.
+__device__ __forceinline__ int exp_above(float m) {
+  if (!(m > 0.0f)) return kNoExp;
+  const int be = (int)((__float_as_uint(m) >> 23) & 0xFF);
+  return be == 0 ? -126 : be - 126;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (__bf16)p[j];
-  return r;
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
 }
 
-// x from lane J of this lane's 16-lane row (DPP row broadcast).
-template <int J>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, true));
+// x from lane 0 of this lane's 16-lane row (DPP row broadcast).
+__device__ __forceinline__ uint32_t row_bcast0(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150, 0xF, 0xF, true);
 }
 
-// Work-group -> (head, slice); a head's slices share one XCD when N % 8 == 0.
-__device__ __forceinline__ void wg_identity(int N, int S, int& n, int& slice) {
-  const int wg = blockIdx.x;
-  if ((N & 7) == 0) {
-    const int xcd = wg & 7;
-    const int r = wg >> 3;
-    n = (r / S) * 8 + xcd;
-    slice = r % S;
-  } else {
-    n = wg / S;
-    slice = wg % S;
+__device__ __forceinline__ f16x2 as_h2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
+__device__ __forceinline__ uint32_t as_u(f16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Largest |x| of the eight bf16 values in a 16-byte group, as a bf16 bit
+// pattern: |x| orders like the low 15 bits of the pattern.
+__device__ __forceinline__ uint32_t absmax_bits(uint4 w) {
+  const uint32_t m0 = max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu);
+  const uint32_t m1 = max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu);
+  const uint32_t m2 = max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu);
+  const uint32_t m3 = max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu);
+  return max(max(m0, m1), max(m2, m3));
+}
+
+// Eight bf16 values times 2^e, rounded to float16 (nearest even).
+__device__ __forceinline__ uint4 bf16x8_to_f16_scaled(uint4 w, int e) {
+  const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_ldexpf(bf16f(in[i] & 0xFFFFu), e);
+    const float hi = __builtin_ldexpf(bf16f(in[i] >> 16), e);
+    out[i] = as_u(f16x2{(_Float16)lo, (_Float16)hi});
   }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// Work-group -> (head, feature slice, value half); a head's work-groups share
+// one XCD when N % 8 == 0.
+__device__ __forceinline__ void wg_identity(int N, int SF, int& n, int& sf, int& ch) {
+  const int wg = blockIdx.x;
+  const int per = 2 * SF;
+  int local;
+  if ((N & 7) == 0) {
+    const int r = wg >> 3;
+    n = (r / per) * 8 + (wg & 7);
+    local = r % per;
+  } else {
+    n = wg / per;
+    local = wg % per;
+  }
+  sf = local >> 1;
+  ch = local & 1;
 }
 
 // ------------------------------------------------------------ tile structure
-
-constexpr int kUW = 4;                            // update waves (own G, s)
-constexpr int kRW = 4;                            // readout waves
-constexpr int kThreads3 = 64 * (kUW + kRW);
-constexpr int kCS = 64;                           // staged sub-chunk (tokens), at most
-constexpr int kQS = kDim + 4;                     // q row stride (floats)
-constexpr int kKS = kCS + 4;                      // k^T row stride (floats)
 
 // Block pairs X <= Y in order (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3).
 __host__ __device__ constexpr int bp_x(int bp) { return bp < 4 ? 0 : bp < 7 ? 1 : bp < 9 ? 2 : 3; }
@@ -131,41 +177,45 @@ __host__ __device__ constexpr int factor_bp(int G, int i) {
   return G == 1 ? i : G == 2 ? (i < 2 ? i : i == 2 ? 4 : i + 4) : (i == 0 ? 0 : i == 1 ? 4 : i == 2 ? 7 : 9);
 }
 
-// The tiles of one slice. S = 8: tile u is (block pair u / 2, j = j0 + u % 2)
-// with j0 = 2 * slice; S = 16: tile u is (block pair u, j = slice), block
-// pairs taken from the factor structure's list. Readout pairs are tiles
-// (2p, 2p + 1); update wave w and readout half h take contiguous shares.
-template <int S, int G>
+// The tiles of one feature slice: SF = 4 slices hold j = 4 sf + jj (jj < 4),
+// SF = 8 slices j = 2 sf + jj (jj < 2), each over the factor structure's
+// block pairs. Tile u is (jj = u / kBP, block pair u % kBP); update wave w
+// owns tiles [w kNU, (w + 1) kNU), which share one jj; readout pair p is
+// tiles (2p, 2p + 1), and readout half h owns pairs [h kNP, (h + 1) kNP).
+template <int SF, int G>
 struct Slice {
-  static_assert(S == 8 || S == 16, "slices per head");
+  static_assert(SF == 4 || SF == 8, "feature slices per head");
   static_assert(G == 1 || G == 2 || G == 4, "factors");
   static constexpr int kBP = factor_bps(G);
-  static constexpr int kTiles = S == 8 ? 2 * kBP : kBP;
+  static constexpr int kJ = 16 / SF;
+  static constexpr int kTiles = kJ * kBP;
   static constexpr int kPairs = kTiles / 2;
-  static constexpr int kJ = S == 8 ? 2 : 1;  // values of j in a slice
-  __host__ __device__ static constexpr int bp(int u) { return factor_bp(G, S == 8 ? u >> 1 : u); }
-  __host__ __device__ static constexpr int jj(int u) { return S == 8 ? (u & 1) : 0; }
+  static constexpr int kNU = kTiles / kUW;
+  static constexpr int kNP = kPairs / 2;
+  static_assert(kTiles % kUW == 0 && kPairs % 2 == 0 && kBP % kNU == 0, "tile split");
+  static constexpr int kNB = 4 * kJ;  // Gram columns b of a slice
+  __host__ __device__ static constexpr int jj(int u) { return u / kBP; }
+  __host__ __device__ static constexpr int bp(int u) { return factor_bp(G, u % kBP); }
   __host__ __device__ static constexpr int X(int u) { return bp_x(bp(u)); }
   __host__ __device__ static constexpr int Y(int u) { return bp_y(bp(u)); }
-  // update wave w owns tiles [upd_first(w), upd_first(w) + upd_count(w))
-  __host__ __device__ static constexpr int upd_count(int w) { return kTiles / 4 + (w < kTiles % 4 ? 1 : 0); }
-  __host__ __device__ static constexpr int upd_first(int w) { return w * (kTiles / 4) + (w < kTiles % 4 ? w : kTiles % 4); }
-  // readout half h owns pairs [rd_first(h), rd_first(h) + rd_count(h))
-  __host__ __device__ static constexpr int rd_first(int h) { return h * ((kPairs + 1) / 2); }
-  __host__ __device__ static constexpr int rd_count(int h) { return h == 0 ? (kPairs + 1) / 2 : kPairs / 2; }
-  __host__ __device__ static constexpr bool upd_uses_x(int w, int b) {
-    for (int u = upd_first(w); u < upd_first(w) + upd_count(w); ++u)
-      if (X(u) == b) return true;
+  __host__ __device__ static constexpr bool upd_uses_x(int w, int x) {
+    for (int u = w * kNU; u < (w + 1) * kNU; ++u)
+      if (X(u) == x) return true;
     return false;
   }
-  __host__ __device__ static constexpr bool upd_uses_y(int w, int b) {
-    for (int u = upd_first(w); u < upd_first(w) + upd_count(w); ++u)
-      if (Y(u) == b) return true;
+  __host__ __device__ static constexpr bool upd_uses_y(int w, int y) {
+    for (int u = w * kNU; u < (w + 1) * kNU; ++u)
+      if (Y(u) == y) return true;
     return false;
   }
-  __host__ __device__ static constexpr bool rd_uses_x(int h, int b) {
-    for (int u = 2 * rd_first(h); u < 2 * (rd_first(h) + rd_count(h)); ++u)
-      if (X(u) == b) return true;
+  __host__ __device__ static constexpr bool rd_uses_x(int h, int x) {
+    for (int u = 2 * h * kNP; u < 2 * (h + 1) * kNP; ++u)
+      if (X(u) == x) return true;
+    return false;
+  }
+  __host__ __device__ static constexpr bool rd_uses_y(int h, int y) {
+    for (int u = 2 * h * kNP; u < 2 * (h + 1) * kNP; ++u)
+      if (Y(u) == y) return true;
     return false;
   }
 };
@@ -180,67 +230,58 @@ __device__ __forceinline__ int feat_abi(int a, int b) {
   return f * (p * (p + 1) / 2) + i * p - i * (i - 1) / 2 + (j - i);
 }
 
-template <int S, int G>
+template <int G>
+__host__ __device__ __forceinline__ bool same_factor(int a, int b) {
+  constexpr int p = kDim / G;
+  return a / p == b / p;
+}
+
+template <int SF, int G>
 struct StateLds {
+  uint4 hs[Slice<SF, G>::kPairs][2][64];  // weighted state, float16 B fragments
+  f32x4 xs[kRW][2][64];                   // readout trade: one token tile's accumulators
   // staged sub-chunks, double buffered (the next is staged during this one)
-  float qs[2][kCS][kQS];                          // q rows (fp32)
-  float kt[2][kDim][kKS];                         // k transposed (fp32)
-  uint16_t vt[2][kDim][kCS + 8];                  // v transposed (bf16)
-  uint4 hs[Slice<S, G>::kPairs][4][64];           // G at the chunk start, bf16 B fragments
-  uint4 ss[Slice<S, G>::kPairs][4];               // s as bf16 per pair and lane quarter
-  f32x4 xs[kRW][5][64];                           // readout trade: one token tile's accumulators
+  _Float16 qs[2][kCS][kDim + kPad];       // q rows, scaled per token
+  _Float16 kt[2][kDim][kCS + kPad];       // k columns, scaled per sub-chunk
+  uint16_t kr[2][kDim][kCS + kPad];       // raw k columns (bf16), for the Gram matrix
+  _Float16 vt[2][kCols][kCS + kPad];      // v columns of the work-group's half, scaled
+  int qe[2][kCS];                         // per-token query exponent
+  int sc[2][2];                           // per buffer: key exponent ek, state exponent G
+  float qmx[kRW][kCS];                    // staging: per wave and token, max |q| over its dims
+  float kvmx[kRW][2];                     // staging: per wave, max |k| and max |v|
+  float umx[kUW];                         // per update wave, max |state|
+  int pub_e;                              // exponent of the published state (G + P)
 };
 
 // LDS-only work-group barrier: waits for this wave's LDS traffic, not for
-// outstanding global loads or atomics.
+// outstanding global loads.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
 }
 
-// One 16-byte group (8 dims) of q, k and v for one token of the next
-// sub-chunk. The loads are unconditional (a token past the end reads the last
-// row and is zeroed at staging), so that no branch has to wait for them.
+// One token's share of a sub-chunk for staging wave W: q and k dims
+// 16 W .. 16 W + 15, v dims 32 ch + 8 W .. + 7. The loads are unconditional (a
+// token past the end reads the last row and is zeroed), so that no branch
+// has to wait for them.
 struct Prefetch {
-  uint4 q, k, v;
+  uint4 q[2], k[2], v;
   bool ok;
 };
 
 __device__ __forceinline__ Prefetch prefetch(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                              const uint16_t* __restrict__ v, size_t row0, int n0, int T, int t,
-                                             int grp) {
+                                             int W, int ch) {
   Prefetch p;
-  const size_t off = (row0 + min(n0 + t, T - 1)) * kDim + 8 * grp;
-  p.q = *reinterpret_cast<const uint4*>(q + off);
-  p.k = *reinterpret_cast<const uint4*>(k + off);
-  p.v = *reinterpret_cast<const uint4*>(v + off);
+  const size_t row = (row0 + min(n0 + t, T - 1)) * kDim;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    p.q[g] = *reinterpret_cast<const uint4*>(q + row + 16 * W + 8 * g);
+    p.k[g] = *reinterpret_cast<const uint4*>(k + row + 16 * W + 8 * g);
+  }
+  p.v = *reinterpret_cast<const uint4*>(v + row + kCols * ch + 8 * W);
   p.ok = n0 + t < T;
   return p;
-}
-
-// Staging: thread (token t, 8-dim group grp) writes q as fp32 rows, k as
-// fp32 columns and v as bf16 columns.
-// FULL: every token of the sub-chunk exists, so nothing is zeroed.
-template <bool FULL, class Lds>
-__device__ __forceinline__ void stage(Lds& sh, const Prefetch& p, int t, int grp, int buf) {
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  const bool ok = FULL || p.ok;
-  const uint4 pq = ok ? p.q : z, pk = ok ? p.k : z, pv = ok ? p.v : z;
-  const uint32_t qw[4] = {pq.x, pq.y, pq.z, pq.w};
-  const uint32_t kw[4] = {pk.x, pk.y, pk.z, pk.w};
-  const uint32_t vw[4] = {pv.x, pv.y, pv.z, pv.w};
-  const int d0 = 8 * grp;
-  const float4 lo = make_float4(bf16f(qw[0] & 0xFFFF), bf16f(qw[0] >> 16), bf16f(qw[1] & 0xFFFF), bf16f(qw[1] >> 16));
-  const float4 hi = make_float4(bf16f(qw[2] & 0xFFFF), bf16f(qw[2] >> 16), bf16f(qw[3] & 0xFFFF), bf16f(qw[3] >> 16));
-  *reinterpret_cast<float4*>(&sh.qs[buf][t][d0]) = lo;
-  *reinterpret_cast<float4*>(&sh.qs[buf][t][d0 + 4]) = hi;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    sh.kt[buf][d0 + 2 * e][t] = bf16f(kw[e] & 0xFFFF);
-    sh.kt[buf][d0 + 2 * e + 1][t] = bf16f(kw[e] >> 16);
-    sh.vt[buf][d0 + 2 * e][t] = (uint16_t)(vw[e] & 0xFFFF);
-    sh.vt[buf][d0 + 2 * e + 1][t] = (uint16_t)(vw[e] >> 16);
-  }
 }
 
 // Everything a wave of the state kernel needs about its work-group.
@@ -248,166 +289,320 @@ struct StateCtx {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  int T, NC, S, n, slice, j0;
+  int T, NC, n, sf, ch, j0;
   int D;  // features per head in the ABI layout
   const float* H0;
   const float* s0;
   float* HT;
   float* sT;
-  uint16_t* part;  // slice partials [head, chunk, slice, token tile, kTileAcc], or NULL
+  float* part;  // slice partials [head, chunk, slice, token tile, kTilePart], or NULL
+  float* Sg;    // Gram matrix at each chunk start [head, chunk, 64, 64], or NULL
 };
+
+// Staging, first pass (before the middle barrier): maxima of the prefetched
+// values. Lane t < CS holds token t.
+template <int CS, class Lds>
+__device__ __forceinline__ void stage_max(Lds& sh, const Prefetch& p, int W, int lane) {
+  const bool act = lane < CS && p.ok;
+  uint32_t qm = 0, km = 0, vm = 0;
+  if (act) {
+    qm = max(absmax_bits(p.q[0]), absmax_bits(p.q[1]));
+    km = max(absmax_bits(p.k[0]), absmax_bits(p.k[1]));
+    vm = absmax_bits(p.v);
+  }
+  if (lane < CS) sh.qmx[W][lane] = bf16f(qm);
+  const float kw = wave_max(bf16f(km));
+  const float vw = wave_max(bf16f(vm));
+  if (lane == 0) {
+    sh.kvmx[W][0] = kw;
+    sh.kvmx[W][1] = vw;
+  }
+}
+
+// The running state exponent: once the accumulators may hold something (an
+// imported state, or a sub-chunk with nonzero keys and values) it only grows;
+// before that it follows the first nonzero sub-chunk.
+struct ExpTrack {
+  int G = 0;
+  bool live = false;
+  __device__ void see(int E) {
+    G = live ? max(G, E) : E;
+    live = true;
+  }
+};
+
+// Staging, second pass (after the middle barrier): scales and scaled values
+// into buffer `buf`.
+template <int CS, class Lds>
+__device__ __forceinline__ void stage_write(Lds& sh, const Prefetch& p, int W, int lane, int buf, ExpTrack& g) {
+  const float kall = fmaxf(fmaxf(sh.kvmx[0][0], sh.kvmx[1][0]), fmaxf(sh.kvmx[2][0], sh.kvmx[3][0]));
+  const float vall = fmaxf(fmaxf(sh.kvmx[0][1], sh.kvmx[1][1]), fmaxf(sh.kvmx[2][1], sh.kvmx[3][1]));
+  const int ekr = exp_above(kall), ev = exp_above(vall);
+  // a sub-chunk whose keys or values are all zero adds nothing: its values
+  // are staged as zeros and the exponent does not move
+  const bool contributes = ekr != kNoExp && ev != kNoExp;
+  if (contributes) g.see(2 * ekr + ev);
+  const int ek = ekr == kNoExp ? 0 : ekr;
+  if (lane < CS) {
+    const int t = lane;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 q0 = p.ok ? p.q[0] : z, q1 = p.ok ? p.q[1] : z;
+    const uint4 k0 = p.ok ? p.k[0] : z, k1 = p.ok ? p.k[1] : z;
+    const uint4 vv = p.ok && contributes ? p.v : z;
+    const float qm = fmaxf(fmaxf(sh.qmx[0][t], sh.qmx[1][t]), fmaxf(sh.qmx[2][t], sh.qmx[3][t]));
+    const int eqr = exp_above(qm);
+    const int eq = eqr == kNoExp ? 0 : eqr;
+    *reinterpret_cast<uint4*>(&sh.qs[buf][t][16 * W]) = bf16x8_to_f16_scaled(q0, -eq);
+    *reinterpret_cast<uint4*>(&sh.qs[buf][t][16 * W + 8]) = bf16x8_to_f16_scaled(q1, -eq);
+    if (W == 0) sh.qe[buf][t] = eq;
+    const uint4 kh0 = bf16x8_to_f16_scaled(k0, -ek), kh1 = bf16x8_to_f16_scaled(k1, -ek);
+    const uint32_t kraw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const uint32_t kh[8] = {kh0.x, kh0.y, kh0.z, kh0.w, kh1.x, kh1.y, kh1.z, kh1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 16 * W + 2 * e;
+      sh.kr[buf][d][t] = (uint16_t)(kraw[e] & 0xFFFFu);
+      sh.kr[buf][d + 1][t] = (uint16_t)(kraw[e] >> 16);
+      sh.kt[buf][d][t] = as_h2(kh[e])[0];
+      sh.kt[buf][d + 1][t] = as_h2(kh[e])[1];
+    }
+    const uint4 vh = bf16x8_to_f16_scaled(vv, contributes ? 2 * ek - g.G : 0);
+    const uint32_t vw[4] = {vh.x, vh.y, vh.z, vh.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sh.vt[buf][8 * W + 2 * e][t] = as_h2(vw[e])[0];
+      sh.vt[buf][8 * W + 2 * e + 1][t] = as_h2(vw[e])[1];
+    }
+  }
+  if (W == 0 && lane == 0) {
+    sh.sc[buf][0] = ek;
+    sh.sc[buf][1] = g.G;
+  }
+}
 
 // ------------------------------------------------------------- update waves
 
-template <int C, int CS, int S, int G, int W>
-__device__ __forceinline__ void update_wave(StateLds<S, G>& sh, const StateCtx& cx) {
-  using SL = Slice<S, G>;
-  constexpr int U0 = SL::upd_first(W);
-  constexpr int NU = SL::upd_count(W);
+template <int C, int CS, int SF, int G, int W>
+__device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx& cx) {
+  using SL = Slice<SF, G>;
+  constexpr int U0 = W * SL::kNU;
+  constexpr int NU = SL::kNU;
+  constexpr int JJ = SL::jj(U0);  // one value of j per update wave
   constexpr int SUB = C / CS;
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
   const int nsteps = cx.NC * SUB;
+  const int j = cx.j0 + JJ;
   const float inv_sqrt2 = 0.70710678118654752f;
+  const bool gram_wg = cx.ch == 0;  // the first value half also forms the Gram matrix
 
-  // G (value n-tiles 0..3) and s (n-tile 4, column 0) of each owned tile;
+  // Gram column of this lane: the slice's b values 16 Y + j0 + jj
+  const int gb = 16 * (l16 / SL::kJ) + cx.j0 + (l16 % SL::kJ);
+  const bool gb_ok = l16 < SL::kNB;
+
+  // G (value n-tiles 0, 1 of the work-group's half) of each owned tile;
   // lane (l16, q4) holds rows 4 q4 + i, column l16 of an n-tile
-  f32x4 h[NU][5];
+  f32x4 h[NU][2];
+  f32x4 gram = {0.f, 0.f, 0.f, 0.f};
+  float hmax = 0.0f;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const int a0 = 16 * SL::X(U0 + u) + 4 * q4;
-    const int b = 16 * SL::Y(U0 + u) + cx.j0 + SL::jj(U0 + u);
+    const int b = 16 * SL::Y(U0 + u) + j;
 #pragma unroll
-    for (int nt = 0; nt < 5; ++nt) h[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt) h[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (cx.H0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int a = a0 + i;
-      const size_t f = (size_t)cx.n * cx.D + feat_abi<G>(min(a, b), max(a, b));
-      const float sc = a != b ? inv_sqrt2 : 1.0f;
-      if (cx.H0) {
+      for (int i = 0; i < 4; ++i) {
+        const int a = a0 + i;
+        if (a > b) continue;  // mirror rows of a diagonal block are never imported
+        const size_t f = (size_t)cx.n * cx.D + feat_abi<G>(a, b);
+        const float scl = a != b ? inv_sqrt2 : 1.0f;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) h[u][nt][i] = cx.H0[f * kDim + 16 * nt + l16] * sc;
+        for (int nt = 0; nt < 2; ++nt) {
+          const float x = cx.H0[f * kDim + kCols * cx.ch + 16 * nt + l16] * scl;
+          h[u][nt][i] = x;
+          hmax = fmaxf(hmax, fabsf(x));
+        }
       }
-      if (cx.s0 && l16 == 0) h[u][4][i] = cx.s0[f] * sc;
     }
   }
-
-  // B operand of the s n-tile: column 0 is all ones
-  bf16x8 ones;
+  if (gram_wg && cx.s0 && gb_ok) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
+    for (int i = 0; i < 4; ++i) {
+      const int a = 16 * W + 4 * q4 + i;
+      if (a <= gb && same_factor<G>(a, gb))
+        gram[i] = cx.s0[(size_t)cx.n * cx.D + feat_abi<G>(a, gb)] * (a != gb ? inv_sqrt2 : 1.0f);
+    }
+  }
+  hmax = wave_max(hmax);
+  if (lane == 0) sh.umx[W] = hmax;
 
-  auto publish = [&]() {
+  int Gu = 0;  // the accumulators hold G 2^-Gu
+  // publish the state at the start of chunk c; m = max |h| in current units
+  auto publish = [&](int c, float m) {
+    // the largest weighted entry stays below 2^15 in float16
+    const int em = exp_above(2.0f * m);
+    const int P = em == kNoExp ? 0 : em - 15;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+      const int X = SL::X(U0 + u), Y = SL::Y(U0 + u);
       const int pr = (U0 + u) >> 1;
       const int half = (U0 + u) & 1;
+      // readout weight of each row: 2 off the diagonal blocks; on them 2 for
+      // a < b, 1 for a = b, 0 for the mirror rows a > b
+      float wr[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        bf16x4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (__bf16)h[u][nt][i];
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&sh.hs[pr][nt][lane]) + 8 * half) = x;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * q4 + i;
+        const float w = X < Y ? 2.0f : (r < j ? 2.0f : (r == j ? 1.0f : 0.0f));
+        wr[i] = __builtin_ldexpf(w, -P);
       }
-      if (l16 == 0) {
-        bf16x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (__bf16)h[u][4][i];
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&sh.ss[pr][q4]) + 8 * half) = x;
+      for (int nt = 0; nt < 2; ++nt) {
+        const f16x2 lo = {(_Float16)(h[u][nt][0] * wr[0]), (_Float16)(h[u][nt][1] * wr[1])};
+        const f16x2 hi = {(_Float16)(h[u][nt][2] * wr[2]), (_Float16)(h[u][nt][3] * wr[3])};
+        uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<char*>(&sh.hs[pr][nt][lane]) + 8 * half);
+        *dst = make_uint2(as_u(lo), as_u(hi));
+      }
+    }
+    if (W == 0 && lane == 0) sh.pub_e = Gu + P;
+    // the Gram matrix at the start of chunk c: each entry a <= b is written by
+    // its owner at (a, b) and (b, a)
+    if (gram_wg && cx.Sg && c < cx.NC && gb_ok) {
+      float* S = cx.Sg + ((size_t)cx.n * cx.NC + c) * kDim * kDim;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = 16 * W + 4 * q4 + i;
+        if (a <= gb) {
+          S[a * kDim + gb] = gram[i];
+          S[gb * kDim + a] = gram[i];
+        }
       }
     }
   };
-  publish();  // the state at the start of chunk 0
 
-  // k_b sources: lane j' < kJ of each row holds k[token][16 Y + j0 + j']; the
-  // other lanes keep whatever they held (only these lanes are broadcast)
-  float kr[4][8];
+  lds_barrier();  // (B0a) state maxima and the first sub-chunk's maxima posted
+  lds_barrier();  // (B0b) first sub-chunk staged with its exponents
+  Gu = __builtin_amdgcn_readfirstlane(sh.sc[0][1]);
+  {
+    const float s = __builtin_ldexpf(1.0f, -Gu);
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kr[b][i] = 0.0f;
+      for (int nt = 0; nt < 2; ++nt) h[u][nt] *= s;
+    const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
+    publish(0, m * s);  // the state at the start of chunk 0
+  }
+  lds_barrier();  // (B0c) initial state published
 
-  lds_barrier();  // (B0) initial state published, first sub-chunk staged
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
+    const int Gn = __builtin_amdgcn_readfirstlane(sh.sc[buf][1]);
+    if (Gn != Gu) {  // uniform: the state exponent moved
+      const float s = __builtin_ldexpf(1.0f, Gu - Gn);
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) h[u][nt] *= s;
+      Gu = Gn;
+    }
 #pragma unroll
     for (int ks = 0; ks < CS / 32; ++ks) {
       const int t0 = ks * 32 + 8 * q4;
-      bf16x8 vb[4];
+      f16x8 vb[2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = *reinterpret_cast<const bf16x8*>(&sh.vt[buf][16 * nt + l16][t0]);
-      float ka[4][8];
+      for (int nt = 0; nt < 2; ++nt) vb[nt] = *reinterpret_cast<const f16x8*>(&sh.vt[buf][16 * nt + l16][t0]);
+      uint4 ka[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (SL::upd_uses_x(W, b)) {
-          const float4* p = reinterpret_cast<const float4*>(&sh.kt[buf][16 * b + l16][t0]);
-          const float4 x0 = p[0], x1 = p[1];
-          ka[b][0] = x0.x; ka[b][1] = x0.y; ka[b][2] = x0.z; ka[b][3] = x0.w;
-          ka[b][4] = x1.x; ka[b][5] = x1.y; ka[b][6] = x1.z; ka[b][7] = x1.w;
-        }
-      }
-      if (l16 < SL::kJ) {
+      for (int x = 0; x < 4; ++x)
+        if (SL::upd_uses_x(W, x)) ka[x] = *reinterpret_cast<const uint4*>(&sh.kt[buf][16 * x + l16][t0]);
+      uint4 kb[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (SL::upd_uses_y(W, b)) {
-            const float4* p = reinterpret_cast<const float4*>(&sh.kt[buf][16 * b + cx.j0 + l16][t0]);
-            const float4 x0 = p[0], x1 = p[1];
-            kr[b][0] = x0.x; kr[b][1] = x0.y; kr[b][2] = x0.z; kr[b][3] = x0.w;
-            kr[b][4] = x1.x; kr[b][5] = x1.y; kr[b][6] = x1.z; kr[b][7] = x1.w;
-          }
+      for (int y = 0; y < 4; ++y) {
+        if (SL::upd_uses_y(W, y)) {
+          uint4 src = make_uint4(0, 0, 0, 0);
+          if (l16 == 0) src = *reinterpret_cast<const uint4*>(&sh.kt[buf][16 * y + j][t0]);
+          kb[y] = make_uint4(row_bcast0(src.x), row_bcast0(src.y), row_bcast0(src.z), row_bcast0(src.w));
         }
       }
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const int X = SL::X(U0 + u);
-        const int Y = SL::Y(U0 + u);
-        const int J = SL::jj(U0 + u);
-        float p[8];
+        const uint4 xa = ka[SL::X(U0 + u)];
+        const uint4 xb = kb[SL::Y(U0 + u)];
+        const uint32_t p0 = as_u(as_h2(xa.x) * as_h2(xb.x));
+        const uint32_t p1 = as_u(as_h2(xa.y) * as_h2(xb.y));
+        const uint32_t p2 = as_u(as_h2(xa.z) * as_h2(xb.z));
+        const uint32_t p3 = as_u(as_h2(xa.w) * as_h2(xb.w));
+        const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(p0, p1, p2, p3));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = ka[X][i] * (J == 0 ? row_bcast<0>(kr[Y][i]) : row_bcast<1>(kr[Y][i]));
-        const bf16x8 A = pack8(p);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) h[u][nt] = mfma(A, vb[nt], h[u][nt]);
-        h[u][4] = mfma(A, ones, h[u][4]);
+        for (int nt = 0; nt < 2; ++nt) h[u][nt] = mfma_h(A, vb[nt], h[u][nt]);
+      }
+      if (gram_wg) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.kr[buf][16 * W + l16][t0]);
+        bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        if (gb_ok) B = *reinterpret_cast<const bf16x8*>(&sh.kr[buf][gb][t0]);
+        gram = mfma_b(A, B, gram);
       }
     }
-    lds_barrier();  // (B2) sub-chunk consumed, readouts done
-    if (st % SUB == SUB - 1) publish();
+    const bool chunk_end = st % SUB == SUB - 1;
+    if (chunk_end) {
+      float m = 0.0f;
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(h[u][nt][i]));
+      m = wave_max(m);
+      if (lane == 0) sh.umx[W] = m;
+    }
+    lds_barrier();  // (B2) sub-chunk consumed, readouts done, maxima posted
+    if (chunk_end) {
+      const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
+      publish(st / SUB + 1, m);
+    }
     lds_barrier();  // (B1) state published, next sub-chunk staged
   }
 
-  // final state in the ABI layout (sqrt(2) on the off-diagonal features);
-  // of a diagonal block's ordered pairs only a <= b is written
+  // final state in the ABI layout (sqrt(2) on the off-diagonal features)
   const float sqrt2 = 1.41421356237309504880f;
+  if (cx.HT) {
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int a0 = 16 * SL::X(U0 + u) + 4 * q4;
-    const int b = 16 * SL::Y(U0 + u) + cx.j0 + SL::jj(U0 + u);
+    for (int u = 0; u < NU; ++u) {
+      const int a0 = 16 * SL::X(U0 + u) + 4 * q4;
+      const int b = 16 * SL::Y(U0 + u) + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a = a0 + i;
+        if (a > b) continue;
+        const size_t f = (size_t)cx.n * cx.D + feat_abi<G>(a, b);
+        const float scl = __builtin_ldexpf(a < b ? sqrt2 : 1.0f, Gu);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) cx.HT[f * kDim + kCols * cx.ch + 16 * nt + l16] = h[u][nt][i] * scl;
+      }
+    }
+  }
+  if (gram_wg && cx.sT && gb_ok) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int a = a0 + i;
-      if (a > b) continue;
-      const size_t f = (size_t)cx.n * cx.D + feat_abi<G>(a, b);
-      const float sc = a < b ? sqrt2 : 1.0f;
-      if (cx.HT) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) cx.HT[f * kDim + 16 * nt + l16] = h[u][nt][i] * sc;
-      }
-      if (cx.sT && l16 == 0) cx.sT[f] = h[u][4][i] * sc;
+      const int a = 16 * W + 4 * q4 + i;
+      if (a <= gb && same_factor<G>(a, gb))
+        cx.sT[(size_t)cx.n * cx.D + feat_abi<G>(a, gb)] = gram[i] * (a < gb ? sqrt2 : 1.0f);
     }
   }
 }
 
 // ------------------------------------------------------------ readout waves
 
-template <int C, int CS, int S, int G, int W>
-__device__ __forceinline__ void readout_wave(StateLds<S, G>& sh, const StateCtx& cx) {
-  using SL = Slice<S, G>;
-  constexpr int HF = W & 1;                       // half of the pairs
-  constexpr int TP = W >> 1;                      // token tiles 2 TP, 2 TP + 1 of a sub-chunk
-  constexpr int P0 = SL::rd_first(HF);
-  constexpr int NP = SL::rd_count(HF);
+template <int C, int CS, int SF, int G, int W>
+__device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx& cx) {
+  using SL = Slice<SF, G>;
+  constexpr int HF = W & 1;   // half of the pairs
+  constexpr int TP = W >> 1;  // token tiles 2 TP, 2 TP + 1 of a sub-chunk
+  constexpr int P0 = HF * SL::kNP;
+  constexpr int NP = SL::kNP;
   constexpr int SUB = C / CS;
   constexpr bool kActive = 32 * TP < CS;
   const int lane = threadIdx.x & 63;
@@ -417,174 +612,167 @@ __device__ __forceinline__ void readout_wave(StateLds<S, G>& sh, const StateCtx&
   const int nsteps = cx.NC * SUB;
   const bool active = kActive && cx.part != nullptr;
 
-  // the own token tile (2 TP + HF) of the previous sub-step, kept across its
-  // closing barrier until the partner's half has been added
-  f32x4 keep[5];
+  f32x4 keep[2];
 #pragma unroll
-  for (int nt = 0; nt < 5; ++nt) keep[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 2; ++nt) keep[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto flush = [&](int st) {
-    // add the partner's half of the own token tile, write the slice partial
+  auto flush = [&](int st, int buf, int pe) {
+    // add the partner's half of the own token tile, undo the scales
+    // (per-token query exponent, published-state exponent) and write the
+    // float32 partial
     const f32x4* xs = &sh.xs[W ^ 1][0][0];
+    const int tl = 16 * (2 * TP + HF) + 4 * q4;  // tokens tl + i of the sub-chunk
+    float f[4];
 #pragma unroll
-    for (int nt = 0; nt < 5; ++nt) {
-      const f32x4 o = xs[nt * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) keep[nt][i] += o[i];
-    }
+    for (int i = 0; i < 4; ++i) f[i] = __builtin_ldexpf(1.0f, 2 * sh.qe[buf][tl + i] + pe);
     const int c = st / SUB;
     const int tt = ((st % SUB) * CS) / 16 + 2 * TP + HF;
-    uint16_t* pc = cx.part + ((((size_t)cx.n * cx.NC + c) * cx.S + cx.slice) * (C / 16) + tt) * kTileAcc;
+    float* pc = cx.part + ((((size_t)cx.n * cx.NC + c) * SF + cx.sf) * (C / 16) + tt) * kTilePart;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      bf16x4 b;
+    for (int nt = 0; nt < 2; ++nt) {
+      const f32x4 o = xs[nt * 64 + lane];
+      f32x4 r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = (__bf16)keep[nt][i];
-      *reinterpret_cast<bf16x4*>(pc + (nt * 64 + lane) * 4) = b;
-    }
-    if (l16 == 0) {
-      bf16x4 b;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = (__bf16)keep[4][i];
-      *reinterpret_cast<bf16x4*>(pc + 4 * 64 * 4 + 4 * q4) = b;
+      for (int i = 0; i < 4; ++i) r[i] = (keep[nt][i] + o[i]) * f[i];
+      *reinterpret_cast<f32x4*>(pc + ((2 * cx.ch + nt) * 64 + lane) * 4) = r;
     }
   };
 
-  // The readout waves stage the sub-chunks for the whole work-group (wave W:
-  // 8-dim groups 2W and 2W + 1 of every token): the next sub-chunk into the
-  // other buffer while this one is computed, with its loads issued a whole
-  // sub-step earlier.
-  auto pre = [&](int st, Prefetch (&p)[2]) {
+  auto pre = [&](int st) {
     const int n0 = (st / SUB) * C + (st % SUB) * CS;
-#pragma unroll
-    for (int g = 0; g < 2; ++g) p[g] = prefetch(cx.q, cx.k, cx.v, row0, n0, cx.T, lane, 2 * W + g);
+    return prefetch(cx.q, cx.k, cx.v, row0, n0, cx.T, lane, W, cx.ch);
   };
-  auto stage2 = [&](const Prefetch (&p)[2], int buf, int st) {
-    if (lane < CS) {
-      if ((st / SUB) * C + (st % SUB) * CS + CS <= cx.T) {  // uniform: a full sub-chunk
-        stage<true>(sh, p[0], lane, 2 * W, buf);
-        stage<true>(sh, p[1], lane, 2 * W + 1, buf);
-      } else {
-        stage<false>(sh, p[0], lane, 2 * W, buf);
-        stage<false>(sh, p[1], lane, 2 * W + 1, buf);
-      }
-    }
-  };
-  Prefetch pf[2];
-  pre(0, pf);
-  stage2(pf, 0, 0);
-  pre(1, pf);  // past the end: clamped reads, never staged
-  lds_barrier();  // (B0)
+  ExpTrack g;
+  Prefetch pf = pre(0);
+  stage_max<CS>(sh, pf, W, lane);
+  lds_barrier();  // (B0a)
+  if (cx.H0) {
+    // an imported state: the exponent starts where the accumulators hold it
+    // below 2^100 and then only grows
+    const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
+    const int e = exp_above(m);
+    if (e != kNoExp) g.see(e - 100);
+  }
+  stage_write<CS>(sh, pf, W, lane, 0, g);
+  if (nsteps > 1) pf = pre(1);
+  lds_barrier();  // (B0b)
+  lds_barrier();  // (B0c)
 
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
-    if (st + 1 < nsteps) {
-      stage2(pf, buf ^ 1, st + 1);
-      pre(st + 2, pf);
-    }
+    const int pe = sh.pub_e;  // published before this step's middle barrier
+    if (st + 1 < nsteps) stage_max<CS>(sh, pf, W, lane);
     if (active) {
-      // q factors of this lane's token in each of the two token tiles:
-      // qa[tt][X] = q[16 X + 4 q4 + 0..3], qb[tt][u] = w_u q[16 Y_u + j_u]
-      float qa[2][4][4];
-      float qb[2][2 * NP];
+      // q' factors of this lane's token in each of the two token tiles:
+      // qa[tt][X] = q'[16 X + 4 q4 + 0..3], qb[tt][Y] = q'[16 Y + j0 + 0..kJ-1]
+      uint2 qa[2][4];
+      uint32_t qb[2][4][SL::kJ / 2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const float* qrow = sh.qs[buf][32 * TP + 16 * tt + l16];
+        const _Float16* qrow = sh.qs[buf][32 * TP + 16 * tt + l16];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (SL::rd_uses_x(HF, b)) {
-            const float4 x = *reinterpret_cast<const float4*>(qrow + 16 * b + 4 * q4);
-            qa[tt][b][0] = x.x; qa[tt][b][1] = x.y; qa[tt][b][2] = x.z; qa[tt][b][3] = x.w;
+        for (int x = 0; x < 4; ++x)
+          if (SL::rd_uses_x(HF, x)) qa[tt][x] = *reinterpret_cast<const uint2*>(qrow + 16 * x + 4 * q4);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          if (SL::rd_uses_y(HF, y)) {
+            if constexpr (SL::kJ == 4) {
+              const uint2 w2 = *reinterpret_cast<const uint2*>(qrow + 16 * y + cx.j0);
+              qb[tt][y][0] = w2.x;
+              qb[tt][y][1] = w2.y;
+            } else {
+              qb[tt][y][0] = *reinterpret_cast<const uint32_t*>(qrow + 16 * y + cx.j0);
+            }
           }
         }
-#pragma unroll
-        for (int u = 0; u < 2 * NP; ++u) {
-          const int t = 2 * P0 + u;
-          const float w = SL::X(t) < SL::Y(t) ? 2.0f : 1.0f;
-          qb[tt][u] = w * qrow[16 * SL::Y(t) + cx.j0 + SL::jj(t)];
-        }
       }
-      // n-tiles 0..3: numerators; n-tile 4: the denominator in column 0
-      f32x4 acc[2][5];
+      f32x4 acc[2][2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int nt = 0; nt < 5; ++nt) acc[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int pr = P0 + p;
-        bf16x8 B[5];
+        f16x8 B[2];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) B[nt] = __builtin_bit_cast(bf16x8, sh.hs[pr][nt][lane]);
-        // s of this lane's k-slots in column 0, zero elsewhere
-        const uint4 sw = sh.ss[pr][q4];
-        B[4] = __builtin_bit_cast(bf16x8, l16 == 0 ? sw : make_uint4(0, 0, 0, 0));
-        const int X0 = SL::X(2 * pr);
-        const int X1 = SL::X(2 * pr + 1);
+        for (int nt = 0; nt < 2; ++nt) B[nt] = __builtin_bit_cast(f16x8, sh.hs[pr][nt][lane]);
+        constexpr int kU0 = 0;
+        const int u0 = 2 * pr + kU0, u1 = 2 * pr + 1;
+        const int X0 = SL::X(u0), X1 = SL::X(u1), Y0 = SL::Y(u0), Y1 = SL::Y(u1);
+        const int J0 = SL::jj(u0), J1 = SL::jj(u1);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          float f[8];
+          // q'_b of each tile, broadcast to both halves of a packed pair
+          const _Float16 b0 = as_h2(qb[tt][Y0][J0 >> 1])[J0 & 1];
+          const _Float16 b1 = as_h2(qb[tt][Y1][J1 >> 1])[J1 & 1];
+          const f16x2 bb0 = {b0, b0}, bb1 = {b1, b1};
+          const uint32_t p0 = as_u(as_h2(qa[tt][X0].x) * bb0);
+          const uint32_t p1 = as_u(as_h2(qa[tt][X0].y) * bb0);
+          const uint32_t p2 = as_u(as_h2(qa[tt][X1].x) * bb1);
+          const uint32_t p3 = as_u(as_h2(qa[tt][X1].y) * bb1);
+          const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(p0, p1, p2, p3));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f[i] = qa[tt][X0][i] * qb[tt][2 * p];
-            f[4 + i] = qa[tt][X1][i] * qb[tt][2 * p + 1];
-          }
-          const bf16x8 A = pack8(f);
-#pragma unroll
-          for (int nt = 0; nt < 5; ++nt) acc[tt][nt] = mfma(A, B[nt], acc[tt][nt]);
+          for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mfma_h(A, B[nt], acc[tt][nt]);
         }
       }
       // hand the partner its token tile, keep the own one
       f32x4* xs = &sh.xs[W][0][0];
 #pragma unroll
-      for (int nt = 0; nt < 5; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
         xs[nt * 64 + lane] = acc[1 - HF][nt];
         keep[nt] = acc[HF][nt];
       }
     }
     lds_barrier();  // (B2)
-    if (active) flush(st);
+    if (st + 1 < nsteps) {
+      stage_write<CS>(sh, pf, W, lane, buf ^ 1, g);
+      if (st + 2 < nsteps) pf = pre(st + 2);
+    }
+    if (active) flush(st, buf, pe);
     lds_barrier();  // (B1)
   }
 }
 
 // C: the chunk (intra-chunk region of the output); the state kernel stages it
 // in sub-chunks of CS tokens, all read out against the state at the chunk start.
-template <int C, int S, int G>
+template <int C, int SF, int G>
 __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int T,
     const float* __restrict__ H0, const float* __restrict__ s0, float* __restrict__ HT, float* __restrict__ sT,
-    uint16_t* __restrict__ part) {
+    float* __restrict__ part, float* __restrict__ Sg) {
   constexpr int CS = C < kCS ? C : kCS;
   static_assert(C % CS == 0 && CS % 32 == 0, "chunk must be a multiple of the sub-chunk");
-  __shared__ __align__(16) StateLds<S, G> sh;
+  __shared__ __align__(16) StateLds<SF, G> sh;
   StateCtx cx;
   cx.q = q;
   cx.k = k;
   cx.v = v;
   cx.T = T;
   cx.NC = (T + C - 1) / C;
-  cx.S = S;
   cx.D = G * (kDim / G) * (kDim / G + 1) / 2;
-  wg_identity(N, S, cx.n, cx.slice);
-  cx.j0 = S == 8 ? 2 * cx.slice : cx.slice;
+  wg_identity(N, SF, cx.n, cx.sf, cx.ch);
+  cx.j0 = Slice<SF, G>::kJ * cx.sf;
   cx.H0 = H0;
   cx.s0 = s0;
   cx.HT = HT;
   cx.sT = sT;
   cx.part = part;
+  cx.Sg = Sg;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wv) {
-    case 0: update_wave<C, CS, S, G, 0>(sh, cx); break;
-    case 1: update_wave<C, CS, S, G, 1>(sh, cx); break;
-    case 2: update_wave<C, CS, S, G, 2>(sh, cx); break;
-    case 3: update_wave<C, CS, S, G, 3>(sh, cx); break;
-    case 4: readout_wave<C, CS, S, G, 0>(sh, cx); break;
-    case 5: readout_wave<C, CS, S, G, 1>(sh, cx); break;
-    case 6: readout_wave<C, CS, S, G, 2>(sh, cx); break;
-    default: readout_wave<C, CS, S, G, 3>(sh, cx); break;
+    case 0: update_wave<C, CS, SF, G, 0>(sh, cx); break;
+    case 1: update_wave<C, CS, SF, G, 1>(sh, cx); break;
+    case 2: update_wave<C, CS, SF, G, 2>(sh, cx); break;
+    case 3: update_wave<C, CS, SF, G, 3>(sh, cx); break;
+    case 4: readout_wave<C, CS, SF, G, 0>(sh, cx); break;
+    case 5: readout_wave<C, CS, SF, G, 1>(sh, cx); break;
+    case 6: readout_wave<C, CS, SF, G, 2>(sh, cx); break;
+    default: readout_wave<C, CS, SF, G, 3>(sh, cx); break;
   }
 }
+
+// ------------------------------------------------------------ finish kernel
 
 template <int C>
 struct FinishLds {
@@ -613,7 +801,7 @@ __device__ __forceinline__ f32x4 finish_weights(const FinishLds<C>& sh, int kq, 
     for (int ks = 0; ks < kDim / 32; ++ks) {
       const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.ks[kq * 16 + l16][ks * 32 + 8 * q4]);
       const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.qs[mq * 16 + l16][ks * 32 + 8 * q4]);
-      s4 = mfma(A, B, G == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : s4);
+      s4 = mfma_b(A, B, G == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : s4);
       if (G == 2) w4 += s4 * s4;
     }
     if (G == 1) w4 = s4 * s4;
@@ -621,17 +809,18 @@ __device__ __forceinline__ f32x4 finish_weights(const FinishLds<C>& sh, int kq, 
   return w4;
 }
 
-// One work-group per (chunk, head): intra-chunk term + accumulator -> output.
-// The weights are formed transposed (keys as MFMA rows), so the accumulator
-// of two 16-key tiles already is the A operand of the 32-key step of A [V | 1]
-// when its k-slots are read as keys 4 q4 + i (i < 4) of the first tile and
-// 4 q4 + i - 4 of the second; the value fragments take the same key order.
-// The weights never leave registers.
+// One work-group per (chunk, head): intra-chunk term, the denominator's state
+// term q^T S q from the Gram matrix of the chunk start, the sum of the slice
+// partials -> output. The intra-chunk weights are formed transposed (keys as
+// MFMA rows), so the accumulator of two 16-key tiles already is the A operand
+// of the 32-key step of A V when its k-slots are read as keys 4 q4 + i (i < 4)
+// of the first tile and 4 q4 + i - 4 of the second; the value fragments take
+// the same key order. The weights never leave registers.
 template <int C, typename Tout, int G>
 __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ part, int S,
-    Tout* __restrict__ o, int T, float eps) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ part, const float* __restrict__ Sg, int SF, Tout* __restrict__ o, int T,
+    float eps) {
   __shared__ __align__(16) FinishLds<C> sh;
   const int c0 = blockIdx.x * C;
   const int n = blockIdx.y;
@@ -661,6 +850,33 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
       sh.vt[p + 2 * e + 1][t] = (uint16_t)(vw[e] >> 16);
     }
   }
+
+  // the Gram matrix at the chunk start as B fragments of two bf16 pieces:
+  // lane (column 16 nt + l16, dims 32 ks + 8 q4 + e); S is symmetric, so the
+  // fragment is row 16 nt + l16 of S. For G factors only the factors'
+  // diagonal blocks count (phi(q).s = sum over factors of q_f^T S_ff q_f).
+  bf16x8 Shi[2][4], Slo[2][4];
+  {
+    const float* S = Sg + ((size_t)n * gridDim.x + blockIdx.x) * kDim * kDim;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int col = 16 * nt + l16;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const float4* src = reinterpret_cast<const float4*>(S + col * kDim + 32 * ks + 8 * q4);
+        const float4 x0 = src[0], x1 = src[1];
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 32 * ks + 8 * q4 + e;
+          const float x = same_factor<G>(d, col) ? xv[e] : 0.0f;
+          const __bf16 hi = (__bf16)x;
+          Shi[ks][nt][e] = hi;
+          Slo[ks][nt][e] = (__bf16)(x - (float)hi);
+        }
+      }
+    }
+  }
   __syncthreads();
 
   for (int mq = w; mq < C / 16; mq += kWaves) {
@@ -671,7 +887,10 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
     const int qi = mq * 16 + l16;
     float dpart = 0.0f;
     for (int ks = 0; ks <= (mq >> 1); ++ks) {
-      bf16x8 A;
+      // the float32 weights as two bf16 pieces (hi + lo carries 16
+      // significant bits), so the numerator is formed from the same
+      // weights the float32 denominator sums
+      bf16x8 A, Alo;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kq = 2 * ks + h;
@@ -681,7 +900,9 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
           const int ki = kq * 16 + 4 * q4 + i;
           const float a = (ki <= qi && ki < L) ? w4[i] : 0.0f;
           dpart += a;
-          A[4 * h + i] = (__bf16)a;
+          const __bf16 hi = (__bf16)a;
+          A[4 * h + i] = hi;
+          Alo[4 * h + i] = (__bf16)(a - (float)hi);
         }
       }
 #pragma unroll
@@ -690,32 +911,55 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
         const bf16x4 b0 = *reinterpret_cast<const bf16x4*>(vr);
         const bf16x4 b1 = *reinterpret_cast<const bf16x4*>(vr + 16);
         const bf16x8 B = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        ra[nt4] = mfma(A, B, ra[nt4]);
+        ra[nt4] = mfma_b(A, B, ra[nt4]);
+        ra[nt4] = mfma_b(Alo, B, ra[nt4]);
       }
     }
     // the lanes of one query column hold disjoint keys: add the four groups,
     // then fetch the denominators of the accumulator rows 4 q4 + i
     dpart += __shfl_xor(dpart, 16, 64);
     dpart += __shfl_xor(dpart, 32, 64);
-    // lane holds O_in[query mq*16 + 4*q4 + i][value 16*nt4 + l16]; the slice
-    // partials hold four consecutive tokens of one column as bf16
     float den[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) den[i] = __shfl(dpart, 4 * q4 + i, 64) + eps;
-    const uint16_t* pc = part + ((size_t)(n * gridDim.x + blockIdx.x) * S * (C / 16) + mq) * kTileAcc;
-    // the slices' loads are independent: keep several in flight
-#pragma unroll 4
-    for (int s = 0; s < S; ++s) {
-      const uint16_t* ps = pc + (size_t)s * (C / 16) * kTileAcc;
+    // the state term of the denominator: M = Q S (float32 sums of exact
+    // products of q with the two pieces of S), then q . M per query
+    {
+      f32x4 M[4];
 #pragma unroll
-      for (int nt4 = 0; nt4 < 4; ++nt4) {
-        const bf16x4 b = *reinterpret_cast<const bf16x4*>(ps + (nt4 * 64 + lane) * 4);
+      for (int nt = 0; nt < 4; ++nt) M[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ra[nt4][i] += (float)b[i];
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 Aq = *reinterpret_cast<const bf16x8*>(&sh.qs[mq * 16 + l16][32 * ks + 8 * q4]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          M[nt] = mfma_b(Aq, Shi[ks][nt], M[nt]);
+          M[nt] = mfma_b(Aq, Slo[ks][nt], M[nt]);
+        }
       }
-      const bf16x4 b = *reinterpret_cast<const bf16x4*>(ps + 4 * 64 * 4 + 4 * q4);
+      // lane holds M[query mq*16 + 4 q4 + i][column 16 nt + l16]
+      float dx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) den[i] += (float)b[i];
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* qr = sh.qs[mq * 16 + 4 * q4 + i];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) dx[i] += bf16f(qr[16 * nt + l16]) * M[nt][i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o2 = 8; o2 > 0; o2 >>= 1) dx[i] += __shfl_xor(dx[i], o2, 64);
+        den[i] += dx[i];
+      }
+    }
+    // lane holds O_in[query mq*16 + 4*q4 + i][value 16*nt4 + l16]; the slice
+    // partials are float32 in the same order
+    const float* pc = part + ((size_t)(n * gridDim.x + blockIdx.x) * SF * (C / 16) + mq) * kTilePart;
+#pragma unroll 4
+    for (int s = 0; s < SF; ++s) {
+      const float* ps = pc + (size_t)s * (C / 16) * kTilePart;
+#pragma unroll
+      for (int nt4 = 0; nt4 < 4; ++nt4) ra[nt4] += *reinterpret_cast<const f32x4*>(ps + (nt4 * 64 + lane) * 4);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -730,38 +974,36 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
   }
 }
 
-// Slices per head: 16 (one value of j each) while that keeps at most 256
-// work-groups, else 8.
-int slices_for(int N) { return N <= 16 ? 16 : 8; }
-
-// The chunk the kernels run: a request for 32 runs as 64. The chunk only
-// decides which part of each output is summed exactly (the intra-chunk
-// term) and which through the bf16 state; after a 32-token first chunk the
-// state-side rounding can reach the bf16 tolerance on small outputs, and 64
-// halves it.
-int run_chunk(int chunk) { return chunk == 32 ? 64 : chunk; }
+// Feature slices per head: 8 while that keeps at most 256 work-groups
+// (two per slice), else 4.
+int slices_for(int N) { return N <= 16 ? 8 : 4; }
 
 size_t part_bytes(const PrefillArgs& a) {
-  const int S = slices_for(a.N);
-  const int C = run_chunk(a.chunk);
-  const size_t nc = (a.T + C - 1) / C;
-  return align_up((size_t)a.N * nc * S * kAcc * C * sizeof(uint16_t));
+  const int SF = slices_for(a.N);
+  const size_t nc = (a.T + a.chunk - 1) / a.chunk;
+  return align_up((size_t)a.N * nc * SF * (a.chunk / 16) * kTilePart * sizeof(float));
 }
 
-template <int C, int S, int G>
-void launch_state(const PrefillArgs& a, uint16_t* part, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_state_kernel<C, S, G>), dim3(S * a.N), dim3(kThreads3), 0, st,
+size_t gram_bytes(const PrefillArgs& a) {
+  const size_t nc = (a.T + a.chunk - 1) / a.chunk;
+  return align_up((size_t)a.N * nc * kDim * kDim * sizeof(float));
+}
+
+template <int C, int SF, int G>
+void launch_state(const PrefillArgs& a, float* part, float* Sg, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_state_kernel<C, SF, G>), dim3(2 * SF * a.N), dim3(kThreads3), 0, st,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.N, a.T, a.H0, a.s0, a.HT, a.sT, part);
+                     static_cast<const uint16_t*>(a.v), a.N, a.T, a.H0, a.s0, a.HT, a.sT, part, Sg);
 }
 
 template <int C, int G>
 hipError_t launch_c(const PrefillArgs& a, void* ws, hipStream_t st) {
-  uint16_t* part = a.o ? static_cast<uint16_t*>(ws) : nullptr;
-  const int S = slices_for(a.N);
+  float* part = a.o ? static_cast<float*>(ws) : nullptr;
+  float* Sg = a.o ? reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(a)) : nullptr;
+  const int SF = slices_for(a.N);
   prof_begin(st);
-  if (S == 16) launch_state<C, 16, G>(a, part, st);
-  else launch_state<C, 8, G>(a, part, st);
+  if (SF == 8) launch_state<C, 8, G>(a, part, Sg, st);
+  else launch_state<C, 4, G>(a, part, Sg, st);
   prof_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
@@ -769,17 +1011,18 @@ hipError_t launch_c(const PrefillArgs& a, void* ws, hipStream_t st) {
   if (a.out_bf16)
     hipLaunchKernelGGL((prefill_finish_kernel<C, uint16_t, G>), grid, dim3(kThreads), 0, st,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), part, S, static_cast<uint16_t*>(a.o), a.T, a.eps);
+                       static_cast<const uint16_t*>(a.v), part, Sg, SF, static_cast<uint16_t*>(a.o), a.T, a.eps);
   else
     hipLaunchKernelGGL((prefill_finish_kernel<C, float, G>), grid, dim3(kThreads), 0, st,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), part, S, static_cast<float*>(a.o), a.T, a.eps);
+                       static_cast<const uint16_t*>(a.v), part, Sg, SF, static_cast<float*>(a.o), a.T, a.eps);
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_g(const PrefillArgs& a, void* ws, hipStream_t st) {
-  switch (run_chunk(a.chunk)) {
+  switch (a.chunk) {
+    case 32: return launch_c<32, G>(a, ws, st);
     case 64: return launch_c<64, G>(a, ws, st);
     case 128: return launch_c<128, G>(a, ws, st);
   }
@@ -793,7 +1036,7 @@ bool prefill_mfma_supported(const PrefillArgs& a) {
          a.factor_kind == 0 && (a.factors == 1 || a.factors == 2 || a.factors == 4);
 }
 
-size_t prefill_mfma_workspace(const PrefillArgs& a) { return a.o ? part_bytes(a) : 0; }
+size_t prefill_mfma_workspace(const PrefillArgs& a) { return a.o ? part_bytes(a) + gram_bytes(a) : 0; }
 
 hipError_t prefill_mfma_launch(const PrefillArgs& a, void* ws, hipStream_t st) {
   switch (a.factors) {

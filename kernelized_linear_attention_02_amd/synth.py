@@ -40,6 +40,7 @@ __all__ = [
     "HybridCase",
     "hybrid_case",
     "hybrid_decode_tokens",
+    "DecodeStream",
     "CONFIGS",
 ]
 
@@ -211,6 +212,63 @@ def decode_case(N: int, d: int = 64, T0: int = 2048, steps: int = 128, top_k: in
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(work, range(n)))
     return DecodeCase(n, d, steps, top_k, n_fresh, pk, pv, ck, cv, q, k, v, fk, fv, ids)
+
+
+class DecodeStream:
+    """The draws of ``decode_case``, one step at a time.
+
+    Construction draws every head-state's prefix and initial cache (the
+    ``prefix_k``, ``prefix_v``, ``cache0_k``, ``cache0_v`` attributes, as in
+    DecodeCase); each ``next_step()`` then draws the following step's row of
+    q, k, v and fresh candidates for every head-state, from the same
+    per-head-state generators and in the same order, so the values equal
+    ``decode_case(...)`` for the same arguments while only one step is held
+    in memory (the full workload's 128 steps of fresh candidates take 13 GB).
+    Returns (q, k, v, fresh_k, fresh_v) shaped [N, d], [N, n_fresh, d].
+    """
+
+    def __init__(self, N: int, d: int = 64, T0: int = 2048, top_k: int = 16, n_fresh: int = 48,
+                 seed: int = 4, ids=None, threads: int = 8):
+        self.ids = tuple(range(N)) if ids is None else tuple(int(i) for i in ids)
+        n = len(self.ids)
+        self.N, self.d, self.top_k, self.n_fresh, self.threads = n, d, top_k, n_fresh, threads
+        self.scale = np.float32(1.0 / math.sqrt(d))
+        self.rngs = [np.random.default_rng([seed, i]) for i in self.ids]
+        s = 1.0 / math.sqrt(d)
+        self.prefix_k = np.empty((n, T0, d), np.float32)
+        self.prefix_v = np.empty((n, T0, d), np.float32)
+        self.cache0_k = np.empty((n, top_k, d), np.float32)
+        self.cache0_v = np.empty((n, top_k, d), np.float32)
+
+        def work(i):
+            rng = self.rngs[i]
+            self.prefix_k[i] = gaussian(rng, (T0, d), s)
+            self.prefix_v[i] = gaussian(rng, (T0, d))
+            self.cache0_k[i] = gaussian(rng, (top_k, d), s)
+            self.cache0_v[i] = gaussian(rng, (top_k, d))
+
+        with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+            list(ex.map(work, range(n)))
+
+    def drop_prefix(self):
+        """Release the prefix arrays once the initial state is built."""
+        self.prefix_k = self.prefix_v = None
+
+    def next_step(self):
+        n, d, nf, sc = self.N, self.d, self.n_fresh, self.scale
+        rows = np.empty((n, (3 + 2 * nf) * d), np.float32)
+
+        def work(i):
+            rows[i] = gaussian(self.rngs[i], (1, (3 + 2 * nf) * d))[0]
+
+        with ThreadPoolExecutor(max_workers=max(1, self.threads)) as ex:
+            list(ex.map(work, range(n)))
+        q = rows[:, 0:d] * sc
+        k = rows[:, d:2 * d] * sc
+        v = rows[:, 2 * d:3 * d].copy()
+        fk = rows[:, 3 * d:(3 + nf) * d].reshape(n, nf, d) * sc
+        fv = rows[:, (3 + nf) * d:].reshape(n, nf, d).copy()
+        return q, k, v, fk, fv
 
 
 # ----------------------------------------------------------------------------

@@ -168,36 +168,40 @@ def test_prefill_degenerate_inputs(K):
     assert_close(host(K.prefill(q1, k1, v1, chunk=64)), host(v1), RTOL_F32, "T=1")
 
 
-def _prefill_full(K, name, sample_rows, oracle_heads):
+def _prefill_full(K, name, brute_rows_per_head):
+    """The workload as configured, every output row and the final state of
+    every head against the oracle's chunked form (its own chunk of 256), plus
+    seeded rows against the brute-force definition."""
     cfg = S.CONFIGS[name]
     c = S.prefill_case(name, cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
-                       cfg["seed"])
+                       cfg["seed"], threads=16)
     o, HT, sT = K.prefill(dev(c.q, torch.bfloat16), dev(c.k, torch.bfloat16),
                           dev(c.v, torch.bfloat16), chunk=c.chunk, return_state=True)
     torch.cuda.synchronize()
-    go = o.float().cpu().numpy()
+    go, gH, gs = o.float().cpu().numpy(), HT.cpu().numpy(), sT.cpu().numpy()
+    del o, HT, sT
     B, H, T = cfg["B"], cfg["H"], cfg["T"]
     rng = np.random.default_rng(99)
-    # brute-force rows spread over every head (always includes the first and last token)
+    worst = dict(o=0.0, H=0.0, s=0.0, brute=0.0)
     for b in range(B):
         for h in range(H):
-            rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, sample_rows)]))
+            ro, rH, rs = O.prefill_chunked(c.q[b, h], c.k[b, h], c.v[b, h], chunk=256)
+            worst["o"] = max(worst["o"], assert_close(go[b, h], ro, RTOL_BF16, f"o of head ({b},{h})")["max_scaled"])
+            worst["H"] = max(worst["H"], assert_close(gH[b, h], rH, RTOL_BF16, f"H_T of head ({b},{h})")["max_scaled"])
+            worst["s"] = max(worst["s"], assert_close(gs[b, h], rs, RTOL_BF16, f"s_T of head ({b},{h})")["max_scaled"])
+            rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, brute_rows_per_head)]))
             ref = O.prefill_bruteforce_rows(c.q[b, h], c.k[b, h], c.v[b, h], rows)
-            assert_close(go[b, h, rows], ref, RTOL_BF16, f"o rows of head ({b},{h})")
-    # final state of a few heads
-    for (b, h) in oracle_heads:
-        fk = O.phi(c.k[b, h])
-        rH = fk.T @ c.v[b, h].astype(np.float64)
-        assert_close(host(HT[b, h]), rH, RTOL_BF16, f"H_T head ({b},{h})")
-        assert_close(host(sT[b, h]), fk.sum(axis=0), RTOL_BF16, f"s_T head ({b},{h})")
+            rep = assert_close(go[b, h, rows], ref, RTOL_BF16, f"brute-force rows of head ({b},{h})")
+            worst["brute"] = max(worst["brute"], rep["max_scaled"])
+    print(f"[parity] {name}: worst scaled error {worst}", flush=True)
 
 
 def test_prefill_4x8x4096_full_size(K):
-    _prefill_full(K, "prefill_4x8x4096", 24, [(0, 0), (3, 7)])
+    _prefill_full(K, "prefill_4x8x4096", 32)
 
 
 def test_prefill_1x16x65536_full_size(K):
-    _prefill_full(K, "prefill_1x16x65536", 48, [(0, 5)])
+    _prefill_full(K, "prefill_1x16x65536", 64)
 
 
 # ------------------------------------------------------------------ quadratic form
@@ -387,10 +391,32 @@ def test_decode_step_with_selection_matrix_path(K, dtype, out_dtype, eps):
         np.testing.assert_array_equal(host(r["sel_k"])[n], ck[n][sel])
 
 
+def _oracle_chain_check(gpu, H, s, H0s, s0s, inputs, cache0_k, cache0_v, top, check_ids):
+    """Each checked head-state's oracle chain against what the GPU recorded,
+    following the GPU's selections through near-ties (rule R17)."""
+    Hh, sh = host(H), host(s)
+    steps = len(gpu["o"])
+    for j, n in enumerate(check_ids):
+        bad = []
+
+        def choose(tau, sc, sel, j=j):
+            g = gpu["sel"][tau][j]
+            if not O.near_tie_ok(sc, g, top, TIE_REL):
+                bad.append(tau)
+            return g
+        q, k, v, fk, fv = (np.stack([x[i][j] for i in range(steps)]) for x in inputs)
+        ref = O.decode_sre_chain(H0s[j], s0s[j], q, k, v, fk, fv, cache0_k[j], cache0_v[j], top, choose=choose)
+        assert not bad, f"head-state {n}: selection differs outside near-ties at steps {bad}"
+        assert_close(np.array([x[j] for x in gpu["o"]]), ref["o"], RTOL_F32, f"o of head-state {n}")
+        assert_close(np.array([x[j] for x in gpu["scores"]]), ref["scores"], RTOL_F32,
+                     f"scores of head-state {n}")
+        assert_close(Hh[n], ref["H"], RTOL_F32, f"H of head-state {n}")
+        assert_close(sh[n], ref["s"], RTOL_F32, f"s of head-state {n}")
+
+
 def _decode_chain(K, case, steps, check_ids):
     """Run the decode + selection chain on the GPU for all head-states and
-    compare the head-states ``check_ids`` with the oracle, following the GPU
-    through near-ties."""
+    compare the head-states ``check_ids`` with the oracle."""
     N, d, top = case.N, case.d, case.top_k
     H, s = _initial_state(K, case)
     cache_k = dev(case.cache0_k)
@@ -406,27 +432,14 @@ def _decode_chain(K, case, steps, check_ids):
         gpu["scores"].append(host(r["scores"])[check_ids])
         gpu["sel"].append(host(r["sel"]).astype(int)[check_ids])
     torch.cuda.synchronize()
-    Hh, sh = host(H), host(s)
-    for j, n in enumerate(check_ids):
+    H0s, s0s = [], []
+    for n in check_ids:
         fk = O.phi(case.prefix_k[n])
-        H0 = fk.T @ case.prefix_v[n].astype(np.float64)
-        s0 = fk.sum(0)
-        bad = []
-
-        def choose(tau, sc, sel, j=j):
-            g = gpu["sel"][tau][j]
-            if not O.near_tie_ok(sc, g, top, TIE_REL):
-                bad.append(tau)
-            return g
-        ref = O.decode_sre_chain(H0, s0, case.q[:steps, n], case.k[:steps, n], case.v[:steps, n],
-                                 case.fresh_k[:steps, n], case.fresh_v[:steps, n], case.cache0_k[n],
-                                 case.cache0_v[n], top, choose=choose)
-        assert not bad, f"head-state {n}: selection differs outside near-ties at steps {bad}"
-        assert_close(np.array([x[j] for x in gpu["o"]]), ref["o"], RTOL_F32, f"o of head-state {n}")
-        assert_close(np.array([x[j] for x in gpu["scores"]]), ref["scores"], RTOL_F32,
-                     f"scores of head-state {n}")
-        assert_close(Hh[n], ref["H"], RTOL_F32, f"H of head-state {n}")
-        assert_close(sh[n], ref["s"], RTOL_F32, f"s of head-state {n}")
+        H0s.append(fk.T @ case.prefix_v[n].astype(np.float64))
+        s0s.append(fk.sum(0))
+    inputs = [[x[t][check_ids] for t in range(steps)] for x in (case.q, case.k, case.v, case.fresh_k, case.fresh_v)]
+    _oracle_chain_check(gpu, H, s, H0s, s0s, inputs, case.cache0_k[check_ids], case.cache0_v[check_ids], top,
+                        check_ids)
 
 
 def test_decode_chain_small(K):
@@ -434,22 +447,75 @@ def test_decode_chain_small(K):
     _decode_chain(K, case, 12, list(range(8)))
 
 
-def test_decode_sre_4096_full_size(K):
+def test_decode_sre_4096x128_full_chain(K):
+    """The decode workload as configured: 4096 head-states, a 2048-token
+    prefix, 128 steps of update, readout, scoring of 16 cached + 48 fresh
+    candidates and top-16 selection, gathered into the next step's candidate
+    slab as the benchmark runs it. 64 seeded head-states are compared with
+    the oracle at every step (o, scores, selected sets) and at the end (H, s);
+    their initial state too."""
     cfg = S.CONFIGS["decode_sre_4096x128"]
-    steps = 6
-    case = S.decode_case(cfg["N"], d=cfg["d"], T0=cfg["T0"], steps=steps, top_k=cfg["top_k"],
-                         n_fresh=cfg["n_fresh"], seed=cfg["seed"])
-    _decode_chain(K, case, steps, [0, 1, 777, 2048, 4095])
+    N, d, T0, steps, top, nf = cfg["N"], cfg["d"], cfg["T0"], cfg["steps"], cfg["top_k"], cfg["n_fresh"]
+    stream = S.DecodeStream(N, d=d, T0=T0, top_k=top, n_fresh=nf, seed=cfg["seed"], threads=16)
+    check = sorted(set(np.random.default_rng(7).choice(np.arange(1, N - 1), 62, replace=False).tolist())
+                   | {0, N - 1})
+    pk = dev(stream.prefix_k)[None]
+    pv = dev(stream.prefix_v)[None]
+    H, s = K.prefill(pk, pk, pv, chunk=64, outputs=False)
+    H, s = H[0].contiguous(), s[0].contiguous()
+    del pk, pv
+    H0s, s0s = [], []
+    for n in check:
+        fk = O.phi(stream.prefix_k[n])
+        H0s.append(fk.T @ stream.prefix_v[n].astype(np.float64))
+        s0s.append(fk.sum(0))
+    torch.cuda.synchronize()
+    assert_close(host(H)[check], np.stack(H0s), RTOL_F32, "initial H")
+    assert_close(host(s)[check], np.stack(s0s), RTOL_F32, "initial s")
+    stream.drop_prefix()
+    n_cand = top + nf
+    ck = torch.empty((2, N, n_cand, d), device="cuda")
+    cv = torch.empty((2, N, n_cand, d), device="cuda")
+    ck[0, :, :top] = dev(stream.cache0_k)
+    cv[0, :, :top] = dev(stream.cache0_v)
+    o = torch.empty((N, d), device="cuda")
+    sc = torch.empty((N, n_cand), device="cuda")
+    sel = torch.empty((N, top), dtype=torch.int32, device="cuda")
+    gpu = dict(o=[], scores=[], sel=[])
+    inputs = [[], [], [], [], []]
+    for t in range(steps):
+        cur, nxt = t & 1, (t + 1) & 1
+        q, k, v, fk, fv = stream.next_step()
+        ck[cur, :, top:] = dev(fk)
+        cv[cur, :, top:] = dev(fv)
+        K.decode_step(H, s, dev(q), dev(k), dev(v), cand_k=ck[cur], cand_v=cv[cur], top_k=top, gather=True,
+                      out=dict(o=o, scores=sc, sel=sel, sel_k=ck[nxt], sel_v=cv[nxt], sel_stride=n_cand))
+        gpu["o"].append(host(o)[check])
+        gpu["scores"].append(host(sc)[check])
+        gpu["sel"].append(host(sel).astype(int)[check])
+        for lst, x in zip(inputs, (q, k, v, fk, fv)):
+            lst.append(x[check])
+    torch.cuda.synchronize()
+    _oracle_chain_check(gpu, H, s, H0s, s0s, inputs, stream.cache0_k[check], stream.cache0_v[check], top, check)
 
 
 # ------------------------------------------------------------------ hybrid
 
-def _hybrid_check(K, c, heads, dtype, rtol, eps=0.0, out_dtype=None):
+def _hybrid_check(K, c, heads, dtype, rtol, eps=0.0, out_dtype=None, aux=False):
     B, H, T, d = c.q.shape
     scale = 1.0 / math.sqrt(d)
-    o, extra = K.hybrid_prefill(dev(c.q, dtype), dev(c.k, dtype), dev(c.v, dtype), c.window,
-                                c.cache_size, c.refresh, scale, eps=eps, return_state=True,
-                                return_cache=True, return_trace=True, out_dtype=out_dtype)
+    args = (dev(c.q, dtype), dev(c.k, dtype), dev(c.v, dtype), c.window, c.cache_size, c.refresh, scale)
+    kw = dict(eps=eps, return_state=True, return_cache=True, return_trace=True, out_dtype=out_dtype)
+    o, extra = K.hybrid_prefill(*args, **kw)
+    if aux:
+        # readouts on a second stream of the caller's: the same kernels, so
+        # the same bits as the one-stream call
+        side = torch.cuda.Stream()
+        o2, extra2 = K.hybrid_prefill(*args, **kw, aux_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o), "two-stream outputs differ from one-stream outputs"
+        for key in ("H", "s", "cache", "trace"):
+            assert torch.equal(extra2[key], extra[key]), f"two-stream {key} differs"
     torch.cuda.synchronize()
     go, gH, gs = host(o), host(extra["H"]), host(extra["s"])
     gc = extra["cache"].cpu().numpy()
@@ -493,10 +559,11 @@ def test_hybrid_small_bf16(K, d, W, lam, R, T):
     (40, 24, 7, 333, 3, 0.5, torch.float32),      # odd refresh, eps > 0, float32 output
 ])
 def test_hybrid_matrix_path_edge_cases(K, W, lam, R, T, H, eps, out):
-    # d = 64 with bf16 inputs takes the matrix-core path (two streams,
-    # fragment scorer, counting selection)
+    # d = 64 with bf16 inputs takes the matrix-core path (fragment scorer,
+    # counting selection), on one stream and with the readouts on a second
     c = S.hybrid_case("edge", 1, H, T, 64, W, lam, R, seed=90 + T + R, dup_frac=0.1)
-    _hybrid_check(K, c, [(0, h) for h in range(H)], torch.bfloat16, RTOL_BF16, eps=eps, out_dtype=out)
+    _hybrid_check(K, c, [(0, h) for h in range(H)], torch.bfloat16, RTOL_BF16, eps=eps, out_dtype=out,
+                  aux=True)
 
 
 def test_hybrid_special_cases_f32(K):
@@ -521,5 +588,6 @@ def test_hybrid_special_cases_f32(K):
 def test_hybrid_2x16x16384_full_size(K):
     cfg = S.CONFIGS["hybrid_2x16x16384"]
     c = S.hybrid_case("full", cfg["B"], cfg["H"], cfg["T"], cfg["d"], cfg["window"],
-                      cfg["cache_size"], cfg["refresh"], cfg["seed"])
-    _hybrid_check(K, c, [(0, 0), (1, 15)], torch.bfloat16, RTOL_BF16)
+                      cfg["cache_size"], cfg["refresh"], cfg["seed"], threads=16)
+    heads = [(0, 0), (0, 5), (0, 10), (0, 15), (1, 0), (1, 6), (1, 11), (1, 15)]
+    _hybrid_check(K, c, heads, torch.bfloat16, RTOL_BF16, aux=True)

@@ -1,0 +1,28 @@
+"""The seeded generators: the step-by-step decode stream draws exactly the
+values of the whole-workload generator (the full-size decode parity test
+relies on it to keep only one step in memory)."""
+import numpy as np
+
+from kernelized_linear_attention_02_amd import synth as S
+
+
+def test_decode_stream_equals_decode_case():
+    N, d, T0, steps, top, nf = 5, 16, 40, 7, 3, 6
+    whole = S.decode_case(N, d=d, T0=T0, steps=steps, top_k=top, n_fresh=nf, seed=9, ids=[0, 3, 7, 8, 100])
+    st = S.DecodeStream(N, d=d, T0=T0, top_k=top, n_fresh=nf, seed=9, ids=[0, 3, 7, 8, 100], threads=3)
+    for name in ("prefix_k", "prefix_v", "cache0_k", "cache0_v"):
+        np.testing.assert_array_equal(getattr(st, name), getattr(whole, name))
+    for t in range(steps):
+        q, k, v, fk, fv = st.next_step()
+        np.testing.assert_array_equal(q, whole.q[t])
+        np.testing.assert_array_equal(k, whole.k[t])
+        np.testing.assert_array_equal(v, whole.v[t])
+        np.testing.assert_array_equal(fk, whole.fresh_k[t])
+        np.testing.assert_array_equal(fv, whole.fresh_v[t])
+
+
+def test_prefill_case_head_subsets_match():
+    full = S.prefill_case("x", 2, 3, 50, 16, 8, 32, seed=11)
+    sub = S.prefill_case("x", 2, 3, 50, 16, 8, 32, seed=11, heads=[(1, 2), (0, 1)])
+    np.testing.assert_array_equal(sub.q[0, 0], full.q[1, 2])
+    np.testing.assert_array_equal(sub.v[0, 1], full.v[0, 1])
