@@ -30,7 +30,8 @@
 // running exponent G >= 2 ek + log2 max|v| of every sub-chunk seen; the
 // accumulators hold H 2^-G (rescaled when G grows). Queries are scaled per
 // token (undone before the partials are written). The published state is
-// scaled by 2^-P so that its largest weighted entry stays below 2^15.
+// scaled by 2^-P so that a bound on its largest weighted entry stays below
+// 2^15.
 // Accumulation is float32 throughout; the slice partials are float32.
 //
 // State kernel, eight waves, stepping through sub-chunks of up to 64 tokens;
@@ -43,7 +44,8 @@
 //   packed float16 products of its k_a and k_b, k_b coming from lane 0 of its
 //   16-lane row by a DPP broadcast. In the first value half's work-group each
 //   wave also accumulates one X block of the keys' Gram matrix for the
-//   slice's columns b (raw bf16 keys: exact products, float32 sums). At each
+//   slice's columns b (the staged float16 keys hold the bf16 keys exactly up
+//   to the sub-chunk's power of two: exact products, float32 sums). At each
 //   chunk end they publish the weighted state (2 off the diagonal, 1 on it, 0
 //   for mirror rows) as float16 B fragments in LDS and the Gram matrix to
 //   memory.
@@ -52,9 +54,9 @@
 //   token and forms its products from q values in registers. The two waves
 //   sharing tokens trade halves through LDS, and each writes one float32
 //   partial [16 tokens x 32 columns] per token tile in the MFMA accumulator
-//   order. They also stage the sub-chunks (q rows, k columns and raw k
-//   columns, v columns of the work-group's half), in two passes: the scales'
-//   maxima before the middle barrier, the scaled values after it.
+//   order. They also stage the sub-chunks (q rows, k columns, v columns of
+//   the work-group's half), in two passes: the scales' maxima before the
+//   middle barrier, the scaled values after it.
 //
 // Finish kernel. One work-group per (head, chunk): the exact intra-chunk term
 // (squared scores as two bf16 pieces times V), the denominator's state term
@@ -121,15 +123,15 @@ __device__ __forceinline__ uint32_t row_bcast0(uint32_t x) {
 __device__ __forceinline__ f16x2 as_h2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
 __device__ __forceinline__ uint32_t as_u(f16x2 x) { return __builtin_bit_cast(uint32_t, x); }
 
-// Largest |x| of the eight bf16 values in a 16-byte group, as a bf16 bit
-// pattern: |x| orders like the low 15 bits of the pattern.
-__device__ __forceinline__ uint32_t absmax_bits(uint4 w) {
-  const uint32_t m0 = max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu);
-  const uint32_t m1 = max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu);
-  const uint32_t m2 = max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu);
-  const uint32_t m3 = max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu);
-  return max(max(m0, m1), max(m2, m3));
+// Largest |x| of bf16 values as a bf16 bit pattern: |x| orders like the low
+// 15 bits of the pattern (packed 16-bit maxima).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 abs_pair(uint32_t x) { return __builtin_bit_cast(u16x2, x & 0x7FFF7FFFu); }
+__device__ __forceinline__ u16x2 absmax_pairs(uint4 w) {
+  return __builtin_elementwise_max(__builtin_elementwise_max(abs_pair(w.x), abs_pair(w.y)),
+                                   __builtin_elementwise_max(abs_pair(w.z), abs_pair(w.w)));
 }
+__device__ __forceinline__ uint32_t pair_max(u16x2 m) { return max((uint32_t)m[0], (uint32_t)m[1]); }
 
 // Eight bf16 values times 2^e, rounded to float16 (nearest even).
 __device__ __forceinline__ uint4 bf16x8_to_f16_scaled(uint4 w, int e) {
@@ -243,13 +245,12 @@ struct StateLds {
   // staged sub-chunks, double buffered (the next is staged during this one)
   _Float16 qs[2][kCS][kDim + kPad];       // q rows, scaled per token
   _Float16 kt[2][kDim][kCS + kPad];       // k columns, scaled per sub-chunk
-  uint16_t kr[2][kDim][kCS + kPad];       // raw k columns (bf16), for the Gram matrix
   _Float16 vt[2][kCols][kCS + kPad];      // v columns of the work-group's half, scaled
   int qe[2][kCS];                         // per-token query exponent
   int sc[2][2];                           // per buffer: key exponent ek, state exponent G
   float qmx[kRW][kCS];                    // staging: per wave and token, max |q| over its dims
   float kvmx[kRW][2];                     // staging: per wave, max |k| and max |v|
-  float umx[kUW];                         // per update wave, max |state|
+  float umx[kUW];                         // per update wave, max |imported state|
   int pub_e;                              // exponent of the published state (G + P)
 };
 
@@ -306,9 +307,9 @@ __device__ __forceinline__ void stage_max(Lds& sh, const Prefetch& p, int W, int
   const bool act = lane < CS && p.ok;
   uint32_t qm = 0, km = 0, vm = 0;
   if (act) {
-    qm = max(absmax_bits(p.q[0]), absmax_bits(p.q[1]));
-    km = max(absmax_bits(p.k[0]), absmax_bits(p.k[1]));
-    vm = absmax_bits(p.v);
+    qm = pair_max(__builtin_elementwise_max(absmax_pairs(p.q[0]), absmax_pairs(p.q[1])));
+    km = pair_max(__builtin_elementwise_max(absmax_pairs(p.k[0]), absmax_pairs(p.k[1])));
+    vm = pair_max(absmax_pairs(p.v));
   }
   if (lane < CS) sh.qmx[W][lane] = bf16f(qm);
   const float kw = wave_max(bf16f(km));
@@ -356,13 +357,10 @@ __device__ __forceinline__ void stage_write(Lds& sh, const Prefetch& p, int W, i
     *reinterpret_cast<uint4*>(&sh.qs[buf][t][16 * W + 8]) = bf16x8_to_f16_scaled(q1, -eq);
     if (W == 0) sh.qe[buf][t] = eq;
     const uint4 kh0 = bf16x8_to_f16_scaled(k0, -ek), kh1 = bf16x8_to_f16_scaled(k1, -ek);
-    const uint32_t kraw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
     const uint32_t kh[8] = {kh0.x, kh0.y, kh0.z, kh0.w, kh1.x, kh1.y, kh1.z, kh1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = 16 * W + 2 * e;
-      sh.kr[buf][d][t] = (uint16_t)(kraw[e] & 0xFFFFu);
-      sh.kr[buf][d + 1][t] = (uint16_t)(kraw[e] >> 16);
       sh.kt[buf][d][t] = as_h2(kh[e])[0];
       sh.kt[buf][d + 1][t] = as_h2(kh[e])[1];
     }
@@ -404,7 +402,8 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
   // G (value n-tiles 0, 1 of the work-group's half) of each owned tile;
   // lane (l16, q4) holds rows 4 q4 + i, column l16 of an n-tile
   f32x4 h[NU][2];
-  f32x4 gram = {0.f, 0.f, 0.f, 0.f};
+  f32x4 gram = {0.f, 0.f, 0.f, 0.f};  // float32 Gram matrix (true scale)
+  f32x4 gsub = {0.f, 0.f, 0.f, 0.f};  // this sub-chunk's part, in the staged key scale
   float hmax = 0.0f;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
@@ -440,7 +439,11 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
   if (lane == 0) sh.umx[W] = hmax;
 
   int Gu = 0;  // the accumulators hold G 2^-Gu
-  // publish the state at the start of chunk c; m = max |h| in current units
+  // Bound on |h| in current units: the imported state plus one per token
+  // (each token adds k'_a k'_b v'' with every factor below 1), scaled with
+  // the accumulators. Uniform across the wave.
+  float hb = 0.0f;
+  // publish the state at the start of chunk c; m bounds |h| in current units
   auto publish = [&](int c, float m) {
     // the largest weighted entry stays below 2^15 in float16
     const int em = exp_above(2.0f * m);
@@ -493,7 +496,8 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) h[u][nt] *= s;
     const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
-    publish(0, m * s);  // the state at the start of chunk 0
+    hb = m * s;
+    publish(0, hb);  // the state at the start of chunk 0
   }
   lds_barrier();  // (B0c) initial state published
 
@@ -506,6 +510,7 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
       for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) h[u][nt] *= s;
+      hb *= s;
       Gu = Gn;
     }
 #pragma unroll
@@ -540,29 +545,23 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
         for (int nt = 0; nt < 2; ++nt) h[u][nt] = mfma_h(A, vb[nt], h[u][nt]);
       }
       if (gram_wg) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.kr[buf][16 * W + l16][t0]);
-        bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-        if (gb_ok) B = *reinterpret_cast<const bf16x8*>(&sh.kr[buf][gb][t0]);
-        gram = mfma_b(A, B, gram);
+        const f16x8 A = *reinterpret_cast<const f16x8*>(&sh.kt[buf][16 * W + l16][t0]);
+        f16x8 B = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
+        if (gb_ok) B = *reinterpret_cast<const f16x8*>(&sh.kt[buf][gb][t0]);
+        gsub = mfma_h(A, B, gsub);
       }
     }
+    if (gram_wg) {
+      // the sub-chunk's keys were staged times 2^-ek: exact products, so the
+      // float32 Gram matrix gets them back times 4^ek
+      const float s = __builtin_ldexpf(1.0f, 2 * __builtin_amdgcn_readfirstlane(sh.sc[buf][0]));
+      gram += gsub * s;
+      gsub = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    hb += (float)CS;
     const bool chunk_end = st % SUB == SUB - 1;
-    if (chunk_end) {
-      float m = 0.0f;
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(h[u][nt][i]));
-      m = wave_max(m);
-      if (lane == 0) sh.umx[W] = m;
-    }
-    lds_barrier();  // (B2) sub-chunk consumed, readouts done, maxima posted
-    if (chunk_end) {
-      const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
-      publish(st / SUB + 1, m);
-    }
+    lds_barrier();  // (B2) sub-chunk consumed, readouts done
+    if (chunk_end) publish(st / SUB + 1, hb);
     lds_barrier();  // (B1) state published, next sub-chunk staged
   }
 
@@ -666,7 +665,7 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
       // q' factors of this lane's token in each of the two token tiles:
       // qa[tt][X] = q'[16 X + 4 q4 + 0..3], qb[tt][Y] = q'[16 Y + j0 + 0..kJ-1]
       uint2 qa[2][4];
-      uint32_t qb[2][4][SL::kJ / 2];
+      uint32_t qb[2][4][SL::kJ / 2];  // packed pairs of q'_b
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const _Float16* qrow = sh.qs[buf][32 * TP + 16 * tt + l16];
@@ -697,16 +696,16 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
         f16x8 B[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) B[nt] = __builtin_bit_cast(f16x8, sh.hs[pr][nt][lane]);
-        constexpr int kU0 = 0;
-        const int u0 = 2 * pr + kU0, u1 = 2 * pr + 1;
+        const int u0 = 2 * pr, u1 = 2 * pr + 1;
         const int X0 = SL::X(u0), X1 = SL::X(u1), Y0 = SL::Y(u0), Y1 = SL::Y(u1);
         const int J0 = SL::jj(u0), J1 = SL::jj(u1);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          // q'_b of each tile, broadcast to both halves of a packed pair
-          const _Float16 b0 = as_h2(qb[tt][Y0][J0 >> 1])[J0 & 1];
-          const _Float16 b1 = as_h2(qb[tt][Y1][J1 >> 1])[J1 & 1];
-          const f16x2 bb0 = {b0, b0}, bb1 = {b1, b1};
+          // q'_b of each tile, broadcast to both halves (an op_sel of the
+          // packed multiply)
+          const f16x2 c0 = as_h2(qb[tt][Y0][J0 >> 1]), c1 = as_h2(qb[tt][Y1][J1 >> 1]);
+          const f16x2 bb0 = (J0 & 1) ? __builtin_shufflevector(c0, c0, 1, 1) : __builtin_shufflevector(c0, c0, 0, 0);
+          const f16x2 bb1 = (J1 & 1) ? __builtin_shufflevector(c1, c1, 1, 1) : __builtin_shufflevector(c1, c1, 0, 0);
           const uint32_t p0 = as_u(as_h2(qa[tt][X0].x) * bb0);
           const uint32_t p1 = as_u(as_h2(qa[tt][X0].y) * bb0);
           const uint32_t p2 = as_u(as_h2(qa[tt][X1].x) * bb1);
