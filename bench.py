@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_VALU_TFLOPS = 157.3
+PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
@@ -279,7 +280,10 @@ def bench_hybrid(torch, K, S, steps, warmup):
     c = S.hybrid_case("bench", cfg["B"], cfg["H"], cfg["T"], cfg["d"], cfg["window"],
                       cfg["cache_size"], cfg["refresh"], cfg["seed"], threads=16)
     q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (c.q, c.k, c.v))
-    fn = lambda: K.hybrid_prefill(q, k, v, cfg["window"], cfg["cache_size"], cfg["refresh"])
+    # the readouts run on a second stream of the caller's, overlapping the
+    # refresh chain (kla_hybrid_prefill_streams)
+    side = torch.cuda.Stream()
+    fn = lambda: K.hybrid_prefill(q, k, v, cfg["window"], cfg["cache_size"], cfg["refresh"], aux_stream=side)
     # the call issues a few kernels and events per 64-token block, so the
     # library's timing hooks (two more events per refresh) would inflate the
     # wall time: the plain calls are timed, the hooked ones apart
@@ -293,8 +297,59 @@ def bench_hybrid(torch, K, S, steps, warmup):
     step_ms = (time.perf_counter() - t0) * 1e3 / steps
     hooked_ms, kern_ms, per_call = timed_calls(torch, K, fn, max(1, steps // 4), 1)
     B, T = cfg["B"], cfg["T"]
+    work = hybrid_flops(B * cfg["H"], T, cfg["d"], cfg["window"], cfg["cache_size"], cfg["refresh"])
+    achieved = work["total"] / (step_ms * 1e-3) / 1e12
+    fp32_floor_ms = work["fp32_faithful"] / (PEAK_F32_MFMA_TFLOPS * 1e12) * 1e3
     return dict(workload="hybrid_2x16x16384", step_ms=step_ms, tokens_per_s=B * T / (step_ms * 1e-3),
-                hooked_step_ms=hooked_ms, refresh_chain_ms_per_call=kern_ms * per_call)
+                hooked_step_ms=hooked_ms, refresh_chain_ms_per_call=kern_ms * per_call,
+                roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=achieved / PEAK_BF16_TFLOPS, traffic=None,
+                              kernel="whole call (refresh chain, folds, readouts)",
+                              flops_per_launch=work["total"], flops_fp32_faithful=work["fp32_faithful"],
+                              fp32_faithful_floor_ms=fp32_floor_ms,
+                              frac_of_fp32_faithful_floor=fp32_floor_ms / step_ms),
+                arith="bf16 (scores, folds and readouts float32-faithful)")
+
+
+def hybrid_flops(n_heads, T, d, W, lam, R):
+    """Algorithmic work of the hybrid prefill, counted from its definition:
+    the window and cache softmax terms (2 (d + d + 1) flop per query-key
+    pair: the score, the weighted value and the weight), the linear readout
+    phi(q)^T [H | s] per query (2 D (d + 1)), and per scored refresh the SRE
+    of every candidate against [H | s] (2 D (d + 1)) and the fold of every
+    rejected pair (2 D (d + 1) for H and s, less the D squares counted
+    once). The scoring and the fold must be float32-faithful (a score error
+    above the near-tie rule changes the selection chain)."""
+    D = phi_dim(d)
+    nb = -(-T // R)
+    win_pairs = cache_pairs = lin_q = 0
+    sre_c = fold_p = 0
+    f_prev, n_cache = 0, 0
+    for b in range(nb):
+        b0, b1 = b * R, min(T, b * R + R)
+        f = max(0, b0 - W)
+        n_ev = f - f_prev
+        if n_ev > 0:
+            n_cand = n_cache + n_ev
+            if n_cand <= lam:
+                n_cache = n_cand
+            else:
+                sre_c += n_cand
+                fold_p += n_cand - lam
+                n_cache = lam
+        f_prev = f
+        for t in range(b0, b1):
+            win_pairs += t - f + 1
+            cache_pairs += n_cache
+        if f > 0:
+            lin_q += b1 - b0
+    per_pair = 2 * (d + d + 1)
+    readout = lin_q * 2 * D * (d + 1)
+    sre = sre_c * 2 * D * (d + 1)
+    fold = fold_p * (2 * D * (d + 1) - D)
+    total = n_heads * ((win_pairs + cache_pairs) * per_pair + readout + sre + fold)
+    faithful = n_heads * (sre + fold)
+    return dict(total=float(total), fp32_faithful=float(faithful))
 
 
 def hybrid_decode_step_bytes(N, d, W, lam):
@@ -343,18 +398,31 @@ def bench_hybrid_decode(torch, K, S, steps=None):
     )
 
 
-def cpu_baseline(S, name, budget_s):
-    """The oracle (float64, NumPy) on a bounded sample of the workload's heads."""
-    import numpy as np
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([x.get("num_threads", 1) for x in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
 
+
+def _baseline(value, unit, sample):
+    return dict(value=value, unit=unit, cores=_oracle_threads(), kind="oracle", sample=sample)
+
+
+def cpu_baseline(S, name, budget_s):
+    """The oracle (float64, NumPy chunked form) on a bounded sample of the
+    workload's heads, in tokens/s of the whole workload (B*T tokens over all
+    heads; one head-token is 1/H of a token)."""
     import oracle as O
     cfg = S.CONFIGS[name]
     B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    kind = cfg.get("gen", "normalised")
     heads = [(b, h) for b in range(B) for h in range(H)]
     done = 0
     elapsed = 0.0
     for (b, h) in heads:
-        c = S.prefill_case(name, B, H, T, cfg["d_qk"], cfg["d_v"], cfg["chunk"], cfg["seed"],
+        c = S.prefill_case(name, B, H, T, cfg["d_qk"], cfg["d_v"], cfg["chunk"], cfg["seed"], kind=kind,
                            heads=[(b, h)])
         t = time.perf_counter()
         O.prefill_chunked(c.q[0, 0], c.k[0, 0], c.v[0, 0], chunk=256)
@@ -362,15 +430,81 @@ def cpu_baseline(S, name, budget_s):
         done += 1
         if elapsed >= budget_s:
             break
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    tokens = done * T / H  # tokens = B*T over all heads; one head-token is 1/H of a token
-    return dict(value=tokens / elapsed, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{done} of {B * H} heads x {T} tokens, float64 chunked form, "
-                       f"{elapsed:.1f}s of CPU time")
+    tokens = done * T / H
+    extra = "" if done == B * H else f", extrapolated x{B * H / done:g} to all heads"
+    return _baseline(tokens / elapsed, "tokens/s",
+                     f"{done} of {B * H} heads x {T} tokens, float64 chunked form, {elapsed:.1f}s of CPU time"
+                     + extra)
+
+
+def cpu_baseline_decode(S, budget_s):
+    """The oracle's decode + self-recall selection chain (float64) over all
+    128 steps for a bounded sample of head-states, in steps/s of the whole
+    workload (4096 head-states). The initial state is not timed (on the GPU
+    it is not either)."""
+    import numpy as np
+
+    import oracle as O
+    cfg = S.CONFIGS["decode_sre_4096x128"]
+    N, steps = cfg["N"], cfg["steps"]
+    done, elapsed = 0, 0.0
+    n = 0
+    while elapsed < budget_s and n < N:
+        c = S.decode_case(1, d=cfg["d"], T0=cfg["T0"], steps=steps, top_k=cfg["top_k"], n_fresh=cfg["n_fresh"],
+                          seed=cfg["seed"], ids=[n], threads=1)
+        fk = O.phi(c.prefix_k[0])
+        H0, s0 = fk.T @ c.prefix_v[0].astype(np.float64), fk.sum(0)
+        t = time.perf_counter()
+        O.decode_sre_chain(H0, s0, c.q[:, 0], c.k[:, 0], c.v[:, 0], c.fresh_k[:, 0], c.fresh_v[:, 0],
+                           c.cache0_k[0], c.cache0_v[0], cfg["top_k"])
+        elapsed += time.perf_counter() - t
+        done += 1
+        n += 1 + (N // 64)  # head-states spread over the workload
+    per_step_all = elapsed / done * N / steps
+    return _baseline(1.0 / per_step_all, "steps/s",
+                     f"{done} of {N} head-states x {steps} steps (update, readout, 64-candidate scoring, top-16), "
+                     f"float64, {elapsed:.1f}s of CPU time, extrapolated x{N / done:g}")
+
+
+def cpu_baseline_hybrid(S, budget_s):
+    """The oracle's hybrid prefill (float64, block by block) on a bounded
+    sample of heads, in tokens/s of the whole workload."""
+    import oracle as O
+    cfg = S.CONFIGS["hybrid_2x16x16384"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    done, elapsed = 0, 0.0
+    for i in range(B * H):
+        b, h = divmod(i, H)
+        # the workload's own head (b, h): the generator is seeded per head
+        q, k, v, _ = S.hybrid_head(cfg["seed"], b, h, T, cfg["d"])
+        t = time.perf_counter()
+        O.hybrid_prefill(q, k, v, cfg["window"], cfg["cache_size"], cfg["refresh"], 1.0 / math.sqrt(cfg["d"]))
+        elapsed += time.perf_counter() - t
+        done += 1
+        if elapsed >= budget_s:
+            break
+    tokens = done * T / H
+    return _baseline(tokens / elapsed, "tokens/s",
+                     f"{done} of {B * H} heads x {T} tokens, float64 block-by-block refresh chain, "
+                     f"{elapsed:.1f}s of CPU time, extrapolated x{B * H / done:g}")
+
+
+def bench_tiny(torch, K, S, steps, warmup):
+    """The tiny float32 configuration (1 x 1 x 256, d = 16, chunk 32): a
+    launch-bound parity case, timed as a whole call."""
+    cfg = S.CONFIGS["tiny_f32"]
+    c = S.prefill_case("tiny_f32", cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
+                       cfg["seed"], kind="tiny")
+    q, k, v = (torch.from_numpy(x).to("cuda") for x in (c.q, c.k, c.v))
+    o = torch.empty_like(v)
+    step_ms, kern_ms, _ = timed_calls(torch, K, lambda: K.prefill(q, k, v, chunk=cfg["chunk"], out=o),
+                                      max(steps, 20), warmup)
+    D = phi_dim(cfg["d_qk"])
+    flops = (4.0 * D * (cfg["d_v"] + 1) + (cfg["chunk"] + 1) * (cfg["d_qk"] + cfg["d_v"] + 1)) * cfg["T"]
+    return dict(workload="tiny_f32", B=1, H=1, T=cfg["T"], d_qk=cfg["d_qk"], d_v=cfg["d_v"], chunk=cfg["chunk"],
+                step_ms=step_ms, tokens_per_s=cfg["T"] / (step_ms * 1e-3), kernel_ms=kern_ms,
+                flops_per_call=flops, roofline=None,
+                note="launch-bound: 2.65 MFLOP per call; no roofline claim", arith="f32")
 
 
 def main():
@@ -382,7 +516,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-steps", type=int, default=None, help="steps of the decode loop (128)")
-    ap.add_argument("--only", choices=["prefill_1x16x65536", "prefill_4x8x4096_quadratic",
+    ap.add_argument("--only", choices=["tiny_f32", "prefill_1x16x65536", "prefill_4x8x4096_quadratic",
                                        "prefill_4x8x4096_m2", "prefill_4x8x4096_sigma2",
                                        "prefill_4x8x4096_m2_state", "prefill_1x16x65536_m2_state",
                                        "prefill_4x8x4096_backward", "decode_sre_4096x128",
@@ -416,7 +550,9 @@ def main():
         return
     K.load_library()
     if args.only:
-        if args.only == "prefill_1x16x65536":
+        if args.only == "tiny_f32":
+            r = bench_tiny(torch, K, S, args.steps, args.warmup)
+        elif args.only == "prefill_1x16x65536":
             r = bench_prefill(torch, K, S, args.only, args.steps, args.warmup)
         elif args.only == "prefill_4x8x4096_quadratic":
             r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
@@ -441,9 +577,19 @@ def main():
     main_r = bench_prefill(torch, K, S, name, args.steps, args.warmup)
     log(f"[bench] main done: {main_r['step_ms']:.3f} ms/step")
     secondary = []
+    cpu_on = not args.no_cpu_baseline
     if not args.no_secondary:
+        log("[bench] secondary: tiny_f32")
+        r = bench_tiny(torch, K, S, args.steps, args.warmup)
+        if cpu_on:
+            r["cpu_baseline"] = cpu_baseline(S, "tiny_f32", 1.0)
+        secondary.append(r)
         log("[bench] secondary: prefill_1x16x65536")
-        secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1))
+        r = bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1)
+        if cpu_on:
+            log("[bench] cpu baseline (oracle): prefill_1x16x65536")
+            r["cpu_baseline"] = cpu_baseline(S, "prefill_1x16x65536", args.cpu_seconds * 0.5)
+        secondary.append(r)
         log("[bench] secondary: prefill_4x8x4096 in the quadratic form")
         secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup))
         log("[bench] secondary: prefill_4x8x4096 with the KATA-M2 lift (chunked state form)")
@@ -456,16 +602,24 @@ def main():
         log("[bench] secondary: prefill_4x8x4096 backward")
         secondary.append(bench_prefill_backward(torch, K, S, name, args.steps, args.warmup))
         log("[bench] secondary: decode_sre_4096x128")
-        secondary.append(bench_decode(torch, K, S, args.decode_steps, 2))
+        r = bench_decode(torch, K, S, args.decode_steps, 2)
+        if cpu_on:
+            log("[bench] cpu baseline (oracle): decode_sre_4096x128")
+            r["cpu_baseline"] = cpu_baseline_decode(S, args.cpu_seconds * 0.5)
+        secondary.append(r)
         torch.cuda.empty_cache()
         log("[bench] secondary: hybrid_2x16x16384")
-        secondary.append(bench_hybrid(torch, K, S, 3, 1))
+        r = bench_hybrid(torch, K, S, 3, 1)
+        if cpu_on:
+            log("[bench] cpu baseline (oracle): hybrid_2x16x16384")
+            r["cpu_baseline"] = cpu_baseline_hybrid(S, args.cpu_seconds * 0.5)
+        secondary.append(r)
         torch.cuda.empty_cache()
         log("[bench] secondary: hybrid_decode_4096")
         secondary.append(bench_hybrid_decode(torch, K, S))
     cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
+    if cpu_on:
+        log("[bench] cpu baseline (oracle): prefill_4x8x4096")
         cpu = cpu_baseline(S, name, args.cpu_seconds)
 
     cfg = S.CONFIGS[name]

@@ -39,6 +39,7 @@ __all__ = [
     "decode_case",
     "HybridCase",
     "hybrid_case",
+    "hybrid_head",
     "hybrid_decode_tokens",
     "DecodeStream",
     "CONFIGS",
@@ -307,6 +308,12 @@ def _hybrid_head(seed, b, h, T, d, dup_frac, noise, min_cos):
                 k[t] = cand
                 break
     return q, k, v, tuple(int(p) for p in pos)
+
+
+def hybrid_head(seed: int, b: int, h: int, T: int, d: int, dup_frac: float = 0.05, noise: float = 0.04,
+                min_cos: float = 0.9):
+    """Head (b, h) of hybrid_case on its own: (q, k, v, near-duplicate positions)."""
+    return _hybrid_head(seed, b, h, T, d, dup_frac, noise, min_cos)
 
 
 def hybrid_case(name: str, B: int, H: int, T: int, d: int, window: int, cache_size: int,

@@ -26,3 +26,12 @@ def test_prefill_case_head_subsets_match():
     sub = S.prefill_case("x", 2, 3, 50, 16, 8, 32, seed=11, heads=[(1, 2), (0, 1)])
     np.testing.assert_array_equal(sub.q[0, 0], full.q[1, 2])
     np.testing.assert_array_equal(sub.v[0, 1], full.v[0, 1])
+
+
+def test_hybrid_head_matches_case():
+    c = S.hybrid_case("x", 2, 3, 300, 16, 32, 8, 16, seed=7)
+    q, k, v, dups = S.hybrid_head(7, 1, 2, 300, 16)
+    np.testing.assert_array_equal(q, c.q[1, 2])
+    np.testing.assert_array_equal(k, c.k[1, 2])
+    np.testing.assert_array_equal(v, c.v[1, 2])
+    assert dups == c.dup_positions[5]
