@@ -24,7 +24,9 @@
  *   - Memory: every tensor pointer is a device pointer owned by the caller.
  *     The library never allocates or frees device memory and keeps no
  *     state between calls; scratch memory comes from the caller through
- *     `ws`, sized by the matching *_workspace_size query. Every device
+ *     `ws`, sized by the matching *_workspace_size query (the one exception,
+ *     kla_hybrid_decode_step_static, uses an array of the library's own,
+ *     described there). Every device
  *     pointer (tensors and `ws`) must be 16-byte aligned: the kernels move
  *     rows with 16-byte vector accesses. A misaligned pointer is rejected
  *     with KLA_ERR_INVALID_ARGUMENT.
@@ -77,7 +79,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 4
+#define KLA_ABI_VERSION 5
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -418,6 +420,25 @@ KLA_API kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps,
                                     const void* k, const void* v, kla_dtype_t in_dtype, void* o,
                                     kla_dtype_t out_dtype, int32_t* rejected, void* ws,
                                     size_t ws_bytes, kla_stream_t stream);
+/* kla_hybrid_decode_step_static - the same step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments, results and errors are those
+ * of kla_hybrid_decode_step, without `ws`: the scratch lives in a static
+ * device array inside the library, kla_hybrid_decode_static_limit() bytes
+ * (16 MiB) on each device, looked up once per device on the first call made
+ * with that device current. A call whose kla_hybrid_decode_workspace_size
+ * exceeds that limit returns KLA_ERR_UNSUPPORTED and enqueues nothing. The
+ * call allocates and frees nothing. Every call on one device shares that
+ * device's array: calls that overlap on one device (other streams, other
+ * threads) race and must be ordered by the caller. Nothing in the array has
+ * to be cleared between calls. */
+KLA_API size_t kla_hybrid_decode_static_limit(void);
+KLA_API kla_status_t kla_hybrid_decode_step_static(int N, int d_qk, int d_v, float eps,
+                                           const kla_hybrid_cfg_t* cfg, int t,
+                                           const kla_hybrid_state_t* state, const void* q,
+                                           const void* k, const void* v, kla_dtype_t in_dtype,
+                                           void* o, kla_dtype_t out_dtype, int32_t* rejected,
+                                           kla_stream_t stream);
 /* Folds the pending pair into (H, s) and zeroes it (H, s, pend_k, pend_v of
  * `state` are used). */
 KLA_API kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_state_t* state,

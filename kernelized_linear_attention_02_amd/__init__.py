@@ -11,6 +11,8 @@ ABI of include/kla.h); this package only marshals arguments to it:
   sre_select      self-recall-error scoring and top-k selection
   hybrid_prefill  sliding window + linear state + sparse cache
   hybrid_decode_step  the same three memories, one token at a time
+  hybrid_decode_step_static  that step with the library's static scratch
+                      (allocates nothing)
 
 ``synth`` builds the seeded synthetic workloads.
 """
@@ -22,7 +24,9 @@ from ._binding import (  # noqa: F401
     factor_phi_dim,
     hybrid_decode_flush,
     hybrid_decode_state,
+    hybrid_decode_static_limit,
     hybrid_decode_step,
+    hybrid_decode_step_static,
     hybrid_prefill,
     load_library,
     phi_dim,
@@ -36,6 +40,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["prefill", "prefill_quadratic", "prefill_quadratic_backward", "decode_step", "sre_select", "hybrid_prefill",
-           "hybrid_decode_state", "hybrid_decode_step", "hybrid_decode_flush", "phi_dim", "factor_phi_dim",
+           "hybrid_decode_state", "hybrid_decode_step", "hybrid_decode_step_static",
+           "hybrid_decode_static_limit", "hybrid_decode_flush", "phi_dim", "factor_phi_dim",
            "load_library",
            "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

@@ -27,6 +27,7 @@ EXPORTS = (
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill", "kla_hybrid_prefill_streams",
     "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step", "kla_hybrid_decode_flush",
+    "kla_hybrid_decode_static_limit", "kla_hybrid_decode_step_static",
     "kla_profile_enable", "kla_profile_read",
 )
 
@@ -104,6 +105,8 @@ def load_library(path: str = LIB_PATH):
         "kla_hybrid_decode_workspace_size": (i, [i, i, i, hcp, szp]),
         "kla_hybrid_decode_step": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp, sz, vp]),
         "kla_hybrid_decode_flush": (i, [i, i, i, hsp, vp]),
+        "kla_hybrid_decode_static_limit": (sz, []),
+        "kla_hybrid_decode_step_static": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp]),
         "kla_profile_enable": (i, [i]),
         "kla_profile_read": (i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                  ctypes.POINTER(ctypes.c_int)]),
@@ -500,6 +503,42 @@ def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, sof
     check(lib.kla_hybrid_decode_step(N, dqk, dv, float(eps), ctypes.byref(cfg), int(t), ctypes.byref(st),
                                      _ptr(q), _ptr(k), _ptr(v), code, _ptr(o), ocode, _ptr(rej), _ptr(ws),
                                      nbytes.value, _stream(dev)))
+    return (o, rej) if rejected else o
+
+
+def hybrid_decode_static_limit() -> int:
+    """Bytes of the library's static scratch for hybrid_decode_step_static."""
+    return int(load_library().kla_hybrid_decode_static_limit())
+
+
+def hybrid_decode_step_static(state, t: int, q, k, v, window: int, cache_size: int, softmax_scale=None,
+                              eps: float = 0.0, out_dtype=None, rejected: bool = False, out=None,
+                              rejected_out=None):
+    """hybrid_decode_step through the entry point that allocates nothing: its
+    scratch is the library's static per-device array, so no workspace is
+    passed. ``out`` / ``rejected_out`` may pass preallocated outputs; with
+    both given (and contiguous, aligned inputs) this wrapper allocates
+    nothing either. Calls that overlap on one device race."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(q, k, v)
+    st = _hybrid_state_struct(state)
+    q, k, v = _dense(q), _dense(k), _dense(v)
+    N, dqk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    cfg = HybridCfg(int(window), int(cache_size), 1, float(softmax_scale))
+    dev = q.device
+    o = out if out is not None else torch.empty((N, dv), dtype=_torch_dtype(ocode), device=dev)
+    rej = None
+    if rejected:
+        rej = rejected_out if rejected_out is not None else torch.empty((N,), dtype=torch.int32, device=dev)
+    check(lib.kla_hybrid_decode_step_static(N, dqk, dv, float(eps), ctypes.byref(cfg), int(t), ctypes.byref(st),
+                                            _ptr(q), _ptr(k), _ptr(v), code, _ptr(o), ocode, _ptr(rej),
+                                            _stream(dev)))
     return (o, rej) if rejected else o
 
 

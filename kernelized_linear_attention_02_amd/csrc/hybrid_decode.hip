@@ -37,6 +37,7 @@
 //               softmax (online maximum), the joint division, the window
 //               insert, and the new pending pair.
 #include <algorithm>
+#include <mutex>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
@@ -1113,6 +1114,41 @@ hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st)
   KLA_CASE(64, 16) KLA_CASE(64, 32) KLA_CASE(64, 64)
 #undef KLA_CASE
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- static scratch
+
+// Scratch for callers that cannot allocate (HIP graph capture, serving loops,
+// harnesses that forbid device allocation): the scores and linear readouts of
+// kla_hybrid_decode_step_static live in this array instead of a caller
+// workspace. Each device that the library runs on holds its own copy until
+// the process ends. Every call on a device uses that device's copy, so calls
+// that overlap on one device race; nothing in it has to start at zero (every
+// call writes what it reads).
+namespace {
+static __device__ __align__(256) unsigned char scratch[kHybridDecodeStaticScratch];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t hybrid_decode_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // once per device, with that device current: the array's device address
+  // (the name itself is only a host-side stand-in)
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace kla

@@ -649,11 +649,16 @@ kla_status_t kla_hybrid_decode_workspace_size(int N, int d_qk, int d_v, const kl
   return ok();
 }
 
-kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const kla_hybrid_cfg_t* cfg, int t,
-                                    const kla_hybrid_state_t* state, const void* q, const void* k,
-                                    const void* v, kla_dtype_t in_dtype, void* o, kla_dtype_t out_dtype,
-                                    int32_t* rejected, void* ws, size_t ws_bytes, kla_stream_t stream) {
-  const char* fn = "kla_hybrid_decode_step";
+}  // extern "C"
+
+namespace {
+
+// Checks and argument packing shared by the two hybrid decode entry points;
+// `ws` may be NULL here (the static variant brings its own scratch).
+kla_status_t hybrid_decode_args(const char* fn, int N, int d_qk, int d_v, float eps, const kla_hybrid_cfg_t* cfg,
+                                int t, const kla_hybrid_state_t* state, const void* q, const void* k, const void* v,
+                                kla_dtype_t in_dtype, void* o, kla_dtype_t out_dtype, int32_t* rejected,
+                                const void* ws, kla::HybridDecodeArgs* out) {
   kla_status_t st = check_hybrid_decode(N, d_qk, d_v, cfg, fn);
   if (st != KLA_OK) return st;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(KLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
@@ -674,7 +679,8 @@ kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const k
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state pointers must be 16-byte aligned", fn);
   st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"rejected", rejected}, {"ws", ws}});
   if (st != KLA_OK) return st;
-  kla::HybridDecodeArgs a{};
+  kla::HybridDecodeArgs& a = *out;
+  a = kla::HybridDecodeArgs{};
   a.N = N;
   a.dqk = d_qk;
   a.dv = d_v;
@@ -699,9 +705,48 @@ kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const k
   a.v = v;
   a.o = o;
   a.rejected = rejected;
+  return KLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const kla_hybrid_cfg_t* cfg, int t,
+                                    const kla_hybrid_state_t* state, const void* q, const void* k,
+                                    const void* v, kla_dtype_t in_dtype, void* o, kla_dtype_t out_dtype,
+                                    int32_t* rejected, void* ws, size_t ws_bytes, kla_stream_t stream) {
+  const char* fn = "kla_hybrid_decode_step";
+  kla::HybridDecodeArgs a;
+  kla_status_t st = hybrid_decode_args(fn, N, d_qk, d_v, eps, cfg, t, state, q, k, v, in_dtype, o, out_dtype,
+                                       rejected, ws, &a);
+  if (st != KLA_OK) return st;
   st = check_ws(kla::hybrid_decode_workspace(a), ws, ws_bytes, fn);
   if (st != KLA_OK) return st;
   return hip_status(kla::hybrid_decode_launch(a, ws, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t kla_hybrid_decode_static_limit(void) { return kla::kHybridDecodeStaticScratch; }
+
+kla_status_t kla_hybrid_decode_step_static(int N, int d_qk, int d_v, float eps, const kla_hybrid_cfg_t* cfg, int t,
+                                           const kla_hybrid_state_t* state, const void* q, const void* k,
+                                           const void* v, kla_dtype_t in_dtype, void* o, kla_dtype_t out_dtype,
+                                           int32_t* rejected, kla_stream_t stream) {
+  const char* fn = "kla_hybrid_decode_step_static";
+  kla::HybridDecodeArgs a;
+  kla_status_t st = hybrid_decode_args(fn, N, d_qk, d_v, eps, cfg, t, state, q, k, v, in_dtype, o, out_dtype,
+                                       rejected, nullptr, &a);
+  if (st != KLA_OK) return st;
+  const size_t need = kla::hybrid_decode_workspace(a);
+  if (need > kla::kHybridDecodeStaticScratch)
+    return fail(KLA_ERR_UNSUPPORTED,
+                "%s: this call needs %zu bytes of scratch, more than the library's static %zu "
+                "(use kla_hybrid_decode_step with a workspace)",
+                fn, need, (size_t)kla::kHybridDecodeStaticScratch);
+  void* scratch = nullptr;
+  const hipError_t e = kla::hybrid_decode_static_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(kla::hybrid_decode_launch(a, scratch, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_state_t* state,

@@ -161,4 +161,10 @@ hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t
 // Folds the pending pair into (H, s) and clears it (uses N, dqk, dv, H, s, pend_k, pend_v).
 hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st);
 
+// Size of the library's static scratch for the allocation-free hybrid decode
+// step, and its device address on the current device (looked up once per
+// device).
+constexpr size_t kHybridDecodeStaticScratch = size_t(16) << 20;
+hipError_t hybrid_decode_static_scratch(void** out);
+
 }  // namespace kla

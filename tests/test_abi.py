@@ -258,6 +258,7 @@ def test_hybrid_decode_validation(lib):
     no_pend = B.HybridState(*([0x10000] * 7), None, None)
     assert call(state=no_pend) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"pend_k" in lib.kla_last_error()
+
     need = ctypes.c_size_t(0)
     assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == B.KLA_OK
     assert need.value >= 8 * 129 * 4 + 8 * 65 * 4  # scores of lambda + 1 candidates, linear readouts
@@ -274,6 +275,36 @@ def test_hybrid_decode_validation(lib):
 
 
 M = ctypes.c_void_p(0x10008)  # 8-byte aligned only: every call must refuse it
+
+
+def test_hybrid_decode_static_validation(lib):
+    # host-side checks of the allocation-free step: the same argument checks
+    # as the workspace step, then the static scratch limit (all before any
+    # device call, so they run without a GPU)
+    assert lib.kla_hybrid_decode_static_limit() == 16 << 20
+    st = B.HybridState(*([0x10000] * 9))
+    cfg = B.HybridCfg(512, 128, 1, 0.125)
+
+    def call(cfg=cfg, N=8, t=600, state=st, o=P, q=P):
+        return lib.kla_hybrid_decode_step_static(N, 64, 64, 0.0, ctypes.byref(cfg) if cfg else None, t,
+                                                 ctypes.byref(state) if state else None, q, P, P, B.KLA_BF16,
+                                                 o, B.KLA_F32, None, None)
+
+    assert call(cfg=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(N=0) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(t=-1) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(state=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(o=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert call(q=ctypes.c_void_p(0x10004)) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.kla_last_error()
+    # 129 scores + 68 readout floats per head-state: 21290 fit in 16 MiB
+    need = ctypes.c_size_t(0)
+    assert lib.kla_hybrid_decode_workspace_size(21290, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == 0
+    assert need.value <= 16 << 20
+    assert lib.kla_hybrid_decode_workspace_size(21400, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == 0
+    assert need.value > 16 << 20
+    assert call(N=21400) == B.KLA_ERR_UNSUPPORTED
+    assert b"static" in lib.kla_last_error()
 
 
 def _misaligned(lib, status):

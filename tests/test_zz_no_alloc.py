@@ -1,0 +1,112 @@
+"""kla_hybrid_decode_step_static, the hybrid decode step that allocates
+nothing (its scratch is a static per-device array inside the library),
+against kla_hybrid_decode_step with a caller workspace.
+
+Both run the same kernels on the same state, so every output, every
+rejected id and every state tensor must agree bit for bit. Two static calls
+in a row check that a call does not depend on what the previous one left in
+the shared array: the second has fewer head-states (and the third a smaller
+shape on the other kernel path) than the first.
+"""
+import pytest
+
+from kernelized_linear_attention_02_amd import synth as S
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids", "pend_k", "pend_v")
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kernelized_linear_attention_02_amd as K
+    K.load_library()
+    return K
+
+
+def _filled_state(K, q, k, v, W, lam, T0):
+    N, d = q.shape[1], q.shape[2]
+    st = K.hybrid_decode_state(N, d, v.shape[-1], W, lam, "cuda")
+    for t in range(T0):
+        K.hybrid_decode_step(st, t, q[t], k[t], v[t], W, lam)
+    return st
+
+
+def _heads(st, n):
+    return {name: st[name][:n].clone() for name in FIELDS}
+
+
+def _same(a, b, what):
+    assert a.shape == b.shape and a.dtype == b.dtype, what
+    assert torch.equal(a, b), f"{what}: static and workspace entry points differ"
+
+
+def _step_both(K, A, B, t, q, k, v, W, lam, out_dtype=None):
+    """One step of A through the workspace entry point and of B through the
+    static one; B's outputs are preallocated, so nothing is allocated around
+    the static call either."""
+    N, dv = q.shape[0], v.shape[-1]
+    oa, ra = K.hybrid_decode_step(A, t, q, k, v, W, lam, out_dtype=out_dtype, rejected=True)
+    ob = torch.empty((N, dv), dtype=oa.dtype, device="cuda")
+    rb = torch.empty((N,), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    K.hybrid_decode_step_static(B, t, q, k, v, W, lam, out_dtype=out_dtype, rejected=True, out=ob,
+                                rejected_out=rb)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    _same(oa, ob, f"o at t={t}, N={N}")
+    _same(ra, rb, f"rejected at t={t}, N={N}")
+    for name in FIELDS:
+        _same(A[name], B[name], f"state {name} at t={t}, N={N}")
+    return ra
+
+
+def test_static_limit(K):
+    assert K.hybrid_decode_static_limit() == 16 << 20
+
+
+def test_static_step_matches_workspace_step_twice(K):
+    # first call: 1024 head-states at a refresh step of the matrix-core path
+    # (d = 64, window 64, cache 32, bf16 tokens); second call: 96 of them
+    N, d, W, lam = 1024, 64, 64, 32
+    T0 = W + 1 + lam + 8
+    q, k, v = S.hybrid_decode_tokens(N, T0 + 2, d, seed=11, dup_frac=0.05)
+    A = _filled_state(K, q, k, v, W, lam, T0)
+    B = _heads(A, N)
+    print(f"[no_alloc] N={N} d={d} W={W} lam={lam} t={T0}", flush=True)
+    rej = _step_both(K, A, B, T0, q[T0], k[T0], v[T0], W, lam)
+    assert bool((rej >= 0).all())  # every head-state refreshed and folded a pair
+    n2 = 96
+    A2, B2 = _heads(A, n2), _heads(B, n2)
+    t = T0 + 1
+    print(f"[no_alloc] N={n2} t={t}", flush=True)
+    _step_both(K, A2, B2, t, q[t, :n2], k[t, :n2], v[t, :n2], W, lam, out_dtype=torch.float32)
+
+
+def test_static_step_other_path_after_a_larger_call(K):
+    # a larger call on the matrix-core path, then a small float32 call with
+    # d_qk = 32, d_v = 16 (the fold + scoring kernels), which reads less of
+    # the array than the call before wrote
+    N, d, W, lam = 512, 64, 16, 64
+    T0 = W + 1 + lam + 3
+    q, k, v = S.hybrid_decode_tokens(N, T0 + 1, d, seed=12, dup_frac=0.05)
+    A = _filled_state(K, q, k, v, W, lam, T0)
+    B = _heads(A, N)
+    print(f"[no_alloc] N={N} d={d} W={W} lam={lam} t={T0}", flush=True)
+    _step_both(K, A, B, T0, q[T0], k[T0], v[T0], W, lam)
+
+    n2, dqk, dv, W2, lam2 = 40, 32, 16, 8, 12
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    T2 = W2 + 1 + lam2 + 5
+    q2 = torch.nn.functional.normalize(torch.randn((T2 + 1, n2, dqk), generator=g, device="cuda"), dim=-1)
+    k2 = torch.nn.functional.normalize(torch.randn((T2 + 1, n2, dqk), generator=g, device="cuda"), dim=-1)
+    v2 = torch.randn((T2 + 1, n2, dv), generator=g, device="cuda")
+    A2 = _filled_state(K, q2, k2, v2, W2, lam2, T2)
+    B2 = _heads(A2, n2)
+    print(f"[no_alloc] N={n2} dqk={dqk} dv={dv} W={W2} lam={lam2} t={T2}", flush=True)
+    _step_both(K, A2, B2, T2, q2[T2], k2[T2], v2[T2], W2, lam2)
