@@ -27,36 +27,44 @@
 // significands) with exact power-of-two scales that keep every value in
 // float16 range whatever the inputs: each sub-chunk's keys are scaled by
 // 2^-ek (largest |k| below 1) and its values by 2^(2 ek - G), where the
-// running exponent G >= 2 ek + log2 max|v| of every sub-chunk seen; the
-// accumulators hold H 2^-G (rescaled when G grows). Queries are scaled per
-// token (undone before the partials are written). The published state is
-// scaled by 2^-P so that a bound on its largest weighted entry stays below
-// 2^15.
-// Accumulation is float32 throughout; the slice partials are float32.
+// running exponent G is at least 2 ek + log2 max|v| of every sub-chunk seen
+// and large enough that a running bound on every accumulated entry stays
+// below 2^14 in units of 2^G; the accumulators hold H 2^-G (rescaled when G
+// grows), so the published state, weighted by at most 2, fits float16 as it
+// is. Queries are scaled per token (undone before the partials are
+// written). Accumulation is float32 throughout; the slice partials are
+// float32.
 //
-// State kernel, eight waves, stepping through sub-chunks of up to 64 tokens;
-// each step has two barriers: between them the update waves publish the
-// state (at chunk ends), the readout waves write their partials and stage
-// the next sub-chunk; around them every wave computes on the staged one.
+// Staging kernel. One work-group per (head, sub-chunk of up to 64 tokens)
+// converts the sub-chunk once: the exponents, q rows times 2^-eq (per
+// token), k columns times 2^-ek and v columns times 2^-ev (its own largest
+// |v|), as float16 in the layout the state kernel copies into LDS.
+//
+// State kernel, eight waves, stepping through the staged sub-chunks with one
+// barrier per step; the staging buffers, the published state and the
+// readout trade are double-buffered so no wave waits on another within a
+// step.
 //   update waves (4) hold their tiles of G for the whole sequence in MFMA
 //   accumulators and add phi(K)^T V per 32 tokens (mfma 16x16x32 f16): a lane
 //   of the A operand holds feature row r for eight tokens and forms them as
-//   packed float16 products of its k_a and k_b, k_b coming from lane 0 of its
-//   16-lane row by a DPP broadcast. In the first value half's work-group each
-//   wave also accumulates one X block of the keys' Gram matrix for the
-//   slice's columns b (the staged float16 keys hold the bf16 keys exactly up
-//   to the sub-chunk's power of two: exact products, float32 sums). At each
-//   chunk end they publish the weighted state (2 off the diagonal, 1 on it, 0
-//   for mirror rows) as float16 B fragments in LDS and the Gram matrix to
-//   memory.
+//   packed float16 products of its k_a and of k_b (an LDS broadcast read:
+//   the same address on all 16 lanes of a row). In the first value half's
+//   work-group each wave also accumulates one X block of the keys' Gram
+//   matrix for the slice's columns b (the staged float16 keys hold the bf16
+//   keys exactly up to the sub-chunk's power of two: exact products, float32
+//   sums). At each chunk end they publish the state of the next chunk's start
+//   as float16 B fragments in LDS (diagonal-block rows weighted 2 for a < b,
+//   1 for a = b, 0 for the mirror rows), each tile right after its last
+//   product, and the Gram matrix to memory.
 //   readout waves (4): each takes 32 tokens and half of the tile pairs and
 //   reads out phi(Q) G against the state of the chunk start; a lane holds one
-//   token and forms its products from q values in registers. The two waves
-//   sharing tokens trade halves through LDS, and each writes one float32
-//   partial [16 tokens x 32 columns] per token tile in the MFMA accumulator
-//   order. They also stage the sub-chunks (q rows, k columns, v columns of
-//   the work-group's half), in two passes: the scales' maxima before the
-//   middle barrier, the scaled values after it.
+//   token and forms its products from q values in registers (q_b doubled for
+//   the off-diagonal blocks, whose features weigh 2). The two waves sharing
+//   tokens trade halves through LDS, and each writes one float32 partial
+//   [16 tokens x 32 columns] per token tile in the MFMA accumulator order,
+//   a step later. They also copy the staged sub-chunks into LDS (v scaled to
+//   the running exponent) and track the exponents; each sub-chunk is loaded
+//   two steps ahead and written one step ahead.
 //
 // Finish kernel. One work-group per (head, chunk): the exact intra-chunk term
 // (squared scores as two bf16 pieces times V), the denominator's state term
@@ -78,6 +86,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -109,15 +118,17 @@ __device__ __forceinline__ int exp_above(float m) {
   return be == 0 ? -126 : be - 126;
 }
 
+// Largest of the wave's values (all >= 0: they order like their bit
+// patterns), on every lane: DPP shifts within rows of 16, then across rows.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-
-// x from lane 0 of this lane's 16-lane row (DPP row broadcast).
-__device__ __forceinline__ uint32_t row_bcast0(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150, 0xF, 0xF, true);
+  int v = __float_as_int(x);
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
@@ -125,7 +136,6 @@ __device__ __forceinline__ uint32_t as_u(f16x2 x) { return __builtin_bit_cast(ui
 
 // Largest |x| of bf16 values as a bf16 bit pattern: |x| orders like the low
 // 15 bits of the pattern (packed 16-bit maxima).
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u16x2 abs_pair(uint32_t x) { return __builtin_bit_cast(u16x2, x & 0x7FFF7FFFu); }
 __device__ __forceinline__ u16x2 absmax_pairs(uint4 w) {
   return __builtin_elementwise_max(__builtin_elementwise_max(abs_pair(w.x), abs_pair(w.y)),
@@ -134,7 +144,7 @@ __device__ __forceinline__ u16x2 absmax_pairs(uint4 w) {
 __device__ __forceinline__ uint32_t pair_max(u16x2 m) { return max((uint32_t)m[0], (uint32_t)m[1]); }
 
 // Eight bf16 values times 2^e, rounded to float16 (nearest even).
-__device__ __forceinline__ uint4 bf16x8_to_f16_scaled(uint4 w, int e) {
+__device__ __forceinline__ uint4 bf16x8_to_f16_scaled_fp(uint4 w, int e) {
   const uint32_t in[4] = {w.x, w.y, w.z, w.w};
   uint32_t out[4];
 #pragma unroll
@@ -142,6 +152,29 @@ __device__ __forceinline__ uint4 bf16x8_to_f16_scaled(uint4 w, int e) {
     const float lo = __builtin_ldexpf(bf16f(in[i] & 0xFFFFu), e);
     const float hi = __builtin_ldexpf(bf16f(in[i] >> 16), e);
     out[i] = as_u(f16x2{(_Float16)lo, (_Float16)hi});
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// The same for scaled values below 1 (every use here), by exponent
+// arithmetic on the bit patterns: a bf16 significand fits float16's, so a
+// value of float16's normal range is exact; the exponent field is lowered by
+// 112 - e with saturation at zero, which flushes what falls below float16's
+// normal range (magnitudes under 2^-14) to zero. Needs 112 - e >= 1 (bf16
+// subnormals then flush too); below -143, where every value underflows, the
+// shift saturates at 255.
+__device__ __forceinline__ uint4 bf16x8_to_f16_scaled(uint4 w, int e) {
+  if (e > 111) return bf16x8_to_f16_scaled_fp(w, e);
+  const unsigned short k = (unsigned short)(min(112 - e, 255) << 7);
+  const u16x2 K = {k, k};
+  const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u16x2 m = __builtin_bit_cast(u16x2, in[i] & 0x7FFF7FFFu);
+    const u16x2 t = __builtin_elementwise_sub_sat(m, K);
+    const u16x2 f = t << (u16x2){3, 3};
+    out[i] = (in[i] & 0x80008000u) | __builtin_bit_cast(uint32_t, f);
   }
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
@@ -240,18 +273,18 @@ __host__ __device__ __forceinline__ bool same_factor(int a, int b) {
 
 template <int SF, int G>
 struct StateLds {
-  uint4 hs[Slice<SF, G>::kPairs][2][64];  // weighted state, float16 B fragments
-  f32x4 xs[kRW][2][64];                   // readout trade: one token tile's accumulators
-  // staged sub-chunks, double buffered (the next is staged during this one)
+  // published state of the chunk start, by chunk parity: float16 B fragments
+  // (diagonal-block rows weighted 2 / 1 / 0, other tiles unweighted)
+  uint4 hs[2][Slice<SF, G>::kPairs][2][64];
+  f32x4 xs[2][kRW][2][64];                // readout trade, by step parity
+  // staged sub-chunks, by step parity (sub-chunk s + 1 is staged during s)
   _Float16 qs[2][kCS][kDim + kPad];       // q rows, scaled per token
   _Float16 kt[2][kDim][kCS + kPad];       // k columns, scaled per sub-chunk
   _Float16 vt[2][kCols][kCS + kPad];      // v columns of the work-group's half, scaled
   int qe[2][kCS];                         // per-token query exponent
   int sc[2][2];                           // per buffer: key exponent ek, state exponent G
-  float qmx[kRW][kCS];                    // staging: per wave and token, max |q| over its dims
-  float kvmx[kRW][2];                     // staging: per wave, max |k| and max |v|
   float umx[kUW];                         // per update wave, max |imported state|
-  int pub_e;                              // exponent of the published state (G + P)
+  int pub_e[2];                           // exponent of the published state, by chunk parity
 };
 
 // LDS-only work-group barrier: waits for this wave's LDS traffic, not for
@@ -261,28 +294,50 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// One token's share of a sub-chunk for staging wave W: q and k dims
-// 16 W .. 16 W + 15, v dims 32 ch + 8 W .. + 7. The loads are unconditional (a
-// token past the end reads the last row and is zeroed), so that no branch
-// has to wait for them.
-struct Prefetch {
-  uint4 q[2], k[2], v;
-  bool ok;
+// The staged sub-chunks come from the staging kernel below: per head and
+// sub-chunk of CS tokens, float16 q rows (scaled per token), k columns
+// (scaled per sub-chunk) and v columns (scaled by their own maximum), plus
+// the exponents. The readout waves copy a sub-chunk into LDS as 16-byte
+// pieces: 8 CS of q, 8 CS of k and 4 CS of the work-group's v half, dealt
+// round-robin to the 256 lanes r of the four readout waves.
+template <int CS>
+struct Stage {
+  static constexpr int kHalves = 3 * kDim * CS;  // per head and sub-chunk
+  static constexpr int kExps = 4 * CS;           // per token: eq, ek, ev, 0
+  static constexpr int kPieces = 20 * CS;
+  static constexpr int kPerLane = (kPieces + 255) / 256;
 };
 
-__device__ __forceinline__ Prefetch prefetch(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                             const uint16_t* __restrict__ v, size_t row0, int n0, int T, int t,
-                                             int W, int ch) {
-  Prefetch p;
-  const size_t row = (row0 + min(n0 + t, T - 1)) * kDim;
+template <int CS>
+struct StageLoad {
+  uint4 c[Stage<CS>::kPerLane];
+  int eq;      // query exponent of token r (r < CS)
+  int ek, ev;  // the sub-chunk's key and value exponents
+};
+
+template <int CS>
+__device__ __forceinline__ StageLoad<CS> load_stage(const uint16_t* __restrict__ blk, const int* __restrict__ ex,
+                                                    int ch, int r) {
+  constexpr int RW = CS / 8;  // pieces per k or v column
+  StageLoad<CS> L;
+  const int4 e4 = *reinterpret_cast<const int4*>(ex + 4 * min(r, CS - 1));
+  L.eq = e4.x;
+  L.ek = e4.y;
+  L.ev = e4.z;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    p.q[g] = *reinterpret_cast<const uint4*>(q + row + 16 * W + 8 * g);
-    p.k[g] = *reinterpret_cast<const uint4*>(k + row + 16 * W + 8 * g);
+  for (int i = 0; i < Stage<CS>::kPerLane; ++i) {
+    const int c = r + 256 * i;
+    if (c < 8 * CS) {
+      L.c[i] = *reinterpret_cast<const uint4*>(blk + (c >> 3) * kDim + 8 * (c & 7));
+    } else if (c < 16 * CS) {
+      const int e = c - 8 * CS;
+      L.c[i] = *reinterpret_cast<const uint4*>(blk + kDim * CS + (e / RW) * CS + 8 * (e % RW));
+    } else if (c < 20 * CS) {
+      const int e = c - 16 * CS;
+      L.c[i] = *reinterpret_cast<const uint4*>(blk + 2 * kDim * CS + (kCols * ch + e / RW) * CS + 8 * (e % RW));
+    }
   }
-  p.v = *reinterpret_cast<const uint4*>(v + row + kCols * ch + 8 * W);
-  p.ok = n0 + t < T;
-  return p;
+  return L;
 }
 
 // Everything a wave of the state kernel needs about its work-group.
@@ -298,83 +353,66 @@ struct StateCtx {
   float* sT;
   float* part;  // slice partials [head, chunk, slice, token tile, kTilePart], or NULL
   float* Sg;    // Gram matrix at each chunk start [head, chunk, 64, 64], or NULL
+  const uint16_t* stage;  // staged sub-chunks [head, sub-chunk, kStageHalves]
+  const int* exps;        // their exponents [head, sub-chunk, kStageExps]
+  int NS;                 // sub-chunks per head
 };
 
-// Staging, first pass (before the middle barrier): maxima of the prefetched
-// values. Lane t < CS holds token t.
-template <int CS, class Lds>
-__device__ __forceinline__ void stage_max(Lds& sh, const Prefetch& p, int W, int lane) {
-  const bool act = lane < CS && p.ok;
-  uint32_t qm = 0, km = 0, vm = 0;
-  if (act) {
-    qm = pair_max(__builtin_elementwise_max(absmax_pairs(p.q[0]), absmax_pairs(p.q[1])));
-    km = pair_max(__builtin_elementwise_max(absmax_pairs(p.k[0]), absmax_pairs(p.k[1])));
-    vm = pair_max(absmax_pairs(p.v));
-  }
-  if (lane < CS) sh.qmx[W][lane] = bf16f(qm);
-  const float kw = wave_max(bf16f(km));
-  const float vw = wave_max(bf16f(vm));
-  if (lane == 0) {
-    sh.kvmx[W][0] = kw;
-    sh.kvmx[W][1] = vw;
-  }
-}
-
-// The running state exponent: once the accumulators may hold something (an
-// imported state, or a sub-chunk with nonzero keys and values) it only grows;
-// before that it follows the first nonzero sub-chunk.
+// The running state exponent G: the accumulators hold the state times 2^-G.
+// It only grows once the accumulators may hold something (an imported state,
+// or a sub-chunk with nonzero keys and values); before that it follows the
+// first nonzero sub-chunk. It is at least the exponent of every sub-chunk's
+// largest possible term (so the scaled values stay below 1), and large
+// enough that a running bound b on every accumulated entry, in units of 2^G,
+// stays below 2^14: weighted by at most 2, the published state then fits
+// float16 without a further scale.
 struct ExpTrack {
   int G = 0;
   bool live = false;
-  __device__ void see(int E) {
-    G = live ? max(G, E) : E;
+  float b = 0.0f;
+  __device__ void start(float m) {  // an imported state whose largest entry is m > 0
+    G = exp_above(m) - 14;
+    b = __builtin_ldexpf(m, -G);
     live = true;
+  }
+  // n tokens whose every term is below 2^E
+  __device__ void add(int E, int n) {
+    if (!live) {
+      G = E;
+      b = 0.0f;
+      live = true;
+    } else if (E > G) {
+      b = __builtin_ldexpf(b, G - E);
+      G = E;
+    }
+    b += __builtin_ldexpf((float)n, E - G);
+    if (b >= 16384.0f) {
+      const int up = exp_above(b) - 14;
+      b = __builtin_ldexpf(b, -up);
+      G += up;
+    }
   }
 };
 
-// Staging, second pass (after the middle barrier): scales and scaled values
-// into buffer `buf`.
+// Writes a loaded sub-chunk into staging buffer `buf` (v times vs).
 template <int CS, class Lds>
-__device__ __forceinline__ void stage_write(Lds& sh, const Prefetch& p, int W, int lane, int buf, ExpTrack& g) {
-  const float kall = fmaxf(fmaxf(sh.kvmx[0][0], sh.kvmx[1][0]), fmaxf(sh.kvmx[2][0], sh.kvmx[3][0]));
-  const float vall = fmaxf(fmaxf(sh.kvmx[0][1], sh.kvmx[1][1]), fmaxf(sh.kvmx[2][1], sh.kvmx[3][1]));
-  const int ekr = exp_above(kall), ev = exp_above(vall);
-  // a sub-chunk whose keys or values are all zero adds nothing: its values
-  // are staged as zeros and the exponent does not move
-  const bool contributes = ekr != kNoExp && ev != kNoExp;
-  if (contributes) g.see(2 * ekr + ev);
-  const int ek = ekr == kNoExp ? 0 : ekr;
-  if (lane < CS) {
-    const int t = lane;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 q0 = p.ok ? p.q[0] : z, q1 = p.ok ? p.q[1] : z;
-    const uint4 k0 = p.ok ? p.k[0] : z, k1 = p.ok ? p.k[1] : z;
-    const uint4 vv = p.ok && contributes ? p.v : z;
-    const float qm = fmaxf(fmaxf(sh.qmx[0][t], sh.qmx[1][t]), fmaxf(sh.qmx[2][t], sh.qmx[3][t]));
-    const int eqr = exp_above(qm);
-    const int eq = eqr == kNoExp ? 0 : eqr;
-    *reinterpret_cast<uint4*>(&sh.qs[buf][t][16 * W]) = bf16x8_to_f16_scaled(q0, -eq);
-    *reinterpret_cast<uint4*>(&sh.qs[buf][t][16 * W + 8]) = bf16x8_to_f16_scaled(q1, -eq);
-    if (W == 0) sh.qe[buf][t] = eq;
-    const uint4 kh0 = bf16x8_to_f16_scaled(k0, -ek), kh1 = bf16x8_to_f16_scaled(k1, -ek);
-    const uint32_t kh[8] = {kh0.x, kh0.y, kh0.z, kh0.w, kh1.x, kh1.y, kh1.z, kh1.w};
+__device__ __forceinline__ void write_stage(Lds& sh, const StageLoad<CS>& L, int r, int buf, f16x2 vs) {
+  constexpr int RW = CS / 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 16 * W + 2 * e;
-      sh.kt[buf][d][t] = as_h2(kh[e])[0];
-      sh.kt[buf][d + 1][t] = as_h2(kh[e])[1];
+  for (int i = 0; i < Stage<CS>::kPerLane; ++i) {
+    const int c = r + 256 * i;
+    if (c < 8 * CS) {
+      *reinterpret_cast<uint4*>(&sh.qs[buf][c >> 3][8 * (c & 7)]) = L.c[i];
+    } else if (c < 16 * CS) {
+      const int e = c - 8 * CS;
+      *reinterpret_cast<uint4*>(&sh.kt[buf][e / RW][8 * (e % RW)]) = L.c[i];
+    } else if (c < 20 * CS) {
+      const int e = c - 16 * CS;
+      const uint4 v = L.c[i];
+      const uint4 vv = make_uint4(as_u(as_h2(v.x) * vs), as_u(as_h2(v.y) * vs), as_u(as_h2(v.z) * vs),
+                                  as_u(as_h2(v.w) * vs));
+      *reinterpret_cast<uint4*>(&sh.vt[buf][e / RW][8 * (e % RW)]) = vv;
     }
-    const uint4 vh = bf16x8_to_f16_scaled(vv, contributes ? 2 * ek - g.G : 0);
-    const uint32_t vw[4] = {vh.x, vh.y, vh.z, vh.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sh.vt[buf][8 * W + 2 * e][t] = as_h2(vw[e])[0];
-      sh.vt[buf][8 * W + 2 * e + 1][t] = as_h2(vw[e])[1];
-    }
-  }
-  if (W == 0 && lane == 0) {
-    sh.sc[buf][0] = ek;
-    sh.sc[buf][1] = g.G;
   }
 }
 
@@ -398,6 +436,15 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
   // Gram column of this lane: the slice's b values 16 Y + j0 + jj
   const int gb = 16 * (l16 / SL::kJ) + cx.j0 + (l16 % SL::kJ);
   const bool gb_ok = l16 < SL::kNB;
+
+  // readout weight of the rows 4 q4 .. 4 q4 + 3 of a diagonal-block tile
+  // (column j): 2 for a < b, 1 for a = b, 0 for the mirror rows a > b
+  f16x2 wdiag[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * q4 + i;
+    wdiag[i >> 1][i & 1] = (_Float16)(r < j ? 2.0f : (r == j ? 1.0f : 0.0f));
+  }
 
   // G (value n-tiles 0, 1 of the work-group's half) of each owned tile;
   // lane (l16, q4) holds rows 4 q4 + i, column l16 of an n-tile
@@ -439,40 +486,32 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
   if (lane == 0) sh.umx[W] = hmax;
 
   int Gu = 0;  // the accumulators hold G 2^-Gu
-  // Bound on |h| in current units: the imported state plus one per token
-  // (each token adds k'_a k'_b v'' with every factor below 1), scaled with
-  // the accumulators. Uniform across the wave.
-  float hb = 0.0f;
-  // publish the state at the start of chunk c; m bounds |h| in current units
-  auto publish = [&](int c, float m) {
-    // the largest weighted entry stays below 2^15 in float16
-    const int em = exp_above(2.0f * m);
-    const int P = em == kNoExp ? 0 : em - 15;
+  // publish the state at the start of chunk c (float16, diagonal-block rows
+  // weighted; the exponent bound keeps every weighted entry below 2^15)
+  // publish tile u of the state at the start of chunk c (float16,
+  // diagonal-block rows weighted; the exponent bound keeps every weighted
+  // entry below 2^15)
+  auto publish_tile = [&](int c, int u) {
+    const int pb = c & 1;
+    const int X = SL::X(U0 + u), Y = SL::Y(U0 + u);
+    const int pr = (U0 + u) >> 1;
+    const int half = (U0 + u) & 1;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int X = SL::X(U0 + u), Y = SL::Y(U0 + u);
-      const int pr = (U0 + u) >> 1;
-      const int half = (U0 + u) & 1;
-      // readout weight of each row: 2 off the diagonal blocks; on them 2 for
-      // a < b, 1 for a = b, 0 for the mirror rows a > b
-      float wr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * q4 + i;
-        const float w = X < Y ? 2.0f : (r < j ? 2.0f : (r == j ? 1.0f : 0.0f));
-        wr[i] = __builtin_ldexpf(w, -P);
+    for (int nt = 0; nt < 2; ++nt) {
+      f16x2 lo = {(_Float16)h[u][nt][0], (_Float16)h[u][nt][1]};
+      f16x2 hi = {(_Float16)h[u][nt][2], (_Float16)h[u][nt][3]};
+      if (X == Y) {
+        lo *= wdiag[0];
+        hi *= wdiag[1];
       }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const f16x2 lo = {(_Float16)(h[u][nt][0] * wr[0]), (_Float16)(h[u][nt][1] * wr[1])};
-        const f16x2 hi = {(_Float16)(h[u][nt][2] * wr[2]), (_Float16)(h[u][nt][3] * wr[3])};
-        uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<char*>(&sh.hs[pr][nt][lane]) + 8 * half);
-        *dst = make_uint2(as_u(lo), as_u(hi));
-      }
+      uint2* dst = reinterpret_cast<uint2*>(reinterpret_cast<char*>(&sh.hs[pb][pr][nt][lane]) + 8 * half);
+      *dst = make_uint2(as_u(lo), as_u(hi));
     }
-    if (W == 0 && lane == 0) sh.pub_e = Gu + P;
-    // the Gram matrix at the start of chunk c: each entry a <= b is written by
-    // its owner at (a, b) and (b, a)
+  };
+  // the rest of a publish: the exponent and the Gram matrix at the start of
+  // chunk c (each entry a <= b is written by its owner at (a, b) and (b, a))
+  auto publish_rest = [&](int c) {
+    if (W == 0 && lane == 0) sh.pub_e[c & 1] = Gu;
     if (gram_wg && cx.Sg && c < cx.NC && gb_ok) {
       float* S = cx.Sg + ((size_t)cx.n * cx.NC + c) * kDim * kDim;
 #pragma unroll
@@ -485,9 +524,14 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
       }
     }
   };
+  auto publish = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) publish_tile(c, u);
+    publish_rest(c);
+  };
 
-  lds_barrier();  // (B0a) state maxima and the first sub-chunk's maxima posted
-  lds_barrier();  // (B0b) first sub-chunk staged with its exponents
+  lds_barrier();  // (P1) state maxima and the first sub-chunks' maxima posted
+  lds_barrier();  // (P2) first sub-chunk staged with its exponents
   Gu = __builtin_amdgcn_readfirstlane(sh.sc[0][1]);
   {
     const float s = __builtin_ldexpf(1.0f, -Gu);
@@ -495,14 +539,30 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
     for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) h[u][nt] *= s;
-    const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
-    hb = m * s;
-    publish(0, hb);  // the state at the start of chunk 0
+    publish(0);  // the state at the start of chunk 0
   }
-  lds_barrier();  // (B0c) initial state published
+  lds_barrier();  // (P3) initial state published
 
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
+    // every operand of the sub-chunk, loaded at once: value fragments, the
+    // key rows a of the owned tiles' blocks, and k_b for each b block (the
+    // same address on all lanes of a 16-lane row: an LDS broadcast)
+    constexpr int KS = CS / 32;
+    f16x8 vb[KS][2];
+    uint4 ka[KS][4], kb[KS][4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int t0 = ks * 32 + 8 * q4;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) vb[ks][nt] = *reinterpret_cast<const f16x8*>(&sh.vt[buf][16 * nt + l16][t0]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (SL::upd_uses_x(W, x)) ka[ks][x] = *reinterpret_cast<const uint4*>(&sh.kt[buf][16 * x + l16][t0]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        if (SL::upd_uses_y(W, y)) kb[ks][y] = *reinterpret_cast<const uint4*>(&sh.kt[buf][16 * y + j][t0]);
+    }
     const int Gn = __builtin_amdgcn_readfirstlane(sh.sc[buf][1]);
     if (Gn != Gu) {  // uniform: the state exponent moved
       const float s = __builtin_ldexpf(1.0f, Gu - Gn);
@@ -510,39 +570,29 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
       for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) h[u][nt] *= s;
-      hb *= s;
       Gu = Gn;
     }
+    // at a chunk end the state of the next chunk's start is published into
+    // the other buffer (this chunk's readout still reads its own), each tile
+    // a few tiles behind its last product so its accumulators are done
+    const bool pub = st % SUB == SUB - 1;
+    const int cn = st / SUB + 1;
+    constexpr int kLag = 2;
 #pragma unroll
-    for (int ks = 0; ks < CS / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int t0 = ks * 32 + 8 * q4;
-      f16x8 vb[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) vb[nt] = *reinterpret_cast<const f16x8*>(&sh.vt[buf][16 * nt + l16][t0]);
-      uint4 ka[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-        if (SL::upd_uses_x(W, x)) ka[x] = *reinterpret_cast<const uint4*>(&sh.kt[buf][16 * x + l16][t0]);
-      uint4 kb[4];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        if (SL::upd_uses_y(W, y)) {
-          uint4 src = make_uint4(0, 0, 0, 0);
-          if (l16 == 0) src = *reinterpret_cast<const uint4*>(&sh.kt[buf][16 * y + j][t0]);
-          kb[y] = make_uint4(row_bcast0(src.x), row_bcast0(src.y), row_bcast0(src.z), row_bcast0(src.w));
-        }
-      }
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const uint4 xa = ka[SL::X(U0 + u)];
-        const uint4 xb = kb[SL::Y(U0 + u)];
+        const uint4 xa = ka[ks][SL::X(U0 + u)];
+        const uint4 xb = kb[ks][SL::Y(U0 + u)];
         const uint32_t p0 = as_u(as_h2(xa.x) * as_h2(xb.x));
         const uint32_t p1 = as_u(as_h2(xa.y) * as_h2(xb.y));
         const uint32_t p2 = as_u(as_h2(xa.z) * as_h2(xb.z));
         const uint32_t p3 = as_u(as_h2(xa.w) * as_h2(xb.w));
         const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(p0, p1, p2, p3));
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) h[u][nt] = mfma_h(A, vb[nt], h[u][nt]);
+        for (int nt = 0; nt < 2; ++nt) h[u][nt] = mfma_h(A, vb[ks][nt], h[u][nt]);
+        if (ks == KS - 1 && u >= kLag && pub) publish_tile(cn, u - kLag);
       }
       if (gram_wg) {
         const f16x8 A = *reinterpret_cast<const f16x8*>(&sh.kt[buf][16 * W + l16][t0]);
@@ -558,11 +608,12 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
       gram += gsub * s;
       gsub = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    hb += (float)CS;
-    const bool chunk_end = st % SUB == SUB - 1;
-    lds_barrier();  // (B2) sub-chunk consumed, readouts done
-    if (chunk_end) publish(st / SUB + 1, hb);
-    lds_barrier();  // (B1) state published, next sub-chunk staged
+    if (pub) {
+#pragma unroll
+      for (int u = NU - kLag; u < NU; ++u) publish_tile(cn, u);
+      publish_rest(cn);
+    }
+    lds_barrier();  // (B) one barrier per sub-chunk
   }
 
   // final state in the ABI layout (sqrt(2) on the off-diagonal features)
@@ -610,20 +661,20 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
   const size_t row0 = (size_t)cx.n * cx.T;
   const int nsteps = cx.NC * SUB;
   const bool active = kActive && cx.part != nullptr;
+  const int tl = 16 * (2 * TP + HF) + 4 * q4;  // tokens tl + i of the own token tile
 
-  f32x4 keep[2];
+  f32x4 keep[2];  // own token tile of the previous step, awaiting the partner's half
+  float fq[4];    // its scales 2^(2 eq + pe)
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) keep[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto flush = [&](int st, int buf, int pe) {
-    // add the partner's half of the own token tile, undo the scales
-    // (per-token query exponent, published-state exponent) and write the
-    // float32 partial
-    const f32x4* xs = &sh.xs[W ^ 1][0][0];
-    const int tl = 16 * (2 * TP + HF) + 4 * q4;  // tokens tl + i of the sub-chunk
-    float f[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __builtin_ldexpf(1.0f, 2 * sh.qe[buf][tl + i] + pe);
+  for (int i = 0; i < 4; ++i) fq[i] = 1.0f;
+
+  // add the partner's half of the own token tile of step st (traded through
+  // xs[st & 1]), undo the scales and write the float32 partial
+  auto flush = [&](int st, f32x4 k0, f32x4 k1, const float* f) {
+    const f32x4 kk[2] = {k0, k1};
+    const f32x4* xs = &sh.xs[st & 1][W ^ 1][0][0];
     const int c = st / SUB;
     const int tt = ((st % SUB) * CS) / 16 + 2 * TP + HF;
     float* pc = cx.part + ((((size_t)cx.n * cx.NC + c) * SF + cx.sf) * (C / 16) + tt) * kTilePart;
@@ -632,114 +683,239 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
       const f32x4 o = xs[nt * 64 + lane];
       f32x4 r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (keep[nt][i] + o[i]) * f[i];
+      for (int i = 0; i < 4; ++i) r[i] = (kk[nt][i] + o[i]) * f[i];
       *reinterpret_cast<f32x4*>(pc + ((2 * cx.ch + nt) * 64 + lane) * 4) = r;
     }
   };
 
-  auto pre = [&](int st) {
-    const int n0 = (st / SUB) * C + (st % SUB) * CS;
-    return prefetch(cx.q, cx.k, cx.v, row0, n0, cx.T, lane, W, cx.ch);
-  };
-  ExpTrack g;
-  Prefetch pf = pre(0);
-  stage_max<CS>(sh, pf, W, lane);
-  lds_barrier();  // (B0a)
-  if (cx.H0) {
-    // an imported state: the exponent starts where the accumulators hold it
-    // below 2^100 and then only grows
-    const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
-    const int e = exp_above(m);
-    if (e != kNoExp) g.see(e - 100);
-  }
-  stage_write<CS>(sh, pf, W, lane, 0, g);
-  if (nsteps > 1) pf = pre(1);
-  lds_barrier();  // (B0b)
-  lds_barrier();  // (B0c)
-
-  for (int st = 0; st < nsteps; ++st) {
+  // read out the tokens of step st against the state of its chunk start
+  auto compute = [&](int st) {
     const int buf = st & 1;
-    const int pe = sh.pub_e;  // published before this step's middle barrier
-    if (st + 1 < nsteps) stage_max<CS>(sh, pf, W, lane);
-    if (active) {
-      // q' factors of this lane's token in each of the two token tiles:
-      // qa[tt][X] = q'[16 X + 4 q4 + 0..3], qb[tt][Y] = q'[16 Y + j0 + 0..kJ-1]
-      uint2 qa[2][4];
-      uint32_t qb[2][4][SL::kJ / 2];  // packed pairs of q'_b
+    const int c = st / SUB;
+    const int pb = c & 1;
+    const int pe = sh.pub_e[pb];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fq[i] = __builtin_ldexpf(1.0f, 2 * sh.qe[buf][tl + i] + pe);
+    // q' factors of this lane's token in each of the two token tiles:
+    // qa[tt][X] = q'[16 X + 4 q4 + 0..3], qb[tt][Y] = q'[16 Y + j0 + 0..kJ-1]
+    // (qb2 = 2 qb, the weight of the off-diagonal features)
+    uint2 qa[2][4];
+    uint32_t qb[2][4][SL::kJ / 2], qb2[2][4][SL::kJ / 2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const _Float16* qrow = sh.qs[buf][32 * TP + 16 * tt + l16];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (SL::rd_uses_x(HF, x)) qa[tt][x] = *reinterpret_cast<const uint2*>(qrow + 16 * x + 4 * q4);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        if (SL::rd_uses_y(HF, y)) {
+          if constexpr (SL::kJ == 4) {
+            const uint2 w2 = *reinterpret_cast<const uint2*>(qrow + 16 * y + cx.j0);
+            qb[tt][y][0] = w2.x;
+            qb[tt][y][1] = w2.y;
+          } else {
+            qb[tt][y][0] = *reinterpret_cast<const uint32_t*>(qrow + 16 * y + cx.j0);
+          }
+#pragma unroll
+          for (int e = 0; e < SL::kJ / 2; ++e) qb2[tt][y][e] = as_u(as_h2(qb[tt][y][e]) + as_h2(qb[tt][y][e]));
+        }
+      }
+    }
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the state fragments of all pairs, loaded ahead of the products
+    f16x8 Bv[NP][2];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) Bv[p][nt] = __builtin_bit_cast(f16x8, sh.hs[pb][P0 + p][nt][lane]);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int pr = P0 + p;
+      const f16x8* B = Bv[p];
+      const int u0 = 2 * pr, u1 = 2 * pr + 1;
+      const int X0 = SL::X(u0), X1 = SL::X(u1), Y0 = SL::Y(u0), Y1 = SL::Y(u1);
+      const int J0 = SL::jj(u0), J1 = SL::jj(u1);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const _Float16* qrow = sh.qs[buf][32 * TP + 16 * tt + l16];
+        // q'_b of each tile (doubled off the diagonal blocks), broadcast to
+        // both halves (an op_sel of the packed multiply)
+        const f16x2 c0 = as_h2(X0 < Y0 ? qb2[tt][Y0][J0 >> 1] : qb[tt][Y0][J0 >> 1]);
+        const f16x2 c1 = as_h2(X1 < Y1 ? qb2[tt][Y1][J1 >> 1] : qb[tt][Y1][J1 >> 1]);
+        const f16x2 bb0 = (J0 & 1) ? __builtin_shufflevector(c0, c0, 1, 1) : __builtin_shufflevector(c0, c0, 0, 0);
+        const f16x2 bb1 = (J1 & 1) ? __builtin_shufflevector(c1, c1, 1, 1) : __builtin_shufflevector(c1, c1, 0, 0);
+        const uint32_t p0 = as_u(as_h2(qa[tt][X0].x) * bb0);
+        const uint32_t p1 = as_u(as_h2(qa[tt][X0].y) * bb0);
+        const uint32_t p2 = as_u(as_h2(qa[tt][X1].x) * bb1);
+        const uint32_t p3 = as_u(as_h2(qa[tt][X1].y) * bb1);
+        const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(p0, p1, p2, p3));
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          if (SL::rd_uses_x(HF, x)) qa[tt][x] = *reinterpret_cast<const uint2*>(qrow + 16 * x + 4 * q4);
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          if (SL::rd_uses_y(HF, y)) {
-            if constexpr (SL::kJ == 4) {
-              const uint2 w2 = *reinterpret_cast<const uint2*>(qrow + 16 * y + cx.j0);
-              qb[tt][y][0] = w2.x;
-              qb[tt][y][1] = w2.y;
-            } else {
-              qb[tt][y][0] = *reinterpret_cast<const uint32_t*>(qrow + 16 * y + cx.j0);
-            }
-          }
-        }
-      }
-      f32x4 acc[2][2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int pr = P0 + p;
-        f16x8 B[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) B[nt] = __builtin_bit_cast(f16x8, sh.hs[pr][nt][lane]);
-        const int u0 = 2 * pr, u1 = 2 * pr + 1;
-        const int X0 = SL::X(u0), X1 = SL::X(u1), Y0 = SL::Y(u0), Y1 = SL::Y(u1);
-        const int J0 = SL::jj(u0), J1 = SL::jj(u1);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          // q'_b of each tile, broadcast to both halves (an op_sel of the
-          // packed multiply)
-          const f16x2 c0 = as_h2(qb[tt][Y0][J0 >> 1]), c1 = as_h2(qb[tt][Y1][J1 >> 1]);
-          const f16x2 bb0 = (J0 & 1) ? __builtin_shufflevector(c0, c0, 1, 1) : __builtin_shufflevector(c0, c0, 0, 0);
-          const f16x2 bb1 = (J1 & 1) ? __builtin_shufflevector(c1, c1, 1, 1) : __builtin_shufflevector(c1, c1, 0, 0);
-          const uint32_t p0 = as_u(as_h2(qa[tt][X0].x) * bb0);
-          const uint32_t p1 = as_u(as_h2(qa[tt][X0].y) * bb0);
-          const uint32_t p2 = as_u(as_h2(qa[tt][X1].x) * bb1);
-          const uint32_t p3 = as_u(as_h2(qa[tt][X1].y) * bb1);
-          const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(p0, p1, p2, p3));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mfma_h(A, B[nt], acc[tt][nt]);
-        }
-      }
-      // hand the partner its token tile, keep the own one
-      f32x4* xs = &sh.xs[W][0][0];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        xs[nt * 64 + lane] = acc[1 - HF][nt];
-        keep[nt] = acc[HF][nt];
+        for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mfma_h(A, B[nt], acc[tt][nt]);
       }
     }
-    lds_barrier();  // (B2)
-    if (st + 1 < nsteps) {
-      stage_write<CS>(sh, pf, W, lane, buf ^ 1, g);
-      if (st + 2 < nsteps) pf = pre(st + 2);
+    // hand the partner its token tile, keep the own one
+    f32x4* xs = &sh.xs[buf][W][0][0];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      xs[nt * 64 + lane] = acc[1 - HF][nt];
+      keep[nt] = acc[HF][nt];
     }
-    if (active) flush(st, buf, pe);
-    lds_barrier();  // (B1)
+  };
+
+  // Staging: sub-chunk x's data is loaded at the start of step x - 1 and
+  // written to LDS at its end, after the wave's matrix work, so the loads are
+  // consumed in the step that issued them. Every readout wave runs the same
+  // exponent sequence; wave 0 publishes it with the query exponents.
+  const int r = 64 * W + lane;
+  ExpTrack g;
+  auto blk = [&](int x) { return cx.stage + ((size_t)cx.n * cx.NS + x) * Stage<CS>::kHalves; };
+  auto exps = [&](int x) { return cx.exps + ((size_t)cx.n * cx.NS + x) * Stage<CS>::kExps; };
+  // exponents of a loaded sub-chunk: advance G, post them to buffer buf,
+  // return the v factor
+  auto advance = [&](const StageLoad<CS>& L, int buf) {
+    const int ekr = __builtin_amdgcn_readfirstlane(L.ek);
+    const int ev = __builtin_amdgcn_readfirstlane(L.ev);
+    const bool contributes = ekr != kNoExp && ev != kNoExp;
+    if (contributes) g.add(2 * ekr + ev, CS);
+    const int ek = ekr == kNoExp ? 0 : ekr;
+    // v was staged times 2^-ev; the update needs it times 2^(2 ek - G)
+    const _Float16 f = contributes ? (_Float16)__builtin_ldexpf(1.0f, 2 * ek + ev - g.G) : (_Float16)0.0f;
+    if (W == 0) {
+      if (lane < CS) sh.qe[buf][lane] = L.eq;
+      if (lane == 0) {
+        sh.sc[buf][0] = ek;
+        sh.sc[buf][1] = g.G;
+      }
+    }
+    return f16x2{f, f};
+  };
+
+  // sub-chunk x is loaded during step x - 2 (into register set x & 1) and
+  // written to LDS at the end of step x - 1; loads past the last sub-chunk
+  // read the last one again (never written)
+  const int last = cx.NS - 1;
+  StageLoad<CS> La = load_stage<CS>(blk(0), exps(0), cx.ch, r);
+  StageLoad<CS> Lb = load_stage<CS>(blk(min(1, last)), exps(min(1, last)), cx.ch, r);
+  lds_barrier();  // (P1) imported state maxima posted
+  if (cx.H0) {
+    const float m = fmaxf(fmaxf(sh.umx[0], sh.umx[1]), fmaxf(sh.umx[2], sh.umx[3]));
+    if (m > 0.0f) g.start(m);
   }
+  write_stage(sh, La, r, 0, advance(La, 0));
+  La = load_stage<CS>(blk(min(2, last)), exps(min(2, last)), cx.ch, r);
+  lds_barrier();  // (P2)
+  lds_barrier();  // (P3)
+
+  // Ln: sub-chunk st + 1 (loaded a step ago) to write, then receives st + 3
+  auto step = [&](int st, StageLoad<CS>& Ln) {
+    const f32x4 kp0 = keep[0], kp1 = keep[1];
+    const float fp[4] = {fq[0], fq[1], fq[2], fq[3]};
+    if (active) compute(st);
+    if (st >= 1 && active) flush(st - 1, kp0, kp1, fp);
+    if (st + 1 < cx.NS) write_stage(sh, Ln, r, (st + 1) & 1, advance(Ln, (st + 1) & 1));
+    Ln = load_stage<CS>(blk(min(st + 3, last)), exps(min(st + 3, last)), cx.ch, r);
+    lds_barrier();  // (B)
+  };
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, Lb);
+    step(st + 1, La);
+  }
+  if (st < nsteps) step(st, Lb);
+  if (active) flush(nsteps - 1, keep[0], keep[1], fq);
 }
 
-// C: the chunk (intra-chunk region of the output); the state kernel stages it
-// in sub-chunks of CS tokens, all read out against the state at the chunk start.
+// ------------------------------------------------------------ staging kernel
+
+// One work-group per (sub-chunk of CS tokens, head): the scales and scaled
+// float16 values the state kernel reads (see Stage). Thread (t, qd) holds
+// dims 16 qd .. 16 qd + 15 of token t's q, k and v. Every element is
+// converted once here instead of once per work-group of its head.
+template <int CS>
+__global__ __launch_bounds__(4 * CS) void prefill_stage_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T,
+    uint16_t* __restrict__ stage, int* __restrict__ exps) {
+  constexpr int NW = 4 * CS / 64;
+  constexpr int RW = CS / 8;
+  __shared__ __align__(16) _Float16 tk[kDim][CS + kPad];
+  __shared__ __align__(16) _Float16 tv[kDim][CS + kPad];
+  __shared__ float red[2][NW];
+  const int x = blockIdx.x, n = blockIdx.y, NS = gridDim.x;
+  const int tid = threadIdx.x, t = tid >> 2, qd = tid & 3;
+  const int tok = x * CS + t;
+  const bool ok = tok < T;
+  const size_t row = ((size_t)n * T + min(tok, T - 1)) * kDim + 16 * qd;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  uint4 qv[2], kv[2], vv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    qv[h] = ok ? *reinterpret_cast<const uint4*>(q + row + 8 * h) : z;
+    kv[h] = ok ? *reinterpret_cast<const uint4*>(k + row + 8 * h) : z;
+    vv[h] = ok ? *reinterpret_cast<const uint4*>(v + row + 8 * h) : z;
+  }
+  // the token's largest |q| over the four threads holding it (adjacent lanes)
+  uint32_t qm = pair_max(__builtin_elementwise_max(absmax_pairs(qv[0]), absmax_pairs(qv[1])));
+  qm = max(qm, (uint32_t)__builtin_amdgcn_mov_dpp((int)qm, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  qm = max(qm, (uint32_t)__builtin_amdgcn_mov_dpp((int)qm, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  const int eqr = exp_above(bf16f(qm));
+  const int eq = eqr == kNoExp ? 0 : eqr;
+  // the sub-chunk's largest |k| and |v|
+  const float km = wave_max(bf16f(pair_max(__builtin_elementwise_max(absmax_pairs(kv[0]), absmax_pairs(kv[1])))));
+  const float vm = wave_max(bf16f(pair_max(__builtin_elementwise_max(absmax_pairs(vv[0]), absmax_pairs(vv[1])))));
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = km;
+    red[1][tid >> 6] = vm;
+  }
+  __syncthreads();
+  float kall = red[0][0], vall = red[1][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    kall = fmaxf(kall, red[0][w]);
+    vall = fmaxf(vall, red[1][w]);
+  }
+  const int ekr = exp_above(kall), evr = exp_above(vall);
+  const int ek = ekr == kNoExp ? 0 : ekr, ev = evr == kNoExp ? 0 : evr;
+  uint16_t* blk = stage + ((size_t)n * NS + x) * Stage<CS>::kHalves;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    *reinterpret_cast<uint4*>(blk + t * kDim + 16 * qd + 8 * h) = bf16x8_to_f16_scaled(qv[h], -eq);
+  // k and v columns, transposed through LDS
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 kh = bf16x8_to_f16_scaled(kv[h], -ek), vh = bf16x8_to_f16_scaled(vv[h], -ev);
+    const uint32_t kw[4] = {kh.x, kh.y, kh.z, kh.w}, vw[4] = {vh.x, vh.y, vh.z, vh.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * qd + 8 * h + 2 * e;
+      tk[d][t] = as_h2(kw[e])[0];
+      tk[d + 1][t] = as_h2(kw[e])[1];
+      tv[d][t] = as_h2(vw[e])[0];
+      tv[d + 1][t] = as_h2(vw[e])[1];
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < kDim * RW; c += 4 * CS) {
+    const int d = c / RW, j = c % RW;
+    *reinterpret_cast<uint4*>(blk + kDim * CS + d * CS + 8 * j) = *reinterpret_cast<const uint4*>(&tk[d][8 * j]);
+    *reinterpret_cast<uint4*>(blk + 2 * kDim * CS + d * CS + 8 * j) = *reinterpret_cast<const uint4*>(&tv[d][8 * j]);
+  }
+  int* e = exps + ((size_t)n * NS + x) * Stage<CS>::kExps;
+  if (qd == 0) *reinterpret_cast<int4*>(e + 4 * t) = make_int4(eq, ekr, evr, 0);
+}
+
+// C: the chunk (intra-chunk region of the output); the state kernel steps
+// through it in staged sub-chunks of CS tokens, all read out against the
+// state at the chunk start.
 template <int C, int SF, int G>
 __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int T,
     const float* __restrict__ H0, const float* __restrict__ s0, float* __restrict__ HT, float* __restrict__ sT,
-    float* __restrict__ part, float* __restrict__ Sg) {
+    float* __restrict__ part, float* __restrict__ Sg, const uint16_t* __restrict__ stage,
+    const int* __restrict__ exps) {
   constexpr int CS = C < kCS ? C : kCS;
   static_assert(C % CS == 0 && CS % 32 == 0, "chunk must be a multiple of the sub-chunk");
   __shared__ __align__(16) StateLds<SF, G> sh;
@@ -758,6 +934,9 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
   cx.sT = sT;
   cx.part = part;
   cx.Sg = Sg;
+  cx.stage = stage;
+  cx.exps = exps;
+  cx.NS = cx.NC * (C / CS);  // staged sub-chunks per head (whole chunks)
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wv) {
     case 0: update_wave<C, CS, SF, G, 0>(sh, cx); break;
@@ -988,21 +1167,46 @@ size_t gram_bytes(const PrefillArgs& a) {
   return align_up((size_t)a.N * nc * kDim * kDim * sizeof(float));
 }
 
+int sub_chunk(int chunk) { return chunk < kCS ? chunk : kCS; }
+
+// Staged sub-chunks per head: whole chunks (the state kernel steps through
+// every sub-chunk of the last, partial chunk; tokens past T stage as zeros).
+size_t staged_sub_chunks(const PrefillArgs& a) {
+  return (size_t)((a.T + a.chunk - 1) / a.chunk) * (a.chunk / sub_chunk(a.chunk));
+}
+
+size_t stage_bytes(const PrefillArgs& a) {
+  return align_up((size_t)a.N * staged_sub_chunks(a) * 3 * kDim * sub_chunk(a.chunk) * sizeof(uint16_t));
+}
+
+size_t exps_bytes(const PrefillArgs& a) {
+  return align_up((size_t)a.N * staged_sub_chunks(a) * 4 * sub_chunk(a.chunk) * sizeof(int));
+}
+
 template <int C, int SF, int G>
-void launch_state(const PrefillArgs& a, float* part, float* Sg, hipStream_t st) {
+void launch_state(const PrefillArgs& a, float* part, float* Sg, const uint16_t* stage, const int* exps,
+                  hipStream_t st) {
   hipLaunchKernelGGL((prefill_state_kernel<C, SF, G>), dim3(2 * SF * a.N), dim3(kThreads3), 0, st,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.N, a.T, a.H0, a.s0, a.HT, a.sT, part, Sg);
+                     static_cast<const uint16_t*>(a.v), a.N, a.T, a.H0, a.s0, a.HT, a.sT, part, Sg, stage, exps);
 }
 
 template <int C, int G>
 hipError_t launch_c(const PrefillArgs& a, void* ws, hipStream_t st) {
-  float* part = a.o ? static_cast<float*>(ws) : nullptr;
-  float* Sg = a.o ? reinterpret_cast<float*>(static_cast<char*>(ws) + part_bytes(a)) : nullptr;
+  constexpr int CS = C < kCS ? C : kCS;
+  char* p = static_cast<char*>(ws);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(p);
+  int* exps = reinterpret_cast<int*>(p + stage_bytes(a));
+  char* rest = p + stage_bytes(a) + exps_bytes(a);
+  float* part = a.o ? reinterpret_cast<float*>(rest) : nullptr;
+  float* Sg = a.o ? reinterpret_cast<float*>(rest + part_bytes(a)) : nullptr;
   const int SF = slices_for(a.N);
+  hipLaunchKernelGGL((prefill_stage_kernel<CS>), dim3((unsigned)staged_sub_chunks(a), a.N), dim3(4 * CS), 0, st,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), a.T, stage, exps);
   prof_begin(st);
-  if (SF == 8) launch_state<C, 8, G>(a, part, Sg, st);
-  else launch_state<C, 4, G>(a, part, Sg, st);
+  if (SF == 8) launch_state<C, 8, G>(a, part, Sg, stage, exps, st);
+  else launch_state<C, 4, G>(a, part, Sg, stage, exps, st);
   prof_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
@@ -1035,7 +1239,9 @@ bool prefill_mfma_supported(const PrefillArgs& a) {
          a.factor_kind == 0 && (a.factors == 1 || a.factors == 2 || a.factors == 4);
 }
 
-size_t prefill_mfma_workspace(const PrefillArgs& a) { return a.o ? part_bytes(a) + gram_bytes(a) : 0; }
+size_t prefill_mfma_workspace(const PrefillArgs& a) {
+  return stage_bytes(a) + exps_bytes(a) + (a.o ? part_bytes(a) + gram_bytes(a) : 0);
+}
 
 hipError_t prefill_mfma_launch(const PrefillArgs& a, void* ws, hipStream_t st) {
   switch (a.factors) {
