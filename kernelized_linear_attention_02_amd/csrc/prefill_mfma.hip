@@ -811,13 +811,14 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
   lds_barrier();  // (P3)
 
   // Ln: sub-chunk st + 1 (loaded a step ago) to write, then receives st + 3
+  // The matrix work comes last in the step, so that right after the barrier
+  // the update waves' operand reads are not queued behind this wave's reads
+  // of the published state.
   auto step = [&](int st, StageLoad<CS>& Ln) {
-    const f32x4 kp0 = keep[0], kp1 = keep[1];
-    const float fp[4] = {fq[0], fq[1], fq[2], fq[3]};
-    if (active) compute(st);
-    if (st >= 1 && active) flush(st - 1, kp0, kp1, fp);
+    if (st >= 1 && active) flush(st - 1, keep[0], keep[1], fq);
     if (st + 1 < cx.NS) write_stage(sh, Ln, r, (st + 1) & 1, advance(Ln, (st + 1) & 1));
     Ln = load_stage<CS>(blk(min(st + 3, last)), exps(min(st + 3, last)), cx.ch, r);
+    if (active) compute(st);
     lds_barrier();  // (B)
   };
   int st = 0;
@@ -938,6 +939,9 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
   cx.exps = exps;
   cx.NS = cx.NC * (C / CS);  // staged sub-chunks per head (whole chunks)
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the update waves carry the longer dependent chain of each step: let them
+  // issue first when both kinds of wave are ready on a SIMD
+  if (wv < kUW) __builtin_amdgcn_s_setprio(2);
   switch (wv) {
     case 0: update_wave<C, CS, SF, G, 0>(sh, cx); break;
     case 1: update_wave<C, CS, SF, G, 1>(sh, cx); break;
