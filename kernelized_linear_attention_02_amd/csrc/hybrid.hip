@@ -688,9 +688,12 @@ __device__ __forceinline__ void hyb_score_block(
 }
 
 // One launch for the two halves of a refresh step that wait on the same
-// work: the scoring of refresh r (work-groups 0 .. n_score - 1, decoded as
-// (head, candidate block, slice)) and the fold of refresh r - 1 (the rest,
-// decoded as (k-step block, head)). Either part may be empty.
+// work: the scoring of refresh r (work-groups 0 .. n_score - 1) and the fold
+// of refresh r - 1 (the rest, decoded as (k-step block, head)). Either part
+// may be empty. Per head the scoring has the correction slice of every
+// candidate block, then the state slices of blocks bnew0 .. n_cblk - 1: the
+// blocks before bnew0 hold only candidates whose sums over the state before
+// the previous fold the previous selection carried over.
 union RefreshShared {
   ScoreShared score;
   FoldLds fold;
@@ -698,7 +701,7 @@ union RefreshShared {
 
 __global__ __launch_bounds__(kThreads, 2) void hyb_refresh_kernel(
     // scoring of refresh r
-    int n_score, int n_cblk, const uint4* __restrict__ HFs, const uint16_t* __restrict__ k,
+    int n_score, int n_cblk, int bnew0, const uint4* __restrict__ HFs, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int T, const int32_t* __restrict__ cache, int cstride, int n_cache, int ev0,
     int n_cand, const int32_t* __restrict__ rej_prev, int rstride, int n_rej_prev, float* __restrict__ part,
     int pstride,
@@ -709,9 +712,11 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_refresh_kernel(
   const int bid = blockIdx.x;
   constexpr int Z = kSZ + 1;
   if (bid < n_score) {
-    const int bz = bid % Z;
-    const int by = (bid / Z) % n_cblk;
-    const int n = bid / (Z * n_cblk);
+    const int per_head = n_cblk + (n_cblk - bnew0) * kSZ;
+    const int n = bid / per_head;
+    const int i = bid % per_head;
+    const int by = i < n_cblk ? i : bnew0 + (i - n_cblk) / kSZ;
+    const int bz = i < n_cblk ? kSZ : (i - n_cblk) % kSZ;
     hyb_score_block(sh.score, n, by, bz, Z, HFs, k, v, T, cache, cstride, n_cache, ev0, n_cand, rej_prev, rstride,
                     n_rej_prev, kSZ, part, pstride);
   } else {
@@ -1258,13 +1263,18 @@ constexpr int kCandMax = 256;  // candidates per refresh, at most (cache + evict
 // tokens with a lower id) and the rest, in rank order, to the rejected list.
 // The result is the one the sort of the generic form gives. The new cache goes
 // to cache_out (not the cache it reads).
+// Candidates c < n_carry take their sums over the state before the previous
+// fold from carry_in[c] (the previous selection's totals) instead of the
+// state slices, plus the correction slice Z - 1; every kept candidate's
+// totals go to carry_out at its new cache position.
 constexpr int kSelThreads = 1024;
 __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
     const float* __restrict__ part, int Z, int pstride, const uint16_t* __restrict__ v, int T,
     float eps, const int32_t* __restrict__ cache, int cstride, int32_t* __restrict__ cache_out,
     int ostride, int n_cache, int ev0, int n_cand, int keep,
     int32_t* __restrict__ rejected, int rstride, int32_t* __restrict__ trace, size_t trace_row_stride,
-    int block, int nblocks, float* __restrict__ scores, int sstride) {
+    int block, int nblocks, float* __restrict__ scores, int sstride, const float* __restrict__ carry_in,
+    int n_carry, float* __restrict__ carry_out) {
   static_assert(kSelThreads == 4 * kCandMax, "four threads per candidate");
   __shared__ uint64_t keys[kCandMax];
   __shared__ int32_t tok[kCandMax];
@@ -1280,14 +1290,12 @@ __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
   if (qd == 0 && live) tok[c] = cand_token(cn, n_cache, ev0, c);
   __syncthreads();
   float err = 0.0f;
-  if (live) {
-    float num[16];
+  float num[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) num[j] = 0.0f;
-    float den = 0.0f;
-#pragma unroll 5
-    for (int z = 0; z < Z; ++z) {
-      const float* pc = part + (((size_t)n * Z + z) * pstride + c) * 68;
+  for (int j = 0; j < 16; ++j) num[j] = 0.0f;
+  float dsum = 0.0f;
+  if (live) {
+    auto add = [&](const float* pc) {
       const float4* p4 = reinterpret_cast<const float4*>(pc + 16 * qd);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1297,9 +1305,16 @@ __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
         num[4 * j + 2] += x.z;
         num[4 * j + 3] += x.w;
       }
-      den += pc[64];
+      dsum += pc[64];
+    };
+    if (c < n_carry) {
+      add(carry_in + ((size_t)n * pstride + c) * 68);
+      add(part + (((size_t)n * Z + Z - 1) * pstride + c) * 68);
+    } else {
+#pragma unroll 5
+      for (int z = 0; z < Z; ++z) add(part + (((size_t)n * Z + z) * pstride + c) * 68);
     }
-    den += eps;
+    const float den = dsum + eps;
     const uint4* vp = reinterpret_cast<const uint4*>(v + ((size_t)n * T + tok[c]) * kFD + 16 * qd);
     const uint4 va = vp[0], vb = vp[1];
     const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
@@ -1337,6 +1352,14 @@ __global__ __launch_bounds__(kSelThreads) void hyb_select_part_kernel(
   }
   pos += __shfl_xor(pos, 1, 64);
   pos += __shfl_xor(pos, 2, 64);
+  if (carry_out && live && rank < keep) {
+    float* co = carry_out + ((size_t)n * pstride + pos) * 68;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(co + 16 * qd + 4 * j) =
+          make_float4(num[4 * j], num[4 * j + 1], num[4 * j + 2], num[4 * j + 3]);
+    if (qd == 0) co[64] = dsum;
+  }
   if (qd == 0 && live) {
     const int32_t id = tok[c];
     if (rank >= keep) {
@@ -1360,6 +1383,7 @@ struct Ws {
   uint4* HF[3];  // state fragments, three versions (matrix-core path only)
   float* xp;  // readout split partials [N][refresh][kRNS][66] (matrix-core path only)
   float* sp;  // score split partials [N][kSZ + 1][kCStride][68] (matrix-core path only)
+  float* carry[2];  // carried candidate sums [N][kCStride][68], by refresh parity (matrix-core path only)
 };
 
 bool matrix_path(const HybridArgs& a) { return a.dqk == 64 && a.dv == 64 && a.in_bf16; }
@@ -1370,6 +1394,10 @@ size_t xp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * a.refresh *
 constexpr int kCStride = kCandMax;
 // plus one slice for the pairs the previous refresh folded
 size_t sp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * (kSZ + 1) * kCStride * 68 * sizeof(float)); }
+size_t carry_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kCStride * 68 * sizeof(float)); }
+// every kRescore-th refresh scores every candidate against the state again,
+// which bounds the rounding the carried sums gather
+constexpr int kRescore = 8;
 
 Ws carve(const HybridArgs& a, void* ws) {
   const int D = phi_dim(a.dqk);
@@ -1413,6 +1441,13 @@ Ws carve(const HybridArgs& a, void* ws) {
   w.xp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
   if (w.xp) p += xp_bytes(a);
   w.sp = matrix_path(a) ? reinterpret_cast<float*>(p) : nullptr;
+  w.carry[0] = w.carry[1] = nullptr;
+  if (w.sp) {
+    p += sp_bytes(a);
+    w.carry[0] = reinterpret_cast<float*>(p);
+    p += carry_bytes(a);
+    w.carry[1] = reinterpret_cast<float*>(p);
+  }
   return w;
 }
 
@@ -1622,14 +1657,18 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, hipStre
         const int x_new = r % 3;          // slot of refresh r
         const int x_cur = (r + 2) % 3;    // slot of refresh r - 1 (2 before the first)
         const int x_old = (r + 1) % 3;    // slot of refresh r - 2 (the zero state for r < 2)
-        // scoring r (state r - 2 + pairs of r - 1) and fold r - 1 in one launch
+        // scoring r (state r - 2 + pairs of r - 1) and fold r - 1 in one launch;
+        // the cached candidates' sums over state r - 2 carry over from
+        // selection r - 1, except at a full re-scoring
         KLA_TRY(slots_free(x_new));
         const int n_cblk = (n_cand + kScoreCand - 1) / kScoreCand;
-        const int n_score = N * n_cblk * (kSZ + 1);
+        const int n_carry = r % kRescore == 0 ? 0 : n_cache;
+        const int bnew0 = n_carry / kScoreCand;
+        const int n_score = N * (n_cblk + (n_cblk - bnew0) * kSZ);
         const int n_fold = r >= 1 ? N * kFoldWGs : 0;
         if (prof) prof_begin(st);
         hipLaunchKernelGGL(hyb_refresh_kernel, dim3(n_score + n_fold), dim3(kThreads), 0, st, n_score, n_cblk,
-                           w.HF[x_old], k, v, a.T, cache[x_cur], kCStride, n_cache, f_prev, n_cand,
+                           bnew0, w.HF[x_old], k, v, a.T, cache[x_cur], kCStride, n_cache, f_prev, n_cand,
                            rej[(r + 1) & 1], kCStride, r >= 1 ? n_rej_prev : 0, w.sp, kCStride, w.H, w.s,
                            w.HF[x_cur], rej[(r + 1) & 1], n_rej_prev);
         KLA_CHECK();
@@ -1638,7 +1677,7 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, hipStre
         hipLaunchKernelGGL(hyb_select_part_kernel, dim3(N), dim3(kSelThreads), 0, st, w.sp, kSZ + 1, kCStride, v,
                            a.T, a.eps, cache[x_cur], kCStride, cache[x_new], kCStride, n_cache, f_prev, n_cand,
                            a.cache_size, rej[r & 1], kCStride, a.trace, (size_t)a.cache_size, b, nblocks,
-                           w.scores, kCStride);
+                           w.scores, kCStride, w.carry[(r + 1) & 1], n_carry, w.carry[r & 1]);
         if (prof) prof_end(st);
         KLA_CHECK();
         n_cache = a.cache_size;
@@ -1663,7 +1702,7 @@ hipError_t enqueue_matrix(const HybridArgs& a, void* ws, hipStream_t st, hipStre
     // the fold of the last refresh alone, then the remaining readouts
     if (r >= 1) {
       KLA_TRY(slots_free(r % 3));
-      hipLaunchKernelGGL(hyb_refresh_kernel, dim3(N * kFoldWGs), dim3(kThreads), 0, st, 0, 1, w.HF[0], k, v, a.T,
+      hipLaunchKernelGGL(hyb_refresh_kernel, dim3(N * kFoldWGs), dim3(kThreads), 0, st, 0, 1, 0, w.HF[0], k, v, a.T,
                          cache[slot], kCStride, 0, 0, 0, rej[(r + 1) & 1], kCStride, 0, w.sp, kCStride, w.H, w.s,
                          w.HF[slot], rej[(r + 1) & 1], n_rej_prev);
       KLA_CHECK();
@@ -1712,7 +1751,8 @@ size_t hybrid_workspace(const HybridArgs& a) {
   b += align_up((size_t)a.N * kCStride * sizeof(float));
   b += align_up((size_t)a.N * kCStride * sizeof(int32_t));
   if (matrix_path(a))
-    b += 3 * align_up((size_t)a.N * kCStride * sizeof(int32_t)) + 3 * hf_bytes(a) + xp_bytes(a) + sp_bytes(a);
+    b += 3 * align_up((size_t)a.N * kCStride * sizeof(int32_t)) + 3 * hf_bytes(a) + xp_bytes(a) + sp_bytes(a) +
+         2 * carry_bytes(a);
   return b;
 }
 
