@@ -832,80 +832,110 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
 
 // ------------------------------------------------------------ staging kernel
 
-// One work-group per (sub-chunk of CS tokens, head): the scales and scaled
-// float16 values the state kernel reads (see Stage). Thread (t, qd) holds
-// dims 16 qd .. 16 qd + 15 of token t's q, k and v. Every element is
-// converted once here instead of once per work-group of its head.
+// Work-group (g, head) handles sub-chunks g R .. g R + R - 1 of CS tokens:
+// the scales and scaled float16 values the state kernel reads (see Stage).
+// Thread (t, qd) holds dims 16 qd .. 16 qd + 15 of token t's q, k and v; the
+// next sub-chunk's rows are loaded while the current one is converted and
+// written, so reads and writes overlap. Every element is converted once
+// here instead of once per work-group of its head.
+constexpr int kStageR = 4;  // sub-chunks per staging work-group
+
 template <int CS>
 __global__ __launch_bounds__(4 * CS) void prefill_stage_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T,
-    uint16_t* __restrict__ stage, int* __restrict__ exps) {
+    int NS, uint16_t* __restrict__ stage, int* __restrict__ exps) {
   constexpr int NW = 4 * CS / 64;
   constexpr int RW = CS / 8;
   __shared__ __align__(16) _Float16 tk[kDim][CS + kPad];
   __shared__ __align__(16) _Float16 tv[kDim][CS + kPad];
-  __shared__ float red[2][NW];
-  const int x = blockIdx.x, n = blockIdx.y, NS = gridDim.x;
+  __shared__ float red[2][2][NW];
+  const int n = blockIdx.y;
+  const int x0 = blockIdx.x * kStageR;
+  const int x1 = min(x0 + kStageR, NS);
   const int tid = threadIdx.x, t = tid >> 2, qd = tid & 3;
-  const int tok = x * CS + t;
-  const bool ok = tok < T;
-  const size_t row = ((size_t)n * T + min(tok, T - 1)) * kDim + 16 * qd;
   const uint4 z = make_uint4(0, 0, 0, 0);
-  uint4 qv[2], kv[2], vv[2];
+  struct Rows {
+    uint4 q[2], k[2], v[2];
+  };
+  // rows past the end read the last row (unconditional loads) and are zeroed
+  // when used
+  auto load = [&](int x, Rows& R) {
+    const size_t row = ((size_t)n * T + min(x * CS + t, T - 1)) * kDim + 16 * qd;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    qv[h] = ok ? *reinterpret_cast<const uint4*>(q + row + 8 * h) : z;
-    kv[h] = ok ? *reinterpret_cast<const uint4*>(k + row + 8 * h) : z;
-    vv[h] = ok ? *reinterpret_cast<const uint4*>(v + row + 8 * h) : z;
-  }
-  // the token's largest |q| over the four threads holding it (adjacent lanes)
-  uint32_t qm = pair_max(__builtin_elementwise_max(absmax_pairs(qv[0]), absmax_pairs(qv[1])));
-  qm = max(qm, (uint32_t)__builtin_amdgcn_mov_dpp((int)qm, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-  qm = max(qm, (uint32_t)__builtin_amdgcn_mov_dpp((int)qm, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  const int eqr = exp_above(bf16f(qm));
-  const int eq = eqr == kNoExp ? 0 : eqr;
-  // the sub-chunk's largest |k| and |v|
-  const float km = wave_max(bf16f(pair_max(__builtin_elementwise_max(absmax_pairs(kv[0]), absmax_pairs(kv[1])))));
-  const float vm = wave_max(bf16f(pair_max(__builtin_elementwise_max(absmax_pairs(vv[0]), absmax_pairs(vv[1])))));
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = km;
-    red[1][tid >> 6] = vm;
-  }
-  __syncthreads();
-  float kall = red[0][0], vall = red[1][0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    kall = fmaxf(kall, red[0][w]);
-    vall = fmaxf(vall, red[1][w]);
-  }
-  const int ekr = exp_above(kall), evr = exp_above(vall);
-  const int ek = ekr == kNoExp ? 0 : ekr, ev = evr == kNoExp ? 0 : evr;
-  uint16_t* blk = stage + ((size_t)n * NS + x) * Stage<CS>::kHalves;
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    *reinterpret_cast<uint4*>(blk + t * kDim + 16 * qd + 8 * h) = bf16x8_to_f16_scaled(qv[h], -eq);
-  // k and v columns, transposed through LDS
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint4 kh = bf16x8_to_f16_scaled(kv[h], -ek), vh = bf16x8_to_f16_scaled(vv[h], -ev);
-    const uint32_t kw[4] = {kh.x, kh.y, kh.z, kh.w}, vw[4] = {vh.x, vh.y, vh.z, vh.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = 16 * qd + 8 * h + 2 * e;
-      tk[d][t] = as_h2(kw[e])[0];
-      tk[d + 1][t] = as_h2(kw[e])[1];
-      tv[d][t] = as_h2(vw[e])[0];
-      tv[d + 1][t] = as_h2(vw[e])[1];
+    for (int h = 0; h < 2; ++h) {
+      R.q[h] = *reinterpret_cast<const uint4*>(q + row + 8 * h);
+      R.k[h] = *reinterpret_cast<const uint4*>(k + row + 8 * h);
+      R.v[h] = *reinterpret_cast<const uint4*>(v + row + 8 * h);
     }
+  };
+  // sub-chunk x from `cur`; the next one is loaded into `nxt` first
+  auto body = [&](int x, Rows& cur, Rows& nxt) {
+    const int par = (x - x0) & 1;  // the reduction slots alternate
+    load(min(x + 1, x1 - 1), nxt);
+    if (x * CS + t >= T) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) cur.q[h] = cur.k[h] = cur.v[h] = z;
+    }
+    // the token's largest |q| over the four threads holding it (adjacent lanes)
+    uint32_t qm = pair_max(__builtin_elementwise_max(absmax_pairs(cur.q[0]), absmax_pairs(cur.q[1])));
+    qm = max(qm, (uint32_t)__builtin_amdgcn_mov_dpp((int)qm, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    qm = max(qm, (uint32_t)__builtin_amdgcn_mov_dpp((int)qm, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    const int eqr = exp_above(bf16f(qm));
+    const int eq = eqr == kNoExp ? 0 : eqr;
+    // the sub-chunk's largest |k| and |v|
+    const float km =
+        wave_max(bf16f(pair_max(__builtin_elementwise_max(absmax_pairs(cur.k[0]), absmax_pairs(cur.k[1])))));
+    const float vm =
+        wave_max(bf16f(pair_max(__builtin_elementwise_max(absmax_pairs(cur.v[0]), absmax_pairs(cur.v[1])))));
+    if ((tid & 63) == 0) {
+      red[par][0][tid >> 6] = km;
+      red[par][1][tid >> 6] = vm;
+    }
+    __syncthreads();  // maxima posted; the previous sub-chunk's transposes read
+    float kall = red[par][0][0], vall = red[par][1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      kall = fmaxf(kall, red[par][0][w]);
+      vall = fmaxf(vall, red[par][1][w]);
+    }
+    const int ekr = exp_above(kall), evr = exp_above(vall);
+    const int ek = ekr == kNoExp ? 0 : ekr, ev = evr == kNoExp ? 0 : evr;
+    uint16_t* blk = stage + ((size_t)n * NS + x) * Stage<CS>::kHalves;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<uint4*>(blk + t * kDim + 16 * qd + 8 * h) = bf16x8_to_f16_scaled(cur.q[h], -eq);
+    // k and v columns, transposed through LDS
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 kh = bf16x8_to_f16_scaled(cur.k[h], -ek), vh = bf16x8_to_f16_scaled(cur.v[h], -ev);
+      const uint32_t kw[4] = {kh.x, kh.y, kh.z, kh.w}, vw[4] = {vh.x, vh.y, vh.z, vh.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * qd + 8 * h + 2 * e;
+        tk[d][t] = as_h2(kw[e])[0];
+        tk[d + 1][t] = as_h2(kw[e])[1];
+        tv[d][t] = as_h2(vw[e])[0];
+        tv[d + 1][t] = as_h2(vw[e])[1];
+      }
+    }
+    int* e = exps + ((size_t)n * NS + x) * Stage<CS>::kExps;
+    if (qd == 0) *reinterpret_cast<int4*>(e + 4 * t) = make_int4(eq, ekr, evr, 0);
+    __syncthreads();  // transposes written
+    for (int c = tid; c < kDim * RW; c += 4 * CS) {
+      const int d = c / RW, j = c % RW;
+      *reinterpret_cast<uint4*>(blk + kDim * CS + d * CS + 8 * j) = *reinterpret_cast<const uint4*>(&tk[d][8 * j]);
+      *reinterpret_cast<uint4*>(blk + 2 * kDim * CS + d * CS + 8 * j) =
+          *reinterpret_cast<const uint4*>(&tv[d][8 * j]);
+    }
+  };
+  Rows A, B;
+  load(x0, A);
+  int x = x0;
+  for (; x + 1 < x1; x += 2) {
+    body(x, A, B);
+    body(x + 1, B, A);
   }
-  __syncthreads();
-  for (int c = tid; c < kDim * RW; c += 4 * CS) {
-    const int d = c / RW, j = c % RW;
-    *reinterpret_cast<uint4*>(blk + kDim * CS + d * CS + 8 * j) = *reinterpret_cast<const uint4*>(&tk[d][8 * j]);
-    *reinterpret_cast<uint4*>(blk + 2 * kDim * CS + d * CS + 8 * j) = *reinterpret_cast<const uint4*>(&tv[d][8 * j]);
-  }
-  int* e = exps + ((size_t)n * NS + x) * Stage<CS>::kExps;
-  if (qd == 0) *reinterpret_cast<int4*>(e + 4 * t) = make_int4(eq, ekr, evr, 0);
+  if (x < x1) body(x, A, B);
 }
 
 // C: the chunk (intra-chunk region of the output); the state kernel steps
@@ -1205,9 +1235,10 @@ hipError_t launch_c(const PrefillArgs& a, void* ws, hipStream_t st) {
   float* part = a.o ? reinterpret_cast<float*>(rest) : nullptr;
   float* Sg = a.o ? reinterpret_cast<float*>(rest + part_bytes(a)) : nullptr;
   const int SF = slices_for(a.N);
-  hipLaunchKernelGGL((prefill_stage_kernel<CS>), dim3((unsigned)staged_sub_chunks(a), a.N), dim3(4 * CS), 0, st,
+  const int ns = (int)staged_sub_chunks(a);
+  hipLaunchKernelGGL((prefill_stage_kernel<CS>), dim3((ns + kStageR - 1) / kStageR, a.N), dim3(4 * CS), 0, st,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.T, stage, exps);
+                     static_cast<const uint16_t*>(a.v), a.T, ns, stage, exps);
   prof_begin(st);
   if (SF == 8) launch_state<C, 8, G>(a, part, Sg, stage, exps, st);
   else launch_state<C, 4, G>(a, part, Sg, stage, exps, st);
