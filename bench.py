@@ -125,9 +125,10 @@ def timed_calls(torch, K, fn, steps, warmup):
     return (t1 - t0) * 1e3 / steps, (kms / nk if nk else float("nan")), nk / steps
 
 
-def bench_prefill(torch, K, S, name, steps, warmup, factors=1):
-    """kla_prefill on a configuration (factors > 1: the concatenated
-    multi-factor lift KATA-Mg through kla_prefill_factors)."""
+def bench_prefill(torch, K, S, name, steps, warmup, factors=1, factor_kind="concat"):
+    """kla_prefill on a configuration (factors > 1: a multi-factor lift
+    through kla_prefill_factors, the concatenated KATA-Mg on the matrix path
+    or the summed KATA-Sigma-g on the float32 vector path)."""
     cfg = S.CONFIGS[name]
     c = S.prefill_case(name, cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
                        cfg["seed"])
@@ -135,23 +136,26 @@ def bench_prefill(torch, K, S, name, steps, warmup, factors=1):
     del c
     o = torch.empty_like(v)
     step_ms, kern_ms, per_step = timed_calls(
-        torch, K, lambda: K.prefill(q, k, v, chunk=cfg["chunk"], out=o, factors=factors), steps, warmup)
+        torch, K, lambda: K.prefill(q, k, v, chunk=cfg["chunk"], out=o, factors=factors, factor_kind=factor_kind),
+        steps, warmup)
     B, H, T, d, dv = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
-    D = phi_dim(d) if factors == 1 else K.factor_phi_dim(d, factors)
+    D = phi_dim(d) if factors == 1 else K.factor_phi_dim(d, factors, factor_kind)
     head_tokens = B * H * T
     # dominant kernel: cross-chunk readout phi(Q)[H|s] and update phi(K)^T[V|1]
     kern_flops = 4.0 * D * (dv + 1) * head_tokens
     # whole call: plus the causal intra-chunk term
     C = cfg["chunk"]
     call_flops = kern_flops + (C + 1) * (d + dv + 1) * head_tokens
-    mfma = K.prefill_uses_matrix_cores()
+    mfma = K.prefill_uses_matrix_cores() and (factors == 1 or factor_kind == "concat")
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_F32_VALU_TFLOPS
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
     traffic = None
     if mfma and factors == 1:
         traffic = measured_traffic("prefill_mfma.hip", f"prefill_state_kernel_{name}_traffic.md")
     return dict(
-        workload=name + ("" if factors == 1 else f" (KATA-M{factors}, chunked state form, D = {D})"),
+        workload=name + ("" if factors == 1 else
+                         f" (KATA-{'M' if factor_kind == 'concat' else 'Sigma-'}{factors}, chunked state form, "
+                         f"D = {D}{'' if mfma else ', float32 vector path'})"),
         B=B, H=H, T=T, d_qk=d, d_v=dv, chunk=C, step_ms=step_ms,
         tokens_per_s=B * T / (step_ms * 1e-3), head_tokens_per_s=head_tokens / (step_ms * 1e-3),
         call_tflops=call_flops / (step_ms * 1e-3) / 1e12,
@@ -519,6 +523,7 @@ def main():
     ap.add_argument("--only", choices=["tiny_f32", "prefill_1x16x65536", "prefill_4x8x4096_quadratic",
                                        "prefill_4x8x4096_m2", "prefill_4x8x4096_sigma2",
                                        "prefill_4x8x4096_m2_state", "prefill_1x16x65536_m2_state",
+                                       "prefill_4x8x4096_sigma2_state",
                                        "prefill_4x8x4096_backward", "decode_sre_4096x128",
                                        "hybrid_2x16x16384", "hybrid_decode_4096"],
                     help="run just this secondary workload and print its line (for profiling)")
@@ -556,6 +561,8 @@ def main():
             r = bench_prefill(torch, K, S, args.only, args.steps, args.warmup)
         elif args.only == "prefill_4x8x4096_quadratic":
             r = bench_prefill_quadratic(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
+        elif args.only == "prefill_4x8x4096_sigma2_state":
+            r = bench_prefill(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup, factors=2, factor_kind="sum")
         elif args.only.endswith("_m2_state"):
             r = bench_prefill(torch, K, S, args.only[:-len("_m2_state")], args.steps, args.warmup, factors=2)
         elif args.only in ("prefill_4x8x4096_m2", "prefill_4x8x4096_sigma2"):
@@ -594,6 +601,8 @@ def main():
         secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup))
         log("[bench] secondary: prefill_4x8x4096 with the KATA-M2 lift (chunked state form)")
         secondary.append(bench_prefill(torch, K, S, name, args.steps, args.warmup, factors=2))
+        log("[bench] secondary: prefill_4x8x4096 with the KATA-Sigma-2 lift (chunked state form)")
+        secondary.append(bench_prefill(torch, K, S, name, max(2, args.steps // 10), 1, factors=2, factor_kind="sum"))
         log("[bench] secondary: prefill_1x16x65536 with the KATA-M2 lift (chunked state form)")
         secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1, factors=2))
         for g, kind in ((2, "concat"), (2, "sum")):

@@ -79,7 +79,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 5
+#define KLA_ABI_VERSION 6
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -135,30 +135,40 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
 #define KLA_FACTORS_SUM 1
 
 /* ------------------------------------------------------------------------
- * kla_prefill_factors - kla_prefill with the concatenated multi-factor lift
- * (KATA §2.3, "Variantes": KATA-Mg; the factors read as g equal slices of the
- * d_qk dimensions, see kla_prefill_quadratic_factors below). The state holds
- * only the features inside each factor:
- *   D_g = g p (p + 1) / 2 features, p = d_qk / g  (2080, 1056, 544 for
- *   d_qk = 64 and g = 1, 2, 4),
- * laid out factor by factor, each block in the vec_sym order of kla_prefill
- * (upper triangle row-major, sqrt(2) off the diagonal) over its p dimensions;
- * H0/s0/H_T/s_T are [N, D_g, d_v] and [N, D_g] float32. The outputs are those
- * of kla_prefill_quadratic_factors with KLA_FACTORS_CONCAT.
+ * kla_prefill_factors - kla_prefill with a multi-factor lift (KATA §2.3,
+ * "Variantes"; the factors read as g equal slices of p = d_qk / g of the
+ * d_qk dimensions, see kla_prefill_quadratic_factors below):
+ *   KLA_FACTORS_CONCAT (KATA-Mg): the factors' rank-one lifts concatenated,
+ *     D_g = g p (p + 1) / 2 features (2080, 1056, 544 for d_qk = 64 and
+ *     g = 1, 2, 4), laid out factor by factor, each block in the vec_sym
+ *     order of kla_prefill (upper triangle row-major, sqrt(2) off the
+ *     diagonal) over its p dimensions. bf16 inputs with d_qk = d_v = 64 run
+ *     on the matrix path, the rest on the float32 vector path (1e-4).
+ *   KLA_FACTORS_SUM (KATA-Sigma-g): the lift of sum_i x_i x_i^T,
+ *     D = p (p + 1) / 2 features (2080, 528, 136), in the vec_sym order over
+ *     p dimensions, feature (a, b) = sum_i x_i,a x_i,b (times sqrt(2) for
+ *     a < b); every shape runs on the float32 vector path (float32
+ *     arithmetic, 1e-4 relative; bf16 inputs are read exactly).
+ * H0/s0/H_T/s_T are [N, D, d_v] and [N, D] float32 in that layout. The
+ * outputs are those of kla_prefill_quadratic_factors with the same kind.
  *
- *   kind    : KLA_FACTORS_CONCAT (KLA_FACTORS_SUM returns
- *             KLA_ERR_UNSUPPORTED: the summed lift is served by the quadratic
- *             form only).
- *   factors : 1, 2 or 4 (1 is kla_prefill).
- *   other arguments and the workspace: as for kla_prefill
- *             (kla_prefill_workspace_size of the same shape and chunk).
- * Every shape kla_prefill supports: bf16 inputs with d_qk = d_v = 64 run on
- * the matrix path, the rest on the float32 vector path (1e-4 relative).
+ *   kind    : KLA_FACTORS_CONCAT or KLA_FACTORS_SUM.
+ *   factors : 1, 2 or 4 (1 is kla_prefill, for either kind).
+ *   ws      : at least kla_prefill_factors_workspace_size(shp, chunk, kind,
+ *             factors, o != NULL) bytes (for KLA_FACTORS_CONCAT,
+ *             kla_prefill_workspace_size of the same shape and chunk is
+ *             enough too).
+ *   other arguments: as for kla_prefill.
+ * Every shape kla_prefill supports.
  * ------------------------------------------------------------------------ */
 KLA_API kla_status_t kla_prefill_factors(const kla_shape_t* shp, int chunk, int kind, int factors,
                                          const void* q, const void* k, const void* v, void* o,
                                          const float* H0, const float* s0, float* H_T, float* s_T,
                                          void* ws, size_t ws_bytes, kla_stream_t stream);
+/* Workspace bytes of kla_prefill_factors for this shape, chunk, kind and
+ * number of factors, with (with_output != 0) or without outputs. */
+KLA_API kla_status_t kla_prefill_factors_workspace_size(const kla_shape_t* shp, int chunk, int kind,
+                                                        int factors, int with_output, size_t* bytes);
 
 /* ------------------------------------------------------------------------
  * kla_prefill_quadratic - the same causal outputs in the quadratic form

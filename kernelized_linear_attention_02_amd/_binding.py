@@ -22,7 +22,7 @@ KLA_FACTORS_CONCAT, KLA_FACTORS_SUM = 0, 1
 EXPORTS = (
     "kla_abi_version", "kla_phi_dim", "kla_status_string", "kla_last_error",
     "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill", "kla_prefill_quadratic",
-    "kla_prefill_quadratic_factors", "kla_prefill_factors", "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
+    "kla_prefill_quadratic_factors", "kla_prefill_factors", "kla_prefill_factors_workspace_size", "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
     "kla_decode_workspace_size", "kla_decode_step",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill", "kla_hybrid_prefill_streams",
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH):
         "kla_prefill_quadratic": (i, [shp, vp, vp, vp, vp, vp, vp]),
         "kla_prefill_quadratic_factors": (i, [shp, i, i, vp, vp, vp, vp, vp, vp]),
         "kla_prefill_factors": (i, [shp, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kla_prefill_factors_workspace_size": (i, [shp, i, i, i, i, szp]),
         "kla_prefill_quadratic_backward_workspace_size": (i, [shp, szp]),
         "kla_prefill_quadratic_backward": (i, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
@@ -190,13 +191,14 @@ def prefill_uses_matrix_cores(B=4, H=8, T=4096, d_qk=64, d_v=64, chunk=64, dtype
 
 
 def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, eps: float = 0.0,
-            out_dtype=None, outputs: bool = True, out=None, factors: int = 1):
+            out_dtype=None, outputs: bool = True, out=None, factors: int = 1, factor_kind: str = "concat"):
     """Chunked causal prefill. q, k [B, H, T, d_qk]; v [B, H, T, d_v] (float32 or
     bfloat16, same dtype). ``state`` = (H0, s0) float32 resumes a previous call.
     Returns o, or (o, H_T, s_T) with ``return_state``; with ``outputs=False``
-    only (H_T, s_T). ``factors`` > 1 selects the concatenated multi-factor
-    lift KATA-Mg (kla_prefill_factors; any supported shape), whose state has
-    factor_phi_dim(d_qk, factors) features."""
+    only (H_T, s_T). ``factors`` > 1 selects a multi-factor lift
+    (kla_prefill_factors; any supported shape): ``factor_kind`` "concat"
+    (KATA-Mg) or "sum" (KATA-Sigma-g), whose state has
+    factor_phi_dim(d_qk, factors, factor_kind) features."""
     torch = _torch()
     lib = load_library()
     _need_device(q, k, v)
@@ -210,7 +212,9 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
     code = _dtype_code(q)
     ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
     shp = Shape(B, Hh, T, dqk, dv, code, ocode, float(eps))
-    D = phi_dim(dqk) if factors == 1 else factor_phi_dim(dqk, factors)
+    if factor_kind not in FACTOR_KINDS:
+        raise ValueError(f"factor_kind must be one of {tuple(FACTOR_KINDS)}")
+    D = phi_dim(dqk) if factors == 1 else factor_phi_dim(dqk, factors, factor_kind)
     dev = q.device
     if outputs and out is not None:
         if out.shape != (B, Hh, T, dv) or out.dtype != _torch_dtype(ocode) or not out.is_contiguous():
@@ -230,14 +234,18 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
         if H0.numel() != B * Hh * D * dv or s0.numel() != B * Hh * D:
             raise ValueError("state shape does not match [B, H, D, d_v], [B, H, D]")
     nbytes = ctypes.c_size_t(0)
-    check(lib.kla_prefill_workspace_size(ctypes.byref(shp), int(chunk), int(outputs), ctypes.byref(nbytes)))
+    if factors == 1:
+        check(lib.kla_prefill_workspace_size(ctypes.byref(shp), int(chunk), int(outputs), ctypes.byref(nbytes)))
+    else:
+        check(lib.kla_prefill_factors_workspace_size(ctypes.byref(shp), int(chunk), FACTOR_KINDS[factor_kind],
+                                                     int(factors), int(outputs), ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
     if factors == 1:
         check(lib.kla_prefill(ctypes.byref(shp), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                               _ptr(H0), _ptr(s0), _ptr(HT), _ptr(sT), _ptr(ws), nbytes.value,
                               _stream(dev)))
     else:
-        check(lib.kla_prefill_factors(ctypes.byref(shp), int(chunk), KLA_FACTORS_CONCAT, int(factors),
+        check(lib.kla_prefill_factors(ctypes.byref(shp), int(chunk), FACTOR_KINDS[factor_kind], int(factors),
                                       _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(H0), _ptr(s0), _ptr(HT),
                                       _ptr(sT), _ptr(ws), nbytes.value, _stream(dev)))
     if not outputs:
@@ -248,10 +256,11 @@ def prefill(q, k, v, chunk: int = 64, state=None, return_state: bool = False, ep
 FACTOR_KINDS = {"concat": 0, "sum": 1}
 
 
-def factor_phi_dim(d: int, factors: int) -> int:
-    """State features of the concatenated multi-factor lift: g p(p+1)/2, p = d / g."""
+def factor_phi_dim(d: int, factors: int, kind: str = "concat") -> int:
+    """State features of a multi-factor lift, p = d / g: g p(p+1)/2 for the
+    concatenated lift, p(p+1)/2 for the summed one."""
     p = d // factors
-    return factors * p * (p + 1) // 2
+    return (1 if kind == "sum" else factors) * p * (p + 1) // 2
 
 
 def prefill_quadratic(q, k, v, eps: float = 0.0, out_dtype=None, out=None, return_den: bool = False,

@@ -305,7 +305,7 @@ kla_status_t kla_prefill_workspace_size(const kla_shape_t* shp, int chunk, int w
 
 namespace {
 
-kla_status_t prefill_call(const char* fn, const kla_shape_t* shp, int chunk, int factors, const void* q,
+kla_status_t prefill_call(const char* fn, const kla_shape_t* shp, int chunk, int factors, int kind, const void* q,
                           const void* k, const void* v, void* o, const float* H0, const float* s0, float* H_T,
                           float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
   kla_status_t st = check_shape(shp, fn);
@@ -332,6 +332,7 @@ kla_status_t prefill_call(const char* fn, const kla_shape_t* shp, int chunk, int
   a.HT = H_T;
   a.sT = s_T;
   a.factors = factors;
+  a.factor_kind = factors > 1 ? kind : 0;  // with one factor both lifts are the rank-one lift
   const size_t need = prefill_ws(a);
   st = check_ws(need, ws, ws_bytes, fn);
   if (st != KLA_OK) return st;
@@ -345,21 +346,40 @@ kla_status_t prefill_call(const char* fn, const kla_shape_t* shp, int chunk, int
 kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* q, const void* k,
                          const void* v, void* o, const float* H0, const float* s0, float* H_T,
                          float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
-  return prefill_call("kla_prefill", shp, chunk, 1, q, k, v, o, H0, s0, H_T, s_T, ws, ws_bytes, stream);
+  return prefill_call("kla_prefill", shp, chunk, 1, KLA_FACTORS_CONCAT, q, k, v, o, H0, s0, H_T, s_T, ws, ws_bytes,
+                      stream);
 }
 
 kla_status_t kla_prefill_factors(const kla_shape_t* shp, int chunk, int kind, int factors, const void* q,
                                  const void* k, const void* v, void* o, const float* H0, const float* s0,
                                  float* H_T, float* s_T, void* ws, size_t ws_bytes, kla_stream_t stream) {
   const char* fn = "kla_prefill_factors";
-  if (kind == KLA_FACTORS_SUM)
-    return fail(KLA_ERR_UNSUPPORTED, "%s: the summed-factor lift is served by kla_prefill_quadratic_factors only",
-                fn);
-  if (kind != KLA_FACTORS_CONCAT)
+  if (kind != KLA_FACTORS_CONCAT && kind != KLA_FACTORS_SUM)
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: kind %d is neither KLA_FACTORS_CONCAT nor KLA_FACTORS_SUM", fn, kind);
   if (factors != 1 && factors != 2 && factors != 4)
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: factors = %d (1, 2 or 4 supported)", fn, factors);
-  return prefill_call(fn, shp, chunk, factors, q, k, v, o, H0, s0, H_T, s_T, ws, ws_bytes, stream);
+  return prefill_call(fn, shp, chunk, factors, kind, q, k, v, o, H0, s0, H_T, s_T, ws, ws_bytes, stream);
+}
+
+kla_status_t kla_prefill_factors_workspace_size(const kla_shape_t* shp, int chunk, int kind, int factors,
+                                                int with_output, size_t* bytes) {
+  const char* fn = "kla_prefill_factors_workspace_size";
+  if (!bytes) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", fn);
+  *bytes = 0;
+  kla_status_t st = check_shape(shp, fn);
+  if (st != KLA_OK) return st;
+  if (chunk != 32 && chunk != 64 && chunk != 128)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: chunk must be 32, 64 or 128 (got %d)", fn, chunk);
+  if (kind != KLA_FACTORS_CONCAT && kind != KLA_FACTORS_SUM)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: kind %d is neither KLA_FACTORS_CONCAT nor KLA_FACTORS_SUM", fn, kind);
+  if (factors != 1 && factors != 2 && factors != 4)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: factors = %d (1, 2 or 4 supported)", fn, factors);
+  kla::PrefillArgs a = make_prefill(shp, chunk);
+  a.o = with_output ? reinterpret_cast<void*>(1) : nullptr;
+  a.factors = factors;
+  a.factor_kind = factors > 1 ? kind : 0;
+  *bytes = prefill_ws(a);
+  return ok();
 }
 
 kla_status_t kla_prefill_quadratic(const kla_shape_t* shp, const void* q, const void* k, const void* v,

@@ -32,8 +32,9 @@ struct PrefillArgs {
   float* HT;
   float* sT;
   float* den;  // quadratic form only: row denominators [N, T], or NULL
-  // quadratic form only: multi-factor lift, kind 0 concatenated (KATA-Mg),
-  // 1 summed (KATA-Sigma-g), over `factors` equal slices (1: rank-one lift)
+  // multi-factor lift, kind 0 concatenated (KATA-Mg), 1 summed
+  // (KATA-Sigma-g: quadratic form and float32 vector path), over `factors`
+  // equal slices (1: rank-one lift)
   int factor_kind = 0;
   int factors = 1;
 };

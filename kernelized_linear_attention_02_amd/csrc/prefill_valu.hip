@@ -7,10 +7,15 @@
 // This is the general path: any supported (d_qk, d_v, chunk), float32 or
 // bf16 inputs, float32 arithmetic throughout (1e-4 relative parity). It is
 // also the state builder for decode (state-only mode, no outputs). With G > 1
-// factors (KATA-Mg, KATA §2.3 "Variantes", read as G equal slices of the
-// d_qk dimensions with their rank-one lifts concatenated) the features are
-// the pairs inside each factor, factor by factor, and the intra-chunk weight
-// is the sum of the factors' squared scores.
+// factors (KATA §2.3 "Variantes", read as G equal slices of p = d_qk / G
+// dimensions) it serves both multi-factor lifts:
+//   KATA-Mg, the factors' rank-one lifts concatenated: the features are the
+//   pairs inside each factor, factor by factor, and the intra-chunk weight
+//   is the sum of the factors' squared scores, sum_i (q_i . k_i)^2;
+//   KATA-Sigma-g, the lift of the summed outer products sum_i x_i x_i^T: the
+//   p(p+1)/2 features are the pairs (a, b) of one factor's dimensions, each
+//   summed over the factors (sum_i x_i,a x_i,b), and the intra-chunk weight
+//   is sum_{i,j} (q_i . k_j)^2 - the smallest state of the variants.
 //
 // Work split. The state of one head is D x d_v floats (D = d_qk(d_qk+1)/2),
 // too large for one CU at d_qk = 64, so every head is split into S feature
@@ -19,6 +24,8 @@
 // (the prefix sum is the register-resident running state). The readout of a
 // slice is a partial numerator/denominator per token; a second kernel adds
 // the S partials to the exact intra-chunk term and divides.
+#include <algorithm>
+
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
 
@@ -30,20 +37,32 @@ constexpr int kMaxSlice = 256;  // features per slice
 constexpr int kTok = 16;        // token tile
 
 // Pair (a, b) of feature f of the G-factor lift over d dimensions (G = 1:
-// the rank-one lift), packed as a | (b << 8).
-__device__ __forceinline__ uint16_t factor_pair(int f, int d, int G) {
+// the rank-one lift), packed as a | (b << 8): for the concatenated lift the
+// dimensions of factor f / (p(p+1)/2); for the summed lift a pair of the
+// first factor's dimensions (the feature adds the same pair of every factor).
+__device__ __forceinline__ uint16_t factor_pair(int f, int d, int G, int kind) {
   const int p = d / G;
+  if (kind == 1) return phi_pair(f, p);
   const int dp = p * (p + 1) / 2;
   const int fi = f / dp;
   const uint16_t ab = phi_pair(f - fi * dp, p);
   return static_cast<uint16_t>(ab + (fi * p) * 0x0101);
 }
 
+// Feature value of pair ab: the rank-one or concatenated lift reads it
+// directly; the summed lift adds it over the G factors of p dimensions.
+__device__ __forceinline__ float factor_phi(const float* x, uint16_t ab, int kind, int G, int p) {
+  if (kind != 1) return phi_of(x, ab);
+  float acc = 0.0f;
+  for (int i = 0; i < G; ++i) acc += phi_of(x + i * p, ab);
+  return acc;
+}
+
 template <int DQK, int DV, typename Tin>
 __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, int T,
     int chunk, int S, int Fs, const float* __restrict__ H0, const float* __restrict__ s0,
-    float* __restrict__ HT, float* __restrict__ sT, float* __restrict__ part, int D, int factors) {
+    float* __restrict__ HT, float* __restrict__ sT, float* __restrict__ part, int D, int factors, int kind) {
   constexpr int G = kThreads / DV;    // feature groups
   constexpr int J = kMaxSlice / G;    // features per thread
   constexpr int W = kThreads / 64;    // waves
@@ -62,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
   __shared__ float red[kTok][G][DV];
   __shared__ float rden[kTok][W];
 
-  for (int i = threadIdx.x; i < fcount; i += blockDim.x) tab[i] = factor_pair(f0 + i, DQK, factors);
+  for (int i = threadIdx.x; i < fcount; i += blockDim.x) tab[i] = factor_pair(f0 + i, DQK, factors, kind);
+  const int fp = DQK / factors;
 
   float h[J];
 #pragma unroll
@@ -92,10 +112,10 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
 #pragma unroll
           for (int j = 0; j < J; ++j) {
             const int fl = g + G * j;
-            if (fl < fcount) acc += phi_of(xs[r], tab[fl]) * h[j];
+            if (fl < fcount) acc += factor_phi(xs[r], tab[fl], kind, factors, fp) * h[j];
           }
           red[r][g][c] = acc;
-          float dd = tid < fcount ? phi_of(xs[r], tab[tid]) * sm : 0.0f;
+          float dd = tid < fcount ? factor_phi(xs[r], tab[tid], kind, factors, fp) * sm : 0.0f;
           dd = wave_sum(dd);
           if ((tid & 63) == 0) rden[r][tid >> 6] = dd;
         }
@@ -132,9 +152,9 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
 #pragma unroll
         for (int j = 0; j < J; ++j) {
           const int fl = g + G * j;
-          if (fl < fcount) h[j] += phi_of(xs[r], tab[fl]) * vv;
+          if (fl < fcount) h[j] += factor_phi(xs[r], tab[fl], kind, factors, fp) * vv;
         }
-        if (tid < fcount) sm += phi_of(xs[r], tab[tid]);
+        if (tid < fcount) sm += factor_phi(xs[r], tab[tid], kind, factors, fp);
       }
       __syncthreads();
     }
@@ -153,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
 template <int DQK, int DV, typename Tin, typename Tout>
 __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    Tout* __restrict__ o, int T, int chunk, int S, const float* __restrict__ part, float eps, int factors) {
+    Tout* __restrict__ o, int T, int chunk, int S, const float* __restrict__ part, float eps, int factors,
+    int kind) {
   constexpr int QB = 16;
   constexpr int KB = 32;
   constexpr int M = DV / 16;
@@ -196,15 +217,27 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(
     __syncthreads();
     for (int i = tid; i < QB * KB; i += kThreads) {
       const int qq = i / KB, kk = i % KB;
-      // sum over the factors (p dimensions each) of the squared factor scores
-      const int pm = DQK / factors - 1;
-      float dot = 0.0f, wsum = 0.0f;
+      // concatenated lift: the sum over the factors (p dimensions each) of
+      // the squared factor scores; summed lift: of every factor pair's
+      const int p = DQK / factors;
+      const int pm = p - 1;
+      float wsum = 0.0f;
+      if (kind == 1) {
+        for (int fi = 0; fi < factors; ++fi)
+          for (int fj = 0; fj < factors; ++fj) {
+            float dot = 0.0f;
+            for (int d = 0; d < p; ++d) dot += qs[qq][fi * p + d] * ks[kk][fj * p + d];
+            wsum += dot * dot;
+          }
+      } else {
+        float dot = 0.0f;
 #pragma unroll
-      for (int d = 0; d < DQK; ++d) {
-        dot += qs[qq][d] * ks[kk][d];
-        const bool end = ((d + 1) & pm) == 0;
-        wsum += end ? dot * dot : 0.0f;
-        dot = end ? 0.0f : dot;
+        for (int d = 0; d < DQK; ++d) {
+          dot += qs[qq][d] * ks[kk][d];
+          const bool end = ((d + 1) & pm) == 0;
+          wsum += end ? dot * dot : 0.0f;
+          dot = end ? 0.0f : dot;
+        }
       }
       const bool ok = (kk < nk) && (kt + kk <= t0 + qq) && (qq < nq);
       w[qq][kk] = ok ? wsum : 0.0f;
@@ -235,32 +268,39 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(
   }
 }
 
-int slices_for(int D) { return (D + kMaxSlice - 1) / kMaxSlice; }
+// Feature slices per head: enough for the features (at most kMaxSlice each)
+// and, for small states or few heads, enough work-groups to fill the GPU
+// (slices of at least 32 features).
+int slices_for(int D, int N) {
+  const int s0 = (D + kMaxSlice - 1) / kMaxSlice;
+  const int fill = (256 + N - 1) / N;
+  return std::max(s0, std::min(fill, (D + 31) / 32));
+}
 
-// features of the G-factor lift over d dimensions
-int factor_dim(int d, int G) {
+// features of the G-factor lift over d dimensions (kind 0 concatenated, 1 summed)
+int factor_dim(int d, int G, int kind) {
   const int p = d / G;
-  return G * p * (p + 1) / 2;
+  return (kind == 1 ? 1 : G) * p * (p + 1) / 2;
 }
 
 template <int DQK, int DV, typename Tin, typename Tout>
 hipError_t launch_typed(const PrefillArgs& a, void* ws, hipStream_t st) {
-  const int D = factor_dim(DQK, a.factors);
-  const int S = slices_for(D);
+  const int D = factor_dim(DQK, a.factors, a.factor_kind);
+  const int S = slices_for(D, a.N);
   const int Fs = (D + S - 1) / S;
   float* part = a.o ? static_cast<float*>(ws) : nullptr;
   prof_begin(st);
   hipLaunchKernelGGL((prefill_slice_kernel<DQK, DV, Tin>), dim3(S, a.N), dim3(kThreads), 0, st,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), a.T, a.chunk, S, Fs, a.H0, a.s0, a.HT, a.sT,
-                     part, D, a.factors);
+                     part, D, a.factors, a.factor_kind);
   prof_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.o) return e;
   hipLaunchKernelGGL((prefill_combine_kernel<DQK, DV, Tin, Tout>), dim3((a.T + 15) / 16, a.N),
                      dim3(kThreads), 0, st, static_cast<const Tin*>(a.q),
                      static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
-                     static_cast<Tout*>(a.o), a.T, a.chunk, S, part, a.eps, a.factors);
+                     static_cast<Tout*>(a.o), a.T, a.chunk, S, part, a.eps, a.factors, a.factor_kind);
   return hipGetLastError();
 }
 
@@ -288,12 +328,13 @@ hipError_t launch_dv(const PrefillArgs& a, void* ws, hipStream_t st) {
 
 size_t prefill_valu_workspace(const PrefillArgs& a) {
   if (!a.o) return 0;
-  const int S = slices_for(phi_dim(a.dqk));
+  const int S = slices_for(factor_dim(a.dqk, a.factors, a.factor_kind), a.N);
   return align_up((size_t)a.N * S * a.T * (a.dv + 1) * sizeof(float));
 }
 
 hipError_t prefill_valu_launch(const PrefillArgs& a, void* ws, hipStream_t st) {
-  if (a.factor_kind != 0 || (a.factors != 1 && a.factors != 2 && a.factors != 4)) return hipErrorInvalidValue;
+  if ((a.factor_kind != 0 && a.factor_kind != 1) || (a.factors != 1 && a.factors != 2 && a.factors != 4))
+    return hipErrorInvalidValue;
   switch (a.dqk) {
     case 16: return launch_dv<16>(a, ws, st);
     case 32: return launch_dv<32>(a, ws, st);

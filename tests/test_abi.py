@@ -186,15 +186,40 @@ def test_prefill_quadratic_factors_rejects(lib):
     assert call(ctypes.byref(_shape(in_dtype=B.KLA_F32)), 1, 4, P, P, P, P, None, None) == B.KLA_ERR_UNSUPPORTED
 
 
+def test_prefill_factors_workspace_query(lib):
+    q = lib.kla_prefill_factors_workspace_size
+    shp = ctypes.byref(_shape())
+    n = ctypes.c_size_t(0)
+    assert q(shp, 64, B.KLA_FACTORS_SUM, 2, 1, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert q(None, 64, B.KLA_FACTORS_SUM, 2, 1, ctypes.byref(n)) == B.KLA_ERR_INVALID_ARGUMENT
+    assert q(shp, 48, B.KLA_FACTORS_SUM, 2, 1, ctypes.byref(n)) == B.KLA_ERR_UNSUPPORTED
+    assert q(shp, 64, 7, 2, 1, ctypes.byref(n)) == B.KLA_ERR_INVALID_ARGUMENT
+    assert q(shp, 64, B.KLA_FACTORS_SUM, 3, 1, ctypes.byref(n)) == B.KLA_ERR_INVALID_ARGUMENT
+    sizes = {}
+    for kind in (B.KLA_FACTORS_CONCAT, B.KLA_FACTORS_SUM):
+        for g in (1, 2, 4):
+            assert q(shp, 64, kind, g, 1, ctypes.byref(n)) == B.KLA_OK
+            sizes[kind, g] = n.value
+    # one factor is kla_prefill for either kind
+    base = ctypes.c_size_t(0)
+    assert lib.kla_prefill_workspace_size(shp, 64, 1, ctypes.byref(base)) == B.KLA_OK
+    assert sizes[B.KLA_FACTORS_CONCAT, 1] == sizes[B.KLA_FACTORS_SUM, 1] == base.value
+    # the concatenated lift fits kla_prefill's workspace, as documented
+    assert sizes[B.KLA_FACTORS_CONCAT, 2] <= base.value and sizes[B.KLA_FACTORS_CONCAT, 4] <= base.value
+    assert sizes[B.KLA_FACTORS_SUM, 2] > 0
+
+
 def test_prefill_factors_rejects(lib):
     call = lib.kla_prefill_factors
     shp = ctypes.byref(_shape())
 
     def go(kind=B.KLA_FACTORS_CONCAT, g=2, shape=shp, chunk=64):
         return call(shape, chunk, kind, g, P, P, P, P, None, None, None, None, P, 1 << 40, None)
-    assert go(kind=B.KLA_FACTORS_SUM) == B.KLA_ERR_UNSUPPORTED
-    assert b"quadratic" in lib.kla_last_error()
     assert go(kind=5) == B.KLA_ERR_INVALID_ARGUMENT
+    # the summed lift is served (vector path): with a huge workspace claim the
+    # checks pass up to the launch, which has no GPU here
+    for g in (0, 3, 8):
+        assert go(kind=B.KLA_FACTORS_SUM, g=g) == B.KLA_ERR_INVALID_ARGUMENT
     for g in (0, 3, 8):
         assert go(g=g) == B.KLA_ERR_INVALID_ARGUMENT
     assert go(chunk=48) == B.KLA_ERR_UNSUPPORTED

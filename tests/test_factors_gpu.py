@@ -205,3 +205,58 @@ def test_factors_vector_path_bf16_inputs(K, g):
         assert_close(host(o)[0, h], ro, RTOL_F32, f"o g={g} head {h}")
         assert_close(host(HT)[0, h], rH, RTOL_F32, f"H_T g={g} head {h}")
         assert_close(host(sT)[0, h], rs, RTOL_F32, f"s_T g={g} head {h}")
+
+
+# ---- the summed lift (KATA-Sigma-g) through the chunked state form: the
+# float32 vector path for every shape, float32 arithmetic on exact inputs, so
+# the float32 bound against the oracle's state form of the same lift
+
+@pytest.mark.parametrize("g", [2, 4])
+@pytest.mark.parametrize("B,H,T,dqk,dv,chunk,eps,dtype", [
+    (1, 2, 100, 64, 64, 64, 0.0, torch.float32), (2, 3, 77, 32, 16, 32, 0.2, torch.float32),
+    (1, 2, 300, 16, 64, 128, 0.0, torch.float32), (1, 1, 1, 32, 32, 64, 0.0, torch.float32),
+    (2, 2, 130, 64, 64, 64, 0.0, torch.bfloat16), (1, 3, 97, 64, 32, 32, 0.1, torch.bfloat16)])
+def test_factors_sum_state_form_every_row(K, g, B, H, T, dqk, dv, chunk, eps, dtype):
+    c = S.prefill_case("factors_sum_state", B, H, T, dqk, dv, chunk, seed=600 + g + T + dqk)
+    o, HT, sT = K.prefill(dev(c.q, dtype), dev(c.k, dtype), dev(c.v, dtype), chunk=chunk, eps=eps,
+                          return_state=True, out_dtype=torch.float32, factors=g, factor_kind="sum")
+    torch.cuda.synchronize()
+    D = K.factor_phi_dim(dqk, g, "sum")
+    assert D == (dqk // g) * (dqk // g + 1) // 2
+    assert HT.shape == (B, H, D, dv) and sT.shape == (B, H, D)
+    # the oracle sees the values the GPU read (bf16-rounded for bf16 inputs)
+    q, k, v = (host(dev(x, dtype)) for x in (c.q, c.k, c.v))
+    for b in range(B):
+        for h in range(H):
+            ro, rH, rs = O.prefill_factors_recurrent(q[b, h], k[b, h], v[b, h], g, "sum", eps=eps)
+            assert_close(host(o)[b, h], ro, RTOL_F32, f"o g={g} head ({b},{h})")
+            assert_close(host(HT)[b, h], rH, RTOL_F32, f"H_T g={g} head ({b},{h})")
+            assert_close(host(sT)[b, h], rs, RTOL_F32, f"s_T g={g} head ({b},{h})")
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_factors_sum_state_form_resume(K, g):
+    # two calls carrying the summed lift's state equal one call, and equal the
+    # closed-form definition sum_{i,j} (q_i . k_j)^2; state-only mode too
+    c = S.prefill_case("factors_sum_resume", 1, 2, 400, 64, 64, 64, seed=640 + g)
+    q, k, v = (dev(x, torch.float32) for x in (c.q, c.k, c.v))
+    T1 = 150
+    o1, H1, s1 = K.prefill(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], chunk=64, return_state=True, factors=g,
+                           factor_kind="sum")
+    o2 = K.prefill(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], chunk=128, state=(H1, s1), factors=g,
+                   factor_kind="sum")
+    Hs, ss = K.prefill(q, k, v, chunk=32, outputs=False, factors=g, factor_kind="sum")
+    for h in range(2):
+        ro = O.prefill_factors_bruteforce(c.q[0, h], c.k[0, h], c.v[0, h], g, "sum")
+        assert_close(host(torch.cat([o1, o2], dim=2))[0, h], ro, RTOL_F32, f"resumed o head {h}")
+        _, rH, rs = O.prefill_factors_recurrent(c.q[0, h], c.k[0, h], c.v[0, h], g, "sum")
+        assert_close(host(Hs)[0, h], rH, RTOL_F32, f"state-only H head {h}")
+        assert_close(host(ss)[0, h], rs, RTOL_F32, f"state-only s head {h}")
+
+
+def test_factors_sum_one_factor_is_prefill(K):
+    c = S.prefill_case("factors_sum_one", 1, 2, 120, 32, 32, 32, seed=660)
+    q, k, v = (dev(x, torch.float32) for x in (c.q, c.k, c.v))
+    a = K.prefill(q, k, v, chunk=32)
+    b = K.prefill(q, k, v, chunk=32, factors=1, factor_kind="sum")
+    assert torch.equal(a, b)
