@@ -129,9 +129,13 @@ struct HybridArgs {
 };
 
 size_t hybrid_workspace(const HybridArgs& a);
-// aux: a second stream of the caller's for the readouts of the matrix-core
-// path, or NULL to run everything on `st`.
+// aux: a second stream of the caller's for the batch work of the matrix-core
+// path (folds, state sums, readouts), or NULL to run everything on `st`.
 hipError_t hybrid_launch(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux);
+// The matrix-core form (d_qk = d_v = 64, bf16 inputs).
+bool hybrid_mfma_supported(const HybridArgs& a);
+size_t hybrid_mfma_workspace(const HybridArgs& a);
+hipError_t hybrid_mfma_launch(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux);
 
 // Token-by-token hybrid: one token for every head-state.
 struct HybridDecodeArgs {
