@@ -49,9 +49,9 @@ constexpr int kL = 4;          // refreshes per batch
 constexpr int kRingB = 4;      // batches the cache, carry and rejected rings hold
 constexpr int kRing = kL * kRingB;
 constexpr int kBaseSlots = 3;  // batches of new-candidate state sums in flight
-constexpr int kSZ = 5;         // feature splits of the state sums per (head, candidate block)
+constexpr int kSZ = 4;         // feature splits of the state sums per (head, candidate block)
 constexpr int kScoreCand = 64;
-constexpr int kRNS = 8;   // readout splits per (head, query block)
+constexpr int kRNS = 4;   // readout splits per (head, query block)
 constexpr int kRB = 8;    // blocks per readout launch, at most
 constexpr int kHFPieces = 3;
 
@@ -136,7 +136,9 @@ __device__ __forceinline__ int kslot_row(int q4, int j) { return j < 4 ? 4 * q4 
 // float32, split into PIECES exact (3) or 16-bit (2) bf16 pieces for the
 // product with V (bf16, exact). acc[nt] lane (l16, q4): rows 4 q4 + i, value
 // column 4 l16 + nt; den: lane (l16, q4) holds part of row l16's sum (the
-// caller adds over q4). `live` masks rows (their weights are zeroed).
+// caller adds over q4). `live` masks rows (their weights are zeroed). The
+// next 32-pair step's rows are loaded while the current one is computed
+// (always issued, the last step reloaded, so the wait counts stay exact).
 template <int PIECES>
 __device__ __forceinline__ void closed_form_pairs(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                   size_t base, const int32_t* __restrict__ ptok, int g0, int g1,
@@ -145,23 +147,34 @@ __device__ __forceinline__ void closed_form_pairs(const uint16_t* __restrict__ k
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
-  for (int j0 = g0; j0 < g1; j0 += 32) {
-    uint4 ka[2][2];
+  if (g0 >= g1) return;
+  auto load = [&](int j0, uint4 (&ka)[2][2], uint2 (&vr)[8]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int g = j0 + 16 * h + l16;
       const bool ok = g < g1;
-      const size_t row = base + (size_t)(ok ? ptok[g] : 0) * kFD;
+      const size_t row = base + (size_t)(ok ? ptok[g] : ptok[g0]) * kFD;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        ka[h][ks] = ok ? *reinterpret_cast<const uint4*>(k + row + 32 * ks + 8 * q4) : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 u = *reinterpret_cast<const uint4*>(k + row + 32 * ks + 8 * q4);
+        ka[h][ks] = ok ? u : make_uint4(0, 0, 0, 0);
+      }
     }
-    uint2 vr[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int g = j0 + kslot_row(q4, j);
-      vr[j] = g < g1 ? *reinterpret_cast<const uint2*>(v + base + (size_t)ptok[g] * kFD + 4 * l16) : make_uint2(0, 0);
+      const bool ok = g < g1;
+      const uint2 u = *reinterpret_cast<const uint2*>(v + base + (size_t)(ok ? ptok[g] : ptok[g0]) * kFD + 4 * l16);
+      vr[j] = ok ? u : make_uint2(0, 0);
     }
+  };
+  uint4 ka[2][2];
+  uint2 vr[8];
+  load(g0, ka, vr);
+  for (int j0 = g0; j0 < g1; j0 += 32) {
+    uint4 kn[2][2];
+    uint2 vn[8];
+    load(j0 + 32 < g1 ? j0 + 32 : j0, kn, vn);
     float x[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -195,6 +208,12 @@ __device__ __forceinline__ void closed_form_pairs(const uint16_t* __restrict__ k
         acc[nt] = mfma16x16x32(A1, B, acc[nt]);
       }
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) ka[h][ks] = kn[h][ks];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vr[j] = vn[j];
   }
 }
 
@@ -208,8 +227,8 @@ struct ChainArgs {
   int n_cache;
   const float* carry_in;    // its entries' sums over the state before the previous fold, [N][kCStride][68]
   int ev0, n_ev;            // tokens ev0 .. ev0 + n_ev - 1 are evicted at this refresh
-  const float* base;        // new candidate c's sums over an older state version, split z:
-  int base_stride;          //   base + ((n kSZ + z) base_stride + c) 68; NULL: the zero state
+  const float* base;        // new candidate c's sums over an older state version at
+  int base_stride;          //   base + (n base_stride + c) 68; NULL: the zero state
   const int32_t* rej;       // rejected-list ring [kRing][N][kCStride]
   PairSets prev;            // pairs of the previous refresh (cached candidates)
   PairSets since;           // pairs rejected after the base's state version (new candidates)
@@ -224,27 +243,62 @@ struct ChainArgs {
 constexpr int kChainThreads = 1024;
 constexpr int kChainWaves = kChainThreads / 64;
 constexpr int kItemsMax = kChainWaves + 1;
+constexpr int kRound = 256;          // pairs staged in LDS at a time
+constexpr int kRowH = kFD + 8;       // staged row stride (bf16), 144 bytes
 struct ChainLds {
-  float red[kItemsMax][16][68];     // per work item: 16 candidates' numerators (64) and denominator
-  int32_t ptok_prev[kPairMax];
-  int32_t ptok_since[2 * kL * kPairMax];
+  uint16_t pk[kRound][kRowH];        // staged pair keys
+  uint16_t pv[kRound][kRowH];        // staged pair values
+  float red[kItemsMax][16][68];      // per work item: 16 candidates' numerators (64) and denominator
+  int32_t ptok[kPairMax + 2 * kL * kPairMax];  // previous refresh's pairs (padded to 32), then the later ones
   uint64_t keys[kCandMax];
   int32_t tok[kCandMax];
   int32_t kid[kCandMax];
+  int32_t rank[kCandMax];
+  int32_t pos[kCandMax];
 };
 
+// Token ids of the sets of `ps` for head n into dst; every thread of the
+// (1024-thread) block issues its loads (at most one per set) before it
+// stores any.
+__device__ __forceinline__ int chain_gather(const PairSets& ps, const int32_t* __restrict__ rej, int N, int n,
+                                            int32_t* dst) {
+  static_assert(kChainThreads >= kPairMax, "one entry per thread and set");
+  const int tid = threadIdx.x;
+  int32_t x[2 * kL];
+#pragma unroll
+  for (int s = 0; s < 2 * kL; ++s)
+    x[s] = (s < ps.n && tid < ps.cnt[s]) ? rej[((size_t)ps.slot[s] * N + n) * kCStride + tid] : 0;
+  int off = 0;
+#pragma unroll
+  for (int s = 0; s < 2 * kL; ++s) {
+    if (s < ps.n) {
+      if (tid < ps.cnt[s]) dst[off + tid] = x[s];
+      off += ps.cnt[s];
+    }
+  }
+  return off;
+}
+
 // One refresh of every head (one work-group each): closed-form terms, scores,
-// selection. Candidates are cut into tiles of 16 (cached tiles, then new
-// ones); a work item is one tile and a share of its pair list, and the waves
-// take the items in turn (new tiles, which have the longer lists, get the
-// spare waves). Then four threads per candidate add its item partials and
-// its carried or state sums,
+// selection. The pair list is the previous refresh's pairs (padded to 32),
+// then the pairs rejected after the new candidates' state version; rounds of
+// 256 pairs are staged in LDS (keys and values, bf16) and shared by every
+// work item. Candidates are cut into tiles of 16 (cached tiles, which take
+// the first part of the list, then new ones, which take the second); a work
+// item is one tile and a share of its pairs, and the waves take the items in
+// turn (new tiles, which have the longer lists, get the spare waves). For a
+// 32-pair step, S^T = K_j X^T on bf16 MFMA (exact products, float32 sums),
+// the squares are split into three exact bf16 pieces for the product with V
+// (bf16), so the numerators are float32 sums of exact products, as in a fold.
+// Then four threads per candidate add its item partials to its carried or
+// state sums,
 //   score_c = || num_c / (den_c + eps) - v_c ||^2   (prediction 0 when the
 //   denominator is 0),
-// and rank it by counting the larger (score, token id) keys; the keep best go
-// to the cache in ascending token order (their place is the number of kept
-// tokens with a lower id) with their sums, the rest in rank order to the
-// rejected list — the order the sort of the generic form gives.
+// and each candidate's rank is the number of larger (score, token id) keys
+// (wave ballots); the keep best go to the cache in ascending token order
+// (their place is the number of kept tokens with a lower id) with their
+// sums, the rest in rank order to the rejected list — the order the sort of
+// the generic form gives.
 __global__ __launch_bounds__(kChainThreads) void hyb_chain_kernel(const ChainArgs a) {
   __shared__ __align__(16) ChainLds sh;
   const int n = blockIdx.x;
@@ -254,89 +308,168 @@ __global__ __launch_bounds__(kChainThreads) void hyb_chain_kernel(const ChainArg
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
   const int n_cand = a.n_cache + a.n_ev;
-  const int32_t* cin = a.cache_in + (size_t)n * kCStride;
   const size_t base = (size_t)n * a.T * kFD;
-  for (int c = tid; c < n_cand; c += kChainThreads) sh.tok[c] = c < a.n_cache ? cin[c] : a.ev0 + (c - a.n_cache);
-  const int np_prev = gather_pair_tokens(a.prev, a.rej, a.N, n, sh.ptok_prev);
-  const int np_since = gather_pair_tokens(a.since, a.rej, a.N, n, sh.ptok_since);
+  {
+    const int32_t* cin = a.cache_in + (size_t)n * kCStride;
+    if (tid < n_cand) sh.tok[tid] = tid < a.n_cache ? cin[tid] : a.ev0 + (tid - a.n_cache);
+  }
+  const int np_prev = chain_gather(a.prev, a.rej, a.N, n, sh.ptok);
+  const int p0 = (np_prev + 31) & ~31;  // first pair of the new candidates' list
+  if (tid >= np_prev && tid < p0) sh.ptok[tid] = 0;  // padding: a valid token, never counted
+  const int np_since = chain_gather(a.since, a.rej, a.N, n, sh.ptok + p0);
+  const int np_all = p0 + np_since;
+  // four adjacent threads per candidate (after the closed-form terms):
+  // quarter qd of its columns; its carried or state sums are loaded now
+  const int c = tid >> 2;
+  const int qd = tid & 3;
+  const bool live = c < n_cand;
+  float4 pre[4] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f),
+                   make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  float pre_den = 0.0f;
+  {
+    const float* row = nullptr;
+    if (live && c < a.n_cache) row = a.carry_in + ((size_t)n * kCStride + c) * 68;
+    if (live && c >= a.n_cache && a.base) row = a.base + ((size_t)n * a.base_stride + (c - a.n_cache)) * 68;
+    if (row) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pre[j] = reinterpret_cast<const float4*>(row + 16 * qd)[j];
+      pre_den = row[64];
+    }
+  }
   __syncthreads();
 
   const int ncT = (a.n_cache + 15) / 16;
   const int neT = (a.n_ev + 15) / 16;
   const int P = neT > 0 ? max(1, (kChainWaves - ncT) / neT) : 1;
   const int n_items = ncT + neT * P;
-  for (int it = w; it < n_items; it += kChainWaves) {
+  // work item of this wave in slot s: tile, pair range [g0, g1) of the list
+  auto item = [&](int it, int& c0, int& c_end, int& g0, int& g1) {
     const bool cached = it < ncT;
     const int tile = cached ? it : (it - ncT) / P;
     const int part = cached ? 0 : (it - ncT) % P;
     const int parts = cached ? 1 : P;
-    const int c0 = cached ? 16 * tile : a.n_cache + 16 * tile;
-    const int c_end = cached ? a.n_cache : n_cand;
+    c0 = cached ? 16 * tile : a.n_cache + 16 * tile;
+    c_end = cached ? a.n_cache : n_cand;
     const int np = cached ? np_prev : np_since;
+    const int off = cached ? 0 : p0;
     const int nch = (np + 31) / 32;
-    const int g0 = 32 * (part * nch / parts);
-    const int g1 = min(np, 32 * ((part + 1) * nch / parts));
+    g0 = off + 32 * (part * nch / parts);
+    g1 = off + min(np, 32 * ((part + 1) * nch / parts));
+  };
+  const int n_rounds = (np_all + kRound - 1) / kRound;
+  for (int slot = 0; slot * kChainWaves < n_items; ++slot) {
+    const int it = w + slot * kChainWaves;
+    int c0 = 0, c_end = 0, g0 = 0, g1 = 0;
+    if (it < n_items) item(it, c0, c_end, g0, g1);
     const int cc = c0 + l16;
-    const bool live = cc < c_end;
+    const bool rl = it < n_items && cc < c_end;
     bf16x8 xb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint4 u =
-          live ? *reinterpret_cast<const uint4*>(a.k + base + (size_t)sh.tok[cc] * kFD + 32 * ks + 8 * q4)
-               : make_uint4(0, 0, 0, 0);
+          rl ? *reinterpret_cast<const uint4*>(a.k + base + (size_t)sh.tok[cc] * kFD + 32 * ks + 8 * q4)
+             : make_uint4(0, 0, 0, 0);
       xb[ks] = __builtin_bit_cast(bf16x8, u);
     }
     f32x4 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float den = 0.0f;
-    closed_form_pairs<3>(a.k, a.v, base, cached ? sh.ptok_prev : sh.ptok_since, g0, g1, xb, live, acc, den);
-    den += __shfl_xor(den, 16, 64);
-    den += __shfl_xor(den, 32, 64);
+    for (int rd = 0; rd < n_rounds; ++rd) {
+      const int r0 = rd * kRound;
+      // stage pairs r0 .. r0 + 255: four threads per pair, 32 bytes of its key and value each
+      {
+        const int r = tid >> 2, part = tid & 3;
+        const int g = r0 + r;
+        const int tk = g < np_all ? sh.ptok[g] : 0;
+        const uint4* kp = reinterpret_cast<const uint4*>(a.k + base + (size_t)tk * kFD + 16 * part);
+        const uint4* vp = reinterpret_cast<const uint4*>(a.v + base + (size_t)tk * kFD + 16 * part);
+        const uint4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+        __syncthreads();  // the previous round's reads are done
+        uint4* kd = reinterpret_cast<uint4*>(&sh.pk[r][16 * part]);
+        uint4* vd = reinterpret_cast<uint4*>(&sh.pv[r][16 * part]);
+        kd[0] = k0;
+        kd[1] = k1;
+        vd[0] = v0;
+        vd[1] = v1;
+      }
+      __syncthreads();
+      const int a0 = max(g0, r0), a1 = min(g1, r0 + kRound);
+      for (int j0 = a0; j0 < a1; j0 += 32) {
+        const int rj = j0 - r0;
+        float x[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = j0 + 16 * h + l16 < a1;
+          f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sh.red[it][4 * q4 + i][4 * l16 + nt] = acc[nt][i];
-    if (q4 == 0) sh.red[it][l16][64] = den;
+          for (int ks = 0; ks < 2; ++ks) {
+            uint4 u = *reinterpret_cast<const uint4*>(&sh.pk[rj + 16 * h + l16][32 * ks + 8 * q4]);
+            if (!ok) u = make_uint4(0, 0, 0, 0);
+            s4 = mfma16x16x32(__builtin_bit_cast(bf16x8, u), xb[ks], s4);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float wgt = rl ? s4[i] * s4[i] : 0.0f;
+            den += wgt;
+            x[4 * h + i] = wgt;
+          }
+        }
+        uint2 vr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kr = kslot_row(q4, j);
+          uint2 u = *reinterpret_cast<const uint2*>(&sh.pv[rj + kr][4 * l16]);
+          vr[j] = j0 + kr < a1 ? u : make_uint2(0, 0);
+        }
+        bf16x8 A0, A1, A2;
+        split3(x, A0, A1, A2);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const bf16x8 B = value_operand(vr, nt);
+          acc[nt] = mfma16x16x32(A0, B, acc[nt]);
+          acc[nt] = mfma16x16x32(A1, B, acc[nt]);
+          acc[nt] = mfma16x16x32(A2, B, acc[nt]);
+        }
+      }
+    }
+    if (it < n_items) {
+      den += __shfl_xor(den, 16, 64);
+      den += __shfl_xor(den, 32, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) sh.red[it][4 * q4 + i][4 * l16 + nt] = acc[nt][i];
+      if (q4 == 0) sh.red[it][l16][64] = den;
+    }
   }
   __syncthreads();
 
-  // four adjacent threads per candidate: quarter qd of its columns, and of
-  // the keys it counts against
-  const int c = tid >> 2;
-  const int qd = tid & 3;
-  const bool live = c < n_cand;
   float num[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) num[j] = 0.0f;
-  float dsum = 0.0f;
+  for (int j = 0; j < 4; ++j) {
+    num[4 * j] = pre[j].x;
+    num[4 * j + 1] = pre[j].y;
+    num[4 * j + 2] = pre[j].z;
+    num[4 * j + 3] = pre[j].w;
+  }
+  float dsum = pre_den;
   float err = 0.0f;
   if (live) {
+    const uint4* vp = reinterpret_cast<const uint4*>(a.v + base + (size_t)sh.tok[c] * kFD + 16 * qd);
+    const uint4 va = vp[0], vb = vp[1];
     auto add = [&](const float* pc) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 x = reinterpret_cast<const float4*>(pc + 16 * qd)[j];
-        num[4 * j] += x.x;
-        num[4 * j + 1] += x.y;
-        num[4 * j + 2] += x.z;
-        num[4 * j + 3] += x.w;
-      }
+      for (int j = 0; j < 16; ++j) num[j] += pc[16 * qd + j];
       dsum += pc[64];
     };
     if (c < a.n_cache) {
-      add(a.carry_in + ((size_t)n * kCStride + c) * 68);
       add(&sh.red[c / 16][c % 16][0]);
     } else {
       const int e = c - a.n_cache;
-      if (a.base) {
-#pragma unroll
-        for (int z = 0; z < kSZ; ++z) add(a.base + (((size_t)n * kSZ + z) * a.base_stride + e) * 68);
-      }
       for (int p = 0; p < P; ++p) add(&sh.red[ncT + (e / 16) * P + p][e % 16][0]);
     }
     const float dn = dsum + a.eps;
-    const uint4* vp = reinterpret_cast<const uint4*>(a.v + base + (size_t)sh.tok[c] * kFD + 16 * qd);
-    const uint4 va = vp[0], vb = vp[1];
     const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -350,58 +483,88 @@ __global__ __launch_bounds__(kChainThreads) void hyb_chain_kernel(const ChainArg
   err += __shfl_xor(err, 2, 64);
   if (qd == 0 && live) sh.keys[c] = topk_key(err, (uint32_t)sh.tok[c]);
   __syncthreads();
-  uint64_t key = 0;
-  int rank = 0;
-  if (live) {
-    key = sh.keys[c];
-    for (int j = qd; j < n_cand; j += 4) rank += sh.keys[j] > key ? 1 : 0;
+  // ranks: wave w takes candidates w, w + 16, ...; lane l holds keys l, 64 + l, ...
+  {
+    uint64_t kk[kCandMax / 64];
+#pragma unroll
+    for (int i = 0; i < kCandMax / 64; ++i) kk[i] = 64 * i + lane < n_cand ? sh.keys[64 * i + lane] : 0ull;
+    for (int cw = w; cw < n_cand; cw += kChainWaves) {
+      // key cw from the lane that holds it
+      uint64_t kx = kk[0];
+#pragma unroll
+      for (int i = 1; i < kCandMax / 64; ++i)
+        if ((cw >> 6) == i) kx = kk[i];
+      const uint32_t khi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kx >> 32), cw & 63);
+      const uint32_t klo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kx, cw & 63);
+      const uint64_t key = ((uint64_t)khi << 32) | (uint64_t)klo;
+      int rk = 0;
+#pragma unroll
+      for (int i = 0; i < kCandMax / 64; ++i) rk += __popcll(__ballot(kk[i] > key));
+      if (lane == 0) {
+        sh.rank[cw] = rk;
+        sh.kid[cw] = rk < a.keep ? sh.tok[cw] : 0x7FFFFFFF;
+      }
+    }
   }
-  rank += __shfl_xor(rank, 1, 64);
-  rank += __shfl_xor(rank, 2, 64);
-  if (qd == 0 && live) sh.kid[c] = rank < a.keep ? sh.tok[c] : 0x7FFFFFFF;
   __syncthreads();
-  int pos = 0;
-  if (live && rank < a.keep) {
-    const int32_t id = sh.tok[c];
-    for (int j = qd; j < n_cand; j += 4) pos += sh.kid[j] < id ? 1 : 0;
+  // places of the kept tokens: the number of kept tokens with a lower id
+  {
+    int32_t ki[kCandMax / 64];
+#pragma unroll
+    for (int i = 0; i < kCandMax / 64; ++i) ki[i] = 64 * i + lane < n_cand ? sh.kid[64 * i + lane] : 0x7FFFFFFF;
+    for (int cw = w; cw < n_cand; cw += kChainWaves) {
+      int32_t kx = ki[0];
+#pragma unroll
+      for (int i = 1; i < kCandMax / 64; ++i)
+        if ((cw >> 6) == i) kx = ki[i];
+      const int32_t id = __builtin_amdgcn_readlane(kx, cw & 63);
+      int ps = 0;
+#pragma unroll
+      for (int i = 0; i < kCandMax / 64; ++i) ps += __popcll(__ballot(ki[i] < id));
+      if (lane == 0) sh.pos[cw] = ps;
+    }
   }
-  pos += __shfl_xor(pos, 1, 64);
-  pos += __shfl_xor(pos, 2, 64);
-  if (live && rank < a.keep) {
+  __syncthreads();
+  if (!live) return;
+  const int rank = sh.rank[c];
+  if (rank < a.keep) {
+    const int pos = sh.pos[c];
     float* co = a.carry_out + ((size_t)n * kCStride + pos) * 68;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<float4*>(co + 16 * qd + 4 * j) =
           make_float4(num[4 * j], num[4 * j + 1], num[4 * j + 2], num[4 * j + 3]);
-    if (qd == 0) co[64] = dsum;
-  }
-  if (qd == 0 && live) {
-    const int32_t id = sh.tok[c];
-    if (rank >= a.keep) {
-      a.rej_out[(size_t)n * kCStride + rank - a.keep] = id;
-    } else {
-      a.cache_out[(size_t)n * kCStride + pos] = id;
-      if (a.trace) a.trace[((size_t)n * a.nblocks + a.block) * a.trace_row_stride + pos] = id;
+    if (qd == 0) {
+      co[64] = dsum;
+      a.cache_out[(size_t)n * kCStride + pos] = sh.tok[c];
+      if (a.trace) a.trace[((size_t)n * a.nblocks + a.block) * a.trace_row_stride + pos] = sh.tok[c];
     }
+  } else if (qd == 0) {
+    a.rej_out[(size_t)n * kCStride + rank - a.keep] = sh.tok[c];
   }
 }
 
 // ---------------------------------------------------------------- fold (off the chain)
 
+constexpr int kFoldRows = 256;  // pairs staged at a time
 struct FoldLds {
-  float kt[kFD][kPairMax + 4];
-  uint16_t vt[kFD][kPairMax + 8];
+  uint16_t kt[kFD][kFoldRows + 8];  // staged keys, transposed (bf16)
+  uint16_t vt[kFD][kFoldRows + 8];  // staged values, transposed
+  int32_t tok[kL * kPairMax];       // the batch's pairs, set after set
 };
-constexpr int kFoldWGs = (kFKS + kWaves - 1) / kWaves;  // work-groups per head, one k-step per wave
+constexpr int kFoldWaves = 5;                                  // one k-step per wave
+constexpr int kFoldThreads = 64 * kFoldWaves;
+constexpr int kFoldWGs = (kFKS + kFoldWaves - 1) / kFoldWaves;  // 13 work-groups per head
 
 // Work-group (bx, n): H += sum_j phi(k_j) v_j^T, s += sum_j phi(k_j) over the
-// pairs of `sets`, for k-step 4 bx + w of head n. Each wave's accumulators
-// are seeded with the stored float32 state, take every set in turn (staged
-// in LDS, 128 pairs at most), and go back to H, s and, as three exact bf16
-// pieces, to the fragments of the next state version. Feature products are
-// float32, split exactly into three bf16 pieces, and v is bf16, so every
-// MFMA product is exact and the sums are float32.
-__global__ __launch_bounds__(kThreads) void hyb_fold_kernel(float* __restrict__ H, float* __restrict__ s,
+// pairs of `sets`, for k-step 5 bx + w of head n. Each wave's accumulators
+// are seeded with the stored float32 state, take the pairs 256 at a time
+// (staged in LDS, one row per thread), and go back to H, s and, as three
+// exact bf16 pieces, to the fragments of the next state version. Feature
+// products are float32 (from bf16 keys), split exactly into three bf16
+// pieces, and v is bf16, so every MFMA product is exact and the sums are
+// float32.
+__global__ __launch_bounds__(kFoldThreads) void hyb_fold_kernel(float* __restrict__ H, float* __restrict__ s,
                                                             uint4* __restrict__ HF, const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v, int T,
                                                             const int32_t* __restrict__ rej, int N,
@@ -413,8 +576,9 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_kernel(float* __restrict__ 
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
-  const int ks = blockIdx.x * kWaves + w;
+  const int ks = blockIdx.x * kFoldWaves + w;
   const bool act = ks < kFKS;
+  const int total = gather_pair_tokens(sets, rej, N, n, sh.tok);
   float* Hn = H + (size_t)n * kFPhi * kFD;
   float* sn = s + (size_t)n * kFPhi;
   f32x4 acc[2][5];
@@ -449,46 +613,51 @@ __global__ __launch_bounds__(kThreads) void hyb_fold_kernel(float* __restrict__ 
     fb[t] = ab >> 8;
     wgt[t] = fa[t] == fb[t] ? 1.0f : kSqrt2;
   }
-  for (int si = 0; si < sets.n; ++si) {
-    int slot = sets.slot[0], cnt = sets.cnt[0];
+  __syncthreads();
+  for (int r0 = 0; r0 < total; r0 += kFoldRows) {
+    const int R = min(kFoldRows, total - r0);
+    // row tid of the round: its key and value (zeros past the count); every
+    // thread takes part in the barriers
+    {
+      uint4 ku[8], vu[8];
+      const bool ok = tid < R;  // R <= kFoldRows
+      const size_t row = ((size_t)n * T + (ok ? sh.tok[min(r0 + tid, kL * kPairMax - 1)] : 0)) * kFD;
 #pragma unroll
-    for (int u = 1; u < kL; ++u)
-      if (si == u) {
-        slot = sets.slot[u];
-        cnt = sets.cnt[u];
+      for (int j = 0; j < 8; ++j) {
+        ku[j] = ok ? reinterpret_cast<const uint4*>(k + row)[j] : make_uint4(0, 0, 0, 0);
+        vu[j] = ok ? reinterpret_cast<const uint4*>(v + row)[j] : make_uint4(0, 0, 0, 0);
       }
-    const int32_t* rj = rej + ((size_t)slot * N + n) * kCStride;
-    const int R = (cnt + 31) & ~31;  // rows padded to whole k-steps (zeros)
-    if (si > 0) __syncthreads();
-    for (int i = tid; i < R * (kFD / 4); i += kThreads) {
-      const int r = i / (kFD / 4);
-      const int d4 = i % (kFD / 4);
-      uint2 ku = make_uint2(0, 0), vu = ku;
-      if (r < cnt) {
-        const size_t row = ((size_t)n * T + rj[r]) * kFD + 4 * d4;
-        ku = *reinterpret_cast<const uint2*>(k + row);
-        vu = *reinterpret_cast<const uint2*>(v + row);
+      if (r0 > 0) __syncthreads();  // the previous round's reads are done
+      if (tid < kFoldRows) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t kw[4] = {ku[j].x, ku[j].y, ku[j].z, ku[j].w};
+          const uint32_t vw[4] = {vu[j].x, vu[j].y, vu[j].z, vu[j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sh.kt[8 * j + 2 * e][tid] = (uint16_t)(kw[e] & 0xFFFF);
+            sh.kt[8 * j + 2 * e + 1][tid] = (uint16_t)(kw[e] >> 16);
+            sh.vt[8 * j + 2 * e][tid] = (uint16_t)(vw[e] & 0xFFFF);
+            sh.vt[8 * j + 2 * e + 1][tid] = (uint16_t)(vw[e] >> 16);
+          }
+        }
       }
-      sh.kt[4 * d4 + 0][r] = __uint_as_float(ku.x << 16);
-      sh.kt[4 * d4 + 1][r] = __uint_as_float(ku.x & 0xFFFF0000u);
-      sh.kt[4 * d4 + 2][r] = __uint_as_float(ku.y << 16);
-      sh.kt[4 * d4 + 3][r] = __uint_as_float(ku.y & 0xFFFF0000u);
-      sh.vt[4 * d4 + 0][r] = (uint16_t)(vu.x & 0xFFFF);
-      sh.vt[4 * d4 + 1][r] = (uint16_t)(vu.x >> 16);
-      sh.vt[4 * d4 + 2][r] = (uint16_t)(vu.y & 0xFFFF);
-      sh.vt[4 * d4 + 3][r] = (uint16_t)(vu.y >> 16);
     }
     __syncthreads();
     if (act) {
+      const int KS = (R + 31) / 32;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        for (int kk = 0; kk < R / 32; ++kk) {
-          const float4* pa = reinterpret_cast<const float4*>(&sh.kt[fa[t]][32 * kk + 8 * q4]);
-          const float4* pb = reinterpret_cast<const float4*>(&sh.kt[fb[t]][32 * kk + 8 * q4]);
-          const float4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
-          const float p[8] = {a0.x * b0.x * wgt[t], a0.y * b0.y * wgt[t], a0.z * b0.z * wgt[t],
-                              a0.w * b0.w * wgt[t], a1.x * b1.x * wgt[t], a1.y * b1.y * wgt[t],
-                              a1.z * b1.z * wgt[t], a1.w * b1.w * wgt[t]};
+        for (int kk = 0; kk < KS; ++kk) {
+          const uint4 ua = *reinterpret_cast<const uint4*>(&sh.kt[fa[t]][32 * kk + 8 * q4]);
+          const uint4 ub = *reinterpret_cast<const uint4*>(&sh.kt[fb[t]][32 * kk + 8 * q4]);
+          const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[2 * e] = __uint_as_float(wa[e] << 16) * __uint_as_float(wb[e] << 16) * wgt[t];
+            p[2 * e + 1] = __uint_as_float(wa[e] & 0xFFFF0000u) * __uint_as_float(wb[e] & 0xFFFF0000u) * wgt[t];
+          }
           bf16x8 A0, A1, A2;
           split3(p, A0, A1, A2);
 #pragma unroll
@@ -746,52 +915,68 @@ __global__ __launch_bounds__(kThreads, 2) void hyb_state_sums_kernel(const uint4
   }
 }
 
+// out[n][c] = sum_z part[n][z][c] for c < count (68 floats each): the state
+// sums of a batch's new candidates, one row per candidate for the chain.
+__global__ __launch_bounds__(kThreads) void hyb_sum_splits_kernel(const float* __restrict__ part, int pstride,
+                                                                  float* __restrict__ out, int count) {
+  const int n = blockIdx.y;
+  const int i = blockIdx.x * kThreads + threadIdx.x;  // (candidate, float4)
+  if (i >= count * 17) return;
+  const int c = i / 17, q = i % 17;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int z = 0; z < kSZ; ++z) {
+    const float4 y = reinterpret_cast<const float4*>(part + (((size_t)n * kSZ + z) * pstride + c) * 68)[q];
+    x.x += y.x;
+    x.y += y.y;
+    x.z += y.z;
+    x.w += y.w;
+  }
+  reinterpret_cast<float4*>(out + ((size_t)n * pstride + c) * 68)[q] = x;
+}
+
 // ---------------------------------------------------------------- readout (off the chain)
 //
-// Work-group (query block, head n, kRNS z + sp) of a launch serving up to kRB
-// blocks (z) of `refresh` tokens; wave w owns queries t0 + 16 w .. + 15.
-// Softmax keys are the block's cache entries and then the window [f, t].
-// Scores come from S^T = K Q^T on bf16 MFMA (exact products, float32 sums):
-// lane (l16, q4) holds the scores of query l16 against keys 4 q4 + i of
-// each 16-key half. Pass 1 finds each query's maximum m (clamped at 0, since
-// the joint normalisation divides the linear terms by e^m too); pass 2 forms
-// P = e^(tau s - m) in two bf16 pieces and P [V | 1]. The linear term is
-// phi(q)^T [H | s] over the state version the launch reads (two-piece
-// fragments, hi*hi + hi*lo + lo*hi with two-piece phi(q); wave w takes the
-// k-steps ks = w mod 4 and the four partials meet in LDS), plus the pairs
-// rejected after that version up to the block's refresh in closed form,
-// (q . k_j)^2 [v_j | 1]. Split sp of kRNS takes a share of the softmax keys,
-// of the closed-form pairs and of the state k-steps, and writes per query
-// its numerator and denominator scaled by e^-m_sp, and m_sp, to
-// xp[n][qoff + query][sp][66] for hyb_readout_combine_kernel.
+// A launch reads out up to kRB blocks of `refresh` tokens with two kernels,
+// joined by a third. For query t of block z:
+//   keys   (work-group (query block, head, kRNS z + sp)): the softmax terms
+//          over split sp's share of the block's keys (cache entries, then
+//          the window [f, t]) and of the closed-form pairs (those rejected
+//          after the state version, up to the block's refresh); writes
+//          num_sp, den_sp scaled by e^-m_sp, and m_sp, to xp;
+//   state  (work-group (query block and k-step range g, head, z)):
+//          phi(q)^T [H | s] over range g's feature k-steps of the state
+//          version, unscaled, to lp;
+//   combine: m = max m_sp, o = (sum e^(m_sp - m) num_sp + e^-m sum_g lin_g)
+//          / (sum e^(m_sp - m) den_sp + e^-m (sum_g lin_g,den + eps)).
+// The keys kernel: wave w owns queries t0 + 16 w .. + 15. Scores come from
+// S^T = K Q^T on bf16 MFMA (exact products, float32 sums): lane (l16, q4)
+// holds the scores of query l16 against keys 4 q4 + i of each 16-key half.
+// One pass over the keys keeps each query's running maximum m (clamped at
+// 0, since the joint normalisation divides the linear terms by e^m too),
+// rescales what it has accumulated when m grows, and adds P = e^(tau s - m)
+// in two bf16 pieces times [V | 1]; the closed-form pairs add
+// (q . k_j)^2 [v_j | 1] (weights in two bf16 pieces), scaled by e^-m.
 constexpr int kRW = 4;         // waves (16 queries each) per work-group
 constexpr int kRT = 64 * kRW;  // threads
 constexpr int kRQ = 16 * kRW;  // queries per work-group
 constexpr int kRK = 32;        // keys per tile
 constexpr int kPT = 2;         // key tiles per iteration (and in flight)
-constexpr int kPF = 2;         // state k-steps per iteration (and in flight)
+constexpr int kSR = 4;         // k-step ranges of the state term
 
 struct ReadoutBlocks {
   int nb;
   int t_begin[kRB], t_end[kRB], f[kRB], n_cache[kRB];
   int npairs[kRB];  // closed-form pairs: a prefix of the launch's pair sets
-  int qoff[kRB];    // first row of the block in xp
+  int qoff[kRB];    // first row of the block in xp and lp
   const int32_t* cache[kRB];
 };
 
-struct ReadoutLds {
-  float qf[kRQ][kFD + 1];       // query rows (float32) for phi(q)
-  uint16_t tab[kFPhi];          // feature pairs
-  float4 red[kRW][kRW][5][64];  // linear partials: [source wave][token tile][n-tile][lane]
-  float mq[kRQ];                // per-query maximum
-  int32_t ptok[kL * kPairMax];  // closed-form pair tokens
-};
-
-__global__ __launch_bounds__(kRT) void hyb_readout_kernel(
+__global__ __launch_bounds__(kRT) void hyb_readout_keys_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T,
-    const uint4* __restrict__ HF, const ReadoutBlocks rb, const PairSets cf, const int32_t* __restrict__ rej,
-    int N, float scale, float* __restrict__ xp, int xq) {
-  __shared__ __align__(16) ReadoutLds sh;
+    const ReadoutBlocks rb, const PairSets cf, const int32_t* __restrict__ rej, int N, float scale,
+    float* __restrict__ xp, int xq) {
+  __shared__ int32_t ptok[kL * kPairMax];
   const int n = blockIdx.y;
   const int z = blockIdx.z / kRNS;
   const int sp = blockIdx.z % kRNS;
@@ -823,18 +1008,7 @@ __global__ __launch_bounds__(kRT) void hyb_readout_kernel(
   const int32_t* cn = cache + (size_t)n * kCStride;
   // keys: cache, then window tokens f .. tq_end - 1
   const int n_keys = n_cache + (tq_end - f);
-
-  for (int i = tid; i < kFPhi; i += kRT) sh.tab[i] = kPairs.ab[i];
-  for (int i = tid; i < kRQ * (kFD / 4); i += kRT) {
-    const int r = i / (kFD / 4), d4 = i % (kFD / 4);
-    uint2 u = make_uint2(0, 0);
-    if (t0 + r < tq_end) u = *reinterpret_cast<const uint2*>(q + base + (size_t)(t0 + r) * kFD + 4 * d4);
-    sh.qf[r][4 * d4 + 0] = __uint_as_float(u.x << 16);
-    sh.qf[r][4 * d4 + 1] = __uint_as_float(u.x & 0xFFFF0000u);
-    sh.qf[r][4 * d4 + 2] = __uint_as_float(u.y << 16);
-    sh.qf[r][4 * d4 + 3] = __uint_as_float(u.y & 0xFFFF0000u);
-  }
-  if (ncf > 0) gather_pair_tokens(cf, rej, N, n, sh.ptok);
+  if (ncf > 0) gather_pair_tokens(cf, rej, N, n, ptok);
   // Q^T as the B operand of S^T = K Q^T: lane (l16 = query, q4) holds dims 8 q4 .. + 7 (+ 32 ks)
   bf16x8 qb[2];
 #pragma unroll
@@ -843,7 +1017,7 @@ __global__ __launch_bounds__(kRT) void hyb_readout_kernel(
     if (my_t < tq_end) u = *reinterpret_cast<const uint4*>(q + base + (size_t)my_t * kFD + 32 * ks + 8 * q4);
     qb[ks] = __builtin_bit_cast(bf16x8, u);
   }
-  __syncthreads();
+  if (ncf > 0) __syncthreads();
 
   auto key_token = [&](int j) { return j < n_cache ? cn[j] : f + (j - n_cache); };
   // this split's keys, cut to the ones any query of the wave sees
@@ -889,49 +1063,17 @@ __global__ __launch_bounds__(kRT) void hyb_readout_kernel(
     }
   };
 
-  // ---- pass 1: per-query maximum (kPT key tiles per iteration, the next kPT in flight)
-  float mx = 0.0f;  // never below 0
-  {
-    uint4 ka[kPT][2][2];
-#pragma unroll
-    for (int t = 0; t < kPT; ++t) load_k(kbeg + kRK * t, ka[t]);
-    for (int j0 = kbeg; j0 < wave_keys; j0 += kRK * kPT) {
-      uint4 kn[kPT][2][2];
-      const bool more = j0 + kRK * kPT < wave_keys;
-      if (more) {
-#pragma unroll
-        for (int t = 0; t < kPT; ++t) load_k(j0 + kRK * (kPT + t), kn[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < kPT; ++t) {
-        float sc[2][4];
-        scores(j0 + kRK * t, ka[t], sc);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[h][i]);
-      }
-      if (more) {
-#pragma unroll
-        for (int t = 0; t < kPT; ++t)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) ka[t][h][ks] = kn[t][h][ks];
-      }
-    }
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if (q4 == 0) sh.mq[16 * w + l16] = mx;
-
-  // ---- pass 2: P [V | 1]
+  // ---- one pass over the split's keys (kPT tiles per iteration, the next kPT
+  // in flight) with a running per-query maximum m (never below 0): a tile that
+  // raises it rescales the accumulated P [V | 1] by e^(m_old - m_new), then
+  // adds P = e^(tau s - m) (two bf16 pieces) times [V | 1]
   bf16x8 ones;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(l16 == 0 ? 1.0f : 0.0f);
   f32x4 acc[5];
 #pragma unroll
   for (int nt = 0; nt < 5; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mx = 0.0f;  // lane (l16, q4): query l16's running maximum
   {
     uint4 ka[kPT][2][2];
     uint2 vr[kPT][8];
@@ -955,7 +1097,22 @@ __global__ __launch_bounds__(kRT) void hyb_readout_kernel(
       for (int t = 0; t < kPT; ++t) {
         float sc[2][4];
         scores(j0 + kRK * t, ka[t], sc);
-        // P = p0 + p1 (two bf16 pieces, 16 significant bits); v and 1 are exact in bf16
+        float tm = mx;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tm = fmaxf(tm, sc[h][i]);
+        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        const float alpha = __expf(mx - tm);
+        mx = tm;
+        // accumulator rows 4 q4 + i are queries 4 q4 + i: their factors sit in lanes 4 q4 + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * q4 + i, 64);
+#pragma unroll
+          for (int nt = 0; nt < 5; ++nt) acc[nt][i] *= ai;
+        }
         float pf[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -995,131 +1152,175 @@ __global__ __launch_bounds__(kRT) void hyb_readout_kernel(
     const int cspan = (((ncf + kRNS - 1) / kRNS) + 31) / 32 * 32;
     const int g0 = min(ncf, sp * cspan);
     const int g1 = min(ncf, g0 + cspan);
-    closed_form_pairs<2>(k, v, base, sh.ptok, g0, g1, qb, my_t < tq_end, cfa, cfd);
+    closed_form_pairs<2>(k, v, base, ptok, g0, g1, qb, my_t < tq_end, cfa, cfd);
   }
-  // lane (l16, q4) holds part of query l16's denominator: into acc layout
-  // (rows 4 q4 + i) through the query's lanes
   cfd += __shfl_xor(cfd, 16, 64);
   cfd += __shfl_xor(cfd, 32, 64);
 
-  // ---- linear readout phi(q)^T [H | s]: this wave's k-steps, all 64 queries
-  f32x4 lin[kRW][5];
-#pragma unroll
-  for (int tt = 0; tt < kRW; ++tt)
-#pragma unroll
-    for (int nt = 0; nt < 5; ++nt) lin[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (HF) {
-    // k-steps ks = w + kRW (kPF i + t): kPF per iteration, the next kPF in flight
-    auto load_f = [&](int ks, uint4 (&x)[2][5]) {
-#pragma unroll
-      for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-        for (int nt = 0; nt < 5; ++nt)
-          x[pc][nt] = ks < kFKS ? HF[hf_index(n, ks, pc, nt, lane)] : make_uint4(0, 0, 0, 0);
-    };
-    uint4 fr[kPF][2][5];
-    const int kst = kRNS * kRW;  // k-step stride of this split's waves
-#pragma unroll
-    for (int t = 0; t < kPF; ++t) load_f(sp * kRW + w + kst * t, fr[t]);
-    for (int ks0 = sp * kRW + w; ks0 < kFKS; ks0 += kst * kPF) {
-      uint4 fn[kPF][2][5];
-      const bool more = ks0 + kst * kPF < kFKS;
-      if (more) {
-#pragma unroll
-        for (int t = 0; t < kPF; ++t) load_f(ks0 + kst * (kPF + t), fn[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < kPF; ++t) {
-        const int ks = ks0 + kst * t;
-        if (ks < kFKS) {
-          // features of this lane's k-slots: 32 ks + kslot_row(q4, j)
-          int fa[8], fb[8];
-          float wg[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint16_t ab = sh.tab[32 * ks + kslot_row(q4, j)];
-            fa[j] = ab & 0xFF;
-            fb[j] = ab >> 8;
-            wg[j] = fa[j] == fb[j] ? 1.0f : kSqrt2;
-          }
-#pragma unroll
-          for (int tt = 0; tt < kRW; ++tt) {
-            const float* qrow = sh.qf[16 * tt + l16];
-            float p[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = qrow[fa[j]] * qrow[fb[j]] * wg[j];
-            bf16x8 A0, A1;
-            split2(p, A0, A1);
-#pragma unroll
-            for (int nt = 0; nt < 5; ++nt) {
-              const bf16x8 B0 = __builtin_bit_cast(bf16x8, fr[t][0][nt]);
-              const bf16x8 B1 = __builtin_bit_cast(bf16x8, fr[t][1][nt]);
-              lin[tt][nt] = mfma16x16x32(A0, B0, lin[tt][nt]);
-              lin[tt][nt] = mfma16x16x32(A0, B1, lin[tt][nt]);
-              lin[tt][nt] = mfma16x16x32(A1, B0, lin[tt][nt]);
-            }
-          }
-        }
-      }
-      if (more) {
-#pragma unroll
-        for (int t = 0; t < kPF; ++t)
-#pragma unroll
-          for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-            for (int nt = 0; nt < 5; ++nt) fr[t][pc][nt] = fn[t][pc][nt];
-      }
-    }
-  }
-#pragma unroll
-  for (int tt = 0; tt < kRW; ++tt)
-#pragma unroll
-    for (int nt = 0; nt < 5; ++nt)
-      sh.red[w][tt][nt][lane] = make_float4(lin[tt][nt][0], lin[tt][nt][1], lin[tt][nt][2], lin[tt][nt][3]);
-  __syncthreads();
-  // this wave's queries (token tile w): sum of the four partials and the
-  // closed-form terms
-  f32x4 ln[5];
-#pragma unroll
-  for (int nt = 0; nt < 5; ++nt) {
-    ln[nt] = nt < 4 ? cfa[nt] : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < kRW; ++r) {
-      const float4 y = sh.red[r][w][nt][lane];
-      ln[nt][0] += y.x;
-      ln[nt][1] += y.y;
-      ln[nt][2] += y.z;
-      ln[nt][3] += y.w;
-    }
-  }
-  // closed-form denominators: query 4 q4 + i of the wave sits in lane
-  // (4 q4 + i, any q4')
-  float cden[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) cden[i] = __shfl(cfd, 4 * q4 + i, 64);
-
-  // ---- partials of this split, scaled by e^-m_sp: numerator, denominator (no eps), m_sp
+  // ---- partials of this split, scaled by e^-m_sp: numerator, denominator (no eps), m_sp;
+  // query 4 q4 + i of the wave (rows of the accumulators) sits in lane 4 q4 + i of mx and cfd
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * w + 4 * q4 + i;
+    const float m = __shfl(mx, 4 * q4 + i, 64);
+    const float cd = __shfl(cfd, 4 * q4 + i, 64);
     if (t0 + r < tq_end) {
-      const float m = sh.mq[r];
       const float e = __expf(-m);
       float* xr = xp + (((size_t)n * xq + qoff + (t0 + r - t_begin)) * kRNS + sp) * 66;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) xr[4 * l16 + nt] = acc[nt][i] + e * ln[nt][i];
+      for (int nt = 0; nt < 4; ++nt) xr[4 * l16 + nt] = acc[nt][i] + e * cfa[nt][i];
       if (l16 == 0) {
-        xr[64] = acc[4][i] + e * (ln[4][i] + cden[i]);
+        xr[64] = acc[4][i] + e * cd;
         xr[65] = m;
       }
     }
   }
 }
 
-// Joins the kRNS split partials of every block of a launch: m = max m_sp,
-// o = sum e^(m_sp - m) num_sp / (sum e^(m_sp - m) den_sp + e^-m eps).
+// The state term: work-group (query block qb and range g as kSR qb + g, head
+// n, block z) takes feature k-steps [g 65 / kSR, (g + 1) 65 / kSR) of the
+// state version for the block's 64 queries; wave w takes the range's k-steps
+// w, w + 4, ... for all four 16-query tiles (two-piece fragments,
+// hi*hi + hi*lo + lo*hi with two-piece phi(q)), and the four partials of a
+// tile meet in LDS, one tile at a time. Output column 4 l16 + nt sits in
+// n-tile nt of lane (l16, q4), rows 4 q4 + i.
+struct StateLds {
+  float qf[kRQ][kFD + 1];  // query rows (float32) for phi(q)
+  uint16_t tab[kFPhi];     // feature pairs
+  float4 red[kRW][5][64];  // one token tile's partials from the four waves
+};
+
+__global__ __launch_bounds__(kRT, 2) void hyb_readout_state_kernel(const uint16_t* __restrict__ q, int T,
+                                                                   const uint4* __restrict__ HF,
+                                                                   const ReadoutBlocks rb, float* __restrict__ lp,
+                                                                   int xq) {
+  __shared__ __align__(16) StateLds sh;
+  const int n = blockIdx.y;
+  const int z = blockIdx.z;
+  const int g = blockIdx.x % kSR;
+  const int qblk = blockIdx.x / kSR;
+  int t_begin = rb.t_begin[0], t_end = rb.t_end[0], qoff = rb.qoff[0];
+#pragma unroll
+  for (int u = 1; u < kRB; ++u)
+    if (z == u) {
+      t_begin = rb.t_begin[u];
+      t_end = rb.t_end[u];
+      qoff = rb.qoff[u];
+    }
+  const int t0 = t_begin + kRQ * qblk;
+  if (z >= rb.nb || t0 >= t_end) return;
+  const int tq_end = min(t_end, t0 + kRQ);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  const size_t base = (size_t)n * T * kFD;
+  for (int i = tid; i < kFPhi / 8; i += kRT)
+    reinterpret_cast<uint4*>(sh.tab)[i] = reinterpret_cast<const uint4*>(kPairs.ab)[i];
+  for (int i = tid; i < kRQ * (kFD / 4); i += kRT) {
+    const int r = i / (kFD / 4), d4 = i % (kFD / 4);
+    uint2 u = make_uint2(0, 0);
+    if (t0 + r < tq_end) u = *reinterpret_cast<const uint2*>(q + base + (size_t)(t0 + r) * kFD + 4 * d4);
+    sh.qf[r][4 * d4 + 0] = __uint_as_float(u.x << 16);
+    sh.qf[r][4 * d4 + 1] = __uint_as_float(u.x & 0xFFFF0000u);
+    sh.qf[r][4 * d4 + 2] = __uint_as_float(u.y << 16);
+    sh.qf[r][4 * d4 + 3] = __uint_as_float(u.y & 0xFFFF0000u);
+  }
+  __syncthreads();
+
+  const int k0 = (g * kFKS) / kSR, k1 = ((g + 1) * kFKS) / kSR;
+  f32x4 lin[kRW][5];
+#pragma unroll
+  for (int tt = 0; tt < kRW; ++tt)
+#pragma unroll
+    for (int nt = 0; nt < 5; ++nt) lin[tt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_f = [&](int ks, uint4 (&x)[2][5]) {
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+      for (int nt = 0; nt < 5; ++nt) x[pc][nt] = HF[hf_index(n, min(ks, kFKS - 1), pc, nt, lane)];
+  };
+  uint4 fr[2][5];
+  load_f(k0 + w, fr);
+  for (int ks = k0 + w; ks < k1; ks += kRW) {
+    uint4 fn[2][5];
+    const bool more = ks + kRW < k1;
+    if (more) load_f(ks + kRW, fn);
+    // features of this lane's k-slots: 32 ks + kslot_row(q4, j)
+    int fa[8], fb[8];
+    float wg[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint16_t ab = sh.tab[32 * ks + kslot_row(q4, j)];
+      fa[j] = ab & 0xFF;
+      fb[j] = ab >> 8;
+      wg[j] = fa[j] == fb[j] ? 1.0f : kSqrt2;
+    }
+#pragma unroll
+    for (int tt = 0; tt < kRW; ++tt) {
+      const float* qrow = sh.qf[16 * tt + l16];
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = qrow[fa[j]] * qrow[fb[j]] * wg[j];
+      bf16x8 A0, A1;
+      split2(p, A0, A1);
+#pragma unroll
+      for (int nt = 0; nt < 5; ++nt) {
+        const bf16x8 B0 = __builtin_bit_cast(bf16x8, fr[0][nt]);
+        const bf16x8 B1 = __builtin_bit_cast(bf16x8, fr[1][nt]);
+        lin[tt][nt] = mfma16x16x32(A0, B0, lin[tt][nt]);
+        lin[tt][nt] = mfma16x16x32(A0, B1, lin[tt][nt]);
+        lin[tt][nt] = mfma16x16x32(A1, B0, lin[tt][nt]);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+        for (int nt = 0; nt < 5; ++nt) fr[pc][nt] = fn[pc][nt];
+    }
+  }
+  // token tile tt's four partials meet in LDS; wave tt keeps the sum
+  f32x4 ln[5];
+#pragma unroll
+  for (int tt = 0; tt < kRW; ++tt) {
+#pragma unroll
+    for (int nt = 0; nt < 5; ++nt)
+      sh.red[w][nt][lane] = make_float4(lin[tt][nt][0], lin[tt][nt][1], lin[tt][nt][2], lin[tt][nt][3]);
+    __syncthreads();
+    if (w == tt) {
+#pragma unroll
+      for (int nt = 0; nt < 5; ++nt) {
+        ln[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < kRW; ++r) {
+          const float4 y = sh.red[r][nt][lane];
+          ln[nt][0] += y.x;
+          ln[nt][1] += y.y;
+          ln[nt][2] += y.z;
+          ln[nt][3] += y.w;
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * q4 + i;
+    if (t0 + r < tq_end) {
+      float* lr = lp + (((size_t)n * xq + qoff + (t0 + r - t_begin)) * kSR + g) * 65;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) lr[4 * l16 + nt] = ln[nt][i];
+      if (l16 == 0) lr[64] = ln[4][i];
+    }
+  }
+}
+
+// Joins the kRNS key partials and the ng state ranges of every block of a launch.
 template <typename Tout>
-__global__ __launch_bounds__(kThreads) void hyb_readout_combine_kernel(const float* __restrict__ xp, int xq,
+__global__ __launch_bounds__(kThreads) void hyb_readout_combine_kernel(const float* __restrict__ xp,
+                                                                     const float* __restrict__ lp, int ng, int xq,
                                                                      const ReadoutBlocks rb, Tout* __restrict__ o,
                                                                      int T, float eps) {
   const int n = blockIdx.y;
@@ -1136,15 +1337,25 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_combine_kernel(const flo
   const int r = idx >> 6, c = idx & 63;
   const int t = t_begin + r;
   if (z >= rb.nb || t >= t_end) return;
-  const float* xr = xp + ((size_t)n * xq + qoff + r) * kRNS * 66;
+  const size_t row = (size_t)n * xq + qoff + r;
+  const float* xr = xp + row * kRNS * 66;
   float m = 0.0f;
   for (int sp = 0; sp < kRNS; ++sp) m = fmaxf(m, xr[sp * 66 + 65]);
-  float num = 0.0f, den = __expf(-m) * eps;
+  float num = 0.0f, den = 0.0f;
   for (int sp = 0; sp < kRNS; ++sp) {
     const float e = __expf(xr[sp * 66 + 65] - m);
     num += e * xr[sp * 66 + c];
     den += e * xr[sp * 66 + 64];
   }
+  float lnum = 0.0f, lden = eps;
+  const float* lr = lp + row * kSR * 65;
+  for (int g = 0; g < ng; ++g) {
+    lnum += lr[g * 65 + c];
+    lden += lr[g * 65 + 64];
+  }
+  const float e = __expf(-m);
+  num += e * lnum;
+  den += e * lden;
   Elem<Tout>::store(o, ((size_t)n * T + t) * kFD + c, den != 0.0f ? num / den : 0.0f);
 }
 
@@ -1198,8 +1409,10 @@ struct Ws {
   int32_t* cache;  // [kRing + 1][N][kCStride]; slot kRing: before the first refresh
   float* carry;    // [kRing + 1][N][kCStride][68]
   int32_t* rej;    // [kRing][N][kCStride]
-  float* base;     // [kBaseSlots][N][kSZ][kL evs][68]
+  float* part;     // [N][kSZ][kL evs][68]: state sums of a batch's new candidates, by feature split
+  float* base;     // [kBaseSlots][N][kL evs][68]: their sums
   float* xp;       // [N][kRB refresh][kRNS][66]
+  float* lp;       // [N][kRB refresh][kSR][65]
 };
 
 size_t hf_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kFKS * kHFPieces * 5 * 64 * sizeof(uint4)); }
@@ -1209,9 +1422,11 @@ size_t carry_bytes(const HybridArgs& a) {
 }
 size_t rej_bytes(const HybridArgs& a) { return align_up((size_t)kRing * a.N * kCStride * sizeof(int32_t)); }
 int evs_of(const HybridArgs& a) { return (a.refresh + 63) / 64 * 64; }
-size_t base_slot_floats(const HybridArgs& a) { return (size_t)a.N * kSZ * kL * evs_of(a) * 68; }
+size_t base_slot_floats(const HybridArgs& a) { return (size_t)a.N * kL * evs_of(a) * 68; }
+size_t part_bytes(const HybridArgs& a) { return align_up(kSZ * base_slot_floats(a) * sizeof(float)); }
 size_t base_bytes(const HybridArgs& a) { return align_up(kBaseSlots * base_slot_floats(a) * sizeof(float)); }
 size_t xp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kRB * a.refresh * kRNS * 66 * sizeof(float)); }
+size_t lp_bytes(const HybridArgs& a) { return align_up((size_t)a.N * kRB * a.refresh * kSR * 65 * sizeof(float)); }
 
 Ws carve(const HybridArgs& a, void* ws) {
   char* p = static_cast<char*>(ws);
@@ -1227,8 +1442,10 @@ Ws carve(const HybridArgs& a, void* ws) {
   w.cache = reinterpret_cast<int32_t*>(take(cache_bytes(a)));
   w.carry = reinterpret_cast<float*>(take(carry_bytes(a)));
   w.rej = reinterpret_cast<int32_t*>(take(rej_bytes(a)));
+  w.part = reinterpret_cast<float*>(take(part_bytes(a)));
   w.base = reinterpret_cast<float*>(take(base_bytes(a)));
   w.xp = reinterpret_cast<float*>(take(xp_bytes(a)));
+  w.lp = reinterpret_cast<float*>(take(lp_bytes(a)));
   return w;
 }
 
@@ -1347,10 +1564,14 @@ hipError_t enqueue(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t au
           qmax = std::max(qmax, bl.t1 - bl.t0);
         }
         for (int z = rb.nb; z < kRB; ++z) rb.cache[z] = rb.cache[0];
-        hipLaunchKernelGGL(hyb_readout_kernel, dim3((qmax + kRQ - 1) / kRQ, N, kRNS * rb.nb), dim3(kRT), 0, sb, q, k,
-                           v, a.T, HF, rb, cf, w.rej, N, a.scale, w.xp, kRB * a.refresh);
+        const int nqb = (qmax + kRQ - 1) / kRQ;
+        hipLaunchKernelGGL(hyb_readout_keys_kernel, dim3(nqb, N, kRNS * rb.nb), dim3(kRT), 0, sb, q, k, v, a.T, rb,
+                           cf, w.rej, N, a.scale, w.xp, kRB * a.refresh);
+        if (HF)
+          hipLaunchKernelGGL(hyb_readout_state_kernel, dim3(nqb * kSR, N, rb.nb), dim3(kRT), 0, sb, q, a.T, HF, rb,
+                             w.lp, kRB * a.refresh);
         hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>), dim3((qmax * kFD + kThreads - 1) / kThreads, N, rb.nb),
-                           dim3(kThreads), 0, sb, w.xp, kRB * a.refresh, rb, o, a.T, a.eps);
+                           dim3(kThreads), 0, sb, w.xp, w.lp, HF ? kSR : 0, kRB * a.refresh, rb, o, a.T, a.eps);
         KLA_CHECK();
       }
       return hipSuccess;
@@ -1398,7 +1619,7 @@ hipError_t enqueue(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t au
         KLA_TRY(hipEventRecord(ev.chain(), st));
         KLA_TRY(hipStreamWaitEvent(sb, ev.chain(), 0));
       }
-      hipLaunchKernelGGL(hyb_fold_kernel, dim3(kFoldWGs, N), dim3(kThreads), 0, sb, w.H, w.s, w.HF[m % 2], k, v,
+      hipLaunchKernelGGL(hyb_fold_kernel, dim3(kFoldWGs, N), dim3(kFoldThreads), 0, sb, w.H, w.s, w.HF[m % 2], k, v,
                          a.T, w.rej, N, sets_of(r0, r1));
       KLA_CHECK();
       if (m + 2 < M) {
@@ -1412,7 +1633,9 @@ hipError_t enqueue(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t au
           ev_max = std::max(ev_max, eb.n_ev[i]);
         }
         hipLaunchKernelGGL(hyb_state_sums_kernel, dim3(((ev_max + kScoreCand - 1) / kScoreCand) * kSZ, eb.nr, N),
-                           dim3(kThreads), 0, sb, w.HF[m % 2], k, a.T, eb, evs, base_slot(m + 2));
+                           dim3(kThreads), 0, sb, w.HF[m % 2], k, a.T, eb, evs, w.part);
+        hipLaunchKernelGGL(hyb_sum_splits_kernel, dim3((kL * evs * 17 + kThreads - 1) / kThreads, N), dim3(kThreads),
+                           0, sb, w.part, kL * evs, base_slot(m + 2), kL * evs);
         KLA_CHECK();
       }
       if (two) KLA_TRY(hipEventRecord(ev.sums(m), sb));
@@ -1448,7 +1671,8 @@ size_t hybrid_mfma_workspace(const HybridArgs& a) {
   size_t b = 0;
   if (!a.HT) b += align_up((size_t)a.N * kFPhi * kFD * sizeof(float));
   if (!a.sT) b += align_up((size_t)a.N * kFPhi * sizeof(float));
-  return b + 2 * hf_bytes(a) + cache_bytes(a) + carry_bytes(a) + rej_bytes(a) + base_bytes(a) + xp_bytes(a);
+  return b + 2 * hf_bytes(a) + cache_bytes(a) + carry_bytes(a) + rej_bytes(a) + part_bytes(a) + base_bytes(a) + xp_bytes(a) +
+         lp_bytes(a);
 }
 
 hipError_t hybrid_mfma_launch(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t aux) {
