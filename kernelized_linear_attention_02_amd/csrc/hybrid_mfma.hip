@@ -546,37 +546,32 @@ __global__ __launch_bounds__(kChainThreads) void hyb_chain_kernel(const ChainArg
 
 // ---------------------------------------------------------------- fold (off the chain)
 
-constexpr int kFoldRows = 256;  // pairs staged at a time
+constexpr int kFoldRows = 128;  // pairs staged at a time
 struct FoldLds {
   uint16_t kt[kFD][kFoldRows + 8];  // staged keys, transposed (bf16)
   uint16_t vt[kFD][kFoldRows + 8];  // staged values, transposed
   int32_t tok[kL * kPairMax];       // the batch's pairs, set after set
 };
-constexpr int kFoldWaves = 5;                                  // one k-step per wave
-constexpr int kFoldThreads = 64 * kFoldWaves;
-constexpr int kFoldWGs = (kFKS + kFoldWaves - 1) / kFoldWaves;  // 13 work-groups per head
+constexpr int kFoldWGs = (kFKS + kWaves - 1) / kWaves;  // work-groups per head, one k-step per wave
 
-// Work-group (bx, n): H += sum_j phi(k_j) v_j^T, s += sum_j phi(k_j) over the
-// pairs of `sets`, for k-step 5 bx + w of head n. Each wave's accumulators
-// are seeded with the stored float32 state, take the pairs 256 at a time
-// (staged in LDS, one row per thread), and go back to H, s and, as three
-// exact bf16 pieces, to the fragments of the next state version. Feature
-// products are float32 (from bf16 keys), split exactly into three bf16
-// pieces, and v is bf16, so every MFMA product is exact and the sums are
-// float32.
-__global__ __launch_bounds__(kFoldThreads) void hyb_fold_kernel(float* __restrict__ H, float* __restrict__ s,
-                                                            uint4* __restrict__ HF, const uint16_t* __restrict__ k,
-                                                            const uint16_t* __restrict__ v, int T,
-                                                            const int32_t* __restrict__ rej, int N,
-                                                            const PairSets sets) {
-  __shared__ __align__(16) FoldLds sh;
-  const int n = blockIdx.y;
+// Work-group (bx, n) of the fold: H += sum_j phi(k_j) v_j^T, s += sum_j phi(k_j)
+// over the pairs of `sets`, for k-step 4 bx + w of head n. Each wave's
+// accumulators are seeded with the stored float32 state, take the pairs 128
+// at a time (staged in LDS, two threads per row), and go back to H, s and,
+// as three exact bf16 pieces, to the fragments of the next state version.
+// Feature products are float32 (from bf16 keys), split exactly into three
+// bf16 pieces, and v is bf16, so every MFMA product is exact and the sums
+// are float32.
+__device__ __forceinline__ void fold_block(FoldLds& sh, int bx, int n, float* __restrict__ H,
+                                           float* __restrict__ s, uint4* __restrict__ HF,
+                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T,
+                                           const int32_t* __restrict__ rej, int N, const PairSets& sets) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
-  const int ks = blockIdx.x * kFoldWaves + w;
+  const int ks = bx * kWaves + w;
   const bool act = ks < kFKS;
   const int total = gather_pair_tokens(sets, rej, N, n, sh.tok);
   float* Hn = H + (size_t)n * kFPhi * kFD;
@@ -616,30 +611,29 @@ __global__ __launch_bounds__(kFoldThreads) void hyb_fold_kernel(float* __restric
   __syncthreads();
   for (int r0 = 0; r0 < total; r0 += kFoldRows) {
     const int R = min(kFoldRows, total - r0);
-    // row tid of the round: its key and value (zeros past the count); every
-    // thread takes part in the barriers
+    // row r of the round, half hf of its key and value (zeros past the count)
     {
-      uint4 ku[8], vu[8];
-      const bool ok = tid < R;  // R <= kFoldRows
-      const size_t row = ((size_t)n * T + (ok ? sh.tok[min(r0 + tid, kL * kPairMax - 1)] : 0)) * kFD;
+      const int r = tid >> 1, hf = tid & 1;
+      const bool ok = r < R;
+      const size_t row = ((size_t)n * T + (ok ? sh.tok[min(r0 + r, kL * kPairMax - 1)] : 0)) * kFD + 32 * hf;
+      uint4 ku[4], vu[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         ku[j] = ok ? reinterpret_cast<const uint4*>(k + row)[j] : make_uint4(0, 0, 0, 0);
         vu[j] = ok ? reinterpret_cast<const uint4*>(v + row)[j] : make_uint4(0, 0, 0, 0);
       }
       if (r0 > 0) __syncthreads();  // the previous round's reads are done
-      if (tid < kFoldRows) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t kw[4] = {ku[j].x, ku[j].y, ku[j].z, ku[j].w};
-          const uint32_t vw[4] = {vu[j].x, vu[j].y, vu[j].z, vu[j].w};
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kw[4] = {ku[j].x, ku[j].y, ku[j].z, ku[j].w};
+        const uint32_t vw[4] = {vu[j].x, vu[j].y, vu[j].z, vu[j].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sh.kt[8 * j + 2 * e][tid] = (uint16_t)(kw[e] & 0xFFFF);
-            sh.kt[8 * j + 2 * e + 1][tid] = (uint16_t)(kw[e] >> 16);
-            sh.vt[8 * j + 2 * e][tid] = (uint16_t)(vw[e] & 0xFFFF);
-            sh.vt[8 * j + 2 * e + 1][tid] = (uint16_t)(vw[e] >> 16);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int d = 32 * hf + 8 * j + 2 * e;
+          sh.kt[d][r] = (uint16_t)(kw[e] & 0xFFFF);
+          sh.kt[d + 1][r] = (uint16_t)(kw[e] >> 16);
+          sh.vt[d][r] = (uint16_t)(vw[e] & 0xFFFF);
+          sh.vt[d + 1][r] = (uint16_t)(vw[e] >> 16);
         }
       }
     }
@@ -972,30 +966,17 @@ struct ReadoutBlocks {
   const int32_t* cache[kRB];
 };
 
-__global__ __launch_bounds__(kRT) void hyb_readout_keys_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int T,
-    const ReadoutBlocks rb, const PairSets cf, const int32_t* __restrict__ rej, int N, float scale,
-    float* __restrict__ xp, int xq) {
-  __shared__ int32_t ptok[kL * kPairMax];
-  const int n = blockIdx.y;
-  const int z = blockIdx.z / kRNS;
-  const int sp = blockIdx.z % kRNS;
-  int t_begin = rb.t_begin[0], t_end = rb.t_end[0], f = rb.f[0], n_cache = rb.n_cache[0], ncf = rb.npairs[0],
-      qoff = rb.qoff[0];
-  const int32_t* cache = rb.cache[0];
-#pragma unroll
-  for (int u = 1; u < kRB; ++u)
-    if (z == u) {
-      t_begin = rb.t_begin[u];
-      t_end = rb.t_end[u];
-      f = rb.f[u];
-      n_cache = rb.n_cache[u];
-      ncf = rb.npairs[u];
-      qoff = rb.qoff[u];
-      cache = rb.cache[u];
-    }
-  const int t0 = t_begin + kRQ * blockIdx.x;
-  if (z >= rb.nb || t0 >= t_end) return;
+__device__ __forceinline__ void readout_keys_block(int32_t* ptok, int qblk, int n, int z, int sp,
+                                                   const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v, int T, const ReadoutBlocks& rb,
+                                                   const PairSets& cf, const int32_t* __restrict__ rej, int N,
+                                                   float scale, float* __restrict__ xp, int xq) {
+  if (z >= rb.nb) return;
+  const int t_begin = rb.t_begin[z], t_end = rb.t_end[z], f = rb.f[z], n_cache = rb.n_cache[z],
+            ncf = rb.npairs[z], qoff = rb.qoff[z];
+  const int32_t* cache = rb.cache[z];
+  const int t0 = t_begin + kRQ * qblk;
+  if (t0 >= t_end) return;
   const int tq_end = min(t_end, t0 + kRQ);  // queries [t0, tq_end)
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1190,25 +1171,14 @@ struct StateLds {
   float4 red[kRW][5][64];  // one token tile's partials from the four waves
 };
 
-__global__ __launch_bounds__(kRT, 2) void hyb_readout_state_kernel(const uint16_t* __restrict__ q, int T,
-                                                                   const uint4* __restrict__ HF,
-                                                                   const ReadoutBlocks rb, float* __restrict__ lp,
-                                                                   int xq) {
-  __shared__ __align__(16) StateLds sh;
-  const int n = blockIdx.y;
-  const int z = blockIdx.z;
-  const int g = blockIdx.x % kSR;
-  const int qblk = blockIdx.x / kSR;
-  int t_begin = rb.t_begin[0], t_end = rb.t_end[0], qoff = rb.qoff[0];
-#pragma unroll
-  for (int u = 1; u < kRB; ++u)
-    if (z == u) {
-      t_begin = rb.t_begin[u];
-      t_end = rb.t_end[u];
-      qoff = rb.qoff[u];
-    }
+__device__ __forceinline__ void readout_state_block(StateLds& sh, int qblk, int g, int n, int z,
+                                                    const uint16_t* __restrict__ q, int T,
+                                                    const uint4* __restrict__ HF, const ReadoutBlocks& rb,
+                                                    float* __restrict__ lp, int xq) {
+  if (z >= rb.nb) return;
+  const int t_begin = rb.t_begin[z], t_end = rb.t_end[z], qoff = rb.qoff[z];
   const int t0 = t_begin + kRQ * qblk;
-  if (z >= rb.nb || t0 >= t_end) return;
+  if (t0 >= t_end) return;
   const int tq_end = min(t_end, t0 + kRQ);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1325,18 +1295,12 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_combine_kernel(const flo
                                                                      int T, float eps) {
   const int n = blockIdx.y;
   const int z = blockIdx.z;
-  int t_begin = rb.t_begin[0], t_end = rb.t_end[0], qoff = rb.qoff[0];
-#pragma unroll
-  for (int u = 1; u < kRB; ++u)
-    if (z == u) {
-      t_begin = rb.t_begin[u];
-      t_end = rb.t_end[u];
-      qoff = rb.qoff[u];
-    }
+  if (z >= rb.nb) return;
+  const int t_begin = rb.t_begin[z], t_end = rb.t_end[z], qoff = rb.qoff[z];
   const int idx = blockIdx.x * kThreads + threadIdx.x;  // (query, column)
   const int r = idx >> 6, c = idx & 63;
   const int t = t_begin + r;
-  if (z >= rb.nb || t >= t_end) return;
+  if (t >= t_end) return;
   const size_t row = (size_t)n * xq + qoff + r;
   const float* xr = xp + row * kRNS * 66;
   float m = 0.0f;
@@ -1357,6 +1321,46 @@ __global__ __launch_bounds__(kThreads) void hyb_readout_combine_kernel(const flo
   num += e * lnum;
   den += e * lden;
   Elem<Tout>::store(o, ((size_t)n * T + t) * kFD + c, den != 0.0f ? num / den : 0.0f);
+}
+
+// Launches of the batch work: the fold (work-group (k-step block, head)),
+// then the readout key terms (work-group (query block, head, kRNS block +
+// split)) and state terms (work-group (kSR query block + range, head,
+// block)).
+__global__ __launch_bounds__(kThreads) void hyb_fold_kernel(float* __restrict__ H, float* __restrict__ s,
+                                                            uint4* __restrict__ HF, const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v, int T,
+                                                            const int32_t* __restrict__ rej, int N,
+                                                            const PairSets sets) {
+  __shared__ __align__(16) FoldLds sh;
+  fold_block(sh, blockIdx.x, blockIdx.y, H, s, HF, k, v, T, rej, N, sets);
+}
+
+struct ReadoutArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int T, N;
+  const uint4* HF;  // the state version read; NULL: the zero state
+  ReadoutBlocks rb;
+  PairSets cf;
+  const int32_t* rej;
+  float scale;
+  float* xp;
+  float* lp;
+  int xq;
+};
+
+__global__ __launch_bounds__(kRT) void hyb_readout_keys_kernel(const ReadoutArgs a) {
+  __shared__ int32_t ptok[kL * kPairMax];
+  readout_keys_block(ptok, blockIdx.x, blockIdx.y, blockIdx.z / kRNS, blockIdx.z % kRNS, a.q, a.k, a.v, a.T, a.rb,
+                     a.cf, a.rej, a.N, a.scale, a.xp, a.xq);
+}
+
+__global__ __launch_bounds__(kRT, 2) void hyb_readout_state_kernel(const ReadoutArgs a) {
+  __shared__ __align__(16) StateLds sh;
+  readout_state_block(sh, blockIdx.x / kSR, blockIdx.x % kSR, blockIdx.y, blockIdx.z, a.q, a.T, a.HF, a.rb, a.lp,
+                      a.xq);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1539,15 +1543,20 @@ hipError_t enqueue(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t au
   }
   const hipError_t loop_err = [&]() -> hipError_t {
     hipError_t e;
-    // readouts of blocks [i0, i1) (all served by refreshes of batch m, or by
-    // none when m < 0), against state version m - 1
-    auto readouts = [&](int i0, int i1, int m) -> hipError_t {
+    // Batch work of batch m (m < 0: the blocks before the first refresh):
+    // the fold of its pairs into state version m (m >= 0) and the readouts
+    // of blocks [i0, i1) against version m - 1 (the zero state for m < 1)
+    // and the batch's pairs up to each block's refresh, in launches of at
+    // most kRB blocks; `mid` issues the work that waits for the fold, before
+    // the first readouts.
+    auto batch_work = [&](int i0, int i1, int m, const auto& mid) -> hipError_t {
       hipError_t e;
       const uint4* HF = m >= 1 ? w.HF[(m - 1) % 2] : nullptr;
       const PairSets cf = m >= 0 ? sets_of(m * kL, std::min(nR, (m + 1) * kL)) : PairSets{};
-      for (int j0 = i0; j0 < i1; j0 += kRB) {
+      bool first = true;
+      for (int j0 = i0; first || j0 < i1; j0 += kRB) {
         ReadoutBlocks rb{};
-        rb.nb = std::min(kRB, i1 - j0);
+        rb.nb = std::max(0, std::min(kRB, i1 - j0));
         int qmax = 0;
         for (int z = 0; z < rb.nb; ++z) {
           const Block& bl = plan.B[j0 + z];
@@ -1563,15 +1572,37 @@ hipError_t enqueue(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t au
           rb.npairs[z] = np;
           qmax = std::max(qmax, bl.t1 - bl.t0);
         }
-        for (int z = rb.nb; z < kRB; ++z) rb.cache[z] = rb.cache[0];
+        for (int z = rb.nb; z < kRB; ++z) rb.cache[z] = cache_slot(-1);
         const int nqb = (qmax + kRQ - 1) / kRQ;
-        hipLaunchKernelGGL(hyb_readout_keys_kernel, dim3(nqb, N, kRNS * rb.nb), dim3(kRT), 0, sb, q, k, v, a.T, rb,
-                           cf, w.rej, N, a.scale, w.xp, kRB * a.refresh);
-        if (HF)
-          hipLaunchKernelGGL(hyb_readout_state_kernel, dim3(nqb * kSR, N, rb.nb), dim3(kRT), 0, sb, q, a.T, HF, rb,
-                             w.lp, kRB * a.refresh);
-        hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>), dim3((qmax * kFD + kThreads - 1) / kThreads, N, rb.nb),
-                           dim3(kThreads), 0, sb, w.xp, w.lp, HF ? kSR : 0, kRB * a.refresh, rb, o, a.T, a.eps);
+        if (first && m >= 0) {
+          hipLaunchKernelGGL(hyb_fold_kernel, dim3(kFoldWGs, N), dim3(kThreads), 0, sb, w.H, w.s, w.HF[m % 2], k, v,
+                             a.T, w.rej, N, cf);
+          KLA_CHECK();
+        }
+        if (first) KLA_TRY(mid());
+        first = false;
+        if (rb.nb > 0) {
+          ReadoutArgs ra{};
+          ra.q = q;
+          ra.k = k;
+          ra.v = v;
+          ra.T = a.T;
+          ra.N = N;
+          ra.HF = HF;
+          ra.rb = rb;
+          ra.cf = cf;
+          ra.rej = w.rej;
+          ra.scale = a.scale;
+          ra.xp = w.xp;
+          ra.lp = w.lp;
+          ra.xq = kRB * a.refresh;
+          hipLaunchKernelGGL(hyb_readout_keys_kernel, dim3(nqb, N, kRNS * rb.nb), dim3(kRT), 0, sb, ra);
+          if (HF) hipLaunchKernelGGL(hyb_readout_state_kernel, dim3(nqb * kSR, N, rb.nb), dim3(kRT), 0, sb, ra);
+        }
+        KLA_CHECK();
+        if (rb.nb > 0)
+          hipLaunchKernelGGL((hyb_readout_combine_kernel<Tout>), dim3((qmax * kFD + kThreads - 1) / kThreads, N, rb.nb),
+                             dim3(kThreads), 0, sb, w.xp, w.lp, HF ? kSR : 0, kRB * a.refresh, rb, o, a.T, a.eps);
         KLA_CHECK();
       }
       return hipSuccess;
@@ -1579,7 +1610,7 @@ hipError_t enqueue(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t au
     // blocks before the first refresh: the zero state
     int i_blk = 0;
     while (i_blk < nblocks && plan.B[i_blk].r < 0) ++i_blk;
-    KLA_TRY(readouts(0, i_blk, -1));
+    KLA_TRY(batch_work(0, i_blk, -1, [] { return hipSuccess; }));
     for (int m = 0; m < M; ++m) {
       const int r0 = m * kL;
       const int r1 = std::min(nR, r0 + kL);
@@ -1619,29 +1650,31 @@ hipError_t enqueue(const HybridArgs& a, void* ws, hipStream_t st, hipStream_t au
         KLA_TRY(hipEventRecord(ev.chain(), st));
         KLA_TRY(hipStreamWaitEvent(sb, ev.chain(), 0));
       }
-      hipLaunchKernelGGL(hyb_fold_kernel, dim3(kFoldWGs, N), dim3(kFoldThreads), 0, sb, w.H, w.s, w.HF[m % 2], k, v,
-                         a.T, w.rej, N, sets_of(r0, r1));
-      KLA_CHECK();
-      if (m + 2 < M) {
-        EvictBatch eb{};
-        const int s0 = (m + 2) * kL;
-        eb.nr = std::min(nR, s0 + kL) - s0;
-        int ev_max = 0;
-        for (int i = 0; i < eb.nr; ++i) {
-          eb.ev0[i] = plan.R[s0 + i].ev0;
-          eb.n_ev[i] = plan.R[s0 + i].n_ev;
-          ev_max = std::max(ev_max, eb.n_ev[i]);
+      // after the fold: the state sums of the tokens batch m + 2 evicts
+      auto sums = [&]() -> hipError_t {
+        hipError_t e;
+        if (m + 2 < M) {
+          EvictBatch eb{};
+          const int s0 = (m + 2) * kL;
+          eb.nr = std::min(nR, s0 + kL) - s0;
+          int ev_max = 0;
+          for (int i = 0; i < eb.nr; ++i) {
+            eb.ev0[i] = plan.R[s0 + i].ev0;
+            eb.n_ev[i] = plan.R[s0 + i].n_ev;
+            ev_max = std::max(ev_max, eb.n_ev[i]);
+          }
+          hipLaunchKernelGGL(hyb_state_sums_kernel, dim3(((ev_max + kScoreCand - 1) / kScoreCand) * kSZ, eb.nr, N),
+                             dim3(kThreads), 0, sb, w.HF[m % 2], k, a.T, eb, evs, w.part);
+          hipLaunchKernelGGL(hyb_sum_splits_kernel, dim3((kL * evs * 17 + kThreads - 1) / kThreads, N),
+                             dim3(kThreads), 0, sb, w.part, kL * evs, base_slot(m + 2), kL * evs);
+          KLA_CHECK();
         }
-        hipLaunchKernelGGL(hyb_state_sums_kernel, dim3(((ev_max + kScoreCand - 1) / kScoreCand) * kSZ, eb.nr, N),
-                           dim3(kThreads), 0, sb, w.HF[m % 2], k, a.T, eb, evs, w.part);
-        hipLaunchKernelGGL(hyb_sum_splits_kernel, dim3((kL * evs * 17 + kThreads - 1) / kThreads, N), dim3(kThreads),
-                           0, sb, w.part, kL * evs, base_slot(m + 2), kL * evs);
-        KLA_CHECK();
-      }
-      if (two) KLA_TRY(hipEventRecord(ev.sums(m), sb));
+        if (two) KLA_TRY(hipEventRecord(ev.sums(m), sb));
+        return hipSuccess;
+      };
       int i_end = i_blk;
       while (i_end < nblocks && plan.B[i_end].r < r1) ++i_end;
-      KLA_TRY(readouts(i_blk, i_end, m));
+      KLA_TRY(batch_work(i_blk, i_end, m, sums));
       i_blk = i_end;
     }
     return hipSuccess;
