@@ -162,7 +162,9 @@ def bench_prefill(torch, K, S, name, steps, warmup, factors=1, factor_kind="conc
         roofline=dict(bound="mfma" if mfma else "alu", achieved=achieved, peak=peak, unit="TFLOP/s",
                       frac=achieved / peak, kernel_ms=kern_ms,
                       traffic=traffic,
-                      kernel="prefill state/readout", flops_per_launch=kern_flops),
+                      kernel="prefill state/readout", flops_per_launch=kern_flops,
+                      # the whole call (staging, state kernel, intra-chunk finish) against the same peak
+                      call_frac=call_flops / (step_ms * 1e-3) / 1e12 / peak),
         arith="bf16" if mfma else "f32",
     )
 
