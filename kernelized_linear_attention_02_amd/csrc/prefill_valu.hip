@@ -21,9 +21,13 @@
 // too large for one CU at d_qk = 64, so every head is split into S feature
 // slices of at most 256 features; a work-group owns one (slice, head) pair,
 // keeps its slice of H and s in registers and walks the chunks in order
-// (the prefix sum is the register-resident running state). The readout of a
-// slice is a partial numerator/denominator per token; a second kernel adds
-// the S partials to the exact intra-chunk term and divides.
+// (the prefix sum is the register-resident running state). Tokens go in
+// tiles of 16: each tile's features are formed once into LDS (thread f forms
+// feature f for every token), laid out so that a thread's own features are
+// contiguous, and the readout and update read them as broadcast 16-byte
+// loads; the next tile's rows are loaded while the current one is used. The
+// readout of a slice is a partial numerator/denominator per token; a second
+// kernel adds the S partials to the exact intra-chunk term and divides.
 #include <algorithm>
 
 #include "kla_device.hpp"
@@ -66,6 +70,7 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
   constexpr int G = kThreads / DV;    // feature groups
   constexpr int J = kMaxSlice / G;    // features per thread
   constexpr int W = kThreads / 64;    // waves
+  static_assert(J % 4 == 0, "features per thread in float4 groups");
 
   const int slice = blockIdx.x;
   const int n = blockIdx.y;
@@ -78,6 +83,9 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
   __shared__ uint16_t tab[kMaxSlice];
   __shared__ float xs[kTok][DQK + 1];
   __shared__ float vs[kTok][DV];
+  // features of a token tile, formed once per token: feature fl = g + G j of
+  // the slice at ph[r][g][j], so a thread's J features are contiguous
+  __shared__ __align__(16) float ph[kTok][G][J];
   __shared__ float red[kTok][G][DV];
   __shared__ float rden[kTok][W];
 
@@ -95,69 +103,136 @@ __global__ __launch_bounds__(kThreads) void prefill_slice_kernel(
 
   const size_t bqk = (size_t)n * T * DQK;
   const size_t bv = (size_t)n * T * DV;
+  // features of the tile in xs (zero past the slice): thread tid forms feature tid for every token
+  auto form = [&]() {
+    const bool ok = tid < fcount;
+    const uint16_t ab = ok ? tab[tid] : 0;
+    const int gg = tid % G, jj = tid / G;
+#pragma unroll 4
+    for (int r = 0; r < kTok; ++r) ph[r][gg][jj] = ok ? factor_phi(xs[r], ab, kind, factors, fp) : 0.0f;
+  };
+  // this thread's features fill jused of its J slots; later float4 groups are skipped
+  const int jused = (fcount - g + G - 1) / G;
 
-  for (int c0 = 0; c0 < T; c0 += chunk) {
-    const int L = min(chunk, T - c0);
-    if (part) {
-      // readout of the state at the chunk start, one token tile at a time
-      for (int t0 = 0; t0 < L; t0 += kTok) {
-        const int nb = min(kTok, L - t0);
-        for (int i = tid; i < kTok * DQK; i += kThreads) {
-          const int r = i / DQK, d = i % DQK;
-          xs[r][d] = r < nb ? Elem<Tin>::load(q, bqk + (size_t)(c0 + t0 + r) * DQK + d) : 0.0f;
-        }
-        __syncthreads();
-        for (int r = 0; r < kTok; ++r) {
-          float acc = 0.0f;
+  // The tiles in order: per chunk, the query tiles of the readout (when
+  // outputs are wanted), then the key/value tiles of the update. The next
+  // tile's rows are loaded into registers while the current one is used.
+  constexpr int kPX = kTok * DQK / kThreads;
+  constexpr int kPV = kTok * DV / kThreads;
+  static_assert(kPX * kThreads == kTok * DQK && kPV * kThreads == kTok * DV, "tile loads");
+  struct Tile {
+    int c0, t0, upd;  // upd: 0 readout (q), 1 update (k, v)
+  };
+  auto first_tile = [&]() { return Tile{0, 0, part ? 0 : 1}; };
+  auto next_tile = [&](Tile t) {
+    const int L = min(chunk, T - t.c0);
+    if (t.t0 + kTok < L) return Tile{t.c0, t.t0 + kTok, t.upd};
+    if (!t.upd) return Tile{t.c0, 0, 1};
+    return Tile{t.c0 + chunk, 0, part ? 0 : 1};
+  };
+  float px[kPX], pv[kPV];
+  auto fetch = [&](Tile t) {
+    const int L = t.c0 < T ? min(chunk, T - t.c0) : 0;
+    const int nb = max(0, min(kTok, L - t.t0));
+    const Tin* src = t.upd ? k : q;
 #pragma unroll
-          for (int j = 0; j < J; ++j) {
-            const int fl = g + G * j;
-            if (fl < fcount) acc += factor_phi(xs[r], tab[fl], kind, factors, fp) * h[j];
-          }
-          red[r][g][c] = acc;
-          float dd = tid < fcount ? factor_phi(xs[r], tab[tid], kind, factors, fp) * sm : 0.0f;
-          dd = wave_sum(dd);
-          if ((tid & 63) == 0) rden[r][tid >> 6] = dd;
-        }
-        __syncthreads();
-        for (int i = tid; i < nb * (DV + 1); i += kThreads) {
-          const int r = i / (DV + 1), cc = i % (DV + 1);
-          float sum = 0.0f;
-          if (cc < DV) {
+    for (int e = 0; e < kPX; ++e) {
+      const int i = tid + e * kThreads;
+      const int r = i / DQK, d = i % DQK;
+      px[e] = r < nb ? Elem<Tin>::load(src, bqk + (size_t)(t.c0 + t.t0 + r) * DQK + d) : 0.0f;
+    }
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg) sum += red[r][gg][cc];
-          } else {
+    for (int e = 0; e < kPV; ++e) {
+      const int i = tid + e * kThreads;
+      const int r = i / DV, d = i % DV;
+      pv[e] = (t.upd && r < nb) ? Elem<Tin>::load(v, bv + (size_t)(t.c0 + t.t0 + r) * DV + d) : 0.0f;
+    }
+  };
+  Tile cur = first_tile();
+  fetch(cur);
+  while (cur.c0 < T) {
+    const int L = min(chunk, T - cur.c0);
+    const int nb = min(kTok, L - cur.t0);
 #pragma unroll
-            for (int w = 0; w < W; ++w) sum += rden[r][w];
-          }
-          part[(((size_t)n * S + slice) * T + c0 + t0 + r) * (DV + 1) + cc] = sum;
-        }
-        __syncthreads();
+    for (int e = 0; e < kPX; ++e) {
+      const int i = tid + e * kThreads;
+      xs[i / DQK][i % DQK] = px[e];
+    }
+    if (cur.upd) {
+#pragma unroll
+      for (int e = 0; e < kPV; ++e) {
+        const int i = tid + e * kThreads;
+        vs[i / DV][i % DV] = pv[e];
       }
     }
-    // state update with the whole chunk
-    for (int t0 = 0; t0 < L; t0 += kTok) {
-      const int nb = min(kTok, L - t0);
-      for (int i = tid; i < kTok * DQK; i += kThreads) {
-        const int r = i / DQK, d = i % DQK;
-        xs[r][d] = r < nb ? Elem<Tin>::load(k, bqk + (size_t)(c0 + t0 + r) * DQK + d) : 0.0f;
+    const Tile nxt = next_tile(cur);
+    if (nxt.c0 < T) fetch(nxt);
+    __syncthreads();
+    form();
+    __syncthreads();
+    if (!cur.upd) {
+      // readout of the state at the chunk start
+#pragma unroll 1
+      for (int r = 0; r < kTok; ++r) {
+        const float4* pr = reinterpret_cast<const float4*>(ph[r][g]);
+        float acc = 0.0f;
+#pragma unroll
+        for (int j4 = 0; j4 < J / 4; ++j4) {
+          if (4 * j4 < jused) {
+            const float4 x = pr[j4];
+            acc += x.x * h[4 * j4] + x.y * h[4 * j4 + 1] + x.z * h[4 * j4 + 2] + x.w * h[4 * j4 + 3];
+          }
+        }
+        red[r][g][c] = acc;
       }
-      for (int i = tid; i < kTok * DV; i += kThreads) {
-        const int r = i / DV, d = i % DV;
-        vs[r][d] = r < nb ? Elem<Tin>::load(v, bv + (size_t)(c0 + t0 + r) * DV + d) : 0.0f;
+      // denominators: every token's product first, then the wave sums side by side
+      {
+        float dd[kTok];
+#pragma unroll
+        for (int r = 0; r < kTok; ++r) dd[r] = tid < fcount ? ph[r][tid % G][tid / G] * sm : 0.0f;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+          for (int r = 0; r < kTok; ++r) dd[r] += __shfl_xor(dd[r], off, 64);
+        if ((tid & 63) == 0) {
+#pragma unroll
+          for (int r = 0; r < kTok; ++r) rden[r][tid >> 6] = dd[r];
+        }
       }
       __syncthreads();
+      for (int i = tid; i < nb * (DV + 1); i += kThreads) {
+        const int r = i / (DV + 1), cc = i % (DV + 1);
+        float sum = 0.0f;
+        if (cc < DV) {
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) sum += red[r][gg][cc];
+        } else {
+#pragma unroll
+          for (int w = 0; w < W; ++w) sum += rden[r][w];
+        }
+        part[(((size_t)n * S + slice) * T + cur.c0 + cur.t0 + r) * (DV + 1) + cc] = sum;
+      }
+    } else {
+      // state update with the tile's keys and values
+#pragma unroll 1
       for (int r = 0; r < nb; ++r) {
         const float vv = vs[r][c];
+        const float4* pr = reinterpret_cast<const float4*>(ph[r][g]);
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-          const int fl = g + G * j;
-          if (fl < fcount) h[j] += factor_phi(xs[r], tab[fl], kind, factors, fp) * vv;
+        for (int j4 = 0; j4 < J / 4; ++j4) {
+          if (4 * j4 < jused) {
+            const float4 x = pr[j4];
+            h[4 * j4] += x.x * vv;
+            h[4 * j4 + 1] += x.y * vv;
+            h[4 * j4 + 2] += x.z * vv;
+            h[4 * j4 + 3] += x.w * vv;
+          }
         }
-        if (tid < fcount) sm += factor_phi(xs[r], tab[tid], kind, factors, fp);
+        if (tid < fcount) sm += ph[r][tid % G][tid / G];
       }
-      __syncthreads();
     }
+    __syncthreads();
+    cur = nxt;
   }
   if (HT) {
 #pragma unroll
@@ -271,6 +346,9 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(
 // Feature slices per head: enough for the features (at most kMaxSlice each)
 // and, for small states or few heads, enough work-groups to fill the GPU
 // (slices of at least 32 features).
+// Slices per head: at most 256 features each, and more (down to 32 each)
+// until the launch has about one work-group per CU (more slices repeat the
+// per-tile work of every work-group and measured slower).
 int slices_for(int D, int N) {
   const int s0 = (D + kMaxSlice - 1) / kMaxSlice;
   const int fill = (256 + N - 1) / N;
