@@ -79,7 +79,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 6
+#define KLA_ABI_VERSION 7
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -396,9 +396,20 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  *                n = min(lambda, max(0, t - W - 1)) before the call and
  *                min(lambda, max(0, t - W)) after it; other rows are unused.
  *                May be NULL when lambda = 0.
+ *   cache_sums : [N, lambda, d_v + 4]: for cached row i, the sums of its key
+ *                against the linear state (pending pair included),
+ *                (phi(k_i)^T H', phi(k_i)^T s') with H' = H + phi(pend_k)
+ *                pend_v^T, s' = s + phi(pend_k), in columns 0 .. d_v - 1 and
+ *                d_v (the last three of a row are padding, for 16-byte rows). Each call keeps them: a
+ *                fold of pair r adds (k_i . k_r)^2 [v_r | 1] (KATA page §2.2:
+ *                phi(x) . phi(y) = (x . y)^2), and a pair entering the cache
+ *                takes its sums from the call's pass over H. The refresh
+ *                scores candidates from them. Zero for a zero state; may be
+ *                NULL when lambda = 0.
  * To continue from a prefill of t tokens, the caller fills the window rows of
  * tokens max(0, t - W - 1) .. t - 1, the cache rows and the state the prefill
- * left, with a zero pending pair.
+ * left, with a zero pending pair, then calls kla_hybrid_decode_prime to
+ * compute cache_sums.
  *
  *   q, k : [N, d_qk]; v : [N, d_v]; in_dtype.   o : [N, d_v], out_dtype.
  *   rejected : [N] int32, or NULL: the token id folded by this call (now
@@ -406,9 +417,7 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  *   ws : workspace of kla_hybrid_decode_workspace_size bytes.
  * Every state pointer must be 16-byte aligned.
  * Supported: d_qk, d_v in {16, 32, 64}; refresh = 1; window >= 0;
- * 0 <= cache_size <= 255; t >= 0; softmax_scale finite. With
- * d_qk = d_v = 64 and 1 <= cache_size <= 128 the scoring runs on the matrix
- * cores in the same pass over H as the fold and the readout.
+ * 0 <= cache_size <= 255; t >= 0; softmax_scale finite.
  * ------------------------------------------------------------------------ */
 typedef struct {
   float* H;
@@ -420,6 +429,7 @@ typedef struct {
   int32_t* cache_ids;
   float* pend_k;
   float* pend_v;
+  float* cache_sums;
 } kla_hybrid_state_t;
 
 KLA_API kla_status_t kla_hybrid_decode_workspace_size(int N, int d_qk, int d_v,
@@ -450,9 +460,18 @@ KLA_API kla_status_t kla_hybrid_decode_step_static(int N, int d_qk, int d_v, flo
                                            void* o, kla_dtype_t out_dtype, int32_t* rejected,
                                            kla_stream_t stream);
 /* Folds the pending pair into (H, s) and zeroes it (H, s, pend_k, pend_v of
- * `state` are used). */
+ * `state` are used). The linear state H + phi(pend_k) pend_v^T does not
+ * change, so cache_sums stay valid. */
 KLA_API kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_state_t* state,
                                      kla_stream_t stream);
+/* kla_hybrid_decode_prime - computes cache_sums for the cached rows
+ * 0 .. min(lambda, max(0, t - W - 1)) - 1 of a state about to take token t
+ * (H, s, pend_k, pend_v, cache_k and cache_sums of `state` are used), in
+ * float32: sum_f phi_f(k_i) H_f + (k_i . pend_k)^2 pend_v and the same for s.
+ * For a state filled from elsewhere (a prefill); a state that only ever went
+ * through kla_hybrid_decode_step keeps its sums itself. */
+KLA_API kla_status_t kla_hybrid_decode_prime(int N, int d_qk, int d_v, const kla_hybrid_cfg_t* cfg, int t,
+                                     const kla_hybrid_state_t* state, kla_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing without a profiler. While enabled on the calling thread,

@@ -27,7 +27,7 @@ EXPORTS = (
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill", "kla_hybrid_prefill_streams",
     "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step", "kla_hybrid_decode_flush",
-    "kla_hybrid_decode_static_limit", "kla_hybrid_decode_step_static",
+    "kla_hybrid_decode_prime", "kla_hybrid_decode_static_limit", "kla_hybrid_decode_step_static",
     "kla_profile_enable", "kla_profile_read",
 )
 
@@ -61,7 +61,8 @@ class HybridState(ctypes.Structure):
     _fields_ = [("H", ctypes.c_void_p), ("s", ctypes.c_void_p),
                 ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
                 ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
-                ("cache_ids", ctypes.c_void_p), ("pend_k", ctypes.c_void_p), ("pend_v", ctypes.c_void_p)]
+                ("cache_ids", ctypes.c_void_p), ("pend_k", ctypes.c_void_p), ("pend_v", ctypes.c_void_p),
+                ("cache_sums", ctypes.c_void_p)]
 
 
 _lib = None
@@ -106,6 +107,7 @@ def load_library(path: str = LIB_PATH):
         "kla_hybrid_decode_workspace_size": (i, [i, i, i, hcp, szp]),
         "kla_hybrid_decode_step": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp, sz, vp]),
         "kla_hybrid_decode_flush": (i, [i, i, i, hsp, vp]),
+        "kla_hybrid_decode_prime": (i, [i, i, i, hcp, i, hsp, vp]),
         "kla_hybrid_decode_static_limit": (sz, []),
         "kla_hybrid_decode_step_static": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp]),
         "kla_profile_enable": (i, [i]),
@@ -458,8 +460,9 @@ def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: in
     """Zeroed token-by-token hybrid state for N head-states: a dict of device
     tensors H [N, D, d_v], s [N, D], win_k [N, window+1, d_qk],
     win_v [N, window+1, d_v], cache_k [N, cache_size, d_qk],
-    cache_v [N, cache_size, d_v], pend_k [N, d_qk], pend_v [N, d_v] (float32)
-    and cache_ids [N, cache_size] int32."""
+    cache_v [N, cache_size, d_v], pend_k [N, d_qk], pend_v [N, d_v],
+    cache_sums [N, cache_size, d_v + 4] (float32; numerators, denominator,
+    padding) and cache_ids [N, cache_size] int32."""
     torch = _torch()
     D = phi_dim(d_qk)
     f32 = dict(dtype=torch.float32, device=device)
@@ -468,10 +471,11 @@ def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: in
         win_k=torch.zeros((N, window + 1, d_qk), **f32), win_v=torch.zeros((N, window + 1, d_v), **f32),
         cache_k=torch.zeros((N, cache_size, d_qk), **f32), cache_v=torch.zeros((N, cache_size, d_v), **f32),
         cache_ids=torch.full((N, cache_size), -1, dtype=torch.int32, device=device),
-        pend_k=torch.zeros((N, d_qk), **f32), pend_v=torch.zeros((N, d_v), **f32))
+        pend_k=torch.zeros((N, d_qk), **f32), pend_v=torch.zeros((N, d_v), **f32),
+        cache_sums=torch.zeros((N, cache_size, d_v + 4), **f32))
 
 
-_STATE_FIELDS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids", "pend_k", "pend_v")
+_STATE_FIELDS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids", "pend_k", "pend_v", "cache_sums")
 
 
 def _hybrid_state_struct(state):
@@ -559,6 +563,19 @@ def hybrid_decode_flush(state):
     N, dqk = state["pend_k"].shape
     dv = state["pend_v"].shape[-1]
     check(lib.kla_hybrid_decode_flush(N, dqk, dv, ctypes.byref(st), _stream(state["H"].device)))
+
+
+def hybrid_decode_prime(state, t: int, window: int, cache_size: int):
+    """Compute state['cache_sums'] from H, s, the pending pair and the cached
+    keys, for a state filled from elsewhere (a prefill) that takes token t
+    next."""
+    lib = load_library()
+    st = _hybrid_state_struct(state)
+    N, dqk = state["pend_k"].shape
+    dv = state["pend_v"].shape[-1]
+    cfg = HybridCfg(int(window), int(cache_size), 1, 1.0)
+    check(lib.kla_hybrid_decode_prime(N, dqk, dv, ctypes.byref(cfg), int(t), ctypes.byref(st),
+                                      _stream(state["H"].device)))
 
 
 def profile_enable(on: bool = True):

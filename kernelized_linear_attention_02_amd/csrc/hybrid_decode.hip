@@ -24,25 +24,30 @@
 // H is then read and written once per token. A zero pending pair folds
 // nothing (phi(0) = 0).
 //
+// Carried sums: every cached pair i keeps its sums against the linear state
+// (pending pair included), (phi(k_i)^T H, phi(k_i)^T s), in the caller's
+// state. A fold of pair r changes them by the same closed form,
+// (k_i . k_r)^2 [v_r | 1], so the candidates of a refresh are scored from
+// their sums; only the evicted pair, new to the cache, takes its sums from
+// the pass over H.
+//
 // Kernels (all counts are known on the host from t):
-//   state pass  d_qk = d_v = 64, cache <= 128: one work-group per
-//               head-state streams H once: pending fold, linear readout of
-//               q, and the self-recall numerators of the cache candidates on
-//               the bf16 matrix cores (float32-faithful split products) and
-//               of the evicted pair on the vector units;
-//   other shapes: a fold + readout pass over H, then the shared float32
-//               scoring block over the cache + evicted candidates;
-//   mix         per head-state: the rejected pair (lowest (score, -id)), cache
-//               update, the closed-form fold term, the window and cache
-//               softmax (online maximum), the joint division, the window
-//               insert, and the new pending pair.
+//   state pass  one work-group per head-state streams H once: pending fold,
+//               linear readouts of q and of the evicted key (d_qk = d_v =
+//               64: 72 tiles in block order; other shapes: the generic pass);
+//   mix         per head-state: the candidates' scores from their sums, the
+//               rejected pair (lowest (score, -id)), the closed-form fold
+//               term for the kept pairs' sums and for the readout, the cache
+//               update, the window and cache softmax (online maximum), the
+//               joint division, the window insert, and the new pending pair;
+//   prime       the cached pairs' sums from (H, s) and the pending pair, for
+//               a state filled from elsewhere.
 #include <algorithm>
 #include <mutex>
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
 #include "mfma_bf16.hpp"
-#include "sre_block.hpp"
 
 namespace kla {
 namespace {
@@ -77,25 +82,32 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 
 // One work-group per head-state: the pending pair is folded into (H, s)
 // and cleared; with READ, lin[n] = (phi(q)^T H, phi(q)^T s) of the folded
-// state (denominator without eps) at lin[n * lstride + 0 .. d_v].
+// state (denominator without eps) at lin[n * lstride + 0 .. d_v], and, when
+// a token leaves the window (ek: its key row), the same readout of its key
+// at esum[n * lstride + ...].
 template <int DQK, int DV, typename Tin, bool READ>
 __global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
     float* __restrict__ H, float* __restrict__ s, float* __restrict__ pend_k, float* __restrict__ pend_v,
-    const Tin* __restrict__ q, float* __restrict__ lin, int lstride) {
+    const Tin* __restrict__ q, float* __restrict__ lin, int lstride, const float* __restrict__ win_k, int wrows,
+    int slot, bool evict, float* __restrict__ esum) {
   constexpr int D = phi_dim(DQK);
   constexpr int G = kThreads / DV;
   __shared__ float pq[READ ? D : 1];
+  __shared__ float pe[READ ? D : 1];
   __shared__ float pk[D];
-  __shared__ float qv[DQK], kv[DQK], vv[DV];
+  __shared__ float qv[DQK], ev[DQK], kv[DQK], vv[DV];
   __shared__ uint16_t tab[D];
   __shared__ float num[G][DV];
+  __shared__ float enm[G][DV];
   __shared__ float red[kWaves];
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int c = tid % DV;
   const int g = tid / DV;
+  const bool ev_on = READ && evict;
   for (int d = tid; d < DQK; d += kThreads) {
     if (READ) qv[d] = Elem<Tin>::load(q, (size_t)n * DQK + d);
+    if (ev_on) ev[d] = win_k[((size_t)n * wrows + slot) * DQK + d];
     kv[d] = pend_k[(size_t)n * DQK + d];
   }
   for (int d = tid; d < DV; d += kThreads) vv[d] = pend_v[(size_t)n * DV + d];
@@ -104,68 +116,56 @@ __global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
   for (int f = tid; f < D; f += kThreads) {
     pk[f] = phi_of(kv, tab[f]);
     if (READ) pq[f] = phi_of(qv, tab[f]);
+    if (ev_on) pe[f] = phi_of(ev, tab[f]);
   }
   __syncthreads();
   float* Hn = H + (size_t)n * D * DV;
   float* sn = s + (size_t)n * D;
   const float vc = vv[c];
-  float acc = 0.0f;
+  float acc = 0.0f, eacc = 0.0f;
 #pragma unroll 8
   for (int f = g; f < D; f += G) {
     const float h = Hn[(size_t)f * DV + c] + pk[f] * vc;
     Hn[(size_t)f * DV + c] = h;
     if (READ) acc += pq[f] * h;
+    if (ev_on) eacc += pe[f] * h;
   }
-  float den = 0.0f;
+  float den = 0.0f, eden = 0.0f;
   for (int f = tid; f < D; f += kThreads) {
     const float x = sn[f] + pk[f];
     sn[f] = x;
     if (READ) den += pq[f] * x;
+    if (ev_on) eden += pe[f] * x;
   }
   if (READ) {
     num[g][c] = acc;
-    const float dsum = block_sum(den, red);  // its barriers also publish num
+    if (ev_on) enm[g][c] = eacc;
+    const float dsum = block_sum(den, red);  // its barriers also publish num and enm
+    const float esm = ev_on ? block_sum(eden, red) : 0.0f;
     if (g == 0) {
-      float x = 0.0f;
+      float x = 0.0f, y = 0.0f;
 #pragma unroll
-      for (int i = 0; i < G; ++i) x += num[i][c];
+      for (int i = 0; i < G; ++i) {
+        x += num[i][c];
+        if (ev_on) y += enm[i][c];
+      }
       lin[(size_t)n * lstride + c] = x;
+      if (ev_on) esum[(size_t)n * lstride + c] = y;
     }
-    if (tid == 0) lin[(size_t)n * lstride + DV] = dsum;
+    if (tid == 0) {
+      lin[(size_t)n * lstride + DV] = dsum;
+      if (ev_on) esum[(size_t)n * lstride + DV] = esm;
+    }
   }
   // every read of the pending pair went through LDS before the first barrier
   for (int d = tid; d < DQK; d += kThreads) pend_k[(size_t)n * DQK + d] = 0.0f;
   for (int d = tid; d < DV; d += kThreads) pend_v[(size_t)n * DV + d] = 0.0f;
 }
 
-// Self-recall error of the lambda + 1 candidates (cache rows, then the
-// evicted window row) against the folded state, in float32.
-template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads) void hdec_score_kernel(
-    const float* __restrict__ H, const float* __restrict__ s, const float* __restrict__ cache_k,
-    const float* __restrict__ cache_v, const float* __restrict__ win_k, const float* __restrict__ win_v,
-    int lambda, int wrows, int slot, float* __restrict__ scores, int sstride, float eps) {
-  constexpr int D = phi_dim(DQK);
-  __shared__ SreShared<DQK, DV> sh;
-  const int n = blockIdx.y;
-  auto load_k = [&](int c, int d) {
-    return c < lambda ? cache_k[((size_t)n * lambda + c) * DQK + d]
-                      : win_k[((size_t)n * wrows + slot) * DQK + d];
-  };
-  auto load_v = [&](int c, int d) {
-    return c < lambda ? cache_v[((size_t)n * lambda + c) * DV + d]
-                      : win_v[((size_t)n * wrows + slot) * DV + d];
-  };
-  sre_block<DQK, DV>(sh, H + (size_t)n * D * DV, s + (size_t)n * D, blockIdx.x * 64, lambda + 1, load_k,
-                     load_v, scores + (size_t)n * sstride, eps);
-}
-
 // ---------------------------------------------------------------- matrix-core state pass
 
 constexpr int kFD = 64;
 constexpr int kFDim = kFD * (kFD + 1) / 2;  // 2080
-constexpr int kFMaxCache = 128;
-constexpr int kKS = kFD + 4;                // padded LDS key rows (16-byte aligned)
 // Feature order of the pass: 8 x 8 blocks (A, B), A <= B, of the pairs
 // (a, b), a <= b; a block is two MFMA k-steps ("tiles") of 32 features. In
 // tile t of block (A, B) the lane quarter q4 takes a = 8A + 4t + q4 and
@@ -193,11 +193,6 @@ struct StateLds {
   alignas(16) float pk[kFD];
   alignas(16) float pv[kFD];
   alignas(16) float ek[kFD];
-  union {
-    float ck[kFMaxCache][kKS];                // cache keys (tile loop)
-    float4 red[kFMaxCache / 16][4][64];       // numerator partials (after it)
-  };
-  float den[kWaves][kFMaxCache];
   float onum[kWaves][kFD];
   float enm[kWaves][kFD];
   float oden[kWaves];
@@ -236,21 +231,14 @@ __device__ __forceinline__ void phi8(const float* x, const TileCoords& tc, float
 
 // One work-group per head-state; its four waves take the 72 tiles in turn.
 // A lane (l16, q4) holds its eight state rows of a tile at columns
-// 4*l16 .. 4*l16+3 (16-byte loads), adds the pending fold, writes them back
-// and accumulates the float32 readouts of q and of the evicted key. The same
-// registers are the B operand of the cache candidates' numerators
-// phi(K_c) H on the matrix cores: the state is split exactly into three bf16
-// pieces, the candidate features into two, and the product is
-// p0 (h0 + h1 + h2) + p1 h0 with float32 accumulation. MT 16-row candidate
-// blocks (0: no scoring in this call).
-template <int MT, typename Tin>
-__global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
+// 4*l16 .. 4*l16+3 (16-byte loads, the next tile's in flight), adds the
+// pending fold, writes them back and accumulates the float32 readouts of q
+// and, when a token leaves the window, of its key.
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void hdec_state_kernel(
     float* __restrict__ H, float* __restrict__ s, const float* __restrict__ pend_k,
-    const float* __restrict__ pend_v, const Tin* __restrict__ q, const float* __restrict__ cache_k,
-    const float* __restrict__ cache_v, const float* __restrict__ win_k, const float* __restrict__ win_v,
-    int wrows, int slot, int lambda, float* __restrict__ scores, int sstride, float* __restrict__ lin,
-    int lstride, float eps) {
-  constexpr int MTA = MT > 0 ? MT : 1;
+    const float* __restrict__ pend_v, const Tin* __restrict__ q, const float* __restrict__ win_k, int wrows,
+    int slot, bool evict, float* __restrict__ lin, float* __restrict__ esum, int lstride) {
   __shared__ __align__(16) StateLds sh;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
@@ -282,28 +270,11 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
     sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kFD + tid);
     sh.pk[tid] = pend_k[(size_t)n * kFD + tid];
     sh.pv[tid] = pend_v[(size_t)n * kFD + tid];
-    if (MT > 0) sh.ek[tid] = win_k[((size_t)n * wrows + slot) * kFD + tid];
-  }
-  if (MT > 0) {
-    for (int i = tid; i < 16 * MT * (kFD / 4); i += kThreads) {
-      const int c = i / (kFD / 4);
-      const int d4 = i % (kFD / 4);
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < lambda) x = *reinterpret_cast<const float4*>(cache_k + ((size_t)n * lambda + c) * kFD + 4 * d4);
-      *reinterpret_cast<float4*>(&sh.ck[c][4 * d4]) = x;
-    }
+    sh.ek[tid] = evict ? win_k[((size_t)n * wrows + slot) * kFD + tid] : 0.0f;
   }
   __syncthreads();
 
   const float4 v4 = *reinterpret_cast<const float4*>(&sh.pv[4 * l16]);
-  f32x4 acc[MTA][4];
-#pragma unroll
-  for (int mt = 0; mt < MTA; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dacc[MTA];
-#pragma unroll
-  for (int mt = 0; mt < MTA; ++mt) dacc[mt] = 0.0f;
   float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 eacc = make_float4(0.f, 0.f, 0.f, 0.f);
   float oden = 0.0f, eden = 0.0f;
@@ -322,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
     float pk[8], pq[8], pe[8];
     phi8(sh.pk, tc, pk);
     phi8(sh.qs, tc, pq);
-    if (MT > 0) phi8(sh.ek, tc, pe);
+    phi8(sh.ek, tc, pe);  // zero without an evicted key
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= tc.jmin) {
@@ -338,13 +309,11 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
       oacc.z += pq[j] * h[j].z;
       oacc.w += pq[j] * h[j].w;
       oden += pq[j] * sj[j];
-      if (MT > 0) {
-        eacc.x += pe[j] * h[j].x;
-        eacc.y += pe[j] * h[j].y;
-        eacc.z += pe[j] * h[j].z;
-        eacc.w += pe[j] * h[j].w;
-        eden += pe[j] * sj[j];
-      }
+      eacc.x += pe[j] * h[j].x;
+      eacc.y += pe[j] * h[j].y;
+      eacc.z += pe[j] * h[j].z;
+      eacc.w += pe[j] * h[j].w;
+      eden += pe[j] * sj[j];
     }
     // lane l16 = j of each quarter writes s of slot j: a contiguous 32-byte run
     {
@@ -352,35 +321,6 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
 #pragma unroll
       for (int j = 1; j < 8; ++j) x = l16 == j ? sj[j] : x;
       if (l16 < 8 && l16 >= tc.jmin) sn[tc.f0 + l16] = x;
-    }
-
-    if (MT > 0) {
-      bf16x8 ahi[MTA], alo[MTA];
-#pragma unroll
-      for (int mt = 0; mt < MTA; ++mt) {
-        float p[8];
-        phi8(sh.ck[16 * mt + l16], tc, p);
-        float dd = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dd += p[j] * sj[j];
-        dacc[mt] += dd;
-        split2(p, ahi[mt], alo[mt]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
-        bf16x8 b0, b1, b2;
-        split3(x, b0, b1, b2);
-#pragma unroll
-        for (int mt = 0; mt < MTA; ++mt) {
-          acc[mt][nt] = mfma16x16x32(ahi[mt], b0, acc[mt][nt]);
-          acc[mt][nt] = mfma16x16x32(ahi[mt], b1, acc[mt][nt]);
-          acc[mt][nt] = mfma16x16x32(ahi[mt], b2, acc[mt][nt]);
-          acc[mt][nt] = mfma16x16x32(alo[mt], b0, acc[mt][nt]);
-        }
-      }
     }
     if (more) {
 #pragma unroll
@@ -392,326 +332,8 @@ __global__ __launch_bounds__(kThreads, 1) void hdec_state_kernel(
     }
   }
 
-  // ---- vector-unit readouts: sum over the lane quarters, then over waves
+  // ---- readouts: sum over the lane quarters, then over waves
   {
-    float ox[4] = {oacc.x, oacc.y, oacc.z, oacc.w};
-    float ex[4] = {eacc.x, eacc.y, eacc.z, eacc.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ox[i] += __shfl_xor(ox[i], 16, 64);
-      ox[i] += __shfl_xor(ox[i], 32, 64);
-      if (MT > 0) {
-        ex[i] += __shfl_xor(ex[i], 16, 64);
-        ex[i] += __shfl_xor(ex[i], 32, 64);
-      }
-    }
-    oden += __shfl_xor(oden, 16, 64);
-    oden += __shfl_xor(oden, 32, 64);
-    if (MT > 0) {
-      eden += __shfl_xor(eden, 16, 64);
-      eden += __shfl_xor(eden, 32, 64);
-    }
-    if (q4 == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sh.onum[w][4 * l16 + i] = ox[i];
-        if (MT > 0) sh.enm[w][4 * l16 + i] = ex[i];
-      }
-    }
-    if (lane == 0) {
-      sh.oden[w] = oden;
-      if (MT > 0) sh.eden[w] = eden;
-    }
-  }
-  if (MT > 0) {
-#pragma unroll
-    for (int mt = 0; mt < MTA; ++mt) {
-      float d = dacc[mt];
-      d += __shfl_xor(d, 16, 64);
-      d += __shfl_xor(d, 32, 64);
-      if (q4 == 0) sh.den[w][16 * mt + l16] = d;
-    }
-  }
-  // numerators: the waves add into the LDS copy in turn and the last one keeps
-  // the sum (the first barrier also ends every read of the cache keys, whose
-  // LDS the partials reuse); with MT = 0 this only publishes the readouts
-  for (int r = 0; r < kWaves; ++r) {
-    __syncthreads();
-    if (MT > 0 && w == r) {
-#pragma unroll
-      for (int mt = 0; mt < MTA; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          f32x4 x = acc[mt][nt];
-          if (r > 0) {
-            const float4 y = sh.red[mt][nt][lane];
-            x[0] += y.x;
-            x[1] += y.y;
-            x[2] += y.z;
-            x[3] += y.w;
-          }
-          acc[mt][nt] = x;
-          if (r + 1 < kWaves) sh.red[mt][nt][lane] = make_float4(x[0], x[1], x[2], x[3]);
-        }
-    }
-  }
-  if (w == 0) {
-    // wave 0: the linear readout of q, then the evicted pair's score
-    float num = 0.0f, den = 0.0f;
-#pragma unroll
-    for (int r = 0; r < kWaves; ++r) {
-      num += sh.onum[r][lane];
-      den += sh.oden[r];
-    }
-    lin[(size_t)n * lstride + lane] = num;
-    if (lane == 0) lin[(size_t)n * lstride + kFD] = den;
-    if (MT > 0) {
-      float en = 0.0f, ed = eps;
-#pragma unroll
-      for (int r = 0; r < kWaves; ++r) {
-        en += sh.enm[r][lane];
-        ed += sh.eden[r];
-      }
-      const float pred = ed != 0.0f ? en / ed : 0.0f;
-      const float diff = pred - win_v[((size_t)n * wrows + slot) * kFD + lane];
-      const float err = wave_sum(diff * diff);
-      if (lane == 0) scores[(size_t)n * sstride + lambda] = err;
-    }
-  }
-  if (MT > 0 && w == kWaves - 1) {
-    // lane (l16, q4) holds candidates 16*mt + 4*q4 + i at state columns 4*l16 + nt
-#pragma unroll
-    for (int mt = 0; mt < MTA; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * mt + 4 * q4 + i;
-        const bool live = c < lambda;
-        float den = eps;
-#pragma unroll
-        for (int r = 0; r < kWaves; ++r) den += sh.den[r][c];
-        float4 vc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (live) vc = *reinterpret_cast<const float4*>(cache_v + ((size_t)n * lambda + c) * kFD + 4 * l16);
-        float err = 0.0f;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float pred = den != 0.0f ? acc[mt][nt][i] / den : 0.0f;
-          const float diff = pred - comp(vc, nt);
-          err += diff * diff;
-        }
-        err += __shfl_xor(err, 1, 64);
-        err += __shfl_xor(err, 2, 64);
-        err += __shfl_xor(err, 4, 64);
-        err += __shfl_xor(err, 8, 64);
-        if (l16 == 0 && live) scores[(size_t)n * sstride + c] = err;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- matrix-core state pass, 8 waves
-
-// LDS-only work-group barrier: waits for this wave's LDS traffic, not for its
-// global loads in flight.
-__device__ __forceinline__ void lds_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-constexpr int kThreads2 = 512;
-constexpr int kPairs2 = 4;  // producer/consumer wave pairs, one per SIMD
-
-struct State2Lds {
-  alignas(16) float qs[kFD];
-  alignas(16) float pk[kFD];
-  alignas(16) float pv[kFD];
-  alignas(16) float ek[kFD];
-  union {
-    struct {
-      float ck[kFMaxCache][kKS];        // cache keys
-      uint4 bp[kPairs2][2][12][64];     // B pieces [pair][buffer][3 * nt + piece][lane]
-      float sj[kPairs2][2][4][8];       // s of each lane quarter's 8 slots
-    } lp;
-    float4 red[kFMaxCache / 16][4][64];  // numerator partials (after the tile loop)
-  };
-  float den[kPairs2][kFMaxCache];
-  float onum[kPairs2][kFD];
-  float enm[kPairs2][kFD];
-  float oden[kPairs2];
-  float eden[kPairs2];
-};
-
-// Same pass as hdec_state_kernel with two waves per SIMD. Pair p = (wave p,
-// wave p + 4) walks tiles p, p + 4, ...: the producer (wave p) loads its
-// tile, folds, writes it back, accumulates the readouts, splits it into the
-// three bf16 B pieces and publishes them in LDS; after the barrier both
-// waves take them from there. The producer runs candidate
-// blocks 0..3 and the consumer blocks 4..MT-1 against the same pieces, so
-// each wave keeps at most four blocks of accumulators.
-template <int MT, typename Tin>
-__global__ __launch_bounds__(kThreads2, 1) void hdec_state2_kernel(
-    float* __restrict__ H, float* __restrict__ s, const float* __restrict__ pend_k,
-    const float* __restrict__ pend_v, const Tin* __restrict__ q, const float* __restrict__ cache_k,
-    const float* __restrict__ cache_v, const float* __restrict__ win_k, const float* __restrict__ win_v,
-    int wrows, int slot, int lambda, float* __restrict__ scores, int sstride, float* __restrict__ lin,
-    int lstride, float eps) {
-  static_assert(MT > 4 && MT <= kFMaxCache / 16, "the consumer needs one to four blocks");
-  __shared__ __align__(16) State2Lds sh;
-  const int n = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wv & 3;
-  const bool prod = wv < kPairs2;
-  const int lane = tid & 63;
-  const int l16 = lane & 15;
-  const int q4 = lane >> 4;
-  float* Hn = H + (size_t)n * kFDim * kFD;
-  float* sn = s + (size_t)n * kFDim;
-  const int mb = prod ? 0 : 4;       // first candidate block of this wave
-  const int mc = prod ? 4 : MT - 4;  // its number of blocks
-
-  auto load_tile = [&](const TileCoords& tc, float4 (&h)[8], float (&sj)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      sj[j] = 0.0f;
-      if (j >= tc.jmin) {
-        h[j] = *reinterpret_cast<const float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16);
-        sj[j] = sn[tc.f0 + j];
-      }
-    }
-  };
-  TileCoords tc = tile_coords(pair, q4);
-  float4 h[8];
-  float sj[8];
-  if (prod) load_tile(tc, h, sj);
-
-  if (tid < kFD) {
-    sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kFD + tid);
-    sh.pk[tid] = pend_k[(size_t)n * kFD + tid];
-    sh.pv[tid] = pend_v[(size_t)n * kFD + tid];
-    sh.ek[tid] = win_k[((size_t)n * wrows + slot) * kFD + tid];
-  }
-  for (int i = tid; i < 16 * MT * (kFD / 4); i += kThreads2) {
-    const int c = i / (kFD / 4);
-    const int d4 = i % (kFD / 4);
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c < lambda) x = *reinterpret_cast<const float4*>(cache_k + ((size_t)n * lambda + c) * kFD + 4 * d4);
-    *reinterpret_cast<float4*>(&sh.lp.ck[c][4 * d4]) = x;
-  }
-  __syncthreads();
-
-  const float4 v4 = *reinterpret_cast<const float4*>(&sh.pv[4 * l16]);
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dacc[4] = {0.f, 0.f, 0.f, 0.f};
-  float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 eacc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float oden = 0.0f, eden = 0.0f;
-
-  int it = 0;
-#pragma unroll 1
-  for (int T = pair; T < kFTiles; T += kPairs2, ++it) {
-    const int buf = it & 1;
-    const bool more = T + kPairs2 < kFTiles;
-    const TileCoords tcn = more ? tile_coords(T + kPairs2, q4) : tc;
-    float4 hn[8];
-    float sjn[8];
-    if (prod) {
-      if (more) load_tile(tcn, hn, sjn);
-      float pk[8], pq[8], pe[8];
-      phi8(sh.pk, tc, pk);
-      phi8(sh.qs, tc, pq);
-      phi8(sh.ek, tc, pe);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= tc.jmin) {
-          h[j].x += pk[j] * v4.x;
-          h[j].y += pk[j] * v4.y;
-          h[j].z += pk[j] * v4.z;
-          h[j].w += pk[j] * v4.w;
-          sj[j] += pk[j];
-          *reinterpret_cast<float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16) = h[j];
-        }
-        oacc.x += pq[j] * h[j].x;
-        oacc.y += pq[j] * h[j].y;
-        oacc.z += pq[j] * h[j].z;
-        oacc.w += pq[j] * h[j].w;
-        oden += pq[j] * sj[j];
-        eacc.x += pe[j] * h[j].x;
-        eacc.y += pe[j] * h[j].y;
-        eacc.z += pe[j] * h[j].z;
-        eacc.w += pe[j] * h[j].w;
-        eden += pe[j] * sj[j];
-      }
-      {
-        float x = sj[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) x = l16 == j ? sj[j] : x;
-        if (l16 < 8 && l16 >= tc.jmin) sn[tc.f0 + l16] = x;
-        if (l16 < 8) sh.lp.sj[pair][buf][q4][l16] = x;
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
-        bf16x8 b0, b1, b2;
-        split3(x, b0, b1, b2);
-        sh.lp.bp[pair][buf][3 * nt][lane] = __builtin_bit_cast(uint4, b0);
-        sh.lp.bp[pair][buf][3 * nt + 1][lane] = __builtin_bit_cast(uint4, b1);
-        sh.lp.bp[pair][buf][3 * nt + 2][lane] = __builtin_bit_cast(uint4, b2);
-      }
-    }
-    lds_sync();  // tile T's pieces and s are published
-    if (!prod) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sj[j] = sh.lp.sj[pair][buf][q4][j];
-    }
-    bf16x8 ahi[4], alo[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (m < mc) {
-        float p[8];
-        phi8(sh.lp.ck[16 * (mb + m) + l16], tc, p);
-        float dd = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dd += p[j] * sj[j];
-        dacc[m] += dd;
-        split2(p, ahi[m], alo[m]);
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, sh.lp.bp[pair][buf][3 * nt][lane]);
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, sh.lp.bp[pair][buf][3 * nt + 1][lane]);
-      const bf16x8 b2 = __builtin_bit_cast(bf16x8, sh.lp.bp[pair][buf][3 * nt + 2][lane]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (m < mc) {
-          acc[m][nt] = mfma16x16x32(ahi[m], b0, acc[m][nt]);
-          acc[m][nt] = mfma16x16x32(ahi[m], b1, acc[m][nt]);
-          acc[m][nt] = mfma16x16x32(ahi[m], b2, acc[m][nt]);
-          acc[m][nt] = mfma16x16x32(alo[m], b0, acc[m][nt]);
-        }
-      }
-    }
-    if (prod && more) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        h[j] = hn[j];
-        sj[j] = sjn[j];
-      }
-    }
-    tc = tcn;
-  }
-
-  // ---- vector-unit readouts (producers): over the lane quarters, then the pairs
-  if (prod) {
     float ox[4] = {oacc.x, oacc.y, oacc.z, oacc.w};
     float ex[4] = {eacc.x, eacc.y, eacc.z, eacc.w};
 #pragma unroll
@@ -728,56 +350,20 @@ __global__ __launch_bounds__(kThreads2, 1) void hdec_state2_kernel(
     if (q4 == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sh.onum[pair][4 * l16 + i] = ox[i];
-        sh.enm[pair][4 * l16 + i] = ex[i];
+        sh.onum[w][4 * l16 + i] = ox[i];
+        sh.enm[w][4 * l16 + i] = ex[i];
       }
     }
     if (lane == 0) {
-      sh.oden[pair] = oden;
-      sh.eden[pair] = eden;
+      sh.oden[w] = oden;
+      sh.eden[w] = eden;
     }
   }
+  __syncthreads();
+  if (w == 0) {
+    float num = 0.0f, den = 0.0f, en = 0.0f, ed = 0.0f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m < mc) {
-      float d = dacc[m];
-      d += __shfl_xor(d, 16, 64);
-      d += __shfl_xor(d, 32, 64);
-      if (q4 == 0) sh.den[pair][16 * (mb + m) + l16] = d;
-    }
-  }
-  // numerators: the pairs add into the LDS copy in turn (producers blocks
-  // 0..3, consumers blocks 4..); the last pair keeps the sums. The first
-  // barrier also ends every read of the keys and pieces, whose LDS the
-  // partials reuse.
-  for (int r = 0; r < kPairs2; ++r) {
-    __syncthreads();
-    if (pair == r) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (m < mc) {
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            f32x4 x = acc[m][nt];
-            if (r > 0) {
-              const float4 y = sh.red[mb + m][nt][lane];
-              x[0] += y.x;
-              x[1] += y.y;
-              x[2] += y.z;
-              x[3] += y.w;
-            }
-            acc[m][nt] = x;
-            if (r + 1 < kPairs2) sh.red[mb + m][nt][lane] = make_float4(x[0], x[1], x[2], x[3]);
-          }
-        }
-      }
-    }
-  }
-  if (wv == 0) {
-    // the linear readout of q, then the evicted pair's score
-    float num = 0.0f, den = 0.0f, en = 0.0f, ed = eps;
-#pragma unroll
-    for (int r = 0; r < kPairs2; ++r) {
+    for (int r = 0; r < kWaves; ++r) {
       num += sh.onum[r][lane];
       den += sh.oden[r];
       en += sh.enm[r][lane];
@@ -785,39 +371,9 @@ __global__ __launch_bounds__(kThreads2, 1) void hdec_state2_kernel(
     }
     lin[(size_t)n * lstride + lane] = num;
     if (lane == 0) lin[(size_t)n * lstride + kFD] = den;
-    const float pred = ed != 0.0f ? en / ed : 0.0f;
-    const float diff = pred - win_v[((size_t)n * wrows + slot) * kFD + lane];
-    const float err = wave_sum(diff * diff);
-    if (lane == 0) scores[(size_t)n * sstride + lambda] = err;
-  }
-  if (pair == kPairs2 - 1) {
-    // lane (l16, q4) holds candidates 16*(mb + m) + 4*q4 + i at state columns 4*l16 + nt
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (m < mc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * (mb + m) + 4 * q4 + i;
-          const bool live = c < lambda;
-          float den = eps;
-#pragma unroll
-          for (int r = 0; r < kPairs2; ++r) den += sh.den[r][c];
-          float4 vc = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (live) vc = *reinterpret_cast<const float4*>(cache_v + ((size_t)n * lambda + c) * kFD + 4 * l16);
-          float err = 0.0f;
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const float pred = den != 0.0f ? acc[m][nt][i] / den : 0.0f;
-            const float diff = pred - comp(vc, nt);
-            err += diff * diff;
-          }
-          err += __shfl_xor(err, 1, 64);
-          err += __shfl_xor(err, 2, 64);
-          err += __shfl_xor(err, 4, 64);
-          err += __shfl_xor(err, 8, 64);
-          if (l16 == 0 && live) scores[(size_t)n * sstride + c] = err;
-        }
-      }
+    if (evict) {
+      esum[(size_t)n * lstride + lane] = en;
+      if (lane == 0) esum[(size_t)n * lstride + kFD] = ed;
     }
   }
 }
@@ -831,9 +387,10 @@ struct MixLds {
   alignas(16) float ek[DQK];  // the evicted token
   float vn[DV];
   float ev[DV];
-  float rk[DQK];              // the rejected pair
-  float rv[DV];
+  alignas(16) float rk[DQK];  // the rejected pair
+  alignas(16) float rv[DV];
   float sc[kKeyTile];         // one tile's scores, then weights
+  float err[256];             // the refresh candidates' self-recall errors
   float red[kWaves];
   float num[kThreads / DV][DV];
   unsigned long long kred[kWaves];
@@ -842,16 +399,20 @@ struct MixLds {
 };
 
 // One work-group per head-state. `refresh`: the cache is full and a token
-// is evicted (scores of the lambda + 1 candidates are in `scores`); else with
-// `evict` the evicted token is appended at cache row n_before.
+// is evicted; the lambda + 1 candidates are scored from their sums (the
+// cache rows' carried sums, the evicted pair's from the state pass in
+// `esum`); else with `evict` the evicted token is appended at cache row
+// n_before with its sums. Candidate i's sums and value row are read by
+// TPC = d_v / 16 adjacent threads, 16 columns each.
 template <int DQK, int DV, typename Tin, typename Tout>
 __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o,
     float* __restrict__ win_k, float* __restrict__ win_v, float* __restrict__ cache_k,
     float* __restrict__ cache_v, int32_t* __restrict__ cache_ids, float* __restrict__ pend_k,
-    float* __restrict__ pend_v, int32_t* __restrict__ rejected, const float* __restrict__ scores, int sstride,
-    const float* __restrict__ lin, int lstride, int lambda, int n_before, int n_after, bool refresh,
-    bool evict, int wrows, int win_first, int t, int slot, int evicted_id, float scale, float eps) {
+    float* __restrict__ pend_v, int32_t* __restrict__ rejected, float* __restrict__ cache_sums,
+    const float* __restrict__ esum, const float* __restrict__ lin, int lstride, int lambda, int n_before,
+    int n_after, bool refresh, bool evict, int wrows, int win_first, int t, int slot, int evicted_id, float scale,
+    float eps) {
   constexpr int G = kThreads / DV;  // groups of d_v threads (one value column per thread)
   constexpr int LPK = DQK / 4;      // lanes per key in the score pass (a float4 each)
   constexpr int KPW = 64 / LPK;     // keys per wave and pass
@@ -876,13 +437,56 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   if (tid == 0) sh.rrow = -1;
 
   // ---- the rejected pair: the last of the lambda + 1 candidates in
-  // (score desc, token id asc) order
+  // (score desc, token id asc) order, score_i = || num_i / (den_i + eps) - v_i ||^2.
+  // Candidate i's sums (rows of DVS floats, 16-byte aligned) are read once by
+  // TPC adjacent threads, 16 columns each, and stay in their registers for
+  // the update after the selection.
+  constexpr int TPC = DV / 16;          // threads per candidate, 16 columns each
+  constexpr int CPR = kThreads / TPC;   // candidates per round
+  constexpr int NR = 256 / CPR;         // rounds for lambda + 1 <= 256 candidates
+  constexpr int DPT = DQK / TPC;        // key dimensions per thread (closed-form weights)
+  constexpr int DVS = DV + 4;           // row stride of the sums
+  const int ci = tid / TPC, part = tid % TPC;
   int replaced = -1;  // the cache row the evicted pair now holds
   if (refresh) {
+    float4 cs[NR][4];  // this thread's 16 columns of its candidate in each round
+    float cd[NR];      // and the denominator
+    if (lambda > 0) {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) {
+        const int i = rr * CPR + ci;
+        cd[rr] = 0.0f;
+        float err = 0.0f;
+        if (i <= lambda) {
+          const float* sm = i < lambda ? cache_sums + ((size_t)n * lambda + i) * DVS : esum + (size_t)n * lstride;
+          const float* vr = i < lambda ? cache_v + ((size_t)n * lambda + i) * DV : win_v + srow * DV;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cs[rr][j] = reinterpret_cast<const float4*>(sm + 16 * part)[j];
+          cd[rr] = sm[DV];
+          const float dn = cd[rr] + eps;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4 vv4 = reinterpret_cast<const float4*>(vr + 16 * part)[j];
+            const float x[4] = {cs[rr][j].x, cs[rr][j].y, cs[rr][j].z, cs[rr][j].w};
+            const float y[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pred = dn != 0.0f ? x[e] / dn : 0.0f;
+              const float d = pred - y[e];
+              err += d * d;
+            }
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < TPC; off <<= 1) err += __shfl_xor(err, off, 64);
+        if (i <= lambda && part == 0) sh.err[i] = err;
+      }
+    }
+    __syncthreads();
     unsigned long long worst = ~0ull;
     for (int i = tid; i <= lambda; i += kThreads) {
       const int id = i < lambda ? cache_ids[(size_t)n * lambda + i] : evicted_id;
-      const float x = lambda > 0 ? scores[(size_t)n * sstride + i] : 0.0f;  // a lone candidate is not scored
+      const float x = lambda > 0 ? sh.err[i] : 0.0f;  // a lone candidate is not scored
       worst = min(worst, (unsigned long long)topk_key(x, (uint32_t)id));
     }
 #pragma unroll
@@ -911,6 +515,44 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     }
     if (rejected && tid == 0) rejected[n] = rid;
     replaced = r;
+    // the kept pairs' sums against the state with r folded in: their own (the
+    // evicted pair, now in row r, brings its sums from the pass) plus
+    // (k_i . k_r)^2 [v_r | 1]
+    if (lambda > 0) {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) {
+        const int i = rr * CPR + ci;
+        const bool live = i < lambda;
+        const bool fresh = i == r;
+        const float* kr = fresh ? sh.ek : cache_k + ((size_t)n * lambda + (live ? i : 0)) * DQK;
+        float dot = 0.0f;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) dot += kr[DPT * part + j] * sh.rk[DPT * part + j];
+#pragma unroll
+        for (int off = 1; off < TPC; off <<= 1) dot += __shfl_xor(dot, off, 64);
+        const float wgt = dot * dot;
+        if (live) {
+          float4 x[4];
+          float xd = cd[rr];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = cs[rr][j];
+          if (fresh) {
+            const float* src = esum + (size_t)n * lstride;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = reinterpret_cast<const float4*>(src + 16 * part)[j];
+            xd = src[DV];
+          }
+          float* dst = cache_sums + ((size_t)n * lambda + i) * DVS;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float4 rv4 = *reinterpret_cast<const float4*>(&sh.rv[16 * part + 4 * j]);
+            reinterpret_cast<float4*>(dst + 16 * part)[j] =
+                make_float4(x[j].x + wgt * rv4.x, x[j].y + wgt * rv4.y, x[j].z + wgt * rv4.z, x[j].w + wgt * rv4.w);
+          }
+          if (part == 0) dst[DV] = xd + wgt;
+        }
+      }
+    }
     // (q . k_r)^2 = phi(q)^T phi(k_r), the readout's share of the deferred fold
     if (wave == 0) {
       float x = 0.0f;
@@ -925,6 +567,8 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     if (evict) {
       for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + n_before) * DQK + d] = sh.ek[d];
       for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + n_before) * DV + d] = sh.ev[d];
+      for (int d = tid; d <= DV; d += kThreads)
+        cache_sums[((size_t)n * lambda + n_before) * (DV + 4) + d] = esum[(size_t)n * lstride + d];
       if (tid == 0) cache_ids[(size_t)n * lambda + n_before] = evicted_id;
       replaced = n_before;
     }
@@ -1004,49 +648,71 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   for (int d = tid; d < DV; d += kThreads) win_v[srow * DV + d] = sh.vn[d];
 }
 
+// ---------------------------------------------------------------- prime
+
+// The cached pairs' sums against the linear state of (H, s) and the pending
+// pair: work-group (block of 16 rows, head-state), thread (row e, columns
+// cg, cg + 16, ...): sum_f phi_f(k_e) H_f + (k_e . pend_k)^2 [pend_v | 1],
+// in float32.
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads) void hdec_prime_kernel(const float* __restrict__ H, const float* __restrict__ s,
+                                                              const float* __restrict__ pend_k,
+                                                              const float* __restrict__ pend_v,
+                                                              const float* __restrict__ cache_k, int lambda,
+                                                              int rows, float* __restrict__ cache_sums) {
+  constexpr int D = phi_dim(DQK);
+  constexpr int CPT = DV / 16;  // columns per thread
+  __shared__ float kk[16][DQK];
+  __shared__ float pk[DQK], pv[DV];
+  __shared__ uint16_t tab[D];
+  const int n = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int el = tid / 16, cg = tid % 16;
+  const int e = 16 * blockIdx.x + el;
+  for (int i = tid; i < 16 * DQK; i += kThreads) {
+    const int r = i / DQK, d = i % DQK;
+    const int ee = 16 * blockIdx.x + r;
+    kk[r][d] = ee < rows ? cache_k[((size_t)n * lambda + ee) * DQK + d] : 0.0f;
+  }
+  for (int d = tid; d < DQK; d += kThreads) pk[d] = pend_k[(size_t)n * DQK + d];
+  for (int d = tid; d < DV; d += kThreads) pv[d] = pend_v[(size_t)n * DV + d];
+  build_phi_table(tab, 0, D, DQK);
+  __syncthreads();
+  const float* Hn = H + (size_t)n * D * DV;
+  const float* sn = s + (size_t)n * D;
+  float acc[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) acc[j] = 0.0f;
+  float den = 0.0f;
+  for (int f = 0; f < D; ++f) {
+    const float p = phi_of(kk[el], tab[f]);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] += p * Hn[(size_t)f * DV + cg + 16 * j];
+    den += p * sn[f];
+  }
+  float dot = 0.0f;
+  for (int d = 0; d < DQK; ++d) dot += kk[el][d] * pk[d];
+  const float wgt = dot * dot;
+  if (e < rows) {
+    float* dst = cache_sums + ((size_t)n * lambda + e) * (DV + 4);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) dst[cg + 16 * j] = acc[j] + wgt * pv[cg + 16 * j];
+    if (cg == 0) dst[DV] = den + wgt;
+  }
+}
+
 // ---------------------------------------------------------------- host
 
-size_t scores_bytes(const HybridDecodeArgs& a) { return align_up((size_t)a.N * (a.cache_size + 1) * sizeof(float)); }
 int lin_stride(int dv) { return (dv + 1 + 3) / 4 * 4; }
+size_t lin_bytes(const HybridDecodeArgs& a) { return align_up((size_t)a.N * lin_stride(a.dv) * sizeof(float)); }
 
-bool use_matrix_pass(const HybridDecodeArgs& a) {
-  return a.dqk == kFD && a.dv == kFD && a.cache_size >= 1 && a.cache_size <= kFMaxCache;
-}
-
-template <typename Tin>
-hipError_t launch_state(const HybridDecodeArgs& a, int mt, int wrows, int slot, float* scores, int sstride,
-                        float* lin, int lstride, hipStream_t st) {
-#define KLA_STATE(M)                                                                                            \
-  hipLaunchKernelGGL((hdec_state_kernel<M, Tin>), dim3(a.N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,       \
-                     a.pend_v, static_cast<const Tin*>(a.q), a.cache_k, a.cache_v, a.win_k, a.win_v, wrows,   \
-                     slot, a.cache_size, scores, sstride, lin, lstride, a.eps)
-#define KLA_STATE2(M)                                                                                           \
-  hipLaunchKernelGGL((hdec_state2_kernel<M, Tin>), dim3(a.N), dim3(kThreads2), 0, st, a.H, a.s, a.pend_k,     \
-                     a.pend_v, static_cast<const Tin*>(a.q), a.cache_k, a.cache_v, a.win_k, a.win_v, wrows,   \
-                     slot, a.cache_size, scores, sstride, lin, lstride, a.eps)
-  // up to 64 candidates: one wave per SIMD holds every block; more: two
-  switch (mt) {
-    case 0: KLA_STATE(0); break;
-    case 1: KLA_STATE(1); break;
-    case 2: KLA_STATE(2); break;
-    case 3: KLA_STATE(3); break;
-    case 4: KLA_STATE(4); break;
-    case 5: KLA_STATE2(5); break;
-    case 6: KLA_STATE2(6); break;
-    case 7: KLA_STATE2(7); break;
-    case 8: KLA_STATE2(8); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef KLA_STATE
-#undef KLA_STATE2
-  return hipGetLastError();
-}
+bool use_matrix_pass(const HybridDecodeArgs& a) { return a.dqk == kFD && a.dv == kFD; }
 
 template <int DQK, int DV, typename Tin, typename Tout>
 hipError_t run_hd(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
   char* p = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(p);
-  float* lin = reinterpret_cast<float*>(p + scores_bytes(a));
+  float* lin = reinterpret_cast<float*>(p);
+  float* esum = reinterpret_cast<float*>(p + lin_bytes(a));
   const int N = a.N, W = a.window, lam = a.cache_size, t = a.t;
   const int wrows = W + 1;
   const int slot = t % wrows;  // the evicted token's row, then the new token's
@@ -1055,25 +721,21 @@ hipError_t run_hd(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
   const int n_before = std::min(lam, std::max(0, t - W - 1));
   const bool refresh = evict && n_before == lam;
   const int n_after = std::min(lam, std::max(0, t - W));
-  const int sstride = lam + 1;
   const int lstride = lin_stride(DV);
-  hipError_t e;
   prof_begin(st);
   if (use_matrix_pass(a)) {
-    e = launch_state<Tin>(a, refresh ? (lam + 15) / 16 : 0, wrows, slot, scores, sstride, lin, lstride, st);
+    hipLaunchKernelGGL((hdec_state_kernel<Tin>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k, a.pend_v,
+                       static_cast<const Tin*>(a.q), a.win_k, wrows, slot, evict, lin, esum, lstride);
   } else {
     hipLaunchKernelGGL((hdec_fold_kernel<DQK, DV, Tin, true>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
-                       a.pend_v, static_cast<const Tin*>(a.q), lin, lstride);
-    if (refresh && lam > 0)
-      hipLaunchKernelGGL((hdec_score_kernel<DQK, DV>), dim3((lam + 1 + 63) / 64, N), dim3(kThreads), 0, st, a.H,
-                         a.s, a.cache_k, a.cache_v, a.win_k, a.win_v, lam, wrows, slot, scores, sstride, a.eps);
-    e = hipGetLastError();
+                       a.pend_v, static_cast<const Tin*>(a.q), lin, lstride, a.win_k, wrows, slot, evict, esum);
   }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((hdec_mix_kernel<DQK, DV, Tin, Tout>), dim3(N), dim3(kThreads), 0, st,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
                      static_cast<Tout*>(a.o), a.win_k, a.win_v, a.cache_k, a.cache_v, a.cache_ids, a.pend_k,
-                     a.pend_v, a.rejected, scores, sstride, lin, lstride, lam, n_before, n_after, refresh, evict,
+                     a.pend_v, a.rejected, a.cache_sums, esum, lin, lstride, lam, n_before, n_after, refresh, evict,
                      wrows, std::max(0, t - W), t, slot, evicted_id, a.scale, a.eps);
   prof_end(st);
   return hipGetLastError();
@@ -1088,9 +750,7 @@ hipError_t run_hd_dt(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
 
 }  // namespace
 
-size_t hybrid_decode_workspace(const HybridDecodeArgs& a) {
-  return scores_bytes(a) + align_up((size_t)a.N * lin_stride(a.dv) * sizeof(float));
-}
+size_t hybrid_decode_workspace(const HybridDecodeArgs& a) { return 2 * lin_bytes(a); }
 
 hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
 #define KLA_CASE(A, B) \
@@ -1102,11 +762,27 @@ hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t
   return hipErrorInvalidValue;
 }
 
+hipError_t hybrid_decode_prime_launch(const HybridDecodeArgs& a, hipStream_t st) {
+  const int rows = std::min(a.cache_size, std::max(0, a.t - a.window - 1));
+  if (rows == 0) return hipSuccess;
+#define KLA_CASE(A, B)                                                                                            \
+  if (a.dqk == A && a.dv == B) {                                                                                  \
+    hipLaunchKernelGGL((hdec_prime_kernel<A, B>), dim3((rows + 15) / 16, a.N), dim3(kThreads), 0, st, a.H, a.s,   \
+                       a.pend_k, a.pend_v, a.cache_k, a.cache_size, rows, a.cache_sums);                         \
+    return hipGetLastError();                                                                                     \
+  }
+  KLA_CASE(16, 16) KLA_CASE(16, 32) KLA_CASE(16, 64)
+  KLA_CASE(32, 16) KLA_CASE(32, 32) KLA_CASE(32, 64)
+  KLA_CASE(64, 16) KLA_CASE(64, 32) KLA_CASE(64, 64)
+#undef KLA_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st) {
 #define KLA_CASE(A, B)                                                                                          \
   if (a.dqk == A && a.dv == B) {                                                                                \
     hipLaunchKernelGGL((hdec_fold_kernel<A, B, float, false>), dim3(a.N), dim3(kThreads), 0, st, a.H, a.s,      \
-                       a.pend_k, a.pend_v, nullptr, nullptr, 0);                                               \
+                       a.pend_k, a.pend_v, nullptr, nullptr, 0, nullptr, 1, 0, false, nullptr);                \
     return hipGetLastError();                                                                                   \
   }
   KLA_CASE(16, 16) KLA_CASE(16, 32) KLA_CASE(16, 64)

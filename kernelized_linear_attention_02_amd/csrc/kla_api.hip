@@ -690,12 +690,12 @@ kla_status_t hybrid_decode_args(const char* fn, int N, int d_qk, int d_v, float 
   const kla_hybrid_state_t& S = *state;
   if (!S.H || !S.s || !S.win_k || !S.win_v || !S.pend_k || !S.pend_v)
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, win_k, win_v, pend_k, pend_v are required", fn);
-  if (cfg->cache_size > 0 && (!S.cache_k || !S.cache_v || !S.cache_ids))
-    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cache_k, cache_v, cache_ids are required when cache_size > 0",
-                fn);
+  if (cfg->cache_size > 0 && (!S.cache_k || !S.cache_v || !S.cache_ids || !S.cache_sums))
+    return fail(KLA_ERR_INVALID_ARGUMENT,
+                "%s: cache_k, cache_v, cache_ids, cache_sums are required when cache_size > 0", fn);
   if (!aligned16(S.H) || !aligned16(S.s) || !aligned16(S.win_k) || !aligned16(S.win_v) ||
       !aligned16(S.cache_k) || !aligned16(S.cache_v) || !aligned16(S.cache_ids) || !aligned16(S.pend_k) ||
-      !aligned16(S.pend_v))
+      !aligned16(S.pend_v) || !aligned16(S.cache_sums))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state pointers must be 16-byte aligned", fn);
   st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"rejected", rejected}, {"ws", ws}});
   if (st != KLA_OK) return st;
@@ -720,6 +720,7 @@ kla_status_t hybrid_decode_args(const char* fn, int N, int d_qk, int d_v, float 
   a.cache_ids = S.cache_ids;
   a.pend_k = S.pend_k;
   a.pend_v = S.pend_v;
+  a.cache_sums = S.cache_sums;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -790,6 +791,35 @@ kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_
   a.pend_k = state->pend_k;
   a.pend_v = state->pend_v;
   return hip_status(kla::hybrid_decode_flush_launch(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+kla_status_t kla_hybrid_decode_prime(int N, int d_qk, int d_v, const kla_hybrid_cfg_t* cfg, int t,
+                                     const kla_hybrid_state_t* state, kla_stream_t stream) {
+  const char* fn = "kla_hybrid_decode_prime";
+  kla_status_t st = check_hybrid_decode(N, d_qk, d_v, cfg, fn);
+  if (st != KLA_OK) return st;
+  if (t < 0) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: t must be >= 0 (got %d)", fn, t);
+  if (!state || !state->H || !state->s || !state->pend_k || !state->pend_v)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, pend_k, pend_v are required", fn);
+  if (cfg->cache_size > 0 && (!state->cache_k || !state->cache_sums))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cache_k, cache_sums are required when cache_size > 0", fn);
+  st = check_align(fn, {{"H", state->H}, {"s", state->s}, {"pend_k", state->pend_k}, {"pend_v", state->pend_v},
+                        {"cache_k", state->cache_k}, {"cache_sums", state->cache_sums}});
+  if (st != KLA_OK) return st;
+  kla::HybridDecodeArgs a{};
+  a.N = N;
+  a.dqk = d_qk;
+  a.dv = d_v;
+  a.window = cfg->window;
+  a.cache_size = cfg->cache_size;
+  a.t = t;
+  a.H = state->H;
+  a.s = state->s;
+  a.pend_k = state->pend_k;
+  a.pend_v = state->pend_v;
+  a.cache_k = state->cache_k;
+  a.cache_sums = state->cache_sums;
+  return hip_status(kla::hybrid_decode_prime_launch(a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

@@ -154,6 +154,7 @@ struct HybridDecodeArgs {
   int32_t* cache_ids;
   float* pend_k;  // the rejected pair whose fold is deferred to the next call
   float* pend_v;
+  float* cache_sums;  // [N][cache_size][dv + 4]: the cached pairs' sums against H + the pending fold
   const void* q;
   const void* k;
   const void* v;
@@ -165,6 +166,8 @@ size_t hybrid_decode_workspace(const HybridDecodeArgs& a);
 hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t st);
 // Folds the pending pair into (H, s) and clears it (uses N, dqk, dv, H, s, pend_k, pend_v).
 hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st);
+// Computes cache_sums for the cached rows of step t from H, s and the pending pair.
+hipError_t hybrid_decode_prime_launch(const HybridDecodeArgs& a, hipStream_t st);
 
 // Size of the library's static scratch for the allocation-free hybrid decode
 // step, and its device address on the current device (looked up once per

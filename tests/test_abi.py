@@ -250,7 +250,7 @@ def test_prefill_quadratic_backward_rejects(lib):
 
 
 def test_hybrid_decode_validation(lib):
-    st = B.HybridState(*([0x10000] * 9))
+    st = B.HybridState(*([0x10000] * 10))
     cfg = B.HybridCfg(512, 128, 1, 0.125)
 
     def call(cfg=cfg, N=8, dqk=64, dv=64, t=600, state=st, o=P, ws=P, nbytes=1 << 40, eps=0.0,
@@ -272,21 +272,27 @@ def test_hybrid_decode_validation(lib):
     assert call(in_dtype=7) == B.KLA_ERR_UNSUPPORTED
     assert call(state=None) == B.KLA_ERR_INVALID_ARGUMENT
     assert call(o=None) == B.KLA_ERR_INVALID_ARGUMENT
-    no_cache = B.HybridState(0x10000, 0x10000, 0x10000, 0x10000, None, None, None, 0x10000, 0x10000)
+    no_cache = B.HybridState(0x10000, 0x10000, 0x10000, 0x10000, None, None, None, 0x10000, 0x10000, None)
     assert call(state=no_cache) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"cache_size > 0" in lib.kla_last_error()
     # without a cache, the cache pointers may be NULL (only the workspace check is left)
     assert call(cfg=B.HybridCfg(512, 0, 1, 0.125), state=no_cache, ws=None) == B.KLA_ERR_WORKSPACE
-    odd = B.HybridState(0x10000, 0x10004, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+    odd = B.HybridState(0x10000, 0x10004, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
     assert call(state=odd) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"aligned" in lib.kla_last_error()
-    no_pend = B.HybridState(*([0x10000] * 7), None, None)
+    odd_sums = B.HybridState(*([0x10000] * 9), 0x10004)
+    assert call(state=odd_sums) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.kla_last_error()
+    no_sums = B.HybridState(*([0x10000] * 9), None)
+    assert call(state=no_sums) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"cache_sums" in lib.kla_last_error()
+    no_pend = B.HybridState(*([0x10000] * 7), None, None, 0x10000)
     assert call(state=no_pend) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"pend_k" in lib.kla_last_error()
 
     need = ctypes.c_size_t(0)
     assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == B.KLA_OK
-    assert need.value >= 8 * 129 * 4 + 8 * 65 * 4  # scores of lambda + 1 candidates, linear readouts
+    assert need.value >= 2 * 8 * 65 * 4  # linear readouts of q and of the evicted key
     assert call(ws=None) == B.KLA_ERR_WORKSPACE
     assert call(nbytes=need.value - 1) == B.KLA_ERR_WORKSPACE
     assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, None, ctypes.byref(need)) == \
@@ -298,6 +304,14 @@ def test_hybrid_decode_validation(lib):
     assert flush(0, 64, 64, ctypes.byref(st), None) == B.KLA_ERR_INVALID_ARGUMENT
     assert flush(8, 48, 64, ctypes.byref(st), None) == B.KLA_ERR_UNSUPPORTED
 
+    prime = lib.kla_hybrid_decode_prime
+    assert prime(8, 64, 64, ctypes.byref(cfg), 600, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert prime(8, 64, 64, None, 600, ctypes.byref(st), None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert prime(8, 64, 64, ctypes.byref(cfg), -1, ctypes.byref(st), None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert prime(8, 48, 64, ctypes.byref(cfg), 600, ctypes.byref(st), None) == B.KLA_ERR_UNSUPPORTED
+    assert prime(8, 64, 64, ctypes.byref(cfg), 600, ctypes.byref(no_sums), None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert prime(8, 64, 64, ctypes.byref(cfg), 600, ctypes.byref(odd_sums), None) == B.KLA_ERR_INVALID_ARGUMENT
+
 
 M = ctypes.c_void_p(0x10008)  # 8-byte aligned only: every call must refuse it
 
@@ -307,7 +321,7 @@ def test_hybrid_decode_static_validation(lib):
     # as the workspace step, then the static scratch limit (all before any
     # device call, so they run without a GPU)
     assert lib.kla_hybrid_decode_static_limit() == 16 << 20
-    st = B.HybridState(*([0x10000] * 9))
+    st = B.HybridState(*([0x10000] * 10))
     cfg = B.HybridCfg(512, 128, 1, 0.125)
 
     def call(cfg=cfg, N=8, t=600, state=st, o=P, q=P):
@@ -322,13 +336,13 @@ def test_hybrid_decode_static_validation(lib):
     assert call(o=None) == B.KLA_ERR_INVALID_ARGUMENT
     assert call(q=ctypes.c_void_p(0x10004)) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"aligned" in lib.kla_last_error()
-    # 129 scores + 68 readout floats per head-state: 21290 fit in 16 MiB
+    # two readouts of 68 floats per head-state: 30800 fit in 16 MiB
     need = ctypes.c_size_t(0)
-    assert lib.kla_hybrid_decode_workspace_size(21290, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == 0
+    assert lib.kla_hybrid_decode_workspace_size(30800, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == 0
     assert need.value <= 16 << 20
-    assert lib.kla_hybrid_decode_workspace_size(21400, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == 0
+    assert lib.kla_hybrid_decode_workspace_size(31000, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == 0
     assert need.value > 16 << 20
-    assert call(N=21400) == B.KLA_ERR_UNSUPPORTED
+    assert call(N=31000) == B.KLA_ERR_UNSUPPORTED
     assert b"static" in lib.kla_last_error()
 
 
@@ -366,13 +380,14 @@ def test_every_call_rejects_misaligned_pointers(lib):
                                             None, P, 1 << 40, None))
     _misaligned(lib, lib.kla_hybrid_prefill_streams(ctypes.byref(shp), ctypes.byref(cfg), P, P, P, P, None, None,
                                                     None, M, P, 1 << 40, None, None))
-    # token-by-token hybrid decode and its flush
-    st = B.HybridState(*([0x10000] * 9))
+    # token-by-token hybrid decode, its flush and its prime
+    st = B.HybridState(*([0x10000] * 10))
     hcfg = B.HybridCfg(512, 128, 1, 0.125)
     _misaligned(lib, lib.kla_hybrid_decode_step(8, 64, 64, 0.0, ctypes.byref(hcfg), 600, ctypes.byref(st), P, P,
                                                 M, B.KLA_BF16, P, B.KLA_F32, None, P, 1 << 40, None))
-    bad_pend = B.HybridState(*([0x10000] * 7), 0x10004, 0x10000)
+    bad_pend = B.HybridState(*([0x10000] * 7), 0x10004, 0x10000, 0x10000)
     _misaligned(lib, lib.kla_hybrid_decode_flush(8, 64, 64, ctypes.byref(bad_pend), None))
+    _misaligned(lib, lib.kla_hybrid_decode_prime(8, 64, 64, ctypes.byref(hcfg), 600, ctypes.byref(bad_pend), None))
 
 
 def test_hybrid_streams_entry_validates_like_the_plain_one(lib):

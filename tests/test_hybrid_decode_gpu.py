@@ -166,6 +166,8 @@ def test_hybrid_decode_continues_a_prefill(K):
         for i in range(max(0, T0 - W - 1), T0):
             st["win_k"][n, i % (W + 1)] = dev(k[n, i])
             st["win_v"][n, i % (W + 1)] = dev(v[n, i])
+    # the cached pairs' sums against the imported state
+    K.hybrid_decode_prime(st, T0, W, lam)
     go, grej, st = _run_gpu(K, q, k, v, W, lam, scale, 0.0, torch.float32, None, state=st, t0=T0)
     _check(q, k, v, W, lam, scale, 0.0, go, grej, st, RTOL_F32, t0=T0,
            pre_trace=extra["trace"][0].cpu().numpy())

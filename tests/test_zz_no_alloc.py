@@ -15,7 +15,7 @@ from kernelized_linear_attention_02_amd import synth as S
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-FIELDS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids", "pend_k", "pend_v")
+FIELDS = ("H", "s", "win_k", "win_v", "cache_k", "cache_v", "cache_ids", "pend_k", "pend_v", "cache_sums")
 
 
 @pytest.fixture(scope="module")
