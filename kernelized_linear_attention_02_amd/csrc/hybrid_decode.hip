@@ -47,14 +47,14 @@
 
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
-#include "mfma_bf16.hpp"
 
 namespace kla {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kKeyTile = kThreads;  // softmax keys scored per pass (online max across passes)
+constexpr int kKeyTile = 1024;  // softmax keys scored per pass (online max across passes)
+constexpr int kU = 8;           // row loads in flight per lane in the softmax passes
 
 // Block-wide reductions (kThreads threads); every thread gets the result.
 __device__ __forceinline__ float block_sum(float x, float* red) {
@@ -392,7 +392,7 @@ struct MixLds {
   float sc[kKeyTile];         // one tile's scores, then weights
   float err[256];             // the refresh candidates' self-recall errors
   float red[kWaves];
-  float num[kThreads / DV][DV];
+  alignas(16) float num[kWaves][DV];
   unsigned long long kred[kWaves];
   int rrow;
   float corr;
@@ -413,7 +413,6 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     const float* __restrict__ esum, const float* __restrict__ lin, int lstride, int lambda, int n_before,
     int n_after, bool refresh, bool evict, int wrows, int win_first, int t, int slot, int evicted_id, float scale,
     float eps) {
-  constexpr int G = kThreads / DV;  // groups of d_v threads (one value column per thread)
   constexpr int LPK = DQK / 4;      // lanes per key in the score pass (a float4 each)
   constexpr int KPW = 64 / LPK;     // keys per wave and pass
   __shared__ MixLds<DQK, DV> sh;
@@ -421,8 +420,7 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = tid % DV;
-  const int g = tid / DV;
+  const int c = tid % DV;  // the output column of threads tid < DV
 
   const size_t srow = (size_t)n * wrows + slot;
   for (int d = tid; d < DQK; d += kThreads) {
@@ -585,62 +583,107 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   // took is read from its LDS copy
   const int n_old = t - win_first;
   const int n_keys = n_old + 1 + n_after;
+  const int wbase = win_first % wrows;  // ring row of token win_first; j < n_old <= W keeps wbase + j < 2 wrows
+  auto ring = [&](int j) { const int r = wbase + j; return r >= wrows ? r - wrows : r; };
   auto key_row = [&](int j) -> const float* {
-    if (j < n_old) return win_k + ((size_t)n * wrows + (win_first + j) % wrows) * DQK;
+    if (j < n_old) return win_k + ((size_t)n * wrows + ring(j)) * DQK;
     if (j == n_old) return sh.kn;
     const int r = j - n_old - 1;
     return r == replaced ? sh.ek : cache_k + ((size_t)n * lambda + r) * DQK;
   };
   auto val_row = [&](int j) -> const float* {
-    if (j < n_old) return win_v + ((size_t)n * wrows + (win_first + j) % wrows) * DV;
+    if (j < n_old) return win_v + ((size_t)n * wrows + ring(j)) * DV;
     if (j == n_old) return sh.vn;
     const int r = j - n_old - 1;
     return r == replaced ? sh.ev : cache_v + ((size_t)n * lambda + r) * DV;
   };
+  // Scores: LPK lanes per key (a float4 each), KPW keys per wave and step;
+  // weighted sum: LPV lanes per value row (a float4 each), RPW rows per wave
+  // and step. kU steps are loaded before any is used.
+  constexpr int LPV = DV / 4;
+  constexpr int RPW = 64 / LPV;
+  constexpr int KPB = kWaves * KPW;
+  constexpr int RPB = kWaves * RPW;
   const float4 q4 = *reinterpret_cast<const float4*>(&sh.qv[4 * (lane % LPK)]);
+  const int vc = 4 * (lane % LPV);
   // running maximum, starting at 0: the linear terms are scaled by e^{-m} too
   float m = 0.0f;
-  float wsum = 0.0f, acc = 0.0f;
+  float wsum = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < n_keys; j0 += kKeyTile) {
     const int nt = min(kKeyTile, n_keys - j0);
-    for (int jb = wave * KPW; jb < nt; jb += kWaves * KPW) {
-      const int jl = jb + lane / LPK;
-      float x = 0.0f;
-      if (jl < nt) {
-        const float4 k4 = *reinterpret_cast<const float4*>(key_row(j0 + jl) + 4 * (lane % LPK));
-        x = q4.x * k4.x + q4.y * k4.y + q4.z * k4.z + q4.w * k4.w;
+    for (int jb = wave * KPW + lane / LPK; jb < nt; jb += kU * KPB) {  // a key group shares jb
+      float4 k4[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int jl = jb + u * KPB;
+        k4[u] = jl < nt ? *reinterpret_cast<const float4*>(key_row(j0 + jl) + 4 * (lane % LPK))
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int off = LPK / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-      if (jl < nt && lane % LPK == 0) sh.sc[jl] = x * scale;
+      for (int u = 0; u < kU; ++u) {
+        const int jl = jb + u * KPB;
+        float x = q4.x * k4[u].x + q4.y * k4[u].y + q4.z * k4[u].z + q4.w * k4[u].w;
+#pragma unroll
+        for (int off = LPK / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+        if (jl < nt && lane % LPK == 0) sh.sc[jl] = x * scale;
+      }
     }
     __syncthreads();
-    const float tmax = block_max(tid < nt ? sh.sc[tid] : -INFINITY, sh.red);
-    const float m_new = fmaxf(m, tmax);
+    float tm = -INFINITY;
+    for (int j = tid; j < nt; j += kThreads) tm = fmaxf(tm, sh.sc[j]);
+    const float m_new = fmaxf(m, block_max(tm, sh.red));
     const float rs = __expf(m - m_new);
     wsum *= rs;
-    acc *= rs;
-    if (tid < nt) {
-      const float p = __expf(sh.sc[tid] - m_new);
-      sh.sc[tid] = p;
+    acc.x *= rs;
+    acc.y *= rs;
+    acc.z *= rs;
+    acc.w *= rs;
+    for (int j = tid; j < nt; j += kThreads) {
+      const float p = __expf(sh.sc[j] - m_new);
+      sh.sc[j] = p;
       wsum += p;
     }
     __syncthreads();
-    for (int j = g; j < nt; j += G) acc += sh.sc[j] * val_row(j0 + j)[c];
-    __syncthreads();
+    for (int jb = wave * RPW + lane / LPV; jb < nt; jb += kU * RPB) {
+      float4 v4[kU];
+      float pw[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int jl = jb + u * RPB;
+        const bool in = jl < nt;
+        v4[u] = in ? *reinterpret_cast<const float4*>(val_row(j0 + jl) + vc) : make_float4(0.f, 0.f, 0.f, 0.f);
+        pw[u] = in ? sh.sc[jl] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        acc.x += pw[u] * v4[u].x;
+        acc.y += pw[u] * v4[u].y;
+        acc.z += pw[u] * v4[u].z;
+        acc.w += pw[u] * v4[u].w;
+      }
+    }
+    __syncthreads();  // the next tile's scores overwrite sc
     m = m_new;
   }
   const float sm_den = block_sum(wsum, sh.red);
-  sh.num[g][c] = acc;
+#pragma unroll
+  for (int off = LPV; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off, 64);
+    acc.y += __shfl_xor(acc.y, off, 64);
+    acc.z += __shfl_xor(acc.z, off, 64);
+    acc.w += __shfl_xor(acc.w, off, 64);
+  }
+  if (lane < LPV) *reinterpret_cast<float4*>(&sh.num[wave][vc]) = acc;
   __syncthreads();
-  if (g == 0) {
+  if (tid < DV) {
     float sm_num = 0.0f;
 #pragma unroll
-    for (int i = 0; i < G; ++i) sm_num += sh.num[i][c];
+    for (int i = 0; i < kWaves; ++i) sm_num += sh.num[i][tid];
     const float e = __expf(-m);
     const float nn = sm_num + e * lin_num;
     const float dd = sm_den + e * (lin_den + eps);
-    Elem<Tout>::store(o, (size_t)n * DV + c, dd != 0.0f ? nn / dd : 0.0f);
+    Elem<Tout>::store(o, (size_t)n * DV + tid, dd != 0.0f ? nn / dd : 0.0f);
   }
   // ---- the new token enters the window, in the evicted token's row (whose
   // values were copied to LDS before the first barrier)
