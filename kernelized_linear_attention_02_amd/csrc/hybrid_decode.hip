@@ -235,7 +235,7 @@ __device__ __forceinline__ void phi8(const float* x, const TileCoords& tc, float
 // pending fold, writes them back and accumulates the float32 readouts of q
 // and, when a token leaves the window, of its key.
 template <typename Tin>
-__global__ __launch_bounds__(kThreads) void hdec_state_kernel(
+__global__ __launch_bounds__(kThreads, 4) void hdec_state_kernel(
     float* __restrict__ H, float* __restrict__ s, const float* __restrict__ pend_k,
     const float* __restrict__ pend_v, const Tin* __restrict__ q, const float* __restrict__ win_k, int wrows,
     int slot, bool evict, float* __restrict__ lin, float* __restrict__ esum, int lstride) {
@@ -290,30 +290,37 @@ __global__ __launch_bounds__(kThreads) void hdec_state_kernel(
       load_tile(tcn, hn, sjn);
     }
 
-    float pk[8], pq[8], pe[8];
-    phi8(sh.pk, tc, pk);
-    phi8(sh.qs, tc, pq);
-    phi8(sh.ek, tc, pe);  // zero without an evicted key
+    // each lift is formed just before its use (eight values live at a time)
+    float ph[8];
+    phi8(sh.pk, tc, ph);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= tc.jmin) {
-        h[j].x += pk[j] * v4.x;
-        h[j].y += pk[j] * v4.y;
-        h[j].z += pk[j] * v4.z;
-        h[j].w += pk[j] * v4.w;
-        sj[j] += pk[j];
+        h[j].x += ph[j] * v4.x;
+        h[j].y += ph[j] * v4.y;
+        h[j].z += ph[j] * v4.z;
+        h[j].w += ph[j] * v4.w;
+        sj[j] += ph[j];
         *reinterpret_cast<float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16) = h[j];
       }
-      oacc.x += pq[j] * h[j].x;
-      oacc.y += pq[j] * h[j].y;
-      oacc.z += pq[j] * h[j].z;
-      oacc.w += pq[j] * h[j].w;
-      oden += pq[j] * sj[j];
-      eacc.x += pe[j] * h[j].x;
-      eacc.y += pe[j] * h[j].y;
-      eacc.z += pe[j] * h[j].z;
-      eacc.w += pe[j] * h[j].w;
-      eden += pe[j] * sj[j];
+    }
+    phi8(sh.qs, tc, ph);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      oacc.x += ph[j] * h[j].x;
+      oacc.y += ph[j] * h[j].y;
+      oacc.z += ph[j] * h[j].z;
+      oacc.w += ph[j] * h[j].w;
+      oden += ph[j] * sj[j];
+    }
+    phi8(sh.ek, tc, ph);  // zero without an evicted key
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      eacc.x += ph[j] * h[j].x;
+      eacc.y += ph[j] * h[j].y;
+      eacc.z += ph[j] * h[j].z;
+      eacc.w += ph[j] * h[j].w;
+      eden += ph[j] * sj[j];
     }
     // lane l16 = j of each quarter writes s of slot j: a contiguous 32-byte run
     {
