@@ -370,7 +370,7 @@ def hybrid_decode_step_bytes(N, d, W, lam):
     return N * per
 
 
-def bench_hybrid_decode(torch, K, S, steps=None):
+def bench_hybrid_decode(torch, K, S, steps=None, cpu_on=False):
     cfg = S.CONFIGS["hybrid_decode_4096"]
     N, d, W, lam, T0 = cfg["N"], cfg["d"], cfg["window"], cfg["cache_size"], cfg["T0"]
     nsteps = cfg["steps"] if steps is None else steps
@@ -392,6 +392,20 @@ def bench_hybrid_decode(torch, K, S, steps=None):
     step_ms = loop_ms / nsteps
     step_bytes = hybrid_decode_step_bytes(N, d, W, lam)
     achieved = step_bytes / (span_ms * 1e-3) / 1e9
+    cpu = None
+    if cpu_on:
+        # the oracle's hybrid at refresh = 1 over head-state 0's whole token
+        # stream (the same values the GPU saw)
+        import oracle as O
+        hq, hk, hv = (x[:, 0].float().cpu().numpy() for x in (q, k, v))
+        T = hq.shape[0]
+        t = time.perf_counter()
+        O.hybrid_prefill(hq, hk, hv, W, lam, 1, 1.0 / math.sqrt(d))
+        el = time.perf_counter() - t
+        cpu = _baseline(T / el / N, "steps/s",
+                        f"1 of {N} head-states x {T} tokens ({T0} filling, then {nsteps}; from token "
+                        f"{W + 1 + lam} on every token refreshes the cache), float64, refresh = 1, "
+                        f"{el:.1f}s of CPU time, extrapolated x{N}")
     return dict(
         workload="hybrid_decode_4096", N=N, window=W, cache_size=lam, start_token=T0, steps=nsteps,
         step_ms=step_ms, steps_per_s=1e3 / step_ms, kernel_ms=span_ms,
@@ -401,6 +415,7 @@ def bench_hybrid_decode(torch, K, S, steps=None):
                                                "hybrid_decode_step_hybrid_decode_4096_traffic.md"),
                       kernel="hybrid decode step (state pass + mix; one span)",
                       bytes_per_launch=step_bytes),
+        cpu_baseline=cpu,
     )
 
 
@@ -416,31 +431,71 @@ def _baseline(value, unit, sample):
     return dict(value=value, unit=unit, cores=_oracle_threads(), kind="oracle", sample=sample)
 
 
-def cpu_baseline(S, name, budget_s):
-    """The oracle (float64, NumPy chunked form) on a bounded sample of the
-    workload's heads, in tokens/s of the whole workload (B*T tokens over all
-    heads; one head-token is 1/H of a token)."""
+def cpu_baseline_heads(S, name, budget_s, run, what, max_tokens=None):
+    """The oracle on the workload's heads, one at a time, until budget_s of
+    CPU time has been spent, in tokens/s of the whole workload (B*T tokens
+    over all heads; one head-token is 1/H of a token). ``run(O, q, k, v)``
+    is the oracle function of the line; ``max_tokens`` cuts each head to its
+    first tokens (for the linear-time forms, whose cost per token does not
+    depend on T)."""
     import oracle as O
     cfg = S.CONFIGS[name]
     B, H, T = cfg["B"], cfg["H"], cfg["T"]
     kind = cfg.get("gen", "normalised")
     heads = [(b, h) for b in range(B) for h in range(H)]
+    Tr = T if max_tokens is None else min(T, max_tokens)
     done = 0
     elapsed = 0.0
     for (b, h) in heads:
         c = S.prefill_case(name, B, H, T, cfg["d_qk"], cfg["d_v"], cfg["chunk"], cfg["seed"], kind=kind,
                            heads=[(b, h)])
+        q, k, v = c.q[0, 0, :Tr], c.k[0, 0, :Tr], c.v[0, 0, :Tr]
         t = time.perf_counter()
-        O.prefill_chunked(c.q[0, 0], c.k[0, 0], c.v[0, 0], chunk=256)
+        run(O, q, k, v)
         elapsed += time.perf_counter() - t
         done += 1
         if elapsed >= budget_s:
             break
-    tokens = done * T / H
+    tokens = done * Tr / H
     extra = "" if done == B * H else f", extrapolated x{B * H / done:g} to all heads"
+    cut = "" if Tr == T else f" (the first {Tr} of each head's {T} tokens, scaled per token)"
     return _baseline(tokens / elapsed, "tokens/s",
-                     f"{done} of {B * H} heads x {T} tokens, float64 chunked form, {elapsed:.1f}s of CPU time"
-                     + extra)
+                     f"{done} of {B * H} heads x {Tr} tokens{cut}, {what}, {elapsed:.1f}s of CPU time" + extra)
+
+
+def cpu_baseline(S, name, budget_s):
+    """The oracle's chunked form (float64) on a bounded sample of heads."""
+    return cpu_baseline_heads(S, name, budget_s, lambda O, q, k, v: O.prefill_chunked(q, k, v, chunk=256),
+                              "float64 chunked form")
+
+
+def cpu_baseline_quadratic(S, name, budget_s, factors=1, kind="concat"):
+    """The oracle's O(T^2) definition (float64): causal (q.k)^2 weights, or
+    the factor variant's closed-form weights."""
+    if factors == 1:
+        return cpu_baseline_heads(S, name, budget_s, lambda O, q, k, v: O.prefill_bruteforce(q, k, v),
+                                  "float64 quadratic form")
+    return cpu_baseline_heads(S, name, budget_s,
+                              lambda O, q, k, v: O.prefill_factors_bruteforce(q, k, v, factors, kind),
+                              f"float64 quadratic form, {kind} of {factors} factors")
+
+
+def cpu_baseline_factor_state(S, name, budget_s, factors, kind, max_tokens=None):
+    """The oracle's recurrent state form of a factor lift (float64)."""
+    return cpu_baseline_heads(S, name, budget_s,
+                              lambda O, q, k, v: O.prefill_factors_recurrent(q, k, v, factors, kind),
+                              f"float64 recurrent state form, {kind} of {factors} factors", max_tokens)
+
+
+def cpu_baseline_backward(S, name, budget_s):
+    """The oracle's gradients (float64, quadratic form) with an upstream
+    gradient of the same shape (N(0,1), drawn on the host: timing only)."""
+    import numpy as np
+
+    def run(O, q, k, v):
+        do = np.random.default_rng(8).standard_normal(v.shape)
+        O.prefill_backward(q, k, v, do)
+    return cpu_baseline_heads(S, name, budget_s, run, "float64 gradients dq, dk, dv")
 
 
 def cpu_baseline_decode(S, budget_s):
@@ -509,8 +564,13 @@ def bench_tiny(torch, K, S, steps, warmup):
     flops = (4.0 * D * (cfg["d_v"] + 1) + (cfg["chunk"] + 1) * (cfg["d_qk"] + cfg["d_v"] + 1)) * cfg["T"]
     return dict(workload="tiny_f32", B=1, H=1, T=cfg["T"], d_qk=cfg["d_qk"], d_v=cfg["d_v"], chunk=cfg["chunk"],
                 step_ms=step_ms, tokens_per_s=cfg["T"] / (step_ms * 1e-3), kernel_ms=kern_ms,
-                flops_per_call=flops, roofline=None,
-                note="launch-bound: 2.65 MFLOP per call; no roofline claim", arith="f32")
+                flops_per_call=flops,
+                roofline=dict(bound="alu", achieved=flops / (kern_ms * 1e-3) / 1e12, peak=PEAK_F32_VALU_TFLOPS,
+                              unit="TFLOP/s", frac=flops / (kern_ms * 1e-3) / 1e12 / PEAK_F32_VALU_TFLOPS,
+                              traffic=None, kernel="whole call (float32 vector path)",
+                              flops_per_launch=flops),
+                note="launch-bound: 2.65 MFLOP per call, a few microseconds of work in each launch",
+                arith="f32")
 
 
 def main():
@@ -599,19 +659,34 @@ def main():
             log("[bench] cpu baseline (oracle): prefill_1x16x65536")
             r["cpu_baseline"] = cpu_baseline(S, "prefill_1x16x65536", args.cpu_seconds * 0.5)
         secondary.append(r)
+        cs = args.cpu_seconds * 0.2  # the oracle budget of each of the lines below
+
+        def with_cpu(r, f):
+            if cpu_on:
+                log(f"[bench] cpu baseline (oracle): {r['workload']}")
+                r["cpu_baseline"] = f()
+            return r
         log("[bench] secondary: prefill_4x8x4096 in the quadratic form")
-        secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup))
+        secondary.append(with_cpu(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup),
+                                  lambda: cpu_baseline_quadratic(S, name, cs)))
         log("[bench] secondary: prefill_4x8x4096 with the KATA-M2 lift (chunked state form)")
-        secondary.append(bench_prefill(torch, K, S, name, args.steps, args.warmup, factors=2))
+        secondary.append(with_cpu(bench_prefill(torch, K, S, name, args.steps, args.warmup, factors=2),
+                                  lambda: cpu_baseline_factor_state(S, name, cs, 2, "concat")))
         log("[bench] secondary: prefill_4x8x4096 with the KATA-Sigma-2 lift (chunked state form)")
-        secondary.append(bench_prefill(torch, K, S, name, max(2, args.steps // 10), 1, factors=2, factor_kind="sum"))
+        secondary.append(with_cpu(
+            bench_prefill(torch, K, S, name, max(2, args.steps // 10), 1, factors=2, factor_kind="sum"),
+            lambda: cpu_baseline_factor_state(S, name, cs, 2, "sum")))
         log("[bench] secondary: prefill_1x16x65536 with the KATA-M2 lift (chunked state form)")
-        secondary.append(bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1, factors=2))
+        secondary.append(with_cpu(
+            bench_prefill(torch, K, S, "prefill_1x16x65536", max(3, args.steps // 4), 1, factors=2),
+            lambda: cpu_baseline_factor_state(S, "prefill_1x16x65536", cs, 2, "concat", max_tokens=8192)))
         for g, kind in ((2, "concat"), (2, "sum")):
             log(f"[bench] secondary: prefill_4x8x4096 in the quadratic form, {kind} of {g} factors")
-            secondary.append(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup, g, kind))
+            secondary.append(with_cpu(bench_prefill_quadratic(torch, K, S, name, args.steps, args.warmup, g, kind),
+                                      lambda: cpu_baseline_quadratic(S, name, cs, g, kind)))
         log("[bench] secondary: prefill_4x8x4096 backward")
-        secondary.append(bench_prefill_backward(torch, K, S, name, args.steps, args.warmup))
+        secondary.append(with_cpu(bench_prefill_backward(torch, K, S, name, args.steps, args.warmup),
+                                  lambda: cpu_baseline_backward(S, name, cs)))
         log("[bench] secondary: decode_sre_4096x128")
         r = bench_decode(torch, K, S, args.decode_steps, 2)
         if cpu_on:
@@ -627,7 +702,7 @@ def main():
         secondary.append(r)
         torch.cuda.empty_cache()
         log("[bench] secondary: hybrid_decode_4096")
-        secondary.append(bench_hybrid_decode(torch, K, S))
+        secondary.append(bench_hybrid_decode(torch, K, S, cpu_on=cpu_on))
     cpu = None
     if cpu_on:
         log("[bench] cpu baseline (oracle): prefill_4x8x4096")
