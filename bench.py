@@ -358,15 +358,17 @@ def hybrid_flops(n_heads, T, d, W, lam, R):
     return dict(total=float(total), fp32_faithful=float(faithful))
 
 
-def hybrid_decode_step_bytes(N, d, W, lam):
+def hybrid_decode_step_bytes(N, d, W, lam, P):
     """Algorithmic HBM bytes of one steady-state token-by-token hybrid step
-    (window full, cache full, one fold): H and s read and written once; the
-    W older window rows and the lam cache rows read once (keys and values,
+    (window full, cache full, one rejected pair), averaged over the P steps
+    of a fold cycle: H and s read once, and written once every P steps (the
+    rejected pairs wait in P pending slots and are folded together); the W
+    older window rows and the lam cache rows read once (keys and values,
     float32); the evicted row read and the replaced cache row and the new
     window row written; q, k, v (bf16) read and o (bf16) written."""
     D = phi_dim(d)
     row = 2 * d * 4
-    per = 2 * D * d * 4 + 2 * D * 4 + (W + lam) * row + 3 * row + 3 * d * 2 + d * 2 + 2 * 4
+    per = (1.0 + 1.0 / P) * (D * d * 4 + D * 4) + (W + lam) * row + 3 * row + 3 * d * 2 + d * 2 + 2 * 4
     return N * per
 
 
@@ -390,7 +392,9 @@ def bench_hybrid_decode(torch, K, S, steps=None, cpu_on=False):
 
     loop_ms, span_ms, _ = timed_calls(torch, K, loop, 1, 0)
     step_ms = loop_ms / nsteps
-    step_bytes = hybrid_decode_step_bytes(N, d, W, lam)
+    P = K.hybrid_decode_pending_slots()
+    assert nsteps % P == 0, "time whole fold cycles"
+    step_bytes = hybrid_decode_step_bytes(N, d, W, lam, P)
     achieved = step_bytes / (span_ms * 1e-3) / 1e9
     cpu = None
     if cpu_on:

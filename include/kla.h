@@ -79,7 +79,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 7
+#define KLA_ABI_VERSION 8
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -377,17 +377,21 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  *      linear state after the fold, with the weights of kla_hybrid_prefill;
  *   3. the new token's (k, v) enters the window.
  *
- * Deferred fold: the call does not add r's fold to H and s itself. It
- * stores r as the state's pending pair (pend_k, pend_v), and the next call
- * folds it in its own pass over H (so H is read and written once per
- * token). The linear state is therefore always
- *   H + phi(pend_k) pend_v^T,  s + phi(pend_k),
- * and a zero pending pair means nothing is pending. kla_hybrid_decode_flush
- * applies the pending fold to H and s and zeroes the pair.
+ * Deferred folds: the call does not add r's fold to H and s itself. It
+ * stores r in pending slot t mod P of the state (P = KLA_HYBRID_PENDING),
+ * and every call with t mod P = 0 folds all P slots into H and s in its own
+ * pass over H and clears them; the calls between only read H. H is then
+ * read once per token and written once per P tokens. The linear state is
+ * always
+ *   H' = H + sum_j phi(pend_k_j) pend_v_j^T,  s' = s + sum_j phi(pend_k_j),
+ * over the P slots; a zero slot holds nothing (phi(0) = 0), and a slot is
+ * written only by the call t = j (mod P) after the fold that cleared it.
+ * kla_hybrid_decode_flush folds every slot into H and s and zeroes them.
  *
  * State (device memory owned by the caller, float32, updated in place):
  *   H, s       : [N, D, d_v], [N, D] (zero before the first token).
- *   pend_k/pend_v : [N, d_qk] / [N, d_v] (zero before the first token).
+ *   pend_k/pend_v : [N, P, d_qk] / [N, P, d_v] (zero before the first
+ *                token).
  *   win_k/win_v: [N, W + 1, d_qk] / [N, W + 1, d_v]; token i is kept in row
  *                i mod (W + 1) while it is in the window.
  *   cache_k/cache_v/cache_ids : [N, lambda, d_qk] / [N, lambda, d_v] /
@@ -397,9 +401,8 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  *                min(lambda, max(0, t - W)) after it; other rows are unused.
  *                May be NULL when lambda = 0.
  *   cache_sums : [N, lambda, d_v + 4]: for cached row i, the sums of its key
- *                against the linear state (pending pair included),
- *                (phi(k_i)^T H', phi(k_i)^T s') with H' = H + phi(pend_k)
- *                pend_v^T, s' = s + phi(pend_k), in columns 0 .. d_v - 1 and
+ *                against the linear state (pending slots included),
+ *                (phi(k_i)^T H', phi(k_i)^T s'), in columns 0 .. d_v - 1 and
  *                d_v (the last three of a row are padding, for 16-byte rows). Each call keeps them: a
  *                fold of pair r adds (k_i . k_r)^2 [v_r | 1] (KATA page §2.2:
  *                phi(x) . phi(y) = (x . y)^2), and a pair entering the cache
@@ -408,17 +411,21 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  *                NULL when lambda = 0.
  * To continue from a prefill of t tokens, the caller fills the window rows of
  * tokens max(0, t - W - 1) .. t - 1, the cache rows and the state the prefill
- * left, with a zero pending pair, then calls kla_hybrid_decode_prime to
+ * left, with zero pending slots, then calls kla_hybrid_decode_prime to
  * compute cache_sums.
  *
  *   q, k : [N, d_qk]; v : [N, d_v]; in_dtype.   o : [N, d_v], out_dtype.
  *   rejected : [N] int32, or NULL: the token id folded by this call (now
- *              pending), -1 when there was none.
+ *              in pending slot t mod P), -1 when there was none.
  *   ws : workspace of kla_hybrid_decode_workspace_size bytes.
  * Every state pointer must be 16-byte aligned.
  * Supported: d_qk, d_v in {16, 32, 64}; refresh = 1; window >= 0;
  * 0 <= cache_size <= 255; t >= 0; softmax_scale finite.
  * ------------------------------------------------------------------------ */
+/* Pending slots of a token-by-token hybrid state (P above). */
+#define KLA_HYBRID_PENDING 8
+KLA_API int kla_hybrid_decode_pending_slots(void);
+
 typedef struct {
   float* H;
   float* s;
@@ -459,15 +466,16 @@ KLA_API kla_status_t kla_hybrid_decode_step_static(int N, int d_qk, int d_v, flo
                                            const void* k, const void* v, kla_dtype_t in_dtype,
                                            void* o, kla_dtype_t out_dtype, int32_t* rejected,
                                            kla_stream_t stream);
-/* Folds the pending pair into (H, s) and zeroes it (H, s, pend_k, pend_v of
- * `state` are used). The linear state H + phi(pend_k) pend_v^T does not
- * change, so cache_sums stay valid. */
+/* Folds every pending slot into (H, s) and zeroes the slots (H, s, pend_k,
+ * pend_v of `state` are used). The linear state H' does not change, so
+ * cache_sums stay valid. */
 KLA_API kla_status_t kla_hybrid_decode_flush(int N, int d_qk, int d_v, const kla_hybrid_state_t* state,
                                      kla_stream_t stream);
 /* kla_hybrid_decode_prime - computes cache_sums for the cached rows
  * 0 .. min(lambda, max(0, t - W - 1)) - 1 of a state about to take token t
  * (H, s, pend_k, pend_v, cache_k and cache_sums of `state` are used), in
- * float32: sum_f phi_f(k_i) H_f + (k_i . pend_k)^2 pend_v and the same for s.
+ * float32: sum_f phi_f(k_i) H_f + sum_j (k_i . pend_k_j)^2 pend_v_j and the
+ * same for s.
  * For a state filled from elsewhere (a prefill); a state that only ever went
  * through kla_hybrid_decode_step keeps its sums itself. */
 KLA_API kla_status_t kla_hybrid_decode_prime(int N, int d_qk, int d_v, const kla_hybrid_cfg_t* cfg, int t,

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     decode_step,
     factor_phi_dim,
     hybrid_decode_flush,
+    hybrid_decode_pending_slots,
     hybrid_decode_prime,
     hybrid_decode_state,
     hybrid_decode_static_limit,
@@ -42,6 +43,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["prefill", "prefill_quadratic", "prefill_quadratic_backward", "decode_step", "sre_select", "hybrid_prefill",
            "hybrid_decode_state", "hybrid_decode_step", "hybrid_decode_step_static",
-           "hybrid_decode_static_limit", "hybrid_decode_flush", "hybrid_decode_prime", "phi_dim", "factor_phi_dim",
+           "hybrid_decode_static_limit", "hybrid_decode_flush", "hybrid_decode_prime",
+           "hybrid_decode_pending_slots", "phi_dim", "factor_phi_dim",
            "load_library",
            "KlaError", "EXPORTS", "LIB_PATH", "profile_enable", "profile_read"]

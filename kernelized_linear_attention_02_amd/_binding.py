@@ -28,6 +28,7 @@ EXPORTS = (
     "kla_hybrid_workspace_size", "kla_hybrid_prefill", "kla_hybrid_prefill_streams",
     "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step", "kla_hybrid_decode_flush",
     "kla_hybrid_decode_prime", "kla_hybrid_decode_static_limit", "kla_hybrid_decode_step_static",
+    "kla_hybrid_decode_pending_slots",
     "kla_profile_enable", "kla_profile_read",
 )
 
@@ -109,6 +110,7 @@ def load_library(path: str = LIB_PATH):
         "kla_hybrid_decode_flush": (i, [i, i, i, hsp, vp]),
         "kla_hybrid_decode_prime": (i, [i, i, i, hcp, i, hsp, vp]),
         "kla_hybrid_decode_static_limit": (sz, []),
+        "kla_hybrid_decode_pending_slots": (i, []),
         "kla_hybrid_decode_step_static": (i, [i, i, i, f, hcp, i, hsp, vp, vp, vp, i, vp, i, vp, vp]),
         "kla_profile_enable": (i, [i]),
         "kla_profile_read": (i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
@@ -460,18 +462,20 @@ def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: in
     """Zeroed token-by-token hybrid state for N head-states: a dict of device
     tensors H [N, D, d_v], s [N, D], win_k [N, window+1, d_qk],
     win_v [N, window+1, d_v], cache_k [N, cache_size, d_qk],
-    cache_v [N, cache_size, d_v], pend_k [N, d_qk], pend_v [N, d_v],
+    cache_v [N, cache_size, d_v], pend_k [N, P, d_qk], pend_v [N, P, d_v]
+    (P = hybrid_decode_pending_slots()),
     cache_sums [N, cache_size, d_v + 4] (float32; numerators, denominator,
     padding) and cache_ids [N, cache_size] int32."""
     torch = _torch()
     D = phi_dim(d_qk)
+    P = hybrid_decode_pending_slots()
     f32 = dict(dtype=torch.float32, device=device)
     return dict(
         H=torch.zeros((N, D, d_v), **f32), s=torch.zeros((N, D), **f32),
         win_k=torch.zeros((N, window + 1, d_qk), **f32), win_v=torch.zeros((N, window + 1, d_v), **f32),
         cache_k=torch.zeros((N, cache_size, d_qk), **f32), cache_v=torch.zeros((N, cache_size, d_v), **f32),
         cache_ids=torch.full((N, cache_size), -1, dtype=torch.int32, device=device),
-        pend_k=torch.zeros((N, d_qk), **f32), pend_v=torch.zeros((N, d_v), **f32),
+        pend_k=torch.zeros((N, P, d_qk), **f32), pend_v=torch.zeros((N, P, d_v), **f32),
         cache_sums=torch.zeros((N, cache_size, d_v + 4), **f32))
 
 
@@ -519,6 +523,12 @@ def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, sof
     return (o, rej) if rejected else o
 
 
+def hybrid_decode_pending_slots() -> int:
+    """Pending slots of a hybrid decode state: rejected pairs wait there and
+    are folded into (H, s) together every that many tokens."""
+    return int(load_library().kla_hybrid_decode_pending_slots())
+
+
 def hybrid_decode_static_limit() -> int:
     """Bytes of the library's static scratch for hybrid_decode_step_static."""
     return int(load_library().kla_hybrid_decode_static_limit())
@@ -556,22 +566,22 @@ def hybrid_decode_step_static(state, t: int, q, k, v, window: int, cache_size: i
 
 
 def hybrid_decode_flush(state):
-    """Fold the state's pending pair into (H, s) and zero it, so that H and s
-    alone hold the linear memory."""
+    """Fold the state's pending slots into (H, s) and zero them, so that H and
+    s alone hold the linear memory."""
     lib = load_library()
     st = _hybrid_state_struct(state)
-    N, dqk = state["pend_k"].shape
+    N, _, dqk = state["pend_k"].shape
     dv = state["pend_v"].shape[-1]
     check(lib.kla_hybrid_decode_flush(N, dqk, dv, ctypes.byref(st), _stream(state["H"].device)))
 
 
 def hybrid_decode_prime(state, t: int, window: int, cache_size: int):
-    """Compute state['cache_sums'] from H, s, the pending pair and the cached
+    """Compute state['cache_sums'] from H, s, the pending slots and the cached
     keys, for a state filled from elsewhere (a prefill) that takes token t
     next."""
     lib = load_library()
     st = _hybrid_state_struct(state)
-    N, dqk = state["pend_k"].shape
+    N, _, dqk = state["pend_k"].shape
     dv = state["pend_v"].shape[-1]
     cfg = HybridCfg(int(window), int(cache_size), 1, 1.0)
     check(lib.kla_hybrid_decode_prime(N, dqk, dv, ctypes.byref(cfg), int(t), ctypes.byref(st),

@@ -15,33 +15,37 @@
 //      blocked hybrid prefill does with refresh = 1;
 //   3. token t enters the window ring in the row the evicted token left.
 //
-// Deferred fold: the fold of step 1 is not written into (H, s) by the call
-// that decides it. The rejected pair is kept in the state as the pending
-// pair (pend_k, pend_v) and folded by the next call's pass over H, which has
-// to read and write H anyway; the call's own readout adds the fold in closed
-// form, phi(q)^T phi(k_r) = (q . k_r)^2:
-//   num += (q . k_r)^2 v_r,   den += (q . k_r)^2.
-// H is then read and written once per token. A zero pending pair folds
-// nothing (phi(0) = 0).
+// Deferred folds: the fold of step 1 is not written into (H, s) by the call
+// that decides it. The rejected pair waits in pending slot t mod P of the
+// state (P = KLA_HYBRID_PENDING slots), and every call with t mod P = 0 folds
+// all P slots in its pass over H and clears them; the calls between only
+// read H. H is then read once per token and written once per P tokens. A
+// call that does not fold adds the slots to its readouts in closed form,
+// phi(x)^T phi(k_j) = (x . k_j)^2:
+//   num += sum_j (x . k_j)^2 v_j,   den += sum_j (x . k_j)^2,
+// and its own rejected pair r the same way. A zero slot folds nothing
+// (phi(0) = 0).
 //
 // Carried sums: every cached pair i keeps its sums against the linear state
-// (pending pair included), (phi(k_i)^T H, phi(k_i)^T s), in the caller's
+// (pending slots included), (phi(k_i)^T H', phi(k_i)^T s'), in the caller's
 // state. A fold of pair r changes them by the same closed form,
 // (k_i . k_r)^2 [v_r | 1], so the candidates of a refresh are scored from
 // their sums; only the evicted pair, new to the cache, takes its sums from
 // the pass over H.
 //
 // Kernels (all counts are known on the host from t):
-//   state pass  one work-group per head-state streams H once: pending fold,
-//               linear readouts of q and of the evicted key (d_qk = d_v =
-//               64: 72 tiles in block order; other shapes: the generic pass);
+//   state pass  one work-group per head-state streams H once: the pending
+//               folds (every P tokens; else H is only read), linear readouts
+//               of q and of the evicted key (d_qk = d_v = 64: 72 tiles in
+//               block order; other shapes: the generic pass);
 //   mix         per head-state: the candidates' scores from their sums, the
 //               rejected pair (lowest (score, -id)), the closed-form fold
 //               term for the kept pairs' sums and for the readout, the cache
 //               update, the window and cache softmax (online maximum), the
-//               joint division, the window insert, and the new pending pair;
-//   prime       the cached pairs' sums from (H, s) and the pending pair, for
-//               a state filled from elsewhere.
+//               joint division, the window insert, and the pending slot of
+//               the rejected pair;
+//   prime       the cached pairs' sums from (H, s) and the pending slots,
+//               for a state filled from elsewhere.
 #include <algorithm>
 #include <mutex>
 
@@ -53,6 +57,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kPend = KLA_HYBRID_PENDING;  // pending slots, folded together every kPend tokens
 constexpr int kKeyTile = 1024;  // softmax keys scored per pass (online max across passes)
 constexpr int kU = 8;           // row loads in flight per lane in the softmax passes
 
@@ -80,26 +85,28 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 
 // ---------------------------------------------------------------- generic state pass
 
-// One work-group per head-state: the pending pair is folded into (H, s)
-// and cleared; with READ, lin[n] = (phi(q)^T H, phi(q)^T s) of the folded
-// state (denominator without eps) at lin[n * lstride + 0 .. d_v], and, when
-// a token leaves the window (ek: its key row), the same readout of its key
-// at esum[n * lstride + ...].
+// One work-group per head-state. With `fold` the pending slots are folded
+// into (H, s) and cleared; otherwise H and s are only read and, with READ,
+// the slots enter the readouts in closed form. With READ, lin[n] =
+// (phi(q)^T H', phi(q)^T s') of the linear state (denominator without eps)
+// at lin[n * lstride + 0 .. d_v], and, when a token leaves the window (its
+// key row `slot`), the same readout of its key at esum[n * lstride + ...].
 template <int DQK, int DV, typename Tin, bool READ>
 __global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
     float* __restrict__ H, float* __restrict__ s, float* __restrict__ pend_k, float* __restrict__ pend_v,
     const Tin* __restrict__ q, float* __restrict__ lin, int lstride, const float* __restrict__ win_k, int wrows,
-    int slot, bool evict, float* __restrict__ esum) {
+    int slot, bool evict, bool fold, float* __restrict__ esum) {
   constexpr int D = phi_dim(DQK);
   constexpr int G = kThreads / DV;
   __shared__ float pq[READ ? D : 1];
   __shared__ float pe[READ ? D : 1];
-  __shared__ float pk[D];
-  __shared__ float qv[DQK], ev[DQK], kv[DQK], vv[DV];
+  __shared__ float pk[kPend][D];
+  __shared__ float qv[DQK], ev[DQK], kv[kPend][DQK], vv[kPend][DV];
   __shared__ uint16_t tab[D];
   __shared__ float num[G][DV];
   __shared__ float enm[G][DV];
   __shared__ float red[kWaves];
+  __shared__ float wq[kPend], we[kPend];
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int c = tid % DV;
@@ -108,32 +115,53 @@ __global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
   for (int d = tid; d < DQK; d += kThreads) {
     if (READ) qv[d] = Elem<Tin>::load(q, (size_t)n * DQK + d);
     if (ev_on) ev[d] = win_k[((size_t)n * wrows + slot) * DQK + d];
-    kv[d] = pend_k[(size_t)n * DQK + d];
   }
-  for (int d = tid; d < DV; d += kThreads) vv[d] = pend_v[(size_t)n * DV + d];
+  for (int i = tid; i < kPend * DQK; i += kThreads) kv[i / DQK][i % DQK] = pend_k[(size_t)n * kPend * DQK + i];
+  for (int i = tid; i < kPend * DV; i += kThreads) vv[i / DV][i % DV] = pend_v[(size_t)n * kPend * DV + i];
   build_phi_table(tab, 0, D, DQK);
   __syncthreads();
   for (int f = tid; f < D; f += kThreads) {
-    pk[f] = phi_of(kv, tab[f]);
+    if (fold)
+      for (int p = 0; p < kPend; ++p) pk[p][f] = phi_of(kv[p], tab[f]);
     if (READ) pq[f] = phi_of(qv, tab[f]);
     if (ev_on) pe[f] = phi_of(ev, tab[f]);
+  }
+  // closed-form weights of the slots (used without a fold)
+  if (READ && !fold && tid < kPend) {
+    float a = 0.0f, b = 0.0f;
+    for (int d = 0; d < DQK; ++d) {
+      a += qv[d] * kv[tid][d];
+      if (ev_on) b += ev[d] * kv[tid][d];
+    }
+    wq[tid] = a * a;
+    we[tid] = b * b;
   }
   __syncthreads();
   float* Hn = H + (size_t)n * D * DV;
   float* sn = s + (size_t)n * D;
-  const float vc = vv[c];
+  float vc[kPend];
+#pragma unroll
+  for (int p = 0; p < kPend; ++p) vc[p] = vv[p][c];
   float acc = 0.0f, eacc = 0.0f;
-#pragma unroll 8
+#pragma unroll 4
   for (int f = g; f < D; f += G) {
-    const float h = Hn[(size_t)f * DV + c] + pk[f] * vc;
-    Hn[(size_t)f * DV + c] = h;
+    float h = Hn[(size_t)f * DV + c];
+    if (fold) {
+#pragma unroll
+      for (int p = 0; p < kPend; ++p) h += pk[p][f] * vc[p];
+      Hn[(size_t)f * DV + c] = h;
+    }
     if (READ) acc += pq[f] * h;
     if (ev_on) eacc += pe[f] * h;
   }
   float den = 0.0f, eden = 0.0f;
   for (int f = tid; f < D; f += kThreads) {
-    const float x = sn[f] + pk[f];
-    sn[f] = x;
+    float x = sn[f];
+    if (fold) {
+#pragma unroll
+      for (int p = 0; p < kPend; ++p) x += pk[p][f];
+      sn[f] = x;
+    }
     if (READ) den += pq[f] * x;
     if (ev_on) eden += pe[f] * x;
   }
@@ -149,17 +177,31 @@ __global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
         x += num[i][c];
         if (ev_on) y += enm[i][c];
       }
+      if (!fold)
+#pragma unroll
+        for (int p = 0; p < kPend; ++p) {
+          x += wq[p] * vc[p];
+          if (ev_on) y += we[p] * vc[p];
+        }
       lin[(size_t)n * lstride + c] = x;
       if (ev_on) esum[(size_t)n * lstride + c] = y;
     }
     if (tid == 0) {
-      lin[(size_t)n * lstride + DV] = dsum;
-      if (ev_on) esum[(size_t)n * lstride + DV] = esm;
+      float dx = dsum, ex = esm;
+      if (!fold)
+        for (int p = 0; p < kPend; ++p) {
+          dx += wq[p];
+          ex += we[p];
+        }
+      lin[(size_t)n * lstride + DV] = dx;
+      if (ev_on) esum[(size_t)n * lstride + DV] = ex;
     }
   }
-  // every read of the pending pair went through LDS before the first barrier
-  for (int d = tid; d < DQK; d += kThreads) pend_k[(size_t)n * DQK + d] = 0.0f;
-  for (int d = tid; d < DV; d += kThreads) pend_v[(size_t)n * DV + d] = 0.0f;
+  // every read of the slots went through LDS before the first barrier
+  if (fold) {
+    for (int i = tid; i < kPend * DQK; i += kThreads) pend_k[(size_t)n * kPend * DQK + i] = 0.0f;
+    for (int i = tid; i < kPend * DV; i += kThreads) pend_v[(size_t)n * kPend * DV + i] = 0.0f;
+  }
 }
 
 // ---------------------------------------------------------------- matrix-core state pass
@@ -190,8 +232,8 @@ __constant__ BlockTable kBlockTab = BlockTable();
 
 struct StateLds {
   alignas(16) float qs[kFD];
-  alignas(16) float pk[kFD];
-  alignas(16) float pv[kFD];
+  alignas(16) float pk[kPend][kFD];
+  alignas(16) float pv[kPend][kFD];
   alignas(16) float ek[kFD];
   float onum[kWaves][kFD];
   float enm[kWaves][kFD];
@@ -231,14 +273,15 @@ __device__ __forceinline__ void phi8(const float* x, const TileCoords& tc, float
 
 // One work-group per head-state; its four waves take the 72 tiles in turn.
 // A lane (l16, q4) holds its eight state rows of a tile at columns
-// 4*l16 .. 4*l16+3 (16-byte loads, the next tile's in flight), adds the
-// pending fold, writes them back and accumulates the float32 readouts of q
-// and, when a token leaves the window, of its key.
-template <typename Tin>
-__global__ __launch_bounds__(kThreads, 4) void hdec_state_kernel(
-    float* __restrict__ H, float* __restrict__ s, const float* __restrict__ pend_k,
-    const float* __restrict__ pend_v, const Tin* __restrict__ q, const float* __restrict__ win_k, int wrows,
-    int slot, bool evict, float* __restrict__ lin, float* __restrict__ esum, int lstride) {
+// 4*l16 .. 4*l16+3 (16-byte loads, the next tile's in flight). With `fold`
+// it adds the pending slots' folds and writes the rows back; otherwise H is
+// only read and the slots enter the readouts in closed form. It accumulates
+// the float32 readouts of q and, when a token leaves the window, of its key.
+template <typename Tin, bool fold>
+__global__ __launch_bounds__(kThreads) void hdec_state_kernel(
+    float* __restrict__ H, float* __restrict__ s, float* __restrict__ pend_k, float* __restrict__ pend_v,
+    const Tin* __restrict__ q, const float* __restrict__ win_k, int wrows, int slot, bool evict,
+    float* __restrict__ lin, float* __restrict__ esum, int lstride) {
   __shared__ __align__(16) StateLds sh;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
@@ -268,13 +311,14 @@ __global__ __launch_bounds__(kThreads, 4) void hdec_state_kernel(
 
   if (tid < kFD) {
     sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kFD + tid);
-    sh.pk[tid] = pend_k[(size_t)n * kFD + tid];
-    sh.pv[tid] = pend_v[(size_t)n * kFD + tid];
     sh.ek[tid] = evict ? win_k[((size_t)n * wrows + slot) * kFD + tid] : 0.0f;
+  }
+  for (int i = tid; i < kPend * kFD; i += kThreads) {
+    sh.pk[i / kFD][i % kFD] = pend_k[(size_t)n * kPend * kFD + i];
+    sh.pv[i / kFD][i % kFD] = pend_v[(size_t)n * kPend * kFD + i];
   }
   __syncthreads();
 
-  const float4 v4 = *reinterpret_cast<const float4*>(&sh.pv[4 * l16]);
   float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 eacc = make_float4(0.f, 0.f, 0.f, 0.f);
   float oden = 0.0f, eden = 0.0f;
@@ -292,17 +336,25 @@ __global__ __launch_bounds__(kThreads, 4) void hdec_state_kernel(
 
     // each lift is formed just before its use (eight values live at a time)
     float ph[8];
-    phi8(sh.pk, tc, ph);
+    if constexpr (fold) {
+#pragma unroll 1
+      for (int p = 0; p < kPend; ++p) {
+        phi8(sh.pk[p], tc, ph);
+        const float4 v4 = *reinterpret_cast<const float4*>(&sh.pv[p][4 * l16]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= tc.jmin) {
-        h[j].x += ph[j] * v4.x;
-        h[j].y += ph[j] * v4.y;
-        h[j].z += ph[j] * v4.z;
-        h[j].w += ph[j] * v4.w;
-        sj[j] += ph[j];
-        *reinterpret_cast<float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16) = h[j];
+        for (int j = 0; j < 8; ++j) {
+          if (j >= tc.jmin) {  // slots below jmin are not features and stay zero
+            h[j].x += ph[j] * v4.x;
+            h[j].y += ph[j] * v4.y;
+            h[j].z += ph[j] * v4.z;
+            h[j].w += ph[j] * v4.w;
+            sj[j] += ph[j];
+          }
+        }
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j >= tc.jmin) *reinterpret_cast<float4*>(Hn + (size_t)(tc.f0 + j) * kFD + 4 * l16) = h[j];
     }
     phi8(sh.qs, tc, ph);
 #pragma unroll
@@ -323,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 4) void hdec_state_kernel(
       eden += ph[j] * sj[j];
     }
     // lane l16 = j of each quarter writes s of slot j: a contiguous 32-byte run
-    {
+    if constexpr (fold) {
       float x = sj[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) x = l16 == j ? sj[j] : x;
@@ -376,6 +428,20 @@ __global__ __launch_bounds__(kThreads, 4) void hdec_state_kernel(
       en += sh.enm[r][lane];
       ed += sh.eden[r];
     }
+    if (!fold) {
+      // the slots H does not hold yet, in closed form: (x . k_j)^2 [v_j | 1]
+#pragma unroll 1
+      for (int p = 0; p < kPend; ++p) {
+        const float kp = sh.pk[p][lane];
+        const float dq = wave_sum(sh.qs[lane] * kp);
+        const float de = wave_sum(sh.ek[lane] * kp);
+        const float vp = sh.pv[p][lane];
+        num += dq * dq * vp;
+        den += dq * dq;
+        en += de * de * vp;
+        ed += de * de;
+      }
+    }
     lin[(size_t)n * lstride + lane] = num;
     if (lane == 0) lin[(size_t)n * lstride + kFD] = den;
     if (evict) {
@@ -383,6 +449,13 @@ __global__ __launch_bounds__(kThreads, 4) void hdec_state_kernel(
       if (lane == 0) esum[(size_t)n * lstride + kFD] = ed;
     }
   }
+  // the folded slots are cleared (every read of them went through LDS before
+  // the first barrier)
+  if (fold)
+    for (int i = tid; i < kPend * kFD; i += kThreads) {
+      pend_k[(size_t)n * kPend * kFD + i] = 0.0f;
+      pend_v[(size_t)n * kPend * kFD + i] = 0.0f;
+    }
 }
 
 // ---------------------------------------------------------------- mix
@@ -418,8 +491,8 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     float* __restrict__ cache_v, int32_t* __restrict__ cache_ids, float* __restrict__ pend_k,
     float* __restrict__ pend_v, int32_t* __restrict__ rejected, float* __restrict__ cache_sums,
     const float* __restrict__ esum, const float* __restrict__ lin, int lstride, int lambda, int n_before,
-    int n_after, bool refresh, bool evict, int wrows, int win_first, int t, int slot, int evicted_id, float scale,
-    float eps) {
+    int n_after, bool refresh, bool evict, int wrows, int win_first, int t, int slot, int pslot, int evicted_id,
+    float scale, float eps) {
   constexpr int LPK = DQK / 4;      // lanes per key in the score pass (a float4 each)
   constexpr int KPW = 64 / LPK;     // keys per wave and pass
   __shared__ MixLds<DQK, DV> sh;
@@ -510,9 +583,9 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     for (int d = tid; d < DQK; d += kThreads) sh.rk[d] = r >= 0 ? cache_k[((size_t)n * lambda + r) * DQK + d] : sh.ek[d];
     for (int d = tid; d < DV; d += kThreads) sh.rv[d] = r >= 0 ? cache_v[((size_t)n * lambda + r) * DV + d] : sh.ev[d];
     __syncthreads();  // row r is read before it is replaced
-    // the rejected pair's fold is deferred to the next call
-    for (int d = tid; d < DQK; d += kThreads) pend_k[(size_t)n * DQK + d] = sh.rk[d];
-    for (int d = tid; d < DV; d += kThreads) pend_v[(size_t)n * DV + d] = sh.rv[d];
+    // the rejected pair's fold is deferred: it waits in pending slot pslot
+    for (int d = tid; d < DQK; d += kThreads) pend_k[((size_t)n * kPend + pslot) * DQK + d] = sh.rk[d];
+    for (int d = tid; d < DV; d += kThreads) pend_v[((size_t)n * kPend + pslot) * DV + d] = sh.rv[d];
     if (r >= 0) {
       for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + r) * DQK + d] = sh.ek[d];
       for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + r) * DV + d] = sh.ev[d];
@@ -567,8 +640,8 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     }
   } else {
     __syncthreads();
-    for (int d = tid; d < DQK; d += kThreads) pend_k[(size_t)n * DQK + d] = 0.0f;
-    for (int d = tid; d < DV; d += kThreads) pend_v[(size_t)n * DV + d] = 0.0f;
+    for (int d = tid; d < DQK; d += kThreads) pend_k[((size_t)n * kPend + pslot) * DQK + d] = 0.0f;
+    for (int d = tid; d < DV; d += kThreads) pend_v[((size_t)n * kPend + pslot) * DV + d] = 0.0f;
     if (evict) {
       for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + n_before) * DQK + d] = sh.ek[d];
       for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + n_before) * DV + d] = sh.ev[d];
@@ -701,9 +774,9 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
 // ---------------------------------------------------------------- prime
 
 // The cached pairs' sums against the linear state of (H, s) and the pending
-// pair: work-group (block of 16 rows, head-state), thread (row e, columns
-// cg, cg + 16, ...): sum_f phi_f(k_e) H_f + (k_e . pend_k)^2 [pend_v | 1],
-// in float32.
+// slots: work-group (block of 16 rows, head-state), thread (row e, columns
+// cg, cg + 16, ...): sum_f phi_f(k_e) H_f + sum_j (k_e . pend_k_j)^2
+// [pend_v_j | 1], in float32.
 template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads) void hdec_prime_kernel(const float* __restrict__ H, const float* __restrict__ s,
                                                               const float* __restrict__ pend_k,
@@ -713,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void hdec_prime_kernel(const float* __res
   constexpr int D = phi_dim(DQK);
   constexpr int CPT = DV / 16;  // columns per thread
   __shared__ float kk[16][DQK];
-  __shared__ float pk[DQK], pv[DV];
+  __shared__ float pk[kPend][DQK], pv[kPend][DV];
   __shared__ uint16_t tab[D];
   const int n = blockIdx.y;
   const int tid = threadIdx.x;
@@ -724,8 +797,8 @@ __global__ __launch_bounds__(kThreads) void hdec_prime_kernel(const float* __res
     const int ee = 16 * blockIdx.x + r;
     kk[r][d] = ee < rows ? cache_k[((size_t)n * lambda + ee) * DQK + d] : 0.0f;
   }
-  for (int d = tid; d < DQK; d += kThreads) pk[d] = pend_k[(size_t)n * DQK + d];
-  for (int d = tid; d < DV; d += kThreads) pv[d] = pend_v[(size_t)n * DV + d];
+  for (int i = tid; i < kPend * DQK; i += kThreads) pk[i / DQK][i % DQK] = pend_k[(size_t)n * kPend * DQK + i];
+  for (int i = tid; i < kPend * DV; i += kThreads) pv[i / DV][i % DV] = pend_v[(size_t)n * kPend * DV + i];
   build_phi_table(tab, 0, D, DQK);
   __syncthreads();
   const float* Hn = H + (size_t)n * D * DV;
@@ -740,14 +813,19 @@ __global__ __launch_bounds__(kThreads) void hdec_prime_kernel(const float* __res
     for (int j = 0; j < CPT; ++j) acc[j] += p * Hn[(size_t)f * DV + cg + 16 * j];
     den += p * sn[f];
   }
-  float dot = 0.0f;
-  for (int d = 0; d < DQK; ++d) dot += kk[el][d] * pk[d];
-  const float wgt = dot * dot;
+  for (int p = 0; p < kPend; ++p) {
+    float dot = 0.0f;
+    for (int d = 0; d < DQK; ++d) dot += kk[el][d] * pk[p][d];
+    const float wgt = dot * dot;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] += wgt * pv[p][cg + 16 * j];
+    den += wgt;
+  }
   if (e < rows) {
     float* dst = cache_sums + ((size_t)n * lambda + e) * (DV + 4);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) dst[cg + 16 * j] = acc[j] + wgt * pv[cg + 16 * j];
-    if (cg == 0) dst[DV] = den + wgt;
+    for (int j = 0; j < CPT; ++j) dst[cg + 16 * j] = acc[j];
+    if (cg == 0) dst[DV] = den;
   }
 }
 
@@ -772,13 +850,20 @@ hipError_t run_hd(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
   const bool refresh = evict && n_before == lam;
   const int n_after = std::min(lam, std::max(0, t - W));
   const int lstride = lin_stride(DV);
+  const bool fold = t % kPend == 0;  // every slot is folded into (H, s); else H is only read
+  const int pslot = t % kPend;       // the slot this call's rejected pair waits in
   prof_begin(st);
   if (use_matrix_pass(a)) {
-    hipLaunchKernelGGL((hdec_state_kernel<Tin>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k, a.pend_v,
-                       static_cast<const Tin*>(a.q), a.win_k, wrows, slot, evict, lin, esum, lstride);
+    if (fold)
+      hipLaunchKernelGGL((hdec_state_kernel<Tin, true>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
+                         a.pend_v, static_cast<const Tin*>(a.q), a.win_k, wrows, slot, evict, lin, esum, lstride);
+    else
+      hipLaunchKernelGGL((hdec_state_kernel<Tin, false>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
+                         a.pend_v, static_cast<const Tin*>(a.q), a.win_k, wrows, slot, evict, lin, esum, lstride);
   } else {
     hipLaunchKernelGGL((hdec_fold_kernel<DQK, DV, Tin, true>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
-                       a.pend_v, static_cast<const Tin*>(a.q), lin, lstride, a.win_k, wrows, slot, evict, esum);
+                       a.pend_v, static_cast<const Tin*>(a.q), lin, lstride, a.win_k, wrows, slot, evict, fold,
+                       esum);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -786,7 +871,7 @@ hipError_t run_hd(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
                      static_cast<Tout*>(a.o), a.win_k, a.win_v, a.cache_k, a.cache_v, a.cache_ids, a.pend_k,
                      a.pend_v, a.rejected, a.cache_sums, esum, lin, lstride, lam, n_before, n_after, refresh, evict,
-                     wrows, std::max(0, t - W), t, slot, evicted_id, a.scale, a.eps);
+                     wrows, std::max(0, t - W), t, slot, pslot, evicted_id, a.scale, a.eps);
   prof_end(st);
   return hipGetLastError();
 }
@@ -832,7 +917,7 @@ hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st)
 #define KLA_CASE(A, B)                                                                                          \
   if (a.dqk == A && a.dv == B) {                                                                                \
     hipLaunchKernelGGL((hdec_fold_kernel<A, B, float, false>), dim3(a.N), dim3(kThreads), 0, st, a.H, a.s,      \
-                       a.pend_k, a.pend_v, nullptr, nullptr, 0, nullptr, 1, 0, false, nullptr);                \
+                       a.pend_k, a.pend_v, nullptr, nullptr, 0, nullptr, 1, 0, false, true, nullptr);          \
     return hipGetLastError();                                                                                   \
   }
   KLA_CASE(16, 16) KLA_CASE(16, 32) KLA_CASE(16, 64)

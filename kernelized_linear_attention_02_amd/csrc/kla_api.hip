@@ -748,6 +748,7 @@ kla_status_t kla_hybrid_decode_step(int N, int d_qk, int d_v, float eps, const k
 }
 
 size_t kla_hybrid_decode_static_limit(void) { return kla::kHybridDecodeStaticScratch; }
+int kla_hybrid_decode_pending_slots(void) { return KLA_HYBRID_PENDING; }
 
 kla_status_t kla_hybrid_decode_step_static(int N, int d_qk, int d_v, float eps, const kla_hybrid_cfg_t* cfg, int t,
                                            const kla_hybrid_state_t* state, const void* q, const void* k,

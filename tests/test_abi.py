@@ -321,6 +321,9 @@ def test_hybrid_decode_static_validation(lib):
     # as the workspace step, then the static scratch limit (all before any
     # device call, so they run without a GPU)
     assert lib.kla_hybrid_decode_static_limit() == 16 << 20
+    # the pending slots of a hybrid decode state, as the header declares them
+    hdr = open(os.path.join(ROOT, "include", "kla.h")).read()
+    assert lib.kla_hybrid_decode_pending_slots() == int(re.search(r"#define KLA_HYBRID_PENDING (\d+)", hdr).group(1))
     st = B.HybridState(*([0x10000] * 10))
     cfg = B.HybridCfg(512, 128, 1, 0.125)
 

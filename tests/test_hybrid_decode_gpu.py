@@ -63,18 +63,20 @@ def _run_gpu(K, q, k, v, W, lam, scale, eps, in_dtype, out_dtype, state=None, t0
 
 
 def _flush_checked(K, st):
-    """Apply the deferred fold and check it: H gains phi(pend_k) pend_v^T and
-    s gains phi(pend_k) (phi from the oracle), the pending pair becomes zero,
-    and a second flush changes nothing."""
+    """Apply the deferred folds and check them: H gains sum_j phi(pend_k_j)
+    pend_v_j^T over the pending slots and s gains sum_j phi(pend_k_j) (phi
+    from the oracle), the slots become zero, and a second flush changes
+    nothing."""
     pk = host(st["pend_k"])
     pv = host(st["pend_v"])
+    assert pk.shape[1] == K.hybrid_decode_pending_slots()
     H0, s0 = host(st["H"]), host(st["s"])
     K.hybrid_decode_flush(st)
     torch.cuda.synchronize()
-    fk = O.phi(pk)
+    fk = O.phi(pk)  # [N, P, D]
     H1, s1 = host(st["H"]), host(st["s"])
-    assert_close(H1, H0 + fk[:, :, None] * pv[:, None, :], RTOL_F32, "flush H")
-    assert_close(s1, s0 + fk, RTOL_F32, "flush s")
+    assert_close(H1, H0 + np.einsum("npf,npv->nfv", fk, pv), RTOL_F32, "flush H")
+    assert_close(s1, s0 + fk.sum(axis=1), RTOL_F32, "flush s")
     assert not st["pend_k"].any() and not st["pend_v"].any()
     K.hybrid_decode_flush(st)
     torch.cuda.synchronize()
