@@ -358,16 +358,17 @@ def hybrid_flops(n_heads, T, d, W, lam, R):
     return dict(total=float(total), fp32_faithful=float(faithful))
 
 
-def hybrid_decode_step_bytes(N, d, W, lam, P):
+def hybrid_decode_step_bytes(N, d, W, lam, P, row_bytes):
     """Algorithmic HBM bytes of one steady-state token-by-token hybrid step
     (window full, cache full, one rejected pair), averaged over the P steps
     of a fold cycle: H and s read once, and written once every P steps (the
     rejected pairs wait in P pending slots and are folded together); the W
-    older window rows and the lam cache rows read once (keys and values,
-    float32); the evicted row read and the replaced cache row and the new
-    window row written; q, k, v (bf16) read and o (bf16) written."""
+    older window rows and the lam cache rows read once (keys and values, in
+    the tokens' type: row_bytes per element); the evicted row read and the
+    replaced cache row and the new window row written; q, k, v (bf16) read
+    and o (bf16) written."""
     D = phi_dim(d)
-    row = 2 * d * 4
+    row = 2 * d * row_bytes
     per = (1.0 + 1.0 / P) * (D * d * 4 + D * 4) + (W + lam) * row + 3 * row + 3 * d * 2 + d * 2 + 2 * 4
     return N * per
 
@@ -377,7 +378,7 @@ def bench_hybrid_decode(torch, K, S, steps=None, cpu_on=False):
     N, d, W, lam, T0 = cfg["N"], cfg["d"], cfg["window"], cfg["cache_size"], cfg["T0"]
     nsteps = cfg["steps"] if steps is None else steps
     q, k, v = S.hybrid_decode_tokens(N, T0 + nsteps, d, cfg["seed"], cfg["dup_frac"])
-    st = K.hybrid_decode_state(N, d, d, W, lam, "cuda")
+    st = K.hybrid_decode_state(N, d, d, W, lam, "cuda", dtype=torch.bfloat16)
     o = torch.empty((N, d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
     t = time.time()
@@ -394,7 +395,7 @@ def bench_hybrid_decode(torch, K, S, steps=None, cpu_on=False):
     step_ms = loop_ms / nsteps
     P = K.hybrid_decode_pending_slots()
     assert nsteps % P == 0, "time whole fold cycles"
-    step_bytes = hybrid_decode_step_bytes(N, d, W, lam, P)
+    step_bytes = hybrid_decode_step_bytes(N, d, W, lam, P, 2)
     achieved = step_bytes / (span_ms * 1e-3) / 1e9
     cpu = None
     if cpu_on:

@@ -79,7 +79,7 @@ typedef enum {
 typedef enum { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KLA_ABI_VERSION 8
+#define KLA_ABI_VERSION 9
 KLA_API int kla_abi_version(void);
 
 /* D = d_qk (d_qk + 1) / 2, or -1 when d_qk < 1. */
@@ -388,14 +388,16 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  * written only by the call t = j (mod P) after the fold that cleared it.
  * kla_hybrid_decode_flush folds every slot into H and s and zeroes them.
  *
- * State (device memory owned by the caller, float32, updated in place):
+ * State (device memory owned by the caller, updated in place; float32 but
+ * for the window and cache rows, which hold the tokens in row_dtype, the
+ * step's in_dtype: bf16 tokens are kept as they are, at half the bytes):
  *   H, s       : [N, D, d_v], [N, D] (zero before the first token).
  *   pend_k/pend_v : [N, P, d_qk] / [N, P, d_v] (zero before the first
  *                token).
- *   win_k/win_v: [N, W + 1, d_qk] / [N, W + 1, d_v]; token i is kept in row
+ *   win_k/win_v: [N, W + 1, d_qk] / [N, W + 1, d_v] (row_dtype); token i is kept in row
  *                i mod (W + 1) while it is in the window.
- *   cache_k/cache_v/cache_ids : [N, lambda, d_qk] / [N, lambda, d_v] /
- *                [N, lambda] int32. Rows 0 .. n-1 hold the cached pairs and
+ *   cache_k/cache_v/cache_ids : [N, lambda, d_qk] / [N, lambda, d_v]
+ *                (row_dtype) / [N, lambda] int32. Rows 0 .. n-1 hold the cached pairs and
  *                their token ids, in no particular order, with
  *                n = min(lambda, max(0, t - W - 1)) before the call and
  *                min(lambda, max(0, t - W)) after it; other rows are unused.
@@ -413,12 +415,14 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  * tokens max(0, t - W - 1) .. t - 1, the cache rows and the state the prefill
  * left, with zero pending slots, then calls kla_hybrid_decode_prime to
  * compute cache_sums.
+ *   row_dtype  : KLA_F32 or KLA_BF16, equal to the step's in_dtype.
  *
  *   q, k : [N, d_qk]; v : [N, d_v]; in_dtype.   o : [N, d_v], out_dtype.
  *   rejected : [N] int32, or NULL: the token id folded by this call (now
  *              in pending slot t mod P), -1 when there was none.
  *   ws : workspace of kla_hybrid_decode_workspace_size bytes.
- * Every state pointer must be 16-byte aligned.
+ * Every state pointer must be 16-byte aligned. A row_dtype other than
+ * in_dtype is KLA_ERR_INVALID_ARGUMENT.
  * Supported: d_qk, d_v in {16, 32, 64}; refresh = 1; window >= 0;
  * 0 <= cache_size <= 255; t >= 0; softmax_scale finite.
  * ------------------------------------------------------------------------ */
@@ -429,14 +433,15 @@ KLA_API int kla_hybrid_decode_pending_slots(void);
 typedef struct {
   float* H;
   float* s;
-  float* win_k;
-  float* win_v;
-  float* cache_k;
-  float* cache_v;
+  void* win_k;
+  void* win_v;
+  void* cache_k;
+  void* cache_v;
   int32_t* cache_ids;
   float* pend_k;
   float* pend_v;
   float* cache_sums;
+  kla_dtype_t row_dtype; /* element type of win_k, win_v, cache_k, cache_v */
 } kla_hybrid_state_t;
 
 KLA_API kla_status_t kla_hybrid_decode_workspace_size(int N, int d_qk, int d_v,

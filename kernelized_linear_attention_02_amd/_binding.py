@@ -63,7 +63,7 @@ class HybridState(ctypes.Structure):
                 ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
                 ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
                 ("cache_ids", ctypes.c_void_p), ("pend_k", ctypes.c_void_p), ("pend_v", ctypes.c_void_p),
-                ("cache_sums", ctypes.c_void_p)]
+                ("cache_sums", ctypes.c_void_p), ("row_dtype", ctypes.c_int)]
 
 
 _lib = None
@@ -458,22 +458,27 @@ def hybrid_prefill(q, k, v, window: int, cache_size: int, refresh: int, softmax_
     return o, dict(H=HT, s=sT, cache=cT, trace=tr)
 
 
-def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: int, device):
+def hybrid_decode_state(N: int, d_qk: int, d_v: int, window: int, cache_size: int, device, dtype=None):
     """Zeroed token-by-token hybrid state for N head-states: a dict of device
     tensors H [N, D, d_v], s [N, D], win_k [N, window+1, d_qk],
     win_v [N, window+1, d_v], cache_k [N, cache_size, d_qk],
     cache_v [N, cache_size, d_v], pend_k [N, P, d_qk], pend_v [N, P, d_v]
     (P = hybrid_decode_pending_slots()),
     cache_sums [N, cache_size, d_v + 4] (float32; numerators, denominator,
-    padding) and cache_ids [N, cache_size] int32."""
+    padding) and cache_ids [N, cache_size] int32. The window and cache rows
+    are in ``dtype`` (float32 or bfloat16, default float32), which must be
+    the dtype of the tokens the steps take; everything else is float32."""
     torch = _torch()
     D = phi_dim(d_qk)
     P = hybrid_decode_pending_slots()
     f32 = dict(dtype=torch.float32, device=device)
+    rdt = torch.float32 if dtype is None else dtype
+    _dtype_code(torch.empty(0, dtype=rdt))  # float32 or bfloat16
+    rows = dict(dtype=rdt, device=device)
     return dict(
         H=torch.zeros((N, D, d_v), **f32), s=torch.zeros((N, D), **f32),
-        win_k=torch.zeros((N, window + 1, d_qk), **f32), win_v=torch.zeros((N, window + 1, d_v), **f32),
-        cache_k=torch.zeros((N, cache_size, d_qk), **f32), cache_v=torch.zeros((N, cache_size, d_v), **f32),
+        win_k=torch.zeros((N, window + 1, d_qk), **rows), win_v=torch.zeros((N, window + 1, d_v), **rows),
+        cache_k=torch.zeros((N, cache_size, d_qk), **rows), cache_v=torch.zeros((N, cache_size, d_v), **rows),
         cache_ids=torch.full((N, cache_size), -1, dtype=torch.int32, device=device),
         pend_k=torch.zeros((N, P, d_qk), **f32), pend_v=torch.zeros((N, P, d_v), **f32),
         cache_sums=torch.zeros((N, cache_size, d_v + 4), **f32))
@@ -487,7 +492,7 @@ def _hybrid_state_struct(state):
         t_ = state[name]
         if not t_.is_cuda or not t_.is_contiguous():
             raise TypeError(f"state['{name}'] must be a contiguous device tensor (updated in place)")
-    return HybridState(*(state[n].data_ptr() for n in _STATE_FIELDS))
+    return HybridState(*(state[n].data_ptr() for n in _STATE_FIELDS), _dtype_code(state["win_k"]))
 
 
 def hybrid_decode_step(state, t: int, q, k, v, window: int, cache_size: int, softmax_scale=None,

@@ -61,6 +61,21 @@ constexpr int kPend = KLA_HYBRID_PENDING;  // pending slots, folded together eve
 constexpr int kKeyTile = 1024;  // softmax keys scored per pass (online max across passes)
 constexpr int kU = 8;           // row loads in flight per lane in the softmax passes
 
+// Four consecutive elements of a window or cache row (rows are kept in the
+// step's input type; 16-byte aligned groups for float32, 8-byte for bf16).
+template <typename T>
+__device__ __forceinline__ float4 ld4(const T* p);
+template <>
+__device__ __forceinline__ float4 ld4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xFFFF0000u));
+}
+
 // Block-wide reductions (kThreads threads); every thread gets the result.
 __device__ __forceinline__ float block_sum(float x, float* red) {
   x = wave_sum(x);
@@ -94,7 +109,7 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 template <int DQK, int DV, typename Tin, bool READ>
 __global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
     float* __restrict__ H, float* __restrict__ s, float* __restrict__ pend_k, float* __restrict__ pend_v,
-    const Tin* __restrict__ q, float* __restrict__ lin, int lstride, const float* __restrict__ win_k, int wrows,
+    const Tin* __restrict__ q, float* __restrict__ lin, int lstride, const Tin* __restrict__ win_k, int wrows,
     int slot, bool evict, bool fold, float* __restrict__ esum) {
   constexpr int D = phi_dim(DQK);
   constexpr int G = kThreads / DV;
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void hdec_fold_kernel(
   const bool ev_on = READ && evict;
   for (int d = tid; d < DQK; d += kThreads) {
     if (READ) qv[d] = Elem<Tin>::load(q, (size_t)n * DQK + d);
-    if (ev_on) ev[d] = win_k[((size_t)n * wrows + slot) * DQK + d];
+    if (ev_on) ev[d] = Elem<Tin>::load(win_k, ((size_t)n * wrows + slot) * DQK + d);
   }
   for (int i = tid; i < kPend * DQK; i += kThreads) kv[i / DQK][i % DQK] = pend_k[(size_t)n * kPend * DQK + i];
   for (int i = tid; i < kPend * DV; i += kThreads) vv[i / DV][i % DV] = pend_v[(size_t)n * kPend * DV + i];
@@ -280,7 +295,7 @@ __device__ __forceinline__ void phi8(const float* x, const TileCoords& tc, float
 template <typename Tin, bool fold>
 __global__ __launch_bounds__(kThreads) void hdec_state_kernel(
     float* __restrict__ H, float* __restrict__ s, float* __restrict__ pend_k, float* __restrict__ pend_v,
-    const Tin* __restrict__ q, const float* __restrict__ win_k, int wrows, int slot, bool evict,
+    const Tin* __restrict__ q, const Tin* __restrict__ win_k, int wrows, int slot, bool evict,
     float* __restrict__ lin, float* __restrict__ esum, int lstride) {
   __shared__ __align__(16) StateLds sh;
   const int n = blockIdx.x;
@@ -311,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void hdec_state_kernel(
 
   if (tid < kFD) {
     sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kFD + tid);
-    sh.ek[tid] = evict ? win_k[((size_t)n * wrows + slot) * kFD + tid] : 0.0f;
+    sh.ek[tid] = evict ? Elem<Tin>::load(win_k, ((size_t)n * wrows + slot) * kFD + tid) : 0.0f;
   }
   for (int i = tid; i < kPend * kFD; i += kThreads) {
     sh.pk[i / kFD][i % kFD] = pend_k[(size_t)n * kPend * kFD + i];
@@ -487,8 +502,8 @@ struct MixLds {
 template <int DQK, int DV, typename Tin, typename Tout>
 __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o,
-    float* __restrict__ win_k, float* __restrict__ win_v, float* __restrict__ cache_k,
-    float* __restrict__ cache_v, int32_t* __restrict__ cache_ids, float* __restrict__ pend_k,
+    Tin* __restrict__ win_k, Tin* __restrict__ win_v, Tin* __restrict__ cache_k,
+    Tin* __restrict__ cache_v, int32_t* __restrict__ cache_ids, float* __restrict__ pend_k,
     float* __restrict__ pend_v, int32_t* __restrict__ rejected, float* __restrict__ cache_sums,
     const float* __restrict__ esum, const float* __restrict__ lin, int lstride, int lambda, int n_before,
     int n_after, bool refresh, bool evict, int wrows, int win_first, int t, int slot, int pslot, int evicted_id,
@@ -506,11 +521,11 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   for (int d = tid; d < DQK; d += kThreads) {
     sh.qv[d] = Elem<Tin>::load(q, (size_t)n * DQK + d);
     sh.kn[d] = Elem<Tin>::load(k, (size_t)n * DQK + d);
-    if (evict) sh.ek[d] = win_k[srow * DQK + d];
+    if (evict) sh.ek[d] = Elem<Tin>::load(win_k, srow * DQK + d);
   }
   for (int d = tid; d < DV; d += kThreads) {
     sh.vn[d] = Elem<Tin>::load(v, (size_t)n * DV + d);
-    if (evict) sh.ev[d] = win_v[srow * DV + d];
+    if (evict) sh.ev[d] = Elem<Tin>::load(win_v, srow * DV + d);
   }
   if (tid == 0) sh.rrow = -1;
 
@@ -537,14 +552,14 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
         float err = 0.0f;
         if (i <= lambda) {
           const float* sm = i < lambda ? cache_sums + ((size_t)n * lambda + i) * DVS : esum + (size_t)n * lstride;
-          const float* vr = i < lambda ? cache_v + ((size_t)n * lambda + i) * DV : win_v + srow * DV;
+          const Tin* vr = i < lambda ? cache_v + ((size_t)n * lambda + i) * DV : win_v + srow * DV;
 #pragma unroll
           for (int j = 0; j < 4; ++j) cs[rr][j] = reinterpret_cast<const float4*>(sm + 16 * part)[j];
           cd[rr] = sm[DV];
           const float dn = cd[rr] + eps;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float4 vv4 = reinterpret_cast<const float4*>(vr + 16 * part)[j];
+            const float4 vv4 = ld4<Tin>(vr + 16 * part + 4 * j);
             const float x[4] = {cs[rr][j].x, cs[rr][j].y, cs[rr][j].z, cs[rr][j].w};
             const float y[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
 #pragma unroll
@@ -580,15 +595,17 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
         if (cache_ids[(size_t)n * lambda + i] == rid) sh.rrow = i;
     __syncthreads();
     const int r = sh.rrow;
-    for (int d = tid; d < DQK; d += kThreads) sh.rk[d] = r >= 0 ? cache_k[((size_t)n * lambda + r) * DQK + d] : sh.ek[d];
-    for (int d = tid; d < DV; d += kThreads) sh.rv[d] = r >= 0 ? cache_v[((size_t)n * lambda + r) * DV + d] : sh.ev[d];
+    for (int d = tid; d < DQK; d += kThreads)
+      sh.rk[d] = r >= 0 ? Elem<Tin>::load(cache_k, ((size_t)n * lambda + r) * DQK + d) : sh.ek[d];
+    for (int d = tid; d < DV; d += kThreads)
+      sh.rv[d] = r >= 0 ? Elem<Tin>::load(cache_v, ((size_t)n * lambda + r) * DV + d) : sh.ev[d];
     __syncthreads();  // row r is read before it is replaced
     // the rejected pair's fold is deferred: it waits in pending slot pslot
     for (int d = tid; d < DQK; d += kThreads) pend_k[((size_t)n * kPend + pslot) * DQK + d] = sh.rk[d];
     for (int d = tid; d < DV; d += kThreads) pend_v[((size_t)n * kPend + pslot) * DV + d] = sh.rv[d];
     if (r >= 0) {
-      for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + r) * DQK + d] = sh.ek[d];
-      for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + r) * DV + d] = sh.ev[d];
+      for (int d = tid; d < DQK; d += kThreads) Elem<Tin>::store(cache_k, ((size_t)n * lambda + r) * DQK + d, sh.ek[d]);
+      for (int d = tid; d < DV; d += kThreads) Elem<Tin>::store(cache_v, ((size_t)n * lambda + r) * DV + d, sh.ev[d]);
       if (tid == 0) cache_ids[(size_t)n * lambda + r] = evicted_id;
     }
     if (rejected && tid == 0) rejected[n] = rid;
@@ -602,10 +619,19 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
         const int i = rr * CPR + ci;
         const bool live = i < lambda;
         const bool fresh = i == r;
-        const float* kr = fresh ? sh.ek : cache_k + ((size_t)n * lambda + (live ? i : 0)) * DQK;
         float dot = 0.0f;
+        if (fresh) {
 #pragma unroll
-        for (int j = 0; j < DPT; ++j) dot += kr[DPT * part + j] * sh.rk[DPT * part + j];
+          for (int j = 0; j < DPT; ++j) dot += sh.ek[DPT * part + j] * sh.rk[DPT * part + j];
+        } else {
+          const Tin* kr = cache_k + ((size_t)n * lambda + (live ? i : 0)) * DQK + DPT * part;
+#pragma unroll
+          for (int j = 0; j < DPT; j += 4) {
+            const float4 x = ld4<Tin>(kr + j);
+            dot += x.x * sh.rk[DPT * part + j] + x.y * sh.rk[DPT * part + j + 1] + x.z * sh.rk[DPT * part + j + 2] +
+                   x.w * sh.rk[DPT * part + j + 3];
+          }
+        }
 #pragma unroll
         for (int off = 1; off < TPC; off <<= 1) dot += __shfl_xor(dot, off, 64);
         const float wgt = dot * dot;
@@ -643,8 +669,10 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     for (int d = tid; d < DQK; d += kThreads) pend_k[((size_t)n * kPend + pslot) * DQK + d] = 0.0f;
     for (int d = tid; d < DV; d += kThreads) pend_v[((size_t)n * kPend + pslot) * DV + d] = 0.0f;
     if (evict) {
-      for (int d = tid; d < DQK; d += kThreads) cache_k[((size_t)n * lambda + n_before) * DQK + d] = sh.ek[d];
-      for (int d = tid; d < DV; d += kThreads) cache_v[((size_t)n * lambda + n_before) * DV + d] = sh.ev[d];
+      for (int d = tid; d < DQK; d += kThreads)
+        Elem<Tin>::store(cache_k, ((size_t)n * lambda + n_before) * DQK + d, sh.ek[d]);
+      for (int d = tid; d < DV; d += kThreads)
+        Elem<Tin>::store(cache_v, ((size_t)n * lambda + n_before) * DV + d, sh.ev[d]);
       for (int d = tid; d <= DV; d += kThreads)
         cache_sums[((size_t)n * lambda + n_before) * (DV + 4) + d] = esum[(size_t)n * lstride + d];
       if (tid == 0) cache_ids[(size_t)n * lambda + n_before] = evicted_id;
@@ -665,17 +693,20 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   const int n_keys = n_old + 1 + n_after;
   const int wbase = win_first % wrows;  // ring row of token win_first; j < n_old <= W keeps wbase + j < 2 wrows
   auto ring = [&](int j) { const int r = wbase + j; return r >= wrows ? r - wrows : r; };
-  auto key_row = [&](int j) -> const float* {
-    if (j < n_old) return win_k + ((size_t)n * wrows + ring(j)) * DQK;
-    if (j == n_old) return sh.kn;
+  // four elements (from `off`) of key or value row j
+  auto key4 = [&](int j, int off) -> float4 {
+    if (j < n_old) return ld4<Tin>(win_k + ((size_t)n * wrows + ring(j)) * DQK + off);
+    if (j == n_old) return *reinterpret_cast<const float4*>(sh.kn + off);
     const int r = j - n_old - 1;
-    return r == replaced ? sh.ek : cache_k + ((size_t)n * lambda + r) * DQK;
+    return r == replaced ? *reinterpret_cast<const float4*>(sh.ek + off)
+                         : ld4<Tin>(cache_k + ((size_t)n * lambda + r) * DQK + off);
   };
-  auto val_row = [&](int j) -> const float* {
-    if (j < n_old) return win_v + ((size_t)n * wrows + ring(j)) * DV;
-    if (j == n_old) return sh.vn;
+  auto val4 = [&](int j, int off) -> float4 {
+    if (j < n_old) return ld4<Tin>(win_v + ((size_t)n * wrows + ring(j)) * DV + off);
+    if (j == n_old) return *reinterpret_cast<const float4*>(sh.vn + off);
     const int r = j - n_old - 1;
-    return r == replaced ? sh.ev : cache_v + ((size_t)n * lambda + r) * DV;
+    return r == replaced ? *reinterpret_cast<const float4*>(sh.ev + off)
+                         : ld4<Tin>(cache_v + ((size_t)n * lambda + r) * DV + off);
   };
   // Scores: LPK lanes per key (a float4 each), KPW keys per wave and step;
   // weighted sum: LPV lanes per value row (a float4 each), RPW rows per wave
@@ -697,8 +728,7 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int jl = jb + u * KPB;
-        k4[u] = jl < nt ? *reinterpret_cast<const float4*>(key_row(j0 + jl) + 4 * (lane % LPK))
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        k4[u] = jl < nt ? key4(j0 + jl, 4 * (lane % LPK)) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -732,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
       for (int u = 0; u < kU; ++u) {
         const int jl = jb + u * RPB;
         const bool in = jl < nt;
-        v4[u] = in ? *reinterpret_cast<const float4*>(val_row(j0 + jl) + vc) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v4[u] = in ? val4(j0 + jl, vc) : make_float4(0.f, 0.f, 0.f, 0.f);
         pw[u] = in ? sh.sc[jl] : 0.0f;
       }
 #pragma unroll
@@ -767,8 +797,8 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   }
   // ---- the new token enters the window, in the evicted token's row (whose
   // values were copied to LDS before the first barrier)
-  for (int d = tid; d < DQK; d += kThreads) win_k[srow * DQK + d] = sh.kn[d];
-  for (int d = tid; d < DV; d += kThreads) win_v[srow * DV + d] = sh.vn[d];
+  for (int d = tid; d < DQK; d += kThreads) Elem<Tin>::store(win_k, srow * DQK + d, sh.kn[d]);
+  for (int d = tid; d < DV; d += kThreads) Elem<Tin>::store(win_v, srow * DV + d, sh.vn[d]);
 }
 
 // ---------------------------------------------------------------- prime
@@ -777,11 +807,11 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
 // slots: work-group (block of 16 rows, head-state), thread (row e, columns
 // cg, cg + 16, ...): sum_f phi_f(k_e) H_f + sum_j (k_e . pend_k_j)^2
 // [pend_v_j | 1], in float32.
-template <int DQK, int DV>
+template <int DQK, int DV, typename R>
 __global__ __launch_bounds__(kThreads) void hdec_prime_kernel(const float* __restrict__ H, const float* __restrict__ s,
                                                               const float* __restrict__ pend_k,
                                                               const float* __restrict__ pend_v,
-                                                              const float* __restrict__ cache_k, int lambda,
+                                                              const R* __restrict__ cache_k, int lambda,
                                                               int rows, float* __restrict__ cache_sums) {
   constexpr int D = phi_dim(DQK);
   constexpr int CPT = DV / 16;  // columns per thread
@@ -795,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void hdec_prime_kernel(const float* __res
   for (int i = tid; i < 16 * DQK; i += kThreads) {
     const int r = i / DQK, d = i % DQK;
     const int ee = 16 * blockIdx.x + r;
-    kk[r][d] = ee < rows ? cache_k[((size_t)n * lambda + ee) * DQK + d] : 0.0f;
+    kk[r][d] = ee < rows ? Elem<R>::load(cache_k, ((size_t)n * lambda + ee) * DQK + d) : 0.0f;
   }
   for (int i = tid; i < kPend * DQK; i += kThreads) pk[i / DQK][i % DQK] = pend_k[(size_t)n * kPend * DQK + i];
   for (int i = tid; i < kPend * DV; i += kThreads) pv[i / DV][i % DV] = pend_v[(size_t)n * kPend * DV + i];
@@ -851,25 +881,27 @@ hipError_t run_hd(const HybridDecodeArgs& a, void* ws, hipStream_t st) {
   const int n_after = std::min(lam, std::max(0, t - W));
   const int lstride = lin_stride(DV);
   const bool fold = t % kPend == 0;  // every slot is folded into (H, s); else H is only read
+  Tin* wk = static_cast<Tin*>(a.win_k);  // window and cache rows are kept in the input type
   const int pslot = t % kPend;       // the slot this call's rejected pair waits in
   prof_begin(st);
   if (use_matrix_pass(a)) {
     if (fold)
       hipLaunchKernelGGL((hdec_state_kernel<Tin, true>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
-                         a.pend_v, static_cast<const Tin*>(a.q), a.win_k, wrows, slot, evict, lin, esum, lstride);
+                         a.pend_v, static_cast<const Tin*>(a.q), wk, wrows, slot, evict, lin, esum, lstride);
     else
       hipLaunchKernelGGL((hdec_state_kernel<Tin, false>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
-                         a.pend_v, static_cast<const Tin*>(a.q), a.win_k, wrows, slot, evict, lin, esum, lstride);
+                         a.pend_v, static_cast<const Tin*>(a.q), wk, wrows, slot, evict, lin, esum, lstride);
   } else {
     hipLaunchKernelGGL((hdec_fold_kernel<DQK, DV, Tin, true>), dim3(N), dim3(kThreads), 0, st, a.H, a.s, a.pend_k,
-                       a.pend_v, static_cast<const Tin*>(a.q), lin, lstride, a.win_k, wrows, slot, evict, fold,
+                       a.pend_v, static_cast<const Tin*>(a.q), lin, lstride, wk, wrows, slot, evict, fold,
                        esum);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((hdec_mix_kernel<DQK, DV, Tin, Tout>), dim3(N), dim3(kThreads), 0, st,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
-                     static_cast<Tout*>(a.o), a.win_k, a.win_v, a.cache_k, a.cache_v, a.cache_ids, a.pend_k,
+                     static_cast<Tout*>(a.o), wk, static_cast<Tin*>(a.win_v), static_cast<Tin*>(a.cache_k),
+                     static_cast<Tin*>(a.cache_v), a.cache_ids, a.pend_k,
                      a.pend_v, a.rejected, a.cache_sums, esum, lin, lstride, lam, n_before, n_after, refresh, evict,
                      wrows, std::max(0, t - W), t, slot, pslot, evicted_id, a.scale, a.eps);
   prof_end(st);
@@ -900,11 +932,17 @@ hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t
 hipError_t hybrid_decode_prime_launch(const HybridDecodeArgs& a, hipStream_t st) {
   const int rows = std::min(a.cache_size, std::max(0, a.t - a.window - 1));
   if (rows == 0) return hipSuccess;
-#define KLA_CASE(A, B)                                                                                            \
-  if (a.dqk == A && a.dv == B) {                                                                                  \
-    hipLaunchKernelGGL((hdec_prime_kernel<A, B>), dim3((rows + 15) / 16, a.N), dim3(kThreads), 0, st, a.H, a.s,   \
-                       a.pend_k, a.pend_v, a.cache_k, a.cache_size, rows, a.cache_sums);                         \
-    return hipGetLastError();                                                                                     \
+#define KLA_CASE(A, B)                                                                                             \
+  if (a.dqk == A && a.dv == B) {                                                                                   \
+    if (a.in_bf16)                                                                                                 \
+      hipLaunchKernelGGL((hdec_prime_kernel<A, B, uint16_t>), dim3((rows + 15) / 16, a.N), dim3(kThreads), 0, st, \
+                         a.H, a.s, a.pend_k, a.pend_v, static_cast<const uint16_t*>(a.cache_k), a.cache_size, rows, \
+                         a.cache_sums);                                                                            \
+    else                                                                                                           \
+      hipLaunchKernelGGL((hdec_prime_kernel<A, B, float>), dim3((rows + 15) / 16, a.N), dim3(kThreads), 0, st,    \
+                         a.H, a.s, a.pend_k, a.pend_v, static_cast<const float*>(a.cache_k), a.cache_size, rows,   \
+                         a.cache_sums);                                                                            \
+    return hipGetLastError();                                                                                      \
   }
   KLA_CASE(16, 16) KLA_CASE(16, 32) KLA_CASE(16, 64)
   KLA_CASE(32, 16) KLA_CASE(32, 32) KLA_CASE(32, 64)

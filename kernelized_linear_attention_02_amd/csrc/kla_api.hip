@@ -697,6 +697,9 @@ kla_status_t hybrid_decode_args(const char* fn, int N, int d_qk, int d_v, float 
       !aligned16(S.cache_k) || !aligned16(S.cache_v) || !aligned16(S.cache_ids) || !aligned16(S.pend_k) ||
       !aligned16(S.pend_v) || !aligned16(S.cache_sums))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state pointers must be 16-byte aligned", fn);
+  if (S.row_dtype != in_dtype)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: the state's row_dtype (%d) must be the step's in_dtype (%d)", fn,
+                (int)S.row_dtype, (int)in_dtype);
   st = check_align(fn, {{"q", q}, {"k", k}, {"v", v}, {"o", o}, {"rejected", rejected}, {"ws", ws}});
   if (st != KLA_OK) return st;
   kla::HybridDecodeArgs& a = *out;
@@ -804,6 +807,7 @@ kla_status_t kla_hybrid_decode_prime(int N, int d_qk, int d_v, const kla_hybrid_
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: state H, s, pend_k, pend_v are required", fn);
   if (cfg->cache_size > 0 && (!state->cache_k || !state->cache_sums))
     return fail(KLA_ERR_INVALID_ARGUMENT, "%s: cache_k, cache_sums are required when cache_size > 0", fn);
+  if (!dtype_ok(state->row_dtype)) return fail(KLA_ERR_UNSUPPORTED, "%s: unknown row_dtype", fn);
   st = check_align(fn, {{"H", state->H}, {"s", state->s}, {"pend_k", state->pend_k}, {"pend_v", state->pend_v},
                         {"cache_k", state->cache_k}, {"cache_sums", state->cache_sums}});
   if (st != KLA_OK) return st;
@@ -814,6 +818,7 @@ kla_status_t kla_hybrid_decode_prime(int N, int d_qk, int d_v, const kla_hybrid_
   a.window = cfg->window;
   a.cache_size = cfg->cache_size;
   a.t = t;
+  a.in_bf16 = state->row_dtype == KLA_BF16;
   a.H = state->H;
   a.s = state->s;
   a.pend_k = state->pend_k;

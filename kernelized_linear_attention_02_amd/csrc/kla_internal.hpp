@@ -147,14 +147,14 @@ struct HybridDecodeArgs {
   int t;  // tokens each head-state has seen before this one
   float* H;
   float* s;
-  float* win_k;
-  float* win_v;
-  float* cache_k;
-  float* cache_v;
+  void* win_k;  // window and cache rows, in the input type (in_bf16)
+  void* win_v;
+  void* cache_k;
+  void* cache_v;
   int32_t* cache_ids;
-  float* pend_k;  // the rejected pair whose fold is deferred to the next call
+  float* pend_k;  // [N][KLA_HYBRID_PENDING][dqk]: rejected pairs whose folds are deferred
   float* pend_v;
-  float* cache_sums;  // [N][cache_size][dv + 4]: the cached pairs' sums against H + the pending fold
+  float* cache_sums;  // [N][cache_size][dv + 4]: the cached pairs' sums against H + the pending slots
   const void* q;
   const void* k;
   const void* v;

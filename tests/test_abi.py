@@ -249,8 +249,14 @@ def test_prefill_quadratic_backward_rejects(lib):
         B.KLA_ERR_INVALID_ARGUMENT
 
 
+def _hstate(*ptrs, row=B.KLA_BF16):
+    """A hybrid decode state of fake device pointers whose rows are bf16 (the
+    in_dtype these checks pass)."""
+    return B.HybridState(*ptrs, row)
+
+
 def test_hybrid_decode_validation(lib):
-    st = B.HybridState(*([0x10000] * 10))
+    st = _hstate(*([0x10000] * 10))
     cfg = B.HybridCfg(512, 128, 1, 0.125)
 
     def call(cfg=cfg, N=8, dqk=64, dv=64, t=600, state=st, o=P, ws=P, nbytes=1 << 40, eps=0.0,
@@ -272,23 +278,27 @@ def test_hybrid_decode_validation(lib):
     assert call(in_dtype=7) == B.KLA_ERR_UNSUPPORTED
     assert call(state=None) == B.KLA_ERR_INVALID_ARGUMENT
     assert call(o=None) == B.KLA_ERR_INVALID_ARGUMENT
-    no_cache = B.HybridState(0x10000, 0x10000, 0x10000, 0x10000, None, None, None, 0x10000, 0x10000, None)
+    no_cache = _hstate(0x10000, 0x10000, 0x10000, 0x10000, None, None, None, 0x10000, 0x10000, None)
     assert call(state=no_cache) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"cache_size > 0" in lib.kla_last_error()
     # without a cache, the cache pointers may be NULL (only the workspace check is left)
     assert call(cfg=B.HybridCfg(512, 0, 1, 0.125), state=no_cache, ws=None) == B.KLA_ERR_WORKSPACE
-    odd = B.HybridState(0x10000, 0x10004, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+    odd = _hstate(0x10000, 0x10004, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
     assert call(state=odd) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"aligned" in lib.kla_last_error()
-    odd_sums = B.HybridState(*([0x10000] * 9), 0x10004)
+    odd_sums = _hstate(*([0x10000] * 9), 0x10004)
     assert call(state=odd_sums) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"aligned" in lib.kla_last_error()
-    no_sums = B.HybridState(*([0x10000] * 9), None)
+    no_sums = _hstate(*([0x10000] * 9), None)
     assert call(state=no_sums) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"cache_sums" in lib.kla_last_error()
-    no_pend = B.HybridState(*([0x10000] * 7), None, None, 0x10000)
+    no_pend = _hstate(*([0x10000] * 7), None, None, 0x10000)
     assert call(state=no_pend) == B.KLA_ERR_INVALID_ARGUMENT
     assert b"pend_k" in lib.kla_last_error()
+    # the window and cache rows must be in the step's input type
+    f32_rows = _hstate(*([0x10000] * 10), row=B.KLA_F32)
+    assert call(state=f32_rows) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"row_dtype" in lib.kla_last_error()
 
     need = ctypes.c_size_t(0)
     assert lib.kla_hybrid_decode_workspace_size(8, 64, 64, ctypes.byref(cfg), ctypes.byref(need)) == B.KLA_OK
@@ -306,6 +316,8 @@ def test_hybrid_decode_validation(lib):
 
     prime = lib.kla_hybrid_decode_prime
     assert prime(8, 64, 64, ctypes.byref(cfg), 600, None, None) == B.KLA_ERR_INVALID_ARGUMENT
+    bad_rows = _hstate(*([0x10000] * 10), row=7)
+    assert prime(8, 64, 64, ctypes.byref(cfg), 600, ctypes.byref(bad_rows), None) == B.KLA_ERR_UNSUPPORTED
     assert prime(8, 64, 64, None, 600, ctypes.byref(st), None) == B.KLA_ERR_INVALID_ARGUMENT
     assert prime(8, 64, 64, ctypes.byref(cfg), -1, ctypes.byref(st), None) == B.KLA_ERR_INVALID_ARGUMENT
     assert prime(8, 48, 64, ctypes.byref(cfg), 600, ctypes.byref(st), None) == B.KLA_ERR_UNSUPPORTED
@@ -324,7 +336,7 @@ def test_hybrid_decode_static_validation(lib):
     # the pending slots of a hybrid decode state, as the header declares them
     hdr = open(os.path.join(ROOT, "include", "kla.h")).read()
     assert lib.kla_hybrid_decode_pending_slots() == int(re.search(r"#define KLA_HYBRID_PENDING (\d+)", hdr).group(1))
-    st = B.HybridState(*([0x10000] * 10))
+    st = _hstate(*([0x10000] * 10))
     cfg = B.HybridCfg(512, 128, 1, 0.125)
 
     def call(cfg=cfg, N=8, t=600, state=st, o=P, q=P):
@@ -384,11 +396,11 @@ def test_every_call_rejects_misaligned_pointers(lib):
     _misaligned(lib, lib.kla_hybrid_prefill_streams(ctypes.byref(shp), ctypes.byref(cfg), P, P, P, P, None, None,
                                                     None, M, P, 1 << 40, None, None))
     # token-by-token hybrid decode, its flush and its prime
-    st = B.HybridState(*([0x10000] * 10))
+    st = _hstate(*([0x10000] * 10))
     hcfg = B.HybridCfg(512, 128, 1, 0.125)
     _misaligned(lib, lib.kla_hybrid_decode_step(8, 64, 64, 0.0, ctypes.byref(hcfg), 600, ctypes.byref(st), P, P,
                                                 M, B.KLA_BF16, P, B.KLA_F32, None, P, 1 << 40, None))
-    bad_pend = B.HybridState(*([0x10000] * 7), 0x10004, 0x10000, 0x10000)
+    bad_pend = _hstate(*([0x10000] * 7), 0x10004, 0x10000, 0x10000)
     _misaligned(lib, lib.kla_hybrid_decode_flush(8, 64, 64, ctypes.byref(bad_pend), None))
     _misaligned(lib, lib.kla_hybrid_decode_prime(8, 64, 64, ctypes.byref(hcfg), 600, ctypes.byref(bad_pend), None))
 

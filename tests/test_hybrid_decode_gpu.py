@@ -50,7 +50,7 @@ def _gaussian_heads(N, T, dqk, dv, seed):
 def _run_gpu(K, q, k, v, W, lam, scale, eps, in_dtype, out_dtype, state=None, t0=0):
     N, T, dqk = q.shape
     dv = v.shape[-1]
-    st = state if state is not None else K.hybrid_decode_state(N, dqk, dv, W, lam, "cuda")
+    st = state if state is not None else K.hybrid_decode_state(N, dqk, dv, W, lam, "cuda", dtype=in_dtype)
     qd, kd, vd = dev(q, in_dtype), dev(k, in_dtype), dev(v, in_dtype)
     outs, rejs = [], []
     for t in range(t0, T):
@@ -186,7 +186,7 @@ def test_hybrid_decode_4096_full_size(K):
     q, k, v = S.hybrid_decode_tokens(N, T, d, cfg["seed"], cfg["dup_frac"])
     heads = [0, 2901]
     hidx = torch.tensor(heads, device="cuda")
-    st = K.hybrid_decode_state(N, d, d, W, lam, "cuda")
+    st = K.hybrid_decode_state(N, d, d, W, lam, "cuda", dtype=torch.bfloat16)
     o = torch.empty((N, d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
     rej = torch.empty((T, N), dtype=torch.int32, device="cuda")

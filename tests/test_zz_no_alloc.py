@@ -29,7 +29,7 @@ def K():
 
 def _filled_state(K, q, k, v, W, lam, T0):
     N, d = q.shape[1], q.shape[2]
-    st = K.hybrid_decode_state(N, d, v.shape[-1], W, lam, "cuda")
+    st = K.hybrid_decode_state(N, d, v.shape[-1], W, lam, "cuda", dtype=q.dtype)
     for t in range(T0):
         K.hybrid_decode_step(st, t, q[t], k[t], v[t], W, lam)
     return st
@@ -89,7 +89,7 @@ def test_static_step_matches_workspace_step_twice(K):
 
 def test_static_step_other_path_after_a_larger_call(K):
     # a larger call on the matrix-core path, then a small float32 call with
-    # d_qk = 32, d_v = 16 (the fold + scoring kernels), which reads less of
+    # d_qk = 32, d_v = 16 (the generic state pass and the mix), which reads less of
     # the array than the call before wrote
     N, d, W, lam = 512, 64, 16, 64
     T0 = W + 1 + lam + 3
