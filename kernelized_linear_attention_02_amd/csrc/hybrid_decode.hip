@@ -542,6 +542,10 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   const int ci = tid / TPC, part = tid % TPC;
   int replaced = -1;  // the cache row the evicted pair now holds
   if (refresh) {
+    // candidate tid's token id (lambda + 1 <= kThreads: one candidate a
+    // thread), loaded beside the scoring's loads
+    static_assert(kThreads >= 256, "one selection candidate per thread");
+    const int myid = tid < lambda ? cache_ids[(size_t)n * lambda + tid] : evicted_id;
     float4 cs[NR][4];  // this thread's 16 columns of its candidate in each round
     float cd[NR];      // and the denominator
     if (lambda > 0) {
@@ -577,10 +581,9 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
     }
     __syncthreads();
     unsigned long long worst = ~0ull;
-    for (int i = tid; i <= lambda; i += kThreads) {
-      const int id = i < lambda ? cache_ids[(size_t)n * lambda + i] : evicted_id;
-      const float x = lambda > 0 ? sh.err[i] : 0.0f;  // a lone candidate is not scored
-      worst = min(worst, (unsigned long long)topk_key(x, (uint32_t)id));
+    if (tid <= lambda) {
+      const float x = lambda > 0 ? sh.err[tid] : 0.0f;  // a lone candidate is not scored
+      worst = (unsigned long long)topk_key(x, (uint32_t)myid);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) worst = min(worst, __shfl_xor(worst, off, 64));
@@ -590,9 +593,7 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) m = min(m, sh.kred[i]);
     const int rid = (int)topk_index(m);
-    if (rid != evicted_id)
-      for (int i = tid; i < lambda; i += kThreads)
-        if (cache_ids[(size_t)n * lambda + i] == rid) sh.rrow = i;
+    if (rid != evicted_id && tid < lambda && myid == rid) sh.rrow = tid;
     __syncthreads();
     const int r = sh.rrow;
     for (int d = tid; d < DQK; d += kThreads)
