@@ -175,6 +175,45 @@ def test_hybrid_decode_continues_a_prefill(K):
            pre_trace=extra["trace"][0].cpu().numpy())
 
 
+def test_hybrid_decode_continues_a_prefill_bf16_rows(K):
+    # The same recipe with bf16 tokens (d = 64): the prefill runs on float32
+    # tensors holding the bf16-rounded values (the vector path), and the
+    # decode state keeps its window and cache rows in bf16, so the prime
+    # reads bf16 cache keys.
+    N, T0, T, d, W, lam = 2, 180, 300, 64, 32, 20
+    c = S.hybrid_case("hdec_bf16_cont", 1, N, T, d, W, lam, 1, seed=903, dup_frac=0.1)
+    q, k, v = (x[0] for x in (c.q, c.k, c.v))  # [N, T, d], bf16-rounded
+    scale = 0.125
+    _, extra = K.hybrid_prefill(dev(q[None, :, :T0]), dev(k[None, :, :T0]), dev(v[None, :, :T0]), W, lam, 1,
+                                scale, return_state=True, return_cache=True, return_trace=True)
+    st = K.hybrid_decode_state(N, d, d, W, lam, "cuda", dtype=torch.bfloat16)
+    assert st["win_k"].dtype == torch.bfloat16 and st["cache_v"].dtype == torch.bfloat16
+    st["H"].copy_(extra["H"][0])
+    st["s"].copy_(extra["s"][0])
+    ids = extra["cache"][0].cpu().numpy()
+    for n in range(N):
+        for r, i in enumerate(ids[n]):
+            if i >= 0:
+                st["cache_k"][n, r] = dev(k[n, i], torch.bfloat16)
+                st["cache_v"][n, r] = dev(v[n, i], torch.bfloat16)
+                st["cache_ids"][n, r] = int(i)
+        for i in range(max(0, T0 - W - 1), T0):
+            st["win_k"][n, i % (W + 1)] = dev(k[n, i], torch.bfloat16)
+            st["win_v"][n, i % (W + 1)] = dev(v[n, i], torch.bfloat16)
+    K.hybrid_decode_prime(st, T0, W, lam)
+    go, grej, st = _run_gpu(K, q, k, v, W, lam, scale, 0.0, torch.bfloat16, torch.float32, state=st, t0=T0)
+    _check(q, k, v, W, lam, scale, 0.0, go, grej, st, RTOL_F32, t0=T0,
+           pre_trace=extra["trace"][0].cpu().numpy())
+
+
+def test_hybrid_decode_rows_must_match_the_tokens(K):
+    # a bf16-row state stepped with float32 tokens is refused before any launch
+    st = K.hybrid_decode_state(2, 16, 16, 4, 2, "cuda", dtype=torch.bfloat16)
+    x = torch.zeros((2, 16), device="cuda")
+    with pytest.raises(Exception, match="row_dtype"):
+        K.hybrid_decode_step(st, 0, x, x, x, 4, 2)
+
+
 def test_hybrid_decode_4096_full_size(K):
     # The benchmark's workload and launch configuration: 4096 head-states,
     # window 512, cache 128, bf16 tokens, 2048 filling tokens then 128 steps.
