@@ -394,33 +394,36 @@ KLA_API kla_status_t kla_hybrid_prefill_streams(const kla_shape_t* shp, const kl
  *   H, s       : [N, D, d_v], [N, D] (zero before the first token).
  *   pend_k/pend_v : [N, P, d_qk] / [N, P, d_v] (zero before the first
  *                token).
- *   win_k/win_v: [N, W + 1, d_qk] / [N, W + 1, d_v] (row_dtype); token i is kept in row
- *                i mod (W + 1) while it is in the window.
+ *   win_k/win_v: [N, W + 1, d_qk] / [N, W + 1, d_v] (row_dtype); token i
+ *                is kept in row i mod (W + 1) while it is in the window.
  *   cache_k/cache_v/cache_ids : [N, lambda, d_qk] / [N, lambda, d_v]
- *                (row_dtype) / [N, lambda] int32. Rows 0 .. n-1 hold the cached pairs and
- *                their token ids, in no particular order, with
+ *                (row_dtype) / [N, lambda] int32. Rows 0 .. n-1 hold the
+ *                cached pairs and their token ids, in no particular order, with
  *                n = min(lambda, max(0, t - W - 1)) before the call and
  *                min(lambda, max(0, t - W)) after it; other rows are unused.
  *                May be NULL when lambda = 0.
  *   cache_sums : [N, lambda, d_v + 4]: for cached row i, the sums of its key
  *                against the linear state (pending slots included),
  *                (phi(k_i)^T H', phi(k_i)^T s'), in columns 0 .. d_v - 1 and
- *                d_v (the last three of a row are padding, for 16-byte rows). Each call keeps them: a
+ *                d_v (the last three of a row are padding, for 16-byte
+ *                rows). Each call keeps them: a
  *                fold of pair r adds (k_i . k_r)^2 [v_r | 1] (KATA page §2.2:
  *                phi(x) . phi(y) = (x . y)^2), and a pair entering the cache
  *                takes its sums from the call's pass over H. The refresh
  *                scores candidates from them. Zero for a zero state; may be
  *                NULL when lambda = 0.
+ *   row_dtype  : KLA_F32 or KLA_BF16, equal to the step's in_dtype.
  * To continue from a prefill of t tokens, the caller fills the window rows of
  * tokens max(0, t - W - 1) .. t - 1, the cache rows and the state the prefill
  * left, with zero pending slots, then calls kla_hybrid_decode_prime to
  * compute cache_sums.
- *   row_dtype  : KLA_F32 or KLA_BF16, equal to the step's in_dtype.
  *
  *   q, k : [N, d_qk]; v : [N, d_v]; in_dtype.   o : [N, d_v], out_dtype.
  *   rejected : [N] int32, or NULL: the token id folded by this call (now
  *              in pending slot t mod P), -1 when there was none.
- *   ws : workspace of kla_hybrid_decode_workspace_size bytes.
+ *   ws : workspace of kla_hybrid_decode_workspace_size bytes (per
+ *        head-state, the linear readouts of the query and of the evicted
+ *        key).
  * Every state pointer must be 16-byte aligned. A row_dtype other than
  * in_dtype is KLA_ERR_INVALID_ARGUMENT.
  * Supported: d_qk, d_v in {16, 32, 64}; refresh = 1; window >= 0;

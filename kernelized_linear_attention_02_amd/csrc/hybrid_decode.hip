@@ -969,7 +969,8 @@ hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st)
 // ---------------------------------------------------------------- static scratch
 
 // Scratch for callers that cannot allocate (HIP graph capture, serving loops,
-// harnesses that forbid device allocation): the scores and linear readouts of
+// harnesses that forbid device allocation): the linear readouts of the query
+// and of the evicted key (two rows of d_v + 4 floats per head-state) of
 // kla_hybrid_decode_step_static live in this array instead of a caller
 // workspace. Each device that the library runs on holds its own copy until
 // the process ends. Every call on a device uses that device's copy, so calls

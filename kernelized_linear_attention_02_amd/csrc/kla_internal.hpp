@@ -164,9 +164,9 @@ struct HybridDecodeArgs {
 
 size_t hybrid_decode_workspace(const HybridDecodeArgs& a);
 hipError_t hybrid_decode_launch(const HybridDecodeArgs& a, void* ws, hipStream_t st);
-// Folds the pending pair into (H, s) and clears it (uses N, dqk, dv, H, s, pend_k, pend_v).
+// Folds the pending slots into (H, s) and clears them (uses N, dqk, dv, H, s, pend_k, pend_v).
 hipError_t hybrid_decode_flush_launch(const HybridDecodeArgs& a, hipStream_t st);
-// Computes cache_sums for the cached rows of step t from H, s and the pending pair.
+// Computes cache_sums for the cached rows of step t from H, s and the pending slots.
 hipError_t hybrid_decode_prime_launch(const HybridDecodeArgs& a, hipStream_t st);
 
 // Size of the library's static scratch for the allocation-free hybrid decode
