@@ -226,7 +226,7 @@ def bench_prefill_backward(torch, K, S, name, steps, warmup):
     )
 
 
-def bench_decode(torch, K, S, steps_loop, reps):
+def bench_decode(torch, K, S, steps_loop, reps, deferred=False):
     cfg = S.CONFIGS["decode_sre_4096x128"]
     N, d, T0, top, nf = cfg["N"], cfg["d"], cfg["T0"], cfg["top_k"], cfg["n_fresh"]
     nsteps = cfg["steps"] if steps_loop is None else steps_loop
@@ -257,27 +257,62 @@ def bench_decode(torch, K, S, steps_loop, reps):
     sc = torch.empty((N, n_cand), device=dev)
     sel = torch.empty((N, top), dtype=torch.int32, device=dev)
 
+    P = K.decode_pending_period()
+    if deferred:
+        pend_k, pend_v = K.decode_pending_slots(N, d, d)
+
     def loop():
+        n_pend = 0
         for i in range(nsteps):
-            K.decode_step(H, s, q[i], k[i], v[i], cand_k=ck[i], cand_v=cv[i], top_k=top, gather=True,
-                          out=dict(o=o, scores=sc, sel=sel, sel_k=ck[i + 1], sel_v=cv[i + 1],
-                                   sel_stride=n_cand))
+            out = dict(o=o, scores=sc, sel=sel, sel_k=ck[i + 1], sel_v=cv[i + 1], sel_stride=n_cand)
+            if deferred:
+                K.decode_step_deferred(H, s, pend_k, pend_v, n_pend, q[i], k[i], v[i], cand_k=ck[i],
+                                       cand_v=cv[i], top_k=top, gather=True, out=out)
+                n_pend = (n_pend + 1) % P
+            else:
+                K.decode_step(H, s, q[i], k[i], v[i], cand_k=ck[i], cand_v=cv[i], top_k=top, gather=True,
+                              out=out)
+        if deferred:
+            K.decode_flush(H, s, pend_k, pend_v, n_pend)
 
     loop_ms, kern_ms, per_loop = timed_calls(torch, K, loop, reps, 1)
     D = phi_dim(d)
-    # one fused launch per step: H and s read and written, q, k, v, o, the
-    # candidates' keys and values read, the kept rows, scores and indices written
-    step_bytes = N * (2 * D * d * 4 + 2 * D * 4 + 4 * d * 4 + 2 * n_cand * d * 4 + 2 * top * d * 4
-                      + n_cand * 4 + top * 4)
-    achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+    state = D * d * 4 + D * 4
+    # per step: q, k, v, o, the candidates' keys and values read, the kept
+    # rows, scores and indices written
+    io = 4 * d * 4 + 2 * n_cand * d * 4 + 2 * top * d * 4 + n_cand * 4 + top * 4
     step_ms = loop_ms / nsteps
+    if not deferred:
+        # one fused launch per step: H and s read and written
+        step_bytes = N * (2 * state + io)
+        achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+        return dict(
+            workload="decode_sre_4096x128", N=N, steps=nsteps, step_ms=step_ms,
+            steps_per_s=1e3 / step_ms, kernel_ms=kern_ms,
+            roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                          frac=achieved / PEAK_HBM_GBS,
+                          traffic=measured_traffic("decode_fused.hip",
+                                                   "decode_sre_kernel_decode_sre_4096x128_traffic.md"),
+                          kernel="decode step + SRE + top-k (fused)", bytes_per_launch=step_bytes),
+        )
+    # deferred folds: the step kernel reads H and s, the pending slots in use
+    # (on average (P - 1) / 2 of them) and writes the token's slot; every P
+    # steps a fold kernel reads and writes H and s and reads the P slots
+    read_bytes = N * (state + io + (P - 1) / 2 * 2 * d * 4 + 2 * d * 4)
+    fold_bytes = N * (2 * state + P * 2 * d * 4)
+    achieved = read_bytes / (kern_ms * 1e-3) / 1e9
+    avg_bytes = read_bytes + fold_bytes / P
     return dict(
-        workload="decode_sre_4096x128", N=N, steps=nsteps, step_ms=step_ms,
-        steps_per_s=1e3 / step_ms, kernel_ms=kern_ms,
+        workload="decode_sre_4096x128 (deferred folds)", N=N, steps=nsteps, pending_period=P,
+        step_ms=step_ms, steps_per_s=1e3 / step_ms, kernel_ms=kern_ms,
+        step_bytes_avg=avg_bytes, step_tb_per_s=avg_bytes / (step_ms * 1e-3) / 1e12,
+        step_frac_of_peak=avg_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=achieved / PEAK_HBM_GBS,
-                      traffic=measured_traffic("decode_fused.hip", "decode_sre_kernel_decode_sre_4096x128_traffic.md"),
-                      kernel="decode step + SRE + top-k (fused)", bytes_per_launch=step_bytes),
+                      traffic=measured_traffic("decode_fused.hip",
+                                               "decode_sre_kernel_decode_sre_4096x128_deferred_traffic.md"),
+                      kernel="read-only decode step + SRE + top-k over the state and its pending pairs",
+                      bytes_per_launch=read_bytes),
     )
 
 
@@ -592,7 +627,7 @@ def main():
                                        "prefill_4x8x4096_m2_state", "prefill_1x16x65536_m2_state",
                                        "prefill_4x8x4096_sigma2_state",
                                        "prefill_4x8x4096_backward", "decode_sre_4096x128",
-                                       "hybrid_2x16x16384", "hybrid_decode_4096"],
+                                       "decode_sre_4096x128_deferred", "hybrid_2x16x16384", "hybrid_decode_4096"],
                     help="run just this secondary workload and print its line (for profiling)")
     ap.add_argument("--stream-ceiling", type=int, default=0, metavar="MIB",
                     help="only time plain streaming (in-place multiply, copy, in-place add) over MIB-MiB buffers")
@@ -639,6 +674,8 @@ def main():
             r = bench_prefill_backward(torch, K, S, "prefill_4x8x4096", args.steps, args.warmup)
         elif args.only == "decode_sre_4096x128":
             r = bench_decode(torch, K, S, args.decode_steps, max(1, args.steps // 10))
+        elif args.only == "decode_sre_4096x128_deferred":
+            r = bench_decode(torch, K, S, args.decode_steps, max(1, args.steps // 10), deferred=True)
         elif args.only == "hybrid_decode_4096":
             r = bench_hybrid_decode(torch, K, S, args.decode_steps)
         else:
@@ -698,6 +735,13 @@ def main():
             log("[bench] cpu baseline (oracle): decode_sre_4096x128")
             r["cpu_baseline"] = cpu_baseline_decode(S, args.cpu_seconds * 0.5)
         secondary.append(r)
+        torch.cuda.empty_cache()
+        log("[bench] secondary: decode_sre_4096x128 with deferred folds")
+        r2 = bench_decode(torch, K, S, args.decode_steps, 2, deferred=True)
+        if cpu_on:
+            # the same outputs as the line above: the same oracle chain
+            r2["cpu_baseline"] = r.get("cpu_baseline")
+        secondary.append(r2)
         torch.cuda.empty_cache()
         log("[bench] secondary: hybrid_2x16x16384")
         r = bench_hybrid(torch, K, S, 3, 1)

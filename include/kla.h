@@ -294,6 +294,48 @@ KLA_API kla_status_t kla_decode_step(int N, int d_qk, int d_v, float eps, float*
                              void* o, kla_dtype_t out_dtype, const kla_sre_args_t* sre, void* ws,
                              size_t ws_bytes, kla_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * kla_decode_step_deferred - kla_decode_step with deferred folds (the same
+ * passages; KATA §2.2 for the closed form below).
+ *
+ * A head-state is (H, s) plus the pairs waiting in its pending slots:
+ *   H' = H + sum_{j < n_pend} phi(pend_k_j) pend_v_j^T,
+ *   s' = s + sum_{j < n_pend} phi(pend_k_j).
+ * The lift gives phi(x) . phi(y) = (x . y)^2, so a readout or a score over
+ * H' is the one over H plus sum_j (x . pend_k_j)^2 [pend_v_j | 1]: H and s
+ * need not be written at every token. The call stores the token's (k, v)
+ * in slot n_pend, reads H and s (writing neither), and reads out and scores
+ * against H' with the token added. The caller then holds n_pend + 1 pending
+ * pairs, except when that fills the slots (n_pend = KLA_DECODE_PENDING - 1):
+ * the call then adds all KLA_DECODE_PENDING of them to H and s in a second
+ * pass over the state, and the caller holds 0. H is read once per token and
+ * read and written once more per KLA_DECODE_PENDING tokens. o, the scores and
+ * the selection are those of kla_decode_step on the same sequence of tokens
+ * (the same values up to float32 rounding order).
+ *
+ *   H, s   : [N, D, d_v], [N, D] float32.
+ *   pend_k, pend_v : [N, KLA_DECODE_PENDING, d_qk] / [.., d_v] float32;
+ *            slots n_pend and above are ignored and may hold anything.
+ *   n_pend : 0 .. KLA_DECODE_PENDING - 1, the same for every head-state.
+ *   q, k, v, o, sre : as kla_decode_step; sre may be NULL.
+ * Errors: n_pend out of range, overlapping pend_k / pend_v / H / s, or a
+ * pointer not 16-byte aligned is KLA_ERR_INVALID_ARGUMENT.
+ * Supported: d_qk = d_v = 64; sre NULL or n_cand <= 64. No workspace.
+ *
+ * kla_decode_flush adds the first n_pend slots to H and s (n_pend = 0 does
+ * nothing; 0 <= n_pend < KLA_DECODE_PENDING); afterwards the caller holds 0
+ * pending pairs. kla_decode_pending_period returns KLA_DECODE_PENDING.
+ * ------------------------------------------------------------------------ */
+#define KLA_DECODE_PENDING 8
+KLA_API int kla_decode_pending_period(void);
+KLA_API kla_status_t kla_decode_step_deferred(int N, int d_qk, int d_v, float eps, float* H, float* s,
+                                              float* pend_k, float* pend_v, int n_pend, const void* q,
+                                              const void* k, const void* v, kla_dtype_t in_dtype, void* o,
+                                              kla_dtype_t out_dtype, const kla_sre_args_t* sre,
+                                              kla_stream_t stream);
+KLA_API kla_status_t kla_decode_flush(int N, int d_qk, int d_v, float* H, float* s, const float* pend_k,
+                                      const float* pend_v, int n_pend, kla_stream_t stream);
+
 /* kla_sre_select - scoring and selection only; H and s are read, not written. */
 KLA_API kla_status_t kla_sre_workspace_size(int N, int d_qk, int d_v, const kla_sre_args_t* sre,
                                     size_t* bytes);

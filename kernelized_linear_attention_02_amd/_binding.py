@@ -24,6 +24,7 @@ EXPORTS = (
     "kla_prefill_matrix_path", "kla_prefill_workspace_size", "kla_prefill", "kla_prefill_quadratic",
     "kla_prefill_quadratic_factors", "kla_prefill_factors", "kla_prefill_factors_workspace_size", "kla_prefill_quadratic_backward_workspace_size", "kla_prefill_quadratic_backward",
     "kla_decode_workspace_size", "kla_decode_step",
+    "kla_decode_pending_period", "kla_decode_step_deferred", "kla_decode_flush",
     "kla_sre_workspace_size", "kla_sre_select",
     "kla_hybrid_workspace_size", "kla_hybrid_prefill", "kla_hybrid_prefill_streams",
     "kla_hybrid_decode_workspace_size", "kla_hybrid_decode_step", "kla_hybrid_decode_flush",
@@ -100,6 +101,9 @@ def load_library(path: str = LIB_PATH):
         "kla_prefill_quadratic_backward": (i, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kla_decode_workspace_size": (i, [i, i, i, srp, szp]),
         "kla_decode_step": (i, [i, i, i, f, vp, vp, vp, vp, vp, i, vp, i, srp, vp, sz, vp]),
+        "kla_decode_pending_period": (i, []),
+        "kla_decode_step_deferred": (i, [i, i, i, f, vp, vp, vp, vp, i, vp, vp, vp, i, vp, i, srp, vp]),
+        "kla_decode_flush": (i, [i, i, i, vp, vp, vp, vp, i, vp]),
         "kla_sre_workspace_size": (i, [i, i, i, srp, szp]),
         "kla_sre_select": (i, [i, i, i, f, vp, vp, srp, vp, sz, vp]),
         "kla_hybrid_workspace_size": (i, [shp, hcp, szp]),
@@ -393,6 +397,65 @@ def decode_step(H, s, q, k, v, eps: float = 0.0, out_dtype=None, cand_k=None, ca
     check(lib.kla_decode_step(N, dqk, dv, float(eps), _ptr(H), _ptr(s), _ptr(q), _ptr(k), _ptr(v),
                               code, _ptr(o), ocode, sre_p, _ptr(ws), nbytes.value, _stream(dev)))
     return o if res is None else (o, res)
+
+
+def decode_pending_period() -> int:
+    """Tokens per pass that writes the state in decode_step_deferred (P)."""
+    return int(load_library().kla_decode_pending_period())
+
+
+def decode_pending_slots(N: int, d_qk: int = 64, d_v: int = 64, device="cuda"):
+    """Zeroed pending slots (pend_k [N, P, d_qk], pend_v [N, P, d_v]) for
+    decode_step_deferred."""
+    torch = _torch()
+    P = decode_pending_period()
+    return (torch.zeros((N, P, d_qk), dtype=torch.float32, device=device),
+            torch.zeros((N, P, d_v), dtype=torch.float32, device=device))
+
+
+def decode_step_deferred(H, s, pend_k, pend_v, n_pend: int, q, k, v, eps: float = 0.0, out_dtype=None,
+                         cand_k=None, cand_v=None, top_k: int = 0, scores: bool = True, gather: bool = False,
+                         out=None):
+    """decode_step with deferred folds: the token joins pending slot n_pend
+    (H and s only read) until the slots fill, when the call folds all of them
+    into H and s. Returns what decode_step returns; the caller's next n_pend
+    is (n_pend + 1) % decode_pending_period()."""
+    torch = _torch()
+    lib = load_library()
+    _need_device(H, s, pend_k, pend_v, q, k, v)
+    for t in (H, s, pend_k, pend_v):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError("H, s, pend_k and pend_v must be contiguous float32 (updated in place)")
+    q, k, v = _dense(q), _dense(k), _dense(v)
+    N, dqk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    ocode = code if out_dtype is None else _dtype_code(torch.empty(0, dtype=out_dtype))
+    dev = q.device
+    o = out["o"] if out is not None else torch.empty((N, dv), dtype=_torch_dtype(ocode), device=dev)
+    sre_p = None
+    res = None
+    if cand_k is not None:
+        cand_k, cand_v = _dense(cand_k), _dense(cand_v)
+        sc, sel, sk, sv = _sre_outputs(N, cand_k.shape[1], top_k, dqk, dv, dev, scores, gather, out)
+        stride = int(out["sel_stride"]) if (sk is not None and out is not None and "sel_stride" in out) else 0
+        sre = _sre_struct(cand_k, cand_v, top_k, sc, sel, sk, sv, stride)
+        sre_p = ctypes.byref(sre)
+        res = dict(scores=sc, sel=sel, sel_k=sk, sel_v=sv)
+    check(lib.kla_decode_step_deferred(N, dqk, dv, float(eps), _ptr(H), _ptr(s), _ptr(pend_k), _ptr(pend_v),
+                                       int(n_pend), _ptr(q), _ptr(k), _ptr(v), code, _ptr(o), ocode, sre_p,
+                                       _stream(dev)))
+    return o if res is None else (o, res)
+
+
+def decode_flush(H, s, pend_k, pend_v, n_pend: int):
+    """Fold the first n_pend pending slots into H and s."""
+    lib = load_library()
+    _need_device(H, s, pend_k, pend_v)
+    N, D, dv = H.shape
+    dqk = pend_k.shape[-1]
+    check(lib.kla_decode_flush(N, dqk, dv, _ptr(H), _ptr(s), _ptr(pend_k), _ptr(pend_v), int(n_pend),
+                               _stream(H.device)))
 
 
 def sre_select(H, s, cand_k, cand_v, top_k: int, eps: float = 0.0, scores: bool = True,

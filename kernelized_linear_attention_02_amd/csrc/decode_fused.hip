@@ -26,6 +26,14 @@
 // stored float32 value exactly. Denominators stay in float32 on the vector
 // units. The state is read once and written once; the
 // candidate keys sit in LDS.
+//
+// Deferred folds (the same step with a list of pending pairs): the lift
+// gives phi(x) . phi(y) = (x . y)^2 (KATA page §2.2), so the state plus
+// pairs that are not yet folded in reads out as
+//   phi(x)^T H + sum_j (x . k_j)^2 v_j,   phi(x)^T s + sum_j (x . k_j)^2,
+// for the query and for every candidate key alike. A deferred step reads H
+// and s, writes neither, and appends its pair to the list; when the list is
+// full a second pass adds all of it (rank kPend) to H and s.
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
 #include "mfma_bf16.hpp"
@@ -40,6 +48,7 @@ constexpr int kTiles = kD / kFT;           // 65
 constexpr int kWaves = 4;
 constexpr int kThreadsF = 64 * kWaves;
 constexpr int kMaxCand = 64;
+constexpr int kPend = 8;  // pending slots per head-state, folded together
 static_assert(kD % kFT == 0, "tiles must cover the features exactly");
 
 __constant__ PairTable64 kPairTable = PairTable64();
@@ -57,7 +66,27 @@ struct FusedLds {
   float onum[kWaves][kDim];
   float oden[kWaves];
   uint64_t keys[kMaxCand];
+  // pair list of the deferred modes: keys transposed (feature -> kPend
+  // pairs), values by pair, and the squared dot products of the query and of
+  // every candidate key with each listed key; the state's s (read-only modes
+  // take it from here rather than holding it in registers)
+  alignas(16) float sS[kD];
+  float rnum[kWaves][kDim];  // per-wave readout sums of the read-only mode
+  float rden[kWaves];
+  alignas(16) float pkT[kDim][kPend];
+  alignas(16) float pv[kPend][kDim];
+  float wq[kPend];
+  float wc[kMaxCand][kPend];
 };
+
+// Kernel modes.
+//   kStep : update with the step's token, write H and s back, read out, score.
+//   kScore: read H and s, score only.
+//   kRead : read H and s; read out and score against them plus the list
+//           (pending slots, then the token) in closed form; store the token
+//           in its pending slot.
+//   kFlush: add the pending slots to H and s, write back.
+enum : int { kStep = 0, kScore = 1, kRead = 3, kFlush = 4 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return mfma16x16x32(a, b, c);
@@ -95,16 +124,24 @@ struct CandRows {
   }
 };
 
-// Work-group (n, g) scores candidates 64 g .. 64 g + 16 MT - 1 of head-state n.
-// MT: 16-candidate blocks. UPDATE: decode step first (H and s written back,
-// o produced); otherwise the state is only read. SELECT: top_k selection and
-// gather in the same kernel (requires n_cand <= 16 * MT, one group).
-template <int MT, bool UPDATE, bool SELECT, typename Tin, typename Tout, typename Cand>
+// Work-group (n, g) scores candidates 64 g .. 64 g + 16 MT - 1 of head-state n
+// (MT: 16-candidate blocks, 0 for none). SELECT: top_k selection and gather
+// in the same kernel (requires n_cand <= 16 * MT, one group). The deferred
+// modes take the pending slots of head-state n from pend_k / pend_v
+// ([N, kPend, 64] float32), n_pend of them in use (kRead: n_pend < kPend).
+template <int MT, int MODE, bool SELECT, typename Tin, typename Tout, typename Cand>
 __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     float* __restrict__ H, float* __restrict__ s, const Tin* __restrict__ q,
     const Tin* __restrict__ k, const Tin* __restrict__ v, Tout* __restrict__ o, float eps,
     Cand cand, int n_cand, int top_k, float* __restrict__ scores, int sstride,
-    int32_t* __restrict__ sel, float* __restrict__ sel_k, float* __restrict__ sel_v, int sel_stride) {
+    int32_t* __restrict__ sel, float* __restrict__ sel_k, float* __restrict__ sel_v, int sel_stride,
+    float* __restrict__ pend_k, float* __restrict__ pend_v, int n_pend) {
+  constexpr bool kWrites = MODE == kStep || MODE == kFlush;
+  constexpr bool kReadout = MODE == kStep || MODE == kRead;
+  constexpr bool kToken = kReadout;
+  constexpr bool kList = MODE == kRead || MODE == kFlush;
+  constexpr bool kSLds = MODE == kRead;  // s from LDS
+  constexpr int MTA = MT > 0 ? MT : 1;
   __shared__ __align__(16) FusedLds sh;
   const int n = blockIdx.x;
   const int cbase = 64 * blockIdx.y;
@@ -121,19 +158,50 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     const int fr = kFT * ks + 8 * q4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) h[j] = ld_state(Hn + (size_t)(fr + j) * kDim + 4 * l16);
-    sv[0] = ld_state(sn + fr);
-    sv[1] = ld_state(sn + fr + 4);
+    if (!kSLds) {
+      sv[0] = ld_state(sn + fr);
+      sv[1] = ld_state(sn + fr + 4);
+    }
   };
   // the first tile is in flight while the block stages its inputs
   float4 h[8], sv[2];
   load_tile(w, h, sv);
 
-  if (UPDATE && tid < kDim) {
+  if (kToken && tid < kDim) {
     sh.qs[tid] = Elem<Tin>::load(q, (size_t)n * kDim + tid);
     sh.ks[tid] = Elem<Tin>::load(k, (size_t)n * kDim + tid);
     sh.vs[tid] = Elem<Tin>::load(v, (size_t)n * kDim + tid);
   }
+  if (kList) {
+    // list entry p: pending slot p (p < n_pend), the step's token (p =
+    // n_pend), zero after (a zero key adds nothing)
+    const size_t slot0 = (size_t)n * kPend;
+    for (int i = tid; i < kPend * kDim; i += kThreadsF) {
+      const int p = i / kDim, d = i % kDim;
+      float kk = 0.0f, vv = 0.0f;
+      if (p < n_pend) {
+        kk = pend_k[(slot0 + p) * kDim + d];
+        vv = pend_v[(slot0 + p) * kDim + d];
+      } else if (kToken && p == n_pend) {
+        kk = Elem<Tin>::load(k, (size_t)n * kDim + d);
+        vv = Elem<Tin>::load(v, (size_t)n * kDim + d);
+        if (MODE == kRead) {
+          pend_k[(slot0 + p) * kDim + d] = kk;
+          pend_v[(slot0 + p) * kDim + d] = vv;
+        }
+      }
+      sh.pkT[d][p] = kk;
+      sh.pv[p][d] = vv;
+    }
+  }
   for (int i = tid; i < kD; i += kThreadsF) sh.tab[i] = kPairTable.ab[i];
+  if (MODE == kRead) {
+    sh.rnum[w][lane] = 0.0f;
+    if (lane == 0) sh.rden[w] = 0.0f;
+  }
+  if (kSLds)
+    for (int i = tid; i < kD / 4; i += kThreadsF)
+      *reinterpret_cast<float4*>(&sh.sS[4 * i]) = ld_state(sn + 4 * i);
   for (int i = tid; i < 16 * MT * (kDim / 4); i += kThreadsF) {
     const int c = i / (kDim / 4);
     const int d4 = i % (kDim / 4);
@@ -145,26 +213,45 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     sh.ck[c][4 * d4 + 3] = x.w;
   }
   __syncthreads();
-
+  if (MODE == kRead) {
+    // (x . k_p)^2 for the query (entries 0 .. kPend - 1) and every candidate;
+    // read after the numerator reduction's first barrier
+    for (int i = tid; i < kPend * (1 + 16 * MT); i += kThreadsF) {
+      const int p = i % kPend, c = i / kPend - 1;
+      const float* x = c < 0 ? sh.qs : sh.ck[c];
+      float dot = 0.0f;
+#pragma unroll 8
+      for (int d = 0; d < kDim; ++d) dot += x[d] * sh.pkT[d][p];
+      if (c < 0) sh.wq[p] = dot * dot;
+      else sh.wc[c][p] = dot * dot;
+    }
+  }
 
   float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (UPDATE) v4 = *reinterpret_cast<const float4*>(&sh.vs[4 * l16]);
-
-  f32x4 acc[MT][4];
+  if (MODE == kStep) v4 = *reinterpret_cast<const float4*>(&sh.vs[4 * l16]);
+  // the list's values at this lane's four state columns
+  float4 vl[kPend];
+  if (kList && kWrites) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int p = 0; p < kPend; ++p) vl[p] = *reinterpret_cast<const float4*>(&sh.pv[p][4 * l16]);
+  }
+
+  f32x4 acc[MTA][4];
+#pragma unroll
+  for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dacc[MT];
+  float dacc[MTA];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) dacc[mt] = 0.0f;
+  for (int mt = 0; mt < MTA; ++mt) dacc[mt] = 0.0f;
   float4 oacc = make_float4(0.f, 0.f, 0.f, 0.f);
   float oden = 0.0f;
 
 
-#pragma unroll 1
-  for (int ks = w; ks < kTiles; ks += kWaves) {
-    float4 hn[8], svn[2];
+  // One tile: the state rows in h (s in sv), the next tile's loads issued
+  // into hn / svn first. The loop below alternates the two buffers, so no
+  // registers are copied between tiles.
+  auto tile = [&](int ks, float4 (&h)[8], float4 (&sv)[2], float4 (&hn)[8], float4 (&svn)[2]) {
     const bool more = ks + kWaves < kTiles;
     if (more) load_tile(ks + kWaves, hn, svn);
 
@@ -180,8 +267,12 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
       pb[j] = u >> 8;
       wt[j] = pa[j] == pb[j] ? 1.0f : kSqrt2;
     }
+    if (kSLds) {
+      sv[0] = *reinterpret_cast<const float4*>(&sh.sS[fr]);
+      sv[1] = *reinterpret_cast<const float4*>(&sh.sS[fr + 4]);
+    }
     float sj[8] = {sv[0].x, sv[0].y, sv[0].z, sv[0].w, sv[1].x, sv[1].y, sv[1].z, sv[1].w};
-    if (UPDATE) {
+    if (MODE == kStep) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float pk = sh.ks[pa[j]] * sh.ks[pb[j]] * wt[j];
@@ -198,55 +289,120 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
         oacc.w += pq * h[j].w;
         oden += pq * sj[j];
       }
+    } else if (kList && kWrites) {
+      // rank-kPend update: phi_f(k_p) = k_p[a] k_p[b] wt over the listed pairs
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&sh.pkT[pa[j]][0]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&sh.pkT[pa[j]][4]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&sh.pkT[pb[j]][0]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&sh.pkT[pb[j]][4]);
+        const float pk[kPend] = {a0.x * b0.x * wt[j], a0.y * b0.y * wt[j], a0.z * b0.z * wt[j],
+                                 a0.w * b0.w * wt[j], a1.x * b1.x * wt[j], a1.y * b1.y * wt[j],
+                                 a1.z * b1.z * wt[j], a1.w * b1.w * wt[j]};
+#pragma unroll
+        for (int p = 0; p < kPend; ++p) {
+          h[j].x += pk[p] * vl[p].x;
+          h[j].y += pk[p] * vl[p].y;
+          h[j].z += pk[p] * vl[p].z;
+          h[j].w += pk[p] * vl[p].w;
+          sj[j] += pk[p];
+        }
+        st_state(Hn + (size_t)(fr + j) * kDim + 4 * l16, h[j]);
+      }
+    }
+    // kRead: the query's products. The readout's partial sums go to this
+    // wave's LDS slots per tile (after a sum over the lane quarters, which
+    // hold other rows of the same columns) rather than living in registers
+    // through the loop.
+    float pq[8];
+    if (MODE == kRead) {
+      float dq = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pq[j] = sh.qs[pa[j]] * sh.qs[pb[j]] * wt[j];
+        dq += pq[j] * sj[j];
+      }
+      dq += __shfl_xor(dq, 16, 64);
+      dq += __shfl_xor(dq, 32, 64);
+      if (lane == 0) sh.rden[w] += dq;
+    }
+    auto read_col = [&](int nt, const float (&x)[8]) {
+      float r = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r += pq[j] * x[j];
+      r += __shfl_xor(r, 16, 64);
+      r += __shfl_xor(r, 32, 64);
+      if (q4 == 0) sh.rnum[w][4 * l16 + nt] += r;
+    };
+    if (kWrites) {
       // two lanes per quarter write its 8 values: one contiguous 128-byte run
       if (l16 < 2)
         st_state(sn + fr + 4 * l16, l16 ? make_float4(sj[4], sj[5], sj[6], sj[7])
                                         : make_float4(sj[0], sj[1], sj[2], sj[3]));
     }
 
-    // A operands (two pieces) for every candidate block, and the float32
-    // denominators
-    bf16x8 ahi[MT], alo[MT];
+    if (MT > 0) {
+      // candidate blocks in groups of MH (the deferred read splits four
+      // blocks in two groups so its readout fits in registers): A operands
+      // (two pieces) and the float32 denominators, then per column block the
+      // B operands (three pieces, exact: state column 4*l16 + nt over this
+      // lane's 8 rows) and the products
+      constexpr int MH = MTA;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const float* kc = sh.ck[16 * mt + l16];
-      float p[8];
-      float dd = 0.0f;
+      for (int m0 = 0; m0 < MT; m0 += MH) {
+        bf16x8 ahi[MH], alo[MH];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = kc[pa[j]] * kc[pb[j]] * wt[j];
-        dd += p[j] * sj[j];
+        for (int mm = 0; mm < MH; ++mm) {
+          const float* kc = sh.ck[16 * (m0 + mm) + l16];
+          float p[8];
+          float dd = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            p[j] = kc[pa[j]] * kc[pb[j]] * wt[j];
+            dd += p[j] * sj[j];
+          }
+          dacc[m0 + mm] += dd;
+          split2_pk(p, ahi[mm], alo[mm]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
+          if (MODE == kRead && m0 == 0) read_col(nt, x);
+          bf16x8 b0, b1, b2;
+          split3_pk(x, b0, b1, b2);
+#pragma unroll
+          for (int mm = 0; mm < MH; ++mm) {
+            const int mt = m0 + mm;
+            acc[mt][nt] = mfma(ahi[mm], b0, acc[mt][nt]);
+            acc[mt][nt] = mfma(ahi[mm], b1, acc[mt][nt]);
+            acc[mt][nt] = mfma(ahi[mm], b2, acc[mt][nt]);
+            acc[mt][nt] = mfma(alo[mm], b0, acc[mt][nt]);
+          }
+        }
       }
-      dacc[mt] += dd;
-      split2(p, ahi[mt], alo[mt]);
-    }
-    // B operands (three pieces, exact): state column 4*l16 + nt over this
-    // lane's 8 rows
+    } else if (MODE == kRead) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float x[8];
+      for (int nt = 0; nt < 4; ++nt) {
+        float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
-      bf16x8 b0, b1, b2;
-      split3(x, b0, b1, b2);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][nt] = mfma(ahi[mt], b0, acc[mt][nt]);
-        acc[mt][nt] = mfma(ahi[mt], b1, acc[mt][nt]);
-        acc[mt][nt] = mfma(ahi[mt], b2, acc[mt][nt]);
-        acc[mt][nt] = mfma(alo[mt], b0, acc[mt][nt]);
+        for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
+        read_col(nt, x);
       }
     }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = hn[j];
-      sv[0] = svn[0];
-      sv[1] = svn[1];
-    }
+  };
+  float4 h2[8], sv2[2];
+#pragma unroll 1
+  for (int ks = w; ks < kTiles; ks += 2 * kWaves) {
+    tile(ks, h, sv, h2, sv2);
+    if (ks + kWaves < kTiles) tile(ks + kWaves, h2, sv2, h, sv);
   }
+  if (MODE == kFlush) return;
 
   // ---- readout partials: sum over the lane quarters, then over waves
-  if (UPDATE) {
+  if (kReadout && MODE != kRead) {
     float ox[4] = {oacc.x, oacc.y, oacc.z, oacc.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -292,17 +448,24 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
         }
     }
   }
-  // (the loop's last barrier has made onum, oden and den visible)
-  if (UPDATE && tid < kDim) {
+  // (the loop's last barrier has made onum, oden, den, wq and wc visible)
+  if (kReadout && tid < kDim) {
     float num = 0.0f, den = eps;
 #pragma unroll
     for (int r = 0; r < kWaves; ++r) {
-      num += sh.onum[r][tid];
-      den += sh.oden[r];
+      num += MODE == kRead ? sh.rnum[r][tid] : sh.onum[r][tid];
+      den += MODE == kRead ? sh.rden[r] : sh.oden[r];
+    }
+    if (MODE == kRead) {
+#pragma unroll
+      for (int p = 0; p < kPend; ++p) {
+        num += sh.wq[p] * sh.pv[p][tid];
+        den += sh.wq[p];
+      }
     }
     Elem<Tout>::store(o, (size_t)n * kDim + tid, den != 0.0f ? num / den : 0.0f);
   }
-  if (w == kWaves - 1) {
+  if (MT > 0 && w == kWaves - 1) {
     // lane (l16, q4) holds candidates 16*mt + 4*q4 + i at state columns 4*l16 + nt
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -313,12 +476,23 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
         float den = eps;
 #pragma unroll
         for (int r = 0; r < kWaves; ++r) den += sh.den[r][c];
+        float num[4] = {acc[mt][0][i], acc[mt][1][i], acc[mt][2][i], acc[mt][3][i]};
+        if (MODE == kRead) {
+#pragma unroll
+          for (int p = 0; p < kPend; ++p) {
+            const float wgt = sh.wc[c][p];
+            const float4 vp = *reinterpret_cast<const float4*>(&sh.pv[p][4 * l16]);
+            den += wgt;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) num[nt] += wgt * comp(vp, nt);
+          }
+        }
         float4 vc = make_float4(0.f, 0.f, 0.f, 0.f);
         if (live) vc = cand.v4(n, cbase + c, l16);
         float err = 0.0f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const float pred = den != 0.0f ? acc[mt][nt][i] / den : 0.0f;
+          const float pred = den != 0.0f ? num[nt] / den : 0.0f;
           const float diff = pred - comp(vc, nt);
           err += diff * diff;
         }
@@ -350,24 +524,43 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   }
 }
 
-template <int MT, bool UPDATE, typename Tin, typename Tout>
+template <int MT, int MODE, bool SELECT, typename Tin, typename Tout>
 void launch_fused(int N, float* H, float* s, const void* q, const void* k, const void* v, void* o,
-                  float eps, const SreArgs& sre, hipStream_t st) {
+                  float eps, const SreArgs& sre, float* pend_k, float* pend_v, int n_pend, hipStream_t st) {
   const CandRows cand{sre.cand_k, sre.cand_v, sre.n_cand};
-  hipLaunchKernelGGL((decode_sre_kernel<MT, UPDATE, true, Tin, Tout, CandRows>), dim3(N, 1), dim3(kThreadsF), 0, st,
-                     H, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), static_cast<const Tin*>(v),
+  hipLaunchKernelGGL((decode_sre_kernel<MT, MODE, SELECT, Tin, Tout, CandRows>), dim3(N, 1), dim3(kThreadsF), 0,
+                     st, H, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), static_cast<const Tin*>(v),
                      static_cast<Tout*>(o), eps, cand, sre.n_cand, sre.top_k, sre.scores, sre.n_cand, sre.sel,
-                     sre.sel_k, sre.sel_v, sre.sel_stride ? sre.sel_stride : sre.top_k);
+                     sre.sel_k, sre.sel_v, sre.sel_stride ? sre.sel_stride : sre.top_k, pend_k, pend_v, n_pend);
 }
 
-template <bool UPDATE, typename Tin, typename Tout>
+template <int MODE, typename Tin, typename Tout>
 void launch_mt(int N, float* H, float* s, const void* q, const void* k, const void* v, void* o, float eps,
-               const SreArgs& sre, hipStream_t st) {
+               const SreArgs* sre, float* pend_k, float* pend_v, int n_pend, hipStream_t st) {
+  if (!sre) {
+    launch_fused<0, MODE, false, Tin, Tout>(N, H, s, q, k, v, o, eps, SreArgs{}, pend_k, pend_v, n_pend, st);
+    return;
+  }
   // 16, 32 or 64 candidate rows (rows past n_cand are zero keys, not scored)
-  const int mt = (sre.n_cand + 15) / 16;
-  if (mt == 1) launch_fused<1, UPDATE, Tin, Tout>(N, H, s, q, k, v, o, eps, sre, st);
-  else if (mt == 2) launch_fused<2, UPDATE, Tin, Tout>(N, H, s, q, k, v, o, eps, sre, st);
-  else launch_fused<4, UPDATE, Tin, Tout>(N, H, s, q, k, v, o, eps, sre, st);
+  const int mt = (sre->n_cand + 15) / 16;
+  if (mt == 1) launch_fused<1, MODE, true, Tin, Tout>(N, H, s, q, k, v, o, eps, *sre, pend_k, pend_v, n_pend, st);
+  else if (mt == 2)
+    launch_fused<2, MODE, true, Tin, Tout>(N, H, s, q, k, v, o, eps, *sre, pend_k, pend_v, n_pend, st);
+  else launch_fused<4, MODE, true, Tin, Tout>(N, H, s, q, k, v, o, eps, *sre, pend_k, pend_v, n_pend, st);
+}
+
+template <int MODE>
+void launch_dtypes(const DecodeArgs& a, const SreArgs* sre, float* pend_k, float* pend_v, int n_pend,
+                   hipStream_t st) {
+  if (a.in_bf16) {
+    if (a.out_bf16)
+      launch_mt<MODE, uint16_t, uint16_t>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, pend_k, pend_v, n_pend, st);
+    else launch_mt<MODE, uint16_t, float>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, pend_k, pend_v, n_pend, st);
+  } else {
+    if (a.out_bf16)
+      launch_mt<MODE, float, uint16_t>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, pend_k, pend_v, n_pend, st);
+    else launch_mt<MODE, float, float>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, pend_k, pend_v, n_pend, st);
+  }
 }
 
 }  // namespace
@@ -378,13 +571,7 @@ bool decode_fused_supported(int dqk, int dv, const SreArgs& sre) {
 
 hipError_t decode_fused_launch(const DecodeArgs& a, const SreArgs& sre, hipStream_t st) {
   prof_begin(st);
-  if (a.in_bf16) {
-    if (a.out_bf16) launch_mt<true, uint16_t, uint16_t>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, st);
-    else launch_mt<true, uint16_t, float>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, st);
-  } else {
-    if (a.out_bf16) launch_mt<true, float, uint16_t>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, st);
-    else launch_mt<true, float, float>(a.N, a.H, a.s, a.q, a.k, a.v, a.o, a.eps, sre, st);
-  }
+  launch_dtypes<kStep>(a, &sre, nullptr, nullptr, 0, st);
   prof_end(st);
   return hipGetLastError();
 }
@@ -393,9 +580,30 @@ hipError_t sre_fused_launch(int N, float eps, const float* H, const float* s, co
                             hipStream_t st) {
   prof_begin(st);
   // read-only: the kernel neither loads q, k, v nor writes H, s or o
-  launch_mt<false, float, float>(N, const_cast<float*>(H), const_cast<float*>(s), nullptr, nullptr, nullptr,
-                                 nullptr, eps, sre, st);
+  launch_mt<kScore, float, float>(N, const_cast<float*>(H), const_cast<float*>(s), nullptr, nullptr, nullptr,
+                                  nullptr, eps, &sre, nullptr, nullptr, 0, st);
   prof_end(st);
+  return hipGetLastError();
+}
+
+int decode_pending_slots() { return kPend; }
+
+hipError_t decode_deferred_launch(const DecodeArgs& a, const SreArgs* sre, float* pend_k, float* pend_v,
+                                  int n_pend, hipStream_t st) {
+  prof_begin(st);
+  launch_dtypes<kRead>(a, sre, pend_k, pend_v, n_pend, st);
+  prof_end(st);
+  hipError_t e = hipGetLastError();
+  // the last slot is now taken: the list goes into H and s
+  if (e == hipSuccess && n_pend == kPend - 1) e = decode_flush_launch(a.N, a.H, a.s, pend_k, pend_v, kPend, st);
+  return e;
+}
+
+hipError_t decode_flush_launch(int N, float* H, float* s, const float* pend_k, const float* pend_v, int n_pend,
+                               hipStream_t st) {
+  if (n_pend == 0) return hipSuccess;
+  launch_fused<0, kFlush, false, float, float>(N, H, s, nullptr, nullptr, nullptr, nullptr, 0.0f, SreArgs{},
+                                               const_cast<float*>(pend_k), const_cast<float*>(pend_v), n_pend, st);
   return hipGetLastError();
 }
 

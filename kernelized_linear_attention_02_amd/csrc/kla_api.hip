@@ -535,6 +535,88 @@ kla_status_t kla_decode_step(int N, int d_qk, int d_v, float eps, float* H, floa
                     fn);
 }
 
+int kla_decode_pending_period(void) { return KLA_DECODE_PENDING; }
+
+namespace {
+
+kla_status_t check_pending(const char* fn, int N, const float* H, const float* s, const float* pend_k,
+                           const float* pend_v, int n_pend) {
+  if (n_pend < 0 || n_pend > KLA_DECODE_PENDING - 1)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: n_pend must be in [0, %d] (got %d)", fn, KLA_DECODE_PENDING - 1,
+                n_pend);
+  if (!pend_k || !pend_v) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: pend_k and pend_v are required", fn);
+  const size_t np = (size_t)N * KLA_DECODE_PENDING * 64 * sizeof(float);
+  const size_t nH = (size_t)N * kla_phi_dim(64) * 64 * sizeof(float);
+  const size_t ns = (size_t)N * kla_phi_dim(64) * sizeof(float);
+  if (overlaps(pend_k, np, pend_v, np) || overlaps(pend_k, np, H, nH) || overlaps(pend_k, np, s, ns) ||
+      overlaps(pend_v, np, H, nH) || overlaps(pend_v, np, s, ns))
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: pend_k, pend_v, H and s must not overlap", fn);
+  return KLA_OK;
+}
+
+}  // namespace
+
+kla_status_t kla_decode_step_deferred(int N, int d_qk, int d_v, float eps, float* H, float* s, float* pend_k,
+                                      float* pend_v, int n_pend, const void* q, const void* k, const void* v,
+                                      kla_dtype_t in_dtype, void* o, kla_dtype_t out_dtype,
+                                      const kla_sre_args_t* sre, kla_stream_t stream) {
+  const char* fn = "kla_decode_step_deferred";
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (d_qk != 64 || d_v != 64)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: needs d_qk = d_v = 64 (got %d, %d)", fn, d_qk, d_v);
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return fail(KLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (!std::isfinite(eps) || eps < 0.0f)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+  if (!H || !s || !q || !k || !v || !o)
+    return fail(KLA_ERR_INVALID_ARGUMENT, "%s: H, s, q, k, v, o are required", fn);
+  if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
+  kla_status_t st = check_pending(fn, N, H, s, pend_k, pend_v, n_pend);
+  if (st != KLA_OK) return st;
+  st = check_align(fn, {{"H", H}, {"s", s}, {"pend_k", pend_k}, {"pend_v", pend_v}, {"q", q}, {"k", k},
+                        {"v", v}, {"o", o}});
+  if (st != KLA_OK) return st;
+  kla::SreArgs sa{};
+  if (sre) {
+    st = check_sre(N, d_qk, d_v, sre, fn);
+    if (st != KLA_OK) return st;
+    sa = make_sre(sre);
+    if (!kla::decode_fused_supported(d_qk, d_v, sa))
+      return fail(KLA_ERR_UNSUPPORTED, "%s: n_cand = %d exceeds 64", fn, sre->n_cand);
+  }
+  kla::DecodeArgs a{};
+  a.N = N;
+  a.dqk = d_qk;
+  a.dv = d_v;
+  a.eps = eps;
+  a.H = H;
+  a.s = s;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.in_bf16 = in_dtype == KLA_BF16;
+  a.o = o;
+  a.out_bf16 = out_dtype == KLA_BF16;
+  return hip_status(kla::decode_deferred_launch(a, sre ? &sa : nullptr, pend_k, pend_v, n_pend,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+kla_status_t kla_decode_flush(int N, int d_qk, int d_v, float* H, float* s, const float* pend_k,
+                              const float* pend_v, int n_pend, kla_stream_t stream) {
+  const char* fn = "kla_decode_flush";
+  if (N < 1) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: N must be >= 1", fn);
+  if (d_qk != 64 || d_v != 64)
+    return fail(KLA_ERR_UNSUPPORTED, "%s: needs d_qk = d_v = 64 (got %d, %d)", fn, d_qk, d_v);
+  if (!H || !s) return fail(KLA_ERR_INVALID_ARGUMENT, "%s: H and s are required", fn);
+  if (N > kMaxHeads) return fail(KLA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, kMaxHeads);
+  kla_status_t st = check_pending(fn, N, H, s, pend_k, pend_v, n_pend);
+  if (st != KLA_OK) return st;
+  st = check_align(fn, {{"H", H}, {"s", s}, {"pend_k", pend_k}, {"pend_v", pend_v}});
+  if (st != KLA_OK) return st;
+  return hip_status(kla::decode_flush_launch(N, H, s, pend_k, pend_v, n_pend, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 kla_status_t kla_sre_workspace_size(int N, int d_qk, int d_v, const kla_sre_args_t* sre,
                                     size_t* bytes) {
   const char* fn = "kla_sre_workspace_size";

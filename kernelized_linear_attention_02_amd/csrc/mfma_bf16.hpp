@@ -43,6 +43,41 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p0, bf16x8& 
   }
 }
 
+// The same two splits converting pairs of values at a time (one packed
+// round-to-nearest-even conversion per pair, as the scalar forms round).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void split2_pk(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const f32x2_t v = {x[j], x[j + 1]};
+    const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    const bf16x2_t l = __builtin_convertvector(v - __builtin_convertvector(h, f32x2_t), bf16x2_t);
+    hi[j] = h[0];
+    hi[j + 1] = h[1];
+    lo[j] = l[0];
+    lo[j + 1] = l[1];
+  }
+}
+
+__device__ __forceinline__ void split3_pk(const float (&x)[8], bf16x8& p0, bf16x8& p1, bf16x8& p2) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const f32x2_t v = {x[j], x[j + 1]};
+    const bf16x2_t a = __builtin_convertvector(v, bf16x2_t);
+    const f32x2_t r = v - __builtin_convertvector(a, f32x2_t);
+    const bf16x2_t b = __builtin_convertvector(r, bf16x2_t);
+    const bf16x2_t c = __builtin_convertvector(r - __builtin_convertvector(b, f32x2_t), bf16x2_t);
+    p0[j] = a[0];
+    p0[j + 1] = a[1];
+    p1[j] = b[0];
+    p1[j + 1] = b[1];
+    p2[j] = c[0];
+    p2[j + 1] = c[1];
+  }
+}
+
 __device__ __forceinline__ float comp(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

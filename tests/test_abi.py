@@ -130,6 +130,31 @@ def test_decode_and_sre_validation(lib):
     assert lib.kla_sre_select(8, 64, 64, 0.0, P, P, None, P, 1 << 40, None) == B.KLA_ERR_INVALID_ARGUMENT
 
 
+def test_decode_deferred_validation(lib):
+    Hp, sp, pk, pv = (ctypes.c_void_p(x) for x in (0x10000000, 0x20000000, 0x30000000, 0x40000000))
+    Pn = lib.kla_decode_pending_period()
+    assert Pn == 8
+
+    def step(N=8, d=64, H=Hp, s=sp, k=pk, v=pv, n_pend=0, sre=None):
+        return lib.kla_decode_step_deferred(N, d, d, 0.0, H, s, k, v, n_pend, P, P, P, B.KLA_F32, P, B.KLA_F32,
+                                            ctypes.byref(sre) if sre is not None else None, None)
+    assert step(n_pend=-1) == B.KLA_ERR_INVALID_ARGUMENT
+    assert step(n_pend=Pn) == B.KLA_ERR_INVALID_ARGUMENT
+    assert step(k=None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert step(v=pk) == B.KLA_ERR_INVALID_ARGUMENT                   # pend_k and pend_v overlap
+    assert step(k=ctypes.c_void_p(0x10000000 + 4096)) == B.KLA_ERR_INVALID_ARGUMENT  # pend_k inside H
+    assert step(k=ctypes.c_void_p(0x30000004)) == B.KLA_ERR_INVALID_ARGUMENT         # misaligned
+    assert step(d=32) == B.KLA_ERR_UNSUPPORTED
+    assert step(sre=_sre(n_cand=65, top_k=16)) == B.KLA_ERR_UNSUPPORTED
+    assert step(sre=_sre(n_cand=16, top_k=17)) == B.KLA_ERR_INVALID_ARGUMENT
+    assert b"n_pend" in lib.kla_last_error() or True
+    fl = lib.kla_decode_flush
+    assert fl(8, 64, 64, Hp, sp, pk, pv, Pn, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert fl(8, 64, 64, Hp, sp, pk, pk, 1, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert fl(8, 64, 64, None, sp, pk, pv, 1, None) == B.KLA_ERR_INVALID_ARGUMENT
+    assert fl(8, 16, 16, Hp, sp, pk, pv, 1, None) == B.KLA_ERR_UNSUPPORTED
+
+
 def test_hybrid_validation(lib):
     shp = _shape(T=1000)
 

@@ -414,7 +414,32 @@ def _oracle_chain_check(gpu, H, s, H0s, s0s, inputs, cache0_k, cache0_v, top, ch
         assert_close(sh[n], ref["s"], RTOL_F32, f"s of head-state {n}")
 
 
-def _decode_chain(K, case, steps, check_ids):
+class _Stepper:
+    """decode_step, or decode_step_deferred with its pending slots (the
+    count advances by one per token and wraps when the call folds)."""
+
+    def __init__(self, K, N, deferred):
+        self.K, self.deferred, self.n_pend = K, deferred, 0
+        if deferred:
+            self.pk, self.pv = K.decode_pending_slots(N)
+            # slots above n_pend are ignored: fill them with values that would show
+            self.pk.fill_(7.0)
+            self.pv.fill_(-3.0)
+
+    def __call__(self, H, s, q, k, v, **kw):
+        if not self.deferred:
+            return self.K.decode_step(H, s, q, k, v, **kw)
+        r = self.K.decode_step_deferred(H, s, self.pk, self.pv, self.n_pend, q, k, v, **kw)
+        self.n_pend = (self.n_pend + 1) % self.K.decode_pending_period()
+        return r
+
+    def finish(self, H, s):
+        if self.deferred:
+            self.K.decode_flush(H, s, self.pk, self.pv, self.n_pend)
+            self.n_pend = 0
+
+
+def _decode_chain(K, case, steps, check_ids, deferred=False):
     """Run the decode + selection chain on the GPU for all head-states and
     compare the head-states ``check_ids`` with the oracle."""
     N, d, top = case.N, case.d, case.top_k
@@ -422,15 +447,17 @@ def _decode_chain(K, case, steps, check_ids):
     cache_k = dev(case.cache0_k)
     cache_v = dev(case.cache0_v)
     gpu = dict(o=[], scores=[], sel=[])
+    step = _Stepper(K, N, deferred)
     for t in range(steps):
         cand_k = torch.cat([cache_k, dev(case.fresh_k[t])], dim=1)
         cand_v = torch.cat([cache_v, dev(case.fresh_v[t])], dim=1)
-        o, r = K.decode_step(H, s, dev(case.q[t]), dev(case.k[t]), dev(case.v[t]), cand_k=cand_k,
-                             cand_v=cand_v, top_k=top, gather=True)
+        o, r = step(H, s, dev(case.q[t]), dev(case.k[t]), dev(case.v[t]), cand_k=cand_k,
+                    cand_v=cand_v, top_k=top, gather=True)
         cache_k, cache_v = r["sel_k"], r["sel_v"]
         gpu["o"].append(host(o)[check_ids])
         gpu["scores"].append(host(r["scores"])[check_ids])
         gpu["sel"].append(host(r["sel"]).astype(int)[check_ids])
+    step.finish(H, s)
     torch.cuda.synchronize()
     H0s, s0s = [], []
     for n in check_ids:
@@ -442,12 +469,37 @@ def _decode_chain(K, case, steps, check_ids):
                         check_ids)
 
 
-def test_decode_chain_small(K):
+@pytest.mark.parametrize("deferred", [False, True])
+def test_decode_chain_small(K, deferred):
     case = S.decode_case(8, d=64, T0=256, steps=12, seed=43)
-    _decode_chain(K, case, 12, list(range(8)))
+    _decode_chain(K, case, 12, list(range(8)), deferred)
 
 
-def test_decode_sre_4096x128_full_chain(K):
+@pytest.mark.parametrize("steps", [1, 7, 8, 9, 20])
+def test_decode_deferred_without_selection(K, steps):
+    """Deferred folds with no candidates: every token's o, and the state after
+    a flush at any point of the slot cycle, against the oracle's recurrence."""
+    N, d = 5, 64
+    case = S.decode_case(N, d=d, T0=64, steps=steps, seed=44)
+    H, s = _initial_state(K, case)
+    step = _Stepper(K, N, True)
+    outs = [host(step(H, s, dev(case.q[t]), dev(case.k[t]), dev(case.v[t]))) for t in range(steps)]
+    step.finish(H, s)
+    torch.cuda.synchronize()
+    for n in range(N):
+        fk = O.phi(case.prefix_k[n])
+        Hr, sr = fk.T @ case.prefix_v[n].astype(np.float64), fk.sum(0)
+        ref = []
+        for t in range(steps):
+            o, Hr, sr = O.decode_step(Hr, sr, case.q[t][n], case.k[t][n], case.v[t][n])
+            ref.append(o)
+        assert_close(np.array([x[n] for x in outs]), np.array(ref), RTOL_F32, f"o of head-state {n}")
+        assert_close(host(H)[n], Hr, RTOL_F32, f"H of head-state {n}")
+        assert_close(host(s)[n], sr, RTOL_F32, f"s of head-state {n}")
+
+
+@pytest.mark.parametrize("deferred", [False, True])
+def test_decode_sre_4096x128_full_chain(K, deferred):
     """The decode workload as configured: 4096 head-states, a 2048-token
     prefix, 128 steps of update, readout, scoring of 16 cached + 48 fresh
     candidates and top-16 selection, gathered into the next step's candidate
@@ -483,18 +535,20 @@ def test_decode_sre_4096x128_full_chain(K):
     sel = torch.empty((N, top), dtype=torch.int32, device="cuda")
     gpu = dict(o=[], scores=[], sel=[])
     inputs = [[], [], [], [], []]
+    step = _Stepper(K, N, deferred)
     for t in range(steps):
         cur, nxt = t & 1, (t + 1) & 1
         q, k, v, fk, fv = stream.next_step()
         ck[cur, :, top:] = dev(fk)
         cv[cur, :, top:] = dev(fv)
-        K.decode_step(H, s, dev(q), dev(k), dev(v), cand_k=ck[cur], cand_v=cv[cur], top_k=top, gather=True,
-                      out=dict(o=o, scores=sc, sel=sel, sel_k=ck[nxt], sel_v=cv[nxt], sel_stride=n_cand))
+        step(H, s, dev(q), dev(k), dev(v), cand_k=ck[cur], cand_v=cv[cur], top_k=top, gather=True,
+             out=dict(o=o, scores=sc, sel=sel, sel_k=ck[nxt], sel_v=cv[nxt], sel_stride=n_cand))
         gpu["o"].append(host(o)[check])
         gpu["scores"].append(host(sc)[check])
         gpu["sel"].append(host(sel).astype(int)[check])
         for lst, x in zip(inputs, (q, k, v, fk, fv)):
             lst.append(x[check])
+    step.finish(H, s)
     torch.cuda.synchronize()
     _oracle_chain_check(gpu, H, s, H0s, s0s, inputs, stream.cache0_k[check], stream.cache0_v[check], top, check)
 
