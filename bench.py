@@ -295,24 +295,26 @@ def bench_decode(torch, K, S, steps_loop, reps, deferred=False):
                                                    "decode_sre_kernel_decode_sre_4096x128_traffic.md"),
                           kernel="decode step + SRE + top-k (fused)", bytes_per_launch=step_bytes),
         )
-    # deferred folds: the step kernel reads H and s, the pending slots in use
-    # (on average (P - 1) / 2 of them) and writes the token's slot; every P
-    # steps a fold kernel reads and writes H and s and reads the P slots
-    read_bytes = N * (state + io + (P - 1) / 2 * 2 * d * 4 + 2 * d * 4)
-    fold_bytes = N * (2 * state + P * 2 * d * 4)
-    achieved = read_bytes / (kern_ms * 1e-3) / 1e9
-    avg_bytes = read_bytes + fold_bytes / P
+    # deferred folds: one launch per step. P - 1 of every P read H and s, the
+    # pending slots in use (n_pend = 0 .. P - 2, on average (P - 2) / 2 of
+    # them) and write the token's slot; the P-th reads and writes H and s
+    # (adding the P - 1 slots and its token) and reads the slots
+    slot = 2 * d * 4
+    read_bytes = N * (state + io + (P - 2) / 2 * slot + slot)
+    fold_bytes = N * (2 * state + io + (P - 1) * slot)
+    avg_bytes = ((P - 1) * read_bytes + fold_bytes) / P
+    achieved = avg_bytes / (kern_ms * 1e-3) / 1e9
     return dict(
         workload="decode_sre_4096x128 (deferred folds)", N=N, steps=nsteps, pending_period=P,
         step_ms=step_ms, steps_per_s=1e3 / step_ms, kernel_ms=kern_ms,
-        step_bytes_avg=avg_bytes, step_tb_per_s=avg_bytes / (step_ms * 1e-3) / 1e12,
-        step_frac_of_peak=avg_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        bytes_read_only_launch=read_bytes, bytes_fold_launch=fold_bytes,
         roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=achieved / PEAK_HBM_GBS,
                       traffic=measured_traffic("decode_fused.hip",
                                                "decode_sre_kernel_decode_sre_4096x128_deferred_traffic.md"),
-                      kernel="read-only decode step + SRE + top-k over the state and its pending pairs",
-                      bytes_per_launch=read_bytes),
+                      kernel="decode step + SRE + top-k with deferred folds (P - 1 read-only launches, "
+                             "one folding launch, averaged)",
+                      bytes_per_launch=avg_bytes),
     )
 
 

@@ -85,8 +85,10 @@ struct FusedLds {
 //   kRead : read H and s; read out and score against them plus the list
 //           (pending slots, then the token) in closed form; store the token
 //           in its pending slot.
+//   kFold : update with the list (the pending slots, then the token), write
+//           back, read out, score.
 //   kFlush: add the pending slots to H and s, write back.
-enum : int { kStep = 0, kScore = 1, kRead = 3, kFlush = 4 };
+enum : int { kStep = 0, kScore = 1, kFold = 2, kRead = 3, kFlush = 4 };
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return mfma16x16x32(a, b, c);
@@ -136,11 +138,13 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     Cand cand, int n_cand, int top_k, float* __restrict__ scores, int sstride,
     int32_t* __restrict__ sel, float* __restrict__ sel_k, float* __restrict__ sel_v, int sel_stride,
     float* __restrict__ pend_k, float* __restrict__ pend_v, int n_pend) {
-  constexpr bool kWrites = MODE == kStep || MODE == kFlush;
-  constexpr bool kReadout = MODE == kStep || MODE == kRead;
+  constexpr bool kWrites = MODE == kStep || MODE == kFold || MODE == kFlush;
+  constexpr bool kReadout = MODE == kStep || MODE == kFold || MODE == kRead;
   constexpr bool kToken = kReadout;
-  constexpr bool kList = MODE == kRead || MODE == kFlush;
-  constexpr bool kSLds = MODE == kRead;  // s from LDS
+  constexpr bool kList = MODE == kFold || MODE == kRead || MODE == kFlush;
+  constexpr bool kSLds = MODE == kRead || MODE == kFold;  // s from LDS
+  // readout sums per wave in LDS (see read_col below) rather than in registers
+  constexpr bool kLdsOut = MODE == kRead || MODE == kFold;
   constexpr int MTA = MT > 0 ? MT : 1;
   __shared__ __align__(16) FusedLds sh;
   const int n = blockIdx.x;
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     }
   }
   for (int i = tid; i < kD; i += kThreadsF) sh.tab[i] = kPairTable.ab[i];
-  if (MODE == kRead) {
+  if (kLdsOut) {
     sh.rnum[w][lane] = 0.0f;
     if (lane == 0) sh.rden[w] = 0.0f;
   }
@@ -214,16 +218,45 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   }
   __syncthreads();
   if (MODE == kRead) {
-    // (x . k_p)^2 for the query (entries 0 .. kPend - 1) and every candidate;
-    // read after the numerator reduction's first barrier
-    for (int i = tid; i < kPend * (1 + 16 * MT); i += kThreadsF) {
-      const int p = i % kPend, c = i / kPend - 1;
-      const float* x = c < 0 ? sh.qs : sh.ck[c];
-      float dot = 0.0f;
-#pragma unroll 8
-      for (int d = 0; d < kDim; ++d) dot += x[d] * sh.pkT[d][p];
-      if (c < 0) sh.wq[p] = dot * dot;
-      else sh.wc[c][p] = dot * dot;
+    // (x . k_p)^2 for the query (vector 0) and every candidate (vectors
+    // 1 ..): four threads per vector, sixteen dimensions each, all kPend
+    // listed keys at once; read after the numerator reduction's first barrier
+    const int part = tid & 3;
+    constexpr int kVec = 1 + 16 * MT;
+#pragma unroll 1
+    for (int vb = 0; vb < kVec; vb += kThreadsF / 4) {
+      const int vi = vb + (tid >> 2);
+      const float* x = (vi == 0 || vi >= kVec) ? sh.qs : sh.ck[vi - 1];
+      float dot[kPend];
+#pragma unroll
+      for (int p = 0; p < kPend; ++p) dot[p] = 0.0f;
+#pragma unroll
+      for (int dd = 0; dd < 16; ++dd) {
+        const int d = 16 * part + dd;
+        const float xd = x[d];
+        const float4 k0 = *reinterpret_cast<const float4*>(&sh.pkT[d][0]);
+        const float4 k1 = *reinterpret_cast<const float4*>(&sh.pkT[d][4]);
+        dot[0] += xd * k0.x;
+        dot[1] += xd * k0.y;
+        dot[2] += xd * k0.z;
+        dot[3] += xd * k0.w;
+        dot[4] += xd * k1.x;
+        dot[5] += xd * k1.y;
+        dot[6] += xd * k1.z;
+        dot[7] += xd * k1.w;
+      }
+#pragma unroll
+      for (int p = 0; p < kPend; ++p) {
+        dot[p] += __shfl_xor(dot[p], 1, 64);
+        dot[p] += __shfl_xor(dot[p], 2, 64);
+      }
+      if (part == 0 && vi < kVec) {
+#pragma unroll
+        for (int p = 0; p < kPend; ++p) {
+          if (vi == 0) sh.wq[p] = dot[p] * dot[p];
+          else sh.wc[vi - 1][p] = dot[p] * dot[p];
+        }
+      }
     }
   }
 
@@ -231,7 +264,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   if (MODE == kStep) v4 = *reinterpret_cast<const float4*>(&sh.vs[4 * l16]);
   // the list's values at this lane's four state columns
   float4 vl[kPend];
-  if (kList && kWrites) {
+  if (MODE == kFlush) {
 #pragma unroll
     for (int p = 0; p < kPend; ++p) vl[p] = *reinterpret_cast<const float4*>(&sh.pv[p][4 * l16]);
   }
@@ -291,6 +324,12 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
       }
     } else if (kList && kWrites) {
       // rank-kPend update: phi_f(k_p) = k_p[a] k_p[b] wt over the listed pairs
+      // (the fold reloads the list's values per tile, to leave registers to
+      // the scoring)
+      if (MODE == kFold) {
+#pragma unroll
+        for (int p = 0; p < kPend; ++p) vl[p] = *reinterpret_cast<const float4*>(&sh.pv[p][4 * l16]);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float4 a0 = *reinterpret_cast<const float4*>(&sh.pkT[pa[j]][0]);
@@ -316,7 +355,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     // hold other rows of the same columns) rather than living in registers
     // through the loop.
     float pq[8];
-    if (MODE == kRead) {
+    if (kLdsOut) {
       float dq = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -370,7 +409,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
           float x[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[j] = comp(h[j], nt);
-          if (MODE == kRead && m0 == 0) read_col(nt, x);
+          if (kLdsOut && m0 == 0) read_col(nt, x);
           bf16x8 b0, b1, b2;
           split3_pk(x, b0, b1, b2);
 #pragma unroll
@@ -383,7 +422,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
           }
         }
       }
-    } else if (MODE == kRead) {
+    } else if (kLdsOut) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float x[8];
@@ -402,7 +441,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
   if (MODE == kFlush) return;
 
   // ---- readout partials: sum over the lane quarters, then over waves
-  if (kReadout && MODE != kRead) {
+  if (kReadout && !kLdsOut) {
     float ox[4] = {oacc.x, oacc.y, oacc.z, oacc.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -453,8 +492,8 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     float num = 0.0f, den = eps;
 #pragma unroll
     for (int r = 0; r < kWaves; ++r) {
-      num += MODE == kRead ? sh.rnum[r][tid] : sh.onum[r][tid];
-      den += MODE == kRead ? sh.rden[r] : sh.oden[r];
+      num += kLdsOut ? sh.rnum[r][tid] : sh.onum[r][tid];
+      den += kLdsOut ? sh.rden[r] : sh.oden[r];
     }
     if (MODE == kRead) {
 #pragma unroll
@@ -591,12 +630,11 @@ int decode_pending_slots() { return kPend; }
 hipError_t decode_deferred_launch(const DecodeArgs& a, const SreArgs* sre, float* pend_k, float* pend_v,
                                   int n_pend, hipStream_t st) {
   prof_begin(st);
-  launch_dtypes<kRead>(a, sre, pend_k, pend_v, n_pend, st);
+  // the token that takes the last slot folds the whole list into H and s
+  if (n_pend == kPend - 1) launch_dtypes<kFold>(a, sre, pend_k, pend_v, n_pend, st);
+  else launch_dtypes<kRead>(a, sre, pend_k, pend_v, n_pend, st);
   prof_end(st);
-  hipError_t e = hipGetLastError();
-  // the last slot is now taken: the list goes into H and s
-  if (e == hipSuccess && n_pend == kPend - 1) e = decode_flush_launch(a.N, a.H, a.s, pend_k, pend_v, kPend, st);
-  return e;
+  return hipGetLastError();
 }
 
 hipError_t decode_flush_launch(int N, float* H, float* s, const float* pend_k, const float* pend_v, int n_pend,
