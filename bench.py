@@ -127,8 +127,8 @@ def timed_calls(torch, K, fn, steps, warmup):
 
 def bench_prefill(torch, K, S, name, steps, warmup, factors=1, factor_kind="concat"):
     """kla_prefill on a configuration (factors > 1: a multi-factor lift
-    through kla_prefill_factors, the concatenated KATA-Mg on the matrix path
-    or the summed KATA-Sigma-g on the float32 vector path)."""
+    through kla_prefill_factors, the concatenated KATA-Mg or the summed
+    KATA-Sigma-g, on the matrix path for bf16 inputs with d = 64)."""
     cfg = S.CONFIGS[name]
     c = S.prefill_case(name, cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], cfg["chunk"],
                        cfg["seed"])
@@ -146,7 +146,7 @@ def bench_prefill(torch, K, S, name, steps, warmup, factors=1, factor_kind="conc
     # whole call: plus the causal intra-chunk term
     C = cfg["chunk"]
     call_flops = kern_flops + (C + 1) * (d + dv + 1) * head_tokens
-    mfma = K.prefill_uses_matrix_cores() and (factors == 1 or factor_kind == "concat")
+    mfma = K.prefill_uses_matrix_cores()
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_F32_VALU_TFLOPS
     achieved = kern_flops / (kern_ms * 1e-3) / 1e12
     traffic = None

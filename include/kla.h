@@ -147,7 +147,8 @@ KLA_API kla_status_t kla_prefill(const kla_shape_t* shp, int chunk, const void* 
  *   KLA_FACTORS_SUM (KATA-Sigma-g): the lift of sum_i x_i x_i^T,
  *     D = p (p + 1) / 2 features (2080, 528, 136), in the vec_sym order over
  *     p dimensions, feature (a, b) = sum_i x_i,a x_i,b (times sqrt(2) for
- *     a < b); every shape runs on the float32 vector path (float32
+ *     a < b). bf16 inputs with d_qk = d_v = 64 run on the matrix path (bf16
+ *     accuracy, 2e-2), the rest on the float32 vector path (float32
  *     arithmetic, 1e-4 relative; bf16 inputs are read exactly).
  * H0/s0/H_T/s_T are [N, D, d_v] and [N, D] float32 in that layout. The
  * outputs are those of kla_prefill_quadratic_factors with the same kind.

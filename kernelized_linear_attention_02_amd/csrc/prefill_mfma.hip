@@ -203,13 +203,31 @@ __device__ __forceinline__ void wg_identity(int N, int SF, int& n, int& sf, int&
 __host__ __device__ constexpr int bp_x(int bp) { return bp < 4 ? 0 : bp < 7 ? 1 : bp < 9 ? 2 : 3; }
 __host__ __device__ constexpr int bp_y(int bp) { return bp < 4 ? bp : bp < 7 ? bp - 3 : bp < 9 ? bp - 5 : 3; }
 
+// Lift variants, by the template parameter G: G > 0 the concatenation of G
+// factors' rank-one lifts (KATA-Mg; G = 1 the rank-one lift itself), G < 0
+// the summed lift of -G factors (KATA-Sigma-g: feature (a, b) of one
+// factor's dimensions is sum_f x_(f p + a) x_(f p + b), p = 64 / -G).
+__host__ __device__ constexpr int nfac(int G) { return G < 0 ? -G : G; }
+__host__ __device__ constexpr bool summed(int G) { return G < 0; }
+__host__ __device__ constexpr int fdim(int G) { return kDim / nfac(G); }
+// blocks of 16 dimensions between one factor and the next
+__host__ __device__ constexpr int fstride(int G) { return fdim(G) / 16; }
+
 // Block pairs of the lift with G factors (KATA-Mg, concatenated factor lifts:
 // only pairs of dimensions inside one factor of 64 / G dimensions are
 // features): G = 1 all ten, G = 2 the six inside the halves, G = 4 the four
-// diagonal blocks.
-__host__ __device__ constexpr int factor_bps(int G) { return G == 1 ? 10 : G == 2 ? 6 : 4; }
+// diagonal blocks. The summed lifts keep the first factor's pairs: three
+// (G = -2) or one (G = -4); each of their features adds the same pair of
+// blocks of every factor.
+__host__ __device__ constexpr int factor_bps(int G) {
+  return G == 1 ? 10 : G == 2 ? 6 : G == 4 ? 4 : G == -2 ? 3 : 1;
+}
 __host__ __device__ constexpr int factor_bp(int G, int i) {
-  return G == 1 ? i : G == 2 ? (i < 2 ? i : i == 2 ? 4 : i + 4) : (i == 0 ? 0 : i == 1 ? 4 : i == 2 ? 7 : 9);
+  return G == 1    ? i
+         : G == 2  ? (i < 2 ? i : i == 2 ? 4 : i + 4)
+         : G == 4  ? (i == 0 ? 0 : i == 1 ? 4 : i == 2 ? 7 : 9)
+         : G == -2 ? (i < 2 ? i : 4)
+                   : 0;
 }
 
 // The tiles of one feature slice: SF = 4 slices hold j = 4 sf + jj (jj < 4),
@@ -220,7 +238,7 @@ __host__ __device__ constexpr int factor_bp(int G, int i) {
 template <int SF, int G>
 struct Slice {
   static_assert(SF == 4 || SF == 8, "feature slices per head");
-  static_assert(G == 1 || G == 2 || G == 4, "factors");
+  static_assert(G == 1 || G == 2 || G == 4 || G == -2 || G == -4, "factors");
   static constexpr int kBP = factor_bps(G);
   static constexpr int kJ = 16 / SF;
   static constexpr int kTiles = kJ * kBP;
@@ -233,41 +251,52 @@ struct Slice {
   __host__ __device__ static constexpr int bp(int u) { return factor_bp(G, u % kBP); }
   __host__ __device__ static constexpr int X(int u) { return bp_x(bp(u)); }
   __host__ __device__ static constexpr int Y(int u) { return bp_y(bp(u)); }
+  // the summed lifts also read the same blocks of the other factors
+  static constexpr int kNF = summed(G) ? nfac(G) : 1;
   __host__ __device__ static constexpr bool upd_uses_x(int w, int x) {
     for (int u = w * kNU; u < (w + 1) * kNU; ++u)
-      if (X(u) == x) return true;
+      for (int f = 0; f < kNF; ++f)
+        if (X(u) + f * fstride(G) == x) return true;
     return false;
   }
   __host__ __device__ static constexpr bool upd_uses_y(int w, int y) {
     for (int u = w * kNU; u < (w + 1) * kNU; ++u)
-      if (Y(u) == y) return true;
+      for (int f = 0; f < kNF; ++f)
+        if (Y(u) + f * fstride(G) == y) return true;
     return false;
   }
   __host__ __device__ static constexpr bool rd_uses_x(int h, int x) {
     for (int u = 2 * h * kNP; u < 2 * (h + 1) * kNP; ++u)
-      if (X(u) == x) return true;
+      for (int f = 0; f < kNF; ++f)
+        if (X(u) + f * fstride(G) == x) return true;
     return false;
   }
   __host__ __device__ static constexpr bool rd_uses_y(int h, int y) {
     for (int u = 2 * h * kNP; u < 2 * (h + 1) * kNP; ++u)
-      if (Y(u) == y) return true;
+      for (int f = 0; f < kNF; ++f)
+        if (Y(u) + f * fstride(G) == y) return true;
     return false;
   }
 };
 
 // Index of feature (a, b), a <= b in one factor, in the ABI's state layout:
-// the factors' vec_sym blocks in order, each upper-triangular row-major.
+// the factors' vec_sym blocks in order, each upper-triangular row-major (the
+// summed lifts: one such block, a and b in the first factor).
 template <int G>
 __device__ __forceinline__ int feat_abi(int a, int b) {
-  constexpr int p = kDim / G;
+  constexpr int p = fdim(G);
   const int f = a / p;
   const int i = a - f * p, j = b - f * p;
   return f * (p * (p + 1) / 2) + i * p - i * (i - 1) / 2 + (j - i);
 }
 
+// Whether the keys' Gram entry (a, b) belongs to the state: a pair inside
+// one factor, or for the summed lifts a pair inside the first factor (the
+// entry then holds the sum over the factors).
 template <int G>
 __host__ __device__ __forceinline__ bool same_factor(int a, int b) {
-  constexpr int p = kDim / G;
+  constexpr int p = fdim(G);
+  if (summed(G)) return a < p && b < p;
   return a / p == b / p;
 }
 
@@ -431,11 +460,13 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
   const int nsteps = cx.NC * SUB;
   const int j = cx.j0 + JJ;
   const float inv_sqrt2 = 0.70710678118654752f;
-  const bool gram_wg = cx.ch == 0;  // the first value half also forms the Gram matrix
+  // the first value half also forms the Gram matrix (for the summed lifts
+  // only its first factor's rows, each the sum over the factors)
+  const bool gram_wg = cx.ch == 0 && (!summed(G) || W < fstride(G));
 
   // Gram column of this lane: the slice's b values 16 Y + j0 + jj
   const int gb = 16 * (l16 / SL::kJ) + cx.j0 + (l16 % SL::kJ);
-  const bool gb_ok = l16 < SL::kNB;
+  const bool gb_ok = l16 < SL::kNB && (!summed(G) || gb < fdim(G));
 
   // readout weight of the rows 4 q4 .. 4 q4 + 3 of a diagonal-block tile
   // (column j): 2 for a < b, 1 for a = b, 0 for the mirror rows a > b
@@ -585,20 +616,34 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
       for (int u = 0; u < NU; ++u) {
         const uint4 xa = ka[ks][SL::X(U0 + u)];
         const uint4 xb = kb[ks][SL::Y(U0 + u)];
-        const uint32_t p0 = as_u(as_h2(xa.x) * as_h2(xb.x));
-        const uint32_t p1 = as_u(as_h2(xa.y) * as_h2(xb.y));
-        const uint32_t p2 = as_u(as_h2(xa.z) * as_h2(xb.z));
-        const uint32_t p3 = as_u(as_h2(xa.w) * as_h2(xb.w));
-        const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(p0, p1, p2, p3));
+        f16x2 p0 = as_h2(xa.x) * as_h2(xb.x);
+        f16x2 p1 = as_h2(xa.y) * as_h2(xb.y);
+        f16x2 p2 = as_h2(xa.z) * as_h2(xb.z);
+        f16x2 p3 = as_h2(xa.w) * as_h2(xb.w);
+        // summed lifts: the same pair of blocks of the other factors
+#pragma unroll
+        for (int f = 1; f < SL::kNF; ++f) {
+          const uint4 ya = ka[ks][SL::X(U0 + u) + f * fstride(G)];
+          const uint4 yb = kb[ks][SL::Y(U0 + u) + f * fstride(G)];
+          p0 += as_h2(ya.x) * as_h2(yb.x);
+          p1 += as_h2(ya.y) * as_h2(yb.y);
+          p2 += as_h2(ya.z) * as_h2(yb.z);
+          p3 += as_h2(ya.w) * as_h2(yb.w);
+        }
+        const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(as_u(p0), as_u(p1), as_u(p2), as_u(p3)));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) h[u][nt] = mfma_h(A, vb[ks][nt], h[u][nt]);
         if (ks == KS - 1 && u >= kLag && pub) publish_tile(cn, u - kLag);
       }
       if (gram_wg) {
-        const f16x8 A = *reinterpret_cast<const f16x8*>(&sh.kt[buf][16 * W + l16][t0]);
-        f16x8 B = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
-        if (gb_ok) B = *reinterpret_cast<const f16x8*>(&sh.kt[buf][gb][t0]);
-        gsub = mfma_h(A, B, gsub);
+#pragma unroll
+        for (int f = 0; f < SL::kNF; ++f) {
+          const int off = 16 * f * fstride(G);
+          const f16x8 A = *reinterpret_cast<const f16x8*>(&sh.kt[buf][16 * W + off + l16][t0]);
+          f16x8 B = __builtin_bit_cast(f16x8, make_uint4(0, 0, 0, 0));
+          if (gb_ok) B = *reinterpret_cast<const f16x8*>(&sh.kt[buf][gb + off][t0]);
+          gsub = mfma_h(A, B, gsub);
+        }
       }
     }
     if (gram_wg) {
@@ -610,7 +655,7 @@ __device__ __forceinline__ void update_wave(StateLds<SF, G>& sh, const StateCtx&
     }
     if (pub) {
 #pragma unroll
-      for (int u = NU - kLag; u < NU; ++u) publish_tile(cn, u);
+      for (int u = NU > kLag ? NU - kLag : 0; u < NU; ++u) publish_tile(cn, u);
       publish_rest(cn);
     }
     lds_barrier();  // (B) one barrier per sub-chunk
@@ -744,15 +789,28 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
       for (int tt = 0; tt < 2; ++tt) {
         // q'_b of each tile (doubled off the diagonal blocks), broadcast to
         // both halves (an op_sel of the packed multiply)
-        const f16x2 c0 = as_h2(X0 < Y0 ? qb2[tt][Y0][J0 >> 1] : qb[tt][Y0][J0 >> 1]);
-        const f16x2 c1 = as_h2(X1 < Y1 ? qb2[tt][Y1][J1 >> 1] : qb[tt][Y1][J1 >> 1]);
-        const f16x2 bb0 = (J0 & 1) ? __builtin_shufflevector(c0, c0, 1, 1) : __builtin_shufflevector(c0, c0, 0, 0);
-        const f16x2 bb1 = (J1 & 1) ? __builtin_shufflevector(c1, c1, 1, 1) : __builtin_shufflevector(c1, c1, 0, 0);
-        const uint32_t p0 = as_u(as_h2(qa[tt][X0].x) * bb0);
-        const uint32_t p1 = as_u(as_h2(qa[tt][X0].y) * bb0);
-        const uint32_t p2 = as_u(as_h2(qa[tt][X1].x) * bb1);
-        const uint32_t p3 = as_u(as_h2(qa[tt][X1].y) * bb1);
-        const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(p0, p1, p2, p3));
+        f16x2 p0 = {}, p1 = {}, p2 = {}, p3 = {};
+        // summed lifts: the same pair of blocks of every factor
+#pragma unroll
+        for (int f = 0; f < SL::kNF; ++f) {
+          const int o = f * fstride(G);
+          const f16x2 c0 = as_h2(X0 < Y0 ? qb2[tt][Y0 + o][J0 >> 1] : qb[tt][Y0 + o][J0 >> 1]);
+          const f16x2 c1 = as_h2(X1 < Y1 ? qb2[tt][Y1 + o][J1 >> 1] : qb[tt][Y1 + o][J1 >> 1]);
+          const f16x2 bb0 = (J0 & 1) ? __builtin_shufflevector(c0, c0, 1, 1) : __builtin_shufflevector(c0, c0, 0, 0);
+          const f16x2 bb1 = (J1 & 1) ? __builtin_shufflevector(c1, c1, 1, 1) : __builtin_shufflevector(c1, c1, 0, 0);
+          if (f == 0) {
+            p0 = as_h2(qa[tt][X0].x) * bb0;
+            p1 = as_h2(qa[tt][X0].y) * bb0;
+            p2 = as_h2(qa[tt][X1].x) * bb1;
+            p3 = as_h2(qa[tt][X1].y) * bb1;
+          } else {
+            p0 += as_h2(qa[tt][X0 + o].x) * bb0;
+            p1 += as_h2(qa[tt][X0 + o].y) * bb0;
+            p2 += as_h2(qa[tt][X1 + o].x) * bb1;
+            p3 += as_h2(qa[tt][X1 + o].y) * bb1;
+          }
+        }
+        const f16x8 A = __builtin_bit_cast(f16x8, make_uint4(as_u(p0), as_u(p1), as_u(p2), as_u(p3)));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mfma_h(A, B[nt], acc[tt][nt]);
       }
@@ -780,7 +838,8 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
     const int ekr = __builtin_amdgcn_readfirstlane(L.ek);
     const int ev = __builtin_amdgcn_readfirstlane(L.ev);
     const bool contributes = ekr != kNoExp && ev != kNoExp;
-    if (contributes) g.add(2 * ekr + ev, CS);
+    // a summed lift's features add -G products: their bound is -G times larger
+    if (contributes) g.add(2 * ekr + ev + (summed(G) ? (nfac(G) == 2 ? 1 : 2) : 0), CS);
     const int ek = ekr == kNoExp ? 0 : ekr;
     // v was staged times 2^-ev; the update needs it times 2^(2 ek - G)
     const _Float16 f = contributes ? (_Float16)__builtin_ldexpf(1.0f, 2 * ek + ev - g.G) : (_Float16)0.0f;
@@ -956,7 +1015,7 @@ __global__ __launch_bounds__(kThreads3, 1) void prefill_state_kernel(
   cx.v = v;
   cx.T = T;
   cx.NC = (T + C - 1) / C;
-  cx.D = G * (kDim / G) * (kDim / G + 1) / 2;
+  cx.D = (summed(G) ? 1 : G) * fdim(G) * (fdim(G) + 1) / 2;
   wg_identity(N, SF, cx.n, cx.sf, cx.ch);
   cx.j0 = Slice<SF, G>::kJ * cx.sf;
   cx.H0 = H0;
@@ -995,11 +1054,33 @@ struct FinishLds {
 
 // Weights of one 16-key x 16-query tile, key-major: the lane with query
 // column l16 and group q4 gets keys 4 q4 + i of the tile. (q . k)^2, or for
-// G factors the sum of the factors' squared scores.
+// G factors the sum of the factors' squared scores, or for the summed lifts
+// the sum over every pair of factors (i, j) of (q_i . k_j)^2
+// (phi(q) . phi(k) of the summed lift).
 template <int C, int G>
 __device__ __forceinline__ f32x4 finish_weights(const FinishLds<C>& sh, int kq, int mq, int l16, int q4) {
   f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (G == 4) {
+  if constexpr (G == -2) {
+#pragma unroll
+    for (int fk = 0; fk < 2; ++fk)
+#pragma unroll
+      for (int fq = 0; fq < 2; ++fq) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sh.ks[kq * 16 + l16][32 * fk + 8 * q4]);
+        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sh.qs[mq * 16 + l16][32 * fq + 8 * q4]);
+        const f32x4 s4 = mfma_b(A, B, f32x4{0.f, 0.f, 0.f, 0.f});
+        w4 += s4 * s4;
+      }
+  } else if constexpr (G == -4) {
+#pragma unroll
+    for (int fk = 0; fk < 4; ++fk)
+#pragma unroll
+      for (int fq = 0; fq < 4; ++fq) {
+        const s16x4 A = *reinterpret_cast<const s16x4*>(&sh.ks[kq * 16 + l16][16 * fk + 4 * q4]);
+        const s16x4 B = *reinterpret_cast<const s16x4*>(&sh.qs[mq * 16 + l16][16 * fq + 4 * q4]);
+        const f32x4 s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        w4 += s4 * s4;
+      }
+  } else if constexpr (G == 4) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const s16x4 A = *reinterpret_cast<const s16x4*>(&sh.ks[kq * 16 + l16][16 * f + 4 * q4]);
@@ -1067,21 +1148,31 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
   // lane (column 16 nt + l16, dims 32 ks + 8 q4 + e); S is symmetric, so the
   // fragment is row 16 nt + l16 of S. For G factors only the factors'
   // diagonal blocks count (phi(q).s = sum over factors of q_f^T S_ff q_f).
+  // For the summed lifts the state kernel wrote the first factor's block,
+  // already summed over the factors (A = sum_f S_ff), and
+  // phi(q).s = sum_f q_f^T A q_f: every diagonal block holds A.
   bf16x8 Shi[2][4], Slo[2][4];
   {
     const float* S = Sg + ((size_t)n * gridDim.x + blockIdx.x) * kDim * kDim;
+    constexpr int p = fdim(G);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int col = 16 * nt + l16;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const float4* src = reinterpret_cast<const float4*>(S + col * kDim + 32 * ks + 8 * q4);
-        const float4 x0 = src[0], x1 = src[1];
+        const int d0 = 32 * ks + 8 * q4;
+        const float4* src = reinterpret_cast<const float4*>(
+            summed(G) ? S + (col % p) * kDim + (d0 % p) : S + col * kDim + d0);
+        float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+        if (!summed(G) || d0 / p == col / p) {
+          x0 = src[0];
+          x1 = src[1];
+        }
         const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 32 * ks + 8 * q4 + e;
-          const float x = same_factor<G>(d, col) ? xv[e] : 0.0f;
+          const float x = (summed(G) || same_factor<G>(d, col)) ? xv[e] : 0.0f;
           const __bf16 hi = (__bf16)x;
           Shi[ks][nt][e] = hi;
           Slo[ks][nt][e] = (__bf16)(x - (float)hi);
@@ -1186,12 +1277,15 @@ __global__ __launch_bounds__(kThreads) void prefill_finish_kernel(
   }
 }
 
+bool summed_lift(const PrefillArgs& a) { return a.factor_kind == 1 && a.factors > 1; }
+
 // Feature slices per head: 8 while that keeps at most 256 work-groups
-// (two per slice), else 4.
-int slices_for(int N) { return N <= 16 ? 8 : 4; }
+// (two per slice), else 4; 4 for the summed lifts (their 3 or 1 block pairs
+// per value of j fill four update waves only with four values of j).
+int slices_for(const PrefillArgs& a) { return (a.N <= 16 && !summed_lift(a)) ? 8 : 4; }
 
 size_t part_bytes(const PrefillArgs& a) {
-  const int SF = slices_for(a.N);
+  const int SF = slices_for(a);
   const size_t nc = (a.T + a.chunk - 1) / a.chunk;
   return align_up((size_t)a.N * nc * SF * (a.chunk / 16) * kTilePart * sizeof(float));
 }
@@ -1234,14 +1328,18 @@ hipError_t launch_c(const PrefillArgs& a, void* ws, hipStream_t st) {
   char* rest = p + stage_bytes(a) + exps_bytes(a);
   float* part = a.o ? reinterpret_cast<float*>(rest) : nullptr;
   float* Sg = a.o ? reinterpret_cast<float*>(rest + part_bytes(a)) : nullptr;
-  const int SF = slices_for(a.N);
+  const int SF = slices_for(a);
   const int ns = (int)staged_sub_chunks(a);
   hipLaunchKernelGGL((prefill_stage_kernel<CS>), dim3((ns + kStageR - 1) / kStageR, a.N), dim3(4 * CS), 0, st,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.T, ns, stage, exps);
   prof_begin(st);
-  if (SF == 8) launch_state<C, 8, G>(a, part, Sg, stage, exps, st);
-  else launch_state<C, 4, G>(a, part, Sg, stage, exps, st);
+  if constexpr (summed(G)) {
+    launch_state<C, 4, G>(a, part, Sg, stage, exps, st);
+  } else {
+    if (SF == 8) launch_state<C, 8, G>(a, part, Sg, stage, exps, st);
+    else launch_state<C, 4, G>(a, part, Sg, stage, exps, st);
+  }
   prof_end(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !part) return e;
@@ -1271,7 +1369,7 @@ hipError_t launch_g(const PrefillArgs& a, void* ws, hipStream_t st) {
 
 bool prefill_mfma_supported(const PrefillArgs& a) {
   return a.in_bf16 && a.dqk == kDim && a.dv == kDim && (a.chunk == 32 || a.chunk == 64 || a.chunk == 128) &&
-         a.factor_kind == 0 && (a.factors == 1 || a.factors == 2 || a.factors == 4);
+         (a.factor_kind == 0 || a.factor_kind == 1) && (a.factors == 1 || a.factors == 2 || a.factors == 4);
 }
 
 size_t prefill_mfma_workspace(const PrefillArgs& a) {
@@ -1279,6 +1377,11 @@ size_t prefill_mfma_workspace(const PrefillArgs& a) {
 }
 
 hipError_t prefill_mfma_launch(const PrefillArgs& a, void* ws, hipStream_t st) {
+  if (summed_lift(a)) {
+    if (a.factors == 2) return launch_g<-2>(a, ws, st);
+    if (a.factors == 4) return launch_g<-4>(a, ws, st);
+    return hipErrorInvalidValue;
+  }
   switch (a.factors) {
     case 1: return launch_g<1>(a, ws, st);
     case 2: return launch_g<2>(a, ws, st);

@@ -208,14 +208,16 @@ def test_factors_vector_path_bf16_inputs(K, g):
 
 
 # ---- the summed lift (KATA-Sigma-g) through the chunked state form: the
-# float32 vector path for every shape, float32 arithmetic on exact inputs, so
-# the float32 bound against the oracle's state form of the same lift
+# float32 vector path for float32 inputs and for head sizes other than 64
+# (float32 arithmetic on exact inputs, so the float32 bound against the
+# oracle's state form of the same lift); bf16 inputs with d_qk = d_v = 64 take
+# the matrix-core kernel (tests further below, at the bf16 bound)
 
 @pytest.mark.parametrize("g", [2, 4])
 @pytest.mark.parametrize("B,H,T,dqk,dv,chunk,eps,dtype", [
     (1, 2, 100, 64, 64, 64, 0.0, torch.float32), (2, 3, 77, 32, 16, 32, 0.2, torch.float32),
     (1, 2, 300, 16, 64, 128, 0.0, torch.float32), (1, 1, 1, 32, 32, 64, 0.0, torch.float32),
-    (2, 2, 130, 64, 64, 64, 0.0, torch.bfloat16), (1, 3, 97, 64, 32, 32, 0.1, torch.bfloat16)])
+    (1, 3, 97, 64, 32, 32, 0.1, torch.bfloat16), (1, 2, 70, 32, 64, 64, 0.0, torch.bfloat16)])
 def test_factors_sum_state_form_every_row(K, g, B, H, T, dqk, dv, chunk, eps, dtype):
     c = S.prefill_case("factors_sum_state", B, H, T, dqk, dv, chunk, seed=600 + g + T + dqk)
     o, HT, sT = K.prefill(dev(c.q, dtype), dev(c.k, dtype), dev(c.v, dtype), chunk=chunk, eps=eps,
@@ -260,3 +262,71 @@ def test_factors_sum_one_factor_is_prefill(K):
     a = K.prefill(q, k, v, chunk=32)
     b = K.prefill(q, k, v, chunk=32, factors=1, factor_kind="sum")
     assert torch.equal(a, b)
+
+
+# ---- the summed lift on the matrix cores (bf16 inputs, d_qk = d_v = 64):
+# float16 products of the staged inputs, float32 accumulation, so the bf16
+# bound against the oracle's state form on the same rounded inputs
+
+@pytest.mark.parametrize("g", [2, 4])
+@pytest.mark.parametrize("B,H,chunk,T,eps", [(1, 3, 64, 50, 0.0), (2, 2, 128, 300, 0.0), (2, 10, 64, 130, 0.1),
+                                              (1, 17, 32, 97, 0.0), (1, 2, 64, 1, 0.0)])
+def test_factors_sum_matrix_path_every_row(K, g, B, H, chunk, T, eps):
+    assert K.prefill_uses_matrix_cores(B, H, T, 64, 64, chunk)
+    c = S.prefill_case("factors_sum_mfma", B, H, T, 64, 64, chunk, seed=700 + g + T)
+    o, HT, sT = K.prefill(dev(c.q), dev(c.k), dev(c.v), chunk=chunk, eps=eps, return_state=True,
+                          out_dtype=torch.float32, factors=g, factor_kind="sum")
+    torch.cuda.synchronize()
+    D = K.factor_phi_dim(64, g, "sum")
+    assert HT.shape == (B, H, D, 64) and sT.shape == (B, H, D)
+    for b in range(B):
+        for h in range(H):
+            ro, rH, rs = O.prefill_factors_recurrent(c.q[b, h], c.k[b, h], c.v[b, h], g, "sum", eps=eps)
+            assert_close(host(o)[b, h], ro, RTOL_BF16, f"o g={g} head ({b},{h})")
+            assert_close(host(HT)[b, h], rH, RTOL_BF16, f"H_T g={g} head ({b},{h})")
+            assert_close(host(sT)[b, h], rs, RTOL_BF16, f"s_T g={g} head ({b},{h})")
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_factors_sum_matrix_path_resume(K, g):
+    # a state carried between calls (imported, exported) equals one call, and
+    # equals the definition sum_{i,j} (q_i . k_j)^2; state-only mode too
+    c = S.prefill_case("factors_sum_mfma_resume", 1, 3, 500, 64, 64, 64, seed=720 + g)
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    T1 = 192
+    o1, H1, s1 = K.prefill(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], chunk=64, return_state=True, factors=g,
+                           factor_kind="sum")
+    o2, H2, s2 = K.prefill(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], chunk=128, state=(H1, s1),
+                           return_state=True, factors=g, factor_kind="sum")
+    Hs, ss = K.prefill(q, k, v, chunk=32, outputs=False, factors=g, factor_kind="sum")
+    ro = np.stack([O.prefill_factors_bruteforce(c.q[0, h], c.k[0, h], c.v[0, h], g, "sum") for h in range(3)])
+    assert_close(host(torch.cat([o1, o2], dim=2))[0], ro, RTOL_BF16, "resumed o")
+    for h in range(3):
+        _, rH, rs = O.prefill_factors_recurrent(c.q[0, h], c.k[0, h], c.v[0, h], g, "sum")
+        assert_close(host(H2)[0, h], rH, RTOL_BF16, "resumed H")
+        assert_close(host(s2)[0, h], rs, RTOL_BF16, "resumed s")
+        assert_close(host(Hs)[0, h], rH, RTOL_BF16, "state-only H")
+        assert_close(host(ss)[0, h], rs, RTOL_BF16, "state-only s")
+
+
+def test_factors_sum_matrix_path_4x8x4096_full_size(K):
+    # KATA-Sigma-2 on the main prefill workload: every row of two heads against
+    # the oracle's state form, sampled rows of two more against the definition,
+    # the final state of one head
+    cfg = S.CONFIGS["prefill_4x8x4096"]
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    c = S.prefill_case("prefill_4x8x4096", B, H, T, cfg["d_qk"], cfg["d_v"], cfg["chunk"], cfg["seed"])
+    o, HT, sT = K.prefill(dev(c.q), dev(c.k), dev(c.v), chunk=64, return_state=True, factors=2, factor_kind="sum")
+    go, gH, gs = host(o), host(HT), host(sT)
+    for (b, h) in [(0, 0), (B - 1, H - 1)]:
+        ro, rH, rs = O.prefill_factors_recurrent(c.q[b, h], c.k[b, h], c.v[b, h], 2, "sum")
+        assert_close(go[b, h], ro, RTOL_BF16, f"o head ({b},{h})")
+        assert_close(gH[b, h], rH, RTOL_BF16, f"H_T head ({b},{h})")
+        assert_close(gs[b, h], rs, RTOL_BF16, f"s_T head ({b},{h})")
+    rng = np.random.default_rng(8)
+    for (b, h) in [(1, 3), (2, 6)]:
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, T - 1], rng.integers(0, T, 12)]))
+        W = np.where(np.arange(T)[None, :] <= rows[:, None],
+                     O.factor_weights(c.q[b, h][rows], c.k[b, h], 2, "sum"), 0.0)
+        ref = (W @ c.v[b, h].astype(np.float64)) / W.sum(axis=1)[:, None]
+        assert_close(go[b, h, rows], ref, RTOL_BF16, f"o rows head ({b},{h})")
