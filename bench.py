@@ -718,7 +718,7 @@ def main():
                                   lambda: cpu_baseline_factor_state(S, name, cs, 2, "concat")))
         log("[bench] secondary: prefill_4x8x4096 with the KATA-Sigma-2 lift (chunked state form)")
         secondary.append(with_cpu(
-            bench_prefill(torch, K, S, name, max(2, args.steps // 10), 1, factors=2, factor_kind="sum"),
+            bench_prefill(torch, K, S, name, args.steps, args.warmup, factors=2, factor_kind="sum"),
             lambda: cpu_baseline_factor_state(S, name, cs, 2, "sum")))
         log("[bench] secondary: prefill_1x16x65536 with the KATA-M2 lift (chunked state form)")
         secondary.append(with_cpu(
