@@ -391,6 +391,50 @@ def test_decode_step_with_selection_matrix_path(K, dtype, out_dtype, eps):
         np.testing.assert_array_equal(host(r["sel_k"])[n], ck[n][sel])
 
 
+@pytest.mark.parametrize("dtype,out_dtype,eps,n_cand,top_k", [
+    ("f32", "f32", 0.0, 40, 9), ("bf16", "bf16", 0.0, 64, 16), ("f32", "f32", 0.25, 16, 3),
+    ("bf16", "f32", 0.1, 33, 33)])
+def test_decode_deferred_with_selection(K, dtype, out_dtype, eps, n_cand, top_k):
+    """Deferred folds over 11 tokens (a fold at the eighth, a flush of three
+    at the end), with fresh candidates at every token: o, scores, selections
+    and gathered rows of every token against the oracle's recurrence, and the
+    flushed state."""
+    rng = np.random.default_rng(79 + n_cand)
+    N, d, steps = 7, 64, 11
+    pk = rng.standard_normal((N, 120, d)).astype(np.float32) / 8
+    pv = rng.standard_normal((N, 120, d)).astype(np.float32)
+    H, s = K.prefill(dev(pk)[None], dev(pk)[None], dev(pv)[None], chunk=32, outputs=False)
+    H, s = H[0].contiguous(), s[0].contiguous()
+    rH = [O.phi(pk[n]).T @ pv[n].astype(np.float64) for n in range(N)]
+    rs = [O.phi(pk[n]).sum(0) for n in range(N)]
+    tt = tdtype(dtype)
+    rtol_o = RTOL_BF16 if out_dtype == "bf16" else RTOL_F32
+    step = _Stepper(K, N, True)
+    for t in range(steps):
+        q, k, v = (rng.standard_normal((N, d)).astype(np.float32) / f for f in (8, 8, 1))
+        if dtype == "bf16":
+            q, k, v = (S.round_to_bf16(x) for x in (q, k, v))
+        ck = rng.standard_normal((N, n_cand, d)).astype(np.float32) / 8
+        cv = rng.standard_normal((N, n_cand, d)).astype(np.float32)
+        o, r = step(H, s, dev(q, tt), dev(k, tt), dev(v, tt), eps=eps, out_dtype=tdtype(out_dtype),
+                    cand_k=dev(ck), cand_v=dev(cv), top_k=top_k, gather=True)
+        torch.cuda.synchronize()
+        go, gsc, gsel, gsk = host(o), host(r["scores"]), host(r["sel"]).astype(int), host(r["sel_k"])
+        for n in range(N):
+            ro, rH[n], rs[n] = O.decode_step(rH[n], rs[n], q[n], k[n], v[n], eps=eps)
+            assert_close(go[n], ro, rtol_o, f"o token {t} head {n}")
+            rsc = O.sre(rH[n], rs[n], ck[n], cv[n], eps=eps)
+            assert_close(gsc[n], rsc, RTOL_F32, f"scores token {t} head {n}")
+            assert O.near_tie_ok(rsc, gsel[n], top_k, TIE_REL), f"selection token {t} head {n}"
+            np.testing.assert_array_equal(gsk[n], ck[n][gsel[n]])
+    assert step.n_pend == steps % K.decode_pending_period()
+    step.finish(H, s)
+    torch.cuda.synchronize()
+    for n in range(N):
+        assert_close(host(H)[n], rH[n], RTOL_F32, f"H head {n}")
+        assert_close(host(s)[n], rs[n], RTOL_F32, f"s head {n}")
+
+
 def _oracle_chain_check(gpu, H, s, H0s, s0s, inputs, cache0_k, cache0_v, top, check_ids):
     """Each checked head-state's oracle chain against what the GPU recorded,
     following the GPU's selections through near-ties (rule R17)."""
