@@ -32,8 +32,9 @@
 // pairs that are not yet folded in reads out as
 //   phi(x)^T H + sum_j (x . k_j)^2 v_j,   phi(x)^T s + sum_j (x . k_j)^2,
 // for the query and for every candidate key alike. A deferred step reads H
-// and s, writes neither, and appends its pair to the list; when the list is
-// full a second pass adds all of it (rank kPend) to H and s.
+// and s, writes neither, and appends its pair to the list; the step whose
+// pair fills the list adds all of it (rank kPend) to H and s in the same
+// pass that reads them out and scores.
 #include "kla_device.hpp"
 #include "kla_internal.hpp"
 #include "mfma_bf16.hpp"
@@ -130,7 +131,8 @@ struct CandRows {
 // (MT: 16-candidate blocks, 0 for none). SELECT: top_k selection and gather
 // in the same kernel (requires n_cand <= 16 * MT, one group). The deferred
 // modes take the pending slots of head-state n from pend_k / pend_v
-// ([N, kPend, 64] float32), n_pend of them in use (kRead: n_pend < kPend).
+// ([N, kPend, 64] float32), n_pend of them in use (kRead: n_pend < kPend - 1;
+// kFold: n_pend = kPend - 1; kFlush: n_pend <= kPend).
 template <int MT, int MODE, bool SELECT, typename Tin, typename Tout, typename Cand>
 __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     float* __restrict__ H, float* __restrict__ s, const Tin* __restrict__ q,

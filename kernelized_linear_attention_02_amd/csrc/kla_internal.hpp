@@ -107,7 +107,7 @@ hipError_t sre_fused_launch(int N, float eps, const float* H, const float* s, co
                             hipStream_t st);
 // The same step with deferred folds (d_qk = d_v = 64; sre NULL or n_cand <=
 // 64): pend_k / pend_v hold decode_pending_slots() pairs per head-state, the
-// first n_pend in use; n_pend = decode_pending_slots() folds them and the
+// first n_pend in use; n_pend = decode_pending_slots() - 1 folds them and the
 // step's token, fewer only read the state and store the token in slot n_pend.
 int decode_pending_slots();
 hipError_t decode_deferred_launch(const DecodeArgs& a, const SreArgs* sre, float* pend_k, float* pend_v,
