@@ -466,6 +466,18 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
     d += __shfl_xor(d, 32, 64);
     if (q4 == 0) sh.den[w][16 * mt + l16] = d;
   }
+  // the scoring wave's candidate value rows, requested now: they arrive
+  // during the reduction instead of one round trip per candidate later
+  float4 vcs[MTA][4];
+  if (MT > 0 && w == kWaves - 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * mt + 4 * q4 + i;
+        vcs[mt][i] = cbase + c < n_cand ? cand.v4(n, cbase + c, l16) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+  }
   // numerators: waves add into the LDS copy in turn; the last one keeps the sum
   // (the first barrier also ends every read of the candidate keys, whose LDS
   // the partials reuse)
@@ -528,8 +540,7 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
             for (int nt = 0; nt < 4; ++nt) num[nt] += wgt * comp(vp, nt);
           }
         }
-        float4 vc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (live) vc = cand.v4(n, cbase + c, l16);
+        const float4 vc = vcs[mt][i];
         float err = 0.0f;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -551,7 +562,27 @@ __global__ __launch_bounds__(kThreadsF, 2) void decode_sre_kernel(
       for (int c = 16 * MT + lane; c < kMaxCand; c += 64) sh.keys[c] = 0ull;
   }
   if (!SELECT) return;
-  bitonic_sort_desc(sh.keys, kMaxCand);
+  // the 64 keys, one per lane of one wave, sorted in registers (bitonic
+  // network over lane exchanges, no work-group barrier per stage)
+  __syncthreads();
+  if (w == 0) {
+    uint64_t x = sh.keys[lane];
+#pragma unroll
+    for (int kk = 2; kk <= kMaxCand; kk <<= 1) {
+#pragma unroll
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)x, j, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), j, 64);
+        const uint64_t y = ((uint64_t)hi << 32) | lo;
+        // descending inside blocks with (lane & kk) == 0, ascending
+        // otherwise: the lower lane of a pair keeps the larger key there
+        const bool keep_max = ((lane & j) == 0) == ((lane & kk) == 0);
+        x = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+      }
+    }
+    sh.keys[lane] = x;
+  }
+  __syncthreads();
   for (int i = tid; i < top_k; i += kThreadsF) sel[(size_t)n * top_k + i] = (int32_t)topk_index(sh.keys[i]);
   if (sel_k) {
     for (int i = tid; i < top_k * (kDim / 4); i += kThreadsF) {
