@@ -93,10 +93,12 @@ __device__ __forceinline__ uint32_t topk_index(uint64_t key) {
 // Bitonic sort of n (power of two, <= 4 * blockDim.x) keys in LDS, descending.
 // Every thread of the block must call it.
 __device__ __forceinline__ void bitonic_sort_desc(uint64_t* keys, int n) {
+  // read once: after each barrier the compiler would load it again
+  const int nt = blockDim.x;
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       __syncthreads();
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      for (int i = threadIdx.x; i < n; i += nt) {
         const int p = i ^ j;
         if (p > i) {
           const uint64_t x = keys[i];
