@@ -694,21 +694,25 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
   const int n_keys = n_old + 1 + n_after;
   const int wbase = win_first % wrows;  // ring row of token win_first; j < n_old <= W keeps wbase + j < 2 wrows
   auto ring = [&](int j) { const int r = wbase + j; return r >= wrows ? r - wrows : r; };
-  // four elements (from `off`) of key or value row j
-  auto key4 = [&](int j, int off) -> float4 {
-    if (j < n_old) return ld4<Tin>(win_k + ((size_t)n * wrows + ring(j)) * DQK + off);
-    if (j == n_old) return *reinterpret_cast<const float4*>(sh.kn + off);
+  // four elements (from `off`) of key or value row j, 0 <= j < n_keys. The
+  // memory load is issued whatever j is (a row held in LDS — the new token,
+  // the evicted pair's row — loads the window's first row instead and takes
+  // the LDS copy), so the kU loads of a step have no branch between them and
+  // are in flight together.
+  auto row4 = [&](const Tin* win, const Tin* cache, int dim, const float* lds_new, const float* lds_ev, int j,
+                  int off) -> float4 {
     const int r = j - n_old - 1;
-    return r == replaced ? *reinterpret_cast<const float4*>(sh.ek + off)
-                         : ld4<Tin>(cache_k + ((size_t)n * lambda + r) * DQK + off);
+    const bool from_cache = r >= 0 && r != replaced;
+    const int wj = j < n_old ? j : 0;
+    const Tin* p = from_cache ? cache + ((size_t)n * lambda + r) * dim + off
+                              : win + ((size_t)n * wrows + ring(wj)) * dim + off;
+    const float4 g = ld4<Tin>(p);
+    const float4 a = *reinterpret_cast<const float4*>(lds_new + off);
+    const float4 b = *reinterpret_cast<const float4*>(lds_ev + off);
+    return (j < n_old || from_cache) ? g : (j == n_old ? a : b);
   };
-  auto val4 = [&](int j, int off) -> float4 {
-    if (j < n_old) return ld4<Tin>(win_v + ((size_t)n * wrows + ring(j)) * DV + off);
-    if (j == n_old) return *reinterpret_cast<const float4*>(sh.vn + off);
-    const int r = j - n_old - 1;
-    return r == replaced ? *reinterpret_cast<const float4*>(sh.ev + off)
-                         : ld4<Tin>(cache_v + ((size_t)n * lambda + r) * DV + off);
-  };
+  auto key4 = [&](int j, int off) { return row4(win_k, cache_k, DQK, sh.kn, sh.ek, j, off); };
+  auto val4 = [&](int j, int off) { return row4(win_v, cache_v, DV, sh.vn, sh.ev, j, off); };
   // Scores: LPK lanes per key (a float4 each), KPW keys per wave and step;
   // weighted sum: LPV lanes per value row (a float4 each), RPW rows per wave
   // and step. kU steps are loaded before any is used.
@@ -729,7 +733,8 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int jl = jb + u * KPB;
-        k4[u] = jl < nt ? key4(j0 + jl, 4 * (lane % LPK)) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 x = key4(j0 + min(jl, nt - 1), 4 * (lane % LPK));
+        k4[u] = jl < nt ? x : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -763,8 +768,9 @@ __global__ __launch_bounds__(kThreads) void hdec_mix_kernel(
       for (int u = 0; u < kU; ++u) {
         const int jl = jb + u * RPB;
         const bool in = jl < nt;
-        v4[u] = in ? val4(j0 + jl, vc) : make_float4(0.f, 0.f, 0.f, 0.f);
-        pw[u] = in ? sh.sc[jl] : 0.0f;
+        const float4 x = val4(j0 + min(jl, nt - 1), vc);
+        v4[u] = in ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+        pw[u] = in ? sh.sc[min(jl, nt - 1)] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
