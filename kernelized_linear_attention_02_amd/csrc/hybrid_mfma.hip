@@ -97,12 +97,13 @@ struct PairSets {
 // returned). Every thread of the block calls it.
 __device__ __forceinline__ int gather_pair_tokens(const PairSets& ps, const int32_t* __restrict__ rej, int N, int n,
                                                   int32_t* dst) {
+  const int nt = blockDim.x;  // read once (it is reloaded after every store otherwise)
   int off = 0;
 #pragma unroll
   for (int s = 0; s < 2 * kL; ++s) {
     if (s < ps.n) {
       const int32_t* src = rej + ((size_t)ps.slot[s] * N + n) * kCStride;
-      for (int i = threadIdx.x; i < ps.cnt[s]; i += blockDim.x) dst[off + i] = src[i];
+      for (int i = threadIdx.x; i < ps.cnt[s]; i += nt) dst[off + i] = src[i];
       off += ps.cnt[s];
     }
   }
@@ -1013,18 +1014,24 @@ __device__ __forceinline__ void readout_keys_block(int32_t* ptok, int qblk, int 
       const int j = j0 + 16 * h + l16;
       const bool ok = j < wave_keys;
       const size_t row = base + (size_t)(ok ? key_token(j) : 0) * kFD;
+      // loaded whatever ok is (row 0 of the head otherwise) and selected
+      // after, so the tile's loads carry no branch and issue together
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        ka[h][ks] = ok ? *reinterpret_cast<const uint4*>(k + row + 32 * ks + 8 * q4) : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 x = *reinterpret_cast<const uint4*>(k + row + 32 * ks + 8 * q4);
+        ka[h][ks] = ok ? x : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   // value rows of the 8 keys of this lane's k-slots, columns 4 l16 .. + 3
+  // (the same unconditional loads)
   auto load_v = [&](int j0, uint2 (&vr)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kj = j0 + kslot_row(q4, j);
-      vr[j] = kj < wave_keys ? *reinterpret_cast<const uint2*>(v + base + (size_t)key_token(kj) * kFD + 4 * l16)
-                             : make_uint2(0, 0);
+      const bool ok = kj < wave_keys;
+      const uint2 x = *reinterpret_cast<const uint2*>(v + base + (size_t)(ok ? key_token(kj) : 0) * kFD + 4 * l16);
+      vr[j] = ok ? x : make_uint2(0, 0);
     }
   };
   auto scores = [&](int j0, const uint4 (&ka)[2][2], float (&sc)[2][4]) {
