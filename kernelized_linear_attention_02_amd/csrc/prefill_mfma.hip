@@ -893,11 +893,13 @@ __device__ __forceinline__ void readout_wave(StateLds<SF, G>& sh, const StateCtx
 
 // Work-group (g, head) handles sub-chunks g R .. g R + R - 1 of CS tokens:
 // the scales and scaled float16 values the state kernel reads (see Stage).
-// Thread (t, qd) holds dims 16 qd .. 16 qd + 15 of token t's q, k and v; the
-// next sub-chunk's rows are loaded while the current one is converted and
-// written, so reads and writes overlap. Every element is converted once
-// here instead of once per work-group of its head.
-constexpr int kStageR = 4;  // sub-chunks per staging work-group
+// Thread (t, qd) holds dims 16 qd .. 16 qd + 15 of token t's q, k and v; with
+// more than one sub-chunk per work-group, the next sub-chunk's rows are
+// loaded while the current one is converted and written. Every element is
+// converted once here instead of once per work-group of its head. One
+// sub-chunk per work-group measured fastest (of 1, 2 and 4 on 4 x 8 x 4096:
+// the most work-groups in flight).
+constexpr int kStageR = 1;  // sub-chunks per staging work-group
 
 template <int CS>
 __global__ __launch_bounds__(4 * CS) void prefill_stage_kernel(
@@ -930,7 +932,7 @@ __global__ __launch_bounds__(4 * CS) void prefill_stage_kernel(
   // sub-chunk x from `cur`; the next one is loaded into `nxt` first
   auto body = [&](int x, Rows& cur, Rows& nxt) {
     const int par = (x - x0) & 1;  // the reduction slots alternate
-    load(min(x + 1, x1 - 1), nxt);
+    if (x + 1 < x1) load(x + 1, nxt);
     if (x * CS + t >= T) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) cur.q[h] = cur.k[h] = cur.v[h] = z;
