@@ -258,42 +258,26 @@ struct ChainLds {
   int32_t pos[kCandMax];
 };
 
-// Token ids of the sets of `pa` for head n into dst, then those of `pb` from
-// dst + p0 on (p0: the count of pa rounded up to 32; the entries between are
-// set to token 0, a valid row never counted). The counts are known from the
-// sets, so every thread of the (1024-thread) block issues all its loads (at
-// most one per set of each list) before it stores any: one round trip for
-// both lists.
-__device__ __forceinline__ void chain_gather(const PairSets& pa, const PairSets& pb, const int32_t* __restrict__ rej,
-                                             int N, int n, int32_t* dst, int& na, int& p0, int& nb) {
+// Token ids of the sets of `ps` for head n into dst; every thread of the
+// (1024-thread) block issues its loads (at most one per set) before it
+// stores any.
+__device__ __forceinline__ int chain_gather(const PairSets& ps, const int32_t* __restrict__ rej, int N, int n,
+                                            int32_t* dst) {
   static_assert(kChainThreads >= kPairMax, "one entry per thread and set");
   const int tid = threadIdx.x;
-  int32_t xa[2 * kL], xb[2 * kL];
+  int32_t x[2 * kL];
 #pragma unroll
-  for (int s = 0; s < 2 * kL; ++s) {
-    xa[s] = (s < pa.n && tid < pa.cnt[s]) ? rej[((size_t)pa.slot[s] * N + n) * kCStride + tid] : 0;
-    xb[s] = (s < pb.n && tid < pb.cnt[s]) ? rej[((size_t)pb.slot[s] * N + n) * kCStride + tid] : 0;
-  }
+  for (int s = 0; s < 2 * kL; ++s)
+    x[s] = (s < ps.n && tid < ps.cnt[s]) ? rej[((size_t)ps.slot[s] * N + n) * kCStride + tid] : 0;
   int off = 0;
 #pragma unroll
   for (int s = 0; s < 2 * kL; ++s) {
-    if (s < pa.n) {
-      if (tid < pa.cnt[s]) dst[off + tid] = xa[s];
-      off += pa.cnt[s];
+    if (s < ps.n) {
+      if (tid < ps.cnt[s]) dst[off + tid] = x[s];
+      off += ps.cnt[s];
     }
   }
-  na = off;
-  p0 = (na + 31) & ~31;
-  if (tid >= na && tid < p0) dst[tid] = 0;
-  off = p0;
-#pragma unroll
-  for (int s = 0; s < 2 * kL; ++s) {
-    if (s < pb.n) {
-      if (tid < pb.cnt[s]) dst[off + tid] = xb[s];
-      off += pb.cnt[s];
-    }
-  }
-  nb = off - p0;
+  return off;
 }
 
 // One refresh of every head (one work-group each): closed-form terms, scores,
@@ -326,13 +310,17 @@ __global__ __launch_bounds__(kChainThreads) void hyb_chain_kernel(const ChainArg
   const int q4 = lane >> 4;
   const int n_cand = a.n_cache + a.n_ev;
   const size_t base = (size_t)n * a.T * kFD;
-  // candidate tokens (stored with the pair lists below, so that all of the
-  // prologue's loads are in flight together)
-  int32_t tok_c = 0;
-  if (tid < n_cand) tok_c = tid < a.n_cache ? a.cache_in[(size_t)n * kCStride + tid] : a.ev0 + (tid - a.n_cache);
+  {
+    const int32_t* cin = a.cache_in + (size_t)n * kCStride;
+    if (tid < n_cand) sh.tok[tid] = tid < a.n_cache ? cin[tid] : a.ev0 + (tid - a.n_cache);
+  }
+  const int np_prev = chain_gather(a.prev, a.rej, a.N, n, sh.ptok);
+  const int p0 = (np_prev + 31) & ~31;  // first pair of the new candidates' list
+  if (tid >= np_prev && tid < p0) sh.ptok[tid] = 0;  // padding: a valid token, never counted
+  const int np_since = chain_gather(a.since, a.rej, a.N, n, sh.ptok + p0);
+  const int np_all = p0 + np_since;
   // four adjacent threads per candidate (after the closed-form terms):
-  // quarter qd of its columns; its carried or state sums are loaded now,
-  // together with the pair lists
+  // quarter qd of its columns; its carried or state sums are loaded now
   const int c = tid >> 2;
   const int qd = tid & 3;
   const bool live = c < n_cand;
@@ -349,13 +337,6 @@ __global__ __launch_bounds__(kChainThreads) void hyb_chain_kernel(const ChainArg
       pre_den = row[64];
     }
   }
-  // the pair list: the previous refresh's pairs, padded to 32 (p0: the first
-  // pair of the new candidates' list), then the pairs rejected since the new
-  // candidates' state version
-  int np_prev, p0, np_since;
-  chain_gather(a.prev, a.since, a.rej, a.N, n, sh.ptok, np_prev, p0, np_since);
-  const int np_all = p0 + np_since;
-  if (tid < n_cand) sh.tok[tid] = tok_c;
   __syncthreads();
 
   const int ncT = (a.n_cache + 15) / 16;
